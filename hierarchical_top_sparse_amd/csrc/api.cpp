@@ -1,0 +1,294 @@
+// C ABI of libllsa.so: host-side validation, workspace sizing and kernel launches.
+// Every entry point is declared and documented in include/llsa.h.  No C++ exception crosses
+// the boundary; validation failures return before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/llsa.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int32_t fail(int32_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int32_t hip_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return LLSA_OK;
+  return fail(LLSA_ERR_HIP, "%s: %s", what, hipGetErrorString(err));
+}
+
+bool is_pow2(long v) { return v > 0 && (v & (v - 1)) == 0; }
+int log2i(long v) {
+  int b = 0;
+  while ((1L << b) < v) ++b;
+  return b;
+}
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int32_t check_problem(const llsa_problem* p) {
+  if (!p) return fail(LLSA_ERR_NULL, "problem is NULL");
+  if (p->dtype != LLSA_F32 && p->dtype != LLSA_BF16)
+    return fail(LLSA_ERR_DTYPE, "unknown dtype code %d", p->dtype);
+  if (p->layout != LLSA_LAYOUT_MORTON && p->layout != LLSA_LAYOUT_RASTER)
+    return fail(LLSA_ERR_DTYPE, "unknown layout code %d", p->layout);
+  if (p->batch < 1 || p->heads < 1)
+    return fail(LLSA_ERR_SHAPE, "batch (%d) and heads (%d) must be >= 1", p->batch, p->heads);
+  if (!is_pow2(p->height) || !is_pow2(p->width))
+    return fail(LLSA_ERR_SHAPE, "height (%d) and width (%d) must be powers of two", p->height,
+                p->width);
+  if (p->head_dim != 64)
+    return fail(LLSA_ERR_UNSUPPORTED, "head_dim %d: only 64 is implemented", p->head_dim);
+  if (p->block != 16)
+    return fail(p->block > 1 && is_pow2(p->block) && (log2i(p->block) % 2 == 0)
+                    ? LLSA_ERR_UNSUPPORTED
+                    : LLSA_ERR_SHAPE,
+                "block %d: only 16 (4x4 tiles) is implemented", p->block);
+  if (p->levels < 1 || p->levels > LLSA_MAX_LEVELS)
+    return fail(LLSA_ERR_SHAPE, "levels %d out of [1, %d]", p->levels, LLSA_MAX_LEVELS);
+  const long n = (long)p->height * p->width;
+  if (n < 256) return fail(LLSA_ERR_SHAPE, "N = %ld tokens: at least 256 needed", n);
+  if (n > (1L << 30)) return fail(LLSA_ERR_SHAPE, "N = %ld tokens is too large", n);
+  const long span = 1L << (4 * p->levels);
+  if (n % span != 0)
+    return fail(LLSA_ERR_SHAPE, "N = %ld is not divisible by block^levels = %ld", n, span);
+  const long n_top = n / span;
+  if (p->topk < 1 || p->topk > LLSA_MAX_TOPK || p->topk > n_top)
+    return fail(LLSA_ERR_SHAPE, "topk %d out of [1, min(%d, N/B^L = %ld)]", p->topk,
+                LLSA_MAX_TOPK, n_top);
+  if (p->enrich != 0 && p->enrich != 1)
+    return fail(LLSA_ERR_SHAPE, "enrich must be 0 or 1 (got %d)", p->enrich);
+  if (!(p->scale >= 0.f) || std::isinf(p->scale))
+    return fail(LLSA_ERR_SHAPE, "scale must be finite and >= 0");
+  if ((long)p->batch * p->heads * n >= (1L << 31))
+    return fail(LLSA_ERR_SHAPE, "batch*heads*N must be < 2^31");
+  return LLSA_OK;
+}
+
+llsa::Shape make_shape(const llsa_problem* p) {
+  llsa::Shape s{};
+  s.bh = p->batch * p->heads;
+  s.n = p->height * p->width;
+  s.hbits = log2i(p->height);
+  s.wbits = log2i(p->width);
+  s.levels = p->levels;
+  s.topk = p->topk;
+  s.enrich = p->enrich;
+  s.raster = p->layout == LLSA_LAYOUT_RASTER;
+  s.bf16 = p->dtype == LLSA_BF16;
+  s.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim);
+  return s;
+}
+
+#define CHECK_PTR(ptr, name)                                            \
+  do {                                                                  \
+    if (!(ptr)) return fail(LLSA_ERR_NULL, "%s is NULL", name);         \
+    if (!aligned16(ptr)) return fail(LLSA_ERR_ALIGN, "%s is not 16-byte aligned", name); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t llsa_abi_version(void) { return LLSA_ABI_VERSION; }
+
+const char* llsa_status_str(int32_t status) {
+  switch (status) {
+    case LLSA_OK: return "ok";
+    case LLSA_ERR_NULL: return "null pointer";
+    case LLSA_ERR_SHAPE: return "invalid shape";
+    case LLSA_ERR_DTYPE: return "invalid dtype or layout";
+    case LLSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LLSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LLSA_ERR_ALIGN: return "misaligned pointer";
+    case LLSA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* llsa_last_error(void) { return g_last_error.c_str(); }
+
+int32_t llsa_check(const llsa_problem* p) {
+  g_last_error.clear();
+  return check_problem(p);
+}
+
+int32_t llsa_workspace_bytes(const llsa_problem* p, size_t* fwd_bytes, size_t* bwd_bytes) {
+  const int32_t st = check_problem(p);
+  if (st != LLSA_OK) return st;
+  if (!fwd_bytes || !bwd_bytes) return fail(LLSA_ERR_NULL, "output pointer is NULL");
+  *fwd_bytes = 0;
+  *bwd_bytes = llsa::bwd_workspace_bytes(make_shape(p));
+  return LLSA_OK;
+}
+
+int32_t llsa_reorder(const llsa_problem* p, const void* x, void* y, int32_t inverse,
+                     void* stream) {
+  int32_t st = check_problem(p);
+  if (st != LLSA_OK) return st;
+  CHECK_PTR(x, "x");
+  CHECK_PTR(y, "y");
+  if (x == y) return fail(LLSA_ERR_SHAPE, "reorder cannot run in place");
+  if (inverse != 0 && inverse != 1) return fail(LLSA_ERR_SHAPE, "inverse must be 0 or 1");
+  return hip_status(llsa::launch_reorder(make_shape(p), x, y, inverse, (hipStream_t)stream),
+                    "llsa_reorder");
+}
+
+int32_t llsa_pool(const llsa_problem* p, const void* q, const void* k, const void* v,
+                  float* const* q_lv, float* const* k_lv, float* const* v_lv, void* stream) {
+  int32_t st = check_problem(p);
+  if (st != LLSA_OK) return st;
+  const void* x[3] = {q, k, v};
+  float* const* lv[3] = {q_lv, k_lv, v_lv};
+  const char* names[3] = {"q", "k", "v"};
+  bool any = false;
+  for (int t = 0; t < 3; ++t) {
+    if (!x[t]) continue;
+    any = true;
+    if (!aligned16(x[t])) return fail(LLSA_ERR_ALIGN, "%s is not 16-byte aligned", names[t]);
+    if (!lv[t]) return fail(LLSA_ERR_NULL, "level array of %s is NULL", names[t]);
+    for (int l = 1; l <= p->levels; ++l) {
+      float* ptr = lv[t][l - 1];
+      // levels 2..L-1 feed the next level and must be stored when L >= 3
+      if (!ptr && l >= 2 && l < p->levels)
+        return fail(LLSA_ERR_NULL, "%s level %d is needed for level %d", names[t], l, l + 1);
+      if (ptr && !aligned16(ptr))
+        return fail(LLSA_ERR_ALIGN, "%s level %d is not 16-byte aligned", names[t], l);
+    }
+  }
+  if (!any) return fail(LLSA_ERR_NULL, "q, k and v are all NULL");
+  return hip_status(llsa::launch_pool(make_shape(p), x, lv, (hipStream_t)stream), "llsa_pool");
+}
+
+int32_t llsa_select(const llsa_problem* p, const float* const* q_lv, const float* const* k_lv,
+                    int32_t* const* sel, int32_t level_hi, int32_t level_lo, void* stream) {
+  int32_t st = check_problem(p);
+  if (st != LLSA_OK) return st;
+  if (!q_lv || !k_lv || !sel) return fail(LLSA_ERR_NULL, "level or selection array is NULL");
+  if (level_lo < 1 || level_hi > p->levels || level_lo > level_hi)
+    return fail(LLSA_ERR_SHAPE, "levels %d..%d outside 1..%d", level_hi, level_lo, p->levels);
+  for (int l = level_lo; l <= level_hi; ++l) {
+    CHECK_PTR(q_lv[l - 1], "q level");
+    CHECK_PTR(k_lv[l - 1], "k level");
+    CHECK_PTR(sel[l - 1], "selection");
+  }
+  if (level_hi < p->levels) CHECK_PTR(sel[level_hi], "parent selection");
+  return hip_status(llsa::launch_select(make_shape(p), q_lv, k_lv, sel, level_hi, level_lo,
+                                        (hipStream_t)stream),
+                    "llsa_select");
+}
+
+int32_t llsa_attn_fwd(const llsa_problem* p, const void* q, const void* k, const void* v,
+                      const float* const* k_lv, const float* const* v_lv,
+                      const int32_t* const* sel, void* o, float* lse, void* stream) {
+  int32_t st = check_problem(p);
+  if (st != LLSA_OK) return st;
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(o, "o");
+  CHECK_PTR(lse, "lse");
+  if (!sel) return fail(LLSA_ERR_NULL, "sel is NULL");
+  for (int l = 1; l <= p->levels; ++l) {
+    if (l > 1 && !p->enrich) break;
+    CHECK_PTR(sel[l - 1], "selection");
+    if (l >= 2) {
+      if (!k_lv || !v_lv) return fail(LLSA_ERR_NULL, "pooled levels are NULL");
+      CHECK_PTR(k_lv[l - 1], "pooled k");
+      CHECK_PTR(v_lv[l - 1], "pooled v");
+    }
+  }
+  return hip_status(llsa::launch_attn_fwd(make_shape(p), q, k, v, k_lv, v_lv, sel, o, lse,
+                                          (hipStream_t)stream),
+                    "llsa_attn_fwd");
+}
+
+int32_t llsa_index_transpose_workspace(int32_t nmat, int32_t rows, int32_t cols, int32_t k,
+                                       size_t* bytes) {
+  if (!bytes) return fail(LLSA_ERR_NULL, "bytes is NULL");
+  if (nmat < 1 || rows < 1 || cols < 1 || k < 1)
+    return fail(LLSA_ERR_SHAPE, "nmat, rows, cols and k must be >= 1");
+  if ((long)nmat * rows * k >= (1L << 31))
+    return fail(LLSA_ERR_SHAPE, "nmat*rows*k must be < 2^31");
+  const int rbits = log2i(rows);
+  if (((unsigned long)cols + 1) << rbits > (1UL << 32))
+    return fail(LLSA_ERR_SHAPE, "(cols+1) * 2^ceil(log2 rows) exceeds 2^32");
+  *bytes = llsa::transpose_workspace_bytes(nmat, rows, cols, k);
+  return LLSA_OK;
+}
+
+int32_t llsa_index_transpose(int32_t nmat, int32_t rows, int32_t cols, int32_t k,
+                             const int32_t* csr, int32_t* csc_off, int32_t* csc_rows,
+                             void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  int32_t st = llsa_index_transpose_workspace(nmat, rows, cols, k, &need);
+  if (st != LLSA_OK) return st;
+  CHECK_PTR(csr, "csr");
+  CHECK_PTR(csc_off, "csc_off");
+  CHECK_PTR(csc_rows, "csc_rows");
+  if (!ws || ws_bytes < need)
+    return fail(LLSA_ERR_WORKSPACE, "workspace of %zu bytes needed (%zu given)", need, ws_bytes);
+  CHECK_PTR(ws, "ws");
+  return hip_status(llsa::launch_index_transpose(nmat, rows, cols, k, csr, csc_off, csc_rows, ws,
+                                                 (hipStream_t)stream),
+                    "llsa_index_transpose");
+}
+
+int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const void* v,
+                      const void* dout, const float* lse,
+                      const float* const* k_lv, const float* const* v_lv,
+                      const int32_t* const* sel, const int32_t* const* csc_off,
+                      const int32_t* const* csc_rows, void* dq, void* dk, void* dv, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int32_t st = check_problem(p);
+  if (st != LLSA_OK) return st;
+  if (p->dtype != LLSA_BF16)
+    return fail(LLSA_ERR_UNSUPPORTED, "the backward is implemented for bf16 only");
+  if (p->enrich && p->levels >= 2 && (p->levels - 1) * p->topk > 32)
+    return fail(LLSA_ERR_UNSUPPORTED, "backward supports at most 32 coarse keys per query "
+                "((levels-1)*topk = %d)", (p->levels - 1) * p->topk);
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(dout, "dout");
+  CHECK_PTR(lse, "lse");
+  CHECK_PTR(dq, "dq");
+  CHECK_PTR(dk, "dk");
+  CHECK_PTR(dv, "dv");
+  if (!sel || !csc_off || !csc_rows) return fail(LLSA_ERR_NULL, "index arrays are NULL");
+  for (int l = 1; l <= p->levels; ++l) {
+    if (l > 1 && !p->enrich) break;
+    CHECK_PTR(sel[l - 1], "selection");
+    CHECK_PTR(csc_off[l - 1], "csc_off");
+    CHECK_PTR(csc_rows[l - 1], "csc_rows");
+    if (l >= 2) {
+      if (!k_lv || !v_lv) return fail(LLSA_ERR_NULL, "pooled levels are NULL");
+      CHECK_PTR(k_lv[l - 1], "pooled k");
+      CHECK_PTR(v_lv[l - 1], "pooled v");
+    }
+  }
+  const llsa::Shape s = make_shape(p);
+  const size_t need = llsa::bwd_workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(LLSA_ERR_WORKSPACE, "workspace of %zu bytes needed (%zu given)", need, ws_bytes);
+  CHECK_PTR(ws, "ws");
+  return hip_status(llsa::launch_attn_bwd(s, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off,
+                                          csc_rows, dq, dk, dv, ws, (hipStream_t)stream),
+                    "llsa_attn_bwd");
+}
+
+}  // extern "C"

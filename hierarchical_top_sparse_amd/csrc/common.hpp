@@ -1,0 +1,126 @@
+// Shared device helpers for the gfx950 LLSA kernels: vector types, Morton addressing,
+// MFMA wrappers, LDS transpose reads and wave-level reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <type_traits>
+
+namespace llsa {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(int)))) int i32x4;
+
+constexpr int kDim = 64;        // head_dim
+constexpr int kBlock = 16;      // B: a 4x4 pixel tile
+constexpr int kBlockShift = 4;  // log2(B)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------------ token addressing
+// Geometry of the pixel grid: log2 of height/width.  In raster layout a token at Morton
+// position m lives at row y*W + x; in Morton layout at row m.
+struct Grid {
+  int hbits;   // log2(height)
+  int wbits;   // log2(width)
+  int raster;  // 1: tensors are raster-ordered
+};
+
+__device__ __forceinline__ uint32_t compact_even_bits(uint32_t v) {
+  v &= 0x55555555u;
+  v = (v | (v >> 1)) & 0x33333333u;
+  v = (v | (v >> 2)) & 0x0f0f0f0fu;
+  v = (v | (v >> 4)) & 0x00ff00ffu;
+  v = (v | (v >> 8)) & 0x0000ffffu;
+  return v;
+}
+
+// Morton position -> raster index.  Low 2r bits interleave x (even) and y (odd), r = min side
+// bits; the remaining high bits extend the longer side.
+__device__ __forceinline__ int morton_to_raster(int m, int hbits, int wbits) {
+  const int r = hbits < wbits ? hbits : wbits;
+  const uint32_t um = (uint32_t)m;
+  const uint32_t low = um & ((1u << (2 * r)) - 1u);
+  const uint32_t high = um >> (2 * r);
+  uint32_t x = compact_even_bits(low);
+  uint32_t y = compact_even_bits(low >> 1);
+  if (wbits > hbits) x |= high << r;
+  else y |= high << r;
+  return (int)((y << wbits) | x);
+}
+
+__device__ __forceinline__ int token_row(int m, const Grid& g) {
+  return g.raster ? morton_to_raster(m, g.hbits, g.wbits) : m;
+}
+
+// ------------------------------------------------------------------ conversions
+__device__ __forceinline__ bf16x8 cvt8_bf16(const float* f) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (bf16)f[i];
+  return r;
+}
+__device__ __forceinline__ bf16x8 cvt8_bf16(f32x4 a, f32x4 b) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = (bf16)a[i];
+    r[i + 4] = (bf16)b[i];
+  }
+  return r;
+}
+
+// ------------------------------------------------------------------ MFMA
+// v_mfma_f32_16x16x32_bf16: lane l holds A[l%16][8*(l/16) .. +7], B[8*(l/16) .. +7][l%16];
+// the result C[4*(l/16) + i][l%16], i = 0..3.
+__device__ __forceinline__ f32x4 mfma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x16_bf16: lane l holds A[l%16][4*(l/16) .. +3], B[4*(l/16) .. +3][l%16].
+__device__ __forceinline__ f32x4 mfma_bf16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(*(i16x4*)&a, *(i16x4*)&b, c, 0, 0, 0);
+}
+// v_mfma_f32_16x16x4_f32: lane l holds A[l%16][l/16], B[l/16][l%16].
+__device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ LDS transpose read
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4r+c supplies the address of row r,
+// columns 4c..4c+3 of a 4x16 block of 16-bit values; lane n of the group receives column n
+// (rows 0..3).  So reading rows k0..k0+3 of a row-major [k][n] LDS matrix this way gives
+// each lane the MFMA operand slice B[k0 .. k0+3][n].
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* lds_ptr) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
+  return *(bf16x4*)&r;
+}
+
+// Orders this wave's LDS accesses: writes before the barrier are visible to reads after it
+// (LDS requests of one wave are processed in order; the fences stop compiler reordering).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ------------------------------------------------------------------ cross-lane
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+__device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Reduce over the four 16-lane groups (lanes n, n+16, n+32, n+48).
+__device__ __forceinline__ float group4_max(float v) {
+  v = fmaxf(v, shfl_xor_f(v, 16));
+  v = fmaxf(v, shfl_xor_f(v, 32));
+  return v;
+}
+__device__ __forceinline__ float group4_sum(float v) {
+  v += shfl_xor_f(v, 16);
+  v += shfl_xor_f(v, 32);
+  return v;
+}
+
+}  // namespace llsa

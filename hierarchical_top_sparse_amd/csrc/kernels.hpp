@@ -1,0 +1,50 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernel files.
+// Every launcher enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace llsa {
+
+struct Shape {
+  int bh;        // batch * heads
+  int n;         // tokens per head
+  int hbits;     // log2(height)
+  int wbits;     // log2(width)
+  int levels;    // L
+  int topk;      // K
+  int enrich;    // 0/1
+  int raster;    // token tensors in raster order
+  int bf16;      // 1: bf16 token tensors, 0: fp32
+  float scale;   // softmax scale
+  int n_level(int l) const { return n >> (4 * l); }   // B = 16
+};
+
+hipError_t launch_reorder(const Shape& s, const void* x, void* y, int inverse,
+                          hipStream_t stream);
+
+hipError_t launch_pool(const Shape& s, const void* const x[3], float* const* lv[3],
+                       hipStream_t stream);
+
+hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* const* k_lv,
+                         int32_t* const* sel, int level_hi, int level_lo, hipStream_t stream);
+
+hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const void* v,
+                           const float* const* k_lv, const float* const* v_lv,
+                           const int32_t* const* sel, void* o, float* lse, hipStream_t stream);
+
+size_t transpose_workspace_bytes(int nmat, int rows, int cols, int k);
+hipError_t launch_index_transpose(int nmat, int rows, int cols, int k, const int32_t* csr,
+                                  int32_t* off, int32_t* rows_out, void* ws,
+                                  hipStream_t stream);
+
+size_t bwd_workspace_bytes(const Shape& s);
+hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const void* v,
+                           const void* dout, const float* lse,
+                           const float* const* k_lv, const float* const* v_lv,
+                           const int32_t* const* sel, const int32_t* const* csc_off,
+                           const int32_t* const* csc_rows, void* dq, void* dk, void* dv,
+                           void* ws, hipStream_t stream);
+
+}  // namespace llsa

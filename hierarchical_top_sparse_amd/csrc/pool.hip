@@ -1,0 +1,134 @@
+// Hierarchical compression: recursive mean pooling of Q, K and V (paper summary sec. 三:
+// level l has N / B^l tokens, each the mean of B level-(l-1) tokens).
+//
+// pool12_kernel: one workgroup per (tensor, head, group of B level-1 blocks = B^2 tokens).
+//   Reads the B^2 token rows once (coalesced 128/256-byte rows; raster layout reads 4x4 tiles
+//   as 4 row segments), writes level 1 and reduces level 2 through LDS.  HBM-bound.
+// pool_next_kernel: level l >= 3 from level l-1 (fp32, tiny).
+// All sums are fp32 in a fixed order; the 1/B factor is exact.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace llsa {
+
+struct PoolArgs {
+  const void* x[3];
+  float* lv1[3];
+  float* lv2[3];
+};
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void pool12_kernel(PoolArgs args, int n, Grid grid,
+                                                      int groups_per_head) {
+  __shared__ float sh[kBlock][kDim];
+  const int tensor = blockIdx.y;
+  const int head = blockIdx.x / groups_per_head;
+  const int group = blockIdx.x - head * groups_per_head;
+  const int t = threadIdx.x;
+  const int blk = t >> 4;        // level-1 block within the group
+  const int dq = (t & 15) * 4;   // first of 4 channels
+  const int first_tok = (group * kBlock + blk) * kBlock;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (BF16) {
+    const bf16* x = (const bf16*)args.x[tensor] + (long)head * n * kDim;
+#pragma unroll 4
+    for (int i = 0; i < kBlock; ++i) {
+      const int row = token_row(first_tok + i, grid);
+      const bf16x4 v = *(const bf16x4*)(x + (long)row * kDim + dq);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] += (float)v[c];
+    }
+  } else {
+    const float* x = (const float*)args.x[tensor] + (long)head * n * kDim;
+#pragma unroll 4
+    for (int i = 0; i < kBlock; ++i) {
+      const int row = token_row(first_tok + i, grid);
+      const f32x4 v = *(const f32x4*)(x + (long)row * kDim + dq);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] += v[c];
+    }
+  }
+  f32x4 l1;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) l1[c] = acc[c] * (1.0f / kBlock);
+  const int n1 = n >> kBlockShift;
+  if (args.lv1[tensor]) {
+    float* out = args.lv1[tensor] + ((long)head * n1 + group * kBlock + blk) * kDim + dq;
+    *(f32x4*)out = l1;
+  }
+  if (args.lv2[tensor]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sh[blk][dq + c] = l1[c];
+    __syncthreads();
+    if (t < kDim) {
+      float s = 0.f;
+#pragma unroll
+      for (int b = 0; b < kBlock; ++b) s += sh[b][t];
+      const int n2 = n1 >> kBlockShift;
+      args.lv2[tensor][((long)head * n2 + group) * kDim + t] = s * (1.0f / kBlock);
+    }
+  }
+}
+
+struct PoolNextArgs {
+  const float* in[3];
+  float* out[3];
+};
+
+// out[j][d] = mean_t in[j*B + t][d]; one thread per output element.
+__global__ __launch_bounds__(256) void pool_next_kernel(PoolNextArgs args, long total_out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  const int tensor = blockIdx.y;
+  if (i >= total_out) return;
+  const long j = i / kDim;
+  const int d = (int)(i - j * kDim);
+  const float* src = args.in[tensor] + (j * kBlock) * kDim + d;
+  float s = 0.f;
+#pragma unroll
+  for (int t = 0; t < kBlock; ++t) s += src[t * kDim];
+  args.out[tensor][i] = s * (1.0f / kBlock);
+}
+
+hipError_t launch_pool(const Shape& s, const void* const x[3], float* const* lv[3],
+                       hipStream_t stream) {
+  PoolArgs a{};
+  int nt = 0;
+  for (int t = 0; t < 3; ++t) {
+    if (!x[t]) continue;
+    a.x[nt] = x[t];
+    a.lv1[nt] = lv[t][0];
+    a.lv2[nt] = s.levels >= 2 ? lv[t][1] : nullptr;
+    ++nt;
+  }
+  if (nt == 0) return hipSuccess;
+  const int groups_per_head = s.n >> (2 * kBlockShift);
+  const Grid grid{s.hbits, s.wbits, s.raster};
+  const dim3 blocks((unsigned)(s.bh * groups_per_head), (unsigned)nt);
+  if (s.bf16)
+    hipLaunchKernelGGL(pool12_kernel<true>, blocks, dim3(256), 0, stream, a, s.n, grid,
+                       groups_per_head);
+  else
+    hipLaunchKernelGGL(pool12_kernel<false>, blocks, dim3(256), 0, stream, a, s.n, grid,
+                       groups_per_head);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  for (int l = 3; l <= s.levels; ++l) {
+    PoolNextArgs b{};
+    int m = 0;
+    for (int t = 0; t < 3; ++t) {
+      if (!x[t] || !lv[t][l - 1]) continue;
+      b.in[m] = lv[t][l - 2];
+      b.out[m] = lv[t][l - 1];
+      ++m;
+    }
+    if (m == 0) continue;
+    const long total = (long)s.bh * s.n_level(l) * kDim;
+    hipLaunchKernelGGL(pool_next_kernel, dim3((unsigned)((total + 255) / 256), (unsigned)m),
+                       dim3(256), 0, stream, b, total);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+}  // namespace llsa

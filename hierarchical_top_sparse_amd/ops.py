@@ -1,0 +1,113 @@
+"""LLSA as a PyTorch op: the whole hot path through the C ABI.
+
+forward : [reorder] -> pool -> select -> sparse attention (-> inverse reorder)
+backward: CSR->CSC transpose per level -> sparse backward
+
+With layout RASTER (the default) the reorder is folded into the kernels' addressing: the
+inputs are raster-ordered pixel tokens and so are the outputs.  With layout MORTON the caller
+supplies Morton-ordered tokens (llsa_reorder produces them) and gets Morton-ordered outputs.
+PyTorch only allocates device memory and provides the stream.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _abi
+from ._abi import (LLSA_BF16, LLSA_F32, LLSA_LAYOUT_MORTON, LLSA_LAYOUT_RASTER, Problem,
+                   llsa_attn_bwd, llsa_attn_fwd, llsa_index_transpose,
+                   llsa_index_transpose_workspace, llsa_pool, llsa_reorder, llsa_select,
+                   llsa_workspace_bytes)
+
+__all__ = ["Problem", "make_problem", "llsa_forward", "llsa_backward", "llsa_attention",
+           "reorder", "LLSA_BF16", "LLSA_F32", "LLSA_LAYOUT_MORTON", "LLSA_LAYOUT_RASTER"]
+
+
+def make_problem(q: torch.Tensor, height: int, width: int, levels: int, topk: int = 8,
+                 enrich: bool = True, scale: float = 0.0, layout: int = LLSA_LAYOUT_RASTER):
+    b, h, n, d = q.shape
+    if n != height * width:
+        raise ValueError(f"token count {n} != height*width {height * width}")
+    dtype = {torch.bfloat16: LLSA_BF16, torch.float32: LLSA_F32}.get(q.dtype)
+    if dtype is None:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return Problem(batch=b, heads=h, height=height, width=width, levels=levels, topk=topk,
+                   enrich=int(enrich), head_dim=d, scale=scale, dtype=dtype, layout=layout)
+
+
+def reorder(p: Problem, x: torch.Tensor, inverse: bool = False) -> torch.Tensor:
+    y = torch.empty_like(x)
+    llsa_reorder(p, x, y, inverse)
+    return y
+
+
+def llsa_forward(p: Problem, q, k, v):
+    """Returns a dict: o, lse, q_lv, k_lv, v_lv (levels 1..L, v level 1 is None), sel."""
+    dev = q.device
+    lv_shape = lambda l: (p.batch, p.heads, p.n_level(l), p.head_dim)
+    f32 = dict(device=dev, dtype=torch.float32)
+    q_lv = [torch.empty(lv_shape(l), **f32) for l in range(1, p.levels + 1)]
+    k_lv = [torch.empty(lv_shape(l), **f32) for l in range(1, p.levels + 1)]
+    # V's level 1 is only an intermediate of the fused pooling (attention reads levels >= 2)
+    v_lv = [None] + [torch.empty(lv_shape(l), **f32) for l in range(2, p.levels + 1)]
+    need_v = p.enrich and p.levels >= 2
+    llsa_pool(p, q, k, v if need_v else None, q_lv, k_lv, v_lv)
+    sel = [torch.empty((p.batch, p.heads, p.n_level(l), p.topk), device=dev, dtype=torch.int32)
+           for l in range(1, p.levels + 1)]
+    llsa_select(p, q_lv, k_lv, sel)
+    o = torch.empty_like(q)
+    lse = torch.empty((p.batch, p.heads, p.n), **f32)
+    llsa_attn_fwd(p, q, k, v, k_lv, v_lv, sel, o, lse)
+    return dict(o=o, lse=lse, q_lv=q_lv, k_lv=k_lv, v_lv=v_lv, sel=sel)
+
+
+def build_csc(p: Problem, sel):
+    """Per level l: CSC of Sel_l (rows = queries, cols = keys, both n_l): (off, rows)."""
+    levels = p.levels if p.enrich else 1
+    offs, rows = [], []
+    nmat = p.batch * p.heads
+    ws_bytes = max(llsa_index_transpose_workspace(nmat, p.n_level(l), p.n_level(l), p.topk)
+                   for l in range(1, levels + 1))
+    ws = torch.empty(ws_bytes, device=sel[0].device, dtype=torch.uint8)
+    for l in range(1, levels + 1):
+        nl = p.n_level(l)
+        off = torch.empty((p.batch, p.heads, nl + 1), device=ws.device, dtype=torch.int32)
+        r = torch.empty((p.batch, p.heads, nl * p.topk), device=ws.device, dtype=torch.int32)
+        llsa_index_transpose(nmat, nl, nl, p.topk, sel[l - 1], off, r, ws)
+        offs.append(off)
+        rows.append(r)
+    return offs, rows
+
+
+def llsa_backward(p: Problem, q, k, v, fwd: dict, dout):
+    """Returns (dq, dk, dv) for the forward state `fwd`."""
+    offs, rows = build_csc(p, fwd["sel"])
+    _, ws_bytes = llsa_workspace_bytes(p)
+    ws = torch.empty(max(ws_bytes, 16), device=q.device, dtype=torch.uint8)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    llsa_attn_bwd(p, q, k, v, dout, fwd["lse"], fwd["k_lv"], fwd["v_lv"], fwd["sel"], offs,
+                  rows, dq, dk, dv, ws)
+    return dq, dk, dv
+
+
+class _LLSAFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, p):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        fwd = llsa_forward(p, q, k, v)
+        ctx.p = p
+        ctx.fwd = fwd
+        ctx.save_for_backward(q, k, v)
+        return fwd["o"]
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v = ctx.saved_tensors
+        dq, dk, dv = llsa_backward(ctx.p, q, k, v, ctx.fwd, dout.contiguous())
+        return dq, dk, dv, None
+
+
+def llsa_attention(q, k, v, height: int, width: int, levels: int, topk: int = 8,
+                   enrich: bool = True, scale: float = 0.0):
+    """Log-linear sparse attention over raster-ordered pixel tokens [b, H, height*width, 64]."""
+    p = make_problem(q, height, width, levels, topk, enrich, scale, LLSA_LAYOUT_RASTER)
+    return _LLSAFunction.apply(q, k, v, p)

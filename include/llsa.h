@@ -1,0 +1,177 @@
+/*
+ * llsa.h — C ABI of the MI355X (gfx950) Log-linear Sparse Attention library (libllsa.so).
+ *
+ * The method: "Trainable Log-linear Sparse Attention for Efficient Diffusion Transformers"
+ * (paper summary page, sec. 三 Hierarchical Top-K, sec. 四 Hierarchical KV Enrichment,
+ * sec. 4.1 sparse backward via a CSR->CSC sparse index transpose, sec. 4.2 / Figure 2 2D index
+ * reordering), and the popular article on arXiv:2512.16615 (sec. 三 and 四).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Token tensors (q, k, v, o, dout, dq, dk, dv) are contiguous [batch, heads, N, head_dim]
+ *    with N = height * width.  Their token order is `layout`:
+ *      LLSA_LAYOUT_MORTON: already in Morton (Z-order) position order;
+ *      LLSA_LAYOUT_RASTER: raster order y*width + x; the kernels apply the Morton map in
+ *                          their load/store addressing (the reorder step folded into them).
+ *  - Pooled levels, selections, CSC indices and the log-sum-exp are always indexed in
+ *    Morton/block order: level l has n_l = N / block^l tokens.
+ *      level arrays  float   [batch, heads, n_l, head_dim]
+ *      sel[l-1]      int32   [batch, heads, n_l, topk]  (key ids at level l, ascending)
+ *      lse           float   [batch, heads, N]          (natural log, coarse weights included)
+ *  - All data pointers are DEVICE pointers, 16-byte aligned; the caller owns every buffer.
+ *    Inputs must not alias outputs.  The library allocates no device memory and keeps no
+ *    state between calls (only a thread-local error message).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues work;
+ *    none synchronises.  Device faults surface at the caller's next synchronisation.
+ *  - Return value: llsa_status.  Validation errors return before anything is enqueued and
+ *    leave outputs untouched; LLSA_ERR_HIP means a launch failed (outputs undefined).
+ *    llsa_last_error() gives a message for the last failure on the calling thread.
+ *  - Results are deterministic: no atomics, fixed reduction orders.
+ *  - Supported: head_dim 64, block 16 (4x4 pixel tiles), height and width powers of two,
+ *    N % block^levels == 0, 1 <= topk <= min(16, N / block^levels), 1 <= levels <= 6,
+ *    batch*heads*N < 2^31.  dtype bf16 for every call; f32 for reorder/pool/select/attn_fwd.
+ */
+#ifndef LLSA_H
+#define LLSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LLSA_ABI_VERSION 1
+#define LLSA_MAX_LEVELS 6
+#define LLSA_MAX_TOPK 16
+
+typedef enum {
+  LLSA_OK = 0,
+  LLSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  LLSA_ERR_SHAPE = 2,       /* sizes violate the constraints above */
+  LLSA_ERR_DTYPE = 3,       /* unknown dtype or layout code */
+  LLSA_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. head_dim != 64) */
+  LLSA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  LLSA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
+  LLSA_ERR_HIP = 7          /* a HIP launch failed */
+} llsa_status;
+
+typedef enum { LLSA_F32 = 0, LLSA_BF16 = 1 } llsa_dtype;
+typedef enum { LLSA_LAYOUT_MORTON = 0, LLSA_LAYOUT_RASTER = 1 } llsa_layout;
+
+typedef struct {
+  int32_t batch;
+  int32_t heads;
+  int32_t height;   /* pixel rows    (power of two) */
+  int32_t width;    /* pixel columns (power of two) */
+  int32_t head_dim; /* 64 */
+  int32_t block;    /* B: tokens per pooled token; 16 = a 4x4 tile */
+  int32_t levels;   /* L: pooled levels 1..L; the coarsest has N / B^L tokens */
+  int32_t topk;     /* K: keys kept per query at every level */
+  int32_t enrich;   /* 0: fine keys only; 1: also the K selected keys of levels 2..L */
+  float scale;      /* softmax scale; 0 => 1/sqrt(head_dim) */
+  int32_t dtype;    /* llsa_dtype of the token tensors */
+  int32_t layout;   /* llsa_layout of the token tensors */
+} llsa_problem;
+
+/* ABI version (LLSA_ABI_VERSION of the built library). */
+int32_t llsa_abi_version(void);
+
+/* Static string for a status code. */
+const char* llsa_status_str(int32_t status);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* llsa_last_error(void);
+
+/* Host-only validation of a problem description; enqueues nothing. */
+int32_t llsa_check(const llsa_problem* p);
+
+/* Workspace bytes llsa_attn_bwd needs (fwd_bytes is 0: the forward needs none). */
+int32_t llsa_workspace_bytes(const llsa_problem* p, size_t* fwd_bytes, size_t* bwd_bytes);
+
+/*
+ * llsa_reorder — 2D index reordering (paper summary sec. 4.2 / Figure 2; article sec. 四,
+ * "like Z-order or Hilbert curves").  Morton order: bits 2i / 2i+1 of the curve position are
+ * bit i of x / y; bits beyond the shorter side extend the longer one.  inverse = 0:
+ * y[.., m, :] = x[.., raster(m), :]; inverse = 1: y[.., raster(m), :] = x[.., m, :].
+ * x, y: [batch, heads, N, head_dim] of p->dtype; p->layout is ignored.  Bit-exact copy.
+ */
+int32_t llsa_reorder(const llsa_problem* p, const void* x, void* y, int32_t inverse,
+                     void* stream);
+
+/*
+ * llsa_pool — hierarchical compression by recursive mean pooling (summary sec. 三):
+ * X_l[j] = (1/B) * sum_{t<B} X_{l-1}[j*B + t], l = 1..L, X_0 = the Morton-ordered tokens.
+ * q, k, v: token tensors (layout p->layout, dtype p->dtype); a NULL input skips that tensor.
+ * q_lv/k_lv/v_lv: arrays of L float pointers (level l at index l-1), each
+ * [batch, heads, n_l, head_dim]; a NULL entry skips storing that level.  fp32 arithmetic.
+ */
+int32_t llsa_pool(const llsa_problem* p, const void* q, const void* k, const void* v,
+                  float* const* q_lv, float* const* k_lv, float* const* v_lv, void* stream);
+
+/*
+ * llsa_select — coarse-to-fine top-K selection (summary sec. 三; article sec. 三).
+ * Level L: scores Q_L . K_L over all n_L keys, top-K per row.  Level l < L: query a scores
+ * only the K*B children {c*B + t} of Sel_{l+1}[a / B] and keeps the top-K.  Scores are fp32
+ * dot products of the pooled levels; ties go to the lower key id; rows are stored ascending.
+ * Computes levels level_hi down to level_lo (1 <= level_lo <= level_hi <= L); when
+ * level_hi < L, sel[level_hi] (level level_hi + 1) is read as the parent selection.
+ * q_lv, k_lv: L level pointers (only the levels computed are read); sel: L pointers.
+ */
+int32_t llsa_select(const llsa_problem* p, const float* const* q_lv, const float* const* k_lv,
+                    int32_t* const* sel, int32_t level_hi, int32_t level_lo, void* stream);
+
+/*
+ * llsa_attn_fwd — sparse attention with hierarchical KV enrichment (summary sec. 四;
+ * article sec. 三/四: gather of the selected blocks, no dense mask).  Each level-1 query
+ * block p (B queries) attends to the B tokens of each block in sel[0][p] and, if enrich,
+ * for l = 2..L to the pooled keys/values k_lv/v_lv[l-1][sel[l-1][p / B^(l-1)]] with weight
+ * B^l (their exp(score) is multiplied by B^l).  s = scale * q.k; o = sum w e^s v / sum w e^s;
+ * lse = log sum w e^s.  bf16: MFMA with fp32 accumulation and softmax (pooled keys/values are
+ * rounded to bf16 for the MFMA); f32: fp32 MFMA.  k_lv/v_lv: L pointers, levels >= 2 read.
+ * Out-of-range indices in sel are skipped.  o: token tensor (layout), lse: [b, H, N] Morton.
+ */
+int32_t llsa_attn_fwd(const llsa_problem* p, const void* q, const void* k, const void* v,
+                      const float* const* k_lv, const float* const* v_lv,
+                      const int32_t* const* sel, void* o, float* lse, void* stream);
+
+/*
+ * llsa_index_transpose — sparse index transpose CSR -> CSC (summary sec. 4.1; article sec.
+ * 四: per-key counts, offsets by prefix sum, a flat vector of query ids per key).
+ * csr: [nmat, rows, k] int32 column ids of each row (the K keys a query selected);
+ * csc_off: [nmat, cols + 1]; csc_rows: [nmat, rows * k]: the rows that selected column c are
+ * csc_rows[off[c] .. off[c+1]) in ascending order.  Entries outside [0, cols) are dropped
+ * (off[cols] counts the kept ones; later csc_rows entries are unspecified).
+ * Atomic-free (sort of (column, row) codes), so the output is deterministic.
+ * ws: device workspace of llsa_index_transpose_workspace() bytes.
+ * Requires (cols + 1) * 2^ceil(log2 rows) <= 2^32.
+ */
+int32_t llsa_index_transpose_workspace(int32_t nmat, int32_t rows, int32_t cols, int32_t k,
+                                       size_t* bytes);
+int32_t llsa_index_transpose(int32_t nmat, int32_t rows, int32_t cols, int32_t k,
+                             const int32_t* csr, int32_t* csc_off, int32_t* csc_rows,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * llsa_attn_bwd — sparse backward (summary sec. 4.1 and Figure 4: query-major dQ, key-major
+ * dK/dV over the CSC index, no T x T mask).  Per query: P = w e^{s - lse}, dP = dO.v,
+ * D = sum_e P_e dP_e, dS = P (dP - D); dq = scale sum dS k; fine keys get dk += scale dS q,
+ * dv += P dO; a coarse key (l, j) collects the same into dK_l[j], dV_l[j], which are then
+ * spread over its B^l fine tokens with factor 1/B^l (chain rule of the mean pooling).
+ * D is recomputed from the scores (the forward output O is not needed).
+ * No gradient through the selection or the pooled Q.  Outputs: complete dq, dk, dv
+ * (layout p->layout).  csc_off/csc_rows: L pointers, level l from llsa_index_transpose of
+ * sel[l-1] (rows = cols = n_l); levels >= 2 are read only if enrich.  bf16 only.
+ * ws: llsa_workspace_bytes(bwd) bytes of device memory.
+ */
+int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const void* v,
+                      const void* dout, const float* lse,
+                      const float* const* k_lv, const float* const* v_lv,
+                      const int32_t* const* sel, const int32_t* const* csc_off,
+                      const int32_t* const* csc_rows, void* dq, void* dk, void* dv, void* ws,
+                      size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLSA_H */

@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every entry point
+include/llsa.h declares, and every validation error is returned before anything is enqueued.
+Fake device pointers are never dereferenced: each call below fails validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llsa.h")
+
+abi = pytest.importorskip("hierarchical_top_sparse_amd._abi")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(abi._LIB_PATH):
+        pytest.fail("libllsa.so is not built (python -m hierarchical_top_sparse_amd.build)")
+    return abi.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int32_t|const char\*)\s+(llsa_\w+)\(", text, re.M)))
+
+
+def test_header_declares_every_bound_symbol():
+    assert _declared() == sorted(abi.exported_symbols())
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_version_and_status_strings(L):
+    assert L.llsa_abi_version() == 1
+    for code in range(8):
+        assert L.llsa_status_str(code)
+    assert L.llsa_status_str(99) == b"unknown status"
+
+
+def _p(**kw):
+    base = dict(batch=1, heads=2, height=64, width=64, levels=2)
+    base.update(kw)
+    return abi.Problem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), 0),
+    (dict(height=256, width=256, levels=3, dtype=abi.LLSA_BF16), 0),
+    (dict(height=128, width=256, levels=3), 0),
+    (dict(width=48), 2),                    # not a power of two
+    (dict(height=16, width=8), 2),          # fewer than 256 tokens
+    (dict(levels=3), 2),                    # N % B^L != 0
+    (dict(topk=17), 2),                     # above the 16 supported
+    (dict(levels=2, topk=9, height=32, width=64), 2),  # K > N / B^L = 8
+    (dict(topk=0), 2),
+    (dict(head_dim=128), 4),
+    (dict(block=64), 4),                    # a power of 4 but not implemented
+    (dict(block=8), 2),                     # not a square tile
+    (dict(levels=0), 2),
+    (dict(levels=7), 2),
+    (dict(enrich=2), 2),
+    (dict(scale=-1.0), 2),
+    (dict(dtype=5), 3),
+    (dict(layout=7), 3),
+    (dict(batch=0), 2),
+])
+def test_check_status(L, kw, status):
+    p = _p(**kw)
+    assert abi.llsa_check(p) == status, abi.llsa_last_error()
+    if status:
+        assert abi.llsa_last_error()
+
+
+FAKE = 0x10000          # aligned, never dereferenced
+MISALIGNED = 0x10008
+
+
+def test_entry_points_reject_null_and_misaligned(L):
+    p = ctypes.byref(_p().c())
+    assert L.llsa_reorder(p, None, ctypes.c_void_p(FAKE), 0, None) == 1
+    assert L.llsa_reorder(p, ctypes.c_void_p(MISALIGNED), ctypes.c_void_p(FAKE), 0, None) == 6
+    assert L.llsa_reorder(p, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 0, None) == 2
+    assert L.llsa_reorder(p, ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 64), 3, None) == 2
+    assert L.llsa_pool(p, None, None, None, None, None, None, None) == 1
+    null6 = (ctypes.c_void_p * 6)()
+    assert L.llsa_select(p, null6, null6, null6, 2, 1, None) == 1
+    assert L.llsa_select(p, null6, null6, null6, 3, 1, None) == 2
+    assert L.llsa_attn_fwd(p, None, None, None, null6, null6, null6, None, None, None) == 1
+    bf = ctypes.byref(_p(dtype=abi.LLSA_F32).c())
+    assert L.llsa_attn_bwd(bf, *([ctypes.c_void_p(FAKE)] * 5), null6, null6, null6, null6,
+                           null6, *([ctypes.c_void_p(FAKE)] * 4), 1 << 30, None) == 4
+
+
+def test_workspace_queries(L):
+    f, b = abi.llsa_workspace_bytes(_p(dtype=abi.LLSA_BF16))
+    assert f == 0 and b > 0
+    assert abi.llsa_index_transpose_workspace(6, 4096, 4096, 8) == 2 * 4 * 6 * 4096 * 8
+    out = ctypes.c_size_t()
+    assert L.llsa_index_transpose_workspace(1, 0, 4, 8, ctypes.byref(out)) == 2
+    assert L.llsa_index_transpose_workspace(1, 1 << 20, 1 << 13, 8, ctypes.byref(out)) == 2
+    # workspace too small / missing
+    fake = ctypes.c_void_p(FAKE)
+    assert L.llsa_index_transpose(1, 16, 16, 8, fake, fake, fake, None, 0, None) == 5
+    assert L.llsa_index_transpose(1, 16, 16, 8, fake, fake, fake, fake, 8, None) == 5
+    assert L.llsa_index_transpose(1, 16, 16, 8, None, fake, fake, fake, 4096, None) == 1
+
+
+def test_backward_rejects_too_many_coarse_keys(L):
+    p = _p(height=1024, width=1024, levels=4, topk=16, dtype=abi.LLSA_BF16)
+    assert abi.llsa_check(p) == 0
+    fake = ctypes.c_void_p(FAKE)
+    null6 = (ctypes.c_void_p * 6)()
+    st = L.llsa_attn_bwd(ctypes.byref(p.c()), *([fake] * 5), null6, null6, null6, null6, null6,
+                         *([fake] * 4), 1 << 30, None)
+    assert st == 4 and b"coarse" in L.llsa_last_error()

@@ -1,0 +1,283 @@
+"""GPU parity of every hot-path step against the CPU oracle, through the C ABI.
+
+Inputs come from the seeded generator (smooth 2D fields + noise for Q/K, N(0,1) for V/dO);
+shapes follow the workloads: 64x64 fp32 (L=2), 128x128 (L=2), 256x256 (L=3), 512x512 (L=3),
+plus small and ragged cases.  Full-size configurations compare whole heads chosen by index
+(heads are independent), the rest compare every output.
+"""
+import numpy as np
+import pytest
+import torch
+
+from hierarchical_top_sparse_amd import _abi, gen, ops
+from oracle import llsa_oracle as orc
+from tests.parity_util import (assert_close, check_selection, gpu_sel_lists, to64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+RASTER, MORTON = _abi.LLSA_LAYOUT_RASTER, _abi.LLSA_LAYOUT_MORTON
+
+
+def _inputs(batch, heads, height, width, dtype, seed, grad=False):
+    x = gen.make_inputs(batch, heads, height, width, 64, dtype, seed, with_grad=grad)
+    return {k: v.to(DEV) for k, v in x.items()}, {k: to64(v) for k, v in x.items()}
+
+
+def _problem(x, height, width, levels, topk=8, enrich=True, layout=RASTER):
+    return ops.make_problem(x, height, width, levels, topk, enrich, 0.0, layout)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32).cpu()
+
+
+# ----------------------------------------------------------------------------- reorder
+
+
+@pytest.mark.parametrize("h,w,dtype", [(64, 64, torch.float32), (128, 128, torch.bfloat16),
+                                       (64, 256, torch.bfloat16), (256, 64, torch.float32),
+                                       (512, 512, torch.bfloat16)])
+def test_reorder_bit_exact(h, w, dtype):
+    x = torch.randn(1, 3, h * w, 64, dtype=torch.float32).to(dtype).to(DEV)
+    p = _problem(x, h, w, 1, topk=1)
+    y = ops.reorder(p, x)
+    perm = torch.from_numpy(orc.morton_perm(h, w))
+    assert torch.equal(_bits(y), _bits(x.cpu()[:, :, perm, :]))
+    back = ops.reorder(p, y, inverse=True)
+    assert torch.equal(_bits(back), _bits(x))
+
+
+# ----------------------------------------------------------------------------- pooling
+
+
+@pytest.mark.parametrize("h,w,levels,dtype,layout", [
+    (64, 64, 2, torch.float32, RASTER), (128, 128, 2, torch.bfloat16, MORTON),
+    (256, 256, 3, torch.bfloat16, RASTER), (128, 256, 3, torch.bfloat16, RASTER)])
+def test_pool_matches_oracle(h, w, levels, dtype, layout):
+    d, ref = _inputs(1, 2, h, w, dtype, 11)
+    q, k, v = d["q"], d["k"], d["v"]
+    p = _problem(q, h, w, levels, layout=layout)
+    if layout == MORTON:
+        q, k, v = (ops.reorder(p, t) for t in (q, k, v))
+    lv = {t: [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+          for t in "qkv"}
+    _abi.llsa_pool(p, q, k, v, lv["q"], lv["k"], lv["v"])
+    for t in "qkv":
+        want = orc.pool_levels(orc.reorder(ref[t], h, w), 16, levels)
+        for l in range(levels):
+            got = to64(lv[t][l])
+            assert np.abs(got - want[l]).max() <= 1e-5 * max(1.0, np.abs(want[l]).max()), (t, l)
+
+
+# ----------------------------------------------------------------------------- selection
+
+
+@pytest.mark.parametrize("h,w,levels,topk", [(64, 64, 2, 8), (128, 128, 2, 8), (256, 256, 3, 8),
+                                             (128, 256, 3, 5), (64, 64, 1, 16), (64, 64, 2, 3)])
+def test_select_matches_oracle_within_tie_window(h, w, levels, topk):
+    d, ref = _inputs(1, 3, h, w, torch.bfloat16, 21)
+    p = _problem(d["q"], h, w, levels, topk)
+    fwd = ops.llsa_forward(p, d["q"], d["k"], d["v"])
+    q_lv = orc.pool_levels(orc.reorder(ref["q"], h, w), 16, levels)
+    k_lv = orc.pool_levels(orc.reorder(ref["k"], h, w), 16, levels)
+    sel = [s.cpu().numpy().astype(np.int64) for s in fwd["sel"]]
+    flips = check_selection(sel, q_lv, k_lv, topk, f"{h}x{w} L{levels}")
+    total = sum(s.shape[0] * s.shape[1] * s.shape[2] for s in sel)
+    assert flips <= max(2, total // 1000), f"{flips} near-tie flips out of {total} rows"
+
+
+def test_select_single_level_from_given_parent():
+    """llsa_select on one level with an oracle-supplied parent selection."""
+    h = w = 128
+    d, ref = _inputs(1, 2, h, w, torch.bfloat16, 23)
+    p = _problem(d["q"], h, w, 2)
+    fwd = ops.llsa_forward(p, d["q"], d["k"], d["v"])
+    q_lv = orc.pool_levels(orc.reorder(ref["q"], h, w), 16, 2)
+    k_lv = orc.pool_levels(orc.reorder(ref["k"], h, w), 16, 2)
+    parent = np.stack([orc.select_coarsest(q_lv[1][0, i], k_lv[1][0, i], 8) for i in range(2)])
+    sel = [torch.empty_like(fwd["sel"][0]),
+           torch.from_numpy(parent[None].astype(np.int32)).to(DEV)]
+    _abi.llsa_select(p, fwd["q_lv"], fwd["k_lv"], sel, level_hi=1, level_lo=1)
+    got = sel[0].cpu().numpy().astype(np.int64)
+    for i in range(2):
+        from tests.parity_util import check_level
+        check_level(got[0, i], q_lv[0][0, i], k_lv[0][0, i], parent[i], 8, f"head {i}")
+
+
+# ----------------------------------------------------------------------------- transpose
+
+
+@pytest.mark.parametrize("nmat,rows,cols,k,seed", [(1, 16, 16, 8, 0), (3, 256, 256, 8, 1),
+                                                   (2, 4096, 4096, 8, 2), (1, 16384, 16384, 8, 3),
+                                                   (2, 1000, 333, 5, 4), (1, 300, 7, 3, 5)])
+def test_index_transpose_bit_exact(nmat, rows, cols, k, seed):
+    rng = np.random.default_rng(seed)
+    csr = np.stack([np.sort(np.stack([rng.choice(cols, k, replace=False) for _ in range(rows)]),
+                            axis=1) for _ in range(nmat)]).astype(np.int32)
+    if seed == 4:   # unsorted rows and a few out-of-range ids (dropped)
+        csr = csr[:, :, ::-1].copy()
+        csr[0, 3, 1] = cols + 5
+        csr[1, 7, 0] = -2
+    t = torch.from_numpy(csr).to(DEV)
+    off = torch.empty((nmat, cols + 1), dtype=torch.int32, device=DEV)
+    rws = torch.empty((nmat, rows * k), dtype=torch.int32, device=DEV)
+    ws = torch.empty(_abi.llsa_index_transpose_workspace(nmat, rows, cols, k), dtype=torch.uint8,
+                     device=DEV)
+    _abi.llsa_index_transpose(nmat, rows, cols, k, t, off, rws, ws)
+    off, rws = off.cpu().numpy(), rws.cpu().numpy()
+    for m in range(nmat):
+        keep = (csr[m] >= 0) & (csr[m] < cols)
+        want_off, want_rows = orc.csr_to_csc(np.where(keep, csr[m], 0), cols)
+        if not keep.all():   # oracle on the kept entries only
+            flat_rows = np.repeat(np.arange(rows), k)[keep.reshape(-1)]
+            flat_keys = csr[m].reshape(-1)[keep.reshape(-1)]
+            order = np.argsort(flat_keys, kind="stable")
+            want_rows = flat_rows[order]
+            want_off = np.concatenate([[0], np.cumsum(np.bincount(flat_keys, minlength=cols))])
+        assert np.array_equal(off[m], want_off)
+        assert np.array_equal(rws[m][:want_off[-1]], want_rows)
+
+
+# ----------------------------------------------------------------------------- attention
+
+
+def _oracle_sel(ref, h, w, levels, topk, b=0, hh=0):
+    q_lv = orc.pool_levels(orc.reorder(ref["q"][b, hh], h, w), 16, levels)
+    k_lv = orc.pool_levels(orc.reorder(ref["k"][b, hh], h, w), 16, levels)
+    return orc.select(q_lv, k_lv, 16, topk)
+
+
+@pytest.mark.parametrize("h,w,levels,topk,enrich,dtype,layout", [
+    (64, 64, 2, 8, True, torch.float32, RASTER),
+    (64, 64, 2, 8, True, torch.bfloat16, RASTER),
+    (64, 64, 2, 5, True, torch.bfloat16, MORTON),
+    (128, 256, 3, 8, True, torch.bfloat16, RASTER),
+    (128, 128, 2, 7, False, torch.bfloat16, RASTER),
+    (64, 64, 1, 16, False, torch.float32, MORTON),
+])
+def test_attn_fwd_on_oracle_indices(h, w, levels, topk, enrich, dtype, layout):
+    """Forward attention in isolation: GPU attention on the oracle's own selection."""
+    d, ref = _inputs(1, 2, h, w, dtype, 31)
+    p = _problem(d["q"], h, w, levels, topk, enrich, layout)
+    sels = [_oracle_sel(ref, h, w, levels, topk, 0, i) for i in range(2)]
+    sel_t = [torch.from_numpy(np.stack([sels[i][l] for i in range(2)])[None].astype(np.int32))
+             .to(DEV) for l in range(levels)]
+    q, k, v = d["q"], d["k"], d["v"]
+    if layout == MORTON:
+        q, k, v = (ops.reorder(p, t) for t in (q, k, v))
+    kl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    vl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    _abi.llsa_pool(p, None, k, v, None, kl, vl)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, p.n), device=DEV)
+    _abi.llsa_attn_fwd(p, q, k, v, kl, vl, sel_t, o, lse)
+    if layout == MORTON:
+        o = ops.reorder(p, o, inverse=True)
+    res = orc.llsa_forward(ref["q"], ref["k"], ref["v"], h, w, 16, levels, topk, enrich,
+                           sel_override=[sels])
+    assert_close(to64(o), res["o"], dtype, "o")
+    # lse is fp32; with bf16 inputs the pooled keys are rounded to bf16 before the MFMA,
+    # which moves a coarse score by up to 2^-9 of its size: same slack as bf16 storage.
+    assert_close(to64(lse), res["lse"], dtype, "lse")
+
+
+@pytest.mark.parametrize("h,w,levels,topk,enrich,layout", [
+    (64, 64, 2, 8, True, RASTER),
+    (64, 64, 2, 5, True, MORTON),
+    (128, 256, 3, 8, True, RASTER),
+    (128, 128, 2, 8, False, RASTER),
+    (64, 64, 1, 16, False, RASTER),
+])
+def test_attn_bwd_on_oracle_indices(h, w, levels, topk, enrich, layout):
+    """Backward in isolation: GPU gradients on the oracle's selection (and GPU forward)."""
+    d, ref = _inputs(1, 2, h, w, torch.bfloat16, 41, grad=True)
+    p = _problem(d["q"], h, w, levels, topk, enrich, layout)
+    sels = [_oracle_sel(ref, h, w, levels, topk, 0, i) for i in range(2)]
+    sel_t = [torch.from_numpy(np.stack([sels[i][l] for i in range(2)])[None].astype(np.int32))
+             .to(DEV) for l in range(levels)]
+    q, k, v, do = d["q"], d["k"], d["v"], d["do"]
+    if layout == MORTON:
+        q, k, v, do = (ops.reorder(p, t) for t in (q, k, v, do))
+    kl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    vl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    _abi.llsa_pool(p, None, k, v, None, kl, vl)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, p.n), device=DEV)
+    _abi.llsa_attn_fwd(p, q, k, v, kl, vl, sel_t, o, lse)
+    fwd = dict(o=o, lse=lse, k_lv=kl, v_lv=vl, sel=sel_t)
+    dq, dk, dv = ops.llsa_backward(p, q, k, v, fwd, do)
+    if layout == MORTON:
+        dq, dk, dv = (ops.reorder(p, t, inverse=True) for t in (dq, dk, dv))
+    want = orc.llsa_backward(ref["q"], ref["k"], ref["v"], ref["do"], h, w, 16, levels, [sels],
+                             enrich)
+    for name, got, ref_g in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        assert_close(to64(got), ref_g, torch.bfloat16, name)
+
+
+# ----------------------------------------------------------------------------- whole path
+
+
+def _end_to_end(cfg_name, heads_checked, backward):
+    cfg = gen.CONFIGS[cfg_name]
+    h, w, L = cfg["height"], cfg["width"], cfg["levels"]
+    d, ref = _inputs(cfg["batch"], cfg["heads"], h, w, cfg["dtype"], cfg["seed_base"],
+                     grad=backward)
+    p = _problem(d["q"], h, w, L)
+    fwd = ops.llsa_forward(p, d["q"], d["k"], d["v"])
+    grads = ops.llsa_backward(p, d["q"], d["k"], d["v"], fwd, d["do"]) if backward else None
+    torch.cuda.synchronize()
+    sel_np = [s.cpu().numpy().astype(np.int64) for s in fwd["sel"]]
+    for (bi, hi) in heads_checked:
+        sl = (slice(bi, bi + 1), slice(hi, hi + 1))
+        q64, k64, v64 = (ref[t][sl] for t in "qkv")
+        q_lv = orc.pool_levels(orc.reorder(q64, h, w), 16, L)
+        k_lv = orc.pool_levels(orc.reorder(k64, h, w), 16, L)
+        check_selection([s[sl] for s in sel_np], q_lv, k_lv, 8, f"{cfg_name} b{bi} h{hi}")
+        sels = [[[s[bi, hi] for s in sel_np]]]
+        res = orc.llsa_forward(q64, k64, v64, h, w, 16, L, 8, True, sel_override=sels)
+        assert_close(to64(fwd["o"][sl]), res["o"], cfg["dtype"], f"{cfg_name} o b{bi} h{hi}")
+        assert_close(to64(fwd["lse"][sl]), res["lse"], cfg["dtype"], f"{cfg_name} lse")
+        if backward:
+            want = orc.llsa_backward(q64, k64, v64, ref["do"][sl], h, w, 16, L, sels, True)
+            for name, got, ref_g in zip(("dq", "dk", "dv"), grads, want):
+                assert_close(to64(got[sl]), ref_g, cfg["dtype"], f"{cfg_name} {name} b{bi} h{hi}")
+
+
+def test_e2e_tiny64_fp32():
+    _end_to_end("tiny64", [(0, 0), (0, 1)], backward=False)
+
+
+def test_e2e_ffhq128():
+    _end_to_end("ffhq128", [(0, 0), (3, 5), (1, 2)], backward=False)
+
+
+def test_e2e_px256():
+    _end_to_end("px256", [(0, 0), (0, 5)], backward=False)
+
+
+def test_e2e_px256_train():
+    _end_to_end("px256_train", [(0, 0), (1, 4)], backward=True)
+
+
+def test_e2e_px512_train():
+    _end_to_end("px512_train", [(0, 3)], backward=True)
+
+
+def test_deterministic_and_autograd():
+    h = w = 128
+    d, _ = _inputs(1, 2, h, w, torch.bfloat16, 51, grad=True)
+    outs = []
+    for _ in range(2):
+        q, k, v = (d[t].clone().requires_grad_(True) for t in "qkv")
+        o = ops.llsa_attention(q, k, v, h, w, levels=2)
+        o.backward(d["do"])
+        outs.append([o.detach(), q.grad, k.grad, v.grad])
+    for a, b in zip(*outs):
+        assert torch.equal(_bits(a), _bits(b))
+    p = _problem(d["q"], h, w, 2)
+    fwd = ops.llsa_forward(p, d["q"], d["k"], d["v"])
+    grads = ops.llsa_backward(p, d["q"], d["k"], d["v"], fwd, d["do"])
+    assert torch.equal(_bits(fwd["o"]), _bits(outs[0][0]))
+    for g, g2 in zip(grads, outs[0][1:]):
+        assert torch.equal(_bits(g), _bits(g2))
