@@ -73,6 +73,17 @@ __device__ __forceinline__ void split8(const float (&x)[2][4], bf16x8& hi, bf16x
     }
 }
 
+__device__ __forceinline__ void split_f32x8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16 ha = (bf16)a[i], hb = (bf16)b[i];
+    hi[i] = ha;
+    hi[i + 4] = hb;
+    lo[i] = (bf16)(a[i] - (float)ha);
+    lo[i + 4] = (bf16)(b[i] - (float)hb);
+  }
+}
+
 __device__ __forceinline__ bf16x8 zero8() {
   bf16x8 z;
 #pragma unroll
@@ -104,8 +115,8 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* st, int t4, int lane) {
 // ====================================================================== stage 1: query-major
 template <int NST>   // coarse slot tiles (of 16) kept in registers: 0, 1 or 2
 __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 sK[4][32 * kStride];
-  __shared__ __attribute__((aligned(16))) bf16 sV[4][32 * kStride];
+  __shared__ __attribute__((aligned(16))) bf16 sK[4][32 * kStride];    // K rows (hi part)
+  __shared__ __attribute__((aligned(16))) bf16 sKl[4][32 * kStride];   // lo part (pooled keys)
   __shared__ __attribute__((aligned(16))) bf16 sQ[4][16 * kStride];
   __shared__ __attribute__((aligned(16))) bf16 sO[4][16 * kStride];   // dO rows
   __shared__ __attribute__((aligned(16))) bf16 sP[4][2][32 * 16];     // P^T [slot][q], hi/lo
@@ -116,15 +127,16 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   const int g = lane >> 4;
   const int n1 = a.n >> kBlockShift;
   const int n2 = n1 >> kBlockShift;
-  const int head = blockIdx.x / n2;
-  const int a2 = blockIdx.x - head * n2;
+  const int wg = xcd_block(blockIdx.x, gridDim.x);
+  const int head = wg / n2;
+  const int a2 = wg - head * n2;
   const int K = a.topk;
   const long tok_base = (long)head * a.n;
   const int n_coarse = a.enrich ? (a.levels - 1) * K : 0;
   const int n_fine_chunks = (K + 1) >> 1;
   const int n_chunks = n_fine_chunks + ((n_coarse + 31) >> 5);
   bf16* stK = sK[w];
-  bf16* stV = sV[w];
+  bf16* stKl = sKl[w];
   bf16* stQ = sQ[w];
   bf16* stO = sO[w];
   bf16* stP = sP[w][0];
@@ -174,74 +186,100 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 
     for (int ch = 0; ch < n_chunks; ++ch) {
       const bool fine = ch < n_fine_chunks;
-      int j0 = -1, j1 = -1;
+      // ---- lane kk (< 32) resolves key kk of the chunk: row, level, validity (as a mask)
+      long my_row = 0;
+      bool my_ok = false;
       if (fine) {
-        j0 = sel1[2 * ch];
-        j1 = (2 * ch + 1 < K) ? sel1[2 * ch + 1] : -1;
-      }
-      const int cbase = (ch - n_fine_chunks) * 32;
-      // key source of chunk position kk: returns level (0 fine, >= 2 coarse), row, validity
-      auto src = [&](int kk, int& level, long& row) -> bool {
-        if (fine) {
-          const int j = kk < 16 ? j0 : j1;
-          level = 0;
-          if (j < 0 || j >= n1) { row = 0; return false; }
-          row = tok_base + token_row(j * kBlock + (kk & 15), a.grid);
-          return true;
+        const int kk = lane & 31;
+        const int j = kk < 16 ? sel1[2 * ch] : ((2 * ch + 1 < K) ? sel1[2 * ch + 1] : -1);
+        my_ok = j >= 0 && j < n1;
+        my_row = my_ok ? tok_base + token_row(j * kBlock + (kk & 15), a.grid) : 0;
+      } else {
+        const int slot = (ch - n_fine_chunks) * 32 + (lane & 31);
+        if (slot < n_coarse) {
+          const int l = 2 + slot / K;
+          const int nl = a.n >> (kBlockShift * l);
+          const int anc = pb >> (kBlockShift * (l - 1));
+          const int id = a.sel[l - 1][((long)head * nl + anc) * K + (slot % K)];
+          my_ok = id >= 0 && id < nl;
+          my_row = my_ok ? (long)head * nl + id : 0;
         }
-        const int slot = cbase + kk;
-        level = 2;
-        row = 0;
-        if (slot >= n_coarse) return false;
-        const int l = 2 + slot / K;
-        level = l;
-        const int nl = a.n >> (kBlockShift * l);
-        const int anc = pb >> (kBlockShift * (l - 1));
-        const int id = a.sel[l - 1][((long)head * nl + anc) * K + (slot % K)];
-        if (id < 0 || id >= nl) return false;
-        row = (long)head * nl + id;
-        return true;
-      };
-      // ---- stage K and V rows of the chunk (32 rows x 128 B each)
+      }
+      const uint64_t valid = __ballot(my_ok) & 0xffffffffull;
+      auto row_of = [&](int kk) -> long { return __shfl(my_row, kk, 64); };
+      // level of chunk position kk (coarse chunks): arithmetic on its slot, clamped to a level
+    // that exists, so no cross-lane read is needed and a pointer index is always in range
+    auto level_of = [&](int kk) -> int {
+      const int slot = (ch - n_fine_chunks) * 32 + kk;
+      const int l = 2 + (slot > 0 ? slot : 0) / K;
+      return l < a.levels ? l : a.levels;
+    };
+      // ---- stage the chunk's K rows (32 rows x 128 B; pooled keys as hi + lo)
 #pragma unroll
       for (int ins = 0; ins < 4; ++ins) {
         const int row = ins * 8 + (lane >> 3);
         const int piece = (lane & 7) * 8;
-        int level;
-        long r;
-        const bool ok = src(row, level, r);
-        bf16x8 kv = zero8(), vv = zero8();
-        if (ok) {
-          if (level == 0) {
-            kv = *(const bf16x8*)(a.k + r * kDim + piece);
-            vv = *(const bf16x8*)(a.v + r * kDim + piece);
-          } else {
-            const float* kp = a.k_lv[level - 1] + r * kDim + piece;
-            const float* vp = a.v_lv[level - 1] + r * kDim + piece;
-            kv = cvt8_bf16(*(const f32x4*)kp, *(const f32x4*)(kp + 4));
-            vv = cvt8_bf16(*(const f32x4*)vp, *(const f32x4*)(vp + 4));
+        const long r = row_of(row);   // cross-lane read: uniform control flow only
+        const int lvl = level_of(row);
+        const bool ok = (valid >> row) & 1;
+        if (fine) {
+          const bf16x8 kv = ok ? *(const bf16x8*)(a.k + r * kDim + piece) : zero8();
+          *(bf16x8*)(stK + row * kStride + piece) = kv;
+        } else {
+          f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = {0.f, 0.f, 0.f, 0.f};
+          if (ok) {
+            const float* kp = a.k_lv[lvl - 1] + r * kDim + piece;
+            k0 = *(const f32x4*)kp;
+            k1 = *(const f32x4*)(kp + 4);
           }
+          bf16x8 hi, lo;
+          split_f32x8(k0, k1, hi, lo);
+          *(bf16x8*)(stK + row * kStride + piece) = hi;
+          *(bf16x8*)(stKl + row * kStride + piece) = lo;
         }
-        *(bf16x8*)(stK + row * kStride + piece) = kv;
-        *(bf16x8*)(stV + row * kStride + piece) = vv;
       }
       wave_lds_sync();
-      // ---- S^T and dP^T tiles
+      // ---- S^T and dP^T tiles (V rows are read straight from memory as A operands)
       float p[2][4], w1[2][4];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int arow = chunk_key(n, t);
+        const bool aok = (valid >> arow) & 1;
+        const long vr = row_of(arow);   // cross-lane read: uniform control flow only
+        const int alvl = level_of(arow);
         f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
         st = mfma_bf16_k32(lds_row8(stK, arow, 0, g), qh[0], st);
         st = mfma_bf16_k32(lds_row8(stK, arow, 1, g), qh[1], st);
-        dp = mfma_bf16_k32(lds_row8(stV, arow, 0, g), dh[0], dp);
-        dp = mfma_bf16_k32(lds_row8(stV, arow, 1, g), dh[1], dp);
+        if (fine) {
+          bf16x8 v0 = zero8(), v1 = zero8();
+          if (aok) {
+            v0 = *(const bf16x8*)(a.v + vr * kDim + 8 * g);
+            v1 = *(const bf16x8*)(a.v + vr * kDim + 32 + 8 * g);
+          }
+          dp = mfma_bf16_k32(v0, dh[0], dp);
+          dp = mfma_bf16_k32(v1, dh[1], dp);
+        } else {
+          st = mfma_bf16_k32(lds_row8(stKl, arow, 0, g), qh[0], st);
+          st = mfma_bf16_k32(lds_row8(stKl, arow, 1, g), qh[1], st);
+#pragma unroll
+          for (int sidx = 0; sidx < 2; ++sidx) {
+            f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
+            if (aok) {
+              const float* vp = a.v_lv[alvl - 1] + vr * kDim + 32 * sidx + 8 * g;
+              x0 = *(const f32x4*)vp;
+              x1 = *(const f32x4*)(vp + 4);
+            }
+            bf16x8 hi, lo;
+            split_f32x8(x0, x1, hi, lo);
+            dp = mfma_bf16_k32(hi, dh[sidx], dp);
+            dp = mfma_bf16_k32(lo, dh[sidx], dp);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          int level;
-          long r;
-          const bool ok = src(8 * g + i + 4 * t, level, r);
-          const float bias = level ? 4.0f * level : 0.f;
+          const int kk = 8 * g + i + 4 * t;
+          const bool ok = (valid >> kk) & 1;
+          const float bias = fine ? 0.f : 4.0f * (float)level_of(kk);
           const float pv = ok ? exp2f(st[i] * a.c2 + bias - lse2) : 0.f;
           p[t][i] = pv;
           w1[t][i] = pv * dp[i];
@@ -261,6 +299,11 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
         acc_a[t4] = mfma_bf16_k32(kt, a_lo, acc_a[t4]);
         acc_b[t4] = mfma_bf16_k32(kt, b_hi, acc_b[t4]);
         acc_b[t4] = mfma_bf16_k32(kt, b_lo, acc_b[t4]);
+        if (!fine) {
+          const bf16x8 ktl = lds_tr8(stKl, t4, lane);
+          acc_a[t4] = mfma_bf16_k32(ktl, a_hi, acc_a[t4]);
+          acc_b[t4] = mfma_bf16_k32(ktl, b_hi, acc_b[t4]);
+        }
       }
       wave_lds_sync();
     }
@@ -425,7 +468,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   const int n = lane & 15;
   const int g = lane >> 4;
   const int n1 = a.n >> kBlockShift;
-  const long kb = (long)blockIdx.x * 4 + w;
+  const long kb = (long)xcd_block(blockIdx.x, gridDim.x) * 4 + w;
   if (kb >= (long)a.bh * n1) return;
   const int head = (int)(kb / n1);
   const int j = (int)(kb - (long)head * n1);

@@ -107,6 +107,16 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ------------------------------------------------------------------ XCD-aware numbering
+// The dispatcher sends workgroup i to XCD i % 8.  Renumbering gives XCD x the contiguous range
+// [x*q + min(x, r), ...) of logical workgroups (q = n / 8, r = n % 8), so spatially adjacent
+// work shares one L2.
+__device__ __forceinline__ int xcd_block(int bid, int nblocks) {
+  const int x = bid & 7, k = bid >> 3;
+  const int q = nblocks >> 3, r = nblocks & 7;
+  return x * q + (x < r ? x : r) + k;
+}
+
 // ------------------------------------------------------------------ cross-lane
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }
