@@ -30,8 +30,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="px256_train")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--unfused", action="store_true",
-                    help="also time the path with explicit reorder passes")
+    ap.add_argument("--with-copy", action="store_true",
+                    help="also launch one Morton reorder (a plain copy of one token tensor) per "
+                         "step, outside the timed region: the calibration kernel for HBM "
+                         "byte counters")
     return ap.parse_args()
 
 
@@ -141,7 +143,7 @@ def main():
         sys.exit(2)
     import torch
 
-    from hierarchical_top_sparse_amd import gen, ops
+    from hierarchical_top_sparse_amd import _abi, gen, ops
 
     cfg = gen.CONFIGS[args.config]
     h, w, L = cfg["height"], cfg["width"], cfg["levels"]
@@ -161,6 +163,11 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.with_copy:
+        copy_dst = torch.empty_like(q)
+        for _ in range(max(1, args.steps)):
+            _abi.llsa_reorder(p, q, copy_dst, False)
+        torch.cuda.synchronize()
     # timed region: events around every ABI call, on the stream the kernels run on
     ev = {name: [] for name, _ in calls}
     t_start = torch.cuda.Event(enable_timing=True)

@@ -20,6 +20,9 @@ SOURCES = ["api.cpp", "reorder.hip", "pool.hip", "select.hip", "attn_fwd.hip",
 ARCH = "gfx950"
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in ordinary VGPRs: no AGPR<->VGPR copies around the softmax
+         # rescaling of the output accumulator
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wall", "-Wno-unused-result", "-Wno-unused-variable", "-Wno-unused-function"]
 
 

@@ -48,9 +48,9 @@ int32_t check_problem(const llsa_problem* p) {
     return fail(LLSA_ERR_DTYPE, "unknown layout code %d", p->layout);
   if (p->batch < 1 || p->heads < 1)
     return fail(LLSA_ERR_SHAPE, "batch (%d) and heads (%d) must be >= 1", p->batch, p->heads);
-  if (!is_pow2(p->height) || !is_pow2(p->width))
-    return fail(LLSA_ERR_SHAPE, "height (%d) and width (%d) must be powers of two", p->height,
-                p->width);
+  if (!is_pow2(p->height) || !is_pow2(p->width) || p->height < 4 || p->width < 4)
+    return fail(LLSA_ERR_SHAPE, "height (%d) and width (%d) must be powers of two >= 4",
+                p->height, p->width);
   if (p->head_dim != 64)
     return fail(LLSA_ERR_UNSUPPORTED, "head_dim %d: only 64 is implemented", p->head_dim);
   if (p->block != 16)
@@ -62,7 +62,7 @@ int32_t check_problem(const llsa_problem* p) {
     return fail(LLSA_ERR_SHAPE, "levels %d out of [1, %d]", p->levels, LLSA_MAX_LEVELS);
   const long n = (long)p->height * p->width;
   if (n < 256) return fail(LLSA_ERR_SHAPE, "N = %ld tokens: at least 256 needed", n);
-  if (n > (1L << 30)) return fail(LLSA_ERR_SHAPE, "N = %ld tokens is too large", n);
+  if (n > (1L << 23)) return fail(LLSA_ERR_SHAPE, "N = %ld tokens: at most 2^23 supported", n);
   const long span = 1L << (4 * p->levels);
   if (n % span != 0)
     return fail(LLSA_ERR_SHAPE, "N = %ld is not divisible by block^levels = %ld", n, span);

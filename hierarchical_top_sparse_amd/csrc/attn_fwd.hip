@@ -1,17 +1,21 @@
 // Sparse attention forward with hierarchical KV enrichment (paper summary sec. 四; article
 // sec. 三/四: the forward gathers the selected key blocks directly, no dense mask).
 //
-// One wave owns one level-1 query block p (16 queries).  Its keys are processed in chunks of
-// 32: first the 16 tokens of each pair of fine blocks in Sel_1[p], then the coarse keys
-// Sel_l[p / 16^(l-1)] of levels l = 2..L (weight 16^l, i.e. a log2-domain bias of 4l).
+// One wave owns one level-1 query block p (16 queries); a workgroup holds the 4 consecutive
+// blocks of one 8x8-pixel tile, which share their ancestors at every level >= 2.
+//  * Fine keys: the 16 tokens of each pair of blocks in Sel_1[p] form a 32-key chunk.  Block
+//    ids are wave-uniform (scalar registers); every lane's row offset inside a 4x4 tile is a
+//    constant, so a chunk's 16-byte loads need one add each.  The next chunk's loads are issued
+//    before the current chunk is computed (register double buffering).
+//  * Coarse keys: the keys Sel_l[p / 16^(l-1)], l = 2..L, are staged once per workgroup in LDS
+//    (fp32 pooled values split into bf16 hi + lo parts, so the MFMA sees them at ~16 bits),
+//    together with each slot's log2-domain weight bias 4l (weight 16^l).
 //
 // Orientation S^T = K Q^T: the MFMA result gives lane (n, g) the scores of query n against
 // keys 8g..8g+7 of the chunk (two 16x16 tiles whose rows are interleaved so that this holds),
 // so the online-softmax max needs two cross-lane steps and the exponentials already sit in
-// the B-operand layout of O^T += V^T P^T.  V^T comes from the chunk's V rows staged row-major
-// in LDS and read with ds_read_b64_tr_b16.  fp32 online softmax in the exp2 domain.
-// Pooled (fp32) keys/values and the probabilities enter the bf16 MFMA as hi + lo pairs, so
-// the only bf16 rounding is that of the inputs themselves.
+// the B-operand layout of O^T += V^T P^T.  V^T comes from V rows staged row-major in LDS and
+// read with ds_read_b64_tr_b16.  fp32 online softmax in the exp2 domain.
 // fp32 tensors use v_mfma_f32_16x16x4f32 with the same data flow.
 // Workgroups are renumbered so that each XCD (and its L2) works on one contiguous spatial
 // range of query blocks: neighbouring blocks select overlapping key blocks.
@@ -22,8 +26,9 @@ namespace llsa {
 
 constexpr int kMaxLevels = 6;
 constexpr int kFwdWaves = 4;
-constexpr int kStageStrideBf16 = kDim + 8;   // 144-byte rows: 16-byte aligned, staggered banks
-constexpr int kStageStrideF32 = kDim + 4;
+constexpr int kStrideBf16 = kDim + 8;   // 144-byte LDS rows: 16-byte aligned, staggered banks
+constexpr int kStrideF32 = kDim + 4;
+constexpr float kMinusBig = -1e30f;     // running-max floor: keeps exp2 arguments finite
 
 struct FwdArgs {
   const void* q;
@@ -58,197 +63,173 @@ __device__ __forceinline__ void split_bf16(f32x4 a, f32x4 b, bf16x8& hi, bf16x8&
 }
 
 template <bool BF16>
+struct FwdCfg {
+  static constexpr int ES = BF16 ? 2 : 4;              // element bytes
+  static constexpr int kStride = BF16 ? kStrideBf16 : kStrideF32;
+  static constexpr int PPR = kDim * ES / 16;           // 16-byte pieces per row
+  static constexpr int RPI = 64 / PPR;                 // rows staged per load instruction
+  static constexpr int NINS = 32 / RPI;                // load instructions per 32-row chunk
+  static constexpr int KLD = BF16 ? 2 : 4;             // 16-byte loads per A-operand row
+  static constexpr int NB = BF16 ? 4 : 2;              // coarse buffers: K(hi,lo), V(hi,lo)
+  static constexpr int kChunkElems = 32 * kStride;
+};
+
+static size_t fwd_lds_bytes(bool bf16, int n_coarse) {
+  const int es = bf16 ? 2 : 4;
+  const int stride = bf16 ? kStrideBf16 : kStrideF32;
+  const int nb = bf16 ? 4 : 2;
+  const int cchunks = (n_coarse + 31) / 32;
+  return (size_t)es * 32 * stride * (kFwdWaves + cchunks * nb) + sizeof(float) * 32 * cchunks;
+}
+
+template <bool BF16>
 __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(FwdArgs a) {
-  constexpr int kStride = BF16 ? kStageStrideBf16 : kStageStrideF32;
+  using C = FwdCfg<BF16>;
   typedef typename std::conditional<BF16, bf16, float>::type T;
-  // [wave][hi/lo][32 rows]; the lo half is used by bf16 coarse chunks only
-  __shared__ __attribute__((aligned(16))) T stage_all[kFwdWaves][BF16 ? 2 : 1][32 * kStride];
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  T* stage = stage_all[w][0];
-  T* stage_lo = stage_all[w][BF16 ? 1 : 0];
+  const int w = uniform(threadIdx.x >> 6);
   const int n1 = a.n >> kBlockShift;
-  const long qb = (long)xcd_block(blockIdx.x, gridDim.x) * kFwdWaves + w;
-  if (qb >= (long)a.bh * n1) return;
-  const int head = (int)(qb / n1);
-  const int pb = (int)(qb - (long)head * n1);
+  const int qb = uniform(xcd_block(blockIdx.x, gridDim.x) * kFwdWaves) + w;
+  const int head = uniform(qb / n1);   // scalar: buffer descriptors must be wave-uniform
+  const int pb = uniform(qb - head * n1);
   const int n = lane & 15;
   const int g = lane >> 4;
   const int K = a.topk;
   const long tok_base = (long)head * a.n;
+  const int n_coarse = a.enrich ? (a.levels - 1) * K : 0;
+  const int n_cchunks = (n_coarse + 31) >> 5;
+  T* stage = (T*)smem + w * C::kChunkElems;
+  T* cstage = (T*)smem + kFwdWaves * C::kChunkElems;
+  float* cbias = (float*)(cstage + n_cchunks * C::NB * C::kChunkElems);
+
+  // ---- the workgroup's coarse keys and values, shared by its four query blocks
+  if (n_coarse > 0) {
+    const int pb0 = pb & ~(kFwdWaves - 1);
+    for (int e = threadIdx.x; e < n_cchunks * 32 * 8; e += 64 * kFwdWaves) {
+      const int slot = e >> 3;
+      const int c8 = (e & 7) * 8;
+      f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
+      float bias = -INFINITY;
+      if (slot < n_coarse) {
+        const int l = 2 + slot / K;
+        const int nl = a.n >> (kBlockShift * l);
+        const int anc = pb0 >> (kBlockShift * (l - 1));
+        const int id = a.sel[l - 1][((long)head * nl + anc) * K + (slot - (l - 2) * K)];
+        if (id >= 0 && id < nl) {
+          const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
+          const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
+          k0 = *(const f32x4*)kp;
+          k1 = *(const f32x4*)(kp + 4);
+          v0 = *(const f32x4*)vp;
+          v1 = *(const f32x4*)(vp + 4);
+          bias = 4.0f * (float)l;   // log2(16^l)
+        }
+      }
+      T* base = cstage + (slot >> 5) * C::NB * C::kChunkElems + (slot & 31) * C::kStride + c8;
+      if constexpr (BF16) {
+        bf16x8 hi, lo;
+        split_bf16(k0, k1, hi, lo);
+        *(bf16x8*)base = hi;
+        *(bf16x8*)(base + C::kChunkElems) = lo;
+        split_bf16(v0, v1, hi, lo);
+        *(bf16x8*)(base + 2 * C::kChunkElems) = hi;
+        *(bf16x8*)(base + 3 * C::kChunkElems) = lo;
+      } else {
+        *(f32x4*)base = k0;
+        *(f32x4*)(base + 4) = k1;
+        *(f32x4*)(base + C::kChunkElems) = v0;
+        *(f32x4*)(base + C::kChunkElems + 4) = v1;
+      }
+      if (c8 == 0) cbias[slot] = bias;
+    }
+    __syncthreads();
+  }
+
+  const uint32_t head_bytes = (uint32_t)a.n * kDim * C::ES;
+  const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rk = make_rsrc_uniform((const char*)a.k + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
 
   // ---- queries: B operand of S^T
-  const int qrow = token_row(pb * kBlock + n, a.grid);
+  const int qrow = block_corner(pb, a.grid) + tile_offset(n, a.grid);
   bf16x8 qh[2];
   f32x4 qf[4];
   if constexpr (BF16) {
-    const bf16* qp = (const bf16*)a.q + (tok_base + qrow) * kDim;
-    qh[0] = *(const bf16x8*)(qp + 8 * g);
-    qh[1] = *(const bf16x8*)(qp + 32 + 8 * g);
+    qh[0] = buf_load8(rq, (uint32_t)(qrow * kDim + 8 * g) * 2);
+    qh[1] = buf_load8(rq, (uint32_t)(qrow * kDim + 32 + 8 * g) * 2);
   } else {
-    const float* qp = (const float*)a.q + (tok_base + qrow) * kDim + 16 * g;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qf[c] = *(const f32x4*)(qp + 4 * c);
+    for (int c = 0; c < 4; ++c) qf[c] = buf_load4f(rq, (uint32_t)(qrow * kDim + 16 * g + 4 * c) * 4);
   }
 
-  const int32_t* sel1 = a.sel[0] + ((long)head * n1 + pb) * K;
-  const int n_fine_chunks = (K + 1) >> 1;
-  const int n_coarse = a.enrich ? (a.levels - 1) * K : 0;
-  const int n_chunks = n_fine_chunks + ((n_coarse + 31) >> 5);
+  // ---- lane-constant byte offsets inside a block: staged rows and A-operand rows
+  const int srow0 = lane / C::PPR;
+  const int piece = lane % C::PPR;
+  uint32_t st_off[C::NINS];
+#pragma unroll
+  for (int ins = 0; ins < C::NINS; ++ins)
+    st_off[ins] = (uint32_t)(tile_offset((ins * C::RPI + srow0) & 15, a.grid) * kDim * C::ES +
+                             16 * piece);
+  uint32_t ka_off[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    ka_off[t] = (uint32_t)(tile_offset(tile_row_key(n, t) & 15, a.grid) * kDim * C::ES) +
+                (BF16 ? 16 * g : 64 * g);
+  const bool ka_second = n >= 8;    // A rows 8..15 of both tiles come from the second block
+  const bool lane_second = g >= 2;  // this lane's 8 keys come from the second block
 
-  float m_run = -INFINITY;   // running max (log2 domain) of query n
+  const int32_t* sel1 = a.sel[0] + ((long)head * n1 + pb) * K;
+  const int n_fine = (K + 1) >> 1;
+
+  // loads of one fine chunk (issued ahead of use)
+  struct FineLd {
+    i32x4 v[C::NINS];
+    i32x4 k[2][C::KLD];
+    int ok0, ok1;
+  };
+  auto load_fine = [&](int ch) -> FineLd {
+    FineLd f;
+    const int j0 = uniform(sel1[2 * ch]);
+    const int j1 = uniform((2 * ch + 1 < K) ? sel1[2 * ch + 1] : -1);
+    f.ok0 = j0 >= 0 && j0 < n1;
+    f.ok1 = j1 >= 0 && j1 < n1;
+    const uint32_t b0 = f.ok0 ? (uint32_t)block_corner(j0, a.grid) * kDim * C::ES : kNoRow;
+    const uint32_t b1 = f.ok1 ? (uint32_t)block_corner(j1, a.grid) * kDim * C::ES : kNoRow;
+#pragma unroll
+    for (int ins = 0; ins < C::NINS; ++ins)
+      f.v[ins] = __builtin_amdgcn_raw_buffer_load_b128(rv, (ins * C::RPI >= 16 ? b1 : b0) +
+                                                           st_off[ins], 0, 0);
+    const uint32_t kb = ka_second ? b1 : b0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int c = 0; c < C::KLD; ++c)
+        f.k[t][c] = __builtin_amdgcn_raw_buffer_load_b128(
+            rk, kb + ka_off[t] + (BF16 ? 64 * c : 16 * c), 0, 0);
+    return f;
+  };
+
+  float m_run = kMinusBig;   // running max (log2 domain) of query n
   float l_run = 0.f;         // this lane's partial sum of exp2
   f32x4 acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int ch = 0; ch < n_chunks; ++ch) {
-    const bool fine = ch < n_fine_chunks;
-    // ---- per chunk: lane kk (< 32) resolves key kk: its row and level; validity as a mask
-    int j0 = -1, j1 = -1;
-    long my_row = 0;
-    bool my_ok = false;
-    if (fine) {
-      j0 = sel1[2 * ch];
-      j1 = (2 * ch + 1 < K) ? sel1[2 * ch + 1] : -1;
-      const int kk = lane & 31;
-      const int j = kk < 16 ? j0 : j1;
-      my_ok = j >= 0 && j < n1;
-      my_row = my_ok ? tok_base + token_row(j * kBlock + (kk & 15), a.grid) : 0;
-    } else {
-      const int slot = (ch - n_fine_chunks) * 32 + (lane & 31);
-      if (slot < n_coarse) {
-        const int l = 2 + slot / K;
-        const int nl = a.n >> (kBlockShift * l);
-        const int anc = pb >> (kBlockShift * (l - 1));
-        const int id = a.sel[l - 1][((long)head * nl + anc) * K + (slot % K)];
-        my_ok = id >= 0 && id < nl;
-        my_row = my_ok ? (long)head * nl + id : 0;
-      }
-    }
-    const uint64_t valid = __ballot(my_ok) & 0xffffffffull;
-    auto row_of = [&](int kk) -> long { return __shfl(my_row, kk, 64); };
-    // level of chunk position kk (coarse chunks): arithmetic on its slot, clamped to a level
-    // that exists, so no cross-lane read is needed and a pointer index is always in range
-    auto level_of = [&](int kk) -> int {
-      const int slot = (ch - n_fine_chunks) * 32 + kk;
-      const int l = 2 + (slot > 0 ? slot : 0) / K;
-      return l < a.levels ? l : a.levels;
-    };
-
-    // ---- stage this chunk's V rows (row-major, 32 x 64) into LDS
-#pragma unroll
-    for (int ins = 0; ins < (BF16 ? 4 : 8); ++ins) {
-      const int per_row = BF16 ? 8 : 16;                   // 16-byte pieces per row
-      const int row = ins * (64 / per_row) + lane / per_row;
-      const int piece = lane % per_row;
-      const long r = row_of(row);
-      const int lvl = level_of(row);
-      const bool ok = (valid >> row) & 1;
-      if constexpr (BF16) {
-        if (fine) {
-          bf16x8 val;
-          if (ok) {
-            val = *(const bf16x8*)((const bf16*)a.v + r * kDim + 8 * piece);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) val[e] = (bf16)0.f;
-          }
-          *(bf16x8*)(stage + row * kStride + 8 * piece) = val;
-        } else {
-          f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
-          if (ok) {
-            const float* vp = a.v_lv[lvl - 1] + r * kDim + 8 * piece;
-            v0 = *(const f32x4*)vp;
-            v1 = *(const f32x4*)(vp + 4);
-          }
-          bf16x8 hi, lo;
-          split_bf16(v0, v1, hi, lo);
-          *(bf16x8*)(stage + row * kStride + 8 * piece) = hi;
-          *(bf16x8*)(stage_lo + row * kStride + 8 * piece) = lo;
-        }
-      } else {
-        f32x4 val = {0.f, 0.f, 0.f, 0.f};
-        if (ok) {
-          const float* vp = (fine ? (const float*)a.v : a.v_lv[lvl - 1]) + r * kDim + 4 * piece;
-          val = *(const f32x4*)vp;
-        }
-        *(f32x4*)(stage + row * kStride + 4 * piece) = val;
-      }
-    }
-
-    // ---- S^T tiles and scores
-    float sc[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int akk = tile_row_key(n, t);   // A-operand row owned by this lane
-      const long r = row_of(akk);
-      const int lvl = level_of(akk);
-      const bool ok = (valid >> akk) & 1;
-      f32x4 st = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (BF16) {
-        if (fine) {
-          bf16x8 ka0, ka1;
-          if (ok) {
-            const bf16* kp = (const bf16*)a.k + r * kDim;
-            ka0 = *(const bf16x8*)(kp + 8 * g);
-            ka1 = *(const bf16x8*)(kp + 32 + 8 * g);
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ka0[e] = ka1[e] = (bf16)0.f;
-          }
-          st = mfma_bf16_k32(ka0, qh[0], st);
-          st = mfma_bf16_k32(ka1, qh[1], st);
-        } else {
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = {0.f, 0.f, 0.f, 0.f};
-            if (ok) {
-              const float* kp = a.k_lv[lvl - 1] + r * kDim + 32 * s + 8 * g;
-              k0 = *(const f32x4*)kp;
-              k1 = *(const f32x4*)(kp + 4);
-            }
-            bf16x8 hi, lo;
-            split_bf16(k0, k1, hi, lo);
-            st = mfma_bf16_k32(hi, qh[s], st);
-            st = mfma_bf16_k32(lo, qh[s], st);
-          }
-        }
-      } else {
-        f32x4 kf[4];
-        const float* kp = ok ? (fine ? (const float*)a.k : a.k_lv[lvl - 1]) + r * kDim + 16 * g
-                             : nullptr;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) kf[c] = kp ? *(const f32x4*)(kp + 4 * c) : f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) st = mfma_f32_k4(kf[c][e], qf[c][e], st);
-      }
-      // this lane's results: keys kk = 8g + i + 4t
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int kk = 8 * g + i + 4 * t;
-        const float bias = fine ? 0.f : 4.0f * (float)level_of(kk);   // log2(16^l)
-        sc[t][i] = ((valid >> kk) & 1) ? st[i] * a.c2 + bias : -INFINITY;
-      }
-    }
-
-    // ---- online softmax (log2 domain)
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sc[t][i]);
+  // online softmax over one chunk's scores, then O^T += V^T P^T from the row-major V rows at
+  // vbuf (and the lo parts at vlo, if any)
+  auto absorb = [&](float (&sc)[2][4], const T* vbuf, const T* vlo) {
+    float mloc = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
     const float m_new = fmaxf(m_run, group4_max(mloc));
-    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    const float alpha = fast_exp2(m_run - m_new);
     float p[2][4];
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[t][i] = (sc[t][i] == -INFINITY) ? 0.f : exp2f(sc[t][i] - m_new);
+        p[t][i] = fast_exp2(sc[t][i] - m_new);
         psum += p[t][i];
       }
     l_run = l_run * alpha + psum;
@@ -257,38 +238,37 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(FwdArgs a) {
     for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[t4][i] *= alpha;
-
     wave_lds_sync();
-    // ---- O^T += V^T P^T
     if constexpr (BF16) {
-      bf16x8 p_hi, p_lo;
-      split_bf16(f32x4{p[0][0], p[0][1], p[0][2], p[0][3]},
-                 f32x4{p[1][0], p[1][1], p[1][2], p[1][3]}, p_hi, p_lo);
+      bf16x8 pb8;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pb8[i] = (bf16)p[0][i];
+        pb8[i + 4] = (bf16)p[1][i];
+      }
       const int r = (lane & 15) >> 2;
       const int c = lane & 3;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        const int off = (8 * g + r) * kStride + 16 * t4 + 4 * c;
-        const bf16x4 lo4 = lds_read_tr16(stage + off);
-        const bf16x4 hi4 = lds_read_tr16(stage + off + 4 * kStride);
+        const int off = (8 * g + r) * C::kStride + 16 * t4 + 4 * c;
+        const bf16x4 x0 = lds_read_tr16(vbuf + off);
+        const bf16x4 x1 = lds_read_tr16(vbuf + off + 4 * C::kStride);
         bf16x8 vt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          vt[e] = lo4[e];
-          vt[e + 4] = hi4[e];
+          vt[e] = x0[e];
+          vt[e + 4] = x1[e];
         }
-        acc[t4] = mfma_bf16_k32(vt, p_hi, acc[t4]);
-        acc[t4] = mfma_bf16_k32(vt, p_lo, acc[t4]);
-        if (!fine) {
-          const bf16x4 a4 = lds_read_tr16(stage_lo + off);
-          const bf16x4 b4 = lds_read_tr16(stage_lo + off + 4 * kStride);
-          bf16x8 vl;
+        acc[t4] = mfma_bf16_k32(vt, pb8, acc[t4]);
+        if (vlo) {
+          const bf16x4 y0 = lds_read_tr16(vlo + off);
+          const bf16x4 y1 = lds_read_tr16(vlo + off + 4 * C::kStride);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            vl[e] = a4[e];
-            vl[e + 4] = b4[e];
+            vt[e] = y0[e];
+            vt[e + 4] = y1[e];
           }
-          acc[t4] = mfma_bf16_k32(vl, p_hi, acc[t4]);
+          acc[t4] = mfma_bf16_k32(vt, pb8, acc[t4]);
         }
       }
     } else {
@@ -298,16 +278,83 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(FwdArgs a) {
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float vv = stage[(8 * g + i + 4 * t) * kStride + 16 * t4 + n];
+            const float vv = vbuf[(8 * g + i + 4 * t) * C::kStride + 16 * t4 + n];
             acc[t4] = mfma_f32_k4(vv, p[t][i], acc[t4]);
           }
     }
     wave_lds_sync();
+  };
+
+  // one fine chunk from its loads: V rows to LDS, S^T on the MFMA, softmax and PV
+  auto fine_chunk = [&](const FineLd& f) {
+#pragma unroll
+    for (int ins = 0; ins < C::NINS; ++ins)
+      *(i32x4*)(stage + (ins * C::RPI + srow0) * C::kStride + piece * (16 / C::ES)) = f.v[ins];
+    float sc[2][4];
+    const float madd = (lane_second ? f.ok1 : f.ok0) ? 0.f : -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      f32x4 st = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF16) {
+        st = mfma_bf16_k32(*(const bf16x8*)&f.k[t][0], qh[0], st);
+        st = mfma_bf16_k32(*(const bf16x8*)&f.k[t][1], qh[1], st);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 kf = *(const f32x4*)&f.k[t][c];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st = mfma_f32_k4(kf[e], qf[c][e], st);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[t][i] = fmaf(st[i], a.c2, madd);
+    }
+    absorb(sc, stage, nullptr);
+  };
+
+  // ---- fine chunks: two load buffers used in turn, each refilled while the other computes
+  FineLd fa = load_fine(0), fb;
+  for (int ch = 0; ch < n_fine; ch += 2) {
+    if (ch + 1 < n_fine) fb = load_fine(ch + 1);
+    fine_chunk(fa);
+    if (ch + 1 >= n_fine) break;
+    if (ch + 2 < n_fine) fa = load_fine(ch + 2);
+    fine_chunk(fb);
+  }
+
+  // ---- coarse chunks from the workgroup's LDS copy
+  for (int cc = 0; cc < n_cchunks; ++cc) {
+    const T* kb = cstage + cc * C::NB * C::kChunkElems;
+    float sc[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = tile_row_key(n, t);
+      f32x4 st = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF16) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16* rp = kb + row * C::kStride + 32 * s + 8 * g;
+          st = mfma_bf16_k32(*(const bf16x8*)rp, qh[s], st);
+          st = mfma_bf16_k32(*(const bf16x8*)(rp + C::kChunkElems), qh[s], st);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const f32x4 kf = *(const f32x4*)(kb + row * C::kStride + 16 * g + 4 * c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st = mfma_f32_k4(kf[e], qf[c][e], st);
+        }
+      }
+      const f32x4 b4 = *(const f32x4*)(cbias + cc * 32 + 8 * g + 4 * t);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[t][i] = fmaf(st[i], a.c2, b4[i]);
+    }
+    absorb(sc, kb + (BF16 ? 2 : 1) * C::kChunkElems, BF16 ? kb + 3 * C::kChunkElems : nullptr);
   }
 
   // ---- finalize
   const float l_tot = group4_sum(l_run);
-  const float inv = 1.0f / l_tot;
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;   // 0 only if every key was skipped
   if constexpr (BF16) {
     bf16* op = (bf16*)a.o + (tok_base + qrow) * kDim;
 #pragma unroll
@@ -351,12 +398,21 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const v
   a.topk = s.topk;
   a.enrich = s.enrich;
   a.c2 = s.scale * kLog2e;
+  const int n_coarse = s.enrich ? (s.levels - 1) * s.topk : 0;
+  const size_t lds = fwd_lds_bytes(s.bf16, n_coarse);
+  // every workgroup holds 4 whole query blocks of one head (N / 16 is a multiple of 4)
   const long waves = (long)s.bh * (s.n >> kBlockShift);
-  const unsigned blocks = (unsigned)((waves + kFwdWaves - 1) / kFwdWaves);
+  const unsigned blocks = (unsigned)(waves / kFwdWaves);
+  const void* fn = s.bf16 ? (const void*)attn_fwd_kernel<true> : (const void*)attn_fwd_kernel<false>;
+  if (lds > 65536) {
+    const hipError_t e =
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   if (s.bf16)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(blocks), dim3(64 * kFwdWaves), 0, stream, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(blocks), dim3(64 * kFwdWaves), lds, stream, a);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(blocks), dim3(64 * kFwdWaves), 0, stream, a);
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(blocks), dim3(64 * kFwdWaves), lds, stream, a);
   return hipGetLastError();
 }
 

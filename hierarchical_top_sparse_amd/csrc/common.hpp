@@ -56,6 +56,53 @@ __device__ __forceinline__ int token_row(int m, const Grid& g) {
   return g.raster ? morton_to_raster(m, g.hbits, g.wbits) : m;
 }
 
+// Row of the first token of level-1 block j (its 4x4 tile's top-left pixel in raster layout).
+__device__ __forceinline__ int block_corner(int j, const Grid& g) {
+  return g.raster ? morton_to_raster(j << 4, g.hbits, g.wbits) : (j << 4);
+}
+
+// Row offset of token t (0..15) of a level-1 block from the block's first row: in raster
+// layout the tile's pixel (x, y) = (bits 0,2 ; bits 1,3) of t; both sides are >= 4 pixels.
+__device__ __forceinline__ int tile_offset(int t, const Grid& g) {
+  if (!g.raster) return t;
+  const int tx = (t & 1) | ((t >> 1) & 2);
+  const int ty = ((t >> 1) & 1) | ((t >> 2) & 2);
+  return (ty << g.wbits) + tx;
+}
+
+// ------------------------------------------------------------------ buffer loads
+// Raw buffer resources over one head's tensor: 32-bit byte offsets, and any access past
+// `bytes` returns zeros (used for masked rows: offset kNoRow).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kNoRow = 0x80000000u;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ bf16x8 buf_load8(rsrc_t r, uint32_t off) {
+  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return *(const bf16x8*)&v;
+}
+__device__ __forceinline__ f32x4 buf_load4f(rsrc_t r, uint32_t off) {
+  const i32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return *(const f32x4*)&v;
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// A wave-uniform pointer moved to scalar registers (buffer descriptors must be scalar; a
+// descriptor the compiler cannot prove uniform costs a readfirstlane loop per load).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ rsrc_t make_rsrc_uniform(const void* base, uint32_t bytes) {
+  return make_rsrc(uniform_ptr(base), (uint32_t)__builtin_amdgcn_readfirstlane(bytes));
+}
+
+// 2^x on the hardware exp unit (v_exp_f32), no denormal fix-up: arguments here are <= 0 and
+// results below 2^-126 only ever multiply probabilities that are negligible anyway.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ------------------------------------------------------------------ conversions
 __device__ __forceinline__ bf16x8 cvt8_bf16(const float* f) {
   bf16x8 r;

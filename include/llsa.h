@@ -27,9 +27,10 @@
  *    leave outputs untouched; LLSA_ERR_HIP means a launch failed (outputs undefined).
  *    llsa_last_error() gives a message for the last failure on the calling thread.
  *  - Results are deterministic: no atomics, fixed reduction orders.
- *  - Supported: head_dim 64, block 16 (4x4 pixel tiles), height and width powers of two,
- *    N % block^levels == 0, 1 <= topk <= min(16, N / block^levels), 1 <= levels <= 6,
- *    batch*heads*N < 2^31.  dtype bf16 for every call; f32 for reorder/pool/select/attn_fwd.
+ *  - Supported: head_dim 64, block 16 (4x4 pixel tiles), height and width powers of two
+ *    >= 4, 256 <= N <= 2^23, N % block^levels == 0, 1 <= topk <= min(16, N / block^levels),
+ *    1 <= levels <= 6, batch*heads*N < 2^31.  dtype bf16 for every call; f32 for
+ *    reorder/pool/select/attn_fwd.
  */
 #ifndef LLSA_H
 #define LLSA_H

@@ -53,6 +53,8 @@ def _p(**kw):
     (dict(height=128, width=256, levels=3), 0),
     (dict(width=48), 2),                    # not a power of two
     (dict(height=16, width=8), 2),          # fewer than 256 tokens
+    (dict(height=2, width=256, levels=1), 2),   # a side shorter than a 4x4 tile
+    (dict(height=4096, width=4096, levels=1), 2),  # more than 2^23 tokens
     (dict(levels=3), 2),                    # N % B^L != 0
     (dict(topk=17), 2),                     # above the 16 supported
     (dict(levels=2, topk=9, height=32, width=64), 2),  # K > N / B^L = 8
