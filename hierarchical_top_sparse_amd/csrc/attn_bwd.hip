@@ -113,36 +113,101 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* st, int t4, int lane) {
 }
 
 // ====================================================================== stage 1: query-major
+// LDS layout (bf16 elements): per wave, a 32-row staging tile (K rows of a fine chunk; after the
+// chunk loop the block's Q and dO rows for the coarse partial sums) and four 32x16 tiles (P^T,
+// dS^T as hi + lo); then, shared by the workgroup, the coarse keys/values of its level-2
+// group: K hi, K lo, V hi, V lo (32 rows each) and the 32 slot biases (fp32).
+constexpr int kQStage = 32 * kStride;
+constexpr int kQPd = 4 * 32 * 16;
+constexpr int kQPerWave = kQStage + kQPd;
+static size_t bwd_query_lds_bytes(bool coarse) {
+  return sizeof(bf16) * (size_t)(4 * kQPerWave + (coarse ? 4 * kQStage : 0)) +
+         (coarse ? 32 * sizeof(float) : 0);
+}
+
 template <int NST>   // coarse slot tiles (of 16) kept in registers: 0, 1 or 2
 __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 sK[4][32 * kStride];    // K rows (hi part)
-  __shared__ __attribute__((aligned(16))) bf16 sKl[4][32 * kStride];   // lo part (pooled keys)
-  __shared__ __attribute__((aligned(16))) bf16 sQ[4][16 * kStride];
-  __shared__ __attribute__((aligned(16))) bf16 sO[4][16 * kStride];   // dO rows
-  __shared__ __attribute__((aligned(16))) bf16 sP[4][2][32 * 16];     // P^T [slot][q], hi/lo
-  __shared__ __attribute__((aligned(16))) bf16 sS[4][2][32 * 16];     // dS^T [slot][q], hi/lo
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16* lds = (bf16*)smem;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = uniform(threadIdx.x >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
   const int n1 = a.n >> kBlockShift;
   const int n2 = n1 >> kBlockShift;
-  const int wg = xcd_block(blockIdx.x, gridDim.x);
-  const int head = wg / n2;
-  const int a2 = wg - head * n2;
+  const int wg = uniform(xcd_block(blockIdx.x, gridDim.x));
+  const int head = uniform(wg / n2);
+  const int a2 = uniform(wg - head * n2);
   const int K = a.topk;
   const long tok_base = (long)head * a.n;
-  const int n_coarse = a.enrich ? (a.levels - 1) * K : 0;
-  const int n_fine_chunks = (K + 1) >> 1;
-  const int n_chunks = n_fine_chunks + ((n_coarse + 31) >> 5);
-  bf16* stK = sK[w];
-  bf16* stKl = sKl[w];
-  bf16* stQ = sQ[w];
-  bf16* stO = sO[w];
-  bf16* stP = sP[w][0];
-  bf16* stPl = sP[w][1];
-  bf16* stS = sS[w][0];
-  bf16* stSl = sS[w][1];
+  const int n_coarse = NST > 0 ? (a.levels - 1) * K : 0;
+  bf16* stK = lds + w * kQPerWave;            // K rows of a chunk / Q and dO rows of a block
+  bf16* stP = stK + kQStage;                  // P^T hi, P^T lo, dS^T hi, dS^T lo: [slot][q]
+  bf16* cK = lds + 4 * kQPerWave;             // shared coarse K hi (+kQStage: lo)
+  bf16* cV = cK + 2 * kQStage;                // shared coarse V hi (+kQStage: lo)
+  float* cbias = (float*)(cK + 4 * kQStage);
+
+  if (NST > 0) {
+    // ---- the group's coarse keys/values (all 256 queries of the level-2 group share them)
+    const int pb0 = a2 * kBlock;
+    const int e = threadIdx.x;             // 32 slots x 8 pieces of 8 channels
+    const int slot = e >> 3;
+    const int c8 = (e & 7) * 8;
+    f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
+    float bias = -INFINITY;
+    if (slot < n_coarse) {
+      const int l = 2 + slot / K;
+      const int nl = a.n >> (kBlockShift * l);
+      const int anc = pb0 >> (kBlockShift * (l - 1));
+      const int id = a.sel[l - 1][((long)head * nl + anc) * K + (slot - (l - 2) * K)];
+      if (id >= 0 && id < nl) {
+        const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
+        const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
+        k0 = *(const f32x4*)kp;
+        k1 = *(const f32x4*)(kp + 4);
+        v0 = *(const f32x4*)vp;
+        v1 = *(const f32x4*)(vp + 4);
+        bias = 4.0f * (float)l;   // log2(16^l)
+      }
+    }
+    bf16x8 hi, lo;
+    split_f32x8(k0, k1, hi, lo);
+    *(bf16x8*)(cK + slot * kStride + c8) = hi;
+    *(bf16x8*)(cK + kQStage + slot * kStride + c8) = lo;
+    split_f32x8(v0, v1, hi, lo);
+    *(bf16x8*)(cV + slot * kStride + c8) = hi;
+    *(bf16x8*)(cV + kQStage + slot * kStride + c8) = lo;
+    if (c8 == 0) cbias[slot] = bias;
+    __syncthreads();
+  }
+
+  const uint32_t head_bytes = (uint32_t)a.n * kDim * 2;
+  const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rk = make_rsrc_uniform((const char*)a.k + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rdo =
+      make_rsrc_uniform((const char*)a.dout + (size_t)head * head_bytes, head_bytes);
+
+  // lane-constant byte offsets inside a 4x4 block: staged rows and A-operand rows
+  const int srow0 = lane >> 3;
+  const int piece = lane & 7;
+  uint32_t st_off[4];
+#pragma unroll
+  for (int ins = 0; ins < 4; ++ins)
+    st_off[ins] = (uint32_t)(tile_offset((ins * 8 + srow0) & 15, a.grid) * kDim * 2 + 16 * piece);
+  uint32_t va_off[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    va_off[t] = (uint32_t)(tile_offset(chunk_key(n, t) & 15, a.grid) * kDim * 2) + 16 * g;
+  const bool a_second = n >= 8;     // A rows 8..15 of both tiles come from the second block
+  const bool lane_second = g >= 2;  // this lane's 8 keys come from the second block
+  const int n_fine = (K + 1) >> 1;
+
+  struct FineLd {
+    i32x4 k[4];      // staged K rows
+    i32x4 v[2][2];   // V rows as A operands of dP^T
+    int ok0, ok1;
+  };
 
   f32x4 cpk[NST > 0 ? NST : 1][4];   // coarse partial dK (unscaled): [slot tile][d tile]
   f32x4 cpv[NST > 0 ? NST : 1][4];
@@ -153,160 +218,138 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 
   for (int it = 0; it < 4; ++it) {
     const int pb = a2 * kBlock + w * 4 + it;
-    const int qrow = token_row(pb * kBlock + n, a.grid);
-    const bf16* qp = a.q + (tok_base + qrow) * kDim;
-    const bf16* dop = a.dout + (tok_base + qrow) * kDim;
+    const int qcorner = block_corner(pb, a.grid);
+    const int qrow = qcorner + tile_offset(n, a.grid);
     bf16x8 qh[2], dh[2];
-    qh[0] = *(const bf16x8*)(qp + 8 * g);
-    qh[1] = *(const bf16x8*)(qp + 32 + 8 * g);
-    dh[0] = *(const bf16x8*)(dop + 8 * g);
-    dh[1] = *(const bf16x8*)(dop + 32 + 8 * g);
-    const float lse2 = a.lse[tok_base + pb * kBlock + n] * kLog2e;
-    if (NST > 0) {
-      // stage this block's Q and dO rows for the coarse partial sums (k = query axis)
-      const int row = lane >> 2;            // 16 rows, 4 lanes x 32 bytes each
-      const int part = (lane & 3) * 16;
-      const int prow = token_row(pb * kBlock + row, a.grid);
-      const bf16* qs = a.q + (tok_base + prow) * kDim + part;
-      const bf16* ds = a.dout + (tok_base + prow) * kDim + part;
-      *(bf16x8*)(stQ + row * kStride + part) = *(const bf16x8*)qs;
-      *(bf16x8*)(stQ + row * kStride + part + 8) = *(const bf16x8*)(qs + 8);
-      *(bf16x8*)(stO + row * kStride + part) = *(const bf16x8*)ds;
-      *(bf16x8*)(stO + row * kStride + part + 8) = *(const bf16x8*)(ds + 8);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      qh[s] = buf_load8(rq, (uint32_t)(qrow * kDim + 32 * s + 8 * g) * 2);
+      dh[s] = buf_load8(rdo, (uint32_t)(qrow * kDim + 32 * s + 8 * g) * 2);
     }
-
+    const float lse2 = a.lse[tok_base + pb * kBlock + n] * kLog2e;
     const int32_t* sel1 = a.sel[0] + ((long)head * n1 + pb) * K;
+
+    auto load_fine = [&](int ch) -> FineLd {
+      FineLd f;
+      const int j0 = uniform(sel1[2 * ch]);
+      const int j1 = uniform((2 * ch + 1 < K) ? sel1[2 * ch + 1] : -1);
+      f.ok0 = j0 >= 0 && j0 < n1;
+      f.ok1 = j1 >= 0 && j1 < n1;
+      const uint32_t b0 = f.ok0 ? (uint32_t)block_corner(j0, a.grid) * kDim * 2 : kNoRow;
+      const uint32_t b1 = f.ok1 ? (uint32_t)block_corner(j1, a.grid) * kDim * 2 : kNoRow;
+#pragma unroll
+      for (int ins = 0; ins < 4; ++ins)
+        f.k[ins] = __builtin_amdgcn_raw_buffer_load_b128(rk, (ins >= 2 ? b1 : b0) + st_off[ins],
+                                                         0, 0);
+      const uint32_t vb = a_second ? b1 : b0;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          f.v[t][s] = __builtin_amdgcn_raw_buffer_load_b128(rv, vb + va_off[t] + 64 * s, 0, 0);
+      return f;
+    };
+
     // dQ = scale * sum_e P_e (dP_e - D) k_e = scale * (A - D * Bv) with A = sum P dP k and
     // Bv = sum P k, so D = sum_e P_e dP_e is exact (no bf16 O) and one pass suffices.
     f32x4 acc_a[4], acc_b[4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) acc_a[t4] = acc_b[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
     float dpart = 0.f;           // this lane's share of D
-    float pc[2][4], dpc[2][4];   // P and dP of the coarse chunk (the last one)
+    float pc[2][4], dpc[2][4];   // P and dP of the coarse chunk
 
-    for (int ch = 0; ch < n_chunks; ++ch) {
-      const bool fine = ch < n_fine_chunks;
-      // ---- lane kk (< 32) resolves key kk of the chunk: row, level, validity (as a mask)
-      long my_row = 0;
-      bool my_ok = false;
-      if (fine) {
-        const int kk = lane & 31;
-        const int j = kk < 16 ? sel1[2 * ch] : ((2 * ch + 1 < K) ? sel1[2 * ch + 1] : -1);
-        my_ok = j >= 0 && j < n1;
-        my_row = my_ok ? tok_base + token_row(j * kBlock + (kk & 15), a.grid) : 0;
-      } else {
-        const int slot = (ch - n_fine_chunks) * 32 + (lane & 31);
-        if (slot < n_coarse) {
-          const int l = 2 + slot / K;
-          const int nl = a.n >> (kBlockShift * l);
-          const int anc = pb >> (kBlockShift * (l - 1));
-          const int id = a.sel[l - 1][((long)head * nl + anc) * K + (slot % K)];
-          my_ok = id >= 0 && id < nl;
-          my_row = my_ok ? (long)head * nl + id : 0;
-        }
-      }
-      const uint64_t valid = __ballot(my_ok) & 0xffffffffull;
-      auto row_of = [&](int kk) -> long { return __shfl(my_row, kk, 64); };
-      // level of chunk position kk (coarse chunks): arithmetic on its slot, clamped to a level
-    // that exists, so no cross-lane read is needed and a pointer index is always in range
-    auto level_of = [&](int kk) -> int {
-      const int slot = (ch - n_fine_chunks) * 32 + kk;
-      const int l = 2 + (slot > 0 ? slot : 0) / K;
-      return l < a.levels ? l : a.levels;
-    };
-      // ---- stage the chunk's K rows (32 rows x 128 B; pooled keys as hi + lo)
-#pragma unroll
-      for (int ins = 0; ins < 4; ++ins) {
-        const int row = ins * 8 + (lane >> 3);
-        const int piece = (lane & 7) * 8;
-        const long r = row_of(row);   // cross-lane read: uniform control flow only
-        const int lvl = level_of(row);
-        const bool ok = (valid >> row) & 1;
-        if (fine) {
-          const bf16x8 kv = ok ? *(const bf16x8*)(a.k + r * kDim + piece) : zero8();
-          *(bf16x8*)(stK + row * kStride + piece) = kv;
-        } else {
-          f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = {0.f, 0.f, 0.f, 0.f};
-          if (ok) {
-            const float* kp = a.k_lv[lvl - 1] + r * kDim + piece;
-            k0 = *(const f32x4*)kp;
-            k1 = *(const f32x4*)(kp + 4);
-          }
-          bf16x8 hi, lo;
-          split_f32x8(k0, k1, hi, lo);
-          *(bf16x8*)(stK + row * kStride + piece) = hi;
-          *(bf16x8*)(stKl + row * kStride + piece) = lo;
-        }
-      }
-      wave_lds_sync();
-      // ---- S^T and dP^T tiles (V rows are read straight from memory as A operands)
+    // P, P dP of one chunk from its S^T / dP^T tiles; A/B accumulation on the MFMA
+    auto absorb = [&](const f32x4 (&st)[2], const f32x4 (&dp)[2], const float (&add)[2][4],
+                      const bf16* kt_hi, const bf16* kt_lo, bool keep) {
       float p[2][4], w1[2][4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int arow = chunk_key(n, t);
-        const bool aok = (valid >> arow) & 1;
-        const long vr = row_of(arow);   // cross-lane read: uniform control flow only
-        const int alvl = level_of(arow);
-        f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-        st = mfma_bf16_k32(lds_row8(stK, arow, 0, g), qh[0], st);
-        st = mfma_bf16_k32(lds_row8(stK, arow, 1, g), qh[1], st);
-        if (fine) {
-          bf16x8 v0 = zero8(), v1 = zero8();
-          if (aok) {
-            v0 = *(const bf16x8*)(a.v + vr * kDim + 8 * g);
-            v1 = *(const bf16x8*)(a.v + vr * kDim + 32 + 8 * g);
-          }
-          dp = mfma_bf16_k32(v0, dh[0], dp);
-          dp = mfma_bf16_k32(v1, dh[1], dp);
-        } else {
-          st = mfma_bf16_k32(lds_row8(stKl, arow, 0, g), qh[0], st);
-          st = mfma_bf16_k32(lds_row8(stKl, arow, 1, g), qh[1], st);
-#pragma unroll
-          for (int sidx = 0; sidx < 2; ++sidx) {
-            f32x4 x0 = {0.f, 0.f, 0.f, 0.f}, x1 = {0.f, 0.f, 0.f, 0.f};
-            if (aok) {
-              const float* vp = a.v_lv[alvl - 1] + vr * kDim + 32 * sidx + 8 * g;
-              x0 = *(const f32x4*)vp;
-              x1 = *(const f32x4*)(vp + 4);
-            }
-            bf16x8 hi, lo;
-            split_f32x8(x0, x1, hi, lo);
-            dp = mfma_bf16_k32(hi, dh[sidx], dp);
-            dp = mfma_bf16_k32(lo, dh[sidx], dp);
-          }
-        }
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kk = 8 * g + i + 4 * t;
-          const bool ok = (valid >> kk) & 1;
-          const float bias = fine ? 0.f : 4.0f * (float)level_of(kk);
-          const float pv = ok ? exp2f(st[i] * a.c2 + bias - lse2) : 0.f;
+          const float pv = fast_exp2(fmaf(st[t][i], a.c2, add[t][i] - lse2));
           p[t][i] = pv;
-          w1[t][i] = pv * dp[i];
+          w1[t][i] = pv * dp[t][i];
           dpart += w1[t][i];
-          pc[t][i] = pv;
-          dpc[t][i] = dp[i];
+          if (keep) {
+            pc[t][i] = pv;
+            dpc[t][i] = dp[t][i];
+          }
         }
-      }
-      // ---- A^T += K^T (P dP)^T, Bv^T += K^T P^T  (weights as hi + lo pairs)
       bf16x8 a_hi, a_lo, b_hi, b_lo;
       split8(w1, a_hi, a_lo);
       split8(p, b_hi, b_lo);
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        const bf16x8 kt = lds_tr8(stK, t4, lane);
+        const bf16x8 kt = lds_tr8(kt_hi, t4, lane);
         acc_a[t4] = mfma_bf16_k32(kt, a_hi, acc_a[t4]);
         acc_a[t4] = mfma_bf16_k32(kt, a_lo, acc_a[t4]);
         acc_b[t4] = mfma_bf16_k32(kt, b_hi, acc_b[t4]);
         acc_b[t4] = mfma_bf16_k32(kt, b_lo, acc_b[t4]);
-        if (!fine) {
-          const bf16x8 ktl = lds_tr8(stKl, t4, lane);
+        if (kt_lo) {
+          const bf16x8 ktl = lds_tr8(kt_lo, t4, lane);
           acc_a[t4] = mfma_bf16_k32(ktl, a_hi, acc_a[t4]);
           acc_b[t4] = mfma_bf16_k32(ktl, b_hi, acc_b[t4]);
         }
       }
+    };
+
+    auto fine_chunk = [&](const FineLd& f) {
+#pragma unroll
+      for (int ins = 0; ins < 4; ++ins)
+        *(i32x4*)(stK + (ins * 8 + srow0) * kStride + 8 * piece) = f.k[ins];
       wave_lds_sync();
+      f32x4 st[2], dp[2];
+      float add[2][4];
+      const float madd = (lane_second ? f.ok1 : f.ok0) ? 0.f : -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int arow = chunk_key(n, t);
+        st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        st[t] = mfma_bf16_k32(lds_row8(stK, arow, 0, g), qh[0], st[t]);
+        st[t] = mfma_bf16_k32(lds_row8(stK, arow, 1, g), qh[1], st[t]);
+        dp[t] = mfma_bf16_k32(*(const bf16x8*)&f.v[t][0], dh[0], dp[t]);
+        dp[t] = mfma_bf16_k32(*(const bf16x8*)&f.v[t][1], dh[1], dp[t]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) add[t][i] = madd;
+      }
+      absorb(st, dp, add, stK, nullptr, false);
+      wave_lds_sync();
+    };
+
+    // ---- fine chunks: two load buffers used in turn, each refilled while the other computes
+    FineLd fa = load_fine(0), fb;
+    for (int ch = 0; ch < n_fine; ch += 2) {
+      if (ch + 1 < n_fine) fb = load_fine(ch + 1);
+      fine_chunk(fa);
+      if (ch + 1 >= n_fine) break;
+      if (ch + 2 < n_fine) fa = load_fine(ch + 2);
+      fine_chunk(fb);
     }
+
+    // ---- the coarse chunk, from the workgroup's LDS copy
+    if (NST > 0) {
+      f32x4 st[2], dp[2];
+      float add[2][4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int arow = chunk_key(n, t);
+        st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          st[t] = mfma_bf16_k32(lds_row8(cK, arow, s, g), qh[s], st[t]);
+          st[t] = mfma_bf16_k32(lds_row8(cK + kQStage, arow, s, g), qh[s], st[t]);
+          dp[t] = mfma_bf16_k32(lds_row8(cV, arow, s, g), dh[s], dp[t]);
+          dp[t] = mfma_bf16_k32(lds_row8(cV + kQStage, arow, s, g), dh[s], dp[t]);
+        }
+        const f32x4 b4 = *(const f32x4*)(cbias + 8 * g + 4 * t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) add[t][i] = b4[i];
+      }
+      absorb(st, dp, add, cK, cK + kQStage, true);
+    }
+
     const float Dn = group4_sum(dpart);
     if (g == 0) a.dd[tok_base + pb * kBlock + n] = Dn;
     // ---- write dQ (lane holds dQ[n][16 t4 + 4g + i])
@@ -321,7 +364,28 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 
     if (NST > 0) {
       // ---- coarse partials over this block's 16 queries: dV_c += P^T dO, dK_c += dS^T Q,
-      // with dS = P (dP - D) of the coarse chunk (the last chunk, still in registers)
+      // with dS = P (dP - D).  The staging tile now holds the block's Q rows (0..15) and dO
+      // rows (16..31).
+      bf16* stQ = stK;
+      bf16* stO = stK + 16 * kStride;
+      {
+        const int row = lane >> 2;            // 16 rows, 4 lanes x 32 bytes each
+        const int part = (lane & 3) * 16;
+        const uint32_t off =
+            (uint32_t)((qcorner + tile_offset(row, a.grid)) * kDim + part) * 2;
+        const i32x4 q0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
+        const i32x4 q1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
+        const i32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0);
+        const i32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(rdo, off + 16, 0, 0);
+        *(i32x4*)(stQ + row * kStride + part) = q0;
+        *(i32x4*)(stQ + row * kStride + part + 8) = q1;
+        *(i32x4*)(stO + row * kStride + part) = d0;
+        *(i32x4*)(stO + row * kStride + part + 8) = d1;
+      }
+      bf16* pH = stP;
+      bf16* pL = stP + 512;
+      bf16* sH = stP + 1024;
+      bf16* sL = stP + 1536;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -330,10 +394,10 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
           const float dsv = pc[t][i] * (dpc[t][i] - Dn);
           const bf16 ph = (bf16)pc[t][i];
           const bf16 sh = (bf16)dsv;
-          stP[kk * 16 + n] = ph;
-          stPl[kk * 16 + n] = (bf16)(pc[t][i] - (float)ph);
-          stS[kk * 16 + n] = sh;
-          stSl[kk * 16 + n] = (bf16)(dsv - (float)sh);
+          pH[kk * 16 + n] = ph;
+          pL[kk * 16 + n] = (bf16)(pc[t][i] - (float)ph);
+          sH[kk * 16 + n] = sh;
+          sL[kk * 16 + n] = (bf16)(dsv - (float)sh);
         }
       wave_lds_sync();
       const int r = (lane & 15) >> 2;
@@ -341,10 +405,10 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
         const int at = (16 * st + n) * 16 + 4 * g;
-        const bf16x4 pa = *(const bf16x4*)(stP + at);
-        const bf16x4 pl = *(const bf16x4*)(stPl + at);
-        const bf16x4 sa = *(const bf16x4*)(stS + at);
-        const bf16x4 sl = *(const bf16x4*)(stSl + at);
+        const bf16x4 pa = *(const bf16x4*)(pH + at);
+        const bf16x4 pl = *(const bf16x4*)(pL + at);
+        const bf16x4 sa = *(const bf16x4*)(sH + at);
+        const bf16x4 sl = *(const bf16x4*)(sL + at);
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
           const bf16x4 dob = lds_read_tr16(stO + (4 * g + r) * kStride + 16 * t4 + 4 * c);
@@ -362,7 +426,7 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   if (NST > 0) {
     // ---- reduce the four waves' coarse partials (in wave order 0..3) and store them for this
     // level-2 group.  cp*[st][t4][i] at lane (n, g) is slot 16 st + 4g + i, channel 16 t4 + n.
-    float* red = (float*)&sK[0][0];   // reuses the K staging: 2 x NST x 16 x 64 floats <= 16 KB
+    float* red = (float*)cK;   // the shared coarse copy is no longer needed: 16 KB >= 2 x NST KB x 4
     const int half = NST * 16 * kDim;
     for (int turn = 0; turn < 4; ++turn) {
       __syncthreads();
@@ -464,58 +528,93 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 sQ[4][32 * kStride];
   __shared__ __attribute__((aligned(16))) bf16 sO[4][32 * kStride];   // dO rows
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = uniform(threadIdx.x >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
   const int n1 = a.n >> kBlockShift;
-  const long kb = (long)xcd_block(blockIdx.x, gridDim.x) * 4 + w;
-  if (kb >= (long)a.bh * n1) return;
-  const int head = (int)(kb / n1);
-  const int j = (int)(kb - (long)head * n1);
+  // every workgroup holds 4 whole key blocks of one head (N / 16 is a multiple of 4)
+  const int kb = uniform(xcd_block(blockIdx.x, gridDim.x) * 4) + w;
+  const int head = uniform(kb / n1);
+  const int j = uniform(kb - head * n1);
   const long tok_base = (long)head * a.n;
   bf16* stQ = sQ[w];
   bf16* stO = sO[w];
 
+  const uint32_t head_bytes = (uint32_t)a.n * kDim * 2;
+  const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rk = make_rsrc_uniform((const char*)a.k + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rdo =
+      make_rsrc_uniform((const char*)a.dout + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rl = make_rsrc_uniform(a.lse + tok_base, (uint32_t)a.n * 4);
+  const rsrc_t rd = make_rsrc_uniform(a.dd + tok_base, (uint32_t)a.n * 4);
+
   // keys of this block as B operands: lane (n, g) holds row n, channels 32s + 8g .. +7
-  const int krow = token_row(j * kBlock + n, a.grid);
-  const bf16* kp = a.k + (tok_base + krow) * kDim;
-  const bf16* vp = a.v + (tok_base + krow) * kDim;
+  const int krow = block_corner(j, a.grid) + tile_offset(n, a.grid);
   bf16x8 kh[2], vh[2];
-  kh[0] = *(const bf16x8*)(kp + 8 * g);
-  kh[1] = *(const bf16x8*)(kp + 32 + 8 * g);
-  vh[0] = *(const bf16x8*)(vp + 8 * g);
-  vh[1] = *(const bf16x8*)(vp + 32 + 8 * g);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    kh[s] = buf_load8(rk, (uint32_t)(krow * kDim + 32 * s + 8 * g) * 2);
+    vh[s] = buf_load8(rv, (uint32_t)(krow * kDim + 32 * s + 8 * g) * 2);
+  }
+
+  // lane-constant offsets: staged rows (bytes) and this lane's 4 queries per tile (tokens)
+  const int srow0 = lane >> 3;
+  const int piece = lane & 7;
+  uint32_t st_off[4];
+#pragma unroll
+  for (int ins = 0; ins < 4; ++ins)
+    st_off[ins] = (uint32_t)(tile_offset((ins * 8 + srow0) & 15, a.grid) * kDim * 2 + 16 * piece);
+  const bool lane_second = g >= 2;   // this lane's queries come from the second block
 
   const int32_t* off = a.csc_off[0] + (long)head * (n1 + 1);
   const int32_t* rows = a.csc_rows[0] + (long)head * n1 * a.topk;
-  const int e0 = off[j], e1 = off[j + 1];
+  const int e0 = uniform(off[j]);
+  const int e1 = uniform(off[j + 1]);
+
+  struct PairLd {
+    i32x4 q[4], d[4];   // staged Q and dO rows
+    f32x4 l4[2], d4[2];  // lse and D of this lane's queries (tile t: tokens 8g+4t .. +3)
+    int okA, okB;
+  };
+  auto load_pair = [&](int e) -> PairLd {
+    PairLd f;
+    const int pA = uniform(rows[e]);
+    const int pB = uniform(e + 1 < e1 ? rows[e + 1] : -1);
+    f.okA = pA >= 0 && pA < n1;
+    f.okB = pB >= 0 && pB < n1;
+    const uint32_t bA = f.okA ? (uint32_t)block_corner(pA, a.grid) * kDim * 2 : kNoRow;
+    const uint32_t bB = f.okB ? (uint32_t)block_corner(pB, a.grid) * kDim * 2 : kNoRow;
+#pragma unroll
+    for (int ins = 0; ins < 4; ++ins) {
+      const uint32_t o = (ins >= 2 ? bB : bA) + st_off[ins];
+      f.q[ins] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
+      f.d[ins] = __builtin_amdgcn_raw_buffer_load_b128(rdo, o, 0, 0);
+    }
+    const bool okl = lane_second ? f.okB : f.okA;
+    const int pl = lane_second ? pB : pA;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t o = okl ? (uint32_t)(pl * kBlock + ((8 * g + 4 * t) & 15)) * 4 : kNoRow;
+      f.l4[t] = buf_load4f(rl, o);
+      f.d4[t] = buf_load4f(rd, o);
+    }
+    return f;
+  };
+
   f32x4 dka[4], dva[4];
 #pragma unroll
   for (int t4 = 0; t4 < 4; ++t4) dka[t4] = dva[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int e = e0; e < e1; e += 2) {
-    const int pA = rows[e];
-    const int pB = (e + 1 < e1) ? rows[e + 1] : -1;
-    const bool okA = pA >= 0 && pA < n1;
-    const bool okB = pB >= 0 && pB < n1;
-    // ---- stage the pair's Q and dO rows: query position qq = 16*(which) + token
+  auto pair = [&](const PairLd& f) {
 #pragma unroll
     for (int ins = 0; ins < 4; ++ins) {
-      const int row = ins * 8 + (lane >> 3);
-      const int piece = (lane & 7) * 8;
-      const int pblk = row < 16 ? pA : pB;
-      const bool ok = row < 16 ? okA : okB;
-      bf16x8 qv = zero8(), dv = zero8();
-      if (ok) {
-        const long r = tok_base + token_row(pblk * kBlock + (row & 15), a.grid);
-        qv = *(const bf16x8*)(a.q + r * kDim + piece);
-        dv = *(const bf16x8*)(a.dout + r * kDim + piece);
-      }
-      *(bf16x8*)(stQ + row * kStride + piece) = qv;
-      *(bf16x8*)(stO + row * kStride + piece) = dv;
+      *(i32x4*)(stQ + (ins * 8 + srow0) * kStride + 8 * piece) = f.q[ins];
+      *(i32x4*)(stO + (ins * 8 + srow0) * kStride + 8 * piece) = f.d[ins];
     }
     wave_lds_sync();
-    // ---- S and dP tiles (queries x keys): lane (n, g) holds queries 8g + i + 4t, key n
+    // S and dP tiles (queries x keys): lane (n, g) holds queries 8g + i + 4t, key n
+    const float madd = (lane_second ? f.okB : f.okA) ? 0.f : -INFINITY;
     float p[2][4], dsv[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -525,27 +624,17 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       st = mfma_bf16_k32(lds_row8(stQ, arow, 1, g), kh[1], st);
       dp = mfma_bf16_k32(lds_row8(stO, arow, 0, g), vh[0], dp);
       dp = mfma_bf16_k32(lds_row8(stO, arow, 1, g), vh[1], dp);
-      // queries 8g + 4t + i, i = 0..3: four consecutive tokens of one block
-      const int qq = 8 * g + 4 * t;
-      const int pblk = qq < 16 ? pA : pB;
-      const bool ok = qq < 16 ? okA : okB;
-      f32x4 l4 = {0.f, 0.f, 0.f, 0.f}, d4 = {0.f, 0.f, 0.f, 0.f};
-      if (ok) {
-        const long mpos = tok_base + pblk * kBlock + (qq & 15);
-        l4 = *(const f32x4*)(a.lse + mpos);
-        d4 = *(const f32x4*)(a.dd + mpos);
-      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pv = ok ? exp2f(st[i] * a.c2 - l4[i] * kLog2e) : 0.f;
+        const float pv = fast_exp2(fmaf(st[i], a.c2, madd - f.l4[t][i] * kLog2e));
         p[t][i] = pv;
-        dsv[t][i] = pv * (dp[i] - d4[i]);
+        dsv[t][i] = pv * (dp[i] - f.d4[t][i]);
       }
     }
     bf16x8 p_hi, p_lo, ds_hi, ds_lo;
     split8(p, p_hi, p_lo);
     split8(dsv, ds_hi, ds_lo);
-    // ---- dV^T += dO^T P, dK^T += Q^T dS  (contract over the pair's 32 queries)
+    // dV^T += dO^T P, dK^T += Q^T dS  (contract over the pair's 32 queries)
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       const bf16x8 ot = lds_tr8(stO, t4, lane);
@@ -556,6 +645,18 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       dka[t4] = mfma_bf16_k32(qt, ds_lo, dka[t4]);
     }
     wave_lds_sync();
+  };
+
+  // ---- query-block pairs of CSC_1[j]: two load buffers used in turn
+  if (e0 < e1) {
+    PairLd fa = load_pair(e0), fb;
+    for (int e = e0; e < e1; e += 4) {
+      if (e + 2 < e1) fb = load_pair(e + 2);
+      pair(fa);
+      if (e + 2 >= e1) break;
+      if (e + 4 < e1) fa = load_pair(e + 4);
+      pair(fb);
+    }
   }
 
   // ---- push-down of pooled-key gradients and store (lane holds key n, channels 16t4+4g+i)
@@ -587,14 +688,14 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   bf16* dvp = a.dv + (tok_base + krow) * kDim;
 #pragma unroll
   for (int t4 = 0; t4 < 4; ++t4) {
-    bf16x4 rk, rv;
+    bf16x4 rk4, rv4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      rk[i] = (bf16)(dka[t4][i] * a.scale + pdk[t4][i]);
-      rv[i] = (bf16)(dva[t4][i] + pdv[t4][i]);
+      rk4[i] = (bf16)(dka[t4][i] * a.scale + pdk[t4][i]);
+      rv4[i] = (bf16)(dva[t4][i] + pdv[t4][i]);
     }
-    *(bf16x4*)(dkp + 16 * t4 + 4 * g) = rk;
-    *(bf16x4*)(dvp + 16 * t4 + 4 * g) = rv;
+    *(bf16x4*)(dkp + 16 * t4 + 4 * g) = rk4;
+    *(bf16x4*)(dvp + 16 * t4 + 4 * g) = rv4;
   }
 }
 
@@ -683,12 +784,13 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   const int n2 = s.n >> (2 * kBlockShift);
   const unsigned qblocks = (unsigned)(s.bh * n2);
   const int n_coarse = coarse ? (s.levels - 1) * s.topk : 0;
+  const size_t qlds = bwd_query_lds_bytes(n_coarse > 0);
   if (n_coarse == 0)
-    hipLaunchKernelGGL(bwd_query_kernel<0>, dim3(qblocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_query_kernel<0>, dim3(qblocks), dim3(256), qlds, stream, a);
   else if (n_coarse <= 16)
-    hipLaunchKernelGGL(bwd_query_kernel<1>, dim3(qblocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_query_kernel<1>, dim3(qblocks), dim3(256), qlds, stream, a);
   else
-    hipLaunchKernelGGL(bwd_query_kernel<2>, dim3(qblocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(bwd_query_kernel<2>, dim3(qblocks), dim3(256), qlds, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (coarse) {
@@ -706,7 +808,7 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
     }
   }
   const long kwaves = (long)s.bh * (s.n >> kBlockShift);
-  hipLaunchKernelGGL(bwd_key_kernel, dim3((unsigned)((kwaves + 3) / 4)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(bwd_key_kernel, dim3((unsigned)(kwaves / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
