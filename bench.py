@@ -1,15 +1,19 @@
 """LLSA fwd+bwd throughput on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic pixel tokens already
-resident in HBM: (Morton reorder folded into the kernels' addressing) -> pooling -> coarse-to-
-fine selection -> sparse attention forward -> CSR->CSC transpose of every level -> sparse
-backward (dQ, dK, dV).  Prints one JSON line.
+resident in HBM: pooling -> coarse-to-fine selection -> sparse attention forward -> CSR->CSC
+transpose of every level -> sparse backward (dQ, dK, dV); the Morton reorder is folded into
+the kernels' addressing (inputs and outputs stay in raster order).  The step is captured once
+into a HIP graph and replayed; `value` is batch*N tokens per second of graph replays.  A
+second, eager pass with per-kernel HIP events gives each kernel's launch duration; the
+roofline object is for the kernel with the largest total time.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config px256_train] [--no-cpu]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -19,8 +23,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
+KERNEL_SOURCES = {               # kernel -> source file (the traffic record is tied to it)
+    "attn_fwd_kernel": "attn_fwd.hip",
+    "bwd_query_kernel": "attn_bwd.hip",
+    "bwd_key_kernel": "attn_bwd.hip",
+}
 
 
 def parse():
@@ -30,6 +39,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="px256_train")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead")
     ap.add_argument("--with-copy", action="store_true",
                     help="also launch one Morton reorder (a plain copy of one token tensor) per "
                          "step, outside the timed region: the calibration kernel for HBM "
@@ -37,71 +47,45 @@ def parse():
     return ap.parse_args()
 
 
-class Pipeline:
-    """Preallocated buffers and the sequence of C-ABI calls of one training step."""
+def kernel_model(p, elem_bytes=2):
+    """Algorithmic (compulsory) HBM bytes and FLOPs per launch of the attention kernels.
 
-    def __init__(self, p, q, k, v, do):
-        import torch
-        from hierarchical_top_sparse_amd import _abi
-
-        self.abi, self.p = _abi, p
-        self.q, self.k, self.v, self.do = q, k, v, do
-        dev, f32 = q.device, torch.float32
-        lv = lambda l: torch.empty((p.batch, p.heads, p.n_level(l), p.head_dim), device=dev,
-                                   dtype=f32)
-        L = p.levels
-        self.q_lv = [lv(l) for l in range(1, L + 1)]
-        self.k_lv = [lv(l) for l in range(1, L + 1)]
-        self.v_lv = [None] + [lv(l) for l in range(2, L + 1)]
-        self.sel = [torch.empty((p.batch, p.heads, p.n_level(l), p.topk), device=dev,
-                                dtype=torch.int32) for l in range(1, L + 1)]
-        self.o = torch.empty_like(q)
-        self.lse = torch.empty((p.batch, p.heads, p.n), device=dev, dtype=f32)
-        nmat = p.batch * p.heads
-        self.off = [torch.empty((p.batch, p.heads, p.n_level(l) + 1), device=dev,
-                                dtype=torch.int32) for l in range(1, L + 1)]
-        self.rows = [torch.empty((p.batch, p.heads, p.n_level(l) * p.topk), device=dev,
-                                 dtype=torch.int32) for l in range(1, L + 1)]
-        tws = max(_abi.llsa_index_transpose_workspace(nmat, p.n_level(l), p.n_level(l), p.topk)
-                  for l in range(1, L + 1))
-        self.tws = torch.empty(tws, device=dev, dtype=torch.uint8)
-        _, bws = _abi.llsa_workspace_bytes(p)
-        self.bws = torch.empty(bws, device=dev, dtype=torch.uint8)
-        self.dq, self.dk, self.dv = (torch.empty_like(q) for _ in range(3))
-        self.nmat = nmat
-
-    def calls(self):
-        """(name, thunk) for every ABI call of a step, in order."""
-        a, p = self.abi, self.p
-        out = [("pool", lambda: a.llsa_pool(p, self.q, self.k, self.v, self.q_lv, self.k_lv,
-                                            self.v_lv)),
-               ("select", lambda: a.llsa_select(p, self.q_lv, self.k_lv, self.sel)),
-               ("attn_fwd", lambda: a.llsa_attn_fwd(p, self.q, self.k, self.v, self.k_lv,
-                                                    self.v_lv, self.sel, self.o, self.lse))]
-        for l in range(1, p.levels + 1):
-            nl = p.n_level(l)
-            out.append((f"transpose_l{l}", (lambda l=l, nl=nl: a.llsa_index_transpose(
-                self.nmat, nl, nl, p.topk, self.sel[l - 1], self.off[l - 1], self.rows[l - 1],
-                self.tws))))
-        out.append(("attn_bwd", lambda: a.llsa_attn_bwd(
-            p, self.q, self.k, self.v, self.do, self.lse, self.k_lv, self.v_lv,
-            self.sel, self.off, self.rows, self.dq, self.dk, self.dv, self.bws)))
-        return out
-
-
-def algorithmic(p, elem_bytes=2):
-    """Algorithmic (compulsory) HBM bytes and FLOPs per launch of each attention kernel."""
+    T = one [b, H, N, 64] token tensor.  Gathers of selected key blocks count once (the
+    compulsory traffic); index arrays and pooled levels are counted in full.
+    """
     bh, n, d, K, L = p.batch * p.heads, p.n, p.head_dim, p.topk, p.levels
     T = bh * n * d * elem_bytes
-    n1 = n // 16
-    kq = K * 16 + (L - 1) * K           # keys per query
-    coarse = sum(bh * (n // 16 ** l) * d * 4 * 2 for l in range(2, L + 1))   # pooled K, V fp32
+    kq_fine = K * 16
+    n_coarse = (L - 1) * K if p.enrich else 0
+    kq = kq_fine + n_coarse
+    pooled = sum(bh * (n // 16 ** l) * d * 4 * 2 for l in range(2, L + 1)) if p.enrich else 0
     sel_bytes = sum(bh * (n // 16 ** l) * K * 4 for l in range(1, L + 1))
-    fwd_bytes = 4 * T + bh * n * 4 + sel_bytes + coarse
-    # read q, k, v, dO (the forward's O is not needed), write dq, dk, dv
-    bwd_bytes = 7 * T + 2 * bh * n * 4 + 2 * sel_bytes + coarse + bh * (n1 + 1) * 4
-    return dict(T=T, kq=kq, fwd_bytes=fwd_bytes, bwd_bytes=bwd_bytes,
-                fwd_flops=4 * bh * n * kq * d, bwd_flops=10 * bh * n * kq * d)
+    tok4 = bh * n * 4                                     # one fp32 per token (lse or D)
+    n2 = n // 256
+    partials = bh * n2 * n_coarse * d * 4 * 2
+    csc1 = bh * ((n // 16) + 1) * 4 + bh * (n // 16) * K * 4
+    return {
+        "attn_fwd_kernel": dict(bytes=4 * T + tok4 + sel_bytes + pooled,
+                                flops=4 * bh * n * kq * d),
+        "bwd_query_kernel": dict(bytes=5 * T + 2 * tok4 + sel_bytes + pooled + partials,
+                                 flops=6 * bh * n * kq * d),
+        "bwd_key_kernel": dict(bytes=6 * T + 2 * tok4 + csc1,
+                               flops=8 * bh * n * kq_fine * d),
+    }
+
+
+def traffic_record(kernel, config):
+    """Measured HBM bytes per launch from the committed counter record, if it was taken on the
+    current source of the kernel; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "hierarchical_top_sparse_amd", "csrc", KERNEL_SOURCES[kernel])
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec
 
 
 def cpu_baseline(cfg, x, seconds_budget=12.0):
@@ -144,6 +128,7 @@ def main():
     import torch
 
     from hierarchical_top_sparse_amd import _abi, gen, ops
+    from hierarchical_top_sparse_amd.runtime import Step
 
     cfg = gen.CONFIGS[args.config]
     h, w, L = cfg["height"], cfg["width"], cfg["levels"]
@@ -152,60 +137,101 @@ def main():
     dev = torch.device("cuda:0")
     q, k, v, do = (x[t].to(dev) for t in ("q", "k", "v", "do"))
     p = ops.make_problem(q, h, w, L)
-    pipe = Pipeline(p, q, k, v, do)
-    calls = pipe.calls()
+    step = Step(p, q, k, v, do)
+    calls = step.calls()
     stream = torch.cuda.current_stream()
 
-    def step():
-        for _, fn in calls:
-            fn()
-
     for _ in range(args.warmup):
-        step()
+        step.run()
     torch.cuda.synchronize()
     if args.with_copy:
         copy_dst = torch.empty_like(q)
         for _ in range(max(1, args.steps)):
             _abi.llsa_reorder(p, q, copy_dst, False)
         torch.cuda.synchronize()
-    # timed region: events around every ABI call, on the stream the kernels run on
+
+    # ---- eager pass with per-kernel events (launch durations for the roofline)
+    _abi.llsa_profile_read()
+    _abi.llsa_profile_enable(True)
     ev = {name: [] for name, _ in calls}
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record(stream)
+    e_start.record(stream)
     for _ in range(args.steps):
         for name, fn in calls:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
             fn()
-            e1.record(stream)
-            ev[name].append((e0, e1))
-    t_end.record(stream)
+            a1.record(stream)
+            ev[name].append((a0, a1))
+    e_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
+    _abi.llsa_profile_enable(False)
+    kprof = _abi.llsa_profile_read()
+    eager_ms = e_start.elapsed_time(e_end) / args.steps
     per_call = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
                 for name, pairs in ev.items()}
+    per_kernel_ms = {name: tot / cnt for name, (cnt, tot) in kprof.items()}
+    per_step_kernel_ms = {name: tot / args.steps for name, (cnt, tot) in kprof.items()}
+
+    # ---- timed region: graph replays of the whole step
+    if args.no_graph:
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for _ in range(args.steps):
+            step.run()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_step = t0.elapsed_time(t1) / args.steps
+    else:
+        step.capture()
+        for _ in range(args.warmup):
+            step.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for _ in range(args.steps):
+            step.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        ms_step = t0.elapsed_time(t1) / args.steps
     tokens = cfg["batch"] * h * w
     value = tokens / (ms_step / 1e3)
 
-    alg = algorithmic(p)
-    fwd_ms = per_call["attn_fwd"]
-    achieved = alg["fwd_bytes"] / (fwd_ms / 1e3) / 1e9
-    roofline = {"bound": "hbm", "kernel": "attn_fwd_kernel", "achieved": round(achieved, 1),
+    # ---- roofline of the dominant kernel
+    model = kernel_model(p)
+    dominant = max((kname for kname in per_step_kernel_ms if kname in model),
+                   key=lambda kname: per_step_kernel_ms[kname])
+    launch_ms = per_kernel_ms[dominant]
+    achieved = model[dominant]["bytes"] / (launch_ms / 1e3) / 1e9
+    rec = traffic_record(dominant, args.config)
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "alg_bytes_per_launch": alg["fwd_bytes"],
-                "launch_ms": round(fwd_ms, 4),
-                "mfma_tflops": round(alg["fwd_flops"] / (fwd_ms / 1e3) / 1e12, 2)}
-    extra = {"per_call_ms": {k2: round(v2, 4) for k2, v2 in per_call.items()},
-             "attn_bwd_alg_GBps": round(alg["bwd_bytes"] / (per_call["attn_bwd"] / 1e3) / 1e9, 1),
-             "attn_bwd_mfma_tflops": round(alg["bwd_flops"] / (per_call["attn_bwd"] / 1e3) / 1e12,
-                                           2)}
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(cfg, x)
+                "traffic": rec["hbm_bytes_per_launch"] if rec else None,
+                "alg_bytes_per_launch": model[dominant]["bytes"],
+                "launch_ms": round(launch_ms, 4),
+                "mfma_frac": round(model[dominant]["flops"] / (launch_ms / 1e3) / 1e12 /
+                                   BF16_MFMA_PEAK_TFLOPS, 4)}
+    kernels = {}
+    for kname in model:
+        if kname in per_kernel_ms:
+            t = per_kernel_ms[kname] / 1e3
+            kernels[kname] = {"ms": round(per_kernel_ms[kname], 4),
+                              "hbm_frac": round(model[kname]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+                              "mfma_frac": round(model[kname]["flops"] / t / 1e12 /
+                                                 BF16_MFMA_PEAK_TFLOPS, 4)}
+    extra = {"graph": not args.no_graph, "eager_ms_per_step": round(eager_ms, 4),
+             "per_call_ms": {k2: round(v2, 4) for k2, v2 in per_call.items()},
+             "per_kernel_ms_per_step": {k2: round(v2, 4) for k2, v2 in
+                                        sorted(per_step_kernel_ms.items(),
+                                               key=lambda kv: -kv[1])},
+             "attention_kernels": kernels}
+    cpu = None if args.no_cpu else cpu_baseline(cfg, x)
     line = {
         "metric": "LLSA fwd+bwd tokens/s at 256x256 pixels (65,536 tok); % MFMA/HBM peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
             "llsa_index_transpose": ([i32, i32, i32, i32, vp, vp, vp, vp, sz, vp], i32),
             "llsa_attn_bwd": ([P, vp, vp, vp, vp, vp, pp, pp, pp, pp, pp, vp, vp, vp, vp, sz,
                                vp], i32),
+            "llsa_profile_enable": ([i32], i32),
+            "llsa_profile_read": ([ctypes.c_char_p, sz], i32),
         }
         for name, (args, res) in sigs.items():
             fn = getattr(L, name)
@@ -104,7 +106,8 @@ def lib() -> ctypes.CDLL:
 def exported_symbols() -> list:
     return ["llsa_abi_version", "llsa_status_str", "llsa_last_error", "llsa_check",
             "llsa_workspace_bytes", "llsa_reorder", "llsa_pool", "llsa_select", "llsa_attn_fwd",
-            "llsa_index_transpose_workspace", "llsa_index_transpose", "llsa_attn_bwd"]
+            "llsa_index_transpose_workspace", "llsa_index_transpose", "llsa_attn_bwd",
+            "llsa_profile_enable", "llsa_profile_read"]
 
 
 def _raise(status: int, name: str):
@@ -269,3 +272,18 @@ def llsa_attn_bwd(p: Problem, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_
                                _ptrs(csc_off), _ptrs(csc_rows), _ptr(dq), _ptr(dk), _ptr(dv),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "llsa_attn_bwd")
+
+
+def llsa_profile_enable(on: bool):
+    _raise(lib().llsa_profile_enable(int(on)), "llsa_profile_enable")
+
+
+def llsa_profile_read() -> dict:
+    """{kernel name: (launches, total_ms)} since the last read (waits for the events)."""
+    buf = ctypes.create_string_buffer(1 << 16)
+    _raise(lib().llsa_profile_read(buf, len(buf)), "llsa_profile_read")
+    out = {}
+    for line in buf.value.decode().splitlines():
+        name, cnt, ms = line.split()
+        out[name] = (int(cnt), float(ms))
+    return out

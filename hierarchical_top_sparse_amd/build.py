@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libllsa.so")
-SOURCES = ["api.cpp", "reorder.hip", "pool.hip", "select.hip", "attn_fwd.hip",
+SOURCES = ["api.cpp", "profile.cpp", "reorder.hip", "pool.hip", "select.hip", "attn_fwd.hip",
            "transpose.hip", "attn_bwd.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

@@ -482,45 +482,49 @@ __global__ __launch_bounds__(256) void coarse_reduce_kernel(BwdArgs a, int l) {
 }
 
 // dK_l[j] = sum over ancestors a in CSC_l[j] of partial(a, slot of j in Sel_l[a]).
-// One wave per coarse key; lane = channel.
+// One wave per coarse key.  Lanes first resolve up to 64 CSC entries at once (ancestor and
+// slot), then every lane (= channel) sums the partial rows in CSC order.
 __global__ __launch_bounds__(256) void coarse_grad_kernel(BwdArgs a, int l) {
   const int K = a.topk;
   const int nl = a.n >> (kBlockShift * l);
-  const long wave = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int ch = threadIdx.x & 63;
-  if (wave >= (long)a.bh * nl) return;
-  const int head = (int)(wave / nl);
-  const int j = (int)(wave - (long)head * nl);
+  const int wave = uniform((int)(blockIdx.x * 4) + (int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  if (wave >= a.bh * nl) return;
+  const int head = uniform(wave / nl);
+  const int j = uniform(wave - head * nl);
   const int n_coarse = (a.levels - 1) * K;
   const int32_t* off = a.csc_off[l - 1] + (long)head * (nl + 1);
   const int32_t* rows = a.csc_rows[l - 1] + (long)head * nl * K;
   const int32_t* sel = a.sel[l - 1] + (long)head * nl * K;
-  const int e0 = off[j], e1 = off[j + 1];
+  const float* pk = l == 2 ? a.part_k : a.lvl_part_k[l - 1];
+  const float* pv = l == 2 ? a.part_v : a.lvl_part_v[l - 1];
+  const int row_len = l == 2 ? n_coarse : K;   // slots per ancestor in the partial arrays
+  const int e0 = uniform(off[j]);
+  const int e1 = uniform(off[j + 1]);
   float sk = 0.f, sv = 0.f;
-  for (int e = e0; e < e1; ++e) {
-    const int anc = rows[e];
-    if (anc < 0 || anc >= nl) continue;
-    int slot = -1;
-    for (int s = 0; s < K; ++s)
-      if (sel[(long)anc * K + s] == j) slot = s;
-    if (slot < 0) continue;
-    long src;
-    const float* pk;
-    const float* pv;
-    if (l == 2) {
-      src = (((long)head * nl + anc) * n_coarse + slot) * kDim + ch;
-      pk = a.part_k;
-      pv = a.part_v;
-    } else {
-      src = (((long)head * nl + anc) * K + slot) * kDim + ch;
-      pk = a.lvl_part_k[l - 1];
-      pv = a.lvl_part_v[l - 1];
+  for (int base = e0; base < e1; base += 64) {
+    const int e = base + lane;
+    long src = -1;
+    if (e < e1) {
+      const int anc = rows[e];
+      if (anc >= 0 && anc < nl) {
+        int slot = -1;
+        for (int s = 0; s < K; ++s)
+          if (sel[(long)anc * K + s] == j) slot = s;
+        if (slot >= 0) src = (((long)head * nl + anc) * row_len + slot) * kDim;
+      }
     }
-    sk += pk[src];
-    sv += pv[src];
+    const int cnt = min(64, e1 - base);
+    for (int i = 0; i < cnt; ++i) {
+      const long r = __shfl(src, i, 64);   // uniform control flow
+      if (r >= 0) {
+        sk += pk[r + lane];
+        sv += pv[r + lane];
+      }
+    }
   }
-  a.dk_lv[l - 1][((long)head * nl + j) * kDim + ch] = sk;
-  a.dv_lv[l - 1][((long)head * nl + j) * kDim + ch] = sv;
+  a.dk_lv[l - 1][((long)head * nl + j) * kDim + lane] = sk;
+  a.dv_lv[l - 1][((long)head * nl + j) * kDim + lane] = sv;
 }
 
 // ====================================================================== stage 3: key-major
@@ -786,29 +790,29 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   const int n_coarse = coarse ? (s.levels - 1) * s.topk : 0;
   const size_t qlds = bwd_query_lds_bytes(n_coarse > 0);
   if (n_coarse == 0)
-    hipLaunchKernelGGL(bwd_query_kernel<0>, dim3(qblocks), dim3(256), qlds, stream, a);
+    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<0>, dim3(qblocks), dim3(256), qlds, stream, a);
   else if (n_coarse <= 16)
-    hipLaunchKernelGGL(bwd_query_kernel<1>, dim3(qblocks), dim3(256), qlds, stream, a);
+    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<1>, dim3(qblocks), dim3(256), qlds, stream, a);
   else
-    hipLaunchKernelGGL(bwd_query_kernel<2>, dim3(qblocks), dim3(256), qlds, stream, a);
+    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<2>, dim3(qblocks), dim3(256), qlds, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (coarse) {
     for (int l = 3; l <= s.levels; ++l) {
       const long total = (long)s.bh * s.n_level(l) * s.topk * kDim;
-      hipLaunchKernelGGL(coarse_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+      LLSA_LAUNCH("coarse_reduce_kernel", coarse_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
                          0, stream, a, l);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     for (int l = 2; l <= s.levels; ++l) {
       const long waves = (long)s.bh * s.n_level(l);
-      hipLaunchKernelGGL(coarse_grad_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+      LLSA_LAUNCH("coarse_grad_kernel", coarse_grad_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
                          stream, a, l);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
   }
   const long kwaves = (long)s.bh * (s.n >> kBlockShift);
-  hipLaunchKernelGGL(bwd_key_kernel, dim3((unsigned)(kwaves / 4)), dim3(256), 0, stream, a);
+  LLSA_LAUNCH("bwd_key_kernel", bwd_key_kernel, dim3((unsigned)(kwaves / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -410,9 +410,9 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const v
     if (e != hipSuccess) return e;
   }
   if (s.bf16)
-    hipLaunchKernelGGL(attn_fwd_kernel<true>, dim3(blocks), dim3(64 * kFwdWaves), lds, stream, a);
+    LLSA_LAUNCH("attn_fwd_kernel", attn_fwd_kernel<true>, dim3(blocks), dim3(64 * kFwdWaves), lds, stream, a);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<false>, dim3(blocks), dim3(64 * kFwdWaves), lds, stream, a);
+    LLSA_LAUNCH("attn_fwd_kernel", attn_fwd_kernel<false>, dim3(blocks), dim3(64 * kFwdWaves), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -7,6 +7,19 @@
 
 namespace llsa {
 
+// Optional per-kernel timing (profile.cpp): events around each launch while enabled.
+bool profiling_enabled();
+void* prof_begin(const char* name, hipStream_t stream);
+void prof_end(void* handle, hipStream_t stream);
+
+#define LLSA_LAUNCH(name, kernel, grid, block, lds, stream, ...)                      \
+  do {                                                                                 \
+    void* prof_h_ = ::llsa::profiling_enabled() ? ::llsa::prof_begin(name, stream)     \
+                                                : nullptr;                             \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                 \
+    if (prof_h_) ::llsa::prof_end(prof_h_, stream);                                    \
+  } while (0)
+
 struct Shape {
   int bh;        // batch * heads
   int n;         // tokens per head

@@ -105,10 +105,10 @@ hipError_t launch_pool(const Shape& s, const void* const x[3], float* const* lv[
   const Grid grid{s.hbits, s.wbits, s.raster};
   const dim3 blocks((unsigned)(s.bh * groups_per_head), (unsigned)nt);
   if (s.bf16)
-    hipLaunchKernelGGL(pool12_kernel<true>, blocks, dim3(256), 0, stream, a, s.n, grid,
+    LLSA_LAUNCH("pool12_kernel", pool12_kernel<true>, blocks, dim3(256), 0, stream, a, s.n, grid,
                        groups_per_head);
   else
-    hipLaunchKernelGGL(pool12_kernel<false>, blocks, dim3(256), 0, stream, a, s.n, grid,
+    LLSA_LAUNCH("pool12_kernel", pool12_kernel<false>, blocks, dim3(256), 0, stream, a, s.n, grid,
                        groups_per_head);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -123,7 +123,7 @@ hipError_t launch_pool(const Shape& s, const void* const x[3], float* const* lv[
     }
     if (m == 0) continue;
     const long total = (long)s.bh * s.n_level(l) * kDim;
-    hipLaunchKernelGGL(pool_next_kernel, dim3((unsigned)((total + 255) / 256), (unsigned)m),
+    LLSA_LAUNCH("pool_next_kernel", pool_next_kernel, dim3((unsigned)((total + 255) / 256), (unsigned)m),
                        dim3(256), 0, stream, b, total);
     err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -45,7 +45,7 @@ hipError_t launch_reorder(const Shape& s, const void* x, void* y, int inverse,
   const long total = (long)s.bh * s.n << cpr_shift;
   const long per_block = (long)kReorderThreads * kChunksPerThread;
   const long blocks = (total + per_block - 1) / per_block;
-  hipLaunchKernelGGL(reorder_kernel, dim3((unsigned)blocks), dim3(kReorderThreads), 0, stream,
+  LLSA_LAUNCH("reorder_kernel", reorder_kernel, dim3((unsigned)blocks), dim3(kReorderThreads), 0, stream,
                      (const i32x4*)x, (i32x4*)y, s.n, s.hbits, s.wbits, cpr_shift, inverse,
                      total);
   return hipGetLastError();

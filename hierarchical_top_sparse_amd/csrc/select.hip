@@ -162,11 +162,11 @@ hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* 
     const unsigned blocks = (unsigned)((waves + kSelWaves - 1) / kSelWaves);
     const int32_t* parent = coarsest ? nullptr : sel[l];
     if (s.topk <= 8)
-      hipLaunchKernelGGL(select_kernel<8>, dim3(blocks), dim3(64 * kSelWaves), 0, stream,
+      LLSA_LAUNCH("select_kernel", select_kernel<8>, dim3(blocks), dim3(64 * kSelWaves), 0, stream,
                          q_lv[l - 1], k_lv[l - 1], parent, sel[l - 1], s.bh, n_l, s.topk,
                          (int)coarsest);
     else
-      hipLaunchKernelGGL(select_kernel<16>, dim3(blocks), dim3(64 * kSelWaves), 0, stream,
+      LLSA_LAUNCH("select_kernel", select_kernel<16>, dim3(blocks), dim3(64 * kSelWaves), 0, stream,
                          q_lv[l - 1], k_lv[l - 1], parent, sel[l - 1], s.bh, n_l, s.topk,
                          (int)coarsest);
     const hipError_t err = hipGetLastError();

@@ -1,0 +1,91 @@
+"""A preallocated LLSA training step (forward + backward) with optional HIP-graph replay.
+
+`Step` owns every intermediate of one fwd+bwd pass (pooled levels, selections, O, LSE, CSC
+indices, workspaces, gradients) for fixed shapes, and issues the C-ABI calls of a step in
+order.  `capture()` records the whole sequence into a HIP graph (torch.cuda.CUDAGraph on
+ROCm) so that replays do not wait on the host between calls; the library allocates nothing
+and never synchronises, and none of its calls records a memset, so the whole step can be
+captured.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _abi
+
+
+class Step:
+    def __init__(self, p: _abi.Problem, q, k, v, dout):
+        self.p = p
+        self.q, self.k, self.v, self.dout = q, k, v, dout
+        dev, f32 = q.device, torch.float32
+        L = p.levels
+        lv = lambda l: torch.empty((p.batch, p.heads, p.n_level(l), p.head_dim), device=dev,
+                                   dtype=f32)
+        self.q_lv = [lv(l) for l in range(1, L + 1)]
+        self.k_lv = [lv(l) for l in range(1, L + 1)]
+        self.v_lv = [None] + [lv(l) for l in range(2, L + 1)]
+        self.pool_v = bool(p.enrich) and L >= 2
+        self.sel = [torch.empty((p.batch, p.heads, p.n_level(l), p.topk), device=dev,
+                                dtype=torch.int32) for l in range(1, L + 1)]
+        self.o = torch.empty_like(q)
+        self.lse = torch.empty((p.batch, p.heads, p.n), device=dev, dtype=f32)
+        self.csc_levels = L if p.enrich else 1
+        self.off = [torch.empty((p.batch, p.heads, p.n_level(l) + 1), device=dev,
+                                dtype=torch.int32) for l in range(1, self.csc_levels + 1)]
+        self.rows = [torch.empty((p.batch, p.heads, p.n_level(l) * p.topk), device=dev,
+                                 dtype=torch.int32) for l in range(1, self.csc_levels + 1)]
+        self.nmat = p.batch * p.heads
+        tws = max(_abi.llsa_index_transpose_workspace(self.nmat, p.n_level(l), p.n_level(l),
+                                                      p.topk)
+                  for l in range(1, self.csc_levels + 1))
+        self.tws = torch.empty(tws, device=dev, dtype=torch.uint8)
+        _, bws = _abi.llsa_workspace_bytes(p)
+        self.bws = torch.empty(max(bws, 16), device=dev, dtype=torch.uint8)
+        self.dq, self.dk, self.dv = (torch.empty_like(q) for _ in range(3))
+        self.graph = None
+
+    def calls(self):
+        """(name, thunk) for every C-ABI call of one step, in order."""
+        a, p = _abi, self.p
+        out = [("pool", lambda: a.llsa_pool(p, self.q, self.k, self.v if self.pool_v else None,
+                                            self.q_lv, self.k_lv, self.v_lv)),
+               ("select", lambda: a.llsa_select(p, self.q_lv, self.k_lv, self.sel)),
+               ("attn_fwd", lambda: a.llsa_attn_fwd(p, self.q, self.k, self.v, self.k_lv,
+                                                    self.v_lv, self.sel, self.o, self.lse))]
+        for l in range(1, self.csc_levels + 1):
+            nl = p.n_level(l)
+            out.append((f"transpose_l{l}", (lambda l=l, nl=nl: a.llsa_index_transpose(
+                self.nmat, nl, nl, p.topk, self.sel[l - 1], self.off[l - 1], self.rows[l - 1],
+                self.tws))))
+        out.append(("attn_bwd", lambda: a.llsa_attn_bwd(
+            p, self.q, self.k, self.v, self.dout, self.lse, self.k_lv, self.v_lv, self.sel,
+            self.off, self.rows, self.dq, self.dk, self.dv, self.bws)))
+        return out
+
+    def run(self):
+        """One eager step on the current stream."""
+        for _, fn in self.calls():
+            fn()
+
+    def capture(self, warmup: int = 1):
+        """Record one step into a HIP graph (after `warmup` eager steps on a side stream)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(warmup):
+                self.run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        torch.cuda.synchronize()
+        self.graph = g
+        return g
+
+    def replay(self):
+        self.graph.replay()
+
+    def outputs(self):
+        return dict(o=self.o, lse=self.lse, dq=self.dq, dk=self.dk, dv=self.dv, sel=self.sel)

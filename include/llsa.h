@@ -172,6 +172,16 @@ int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const
                       const int32_t* const* csc_rows, void* dq, void* dk, void* dv, void* ws,
                       size_t ws_bytes, void* stream);
 
+/*
+ * Per-kernel timing (profiling aid, not part of the method).  llsa_profile_enable(1) makes
+ * every later kernel launch of the library record a pair of hipEvents on its stream;
+ * llsa_profile_read() waits for the recorded events, writes one line per kernel name,
+ * "<name> <launches> <total_ms>\n", into buf (NUL-terminated, truncated to len), and clears
+ * the records.  Returns LLSA_ERR_HIP if an event could not be read.  Thread-safe.
+ */
+int32_t llsa_profile_enable(int32_t on);
+int32_t llsa_profile_read(char* buf, size_t len);
+
 #ifdef __cplusplus
 }
 #endif
