@@ -10,9 +10,10 @@
 //  2. coarse_reduce_kernel / coarse_grad_kernel: partials of levels >= 3 are summed over the
 //     level-2 groups of each ancestor, then each coarse key j of level l gathers
 //     dK_l[j] = sum over the ancestors a in CSC_l[j] of the partial of a's slot holding j.
-//  3. bwd_key_kernel (key-major, one wave per level-1 key block): walks the query blocks in
-//     CSC_1[j] two at a time, accumulates dK, dV on the MFMA, and adds the pooled gradients
-//     pushed down to the block's tokens (dK_l[ancestor] / 16^l, chain rule of the mean).
+//  3. bwd_key_kernel (key-major, one one-wave workgroup per level-1 key block): walks the
+//     query blocks in CSC_1[j] two at a time, accumulates dK, dV on the MFMA, and adds the
+//     pooled gradients pushed down to the block's tokens (dK_l[ancestor] / 16^l, chain rule
+//     of the mean).
 //
 // MFMA data flow (bf16 16x16x32, fp32 accumulation): products that contract over head_dim
 // read row-major operands; products that contract over keys or queries read their row-major
@@ -147,8 +148,99 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
   bf16* cV = cK + 2 * kQStage;                // shared coarse V hi (+kQStage: lo)
   float* cbias = (float*)(cK + 4 * kQStage);
 
+  const uint32_t head_bytes = (uint32_t)a.n * kDim * 2;
+  const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rk = make_rsrc_uniform((const char*)a.k + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rdo =
+      make_rsrc_uniform((const char*)a.dout + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rl = make_rsrc_uniform(a.lse + tok_base, (uint32_t)a.n * 4);
+
+  // The wave's four query blocks pb_first + b, b = 0..3, form one stream of 4 * n_fine fine
+  // chunks; the loads of the next chunk are always issued before the current one is computed.
+  const int pb_first = a2 * kBlock + w * 4;
+  const int n_fine = (K + 1) >> 1;
+  // picks as a lane-held table: lane 16b + i holds the first-row byte offset of pick i of
+  // block b (kNoRow for i >= K and for an invalid id); chunks take them with v_readlane
+  uint32_t pick_off = kNoRow;
+  if ((lane & 15) < K) {
+    const int j = a.sel[0][((long)head * n1 + pb_first + (lane >> 4)) * K + (lane & 15)];
+    if (j >= 0 && j < n1) pick_off = (uint32_t)block_corner(j, a.grid) * kDim * 2;
+  }
+
+  // lane-constant byte offsets inside a 4x4 block: staged rows and A-operand rows
+  const int srow0 = lane >> 3;
+  const int piece = lane & 7;
+  uint32_t st_off[4];
+#pragma unroll
+  for (int ins = 0; ins < 4; ++ins)
+    st_off[ins] = (uint32_t)(tile_offset((ins * 8 + srow0) & 15, a.grid) * kDim * 2 + 16 * piece);
+  uint32_t va_off[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    va_off[t] = (uint32_t)(tile_offset(chunk_key(n, t) & 15, a.grid) * kDim * 2) + 16 * g;
+  const bool a_second = n >= 8;     // A rows 8..15 of both tiles come from the second block
+  const bool lane_second = g >= 2;  // this lane's 8 keys come from the second block
+
+  // rows of one query block: Q and dO as B operands (lane (n, g): row n, channels 32s + 8g..)
+  // and the row's LSE (natural log, as stored)
+  struct BlockLd {
+    bf16x8 q[2], d[2];
+    float lse;
+  };
+  auto load_block = [&](int b) -> BlockLd {
+    BlockLd r;
+    const int pb = pb_first + b;
+    const int qrow = block_corner(pb, a.grid) + tile_offset(n, a.grid);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      r.q[s] = buf_load8(rq, (uint32_t)(qrow * kDim + 32 * s + 8 * g) * 2);
+      r.d[s] = buf_load8(rdo, (uint32_t)(qrow * kDim + 32 * s + 8 * g) * 2);
+    }
+    r.lse = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)(pb * kBlock + n) * 4, 0, 0));
+    return r;
+  };
+
+  struct FineLd {
+    i32x4 k[4];      // staged K rows
+    i32x4 v[2][2];   // V rows as A operands of dP^T
+    int ok0, ok1;
+  };
+  int lb = 0, lch = 0;   // block and chunk of the next load (lb == 4: past the end)
+  // Every call issues the same loads, also past the last chunk (kNoRow: zeros, no memory
+  // access), so the wait before a chunk's use never drains the loads queued behind it.
+  auto load_next = [&]() -> FineLd {
+    FineLd f;
+    const int idx = min(16 * lb + 2 * lch, 62);
+    uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)pick_off, idx);
+    uint32_t b1 = (uint32_t)__builtin_amdgcn_readlane((int)pick_off, idx + 1);
+    if (lb >= 4) b0 = b1 = kNoRow;
+    f.ok0 = b0 != kNoRow;
+    f.ok1 = b1 != kNoRow;
+#pragma unroll
+    for (int ins = 0; ins < 4; ++ins)
+      f.k[ins] = __builtin_amdgcn_raw_buffer_load_b128(rk, (ins >= 2 ? b1 : b0) + st_off[ins],
+                                                       0, 0);
+    const uint32_t vb = a_second ? b1 : b0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        f.v[t][s] = __builtin_amdgcn_raw_buffer_load_b128(rv, vb + va_off[t] + 64 * s, 0, 0);
+    if (++lch == n_fine) {
+      lch = 0;
+      ++lb;
+    }
+    return f;
+  };
+
+  BlockLd cur = load_block(0), nxt;
+  FineLd fa = load_next(), fb;
+
   if (NST > 0) {
-    // ---- the group's coarse keys/values (all 256 queries of the level-2 group share them)
+    // ---- the group's coarse keys/values (all 256 queries of the level-2 group share them);
+    // their loads overlap the first chunk's
     const int pb0 = a2 * kBlock;
     const int e = threadIdx.x;             // 32 slots x 8 pieces of 8 channels
     const int slot = e >> 3;
@@ -181,34 +273,6 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
     __syncthreads();
   }
 
-  const uint32_t head_bytes = (uint32_t)a.n * kDim * 2;
-  const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
-  const rsrc_t rk = make_rsrc_uniform((const char*)a.k + (size_t)head * head_bytes, head_bytes);
-  const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
-  const rsrc_t rdo =
-      make_rsrc_uniform((const char*)a.dout + (size_t)head * head_bytes, head_bytes);
-
-  // lane-constant byte offsets inside a 4x4 block: staged rows and A-operand rows
-  const int srow0 = lane >> 3;
-  const int piece = lane & 7;
-  uint32_t st_off[4];
-#pragma unroll
-  for (int ins = 0; ins < 4; ++ins)
-    st_off[ins] = (uint32_t)(tile_offset((ins * 8 + srow0) & 15, a.grid) * kDim * 2 + 16 * piece);
-  uint32_t va_off[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-    va_off[t] = (uint32_t)(tile_offset(chunk_key(n, t) & 15, a.grid) * kDim * 2) + 16 * g;
-  const bool a_second = n >= 8;     // A rows 8..15 of both tiles come from the second block
-  const bool lane_second = g >= 2;  // this lane's 8 keys come from the second block
-  const int n_fine = (K + 1) >> 1;
-
-  struct FineLd {
-    i32x4 k[4];      // staged K rows
-    i32x4 v[2][2];   // V rows as A operands of dP^T
-    int ok0, ok1;
-  };
-
   f32x4 cpk[NST > 0 ? NST : 1][4];   // coarse partial dK (unscaled): [slot tile][d tile]
   f32x4 cpv[NST > 0 ? NST : 1][4];
 #pragma unroll
@@ -216,118 +280,78 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) cpk[st][t4] = cpv[st][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int it = 0; it < 4; ++it) {
-    const int pb = a2 * kBlock + w * 4 + it;
-    const int qcorner = block_corner(pb, a.grid);
-    const int qrow = qcorner + tile_offset(n, a.grid);
-    bf16x8 qh[2], dh[2];
+  // dQ = scale * sum_e P_e (dP_e - D) k_e = scale * (A - D * Bv) with A = sum P dP k and
+  // Bv = sum P k, so D = sum_e P_e dP_e is exact (no bf16 O) and one pass suffices.
+  f32x4 acc_a[4], acc_b[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      qh[s] = buf_load8(rq, (uint32_t)(qrow * kDim + 32 * s + 8 * g) * 2);
-      dh[s] = buf_load8(rdo, (uint32_t)(qrow * kDim + 32 * s + 8 * g) * 2);
-    }
-    const float lse2 = a.lse[tok_base + pb * kBlock + n] * kLog2e;
-    const int32_t* sel1 = a.sel[0] + ((long)head * n1 + pb) * K;
+  for (int t4 = 0; t4 < 4; ++t4) acc_a[t4] = acc_b[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dpart = 0.f;           // this lane's share of D
+  float pc[2][4], dpc[2][4];   // P and dP of the coarse chunk
 
-    auto load_fine = [&](int ch) -> FineLd {
-      FineLd f;
-      const int j0 = uniform(sel1[2 * ch]);
-      const int j1 = uniform((2 * ch + 1 < K) ? sel1[2 * ch + 1] : -1);
-      f.ok0 = j0 >= 0 && j0 < n1;
-      f.ok1 = j1 >= 0 && j1 < n1;
-      const uint32_t b0 = f.ok0 ? (uint32_t)block_corner(j0, a.grid) * kDim * 2 : kNoRow;
-      const uint32_t b1 = f.ok1 ? (uint32_t)block_corner(j1, a.grid) * kDim * 2 : kNoRow;
+  // P, P dP of one chunk from its S^T / dP^T tiles; A/B accumulation on the MFMA
+  auto absorb = [&](const f32x4 (&st)[2], const f32x4 (&dp)[2], const float (&add)[2][4],
+                    const bf16* kt_hi, const bf16* kt_lo, bool keep) {
+    float p[2][4], w1[2][4];
+    const float lse2 = cur.lse * kLog2e;
 #pragma unroll
-      for (int ins = 0; ins < 4; ++ins)
-        f.k[ins] = __builtin_amdgcn_raw_buffer_load_b128(rk, (ins >= 2 ? b1 : b0) + st_off[ins],
-                                                         0, 0);
-      const uint32_t vb = a_second ? b1 : b0;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          f.v[t][s] = __builtin_amdgcn_raw_buffer_load_b128(rv, vb + va_off[t] + 64 * s, 0, 0);
-      return f;
-    };
-
-    // dQ = scale * sum_e P_e (dP_e - D) k_e = scale * (A - D * Bv) with A = sum P dP k and
-    // Bv = sum P k, so D = sum_e P_e dP_e is exact (no bf16 O) and one pass suffices.
-    f32x4 acc_a[4], acc_b[4];
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) acc_a[t4] = acc_b[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float dpart = 0.f;           // this lane's share of D
-    float pc[2][4], dpc[2][4];   // P and dP of the coarse chunk
-
-    // P, P dP of one chunk from its S^T / dP^T tiles; A/B accumulation on the MFMA
-    auto absorb = [&](const f32x4 (&st)[2], const f32x4 (&dp)[2], const float (&add)[2][4],
-                      const bf16* kt_hi, const bf16* kt_lo, bool keep) {
-      float p[2][4], w1[2][4];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(fmaf(st[t][i], a.c2, add[t][i] - lse2));
-          p[t][i] = pv;
-          w1[t][i] = pv * dp[t][i];
-          dpart += w1[t][i];
-          if (keep) {
-            pc[t][i] = pv;
-            dpc[t][i] = dp[t][i];
-          }
-        }
-      bf16x8 a_hi, a_lo, b_hi, b_lo;
-      split8(w1, a_hi, a_lo);
-      split8(p, b_hi, b_lo);
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const bf16x8 kt = lds_tr8(kt_hi, t4, lane);
-        acc_a[t4] = mfma_bf16_k32(kt, a_hi, acc_a[t4]);
-        acc_a[t4] = mfma_bf16_k32(kt, a_lo, acc_a[t4]);
-        acc_b[t4] = mfma_bf16_k32(kt, b_hi, acc_b[t4]);
-        acc_b[t4] = mfma_bf16_k32(kt, b_lo, acc_b[t4]);
-        if (kt_lo) {
-          const bf16x8 ktl = lds_tr8(kt_lo, t4, lane);
-          acc_a[t4] = mfma_bf16_k32(ktl, a_hi, acc_a[t4]);
-          acc_b[t4] = mfma_bf16_k32(ktl, b_hi, acc_b[t4]);
+      for (int i = 0; i < 4; ++i) {
+        const float pv = fast_exp2(fmaf(st[t][i], a.c2, add[t][i] - lse2));
+        p[t][i] = pv;
+        w1[t][i] = pv * dp[t][i];
+        dpart += w1[t][i];
+        if (keep) {
+          pc[t][i] = pv;
+          dpc[t][i] = dp[t][i];
         }
       }
-    };
-
-    auto fine_chunk = [&](const FineLd& f) {
+    bf16x8 a_hi, a_lo, b_hi, b_lo;
+    split8(w1, a_hi, a_lo);
+    split8(p, b_hi, b_lo);
 #pragma unroll
-      for (int ins = 0; ins < 4; ++ins)
-        *(i32x4*)(stK + (ins * 8 + srow0) * kStride + 8 * piece) = f.k[ins];
-      wave_lds_sync();
-      f32x4 st[2], dp[2];
-      float add[2][4];
-      const float madd = (lane_second ? f.ok1 : f.ok0) ? 0.f : -INFINITY;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int arow = chunk_key(n, t);
-        st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        st[t] = mfma_bf16_k32(lds_row8(stK, arow, 0, g), qh[0], st[t]);
-        st[t] = mfma_bf16_k32(lds_row8(stK, arow, 1, g), qh[1], st[t]);
-        dp[t] = mfma_bf16_k32(*(const bf16x8*)&f.v[t][0], dh[0], dp[t]);
-        dp[t] = mfma_bf16_k32(*(const bf16x8*)&f.v[t][1], dh[1], dp[t]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) add[t][i] = madd;
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const bf16x8 kt = lds_tr8(kt_hi, t4, lane);
+      acc_a[t4] = mfma_bf16_k32(kt, a_hi, acc_a[t4]);
+      acc_a[t4] = mfma_bf16_k32(kt, a_lo, acc_a[t4]);
+      acc_b[t4] = mfma_bf16_k32(kt, b_hi, acc_b[t4]);
+      acc_b[t4] = mfma_bf16_k32(kt, b_lo, acc_b[t4]);
+      if (kt_lo) {
+        const bf16x8 ktl = lds_tr8(kt_lo, t4, lane);
+        acc_a[t4] = mfma_bf16_k32(ktl, a_hi, acc_a[t4]);
+        acc_b[t4] = mfma_bf16_k32(ktl, b_hi, acc_b[t4]);
       }
-      absorb(st, dp, add, stK, nullptr, false);
-      wave_lds_sync();
-    };
-
-    // ---- fine chunks: two load buffers used in turn, each refilled while the other computes
-    FineLd fa = load_fine(0), fb;
-    for (int ch = 0; ch < n_fine; ch += 2) {
-      if (ch + 1 < n_fine) fb = load_fine(ch + 1);
-      fine_chunk(fa);
-      if (ch + 1 >= n_fine) break;
-      if (ch + 2 < n_fine) fa = load_fine(ch + 2);
-      fine_chunk(fb);
     }
+  };
 
-    // ---- the coarse chunk, from the workgroup's LDS copy
+  auto fine_chunk = [&](const FineLd& f) {
+#pragma unroll
+    for (int ins = 0; ins < 4; ++ins)
+      *(i32x4*)(stK + (ins * 8 + srow0) * kStride + 8 * piece) = f.k[ins];
+    wave_lds_sync();
+    f32x4 st[2], dp[2];
+    float add[2][4];
+    const float madd = (lane_second ? f.ok1 : f.ok0) ? 0.f : -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int arow = chunk_key(n, t);
+      st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st[t] = mfma_bf16_k32(lds_row8(stK, arow, 0, g), cur.q[0], st[t]);
+      st[t] = mfma_bf16_k32(lds_row8(stK, arow, 1, g), cur.q[1], st[t]);
+      dp[t] = mfma_bf16_k32(*(const bf16x8*)&f.v[t][0], cur.d[0], dp[t]);
+      dp[t] = mfma_bf16_k32(*(const bf16x8*)&f.v[t][1], cur.d[1], dp[t]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) add[t][i] = madd;
+    }
+    absorb(st, dp, add, stK, nullptr, false);
+    wave_lds_sync();
+  };
+
+  // the end of query block b: its coarse chunk, D, dQ and its share of the coarse partials
+  auto block_end = [&](int b) {
+    const int pb = pb_first + b;
+    const int qrow = block_corner(pb, a.grid) + tile_offset(n, a.grid);
     if (NST > 0) {
       f32x4 st[2], dp[2];
       float add[2][4];
@@ -338,10 +362,10 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
         dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          st[t] = mfma_bf16_k32(lds_row8(cK, arow, s, g), qh[s], st[t]);
-          st[t] = mfma_bf16_k32(lds_row8(cK + kQStage, arow, s, g), qh[s], st[t]);
-          dp[t] = mfma_bf16_k32(lds_row8(cV, arow, s, g), dh[s], dp[t]);
-          dp[t] = mfma_bf16_k32(lds_row8(cV + kQStage, arow, s, g), dh[s], dp[t]);
+          st[t] = mfma_bf16_k32(lds_row8(cK, arow, s, g), cur.q[s], st[t]);
+          st[t] = mfma_bf16_k32(lds_row8(cK + kQStage, arow, s, g), cur.q[s], st[t]);
+          dp[t] = mfma_bf16_k32(lds_row8(cV, arow, s, g), cur.d[s], dp[t]);
+          dp[t] = mfma_bf16_k32(lds_row8(cV + kQStage, arow, s, g), cur.d[s], dp[t]);
         }
         const f32x4 b4 = *(const f32x4*)(cbias + 8 * g + 4 * t);
 #pragma unroll
@@ -364,23 +388,14 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
 
     if (NST > 0) {
       // ---- coarse partials over this block's 16 queries: dV_c += P^T dO, dK_c += dS^T Q,
-      // with dS = P (dP - D).  The staging tile now holds the block's Q rows (0..15) and dO
-      // rows (16..31).
+      // with dS = P (dP - D).  The staging tile takes the block's Q rows (0..15) and dO rows
+      // (16..31) from the B-operand registers (lane (n, g) holds row n, channels 32s + 8g..).
       bf16* stQ = stK;
       bf16* stO = stK + 16 * kStride;
-      {
-        const int row = lane >> 2;            // 16 rows, 4 lanes x 32 bytes each
-        const int part = (lane & 3) * 16;
-        const uint32_t off =
-            (uint32_t)((qcorner + tile_offset(row, a.grid)) * kDim + part) * 2;
-        const i32x4 q0 = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-        const i32x4 q1 = __builtin_amdgcn_raw_buffer_load_b128(rq, off + 16, 0, 0);
-        const i32x4 d0 = __builtin_amdgcn_raw_buffer_load_b128(rdo, off, 0, 0);
-        const i32x4 d1 = __builtin_amdgcn_raw_buffer_load_b128(rdo, off + 16, 0, 0);
-        *(i32x4*)(stQ + row * kStride + part) = q0;
-        *(i32x4*)(stQ + row * kStride + part + 8) = q1;
-        *(i32x4*)(stO + row * kStride + part) = d0;
-        *(i32x4*)(stO + row * kStride + part + 8) = d1;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        *(bf16x8*)(stQ + n * kStride + 32 * s + 8 * g) = cur.q[s];
+        *(bf16x8*)(stO + n * kStride + 32 * s + 8 * g) = cur.d[s];
       }
       bf16* pH = stP;
       bf16* pL = stP + 512;
@@ -421,6 +436,28 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
       }
       wave_lds_sync();
     }
+    dpart = 0.f;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) acc_a[t4] = acc_b[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  // one step of the stream: (next block's rows,) next chunk's loads, then chunk `f`; returns
+  // false after the last block.  Two call sites alternate the load buffers (no copies).
+  int cb = 0, cch = 0;   // block and chunk being computed
+  auto step = [&](const FineLd& f, FineLd& refill) -> bool {
+    // the next block's rows are loaded before the chunk loads so that waiting for them
+    // (conditional loads) never drains the chunk prefetch
+    if (lch == 0 && lb > 0 && lb < 4) nxt = load_block(lb);
+    refill = load_next();
+    fine_chunk(f);
+    if (++cch < n_fine) return true;
+    block_end(cb);
+    cch = 0;
+    if (++cb == 4) return false;
+    cur = nxt;
+    return true;
+  };
+  while (step(fa, fb) && step(fb, fa)) {
   }
 
   if (NST > 0) {
@@ -528,21 +565,20 @@ __global__ __launch_bounds__(256) void coarse_grad_kernel(BwdArgs a, int l) {
 }
 
 // ====================================================================== stage 3: key-major
-__global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 sQ[4][32 * kStride];
-  __shared__ __attribute__((aligned(16))) bf16 sO[4][32 * kStride];   // dO rows
-  const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
+// One wave per workgroup: key blocks differ widely in how many query blocks picked them, so a
+// wave that finishes early frees its slot at once.
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_kernel(
+    BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 stQ[32 * kStride];
+  __shared__ __attribute__((aligned(16))) bf16 stO[32 * kStride];   // dO rows
+  const int lane = threadIdx.x;
   const int n = lane & 15;
   const int g = lane >> 4;
   const int n1 = a.n >> kBlockShift;
-  // every workgroup holds 4 whole key blocks of one head (N / 16 is a multiple of 4)
-  const int kb = uniform(xcd_block(blockIdx.x, gridDim.x) * 4) + w;
+  const int kb = uniform(xcd_block(blockIdx.x, gridDim.x));
   const int head = uniform(kb / n1);
   const int j = uniform(kb - head * n1);
   const long tok_base = (long)head * a.n;
-  bf16* stQ = sQ[w];
-  bf16* stO = sO[w];
 
   const uint32_t head_bytes = (uint32_t)a.n * kDim * 2;
   const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
@@ -581,25 +617,35 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     f32x4 l4[2], d4[2];  // lse and D of this lane's queries (tile t: tokens 8g+4t .. +3)
     int okA, okB;
   };
-  auto load_pair = [&](int e) -> PairLd {
+  // The query blocks of CSC_1[j] in batches of 64: lane i holds entry base + i as the byte
+  // offset of its first Q/dO row (qtab) and of its first LSE/D value (ttab), kNoRow past the
+  // batch or for an invalid id.  Pairs take them with v_readlane.
+  uint32_t qtab = kNoRow, ttab = kNoRow;
+  int cnt = 0;
+  // Pair k of the batch (entries 2k, 2k+1).  Every call issues the same loads, also past the
+  // batch end (kNoRow: zeros, no memory access), so waiting for a pair never drains the
+  // prefetch queued behind it.
+  auto load_pair = [&](int k) -> PairLd {
     PairLd f;
-    const int pA = uniform(rows[e]);
-    const int pB = uniform(e + 1 < e1 ? rows[e + 1] : -1);
-    f.okA = pA >= 0 && pA < n1;
-    f.okB = pB >= 0 && pB < n1;
-    const uint32_t bA = f.okA ? (uint32_t)block_corner(pA, a.grid) * kDim * 2 : kNoRow;
-    const uint32_t bB = f.okB ? (uint32_t)block_corner(pB, a.grid) * kDim * 2 : kNoRow;
+    const int idx = min(2 * k, 62);
+    uint32_t bA = (uint32_t)__builtin_amdgcn_readlane((int)qtab, idx);
+    uint32_t bB = (uint32_t)__builtin_amdgcn_readlane((int)qtab, idx + 1);
+    uint32_t tA = (uint32_t)__builtin_amdgcn_readlane((int)ttab, idx);
+    uint32_t tB = (uint32_t)__builtin_amdgcn_readlane((int)ttab, idx + 1);
+    if (2 * k >= cnt) bA = tA = kNoRow;
+    if (2 * k + 1 >= cnt) bB = tB = kNoRow;
+    f.okA = bA != kNoRow;
+    f.okB = bB != kNoRow;
 #pragma unroll
     for (int ins = 0; ins < 4; ++ins) {
       const uint32_t o = (ins >= 2 ? bB : bA) + st_off[ins];
       f.q[ins] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
       f.d[ins] = __builtin_amdgcn_raw_buffer_load_b128(rdo, o, 0, 0);
     }
-    const bool okl = lane_second ? f.okB : f.okA;
-    const int pl = lane_second ? pB : pA;
+    const uint32_t tl = lane_second ? tB : tA;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint32_t o = okl ? (uint32_t)(pl * kBlock + ((8 * g + 4 * t) & 15)) * 4 : kNoRow;
+      const uint32_t o = tl + (uint32_t)(((8 * g + 4 * t) & 15) * 4);
       f.l4[t] = buf_load4f(rl, o);
       f.d4[t] = buf_load4f(rd, o);
     }
@@ -652,13 +698,23 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   };
 
   // ---- query-block pairs of CSC_1[j]: two load buffers used in turn
-  if (e0 < e1) {
-    PairLd fa = load_pair(e0), fb;
-    for (int e = e0; e < e1; e += 4) {
-      if (e + 2 < e1) fb = load_pair(e + 2);
+  for (int base = e0; base < e1; base += 64) {
+    cnt = min(64, e1 - base);
+    qtab = ttab = kNoRow;
+    if (lane < cnt) {
+      const int p = rows[base + lane];
+      if (p >= 0 && p < n1) {
+        qtab = (uint32_t)block_corner(p, a.grid) * kDim * 2;
+        ttab = (uint32_t)p * kBlock * 4;
+      }
+    }
+    const int npairs = (cnt + 1) >> 1;
+    PairLd fa = load_pair(0), fb;
+    for (int k = 0; k < npairs; k += 2) {
+      fb = load_pair(k + 1);
       pair(fa);
-      if (e + 2 >= e1) break;
-      if (e + 4 < e1) fa = load_pair(e + 4);
+      if (k + 1 >= npairs) break;
+      fa = load_pair(k + 2);
       pair(fb);
     }
   }
@@ -812,7 +868,7 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
     }
   }
   const long kwaves = (long)s.bh * (s.n >> kBlockShift);
-  LLSA_LAUNCH("bwd_key_kernel", bwd_key_kernel, dim3((unsigned)(kwaves / 4)), dim3(256), 0, stream, a);
+  LLSA_LAUNCH("bwd_key_kernel", bwd_key_kernel, dim3((unsigned)kwaves), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

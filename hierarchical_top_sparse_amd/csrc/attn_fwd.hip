@@ -3,10 +3,12 @@
 //
 // One wave owns one level-1 query block p (16 queries); a workgroup holds the 4 consecutive
 // blocks of one 8x8-pixel tile, which share their ancestors at every level >= 2.
-//  * Fine keys: the 16 tokens of each pair of blocks in Sel_1[p] form a 32-key chunk.  Block
-//    ids are wave-uniform (scalar registers); every lane's row offset inside a 4x4 tile is a
-//    constant, so a chunk's 16-byte loads need one add each.  The next chunk's loads are issued
-//    before the current chunk is computed (register double buffering).
+//  * Fine keys: the 16 tokens of each pair of blocks in Sel_1[p] form a 32-key chunk.  The
+//    picks' first-row offsets are computed once into a lane-held table and taken into scalar
+//    registers with v_readlane; every lane's row offset inside a 4x4 tile is a constant, so a
+//    chunk's 16-byte loads need one add each.  The next chunk's loads are always issued before
+//    the current chunk is computed (register double buffering, no data-dependent branch around
+//    the prefetch, so the wait for a chunk never drains the loads queued behind it).
 //  * Coarse keys: the keys Sel_l[p / 16^(l-1)], l = 2..L, are staged once per workgroup in LDS
 //    (fp32 pooled values split into bf16 hi + lo parts, so the MFMA sees them at ~16 bits),
 //    together with each slot's log2-domain weight bias 4l (weight 16^l).
@@ -103,7 +105,80 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(FwdArgs a) {
   T* cstage = (T*)smem + kFwdWaves * C::kChunkElems;
   float* cbias = (float*)(cstage + n_cchunks * C::NB * C::kChunkElems);
 
-  // ---- the workgroup's coarse keys and values, shared by its four query blocks
+  const uint32_t head_bytes = (uint32_t)a.n * kDim * C::ES;
+  const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rk = make_rsrc_uniform((const char*)a.k + (size_t)head * head_bytes, head_bytes);
+  const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
+
+  // ---- the picks of Sel_1[p] as a lane-held table: lane i < K holds the byte offset of pick
+  // i's first row (kNoRow for an invalid id and for lanes >= K); chunks read it by v_readlane.
+  const int32_t* sel1 = a.sel[0] + ((long)head * n1 + pb) * K;
+  uint32_t pick_off = kNoRow;
+  if (lane < K) {
+    const int j = sel1[lane];
+    if (j >= 0 && j < n1) pick_off = (uint32_t)block_corner(j, a.grid) * kDim * C::ES;
+  }
+
+  // ---- queries: B operand of S^T
+  const int qrow = block_corner(pb, a.grid) + tile_offset(n, a.grid);
+  bf16x8 qh[2];
+  f32x4 qf[4];
+  if constexpr (BF16) {
+    qh[0] = buf_load8(rq, (uint32_t)(qrow * kDim + 8 * g) * 2);
+    qh[1] = buf_load8(rq, (uint32_t)(qrow * kDim + 32 + 8 * g) * 2);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qf[c] = buf_load4f(rq, (uint32_t)(qrow * kDim + 16 * g + 4 * c) * 4);
+  }
+
+  // ---- lane-constant byte offsets inside a block: staged rows and A-operand rows
+  const int srow0 = lane / C::PPR;
+  const int piece = lane % C::PPR;
+  uint32_t st_off[C::NINS];
+#pragma unroll
+  for (int ins = 0; ins < C::NINS; ++ins)
+    st_off[ins] = (uint32_t)(tile_offset((ins * C::RPI + srow0) & 15, a.grid) * kDim * C::ES +
+                             16 * piece);
+  uint32_t ka_off[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+    ka_off[t] = (uint32_t)(tile_offset(tile_row_key(n, t) & 15, a.grid) * kDim * C::ES) +
+                (BF16 ? 16 * g : 64 * g);
+  const bool ka_second = n >= 8;    // A rows 8..15 of both tiles come from the second block
+  const bool lane_second = g >= 2;  // this lane's 8 keys come from the second block
+  const int n_fine = (K + 1) >> 1;
+
+  // loads of fine chunk ch (blocks 2ch, 2ch+1 of the table), issued one chunk ahead of use.
+  // Every call issues the same loads, also past the last chunk (kNoRow: zeros, no memory
+  // access), so the wait before a chunk's use never has to drain the prefetch behind it.
+  struct FineLd {
+    i32x4 v[C::NINS];
+    i32x4 k[2][C::KLD];
+    int ok0, ok1;
+  };
+  auto load_fine = [&](int ch) -> FineLd {
+    FineLd f;
+    const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)pick_off, 2 * ch);
+    const uint32_t b1 = (uint32_t)__builtin_amdgcn_readlane((int)pick_off, 2 * ch + 1);
+    f.ok0 = b0 != kNoRow;
+    f.ok1 = b1 != kNoRow;
+#pragma unroll
+    for (int ins = 0; ins < C::NINS; ++ins)
+      f.v[ins] = __builtin_amdgcn_raw_buffer_load_b128(rv, (ins * C::RPI >= 16 ? b1 : b0) +
+                                                           st_off[ins], 0, 0);
+    const uint32_t kb = ka_second ? b1 : b0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int c = 0; c < C::KLD; ++c)
+        f.k[t][c] = __builtin_amdgcn_raw_buffer_load_b128(
+            rk, kb + ka_off[t] + (BF16 ? 64 * c : 16 * c), 0, 0);
+    return f;
+  };
+  FineLd fa = load_fine(0), fb;
+
+  // ---- the workgroup's coarse keys and values, shared by its four query blocks (their loads
+  // overlap the first fine chunk's)
   if (n_coarse > 0) {
     const int pb0 = pb & ~(kFwdWaves - 1);
     for (int e = threadIdx.x; e < n_cchunks * 32 * 8; e += 64 * kFwdWaves) {
@@ -145,70 +220,6 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(FwdArgs a) {
     }
     __syncthreads();
   }
-
-  const uint32_t head_bytes = (uint32_t)a.n * kDim * C::ES;
-  const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
-  const rsrc_t rk = make_rsrc_uniform((const char*)a.k + (size_t)head * head_bytes, head_bytes);
-  const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
-
-  // ---- queries: B operand of S^T
-  const int qrow = block_corner(pb, a.grid) + tile_offset(n, a.grid);
-  bf16x8 qh[2];
-  f32x4 qf[4];
-  if constexpr (BF16) {
-    qh[0] = buf_load8(rq, (uint32_t)(qrow * kDim + 8 * g) * 2);
-    qh[1] = buf_load8(rq, (uint32_t)(qrow * kDim + 32 + 8 * g) * 2);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qf[c] = buf_load4f(rq, (uint32_t)(qrow * kDim + 16 * g + 4 * c) * 4);
-  }
-
-  // ---- lane-constant byte offsets inside a block: staged rows and A-operand rows
-  const int srow0 = lane / C::PPR;
-  const int piece = lane % C::PPR;
-  uint32_t st_off[C::NINS];
-#pragma unroll
-  for (int ins = 0; ins < C::NINS; ++ins)
-    st_off[ins] = (uint32_t)(tile_offset((ins * C::RPI + srow0) & 15, a.grid) * kDim * C::ES +
-                             16 * piece);
-  uint32_t ka_off[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-    ka_off[t] = (uint32_t)(tile_offset(tile_row_key(n, t) & 15, a.grid) * kDim * C::ES) +
-                (BF16 ? 16 * g : 64 * g);
-  const bool ka_second = n >= 8;    // A rows 8..15 of both tiles come from the second block
-  const bool lane_second = g >= 2;  // this lane's 8 keys come from the second block
-
-  const int32_t* sel1 = a.sel[0] + ((long)head * n1 + pb) * K;
-  const int n_fine = (K + 1) >> 1;
-
-  // loads of one fine chunk (issued ahead of use)
-  struct FineLd {
-    i32x4 v[C::NINS];
-    i32x4 k[2][C::KLD];
-    int ok0, ok1;
-  };
-  auto load_fine = [&](int ch) -> FineLd {
-    FineLd f;
-    const int j0 = uniform(sel1[2 * ch]);
-    const int j1 = uniform((2 * ch + 1 < K) ? sel1[2 * ch + 1] : -1);
-    f.ok0 = j0 >= 0 && j0 < n1;
-    f.ok1 = j1 >= 0 && j1 < n1;
-    const uint32_t b0 = f.ok0 ? (uint32_t)block_corner(j0, a.grid) * kDim * C::ES : kNoRow;
-    const uint32_t b1 = f.ok1 ? (uint32_t)block_corner(j1, a.grid) * kDim * C::ES : kNoRow;
-#pragma unroll
-    for (int ins = 0; ins < C::NINS; ++ins)
-      f.v[ins] = __builtin_amdgcn_raw_buffer_load_b128(rv, (ins * C::RPI >= 16 ? b1 : b0) +
-                                                           st_off[ins], 0, 0);
-    const uint32_t kb = ka_second ? b1 : b0;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int c = 0; c < C::KLD; ++c)
-        f.k[t][c] = __builtin_amdgcn_raw_buffer_load_b128(
-            rk, kb + ka_off[t] + (BF16 ? 64 * c : 16 * c), 0, 0);
-    return f;
-  };
 
   float m_run = kMinusBig;   // running max (log2 domain) of query n
   float l_run = 0.f;         // this lane's partial sum of exp2
@@ -313,12 +324,11 @@ __global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(FwdArgs a) {
   };
 
   // ---- fine chunks: two load buffers used in turn, each refilled while the other computes
-  FineLd fa = load_fine(0), fb;
   for (int ch = 0; ch < n_fine; ch += 2) {
-    if (ch + 1 < n_fine) fb = load_fine(ch + 1);
+    fb = load_fine(ch + 1);
     fine_chunk(fa);
     if (ch + 1 >= n_fine) break;
-    if (ch + 2 < n_fine) fa = load_fine(ch + 2);
+    fa = load_fine(ch + 2);
     fine_chunk(fb);
   }
 
