@@ -1,26 +1,24 @@
 // Sparse attention forward with hierarchical KV enrichment (paper summary sec. 四; article
 // sec. 三/四: the forward gathers the selected key blocks directly, no dense mask).
 //
-// One wave owns one level-1 query block p (16 queries); a workgroup holds the 4 consecutive
-// blocks of one 8x8-pixel tile, which share their ancestors at every level >= 2.
-//  * Fine keys: the 16 tokens of each pair of blocks in Sel_1[p] form a 32-key chunk.  The
-//    picks' first-row offsets are computed once into a lane-held table and taken into scalar
-//    registers with v_readlane; every lane's row offset inside a 4x4 tile is a constant, so a
-//    chunk's 16-byte loads need one add each.  The next chunk's loads are always issued before
-//    the current chunk is computed (register double buffering, no data-dependent branch around
-//    the prefetch, so the wait for a chunk never drains the loads queued behind it).
-//  * Coarse keys: the keys Sel_l[p / 16^(l-1)], l = 2..L, are staged once per workgroup in LDS
-//    (fp32 pooled values split into bf16 hi + lo parts, so the MFMA sees them at ~16 bits),
-//    together with each slot's log2-domain weight bias 4l (weight 16^l).
-//
-// Orientation S^T = K Q^T: the MFMA result gives lane (n, g) the scores of query n against
-// keys 8g..8g+7 of the chunk (two 16x16 tiles whose rows are interleaved so that this holds),
-// so the online-softmax max needs two cross-lane steps and the exponentials already sit in
-// the B-operand layout of O^T += V^T P^T.  V^T comes from V rows staged row-major in LDS and
-// read with ds_read_b64_tr_b16.  fp32 online softmax in the exp2 domain.
-// fp32 tensors use v_mfma_f32_16x16x4f32 with the same data flow.
-// Workgroups are renumbered so that each XCD (and its L2) works on one contiguous spatial
-// range of query blocks: neighbouring blocks select overlapping key blocks.
+// One workgroup owns one level-2 group (the 16 level-1 query blocks of a 16x16-pixel tile,
+// which share their ancestors and so their coarse keys); each of its 4 waves owns 4
+// consecutive query blocks and works on its own, without workgroup barriers:
+//  1. its 4 K picks are ranked in LDS (keys (id, owner)) into the ascending list U of distinct
+//     key blocks, with a 4-bit mask per entry of the blocks that picked it.  Neighbouring query
+//     blocks choose among the same candidates, so U is much shorter than 4 K;
+//  2. the wave streams U: each key block's 16 K rows and 16 V rows are loaded row-major (each
+//     4-lane quad reads 64 contiguous bytes: the vector memory pipeline charges a quad per
+//     distinct cache line, so MFMA-operand-shaped loads cost 4x as much), two blocks ahead of
+//     use in registers, and staged in the wave's LDS tile;
+//  3. for every block of U, each of the wave's query blocks that picked it gets one 16 x 16
+//     tile: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (lane (n, g): scores of query n against
+//     keys 4g..4g+3, the B-operand layout of the next product), online softmax, and
+//     O^T += V^T P^T on v_mfma_f32_16x16x16_bf16 with V^T read by ds_read_b64_tr_b16;
+//  4. the coarse keys Sel_l[ancestor], l = 2..L, staged once per workgroup in LDS (fp32 pooled
+//     values as bf16 hi + lo parts, weight 16^l as the log2-domain bias 4l), then O and LSE.
+// fp32 tensors use v_mfma_f32_16x16x4f32 with the same data flow.  Workgroups are renumbered
+// so that each XCD (and its L2) works on one contiguous spatial range of level-2 groups.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -50,9 +48,6 @@ struct FwdArgs {
   float c2;   // scale * log2(e)
 };
 
-// Row of chunk position kk within S^T tile t: tile row r <-> kk = 8*(r/4) + r%4 + 4t.
-__device__ __forceinline__ int tile_row_key(int r, int t) { return 8 * (r >> 2) + (r & 3) + 4 * t; }
-
 __device__ __forceinline__ void split_bf16(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -64,327 +59,344 @@ __device__ __forceinline__ void split_bf16(f32x4 a, f32x4 b, bf16x8& hi, bf16x8&
   }
 }
 
+constexpr int kWavePicks = 64;     // 4 query blocks x K (K <= 16)
+constexpr int kSentinel = 0x7f000000;
+
 template <bool BF16>
 struct FwdCfg {
-  static constexpr int ES = BF16 ? 2 : 4;              // element bytes
+  static constexpr int ES = BF16 ? 2 : 4;               // element bytes
   static constexpr int kStride = BF16 ? kStrideBf16 : kStrideF32;
-  static constexpr int PPR = kDim * ES / 16;           // 16-byte pieces per row
-  static constexpr int RPI = 64 / PPR;                 // rows staged per load instruction
-  static constexpr int NINS = 32 / RPI;                // load instructions per 32-row chunk
-  static constexpr int KLD = BF16 ? 2 : 4;             // 16-byte loads per A-operand row
-  static constexpr int NB = BF16 ? 4 : 2;              // coarse buffers: K(hi,lo), V(hi,lo)
-  static constexpr int kChunkElems = 32 * kStride;
+  static constexpr int kRowBytes = kDim * ES;
+  static constexpr int PPR = kRowBytes / 16;            // 16-byte pieces per row
+  static constexpr int kTile = 16 * kStride;            // one 16-row tile (elements)
+  static constexpr int NB = BF16 ? 4 : 2;               // coarse buffers: K(hi,lo), V(hi,lo)
+  static constexpr int kBlockPieces = 16 * PPR;         // pieces of one block's rows per tensor
+  static constexpr int kLoads = kBlockPieces / 64;      // row-major loads per lane per tensor
 };
 
+// Dynamic LDS: per wave a K/V tile pair and its pick lists; per workgroup the coarse tiles
+// [ctiles][NB][16][stride] and their biases.
+__host__ __device__ constexpr int fwd_wave_lds_bytes(bool bf16) {
+  return 2 * 16 * (bf16 ? kStrideBf16 * 2 : kStrideF32 * 4) + (int)sizeof(int) * 4 * kWavePicks;
+}
 static size_t fwd_lds_bytes(bool bf16, int n_coarse) {
   const int es = bf16 ? 2 : 4;
   const int stride = bf16 ? kStrideBf16 : kStrideF32;
   const int nb = bf16 ? 4 : 2;
-  const int cchunks = (n_coarse + 31) / 32;
-  return (size_t)es * 32 * stride * (kFwdWaves + cchunks * nb) + sizeof(float) * 32 * cchunks;
+  const int ctiles = (n_coarse + 15) / 16;
+  return kFwdWaves * fwd_wave_lds_bytes(bf16) + (size_t)ctiles * nb * 16 * stride * es +
+         sizeof(float) * 16 * ctiles;
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(64 * kFwdWaves) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 2)))
+void attn_fwd_kernel(FwdArgs a) {
   using C = FwdCfg<BF16>;
   typedef typename std::conditional<BF16, bf16, float>::type T;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
-  const int n1 = a.n >> kBlockShift;
-  const int qb = uniform(xcd_block(blockIdx.x, gridDim.x) * kFwdWaves) + w;
-  const int head = uniform(qb / n1);   // scalar: buffer descriptors must be wave-uniform
-  const int pb = uniform(qb - head * n1);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
+  const int n1 = a.n >> kBlockShift;
+  const int n2 = n1 >> kBlockShift;
+  const int wg = uniform(xcd_block(blockIdx.x, gridDim.x));
+  const int head = uniform(wg / n2);   // scalar: buffer descriptors must be wave-uniform
+  const int a2 = uniform(wg - head * n2);
   const int K = a.topk;
   const long tok_base = (long)head * a.n;
   const int n_coarse = a.enrich ? (a.levels - 1) * K : 0;
-  const int n_cchunks = (n_coarse + 31) >> 5;
-  T* stage = (T*)smem + w * C::kChunkElems;
-  T* cstage = (T*)smem + kFwdWaves * C::kChunkElems;
-  float* cbias = (float*)(cstage + n_cchunks * C::NB * C::kChunkElems);
+  const int ctiles = (n_coarse + 15) >> 4;
 
-  const uint32_t head_bytes = (uint32_t)a.n * kDim * C::ES;
+  char* wbase = smem + w * fwd_wave_lds_bytes(BF16);
+  T* kt = (T*)wbase;                          // the staged key block: K rows, then V rows
+  T* vt = kt + C::kTile;
+  int* keys = (int*)(vt + C::kTile);          // [64] pick keys (id << 8 | index)
+  int* sorted = keys + kWavePicks;            // [64] ascending
+  int* uoff = sorted + kWavePicks;            // [64] first-row byte offset of U[u]
+  int* umask = uoff + kWavePicks;             // [64] blocks of the wave that picked U[u]
+  T* ctile = (T*)(smem + kFwdWaves * fwd_wave_lds_bytes(BF16));
+  float* cbias = (float*)(ctile + ctiles * C::NB * C::kTile);
+
+  const uint32_t head_bytes = (uint32_t)a.n * C::kRowBytes;
   const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
   const rsrc_t rk = make_rsrc_uniform((const char*)a.k + (size_t)head * head_bytes, head_bytes);
   const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
+  const int pb_first = a2 * kBlock + 4 * w;   // the wave's first query block
 
-  // ---- the picks of Sel_1[p] as a lane-held table: lane i < K holds the byte offset of pick
-  // i's first row (kNoRow for an invalid id and for lanes >= K); chunks read it by v_readlane.
-  const int32_t* sel1 = a.sel[0] + ((long)head * n1 + pb) * K;
-  uint32_t pick_off = kNoRow;
-  if (lane < K) {
-    const int j = sel1[lane];
-    if (j >= 0 && j < n1) pick_off = (uint32_t)block_corner(j, a.grid) * kDim * C::ES;
+  // ---- the wave's picks (lane 16b + i: pick i of block b) and its query operands
+  int key = kSentinel | lane;   // sentinels sort after every pick and stay distinct
+  if ((lane & 15) < K) {
+    const int j = a.sel[0][((long)head * n1 + pb_first + (lane >> 4)) * K + (lane & 15)];
+    if (j >= 0 && j < n1) key = (j << 8) | lane;
+  }
+  // B operand of S^T for block bb: lane (n, g) holds query row n, channels 32s + 8g .. +7
+  // (bf16) or 16g + 4c .. +3 (fp32)
+  bf16x8 qh[4][2];
+  f32x4 qf[4][4];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    const uint32_t qrow =
+        (uint32_t)(block_corner(pb_first + bb, a.grid) + tile_offset(n, a.grid)) * C::kRowBytes;
+    if constexpr (BF16) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) qh[bb][s2] = buf_load8(rq, qrow + (32 * s2 + 8 * g) * 2);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qf[bb][c] = buf_load4f(rq, qrow + (16 * g + 4 * c) * 4);
+    }
   }
 
-  // ---- queries: B operand of S^T
-  const int qrow = block_corner(pb, a.grid) + tile_offset(n, a.grid);
-  bf16x8 qh[2];
-  f32x4 qf[4];
-  if constexpr (BF16) {
-    qh[0] = buf_load8(rq, (uint32_t)(qrow * kDim + 8 * g) * 2);
-    qh[1] = buf_load8(rq, (uint32_t)(qrow * kDim + 32 + 8 * g) * 2);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qf[c] = buf_load4f(rq, (uint32_t)(qrow * kDim + 16 * g + 4 * c) * 4);
+  // ---- coarse keys of the group (slot e / 8 of 16 ctiles, channels 8 (e % 8) .. +7): fp32
+  // pooled values as bf16 hi + lo parts (fp32 tensors: as they are) and the slot's bias
+  const int pb0 = a2 * kBlock;
+  for (int e = tid; e < ctiles * 16 * 8; e += 64 * kFwdWaves) {
+    const int cslot = e >> 3, c8 = (e & 7) * 8;
+    f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
+    float bias = -INFINITY;
+    if (cslot < n_coarse) {
+      const int l = 2 + cslot / K;
+      const int nl = a.n >> (kBlockShift * l);
+      const int anc = pb0 >> (kBlockShift * (l - 1));
+      const int id = a.sel[l - 1][((long)head * nl + anc) * K + (cslot - (l - 2) * K)];
+      if (id >= 0 && id < nl) {
+        const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
+        const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
+        k0 = *(const f32x4*)kp;
+        k1 = *(const f32x4*)(kp + 4);
+        v0 = *(const f32x4*)vp;
+        v1 = *(const f32x4*)(vp + 4);
+        bias = 4.0f * (float)l;   // log2(16^l)
+      }
+    }
+    T* base = ctile + (cslot >> 4) * C::NB * C::kTile + (cslot & 15) * C::kStride + c8;
+    if constexpr (BF16) {
+      bf16x8 hi, lo;
+      split_bf16(k0, k1, hi, lo);
+      *(bf16x8*)base = hi;
+      *(bf16x8*)(base + C::kTile) = lo;
+      split_bf16(v0, v1, hi, lo);
+      *(bf16x8*)(base + 2 * C::kTile) = hi;
+      *(bf16x8*)(base + 3 * C::kTile) = lo;
+    } else {
+      *(f32x4*)base = k0;
+      *(f32x4*)(base + 4) = k1;
+      *(f32x4*)(base + C::kTile) = v0;
+      *(f32x4*)(base + C::kTile + 4) = v1;
+    }
+    if (c8 == 0) cbias[cslot] = bias;
   }
 
-  // ---- lane-constant byte offsets inside a block: staged rows and A-operand rows
-  const int srow0 = lane / C::PPR;
-  const int piece = lane % C::PPR;
-  uint32_t st_off[C::NINS];
+  // ---- U: rank of each pick key among the wave's 64, distinct ids, owner masks
+  keys[lane] = key;
+  umask[lane] = 0;
+  wave_lds_sync();
+  {
+    int r = 0;
+#pragma unroll 4
+    for (int u = 0; u < kWavePicks; u += 4) {
+      const i32x4 kk = *(const i32x4*)(keys + u);
 #pragma unroll
-  for (int ins = 0; ins < C::NINS; ++ins)
-    st_off[ins] = (uint32_t)(tile_offset((ins * C::RPI + srow0) & 15, a.grid) * kDim * C::ES +
-                             16 * piece);
-  uint32_t ka_off[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-    ka_off[t] = (uint32_t)(tile_offset(tile_row_key(n, t) & 15, a.grid) * kDim * C::ES) +
-                (BF16 ? 16 * g : 64 * g);
-  const bool ka_second = n >= 8;    // A rows 8..15 of both tiles come from the second block
-  const bool lane_second = g >= 2;  // this lane's 8 keys come from the second block
-  const int n_fine = (K + 1) >> 1;
+      for (int e = 0; e < 4; ++e) r += kk[e] < key ? 1 : 0;
+    }
+    sorted[r] = key;
+  }
+  wave_lds_sync();
+  const int sk = sorted[lane];
+  const bool valid = sk < kSentinel;
+  const int prev = sorted[lane > 0 ? lane - 1 : 0];
+  const bool first = valid && (lane == 0 || (prev >> 8) != (sk >> 8));
+  const uint64_t fm = __builtin_amdgcn_ballot_w64(first);
+  const int n_u = uniform(__builtin_popcountll(fm));
+  {
+    const int u = __builtin_popcountll(fm & (~0ull >> (63 - lane))) - 1;
+    if (first) uoff[u] = block_corner(sk >> 8, a.grid) * C::kRowBytes;
+    if (valid) atomicOr(&umask[u], 1 << ((sk & 63) >> 4));
+  }
+  wave_lds_sync();
 
-  // loads of fine chunk ch (blocks 2ch, 2ch+1 of the table), issued one chunk ahead of use.
-  // Every call issues the same loads, also past the last chunk (kNoRow: zeros, no memory
-  // access), so the wait before a chunk's use never has to drain the prefetch behind it.
-  struct FineLd {
-    i32x4 v[C::NINS];
-    i32x4 k[2][C::KLD];
-    int ok0, ok1;
+  // ---- the stream of U: row-major loads (lane l: pieces l + 64 m of the block's 16 rows),
+  // two blocks ahead of use; past the end kNoRow (zeros, no memory access)
+  uint32_t piece_off[C::kLoads];
+#pragma unroll
+  for (int m = 0; m < C::kLoads; ++m) {
+    const int e = lane + 64 * m;
+    piece_off[m] = (uint32_t)tile_offset(e / C::PPR, a.grid) * C::kRowBytes + 16 * (e % C::PPR);
+  }
+  struct BlockLd {
+    i32x4 k[C::kLoads], v[C::kLoads];
   };
-  auto load_fine = [&](int ch) -> FineLd {
-    FineLd f;
-    const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)pick_off, 2 * ch);
-    const uint32_t b1 = (uint32_t)__builtin_amdgcn_readlane((int)pick_off, 2 * ch + 1);
-    f.ok0 = b0 != kNoRow;
-    f.ok1 = b1 != kNoRow;
+  auto load_u = [&](int u) -> BlockLd {
+    BlockLd f;
+    const uint32_t b = u < n_u ? (uint32_t)uniform(uoff[min(u, kWavePicks - 1)]) : kNoRow;
 #pragma unroll
-    for (int ins = 0; ins < C::NINS; ++ins)
-      f.v[ins] = __builtin_amdgcn_raw_buffer_load_b128(rv, (ins * C::RPI >= 16 ? b1 : b0) +
-                                                           st_off[ins], 0, 0);
-    const uint32_t kb = ka_second ? b1 : b0;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int c = 0; c < C::KLD; ++c)
-        f.k[t][c] = __builtin_amdgcn_raw_buffer_load_b128(
-            rk, kb + ka_off[t] + (BF16 ? 64 * c : 16 * c), 0, 0);
+    for (int m = 0; m < C::kLoads; ++m) {
+      f.k[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, b + piece_off[m], 0, 0);
+      f.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, b + piece_off[m], 0, 0);
+    }
     return f;
   };
-  FineLd fa = load_fine(0), fb;
+  BlockLd fa = load_u(0), fb = load_u(1);
+  __syncthreads();   // coarse tiles staged (the only workgroup barrier)
 
-  // ---- the workgroup's coarse keys and values, shared by its four query blocks (their loads
-  // overlap the first fine chunk's)
-  if (n_coarse > 0) {
-    const int pb0 = pb & ~(kFwdWaves - 1);
-    for (int e = threadIdx.x; e < n_cchunks * 32 * 8; e += 64 * kFwdWaves) {
-      const int slot = e >> 3;
-      const int c8 = (e & 7) * 8;
-      f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
-      float bias = -INFINITY;
-      if (slot < n_coarse) {
-        const int l = 2 + slot / K;
-        const int nl = a.n >> (kBlockShift * l);
-        const int anc = pb0 >> (kBlockShift * (l - 1));
-        const int id = a.sel[l - 1][((long)head * nl + anc) * K + (slot - (l - 2) * K)];
-        if (id >= 0 && id < nl) {
-          const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
-          const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
-          k0 = *(const f32x4*)kp;
-          k1 = *(const f32x4*)(kp + 4);
-          v0 = *(const f32x4*)vp;
-          v1 = *(const f32x4*)(vp + 4);
-          bias = 4.0f * (float)l;   // log2(16^l)
-        }
-      }
-      T* base = cstage + (slot >> 5) * C::NB * C::kChunkElems + (slot & 31) * C::kStride + c8;
-      if constexpr (BF16) {
-        bf16x8 hi, lo;
-        split_bf16(k0, k1, hi, lo);
-        *(bf16x8*)base = hi;
-        *(bf16x8*)(base + C::kChunkElems) = lo;
-        split_bf16(v0, v1, hi, lo);
-        *(bf16x8*)(base + 2 * C::kChunkElems) = hi;
-        *(bf16x8*)(base + 3 * C::kChunkElems) = lo;
-      } else {
-        *(f32x4*)base = k0;
-        *(f32x4*)(base + 4) = k1;
-        *(f32x4*)(base + C::kChunkElems) = v0;
-        *(f32x4*)(base + C::kChunkElems + 4) = v1;
-      }
-      if (c8 == 0) cbias[slot] = bias;
-    }
-    __syncthreads();
+  float m_run[4], l_run[4];   // running max (log2 domain) and this lane's partial sums
+  f32x4 acc[4][4];            // O^T of each block: lane (n, g) holds d = 16 t4 + 4g + i
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    m_run[bb] = kMinusBig;
+    l_run[bb] = 0.f;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) acc[bb][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  float m_run = kMinusBig;   // running max (log2 domain) of query n
-  float l_run = 0.f;         // this lane's partial sum of exp2
-  f32x4 acc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // online softmax over one chunk's scores, then O^T += V^T P^T from the row-major V rows at
-  // vbuf (and the lo parts at vlo, if any)
-  auto absorb = [&](float (&sc)[2][4], const T* vbuf, const T* vlo) {
-    float mloc = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    const float m_new = fmaxf(m_run, group4_max(mloc));
-    const float alpha = fast_exp2(m_run - m_new);
-    float p[2][4];
-    float psum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[t][i] = fast_exp2(sc[t][i] - m_new);
-        psum += p[t][i];
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[t4][i] *= alpha;
-    wave_lds_sync();
+  // One 16-key tile for block bb: scores x = st * c2 + bias (log2 domain), online softmax,
+  // O^T += V^T P^T.  The running max moves only when some score exceeds it by more than
+  // 2^kLazy (a wave vote): below that exp2(x - m_run) <= 2^kLazy is exact in fp32 and within
+  // bf16's range, and O = acc / l is unchanged, so most tiles skip the cross-lane max and the
+  // rescaling.  ktl/vtl: K and V rows (16 x stride); klo/vlo: their lo parts (coarse keys).
+  constexpr float kLazy = 8.f;
+  auto tile = [&](auto bbc, const T* ktl, const T* klo, const T* vtl, const T* vlo,
+                  const float* kbias) {
+    constexpr int bb = decltype(bbc)::value;
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
     if constexpr (BF16) {
-      bf16x8 pb8;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb8[i] = (bf16)p[0][i];
-        pb8[i + 4] = (bf16)p[1][i];
+      for (int s2 = 0; s2 < 2; ++s2) {
+        st = mfma_bf16_k32(*(const bf16x8*)(ktl + n * C::kStride + 32 * s2 + 8 * g), qh[bb][s2],
+                           st);
+        if (klo)
+          st = mfma_bf16_k32(*(const bf16x8*)(klo + n * C::kStride + 32 * s2 + 8 * g),
+                             qh[bb][s2], st);
       }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 kf = *(const f32x4*)(ktl + n * C::kStride + 16 * g + 4 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st = mfma_f32_k4(kf[e], qf[bb][c][e], st);
+      }
+    }
+    float x[4];
+    if (kbias) {
+      const f32x4 b4 = *(const f32x4*)(kbias + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = fmaf(st[i], a.c2, b4[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = st[i] * a.c2;
+    }
+    const float mloc = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run[bb] + kLazy)) {   // wave-uniform
+      const float m_new = fmaxf(m_run[bb], group4_max(mloc));
+      const float alpha = fast_exp2(m_run[bb] - m_new);
+      l_run[bb] *= alpha;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[bb][t4][i] *= alpha;
+      m_run[bb] = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(x[i] - m_run[bb]);
+      l_run[bb] += p[i];
+    }
+    if constexpr (BF16) {
+      bf16x4 pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = (bf16)p[i];
       const int r = (lane & 15) >> 2;
       const int c = lane & 3;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        const int off = (8 * g + r) * C::kStride + 16 * t4 + 4 * c;
-        const bf16x4 x0 = lds_read_tr16(vbuf + off);
-        const bf16x4 x1 = lds_read_tr16(vbuf + off + 4 * C::kStride);
-        bf16x8 vt;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vt[e] = x0[e];
-          vt[e + 4] = x1[e];
-        }
-        acc[t4] = mfma_bf16_k32(vt, pb8, acc[t4]);
-        if (vlo) {
-          const bf16x4 y0 = lds_read_tr16(vlo + off);
-          const bf16x4 y1 = lds_read_tr16(vlo + off + 4 * C::kStride);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vt[e] = y0[e];
-            vt[e + 4] = y1[e];
-          }
-          acc[t4] = mfma_bf16_k32(vt, pb8, acc[t4]);
-        }
+        const int off = (4 * g + r) * C::kStride + 16 * t4 + 4 * c;
+        acc[bb][t4] = mfma_bf16_k16(lds_read_tr16(vtl + off), pb, acc[bb][t4]);
+        if (vlo) acc[bb][t4] = mfma_bf16_k16(lds_read_tr16(vlo + off), pb, acc[bb][t4]);
       }
     } else {
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int i = 0; i < 4; ++i)
+          acc[bb][t4] =
+              mfma_f32_k4(vtl[(4 * g + i) * C::kStride + 16 * t4 + n], p[i], acc[bb][t4]);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  auto for_blocks = [&](auto&& fn) {
+    fn(I0{});
+    fn(I1{});
+    fn(I2{});
+    fn(I3{});
+  };
+
+  // one block of U from its loads: rows to the wave's LDS tile, then the tiles of the blocks
+  // that picked it
+  auto block_u = [&](const BlockLd& f, int u) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float vv = vbuf[(8 * g + i + 4 * t) * C::kStride + 16 * t4 + n];
-            acc[t4] = mfma_f32_k4(vv, p[t][i], acc[t4]);
-          }
+    for (int m = 0; m < C::kLoads; ++m) {
+      const int e = lane + 64 * m;
+      const int at = (e / C::PPR) * C::kStride + (e % C::PPR) * (16 / C::ES);
+      *(i32x4*)(kt + at) = f.k[m];
+      *(i32x4*)(vt + at) = f.v[m];
     }
     wave_lds_sync();
+    const int mask = uniform(umask[u]);
+    for_blocks([&](auto bbc) {
+      if (mask & (1 << decltype(bbc)::value)) tile(bbc, kt, nullptr, vt, nullptr, nullptr);
+    });
+    wave_lds_sync();
   };
+  for (int u = 0; u < n_u; u += 2) {
+    block_u(fa, u);
+    fa = load_u(u + 2);
+    if (u + 1 >= n_u) break;
+    block_u(fb, u + 1);
+    fb = load_u(u + 3);
+  }
 
-  // one fine chunk from its loads: V rows to LDS, S^T on the MFMA, softmax and PV
-  auto fine_chunk = [&](const FineLd& f) {
+  // ---- coarse keys, then O and the LSE of each block
+  for (int ct = 0; ct < ctiles; ++ct) {
+    const T* cb0 = ctile + ct * C::NB * C::kTile;
+    for_blocks([&](auto bbc) {
+      if constexpr (BF16)
+        tile(bbc, cb0, cb0 + C::kTile, cb0 + 2 * C::kTile, cb0 + 3 * C::kTile, cbias + 16 * ct);
+      else
+        tile(bbc, cb0, nullptr, cb0 + C::kTile, nullptr, cbias + 16 * ct);
+    });
+  }
+  for_blocks([&](auto bbc) {
+    constexpr int bb = decltype(bbc)::value;
+    const int pb = pb_first + bb;
+    const int qrow = block_corner(pb, a.grid) + tile_offset(n, a.grid);
+    const float l_tot = group4_sum(l_run[bb]);
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;   // 0 only if every key was skipped
+    if constexpr (BF16) {
+      bf16* op = (bf16*)a.o + (tok_base + qrow) * kDim;
 #pragma unroll
-    for (int ins = 0; ins < C::NINS; ++ins)
-      *(i32x4*)(stage + (ins * C::RPI + srow0) * C::kStride + piece * (16 / C::ES)) = f.v[ins];
-    float sc[2][4];
-    const float madd = (lane_second ? f.ok1 : f.ok0) ? 0.f : -INFINITY;
+      for (int t4 = 0; t4 < 4; ++t4) {
+        bf16x4 r;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      f32x4 st = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (BF16) {
-        st = mfma_bf16_k32(*(const bf16x8*)&f.k[t][0], qh[0], st);
-        st = mfma_bf16_k32(*(const bf16x8*)&f.k[t][1], qh[1], st);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const f32x4 kf = *(const f32x4*)&f.k[t][c];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) st = mfma_f32_k4(kf[e], qf[c][e], st);
-        }
+        for (int i = 0; i < 4; ++i) r[i] = (bf16)(acc[bb][t4][i] * inv);
+        *(bf16x4*)(op + 16 * t4 + 4 * g) = r;
       }
+    } else {
+      float* op = (float*)a.o + (tok_base + qrow) * kDim;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[t][i] = fmaf(st[i], a.c2, madd);
-    }
-    absorb(sc, stage, nullptr);
-  };
-
-  // ---- fine chunks: two load buffers used in turn, each refilled while the other computes
-  for (int ch = 0; ch < n_fine; ch += 2) {
-    fb = load_fine(ch + 1);
-    fine_chunk(fa);
-    if (ch + 1 >= n_fine) break;
-    fa = load_fine(ch + 2);
-    fine_chunk(fb);
-  }
-
-  // ---- coarse chunks from the workgroup's LDS copy
-  for (int cc = 0; cc < n_cchunks; ++cc) {
-    const T* kb = cstage + cc * C::NB * C::kChunkElems;
-    float sc[2][4];
+      for (int t4 = 0; t4 < 4; ++t4) {
+        f32x4 r;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = tile_row_key(n, t);
-      f32x4 st = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (BF16) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16* rp = kb + row * C::kStride + 32 * s + 8 * g;
-          st = mfma_bf16_k32(*(const bf16x8*)rp, qh[s], st);
-          st = mfma_bf16_k32(*(const bf16x8*)(rp + C::kChunkElems), qh[s], st);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const f32x4 kf = *(const f32x4*)(kb + row * C::kStride + 16 * g + 4 * c);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) st = mfma_f32_k4(kf[e], qf[c][e], st);
-        }
+        for (int i = 0; i < 4; ++i) r[i] = acc[bb][t4][i] * inv;
+        *(f32x4*)(op + 16 * t4 + 4 * g) = r;
       }
-      const f32x4 b4 = *(const f32x4*)(cbias + cc * 32 + 8 * g + 4 * t);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[t][i] = fmaf(st[i], a.c2, b4[i]);
     }
-    absorb(sc, kb + (BF16 ? 2 : 1) * C::kChunkElems, BF16 ? kb + 3 * C::kChunkElems : nullptr);
-  }
-
-  // ---- finalize
-  const float l_tot = group4_sum(l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;   // 0 only if every key was skipped
-  if constexpr (BF16) {
-    bf16* op = (bf16*)a.o + (tok_base + qrow) * kDim;
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      bf16x4 r;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = (bf16)(acc[t4][i] * inv);
-      *(bf16x4*)(op + 16 * t4 + 4 * g) = r;
-    }
-  } else {
-    float* op = (float*)a.o + (tok_base + qrow) * kDim;
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      f32x4 r;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = acc[t4][i] * inv;
-      *(f32x4*)(op + 16 * t4 + 4 * g) = r;
-    }
-  }
-  if (g == 0) a.lse[tok_base + pb * kBlock + n] = (m_run + log2f(l_tot)) * kLn2;
+    if (g == 0) a.lse[tok_base + pb * kBlock + n] = (m_run[bb] + log2f(l_tot)) * kLn2;
+  });
 }
 
 hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const void* v,
@@ -410,9 +422,8 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const v
   a.c2 = s.scale * kLog2e;
   const int n_coarse = s.enrich ? (s.levels - 1) * s.topk : 0;
   const size_t lds = fwd_lds_bytes(s.bf16, n_coarse);
-  // every workgroup holds 4 whole query blocks of one head (N / 16 is a multiple of 4)
-  const long waves = (long)s.bh * (s.n >> kBlockShift);
-  const unsigned blocks = (unsigned)(waves / kFwdWaves);
+  // one workgroup per level-2 group (N is a multiple of 16^2)
+  const unsigned blocks = (unsigned)((long)s.bh * (s.n >> (2 * kBlockShift)));
   const void* fn = s.bf16 ? (const void*)attn_fwd_kernel<true> : (const void*)attn_fwd_kernel<false>;
   if (lds > 65536) {
     const hipError_t e =

@@ -141,17 +141,20 @@ __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
 // (rows 0..3).  So reading rows k0..k0+3 of a row-major [k][n] LDS matrix this way gives
 // each lane the MFMA operand slice B[k0 .. k0+3][n].
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ bf16x4 lds_read_tr16(const bf16* lds_ptr) {
   i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_ptr));
   return *(bf16x4*)&r;
 }
 
-// Orders this wave's LDS accesses: writes before the barrier are visible to reads after it
-// (LDS requests of one wave are processed in order; the fences stop compiler reordering).
+// Orders this wave's LDS accesses: writes before it are visible to reads after it, and reads
+// before it complete before later writes.  The LDS executes one wave's requests in issue order,
+// so only compiler reordering has to be stopped: a compiler memory barrier does that without a
+// memory fence (a fence would also wait for every vector load in flight, including the
+// prefetches that load into LDS).
 __device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  asm volatile("" ::: "memory");
 }
 
 // ------------------------------------------------------------------ XCD-aware numbering
@@ -168,16 +171,23 @@ __device__ __forceinline__ int xcd_block(int bid, int nblocks) {
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 __device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }
 
-// Reduce over the four 16-lane groups (lanes n, n+16, n+32, n+48).
+// Reduce over the four 16-lane rows of the wave (lanes n, n+16, n+32, n+48) on the VALU:
+// v_permlane16_swap exchanges rows 0<->1 and 2<->3 between its two operands, and
+// v_permlane32_swap the two 32-lane halves, so with both operands holding v the two results
+// of each swap are v and its partner row's v (the order does not matter for max and sum).
+__device__ __forceinline__ float bits_f(unsigned u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ unsigned f_bits(float f) { return __builtin_bit_cast(unsigned, f); }
 __device__ __forceinline__ float group4_max(float v) {
-  v = fmaxf(v, shfl_xor_f(v, 16));
-  v = fmaxf(v, shfl_xor_f(v, 32));
-  return v;
+  const auto r = __builtin_amdgcn_permlane16_swap(f_bits(v), f_bits(v), false, false);
+  const float m = fmaxf(bits_f(r[0]), bits_f(r[1]));
+  const auto s = __builtin_amdgcn_permlane32_swap(f_bits(m), f_bits(m), false, false);
+  return fmaxf(bits_f(s[0]), bits_f(s[1]));
 }
 __device__ __forceinline__ float group4_sum(float v) {
-  v += shfl_xor_f(v, 16);
-  v += shfl_xor_f(v, 32);
-  return v;
+  const auto r = __builtin_amdgcn_permlane16_swap(f_bits(v), f_bits(v), false, false);
+  const float m = bits_f(r[0]) + bits_f(r[1]);
+  const auto s = __builtin_amdgcn_permlane32_swap(f_bits(m), f_bits(m), false, false);
+  return bits_f(s[0]) + bits_f(s[1]);
 }
 
 }  // namespace llsa
