@@ -43,7 +43,7 @@ struct BwdArgs {
   bf16* dk;
   bf16* dv;
   float* dd;                   // D, [bh, N]
-  float* part_k;               // [bh, n2, n_coarse, 64]
+  float* part_k;               // [bh, n2, kUnits, n_coarse, 64]
   float* part_v;
   float* lvl_part_k[kMaxLv];   // level l >= 3: [bh, n_l, K, 64]
   float* lvl_part_v[kMaxLv];
@@ -114,39 +114,75 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* st, int t4, int lane) {
 }
 
 // ====================================================================== stage 1: query-major
-// LDS layout (bf16 elements): per wave, a 32-row staging tile (K rows of a fine chunk; after the
-// chunk loop the block's Q and dO rows for the coarse partial sums) and four 32x16 tiles (P^T,
-// dS^T as hi + lo); then, shared by the workgroup, the coarse keys/values of its level-2
-// group: K hi, K lo, V hi, V lo (32 rows each) and the 32 slot biases (fp32).
-constexpr int kQStage = 32 * kStride;
-constexpr int kQPd = 4 * 32 * 16;
-constexpr int kQPerWave = kQStage + kQPd;
-static size_t bwd_query_lds_bytes(bool coarse) {
-  return sizeof(bf16) * (size_t)(4 * kQPerWave + (coarse ? 4 * kQStage : 0)) +
-         (coarse ? 32 * sizeof(float) : 0);
+// One workgroup per half of a level-2 group (8 query blocks, which share their coarse keys);
+// each of its 4 waves owns 2 consecutive query blocks and works on its own:
+//  * its 2 K picks are ranked in LDS into the ascending list U of distinct key blocks with a
+//    2-bit mask of the blocks that picked each; U is streamed with row-major loads (16 K rows
+//    and 16 V rows per block, two blocks ahead in registers) through the wave's LDS tiles;
+//  * for each pick, one 16 x 16 tile: S^T = K Q^T and dP^T = V dO^T (16x16x32), P, P dP, and
+//    A += K^T (P dP), Bv += K^T P (16x16x16, hi + lo parts), so D = sum P dP is exact and
+//    dQ = scale (A - D Bv) needs one pass (the bf16 O is never read);
+//  * the coarse keys (staged once per workgroup as bf16 hi + lo) add their tiles; at the end of
+//    a block its coarse scores are recomputed in the Q K^T orientation, which puts P and dS in
+//    the B-operand layout of the partial sums dV_c += P^T dO and dK_c += dS^T Q over the
+//    block's queries (Q and dO rows staged in the wave's tiles);
+//  * the 4 waves' partials are summed in a fixed order into the half-group's partial rows.
+constexpr int kQWaves = 4;
+constexpr int kQBlocks = 2;     // query blocks per wave
+constexpr int kUnits = 2;       // partial units (workgroups) per level-2 group
+constexpr int kQPickList = 64;  // pick-list capacity per wave (2 K <= 32)
+constexpr int kPickSentinel = 0x7f000000;
+
+__host__ __device__ constexpr int bwdq_wave_lds_bytes() {
+  return 2 * 16 * kStride * 2 + 4 * kQPickList * 4 + 48 * 4;
+}
+static size_t bwd_query_lds_bytes(int n_coarse) {
+  const int ctiles = (n_coarse + 15) / 16;
+  return (size_t)kQWaves * bwdq_wave_lds_bytes() + (size_t)ctiles * 4 * 16 * kStride * 2 +
+         sizeof(float) * 16 * ctiles;
 }
 
-template <int NST>   // coarse slot tiles (of 16) kept in registers: 0, 1 or 2
-__global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
+__device__ __forceinline__ void split4(const float (&x)[4], bf16x4& hi, bf16x4& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16 h = (bf16)x[i];
+    hi[i] = h;
+    lo[i] = (bf16)(x[i] - (float)h);
+  }
+}
+
+template <int NCT>   // coarse tiles of 16 slots: 0, 1 or 2
+__global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_query_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  bf16* lds = (bf16*)smem;
-  const int lane = threadIdx.x & 63;
-  const int w = uniform(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = uniform(tid >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
+  const int r4 = (lane & 15) >> 2, c4 = lane & 3;   // transposed-read lane roles
   const int n1 = a.n >> kBlockShift;
   const int n2 = n1 >> kBlockShift;
-  const int wg = uniform(xcd_block(blockIdx.x, gridDim.x));
-  const int head = uniform(wg / n2);
-  const int a2 = uniform(wg - head * n2);
+  const int unit = uniform(xcd_block(blockIdx.x, gridDim.x));
+  const int head = uniform(unit / (kUnits * n2));
+  const int rem = uniform(unit - head * kUnits * n2);
+  const int a2 = rem / kUnits;
+  const int pb_first = a2 * kBlock + (rem % kUnits) * (kBlock / kUnits) + kQBlocks * w;
   const int K = a.topk;
   const long tok_base = (long)head * a.n;
-  const int n_coarse = NST > 0 ? (a.levels - 1) * K : 0;
-  bf16* stK = lds + w * kQPerWave;            // K rows of a chunk / Q and dO rows of a block
-  bf16* stP = stK + kQStage;                  // P^T hi, P^T lo, dS^T hi, dS^T lo: [slot][q]
-  bf16* cK = lds + 4 * kQPerWave;             // shared coarse K hi (+kQStage: lo)
-  bf16* cV = cK + 2 * kQStage;                // shared coarse V hi (+kQStage: lo)
-  float* cbias = (float*)(cK + 4 * kQStage);
+  const int n_coarse = NCT > 0 ? (a.levels - 1) * K : 0;
+
+  char* wb = smem + w * bwdq_wave_lds_bytes();
+  bf16* kt = (bf16*)wb;                 // staged K rows (Q rows at a block's end)
+  bf16* vt = kt + 16 * kStride;         // staged V rows (dO rows at a block's end)
+  int* keys = (int*)(vt + 16 * kStride);
+  int* sorted = keys + kQPickList;
+  int* uoff = sorted + kQPickList;
+  int* umask = uoff + kQPickList;
+  float* lsh = (float*)(umask + kQPickList);   // [2][16] log2-domain LSE of the blocks' queries
+  float* dsh = lsh + 32;                       // [16] D of the current block's queries
+  bf16* ct = (bf16*)(smem + kQWaves * bwdq_wave_lds_bytes());   // [NCT][K hi, K lo, V hi, V lo]
+  float* cbias = (float*)(ct + NCT * 4 * 16 * kStride);
 
   const uint32_t head_bytes = (uint32_t)a.n * kDim * 2;
   const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
@@ -156,334 +192,289 @@ __global__ __launch_bounds__(256) void bwd_query_kernel(BwdArgs a) {
       make_rsrc_uniform((const char*)a.dout + (size_t)head * head_bytes, head_bytes);
   const rsrc_t rl = make_rsrc_uniform(a.lse + tok_base, (uint32_t)a.n * 4);
 
-  // The wave's four query blocks pb_first + b, b = 0..3, form one stream of 4 * n_fine fine
-  // chunks; the loads of the next chunk are always issued before the current one is computed.
-  const int pb_first = a2 * kBlock + w * 4;
-  const int n_fine = (K + 1) >> 1;
-  // picks as a lane-held table: lane 16b + i holds the first-row byte offset of pick i of
-  // block b (kNoRow for i >= K and for an invalid id); chunks take them with v_readlane
-  uint32_t pick_off = kNoRow;
-  if ((lane & 15) < K) {
+  // ---- the wave's picks (lane 16b + i: pick i of block b) and its query-side operands
+  int key = kPickSentinel | lane;
+  if (lane < 16 * kQBlocks && (lane & 15) < K) {
     const int j = a.sel[0][((long)head * n1 + pb_first + (lane >> 4)) * K + (lane & 15)];
-    if (j >= 0 && j < n1) pick_off = (uint32_t)block_corner(j, a.grid) * kDim * 2;
+    if (j >= 0 && j < n1) key = (j << 8) | lane;
+  }
+  bf16x8 qh[kQBlocks][2], dh[kQBlocks][2];   // B operands: lane (n, g) row n, ch 32s + 8g..
+  float lraw[kQBlocks];
+#pragma unroll
+  for (int bb = 0; bb < kQBlocks; ++bb) {
+    const int pb = pb_first + bb;
+    const uint32_t qrow =
+        (uint32_t)(block_corner(pb, a.grid) + tile_offset(n, a.grid)) * kDim * 2;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      qh[bb][s2] = buf_load8(rq, qrow + (32 * s2 + 8 * g) * 2);
+      dh[bb][s2] = buf_load8(rdo, qrow + (32 * s2 + 8 * g) * 2);
+    }
+    lraw[bb] = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)(pb * kBlock + n) * 4, 0, 0));
   }
 
-  // lane-constant byte offsets inside a 4x4 block: staged rows and A-operand rows
-  const int srow0 = lane >> 3;
-  const int piece = lane & 7;
-  uint32_t st_off[4];
-#pragma unroll
-  for (int ins = 0; ins < 4; ++ins)
-    st_off[ins] = (uint32_t)(tile_offset((ins * 8 + srow0) & 15, a.grid) * kDim * 2 + 16 * piece);
-  uint32_t va_off[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-    va_off[t] = (uint32_t)(tile_offset(chunk_key(n, t) & 15, a.grid) * kDim * 2) + 16 * g;
-  const bool a_second = n >= 8;     // A rows 8..15 of both tiles come from the second block
-  const bool lane_second = g >= 2;  // this lane's 8 keys come from the second block
-
-  // rows of one query block: Q and dO as B operands (lane (n, g): row n, channels 32s + 8g..)
-  // and the row's LSE (natural log, as stored)
-  struct BlockLd {
-    bf16x8 q[2], d[2];
-    float lse;
-  };
-  auto load_block = [&](int b) -> BlockLd {
-    BlockLd r;
-    const int pb = pb_first + b;
-    const int qrow = block_corner(pb, a.grid) + tile_offset(n, a.grid);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      r.q[s] = buf_load8(rq, (uint32_t)(qrow * kDim + 32 * s + 8 * g) * 2);
-      r.d[s] = buf_load8(rdo, (uint32_t)(qrow * kDim + 32 * s + 8 * g) * 2);
+  // ---- coarse keys of the group (slot e / 8, channels 8 (e % 8) ..): bf16 hi + lo parts
+  if (NCT > 0) {
+    for (int e = tid; e < NCT * 16 * 8; e += 64 * kQWaves) {
+      const int cslot = e >> 3, c8 = (e & 7) * 8;
+      f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
+      float bias = -INFINITY;
+      if (cslot < n_coarse) {
+        const int l = 2 + cslot / K;
+        const int nl = a.n >> (kBlockShift * l);
+        const int anc = (a2 * kBlock) >> (kBlockShift * (l - 1));
+        const int id = a.sel[l - 1][((long)head * nl + anc) * K + (cslot - (l - 2) * K)];
+        if (id >= 0 && id < nl) {
+          const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
+          const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
+          k0 = *(const f32x4*)kp;
+          k1 = *(const f32x4*)(kp + 4);
+          v0 = *(const f32x4*)vp;
+          v1 = *(const f32x4*)(vp + 4);
+          bias = 4.0f * (float)l;   // log2(16^l)
+        }
+      }
+      bf16* base = ct + (cslot >> 4) * 4 * 16 * kStride + (cslot & 15) * kStride + c8;
+      bf16x8 hi, lo;
+      split_f32x8(k0, k1, hi, lo);
+      *(bf16x8*)base = hi;
+      *(bf16x8*)(base + 16 * kStride) = lo;
+      split_f32x8(v0, v1, hi, lo);
+      *(bf16x8*)(base + 32 * kStride) = hi;
+      *(bf16x8*)(base + 48 * kStride) = lo;
+      if (c8 == 0) cbias[cslot] = bias;
     }
-    r.lse = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)(pb * kBlock + n) * 4, 0, 0));
-    return r;
-  };
+  }
 
-  struct FineLd {
-    i32x4 k[4];      // staged K rows
-    i32x4 v[2][2];   // V rows as A operands of dP^T
-    int ok0, ok1;
+  // ---- U: ranks of the wave's pick keys, distinct ids, owner masks
+  keys[lane] = key;
+  umask[lane] = 0;
+  if (g < kQBlocks) lsh[16 * g + n] = (g == 0 ? lraw[0] : lraw[1]) * kLog2e;
+  wave_lds_sync();
+  {
+    int r = 0;
+#pragma unroll 4
+    for (int u = 0; u < kQPickList; u += 4) {
+      const i32x4 kk = *(const i32x4*)(keys + u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r += kk[e] < key ? 1 : 0;
+    }
+    sorted[r] = key;
+  }
+  wave_lds_sync();
+  float lse2[kQBlocks];   // log2-domain LSE of query n of each block
+#pragma unroll
+  for (int bb = 0; bb < kQBlocks; ++bb) lse2[bb] = lraw[bb] * kLog2e;
+  const int sk = sorted[lane];
+  const bool valid = sk < kPickSentinel;
+  const int prev = sorted[lane > 0 ? lane - 1 : 0];
+  const bool first = valid && (lane == 0 || (prev >> 8) != (sk >> 8));
+  const uint64_t fm = __builtin_amdgcn_ballot_w64(first);
+  const int n_u = uniform(__builtin_popcountll(fm));
+  {
+    const int u = __builtin_popcountll(fm & (~0ull >> (63 - lane))) - 1;
+    if (first) uoff[u] = block_corner(sk >> 8, a.grid) * kDim * 2;
+    if (valid) atomicOr(&umask[u], 1 << ((sk & 63) >> 4));
+  }
+  wave_lds_sync();
+
+  // ---- the stream of U: row-major loads (lane l: pieces l, l + 64 of 16 rows x 8 pieces)
+  uint32_t poff[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int e = lane + 64 * m;
+    poff[m] = (uint32_t)tile_offset(e >> 3, a.grid) * kDim * 2 + 16 * (e & 7);
+  }
+  struct BlockLd {
+    i32x4 k[2], v[2];
   };
-  int lb = 0, lch = 0;   // block and chunk of the next load (lb == 4: past the end)
-  // Every call issues the same loads, also past the last chunk (kNoRow: zeros, no memory
-  // access), so the wait before a chunk's use never drains the loads queued behind it.
-  auto load_next = [&]() -> FineLd {
-    FineLd f;
-    const int idx = min(16 * lb + 2 * lch, 62);
-    uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)pick_off, idx);
-    uint32_t b1 = (uint32_t)__builtin_amdgcn_readlane((int)pick_off, idx + 1);
-    if (lb >= 4) b0 = b1 = kNoRow;
-    f.ok0 = b0 != kNoRow;
-    f.ok1 = b1 != kNoRow;
+  auto load_u = [&](int u) -> BlockLd {
+    BlockLd f;
+    const uint32_t b = u < n_u ? (uint32_t)uniform(uoff[min(u, kQPickList - 1)]) : kNoRow;
 #pragma unroll
-    for (int ins = 0; ins < 4; ++ins)
-      f.k[ins] = __builtin_amdgcn_raw_buffer_load_b128(rk, (ins >= 2 ? b1 : b0) + st_off[ins],
-                                                       0, 0);
-    const uint32_t vb = a_second ? b1 : b0;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        f.v[t][s] = __builtin_amdgcn_raw_buffer_load_b128(rv, vb + va_off[t] + 64 * s, 0, 0);
-    if (++lch == n_fine) {
-      lch = 0;
-      ++lb;
+    for (int m = 0; m < 2; ++m) {
+      f.k[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, b + poff[m], 0, 0);
+      f.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, b + poff[m], 0, 0);
     }
     return f;
   };
+  BlockLd fa = load_u(0), fb = load_u(1);
+  if (NCT > 0) __syncthreads();   // coarse tiles staged
 
-  BlockLd cur = load_block(0), nxt;
-  FineLd fa = load_next(), fb;
-
-  if (NST > 0) {
-    // ---- the group's coarse keys/values (all 256 queries of the level-2 group share them);
-    // their loads overlap the first chunk's
-    const int pb0 = a2 * kBlock;
-    const int e = threadIdx.x;             // 32 slots x 8 pieces of 8 channels
-    const int slot = e >> 3;
-    const int c8 = (e & 7) * 8;
-    f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
-    float bias = -INFINITY;
-    if (slot < n_coarse) {
-      const int l = 2 + slot / K;
-      const int nl = a.n >> (kBlockShift * l);
-      const int anc = pb0 >> (kBlockShift * (l - 1));
-      const int id = a.sel[l - 1][((long)head * nl + anc) * K + (slot - (l - 2) * K)];
-      if (id >= 0 && id < nl) {
-        const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
-        const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
-        k0 = *(const f32x4*)kp;
-        k1 = *(const f32x4*)(kp + 4);
-        v0 = *(const f32x4*)vp;
-        v1 = *(const f32x4*)(vp + 4);
-        bias = 4.0f * (float)l;   // log2(16^l)
-      }
-    }
-    bf16x8 hi, lo;
-    split_f32x8(k0, k1, hi, lo);
-    *(bf16x8*)(cK + slot * kStride + c8) = hi;
-    *(bf16x8*)(cK + kQStage + slot * kStride + c8) = lo;
-    split_f32x8(v0, v1, hi, lo);
-    *(bf16x8*)(cV + slot * kStride + c8) = hi;
-    *(bf16x8*)(cV + kQStage + slot * kStride + c8) = lo;
-    if (c8 == 0) cbias[slot] = bias;
-    __syncthreads();
+  f32x4 acc_a[kQBlocks][4], acc_b[kQBlocks][4];
+  float dpart[kQBlocks];
+#pragma unroll
+  for (int bb = 0; bb < kQBlocks; ++bb) {
+    dpart[bb] = 0.f;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) acc_a[bb][t4] = acc_b[bb][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  f32x4 cpk[NST > 0 ? NST : 1][4];   // coarse partial dK (unscaled): [slot tile][d tile]
-  f32x4 cpv[NST > 0 ? NST : 1][4];
+  // One 16-key tile of block bb: K rows kr (+ lo parts klo), V rows vr (+ vlo), per-key biases.
+  auto tile = [&](auto bbc, const bf16* kr, const bf16* klo, const bf16* vr, const bf16* vlo,
+                  const float* kbias) {
+    constexpr int bb = decltype(bbc)::value;
+    f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = st;
 #pragma unroll
-  for (int st = 0; st < (NST > 0 ? NST : 1); ++st)
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) cpk[st][t4] = cpv[st][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // dQ = scale * sum_e P_e (dP_e - D) k_e = scale * (A - D * Bv) with A = sum P dP k and
-  // Bv = sum P k, so D = sum_e P_e dP_e is exact (no bf16 O) and one pass suffices.
-  f32x4 acc_a[4], acc_b[4];
-#pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4) acc_a[t4] = acc_b[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dpart = 0.f;           // this lane's share of D
-  float pc[2][4], dpc[2][4];   // P and dP of the coarse chunk
-
-  // P, P dP of one chunk from its S^T / dP^T tiles; A/B accumulation on the MFMA
-  auto absorb = [&](const f32x4 (&st)[2], const f32x4 (&dp)[2], const float (&add)[2][4],
-                    const bf16* kt_hi, const bf16* kt_lo, bool keep) {
-    float p[2][4], w1[2][4];
-    const float lse2 = cur.lse * kLog2e;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float pv = fast_exp2(fmaf(st[t][i], a.c2, add[t][i] - lse2));
-        p[t][i] = pv;
-        w1[t][i] = pv * dp[t][i];
-        dpart += w1[t][i];
-        if (keep) {
-          pc[t][i] = pv;
-          dpc[t][i] = dp[t][i];
-        }
+    for (int s2 = 0; s2 < 2; ++s2) {
+      st = mfma_bf16_k32(lds_row8(kr, n, s2, g), qh[bb][s2], st);
+      dp = mfma_bf16_k32(lds_row8(vr, n, s2, g), dh[bb][s2], dp);
+      if (klo) {
+        st = mfma_bf16_k32(lds_row8(klo, n, s2, g), qh[bb][s2], st);
+        dp = mfma_bf16_k32(lds_row8(vlo, n, s2, g), dh[bb][s2], dp);
       }
-    bf16x8 a_hi, a_lo, b_hi, b_lo;
-    split8(w1, a_hi, a_lo);
-    split8(p, b_hi, b_lo);
+    }
+    float p[4], w1[4];
+    f32x4 b4 = {0.f, 0.f, 0.f, 0.f};
+    if (kbias) b4 = *(const f32x4*)(kbias + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(fmaf(st[i], a.c2, b4[i] - lse2[bb]));
+      w1[i] = p[i] * dp[i];
+      dpart[bb] += w1[i];
+    }
+    bf16x4 a_hi, a_lo, b_hi, b_lo;
+    split4(w1, a_hi, a_lo);
+    split4(p, b_hi, b_lo);
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
-      const bf16x8 kt = lds_tr8(kt_hi, t4, lane);
-      acc_a[t4] = mfma_bf16_k32(kt, a_hi, acc_a[t4]);
-      acc_a[t4] = mfma_bf16_k32(kt, a_lo, acc_a[t4]);
-      acc_b[t4] = mfma_bf16_k32(kt, b_hi, acc_b[t4]);
-      acc_b[t4] = mfma_bf16_k32(kt, b_lo, acc_b[t4]);
-      if (kt_lo) {
-        const bf16x8 ktl = lds_tr8(kt_lo, t4, lane);
-        acc_a[t4] = mfma_bf16_k32(ktl, a_hi, acc_a[t4]);
-        acc_b[t4] = mfma_bf16_k32(ktl, b_hi, acc_b[t4]);
+      const int off = (4 * g + r4) * kStride + 16 * t4 + 4 * c4;
+      const bf16x4 ktr = lds_read_tr16(kr + off);
+      acc_a[bb][t4] = mfma_bf16_k16(ktr, a_hi, acc_a[bb][t4]);
+      acc_a[bb][t4] = mfma_bf16_k16(ktr, a_lo, acc_a[bb][t4]);
+      acc_b[bb][t4] = mfma_bf16_k16(ktr, b_hi, acc_b[bb][t4]);
+      acc_b[bb][t4] = mfma_bf16_k16(ktr, b_lo, acc_b[bb][t4]);
+      if (klo) {
+        const bf16x4 ktl = lds_read_tr16(klo + off);
+        acc_a[bb][t4] = mfma_bf16_k16(ktl, a_hi, acc_a[bb][t4]);
+        acc_b[bb][t4] = mfma_bf16_k16(ktl, b_hi, acc_b[bb][t4]);
       }
     }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
-  auto fine_chunk = [&](const FineLd& f) {
+  auto block_u = [&](const BlockLd& f, int u) {
 #pragma unroll
-    for (int ins = 0; ins < 4; ++ins)
-      *(i32x4*)(stK + (ins * 8 + srow0) * kStride + 8 * piece) = f.k[ins];
-    wave_lds_sync();
-    f32x4 st[2], dp[2];
-    float add[2][4];
-    const float madd = (lane_second ? f.ok1 : f.ok0) ? 0.f : -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int arow = chunk_key(n, t);
-      st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      st[t] = mfma_bf16_k32(lds_row8(stK, arow, 0, g), cur.q[0], st[t]);
-      st[t] = mfma_bf16_k32(lds_row8(stK, arow, 1, g), cur.q[1], st[t]);
-      dp[t] = mfma_bf16_k32(*(const bf16x8*)&f.v[t][0], cur.d[0], dp[t]);
-      dp[t] = mfma_bf16_k32(*(const bf16x8*)&f.v[t][1], cur.d[1], dp[t]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) add[t][i] = madd;
+    for (int m = 0; m < 2; ++m) {
+      const int e = lane + 64 * m;
+      const int at = (e >> 3) * kStride + (e & 7) * 8;
+      *(i32x4*)(kt + at) = f.k[m];
+      *(i32x4*)(vt + at) = f.v[m];
     }
-    absorb(st, dp, add, stK, nullptr, false);
+    wave_lds_sync();
+    const int mask = uniform(umask[u]);
+    if (mask & 1) tile(I0{}, kt, nullptr, vt, nullptr, nullptr);
+    if (mask & 2) tile(I1{}, kt, nullptr, vt, nullptr, nullptr);
     wave_lds_sync();
   };
+  for (int u = 0; u < n_u; u += 2) {
+    block_u(fa, u);
+    fa = load_u(u + 2);
+    if (u + 1 >= n_u) break;
+    block_u(fb, u + 1);
+    fb = load_u(u + 3);
+  }
 
-  // the end of query block b: its coarse chunk, D, dQ and its share of the coarse partials
-  auto block_end = [&](int b) {
-    const int pb = pb_first + b;
-    const int qrow = block_corner(pb, a.grid) + tile_offset(n, a.grid);
-    if (NST > 0) {
-      f32x4 st[2], dp[2];
-      float add[2][4];
+  f32x4 cpk[NCT > 0 ? NCT : 1][4], cpv[NCT > 0 ? NCT : 1][4];   // C^T[d][slot]: lane (slot, g)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int arow = chunk_key(n, t);
-        st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < (NCT > 0 ? NCT : 1); ++c)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          st[t] = mfma_bf16_k32(lds_row8(cK, arow, s, g), cur.q[s], st[t]);
-          st[t] = mfma_bf16_k32(lds_row8(cK + kQStage, arow, s, g), cur.q[s], st[t]);
-          dp[t] = mfma_bf16_k32(lds_row8(cV, arow, s, g), cur.d[s], dp[t]);
-          dp[t] = mfma_bf16_k32(lds_row8(cV + kQStage, arow, s, g), cur.d[s], dp[t]);
-        }
-        const f32x4 b4 = *(const f32x4*)(cbias + 8 * g + 4 * t);
+    for (int t4 = 0; t4 < 4; ++t4) cpk[c][t4] = cpv[c][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto finish = [&](auto bbc) {
+    constexpr int bb = decltype(bbc)::value;
+    const int pb = pb_first + bb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) add[t][i] = b4[i];
-      }
-      absorb(st, dp, add, cK, cK + kQStage, true);
+    for (int c = 0; c < NCT; ++c) {
+      const bf16* cb0 = ct + c * 4 * 16 * kStride;
+      tile(bbc, cb0, cb0 + 16 * kStride, cb0 + 32 * kStride, cb0 + 48 * kStride, cbias + 16 * c);
     }
-
-    const float Dn = group4_sum(dpart);
+    const float Dn = group4_sum(dpart[bb]);
     if (g == 0) a.dd[tok_base + pb * kBlock + n] = Dn;
-    // ---- write dQ (lane holds dQ[n][16 t4 + 4g + i])
+    const int qrow = block_corner(pb, a.grid) + tile_offset(n, a.grid);
     bf16* dqp = a.dq + (tok_base + qrow) * kDim;
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
       bf16x4 r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = (bf16)((acc_a[t4][i] - Dn * acc_b[t4][i]) * a.scale);
+      for (int i = 0; i < 4; ++i) r[i] = (bf16)((acc_a[bb][t4][i] - Dn * acc_b[bb][t4][i]) * a.scale);
       *(bf16x4*)(dqp + 16 * t4 + 4 * g) = r;
     }
-
-    if (NST > 0) {
-      // ---- coarse partials over this block's 16 queries: dV_c += P^T dO, dK_c += dS^T Q,
-      // with dS = P (dP - D).  The staging tile takes the block's Q rows (0..15) and dO rows
-      // (16..31) from the B-operand registers (lane (n, g) holds row n, channels 32s + 8g..).
-      bf16* stQ = stK;
-      bf16* stO = stK + 16 * kStride;
+    if (NCT > 0) {
+      // Q and dO rows of the block (row n = query n) in the wave's tiles, D per query
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        *(bf16x8*)(stQ + n * kStride + 32 * s + 8 * g) = cur.q[s];
-        *(bf16x8*)(stO + n * kStride + 32 * s + 8 * g) = cur.d[s];
+      for (int s2 = 0; s2 < 2; ++s2) {
+        *(bf16x8*)(kt + n * kStride + 32 * s2 + 8 * g) = qh[bb][s2];
+        *(bf16x8*)(vt + n * kStride + 32 * s2 + 8 * g) = dh[bb][s2];
       }
-      bf16* pH = stP;
-      bf16* pL = stP + 512;
-      bf16* sH = stP + 1024;
-      bf16* sL = stP + 1536;
+      if (g == 0) dsh[n] = Dn;
+      wave_lds_sync();
+      const f32x4 dq4 = *(const f32x4*)(dsh + 4 * g);          // D of queries 4g + i
+      const f32x4 lq4 = *(const f32x4*)(lsh + 16 * bb + 4 * g);  // LSE of queries 4g + i
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int c = 0; c < NCT; ++c) {
+        const bf16* cb0 = ct + c * 4 * 16 * kStride;
+        // S = Q K_c^T, dP = dO V_c^T: lane (n, g) holds queries 4g + i against slot n
+        f32x4 sq = {0.f, 0.f, 0.f, 0.f}, dpq = sq;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          sq = mfma_bf16_k32(qh[bb][s2], lds_row8(cb0, n, s2, g), sq);
+          sq = mfma_bf16_k32(qh[bb][s2], lds_row8(cb0 + 16 * kStride, n, s2, g), sq);
+          dpq = mfma_bf16_k32(dh[bb][s2], lds_row8(cb0 + 32 * kStride, n, s2, g), dpq);
+          dpq = mfma_bf16_k32(dh[bb][s2], lds_row8(cb0 + 48 * kStride, n, s2, g), dpq);
+        }
+        const float bias = cbias[16 * c + n];
+        float pq[4], sv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int kk = 8 * g + i + 4 * t;
-          const float dsv = pc[t][i] * (dpc[t][i] - Dn);
-          const bf16 ph = (bf16)pc[t][i];
-          const bf16 sh = (bf16)dsv;
-          pH[kk * 16 + n] = ph;
-          pL[kk * 16 + n] = (bf16)(pc[t][i] - (float)ph);
-          sH[kk * 16 + n] = sh;
-          sL[kk * 16 + n] = (bf16)(dsv - (float)sh);
+          pq[i] = fast_exp2(fmaf(sq[i], a.c2, bias - lq4[i]));
+          sv[i] = pq[i] * (dpq[i] - dq4[i]);
         }
-      wave_lds_sync();
-      const int r = (lane & 15) >> 2;
-      const int c = lane & 3;
-#pragma unroll
-      for (int st = 0; st < NST; ++st) {
-        const int at = (16 * st + n) * 16 + 4 * g;
-        const bf16x4 pa = *(const bf16x4*)(pH + at);
-        const bf16x4 pl = *(const bf16x4*)(pL + at);
-        const bf16x4 sa = *(const bf16x4*)(sH + at);
-        const bf16x4 sl = *(const bf16x4*)(sL + at);
+        bf16x4 p_hi, p_lo, s_hi, s_lo;
+        split4(pq, p_hi, p_lo);
+        split4(sv, s_hi, s_lo);
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4) {
-          const bf16x4 dob = lds_read_tr16(stO + (4 * g + r) * kStride + 16 * t4 + 4 * c);
-          const bf16x4 qbt = lds_read_tr16(stQ + (4 * g + r) * kStride + 16 * t4 + 4 * c);
-          cpv[st][t4] = mfma_bf16_k16(pa, dob, cpv[st][t4]);
-          cpv[st][t4] = mfma_bf16_k16(pl, dob, cpv[st][t4]);
-          cpk[st][t4] = mfma_bf16_k16(sa, qbt, cpk[st][t4]);
-          cpk[st][t4] = mfma_bf16_k16(sl, qbt, cpk[st][t4]);
+          const int off = (4 * g + r4) * kStride + 16 * t4 + 4 * c4;
+          const bf16x4 dot = lds_read_tr16(vt + off);   // dO^T
+          const bf16x4 qtt = lds_read_tr16(kt + off);   // Q^T
+          cpv[c][t4] = mfma_bf16_k16(dot, p_hi, cpv[c][t4]);
+          cpv[c][t4] = mfma_bf16_k16(dot, p_lo, cpv[c][t4]);
+          cpk[c][t4] = mfma_bf16_k16(qtt, s_hi, cpk[c][t4]);
+          cpk[c][t4] = mfma_bf16_k16(qtt, s_lo, cpk[c][t4]);
         }
       }
       wave_lds_sync();
     }
-    dpart = 0.f;
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) acc_a[t4] = acc_b[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
+  finish(I0{});
+  finish(I1{});
 
-  // one step of the stream: (next block's rows,) next chunk's loads, then chunk `f`; returns
-  // false after the last block.  Two call sites alternate the load buffers (no copies).
-  int cb = 0, cch = 0;   // block and chunk being computed
-  auto step = [&](const FineLd& f, FineLd& refill) -> bool {
-    // the next block's rows are loaded before the chunk loads so that waiting for them
-    // (conditional loads) never drains the chunk prefetch
-    if (lch == 0 && lb > 0 && lb < 4) nxt = load_block(lb);
-    refill = load_next();
-    fine_chunk(f);
-    if (++cch < n_fine) return true;
-    block_end(cb);
-    cch = 0;
-    if (++cb == 4) return false;
-    cur = nxt;
-    return true;
-  };
-  while (step(fa, fb) && step(fb, fa)) {
-  }
-
-  if (NST > 0) {
-    // ---- reduce the four waves' coarse partials (in wave order 0..3) and store them for this
-    // level-2 group.  cp*[st][t4][i] at lane (n, g) is slot 16 st + 4g + i, channel 16 t4 + n.
-    float* red = (float*)cK;   // the shared coarse copy is no longer needed: 16 KB >= 2 x NST KB x 4
-    const int half = NST * 16 * kDim;
-    for (int turn = 0; turn < 4; ++turn) {
+  if (NCT > 0) {
+    // ---- the 4 waves' partials summed in wave order into the unit's rows (the coarse tiles
+    // are no longer read once every wave has passed the first barrier)
+    float* red = (float*)ct;   // [2][16 NCT][64]: dK then dV
+    const int half = NCT * 16 * kDim;
+    for (int turn = 0; turn < kQWaves; ++turn) {
       __syncthreads();
       if (w == turn) {
 #pragma unroll
-        for (int st = 0; st < NST; ++st)
+        for (int c = 0; c < NCT; ++c)
 #pragma unroll
           for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int e = (16 * st + 4 * g + i) * kDim + 16 * t4 + n;
-              red[e] = (turn ? red[e] : 0.f) + cpk[st][t4][i];
-              red[half + e] = (turn ? red[half + e] : 0.f) + cpv[st][t4][i];
+              const int e = (16 * c + n) * kDim + 16 * t4 + 4 * g + i;
+              red[e] = (turn ? red[e] : 0.f) + cpk[c][t4][i];
+              red[half + e] = (turn ? red[half + e] : 0.f) + cpv[c][t4][i];
             }
       }
     }
     __syncthreads();
-    const long out_base = ((long)head * n2 + a2) * n_coarse * kDim;
-    for (int e = threadIdx.x; e < half; e += 256) {
-      if (e / kDim >= n_coarse) continue;
+    const long out_base = ((long)head * kUnits * n2 + rem) * n_coarse * kDim;
+    for (int e = tid; e < n_coarse * kDim; e += 64 * kQWaves) {
       a.part_k[out_base + e] = red[e] * a.scale;
       a.part_v[out_base + e] = red[half + e];
     }
@@ -509,8 +500,9 @@ __global__ __launch_bounds__(256) void coarse_reduce_kernel(BwdArgs a, int l) {
   const int anc = (int)(anc_g - (long)head * nl);
   const int pslot = (l - 2) * K + slot;
   float sk = 0.f, sv = 0.f;
-  for (int c = 0; c < span; ++c) {
-    const long src = (((long)head * n2 + anc * span + c) * n_coarse + pslot) * kDim + ch;
+  for (int c = 0; c < kUnits * span; ++c) {   // the partial units of the ancestor's groups
+    const long src =
+        (((long)head * kUnits * n2 + (long)anc * kUnits * span + c) * n_coarse + pslot) * kDim + ch;
     sk += a.part_k[src];
     sv += a.part_v[src];
   }
@@ -548,7 +540,8 @@ __global__ __launch_bounds__(256) void coarse_grad_kernel(BwdArgs a, int l) {
         int slot = -1;
         for (int s = 0; s < K; ++s)
           if (sel[(long)anc * K + s] == j) slot = s;
-        if (slot >= 0) src = (((long)head * nl + anc) * row_len + slot) * kDim;
+        if (slot >= 0)   // level 2: the first of the ancestor's kUnits partial units
+          src = (((long)head * nl + anc) * (l == 2 ? kUnits : 1) * row_len + slot) * kDim;
       }
     }
     const int cnt = min(64, e1 - base);
@@ -557,6 +550,13 @@ __global__ __launch_bounds__(256) void coarse_grad_kernel(BwdArgs a, int l) {
       if (r >= 0) {
         sk += pk[r + lane];
         sv += pv[r + lane];
+        if (l == 2) {
+#pragma unroll
+          for (int h = 1; h < kUnits; ++h) {
+            sk += pk[r + (long)h * row_len * kDim + lane];
+            sv += pv[r + (long)h * row_len * kDim + lane];
+          }
+        }
       }
     }
   }
@@ -776,8 +776,8 @@ static BwdLayout bwd_layout(const Shape& s) {
   if (s.enrich && s.levels >= 2) {
     const size_t n2 = (size_t)s.n_level(2);
     const size_t nc = (size_t)(s.levels - 1) * s.topk;
-    L.part_k = take(sizeof(float) * s.bh * n2 * nc * kDim);
-    L.part_v = take(sizeof(float) * s.bh * n2 * nc * kDim);
+    L.part_k = take(sizeof(float) * s.bh * n2 * kUnits * nc * kDim);
+    L.part_v = take(sizeof(float) * s.bh * n2 * kUnits * nc * kDim);
     for (int l = 2; l <= s.levels; ++l) {
       const size_t nl = (size_t)s.n_level(l);
       if (l >= 3) {
@@ -842,15 +842,18 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   a.c2 = s.scale * kLog2e;
 
   const int n2 = s.n >> (2 * kBlockShift);
-  const unsigned qblocks = (unsigned)(s.bh * n2);
+  const unsigned qblocks = (unsigned)(s.bh * n2 * kUnits);
   const int n_coarse = coarse ? (s.levels - 1) * s.topk : 0;
-  const size_t qlds = bwd_query_lds_bytes(n_coarse > 0);
+  const size_t qlds = bwd_query_lds_bytes(n_coarse);
   if (n_coarse == 0)
-    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<0>, dim3(qblocks), dim3(256), qlds, stream, a);
+    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<0>, dim3(qblocks), dim3(64 * kQWaves), qlds,
+                stream, a);
   else if (n_coarse <= 16)
-    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<1>, dim3(qblocks), dim3(256), qlds, stream, a);
+    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<1>, dim3(qblocks), dim3(64 * kQWaves), qlds,
+                stream, a);
   else
-    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<2>, dim3(qblocks), dim3(256), qlds, stream, a);
+    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<2>, dim3(qblocks), dim3(64 * kQWaves), qlds,
+                stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (coarse) {
