@@ -7,9 +7,9 @@
 //     the rounded O is never needed), dQ over the block's fine and coarse keys,
 //     and, for the coarse keys, the workgroup's partial dK/dV sums (every query of a level-2
 //     group shares the same coarse keys).
-//  2. coarse_reduce_kernel / coarse_grad_kernel: partials of levels >= 3 are summed over the
-//     level-2 groups of each ancestor, then each coarse key j of level l gathers
-//     dK_l[j] = sum over the ancestors a in CSC_l[j] of the partial of a's slot holding j.
+//  2. coarse_grad_kernel (one launch for all levels >= 2): each coarse key j of level l gathers
+//     dK_l[j] = sum over the ancestors a in CSC_l[j] of the partials of a's slot holding j,
+//     over every partial unit under a.
 //  3. bwd_key_kernel (key-major, one one-wave workgroup per level-1 key block): walks the
 //     query blocks in CSC_1[j] two at a time, accumulates dK, dV on the MFMA, and adds the
 //     pooled gradients pushed down to the block's tokens (dK_l[ancestor] / 16^l, chain rule
@@ -45,8 +45,6 @@ struct BwdArgs {
   float* dd;                   // D, [bh, N]
   float* part_k;               // [bh, n2, kUnits, n_coarse, 64]
   float* part_v;
-  float* lvl_part_k[kMaxLv];   // level l >= 3: [bh, n_l, K, 64]
-  float* lvl_part_v[kMaxLv];
   float* dk_lv[kMaxLv];        // level l >= 2: [bh, n_l, 64]
   float* dv_lv[kMaxLv];
   int bh;
@@ -482,86 +480,129 @@ void bwd_query_kernel(BwdArgs a) {
 }
 
 // ====================================================================== stage 2: coarse keys
-// Level l >= 3: sum the level-2 group partials of the 16^(l-2) groups under each ancestor.
-__global__ __launch_bounds__(256) void coarse_reduce_kernel(BwdArgs a, int l) {
-  const int K = a.topk;
-  const int n2 = a.n >> (2 * kBlockShift);
-  const int nl = a.n >> (kBlockShift * l);
-  const int span = 1 << (kBlockShift * (l - 2));
-  const int n_coarse = (a.levels - 1) * K;
-  const long total = (long)a.bh * nl * K * kDim;
-  const long e = (long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= total) return;
-  const int ch = (int)(e % kDim);
-  const long rest = e / kDim;
-  const int slot = (int)(rest % K);
-  const long anc_g = rest / K;            // head * nl + anc
-  const int head = (int)(anc_g / nl);
-  const int anc = (int)(anc_g - (long)head * nl);
-  const int pslot = (l - 2) * K + slot;
-  float sk = 0.f, sv = 0.f;
-  for (int c = 0; c < kUnits * span; ++c) {   // the partial units of the ancestor's groups
-    const long src =
-        (((long)head * kUnits * n2 + (long)anc * kUnits * span + c) * n_coarse + pslot) * kDim + ch;
-    sk += a.part_k[src];
-    sv += a.part_v[src];
-  }
-  a.lvl_part_k[l - 1][e] = sk;
-  a.lvl_part_v[l - 1][e] = sv;
-}
+// dK_l[j] = sum over the ancestors a in CSC_l[j] of the partial rows of a's slot holding j, over
+// every partial unit under a (kUnits per level-2 group, 16^(l-2) groups per level-l query).
+// One launch for all levels l >= 2, 16-wave workgroups:
+//  * level 2: one wave per key (16 keys per workgroup); a key sums about K * kUnits rows;
+//  * level >= 3: one workgroup per key; its rows (entry, unit) are dealt round-robin to the 16
+//    waves and the waves' sums are added in a fixed order.
+// Lanes first resolve up to 64 CSC entries into partial-row offsets (lane = entry); every lane
+// then sums one channel of the rows, kCgBatch rows per round with all their loads in flight
+// (buffer loads: rows of missing entries read offset kNoRow, i.e. zeros).  Deterministic.
+constexpr int kCgWaves = 16;
+constexpr int kCgBatch = 16;
 
-// dK_l[j] = sum over ancestors a in CSC_l[j] of partial(a, slot of j in Sel_l[a]).
-// One wave per coarse key.  Lanes first resolve up to 64 CSC entries at once (ancestor and
-// slot), then every lane (= channel) sums the partial rows in CSC order.
-__global__ __launch_bounds__(256) void coarse_grad_kernel(BwdArgs a, int l) {
+struct CoarseGradArgs {
+  int first_block[kMaxLv + 1];   // level l's workgroups start at first_block[l - 1]
+};
+
+// Sums over this wave's share (rows i = part, part + nparts, ...) of key j's partial rows.
+__device__ __forceinline__ void coarse_key_sum(const BwdArgs& a, int l, int head, int j,
+                                               int part, int nparts, int lane, float& sk,
+                                               float& sv) {
   const int K = a.topk;
   const int nl = a.n >> (kBlockShift * l);
-  const int wave = uniform((int)(blockIdx.x * 4) + (int)(threadIdx.x >> 6));
-  const int lane = threadIdx.x & 63;
-  if (wave >= a.bh * nl) return;
-  const int head = uniform(wave / nl);
-  const int j = uniform(wave - head * nl);
+  const int n2 = a.n >> (2 * kBlockShift);
   const int n_coarse = (a.levels - 1) * K;
+  const int span = kUnits << (kBlockShift * (l - 2));   // partial units under one ancestor
+  const uint32_t row_bytes = (uint32_t)n_coarse * kDim * 4;   // one unit's partial rows
+  const uint32_t head_bytes = (uint32_t)n2 * kUnits * row_bytes;
+  const long head_floats = (long)n2 * kUnits * n_coarse * kDim;
+  const rsrc_t rk = make_rsrc_uniform(a.part_k + head * head_floats, head_bytes);
+  const rsrc_t rv = make_rsrc_uniform(a.part_v + head * head_floats, head_bytes);
   const int32_t* off = a.csc_off[l - 1] + (long)head * (nl + 1);
   const int32_t* rows = a.csc_rows[l - 1] + (long)head * nl * K;
   const int32_t* sel = a.sel[l - 1] + (long)head * nl * K;
-  const float* pk = l == 2 ? a.part_k : a.lvl_part_k[l - 1];
-  const float* pv = l == 2 ? a.part_v : a.lvl_part_v[l - 1];
-  const int row_len = l == 2 ? n_coarse : K;   // slots per ancestor in the partial arrays
   const int e0 = uniform(off[j]);
   const int e1 = uniform(off[j + 1]);
-  float sk = 0.f, sv = 0.f;
+  float ak[kCgBatch], av[kCgBatch];
+#pragma unroll
+  for (int u = 0; u < kCgBatch; ++u) ak[u] = av[u] = 0.f;
   for (int base = e0; base < e1; base += 64) {
-    const int e = base + lane;
-    long src = -1;
-    if (e < e1) {
-      const int anc = rows[e];
+    const int cnt = min(64, e1 - base);
+    // lane e: byte offset of entry e's row in unit 0 under its ancestor (kNoRow if none)
+    uint32_t src = kNoRow;
+    if (lane < cnt) {
+      const int anc = rows[base + lane];
       if (anc >= 0 && anc < nl) {
         int slot = -1;
         for (int s = 0; s < K; ++s)
           if (sel[(long)anc * K + s] == j) slot = s;
-        if (slot >= 0)   // level 2: the first of the ancestor's kUnits partial units
-          src = (((long)head * nl + anc) * (l == 2 ? kUnits : 1) * row_len + slot) * kDim;
+        if (slot >= 0)
+          src = (uint32_t)anc * span * row_bytes + (uint32_t)((l - 2) * K + slot) * kDim * 4;
       }
     }
-    const int cnt = min(64, e1 - base);
-    for (int i = 0; i < cnt; ++i) {
-      const long r = __shfl(src, i, 64);   // uniform control flow
-      if (r >= 0) {
-        sk += pk[r + lane];
-        sv += pv[r + lane];
-        if (l == 2) {
+    const int total = cnt * span;
+    for (int i0 = part; i0 < total; i0 += nparts * kCgBatch) {
+      float xk[kCgBatch], xv[kCgBatch];
 #pragma unroll
-          for (int h = 1; h < kUnits; ++h) {
-            sk += pk[r + (long)h * row_len * kDim + lane];
-            sv += pv[r + (long)h * row_len * kDim + lane];
-          }
-        }
+      for (int u = 0; u < kCgBatch; ++u) {
+        const int i = i0 + u * nparts;
+        const int e = i < total ? i / span : 0;
+        const uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)src, e);
+        const uint32_t o = (i < total && r != kNoRow)
+                               ? r + (uint32_t)(i - e * span) * row_bytes + 4 * lane
+                               : kNoRow;
+        xk[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rk, o, 0, 0));
+        xv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, o, 0, 0));
+      }
+#pragma unroll
+      for (int u = 0; u < kCgBatch; ++u) {
+        ak[u] += xk[u];
+        av[u] += xv[u];
       }
     }
   }
-  a.dk_lv[l - 1][((long)head * nl + j) * kDim + lane] = sk;
-  a.dv_lv[l - 1][((long)head * nl + j) * kDim + lane] = sv;
+#pragma unroll
+  for (int w = kCgBatch / 2; w >= 1; w >>= 1)
+#pragma unroll
+    for (int u = 0; u < w; ++u) {
+      ak[u] += ak[u + w];
+      av[u] += av[u + w];
+    }
+  sk = ak[0];
+  sv = av[0];
+}
+
+__global__ __launch_bounds__(64 * kCgWaves) void coarse_grad_kernel(BwdArgs a,
+                                                                    CoarseGradArgs cg) {
+  __shared__ float red[2][kCgWaves][kDim];
+  const int lane = threadIdx.x & 63;
+  const int w = uniform(threadIdx.x >> 6);
+  const int bid = blockIdx.x;
+  if (bid < cg.first_block[2]) {   // level 2: one wave per key
+    const int n2 = a.n >> (2 * kBlockShift);
+    const int f = bid * kCgWaves + w;
+    if (f >= a.bh * n2) return;
+    const int head = uniform(f / n2);
+    const int j = uniform(f - head * n2);
+    float sk, sv;
+    coarse_key_sum(a, 2, head, j, 0, 1, lane, sk, sv);
+    a.dk_lv[1][((long)head * n2 + j) * kDim + lane] = sk;
+    a.dv_lv[1][((long)head * n2 + j) * kDim + lane] = sv;
+    return;
+  }
+  int l = 3;
+  while (l < a.levels && bid >= cg.first_block[l]) ++l;
+  const int nl = a.n >> (kBlockShift * l);
+  const int idx = bid - cg.first_block[l - 1];
+  const int head = uniform(idx / nl);
+  const int j = uniform(idx - head * nl);
+  float sk, sv;
+  coarse_key_sum(a, l, head, j, w, kCgWaves, lane, sk, sv);
+  red[0][w][lane] = sk;
+  red[1][w][lane] = sv;
+  __syncthreads();
+  if (w == 0) {
+    float tk = 0.f, tv = 0.f;
+#pragma unroll
+    for (int x = 0; x < kCgWaves; ++x) {
+      tk += red[0][x][lane];
+      tv += red[1][x][lane];
+    }
+    a.dk_lv[l - 1][((long)head * nl + j) * kDim + lane] = tk;
+    a.dv_lv[l - 1][((long)head * nl + j) * kDim + lane] = tv;
+  }
 }
 
 // ====================================================================== stage 3: key-major
@@ -761,7 +802,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 
 // ====================================================================== host side
 struct BwdLayout {
-  size_t dd, part_k, part_v, lvl_k[kMaxLv], lvl_v[kMaxLv], dk_lv[kMaxLv], dv_lv[kMaxLv], total;
+  size_t dd, part_k, part_v, dk_lv[kMaxLv], dv_lv[kMaxLv], total;
 };
 
 static BwdLayout bwd_layout(const Shape& s) {
@@ -780,10 +821,6 @@ static BwdLayout bwd_layout(const Shape& s) {
     L.part_v = take(sizeof(float) * s.bh * n2 * kUnits * nc * kDim);
     for (int l = 2; l <= s.levels; ++l) {
       const size_t nl = (size_t)s.n_level(l);
-      if (l >= 3) {
-        L.lvl_k[l - 1] = take(sizeof(float) * s.bh * nl * s.topk * kDim);
-        L.lvl_v[l - 1] = take(sizeof(float) * s.bh * nl * s.topk * kDim);
-      }
       L.dk_lv[l - 1] = take(sizeof(float) * s.bh * nl * kDim);
       L.dv_lv[l - 1] = take(sizeof(float) * s.bh * nl * kDim);
     }
@@ -824,10 +861,6 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
     a.part_k = (float*)(base + L.part_k);
     a.part_v = (float*)(base + L.part_v);
     for (int l = 2; l <= s.levels; ++l) {
-      if (l >= 3) {
-        a.lvl_part_k[l - 1] = (float*)(base + L.lvl_k[l - 1]);
-        a.lvl_part_v[l - 1] = (float*)(base + L.lvl_v[l - 1]);
-      }
       a.dk_lv[l - 1] = (float*)(base + L.dk_lv[l - 1]);
       a.dv_lv[l - 1] = (float*)(base + L.dv_lv[l - 1]);
     }
@@ -857,18 +890,17 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (coarse) {
-    for (int l = 3; l <= s.levels; ++l) {
-      const long total = (long)s.bh * s.n_level(l) * s.topk * kDim;
-      LLSA_LAUNCH("coarse_reduce_kernel", coarse_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
-                         0, stream, a, l);
-      if ((err = hipGetLastError()) != hipSuccess) return err;
+    CoarseGradArgs cg{};
+    long blocks = 0;
+    for (int l = 2; l <= s.levels; ++l) {   // level 2: kCgWaves keys per workgroup
+      cg.first_block[l - 1] = (int)blocks;
+      const long keys = (long)s.bh * s.n_level(l);
+      blocks += l == 2 ? (keys + kCgWaves - 1) / kCgWaves : keys;
     }
-    for (int l = 2; l <= s.levels; ++l) {
-      const long waves = (long)s.bh * s.n_level(l);
-      LLSA_LAUNCH("coarse_grad_kernel", coarse_grad_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
-                         stream, a, l);
-      if ((err = hipGetLastError()) != hipSuccess) return err;
-    }
+    for (int l = s.levels; l <= kMaxLv; ++l) cg.first_block[l] = (int)blocks;
+    LLSA_LAUNCH("coarse_grad_kernel", coarse_grad_kernel, dim3((unsigned)blocks),
+                dim3(64 * kCgWaves), 0, stream, a, cg);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const long kwaves = (long)s.bh * (s.n >> kBlockShift);
   LLSA_LAUNCH("bwd_key_kernel", bwd_key_kernel, dim3((unsigned)kwaves), dim3(64), 0, stream, a);

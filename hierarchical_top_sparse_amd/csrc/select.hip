@@ -1,32 +1,60 @@
 // Coarse-to-fine top-K selection (paper summary sec. 三; article sec. 三).
 //
-// One wave scores a group of 16 level-l queries against a shared candidate list:
-//   coarsest level L : the group's candidates are all n_L keys (full Q_L K_L^T);
-//   level l < L      : the group is the 16 children of one level-(l+1) query P, and the
-//                      candidates are the 16 children of each of P's K picks (K*B keys,
-//                      one 16x16 score tile per pick, i.e. 16 contiguous key rows).
+// One launch computes every requested level.  Wave w owns a group of 16 sibling queries at
+// the finest requested level lo (the 16 children of query w at level lo + 1, or 16 coarsest
+// queries when lo = L), and first walks the chain of that group's ancestors from level hi
+// down to lo + 1:
+//   * the ancestor at level lv is a single query, ranked against all n_L keys (lv = L) or
+//     against the K*B children of its parent's picks (lv < L);
+//   * the 16 waves (16^2, ...) under one ancestor rank it redundantly with identical
+//     arithmetic, and only the first of them stores its row, so there is no cross-wave
+//     dependency and the whole selection is one kernel.
+// The group itself is then ranked against the children of its parent's picks.
+//
 // Scores are fp32 dot products on the fp32 MFMA (v_mfma_f32_16x16x4f32) in the S^T
 // orientation: lane (n, g) holds the scores of query n against candidates 4g..4g+3 of each
-// tile.  Each lane streams its candidates through a register top-KMAX list, and the four
-// lanes of a query merge their lists with cross-lane reductions.  Ties go to the lower id;
-// the K picks are stored ascending.
+// 16-row candidate tile.  Tiles are loaded kTilesPerRound at a time, so a ranking costs one or
+// two memory round trips rather than one per tile.
+//  * A group (16 queries): each lane keeps a register top-KMAX list of its candidates, and the
+//    four lanes of a query merge their lists with cross-lane steps.
+//  * A single query is replicated over the 16 columns; each (tile, candidate) is then kept by
+//    exactly one lane (lane (n, g) takes candidate 4g + n % 4 of the tiles t with
+//    t % 4 = n / 4), and the 64 lists are merged across the whole wave.
+// Lists only take strictly better scores: every lane sees its candidates in ascending id order
+// (picks are stored ascending), so ties keep the lower id; merges compare (score, id).  The K
+// picks are stored ascending.  The picks a ranking starts from are held one per lane (lane i:
+// pick i) and read with v_readlane.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace llsa {
 
 constexpr int kSelWaves = 4;
+constexpr int kSelMaxLv = 6;
 constexpr int kNoId = 0x7fffffff;
+constexpr int kTilesPerRound = 4;   // candidate tiles loaded at once
+
+struct SelArgs {
+  const float* q[kSelMaxLv];   // level l at index l - 1: [bh, n_l, 64] fp32
+  const float* k[kSelMaxLv];
+  int32_t* sel[kSelMaxLv];     // [bh, n_l, K]
+  int bh;
+  int n;        // tokens per head (level 0)
+  int levels;   // L
+  int topk;     // K
+  int hi, lo;   // levels computed: hi down to lo
+};
 
 __device__ __forceinline__ bool better(float s1, int i1, float s2, int i2) {
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
+// Inserts a candidate whose id is larger than every id already in the list.
 template <int KMAX>
 __device__ __forceinline__ void list_insert(float (&ls)[KMAX], int (&li)[KMAX], float s, int id) {
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    const bool b = better(s, id, ls[j], li[j]);
+    const bool b = s > ls[j];
     const float ts = ls[j];
     const int ti = li[j];
     ls[j] = b ? s : ts;
@@ -36,77 +64,36 @@ __device__ __forceinline__ void list_insert(float (&ls)[KMAX], int (&li)[KMAX], 
   }
 }
 
-// q_l, k_l: [bh, n_l, 64] fp32.  parent: [bh, n_l / 16, K] (nullptr at the coarsest level).
-// out: [bh, n_l, K].
-template <int KMAX>
-__global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
-    const float* __restrict__ q_l, const float* __restrict__ k_l,
-    const int32_t* __restrict__ parent, int32_t* __restrict__ out, int bh, int n_l, int K,
-    int coarsest) {
-  const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * kSelWaves + (threadIdx.x >> 6);
-  const int groups = (n_l + 15) >> 4;
-  if (wave >= bh * groups) return;
-  const int head = wave / groups;
-  const int grp = wave - head * groups;
-  const int n = lane & 15;
-  const int g = lane >> 4;
-  const float* qh = q_l + (long)head * n_l * kDim;
-  const float* kh = k_l + (long)head * n_l * kDim;
-
-  // B operand: Q[a][16g + s] for k-step s (the d axis is permuted so that each lane reads
-  // 16 contiguous channels).
-  const int a = grp * 16 + n;
-  const bool qvalid = a < n_l;
-  f32x4 qv[4];
+// Candidate rows first + n (channels 16g .. 16g + 15) of a 16-row tile; rows outside
+// [0, n_rows) and tiles with first < 0 read as zeros (their scores are never inserted).
+__device__ __forceinline__ void load_tile(const float* kh, int first, int n_rows, int n, int g,
+                                          f32x4 (&kv)[4]) {
+  const int row = first + n;
+  const bool ok = first >= 0 && row < n_rows;
+  const float* p = kh + (long)(ok ? row : 0) * kDim + 16 * g;
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    qv[c] = qvalid ? *(const f32x4*)(qh + (long)a * kDim + 16 * g + 4 * c) : f32x4{0, 0, 0, 0};
+  for (int c = 0; c < 4; ++c) kv[c] = ok ? *(const f32x4*)(p + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+}
 
-  float ls[KMAX];
-  int li[KMAX];
+// acc[i] = score of query n against candidate 4g + i of the tile: the 64 channels are
+// contracted in four independent MFMA chains (channels 16g + 4c + e, e = 0..3, per chain c).
+__device__ __forceinline__ f32x4 score_tile(const f32x4 (&kv)[4], const f32x4 (&qv)[4]) {
+  f32x4 acc[4];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    ls[j] = -INFINITY;
-    li[j] = kNoId;
+  for (int c = 0; c < 4; ++c) {
+    acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[c] = mfma_f32_k4(kv[c][e], qv[c][e], acc[c]);
   }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
 
-  const int tiles = coarsest ? (n_l + 15) >> 4 : K;
-  const int32_t* prow = coarsest ? nullptr : parent + ((long)head * (n_l >> 4) + grp) * K;
-  const int n_parent = n_l >> 4;
-  for (int ct = 0; ct < tiles; ++ct) {
-    // candidate rows of this tile: first + r, r = 0..15
-    int first;
-    bool tile_ok = true;
-    if (coarsest) {
-      first = ct * 16;
-    } else {
-      const int pick = prow[ct];
-      tile_ok = pick >= 0 && pick < n_parent;
-      first = tile_ok ? pick * 16 : 0;
-    }
-    const int crow = first + n;   // A-operand row owned by this lane (m = lane & 15)
-    const bool cvalid = tile_ok && crow < n_l;
-    f32x4 kv[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      kv[c] = cvalid ? *(const f32x4*)(kh + (long)crow * kDim + 16 * g + 4 * c)
-                     : f32x4{0, 0, 0, 0};
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc = mfma_f32_k4(kv[c][e], qv[c][e], acc);
-    // acc[i] = score of query n against candidate row first + 4g + i
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int cid = first + 4 * g + i;
-      if (tile_ok && cid < n_l) list_insert<KMAX>(ls, li, acc[i], cid);
-    }
-  }
-
-  // merge the four lists of query n (lanes n, n+16, n+32, n+48)
-  int pick[KMAX];
+// Extracts the K best (score, id) of the lists of the lanes in one xor-group (the lanes
+// differing only in the bits of lane_bits), best first, into pick[0..K) of all those lanes
+// (kNoId beyond K), then sorts pick ascending.
+template <int KMAX, int LANE_BITS_LO, int LANE_BITS_HI>
+__device__ __forceinline__ void merge_lists(float (&ls)[KMAX], int (&li)[KMAX], int K,
+                                            int (&pick)[KMAX]) {
 #pragma unroll
   for (int r = 0; r < KMAX; ++r) {
     pick[r] = kNoId;
@@ -114,7 +101,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
       float bs = ls[0];
       int bi = li[0];
 #pragma unroll
-      for (int mask = 16; mask <= 32; mask <<= 1) {
+      for (int mask = LANE_BITS_LO; mask <= LANE_BITS_HI; mask <<= 1) {
         const float os = shfl_xor_f(bs, mask);
         const int oi = shfl_xor_i(bi, mask);
         if (better(os, oi, bs, bi)) {
@@ -134,7 +121,6 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
       }
     }
   }
-  // ascending ids (kNoId entries beyond K sort last)
 #pragma unroll
   for (int i = 0; i < KMAX; ++i)
 #pragma unroll
@@ -144,8 +130,133 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
       pick[j] = lo;
       pick[j + 1] = hi;
     }
+}
+
+// Ranks the queries held in qv (columns n) against one candidate set and returns the K picks,
+// ascending, as pick[0..K) (kNoId beyond K): per query n in the lanes of column n (SINGLE:
+// the one query, in every lane).
+//   all_keys: candidates are all n_rows keys of the level;
+//   else:     candidates are the 16 children of each pick in pickv (lane i holds pick i of
+//             the parent, i < K; ids outside [0, n_rows / 16) are skipped).
+template <int KMAX, bool SINGLE>
+__device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool all_keys,
+                                             int pickv, int K, const f32x4 (&qv)[4], int n,
+                                             int g, int (&pick)[KMAX]) {
+  float ls[KMAX];
+  int li[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    ls[j] = -INFINITY;
+    li[j] = kNoId;
+  }
+  const int n_parent = n_rows >> kBlockShift;
+  const int tiles = all_keys ? (n_rows + 15) >> 4 : K;
+  for (int t0 = 0; t0 < tiles; t0 += kTilesPerRound) {
+    f32x4 kv[kTilesPerRound][4];
+    int first[kTilesPerRound];
+#pragma unroll
+    for (int i = 0; i < kTilesPerRound; ++i) {
+      const int t = t0 + i;
+      first[i] = -1;
+      if (t < tiles) {
+        if (all_keys) {
+          first[i] = 16 * t;
+        } else {
+          const int pk = __builtin_amdgcn_readlane(pickv, t);
+          first[i] = (pk >= 0 && pk < n_parent) ? pk * 16 : -1;
+        }
+      }
+      load_tile(kh, first[i], n_rows, n, g, kv[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kTilesPerRound; ++i) {
+      if (first[i] < 0) continue;
+      const f32x4 acc = score_tile(kv[i], qv);
+      if constexpr (SINGLE) {
+        // tile t0 + i is kept by the lanes with n / 4 == i (t0 is a multiple of 4)
+        if ((n >> 2) == i) {
+          const int e = n & 3;
+          const float sc = e == 0 ? acc[0] : e == 1 ? acc[1] : e == 2 ? acc[2] : acc[3];
+          const int cid = first[i] + 4 * g + e;
+          if (cid < n_rows) list_insert<KMAX>(ls, li, sc, cid);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int cid = first[i] + 4 * g + e;
+          if (cid < n_rows) list_insert<KMAX>(ls, li, acc[e], cid);
+        }
+      }
+    }
+  }
+  if constexpr (SINGLE) merge_lists<KMAX, 1, 32>(ls, li, K, pick);
+  else merge_lists<KMAX, 16, 32>(ls, li, K, pick);
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int K = a.topk;
+  const int lo = a.lo;
+  const int n_lo = a.n >> (kBlockShift * lo);
+  const int groups = (n_lo + 15) >> 4;
+  const int wave =
+      uniform(xcd_block((int)blockIdx.x, (int)gridDim.x) * kSelWaves + (int)(threadIdx.x >> 6));
+  if (wave >= a.bh * groups) return;
+  const int head = uniform(wave / groups);
+  const int grp = uniform(wave - head * groups);
+
+  // picks of the parent of the level being ranked, one per lane
+  int pickv = kNoId;
+  if (lo < a.levels) {
+    // the group's parent is query grp at level lo + 1
+    if (a.hi == lo) {   // parent picks given: sel at level lo + 1
+      if (lane < K) pickv = a.sel[lo][((long)head * (n_lo >> 4) + grp) * K + lane];
+    } else {
+      // chain: ancestors at levels hi .. lo + 1, each a single query
+      for (int lv = a.hi; lv > lo; --lv) {
+        const int shift = kBlockShift * (lv - lo - 1);
+        const int anc = grp >> shift;                 // query id at level lv
+        const int n_lv = a.n >> (kBlockShift * lv);
+        const bool top = lv == a.levels;
+        if (lv == a.hi && !top) {
+          // parent picks of the topmost computed ancestor are given at level hi + 1
+          if (lane < K) pickv = a.sel[lv][((long)head * (n_lv >> 4) + (anc >> 4)) * K + lane];
+        }
+        const float* qrow = a.q[lv - 1] + ((long)head * n_lv + anc) * kDim + 16 * g;
+        f32x4 qv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) qv[c] = *(const f32x4*)(qrow + 4 * c);
+        int pick[KMAX];
+        rank_queries<KMAX, true>(a.k[lv - 1] + (long)head * n_lv * kDim, n_lv, top, pickv, K,
+                                 qv, n, g, pick);
+        int nv = kNoId;
+#pragma unroll
+        for (int r = 0; r < KMAX; ++r)
+          if (lane == r) nv = pick[r];
+        pickv = nv;
+        if ((grp & ((1 << shift) - 1)) == 0 && lane < K)
+          a.sel[lv - 1][((long)head * n_lv + anc) * K + lane] = pickv;
+      }
+    }
+  }
+
+  // the group of 16 queries at level lo
+  const float* qh = a.q[lo - 1] + (long)head * n_lo * kDim;
+  const int q_id = grp * 16 + n;
+  const bool qvalid = q_id < n_lo;
+  f32x4 qv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    qv[c] = qvalid ? *(const f32x4*)(qh + (long)q_id * kDim + 16 * g + 4 * c)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+  int pick[KMAX];
+  rank_queries<KMAX, false>(a.k[lo - 1] + (long)head * n_lo * kDim, n_lo, lo == a.levels, pickv,
+                            K, qv, n, g, pick);
   if (g == 0 && qvalid) {
-    int32_t* dst = out + ((long)head * n_l + a) * K;
+    int32_t* dst = a.sel[lo - 1] + ((long)head * n_lo + q_id) * K;
 #pragma unroll
     for (int r = 0; r < KMAX; ++r)
       if (r < K) dst[r] = pick[r];
@@ -154,25 +265,28 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(
 
 hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* const* k_lv,
                          int32_t* const* sel, int level_hi, int level_lo, hipStream_t stream) {
-  for (int l = level_hi; l >= level_lo; --l) {
-    const int n_l = s.n_level(l);
-    const bool coarsest = (l == s.levels);
-    const int groups = (n_l + 15) >> 4;
-    const long waves = (long)s.bh * groups;
-    const unsigned blocks = (unsigned)((waves + kSelWaves - 1) / kSelWaves);
-    const int32_t* parent = coarsest ? nullptr : sel[l];
-    if (s.topk <= 8)
-      LLSA_LAUNCH("select_kernel", select_kernel<8>, dim3(blocks), dim3(64 * kSelWaves), 0, stream,
-                         q_lv[l - 1], k_lv[l - 1], parent, sel[l - 1], s.bh, n_l, s.topk,
-                         (int)coarsest);
-    else
-      LLSA_LAUNCH("select_kernel", select_kernel<16>, dim3(blocks), dim3(64 * kSelWaves), 0, stream,
-                         q_lv[l - 1], k_lv[l - 1], parent, sel[l - 1], s.bh, n_l, s.topk,
-                         (int)coarsest);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+  SelArgs a{};
+  for (int l = 0; l < s.levels && l < kSelMaxLv; ++l) {
+    a.q[l] = q_lv[l];
+    a.k[l] = k_lv[l];
+    a.sel[l] = sel[l];
   }
-  return hipSuccess;
+  a.bh = s.bh;
+  a.n = s.n;
+  a.levels = s.levels;
+  a.topk = s.topk;
+  a.hi = level_hi;
+  a.lo = level_lo;
+  const int n_lo = s.n_level(level_lo);
+  const long waves = (long)s.bh * ((n_lo + 15) >> 4);   // one per group
+  const unsigned blocks = (unsigned)((waves + kSelWaves - 1) / kSelWaves);
+  if (s.topk <= 8)
+    LLSA_LAUNCH("select_kernel", select_kernel<8>, dim3(blocks), dim3(64 * kSelWaves), 0, stream,
+                a);
+  else
+    LLSA_LAUNCH("select_kernel", select_kernel<16>, dim3(blocks), dim3(64 * kSelWaves), 0,
+                stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace llsa

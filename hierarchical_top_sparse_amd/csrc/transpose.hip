@@ -3,15 +3,21 @@
 //
 // Every entry (row r, column c) becomes the 32-bit code (c << rbits) | r.  Sorting the codes
 // groups entries by column with rows ascending, which is exactly the stable counting-sort
-// order; the per-column counts and their prefix sum are then read off the sorted codes as run
-// boundaries.  No atomics anywhere, so the result is deterministic.
-//  * tile_sort_kernel: bitonic sort of 4096-code tiles, 8 codes per thread in registers.
-//    Compare-exchange partners inside a thread are handled in registers, partners in the same
-//    wave by cross-lane shuffles, and only partners in other waves go through LDS.
-//  * merge_kernel: merges sorted runs pairwise; each workgroup owns 2048 consecutive outputs,
-//    finds its input ranges by a merge-path search, stages them in LDS and merges there.
-//  * csc_finalize_kernel: row ids are the low bits of the codes; off[c] = first position whose
-//    column is >= c.
+// order.  The sort is split into runs that are sorted independently; the CSC is then
+// assembled from per-run column bounds, so that no kernel walks a long dependent chain of
+// memory accesses.  No atomics anywhere, so the result is deterministic.
+//  * tile_sort_kernel: bitonic sort of tiles of up to 4096 codes, 8 codes per thread in
+//    registers (partners inside a thread in registers, in the same wave by cross-lane
+//    shuffles, in other waves through LDS).  When the tiles are the final runs it also writes
+//    the tile's column bounds lb[c] = #codes of the tile with column < c, c = 0..cols, by
+//    binary searches in LDS (8 columns per thread in lockstep).
+//  * merge_kernel: merges sorted runs pairwise (merge-path split, LDS staging); only used
+//    while more than kMaxRuns runs remain.  csc_bounds_kernel then writes the bounds of the
+//    merged runs (the same searches, in memory).
+//  * csc_offsets_kernel (thread per column): off[c] = sum over runs of lb_r[c]; the run-r
+//    codes of column c go to off[c] + sum_{r' < r} count_{r'}(c) onwards (runs are
+//    consecutive row ranges of the CSR, so rows stay ascending).
+//  * csc_scatter_kernel (thread per code): rows[start_r(c) + position in run - lb_r[c]].
 // Codes of columns outside [0, cols) get the column `cols` and sort behind every kept entry.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -22,6 +28,7 @@ constexpr int kPerThread = 8;
 constexpr int kMaxTile = 4096;                     // codes per sort workgroup (512 threads)
 constexpr int kMergeOut = 2048;                    // outputs per merge workgroup
 constexpr int kMergeThreads = 256;
+constexpr int kMaxRuns = 32;                       // sorted runs the CSC is assembled from
 
 __device__ __forceinline__ void cmp_swap(uint32_t& lo, uint32_t& hi, bool asc) {
   const uint32_t a = lo, b = hi;
@@ -77,11 +84,40 @@ __device__ __forceinline__ void bitonic_sort(uint32_t (&v)[kPerThread], uint32_t
 }
 
 // Sorts tiles of THREADS * 8 codes; tile i of matrix m covers entries [i*TILE, +TILE).
+// lb[c] = first position of sorted codes[0, len) whose column is >= c, for the columns
+// c = c_first + j * c_step, j < 8, searched in lockstep (8 independent binary searches).
+// Column `cols` (where dropped entries sort) bounds the kept codes.
+template <typename Codes>
+__device__ __forceinline__ void column_bounds8(const Codes& codes, int len, int c_first, int c_step,
+                                               int cols, int rbits, int32_t* lb) {
+  int lo[8], hi[8];
+  uint32_t key[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    lo[j] = 0;
+    hi[j] = len;
+    key[j] = (uint32_t)min(c_first + j * c_step, cols) << rbits;
+  }
+  for (int span = len; span > 0; span >>= 1) {   // ceil(log2(len + 1)) rounds
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (lo[j] < hi[j]) {
+        const int mid = (lo[j] + hi[j]) >> 1;
+        if (codes[mid] < key[j]) lo[j] = mid + 1;
+        else hi[j] = mid;
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (c_first + j * c_step <= cols) lb[c_first + j * c_step] = lo[j];
+}
+
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void tile_sort_kernel(const int32_t* __restrict__ csr,
                                                             uint32_t* __restrict__ out, int nnz,
                                                             int k, int cols, int rbits,
-                                                            int tiles_per_mat) {
+                                                            int tiles_per_mat,
+                                                            int32_t* __restrict__ bounds) {
   constexpr int TILE = THREADS * kPerThread;
   __shared__ uint32_t s[TILE];
   const int mat = blockIdx.x / tiles_per_mat;
@@ -106,6 +142,16 @@ __global__ __launch_bounds__(THREADS) void tile_sort_kernel(const int32_t* __res
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e)
     if (base + e < nnz) dst[base + e] = v[e];
+  if (bounds) {   // the tiles are the final runs: write this tile's column bounds
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kPerThread; ++e) s[kPerThread * t + e] = v[e];
+    __syncthreads();
+    const int len = min(TILE, nnz - tile * TILE);
+    int32_t* lb = bounds + (long)blockIdx.x * (cols + 1);
+    for (int c0 = t; c0 <= cols; c0 += 8 * THREADS)
+      column_bounds8(s, len, c0, THREADS, cols, rbits, lb);
+  }
 }
 
 // Number of the first `diag` merged outputs that come from A (ties: A first), searched by the
@@ -193,26 +239,70 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const uint32_t* __
   }
 }
 
-// off[c] = first sorted position whose column is >= c; rows = low bits of the codes.
-__global__ __launch_bounds__(256) void csc_finalize_kernel(const uint32_t* __restrict__ codes,
-                                                           int32_t* __restrict__ off,
-                                                           int32_t* __restrict__ rows_out,
-                                                           int nnz, int cols, int rbits,
-                                                           long total) {
-  const long gi = (long)blockIdx.x * 256 + threadIdx.x;
-  if (gi >= total) return;
-  const int mat = (int)(gi / nnz);
-  const int i = (int)(gi - (long)mat * nnz);
-  const uint32_t* c = codes + (long)mat * nnz;
-  int32_t* o = off + (long)mat * (cols + 1);
-  const uint32_t code = c[i];
+// Column bounds of merged runs: thread per (run, 8 columns), searching the run in memory.
+__global__ __launch_bounds__(256) void csc_bounds_kernel(const uint32_t* __restrict__ codes,
+                                                         int32_t* __restrict__ bounds, int nnz,
+                                                         int cols, int rbits, int run,
+                                                         int nruns) {
+  const int mat = blockIdx.z;
+  const int r = blockIdx.y;
+  const int c0 = blockIdx.x * 256 * 8 + threadIdx.x;
+  if (c0 > cols) return;
+  const int len = min(run, nnz - r * run);
+  const uint32_t* cm = codes + (long)mat * nnz + (long)r * run;
+  column_bounds8(cm, len, c0, 256, cols, rbits, bounds + ((long)mat * nruns + r) * (cols + 1));
+}
+
+// Thread per column c = 0..cols: off[c], and start[r][c] = where run r's codes of column c go,
+// minus lb_r[c] (so that a code at run position i lands at start[r][c] + i).
+__global__ __launch_bounds__(256) void csc_offsets_kernel(const int32_t* __restrict__ bounds,
+                                                          int32_t* __restrict__ start,
+                                                          int32_t* __restrict__ off, int cols,
+                                                          int nruns) {
+  const int mat = blockIdx.y;
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c > cols) return;
+  const int32_t* lb = bounds + (long)mat * nruns * (cols + 1);
+  int lo[kMaxRuns], hi[kMaxRuns];
+  int total = 0;
+#pragma unroll
+  for (int r = 0; r < kMaxRuns; ++r) {
+    lo[r] = hi[r] = 0;
+    if (r < nruns) {
+      lo[r] = lb[(long)r * (cols + 1) + c];
+      if (c < cols) hi[r] = lb[(long)r * (cols + 1) + c + 1];
+    }
+    total += lo[r];
+  }
+  off[(long)mat * (cols + 1) + c] = total;
+  if (c == cols) return;
+  int32_t* st = start + (long)mat * nruns * cols;
+  int acc = total;
+#pragma unroll
+  for (int r = 0; r < kMaxRuns; ++r)
+    if (r < nruns) {
+      st[(long)r * cols + c] = acc - lo[r];
+      acc += hi[r] - lo[r];
+    }
+}
+
+// Thread per code: its row goes to start[r][column] + its position in run r.
+__global__ __launch_bounds__(256) void csc_scatter_kernel(const uint32_t* __restrict__ codes,
+                                                          const int32_t* __restrict__ start,
+                                                          int32_t* __restrict__ rows_out, int nnz,
+                                                          int cols, int rbits, int run,
+                                                          int nruns) {
+  const int mat = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= nnz) return;
+  const uint32_t code = codes[(long)mat * nnz + i];
+  const int c = (int)(code >> rbits);
+  if (c >= cols) return;   // dropped entry
+  const int r = i / run;
+  const int local = i - r * run;
   const uint32_t rmask = rbits ? ((1u << rbits) - 1u) : 0u;
-  rows_out[(long)mat * nnz + i] = (int32_t)(code & rmask);
-  const int key = (int)(code >> rbits);
-  const int prev = i > 0 ? (int)(c[i - 1] >> rbits) : -1;
-  for (int kk = prev + 1; kk <= key && kk <= cols; ++kk) o[kk] = i;
-  if (i == nnz - 1)
-    for (int kk = key + 1; kk <= cols; ++kk) o[kk] = nnz;
+  const int pos = start[((long)mat * nruns + r) * cols + c] + local;
+  rows_out[(long)mat * nnz + pos] = (int32_t)(code & rmask);
 }
 
 static int ceil_log2(int v) {
@@ -221,9 +311,37 @@ static int ceil_log2(int v) {
   return b;
 }
 
+struct TransposePlan {
+  int threads;   // tile-sort workgroup size: tiles of threads * 8 codes
+  int tile;
+  int tiles;
+  int run;       // length of the final sorted runs (after merges)
+  int nruns;
+};
+
+static TransposePlan plan_transpose(int rows, int k) {
+  TransposePlan p{};
+  const int nnz = rows * k;
+  p.threads = 64;   // the smallest tile that holds a matrix, up to 4096 codes
+  while (p.threads * kPerThread < nnz && p.threads * kPerThread < kMaxTile) p.threads *= 2;
+  p.tile = p.threads * kPerThread;
+  p.tiles = (nnz + p.tile - 1) / p.tile;
+  p.run = p.tile;
+  while ((nnz + p.run - 1) / p.run > kMaxRuns) p.run <<= 1;
+  p.nruns = (nnz + p.run - 1) / p.run;
+  return p;
+}
+
+// Workspace: two code buffers [nmat, nnz], the run bounds [nmat, nruns, cols + 1] and the run
+// starts [nmat, nruns, cols], each 256-byte aligned.
+static size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
 size_t transpose_workspace_bytes(int nmat, int rows, int cols, int k) {
-  (void)cols;
-  return 2 * sizeof(uint32_t) * (size_t)nmat * (size_t)rows * (size_t)k;
+  const TransposePlan p = plan_transpose(rows, k);
+  const size_t nnz = (size_t)rows * k;
+  return 2 * align256(sizeof(uint32_t) * nmat * nnz) +
+         align256(sizeof(int32_t) * nmat * p.nruns * ((size_t)cols + 1)) +
+         align256(sizeof(int32_t) * nmat * p.nruns * (size_t)cols);
 }
 
 hipError_t launch_index_transpose(int nmat, int rows, int cols, int k, const int32_t* csr,
@@ -231,44 +349,58 @@ hipError_t launch_index_transpose(int nmat, int rows, int cols, int k, const int
                                   hipStream_t stream) {
   const int nnz = rows * k;
   const int rbits = ceil_log2(rows);
-  uint32_t* buf[2] = {(uint32_t*)ws, (uint32_t*)ws + (size_t)nmat * nnz};
-  // the smallest tile that holds a matrix, up to 4096 codes (then merge passes)
-  int threads = 64;
-  while (threads * kPerThread < nnz && threads * kPerThread < kMaxTile) threads *= 2;
-  const int tile = threads * kPerThread;
-  const int tiles = (nnz + tile - 1) / tile;
-  const dim3 grid((unsigned)(nmat * tiles));
-  switch (threads) {
+  const TransposePlan p = plan_transpose(rows, k);
+  char* w = (char*)ws;
+  const size_t code_bytes = align256(sizeof(uint32_t) * nmat * (size_t)nnz);
+  uint32_t* buf[2] = {(uint32_t*)w, (uint32_t*)(w + code_bytes)};
+  int32_t* bounds = (int32_t*)(w + 2 * code_bytes);
+  int32_t* starts =
+      (int32_t*)(w + 2 * code_bytes + align256(sizeof(int32_t) * nmat * p.nruns * ((size_t)cols + 1)));
+  const bool merged = p.nruns < p.tiles;
+  int32_t* tile_bounds = merged ? nullptr : bounds;
+  const dim3 grid((unsigned)(nmat * p.tiles));
+  switch (p.threads) {
     case 64:
-      LLSA_LAUNCH("tile_sort_kernel", tile_sort_kernel<64>, grid, dim3(64), 0, stream, csr, buf[0], nnz, k,
-                         cols, rbits, tiles);
+      LLSA_LAUNCH("tile_sort_kernel", tile_sort_kernel<64>, grid, dim3(64), 0, stream, csr,
+                  buf[0], nnz, k, cols, rbits, p.tiles, tile_bounds);
       break;
     case 128:
-      LLSA_LAUNCH("tile_sort_kernel", tile_sort_kernel<128>, grid, dim3(128), 0, stream, csr, buf[0], nnz, k,
-                         cols, rbits, tiles);
+      LLSA_LAUNCH("tile_sort_kernel", tile_sort_kernel<128>, grid, dim3(128), 0, stream, csr,
+                  buf[0], nnz, k, cols, rbits, p.tiles, tile_bounds);
       break;
     case 256:
-      LLSA_LAUNCH("tile_sort_kernel", tile_sort_kernel<256>, grid, dim3(256), 0, stream, csr, buf[0], nnz, k,
-                         cols, rbits, tiles);
+      LLSA_LAUNCH("tile_sort_kernel", tile_sort_kernel<256>, grid, dim3(256), 0, stream, csr,
+                  buf[0], nnz, k, cols, rbits, p.tiles, tile_bounds);
       break;
     default:
-      LLSA_LAUNCH("tile_sort_kernel", tile_sort_kernel<512>, grid, dim3(512), 0, stream, csr, buf[0], nnz, k,
-                         cols, rbits, tiles);
+      LLSA_LAUNCH("tile_sort_kernel", tile_sort_kernel<512>, grid, dim3(512), 0, stream, csr,
+                  buf[0], nnz, k, cols, rbits, p.tiles, tile_bounds);
       break;
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   int cur = 0;
   const unsigned mtiles = (unsigned)((nnz + kMergeOut - 1) / kMergeOut);
-  for (int run = tile; run < nnz; run <<= 1) {
-    LLSA_LAUNCH("merge_kernel", merge_kernel, dim3(mtiles, (unsigned)nmat), dim3(kMergeThreads), 0,
-                       stream, buf[cur], buf[cur ^ 1], nnz, run);
+  for (int run = p.tile; run < p.run; run <<= 1) {
+    LLSA_LAUNCH("merge_kernel", merge_kernel, dim3(mtiles, (unsigned)nmat), dim3(kMergeThreads),
+                0, stream, buf[cur], buf[cur ^ 1], nnz, run);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     cur ^= 1;
   }
-  const long total = (long)nmat * nnz;
-  LLSA_LAUNCH("csc_finalize_kernel", csc_finalize_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
-                     stream, buf[cur], off, rows_out, nnz, cols, rbits, total);
+  const unsigned code_blocks = (unsigned)((nnz + 255) / 256);
+  if (merged) {
+    LLSA_LAUNCH("csc_bounds_kernel", csc_bounds_kernel,
+                dim3((unsigned)((cols + 1 + 2047) / 2048), (unsigned)p.nruns, (unsigned)nmat),
+                dim3(256), 0, stream, buf[cur], bounds, nnz, cols, rbits, p.run, p.nruns);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  LLSA_LAUNCH("csc_offsets_kernel", csc_offsets_kernel,
+              dim3((unsigned)((cols + 1 + 255) / 256), (unsigned)nmat), dim3(256), 0, stream,
+              bounds, starts, off, cols, p.nruns);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  LLSA_LAUNCH("csc_scatter_kernel", csc_scatter_kernel, dim3(code_blocks, (unsigned)nmat),
+              dim3(256), 0, stream, buf[cur], starts, rows_out, nnz, cols, rbits, p.run,
+              p.nruns);
   return hipGetLastError();
 }
 

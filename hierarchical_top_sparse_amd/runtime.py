@@ -6,6 +6,11 @@ order.  `capture()` records the whole sequence into a HIP graph (torch.cuda.CUDA
 ROCm) so that replays do not wait on the host between calls; the library allocates nothing
 and never synchronises, and none of its calls records a memset, so the whole step can be
 captured.
+
+The CSR->CSC transposes depend only on the selection, and the sparse forward does not read
+them: `run(overlap=True)` (the default) issues them on a second stream, forked after the
+selection and joined before the backward, so that these small, latency-bound kernels run
+beside the HBM-bound forward instead of after it.  All streams have the default priority.
 """
 from __future__ import annotations
 
@@ -44,28 +49,52 @@ class Step:
         self.bws = torch.empty(max(bws, 16), device=dev, dtype=torch.uint8)
         self.dq, self.dk, self.dv = (torch.empty_like(q) for _ in range(3))
         self.graph = None
+        self.side = torch.cuda.Stream(device=dev)
 
-    def calls(self):
-        """(name, thunk) for every C-ABI call of one step, in order."""
+    def _transpose_calls(self):
         a, p = _abi, self.p
-        out = [("pool", lambda: a.llsa_pool(p, self.q, self.k, self.v if self.pool_v else None,
-                                            self.q_lv, self.k_lv, self.v_lv)),
-               ("select", lambda: a.llsa_select(p, self.q_lv, self.k_lv, self.sel)),
-               ("attn_fwd", lambda: a.llsa_attn_fwd(p, self.q, self.k, self.v, self.k_lv,
-                                                    self.v_lv, self.sel, self.o, self.lse))]
+        out = []
         for l in range(1, self.csc_levels + 1):
             nl = p.n_level(l)
             out.append((f"transpose_l{l}", (lambda l=l, nl=nl: a.llsa_index_transpose(
                 self.nmat, nl, nl, p.topk, self.sel[l - 1], self.off[l - 1], self.rows[l - 1],
                 self.tws))))
-        out.append(("attn_bwd", lambda: a.llsa_attn_bwd(
-            p, self.q, self.k, self.v, self.dout, self.lse, self.k_lv, self.v_lv, self.sel,
-            self.off, self.rows, self.dq, self.dk, self.dv, self.bws)))
         return out
 
-    def run(self):
-        """One eager step on the current stream."""
-        for _, fn in self.calls():
+    def calls(self):
+        """(name, thunk) for every C-ABI call of one step, in order (one stream)."""
+        a, p = _abi, self.p
+        head = [("pool", lambda: a.llsa_pool(p, self.q, self.k, self.v if self.pool_v else None,
+                                             self.q_lv, self.k_lv, self.v_lv)),
+                ("select", lambda: a.llsa_select(p, self.q_lv, self.k_lv, self.sel))]
+        fwd = [("attn_fwd", lambda: a.llsa_attn_fwd(p, self.q, self.k, self.v, self.k_lv,
+                                                     self.v_lv, self.sel, self.o, self.lse))]
+        bwd = [("attn_bwd", lambda: a.llsa_attn_bwd(
+            p, self.q, self.k, self.v, self.dout, self.lse, self.k_lv, self.v_lv, self.sel,
+            self.off, self.rows, self.dq, self.dk, self.dv, self.bws))]
+        self._parts = (head, fwd, self._transpose_calls(), bwd)
+        return head + fwd + self._parts[2] + bwd
+
+    def run(self, overlap: bool = True):
+        """One step on the current stream; with overlap, the transposes run on a side stream
+        between the selection and the backward."""
+        self.calls()
+        head, fwd, tr, bwd = self._parts
+        for _, fn in head:
+            fn()
+        if not overlap:
+            for _, fn in fwd + tr + bwd:
+                fn()
+            return
+        main = torch.cuda.current_stream()
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            for _, fn in tr:
+                fn()
+        for _, fn in fwd:
+            fn()
+        main.wait_stream(self.side)
+        for _, fn in bwd:
             fn()
 
     def capture(self, warmup: int = 1):

@@ -100,7 +100,10 @@ def test_entry_points_reject_null_and_misaligned(L):
 def test_workspace_queries(L):
     f, b = abi.llsa_workspace_bytes(_p(dtype=abi.LLSA_BF16))
     assert f == 0 and b > 0
-    assert abi.llsa_index_transpose_workspace(6, 4096, 4096, 8) == 2 * 4 * 6 * 4096 * 8
+    # two code buffers + per-run column bounds (cols + 1) and run starts (cols): 8 runs of 4096
+    a256 = lambda x: (x + 255) // 256 * 256
+    assert abi.llsa_index_transpose_workspace(6, 4096, 4096, 8) == (
+        2 * a256(4 * 6 * 4096 * 8) + a256(4 * 6 * 8 * 4097) + a256(4 * 6 * 8 * 4096))
     out = ctypes.c_size_t()
     assert L.llsa_index_transpose_workspace(1, 0, 4, 8, ctypes.byref(out)) == 2
     assert L.llsa_index_transpose_workspace(1, 1 << 20, 1 << 13, 8, ctypes.byref(out)) == 2

@@ -105,12 +105,47 @@ def test_select_single_level_from_given_parent():
         check_level(got[0, i], q_lv[0][0, i], k_lv[0][0, i], parent[i], 8, f"head {i}")
 
 
+@pytest.mark.parametrize("h,w,L,K,level_hi,level_lo", [
+    (256, 256, 3, 6, 2, 1), (256, 256, 3, 6, 3, 2), (256, 256, 3, 6, 2, 2),
+    (256, 256, 3, 6, 3, 3), (512, 512, 4, 4, 3, 1), (512, 512, 4, 4, 4, 1)])
+def test_select_level_range_from_given_parent(h, w, L, K, level_hi, level_lo):
+    """llsa_select over a sub-range of levels: levels above level_hi come from the oracle;
+    every computed level is checked teacher-forced on the GPU's parents (a chain of several
+    single-query ancestors when level_hi - level_lo >= 2)."""
+    from tests.parity_util import check_level
+    d, ref = _inputs(1, 2, h, w, torch.bfloat16, 29)
+    p = _problem(d["q"], h, w, L, K)
+    fwd = ops.llsa_forward(p, d["q"], d["k"], d["v"])
+    q_lv = orc.pool_levels(orc.reorder(ref["q"], h, w), 16, L)
+    k_lv = orc.pool_levels(orc.reorder(ref["k"], h, w), 16, L)
+    want = [orc.select(q_lv_h, k_lv_h, 16, K) for q_lv_h, k_lv_h in
+            zip(zip(*[x[0] for x in q_lv]), zip(*[x[0] for x in k_lv]))]
+    sel = [torch.full_like(s, -7) for s in fwd["sel"]]
+    for l in range(level_hi + 1, L + 1):
+        sel[l - 1] = torch.from_numpy(np.stack([want[i][l - 1] for i in range(2)])[None]
+                                      .astype(np.int32)).to(DEV)
+    _abi.llsa_select(p, fwd["q_lv"], fwd["k_lv"], sel, level_hi=level_hi, level_lo=level_lo)
+    got = [s.cpu().numpy().astype(np.int64) for s in sel]
+    for l in range(L, 0, -1):
+        for i in range(2):
+            if l > level_hi:
+                continue
+            if l < level_lo:   # untouched
+                assert (got[l - 1][0, i] == -7).all()
+                continue
+            parent = None if l == L else got[l][0, i]
+            check_level(got[l - 1][0, i], q_lv[l - 1][0, i], k_lv[l - 1][0, i], parent, K,
+                        f"levels {level_hi}..{level_lo} head {i} level {l}")
+
+
 # ----------------------------------------------------------------------------- transpose
 
 
 @pytest.mark.parametrize("nmat,rows,cols,k,seed", [(1, 16, 16, 8, 0), (3, 256, 256, 8, 1),
                                                    (2, 4096, 4096, 8, 2), (1, 16384, 16384, 8, 3),
-                                                   (2, 1000, 333, 5, 4), (1, 300, 7, 3, 5)])
+                                                   (2, 1000, 333, 5, 4), (1, 300, 7, 3, 5),
+                                                   (1, 32768, 32768, 8, 6),
+                                                   (1, 40000, 500, 7, 7)])
 def test_index_transpose_bit_exact(nmat, rows, cols, k, seed):
     rng = np.random.default_rng(seed)
     csr = np.stack([np.sort(np.stack([rng.choice(cols, k, replace=False) for _ in range(rows)]),

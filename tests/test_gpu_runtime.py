@@ -1,6 +1,7 @@
-"""GPU checks of the step runner: HIP-graph replays of a whole fwd+bwd step equal the eager
-step bit for bit (several replays, with eager work and synchronisations in between), and the
-per-kernel profiling hook reports every kernel of a step."""
+"""GPU checks of the step runner: HIP-graph replays of a whole fwd+bwd step (transposes on a
+side stream) equal the one-stream eager step bit for bit (several replays, with eager work
+and synchronisations in between), and the per-kernel profiling hook reports every kernel of
+a step."""
 import pytest
 import torch
 
@@ -23,15 +24,18 @@ def _make(h=128, w=128, levels=2, batch=1, heads=2, seed=61):
 @pytest.mark.parametrize("h,w,levels", [(128, 128, 2), (128, 256, 3)])
 def test_graph_replays_match_eager(h, w, levels):
     step = _make(h, w, levels)
-    step.run()
+    step.run(overlap=False)    # one stream: the reference for the overlapped graph
     torch.cuda.synchronize()
     want = {k: v.clone() for k, v in step.outputs().items() if k != "sel"}
     want_sel = [s.clone() for s in step.sel]
+    want_csc = [t.clone() for t in step.off + step.rows]
     step.capture()
     other = _make(64, 64, 2, seed=62)
     for rep in range(3):
         for t in (step.o, step.dq, step.dk, step.dv, step.lse):
             t.zero_()
+        for t in step.off + step.rows + step.sel:
+            t.fill_(-1)
         torch.cuda.synchronize()
         step.replay()
         torch.cuda.synchronize()
@@ -39,6 +43,8 @@ def test_graph_replays_match_eager(h, w, levels):
             assert torch.equal(_bits(getattr(step, name)), _bits(ref)), (rep, name)
         for s, ref in zip(step.sel, want_sel):
             assert torch.equal(s, ref), rep
+        for t, ref in zip(step.off + step.rows, want_csc):
+            assert torch.equal(t, ref), rep
         other.run()             # unrelated eager work between replays
         torch.cuda.synchronize()
 
@@ -54,7 +60,7 @@ def test_profile_hook_reports_every_kernel():
     _abi.llsa_profile_enable(False)
     prof = _abi.llsa_profile_read()
     for name in ("pool12_kernel", "select_kernel", "attn_fwd_kernel", "tile_sort_kernel",
-                 "csc_finalize_kernel", "bwd_query_kernel", "coarse_grad_kernel",
+                 "csc_offsets_kernel", "csc_scatter_kernel", "bwd_query_kernel", "coarse_grad_kernel",
                  "bwd_key_kernel"):
         assert name in prof, name
         cnt, ms = prof[name]
