@@ -92,6 +92,10 @@ def lib() -> ctypes.CDLL:
             "llsa_index_transpose": ([i32, i32, i32, i32, vp, vp, vp, vp, sz, vp], i32),
             "llsa_attn_bwd": ([P, vp, vp, vp, vp, vp, pp, pp, pp, pp, pp, vp, vp, vp, vp, sz,
                                vp], i32),
+            "llsa_dense_attn_fwd": ([i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp],
+                                    i32),
+            "llsa_dense_attn_bwd": ([i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, vp, vp], i32),
             "llsa_profile_enable": ([i32], i32),
             "llsa_profile_read": ([ctypes.c_char_p, sz], i32),
         }
@@ -107,7 +111,8 @@ def exported_symbols() -> list:
     return ["llsa_abi_version", "llsa_status_str", "llsa_last_error", "llsa_check",
             "llsa_workspace_bytes", "llsa_reorder", "llsa_pool", "llsa_select", "llsa_attn_fwd",
             "llsa_index_transpose_workspace", "llsa_index_transpose", "llsa_attn_bwd",
-            "llsa_profile_enable", "llsa_profile_read"]
+            "llsa_dense_attn_fwd", "llsa_dense_attn_bwd", "llsa_profile_enable",
+            "llsa_profile_read"]
 
 
 def _raise(status: int, name: str):
@@ -272,6 +277,35 @@ def llsa_attn_bwd(p: Problem, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_
                                _ptrs(csc_off), _ptrs(csc_rows), _ptr(dq), _ptr(dk), _ptr(dv),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "llsa_attn_bwd")
+
+
+def _dense_shapes(q):
+    if q.dim() < 2:
+        raise ValueError("dense attention tensors are [..., n, head_dim]")
+    n, d = q.shape[-2], q.shape[-1]
+    return q.numel() // (n * d), n, d
+
+
+def llsa_dense_attn_fwd(q, k, v, o, lse, scale=0.0, stream=None):
+    """Dense softmax attention over [..., n, 64] bf16 (the full-attention baseline)."""
+    bh, n, d = _dense_shapes(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _expect(t, tuple(q.shape), torch.bfloat16, name)
+    _expect(lse, tuple(q.shape[:-1]), torch.float32, "lse")
+    _raise(lib().llsa_dense_attn_fwd(bh, n, d, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                     _ptr(lse), _stream(stream)), "llsa_dense_attn_fwd")
+
+
+def llsa_dense_attn_bwd(q, k, v, dout, lse, dq, dk, dv, d_rows, scale=0.0, stream=None):
+    bh, n, d = _dense_shapes(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _expect(t, tuple(q.shape), torch.bfloat16, name)
+    _expect(lse, tuple(q.shape[:-1]), torch.float32, "lse")
+    _expect(d_rows, tuple(q.shape[:-1]), torch.float32, "d_rows")
+    _raise(lib().llsa_dense_attn_bwd(bh, n, d, float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                     _ptr(d_rows), _stream(stream)), "llsa_dense_attn_bwd")
 
 
 def llsa_profile_enable(on: bool):

@@ -292,3 +292,61 @@ int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const
 }
 
 }  // extern "C"
+
+namespace {
+
+int32_t check_dense(int32_t batch_heads, int32_t n, int32_t head_dim, float scale) {
+  if (batch_heads < 1) return fail(LLSA_ERR_SHAPE, "batch_heads %d must be >= 1", batch_heads);
+  if (head_dim != 64)
+    return fail(LLSA_ERR_UNSUPPORTED, "head_dim %d: only 64 is implemented", head_dim);
+  if (n < 128 || n % 128 != 0 || n > (1 << 23))
+    return fail(LLSA_ERR_SHAPE, "N = %d: a multiple of 128 in [128, 2^23] is needed", n);
+  if ((long)batch_heads * n >= (1L << 31))
+    return fail(LLSA_ERR_SHAPE, "batch_heads*N must be < 2^31");
+  if (!(scale >= 0.f) || std::isinf(scale))
+    return fail(LLSA_ERR_SHAPE, "scale must be finite and >= 0");
+  return LLSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t llsa_dense_attn_fwd(int32_t batch_heads, int32_t n, int32_t head_dim, float scale,
+                            const void* q, const void* k, const void* v, void* o, float* lse,
+                            void* stream) {
+  int32_t st = check_dense(batch_heads, n, head_dim, scale);
+  if (st != LLSA_OK) return st;
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(o, "o");
+  CHECK_PTR(lse, "lse");
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
+  return hip_status(llsa::launch_dense_fwd(batch_heads, n, sc, q, k, v, o, lse,
+                                           (hipStream_t)stream),
+                    "llsa_dense_attn_fwd");
+}
+
+int32_t llsa_dense_attn_bwd(int32_t batch_heads, int32_t n, int32_t head_dim, float scale,
+                            const void* q, const void* k, const void* v, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, float* d_rows,
+                            void* stream) {
+  int32_t st = check_dense(batch_heads, n, head_dim, scale);
+  if (st != LLSA_OK) return st;
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(dout, "dout");
+  CHECK_PTR(lse, "lse");
+  CHECK_PTR(dq, "dq");
+  CHECK_PTR(dk, "dk");
+  CHECK_PTR(dv, "dv");
+  CHECK_PTR(d_rows, "d_rows");
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
+  return hip_status(llsa::launch_dense_bwd(batch_heads, n, sc, q, k, v, dout, lse, dq, dk, dv,
+                                           d_rows, (hipStream_t)stream),
+                    "llsa_dense_attn_bwd");
+}
+
+}  // extern "C"

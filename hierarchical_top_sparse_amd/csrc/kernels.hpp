@@ -60,4 +60,11 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
                            const int32_t* const* csc_rows, void* dq, void* dk, void* dv,
                            void* ws, hipStream_t stream);
 
+// Dense softmax attention over [bh, n, 64] bf16 sequences (the full-attention baseline).
+hipError_t launch_dense_fwd(int bh, int n, float scale, const void* q, const void* k,
+                            const void* v, void* o, float* lse, hipStream_t stream);
+hipError_t launch_dense_bwd(int bh, int n, float scale, const void* q, const void* k,
+                            const void* v, const void* dout, const float* lse, void* dq,
+                            void* dk, void* dv, float* dd, hipStream_t stream);
+
 }  // namespace llsa

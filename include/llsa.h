@@ -173,6 +173,28 @@ int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const
                       size_t ws_bytes, void* stream);
 
 /*
+ * llsa_dense_attn_fwd / llsa_dense_attn_bwd — dense softmax attention over all N keys, the
+ * full-attention baseline the sparse method is measured against (paper summary sec. 5.4 and
+ * Figure 3 compare against dense FlashAttention at the same sequence length).  Not part of
+ * the sparse path.  Tokens are a plain sequence (the result does not depend on their order).
+ * q, k, v, o, dout, dq, dk, dv: bf16 [batch_heads, n, head_dim], contiguous, 16-byte aligned;
+ * lse: fp32 [batch_heads, n] (natural log), written by the forward, read by the backward;
+ * d_rows: fp32 [batch_heads, n] caller-owned scratch, receives D = rowsum(dout * o), computed
+ * as sum_j P_ij dP_ij from the recomputed scores (the backward does not read o).
+ * o = softmax(scale q k^T) v, flash-style (fp32 accumulation and softmax; in the forward P
+ * enters the bf16 MFMA rounded to bf16; in the backward P, P dP and dS enter as bf16 hi + lo
+ * pairs, the same arithmetic as llsa_attn_bwd).  Requires head_dim 64 and n a multiple of 128 in [128, 2^23];
+ * scale 0 => 1/sqrt(head_dim).  Deterministic (no atomics).  Errors as for the calls above.
+ */
+int32_t llsa_dense_attn_fwd(int32_t batch_heads, int32_t n, int32_t head_dim, float scale,
+                            const void* q, const void* k, const void* v, void* o, float* lse,
+                            void* stream);
+int32_t llsa_dense_attn_bwd(int32_t batch_heads, int32_t n, int32_t head_dim, float scale,
+                            const void* q, const void* k, const void* v, const void* dout,
+                            const float* lse, void* dq, void* dk, void* dv, float* d_rows,
+                            void* stream);
+
+/*
  * Per-kernel timing (profiling aid, not part of the method).  llsa_profile_enable(1) makes
  * every later kernel launch of the library record a pair of hipEvents on its stream;
  * llsa_profile_read() waits for the recorded events, writes one line per kernel name,

@@ -261,6 +261,42 @@ def attention_backward(q, k, v, k_lv, v_lv, sel, do, block: int, enrich: bool = 
 
 
 # --------------------------------------------------------------------------------------
+# Dense softmax attention: the full-attention baseline the pages compare against
+# ([SUM] sec. 5.4 / Figure 3: speed-up over dense FlashAttention at the same length)
+# --------------------------------------------------------------------------------------
+
+
+def dense_attention_forward(q, k, v, scale: float | None = None):
+    """Per-head dense attention over all keys: (o [N, d], lse [N]).
+
+    o = softmax(scale q k^T) v row by row; lse = log sum_j exp(scale q_i.k_j).
+    """
+    d = q.shape[1]
+    scale = 1.0 / math.sqrt(d) if not scale else scale
+    s = scale * (q @ k.T)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=1, keepdims=True)
+    return (e @ v) / z, (m + np.log(z))[:, 0]
+
+
+def dense_attention_backward(q, k, v, do, scale: float | None = None):
+    """Per-head gradients (dq, dk, dv) of dense attention given upstream dO.
+
+    P = softmax(scale q k^T), dP = dO v^T, dS = P (dP - rowsum(P dP)),
+    dq = scale dS k, dk = scale dS^T q, dv = P^T dO.
+    """
+    d = q.shape[1]
+    scale = 1.0 / math.sqrt(d) if not scale else scale
+    s = scale * (q @ k.T)
+    e = np.exp(s - s.max(axis=1, keepdims=True))
+    prob = e / e.sum(axis=1, keepdims=True)
+    dprob = do @ v.T
+    ds = prob * (dprob - (prob * dprob).sum(axis=1, keepdims=True))
+    return scale * (ds @ k), scale * (ds.T @ q), prob.T @ do
+
+
+# --------------------------------------------------------------------------------------
 # Sparse index transpose: CSR -> CSC  ([SUM] sec. 4.1; [ART] sec. 四)
 # --------------------------------------------------------------------------------------
 

@@ -122,3 +122,17 @@ def test_backward_rejects_too_many_coarse_keys(L):
     st = L.llsa_attn_bwd(ctypes.byref(p.c()), *([fake] * 5), null6, null6, null6, null6, null6,
                          *([fake] * 4), 1 << 30, None)
     assert st == 4 and b"coarse" in L.llsa_last_error()
+
+
+def test_dense_baseline_validation(L):
+    f = ctypes.c_void_p(FAKE)
+    # n must be a multiple of 128, head_dim 64, pointers present
+    assert L.llsa_dense_attn_fwd(2, 1000, 64, 0.0, f, f, f, f, f, None) == 2
+    assert L.llsa_dense_attn_fwd(2, 1024, 128, 0.0, f, f, f, f, f, None) == 4
+    assert L.llsa_dense_attn_fwd(0, 1024, 64, 0.0, f, f, f, f, f, None) == 2
+    assert L.llsa_dense_attn_fwd(2, 1024, 64, -1.0, f, f, f, f, f, None) == 2
+    assert L.llsa_dense_attn_fwd(2, 1024, 64, 0.0, None, f, f, f, f, None) == 1
+    assert L.llsa_dense_attn_fwd(2, 1024, 64, 0.0, f, f, f, f, ctypes.c_void_p(MISALIGNED),
+                                 None) == 6
+    assert L.llsa_dense_attn_bwd(2, 1024, 64, 0.0, *([f] * 8), None, None) == 1
+    assert L.llsa_dense_attn_bwd(2, 64, 64, 0.0, *([f] * 9), None) == 2

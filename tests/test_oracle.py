@@ -347,6 +347,35 @@ def test_backward_full_k_no_enrich_is_dense_gradient():
         assert np.allclose(a, b.grad.numpy(), rtol=0, atol=1e-10)
 
 
+def test_dense_baseline_matches_sdpa_and_autograd():
+    """The dense baseline's oracle equals torch float64 SDPA and its autograd gradients."""
+    n, d = 384, 64
+    q, k, v, do = (_rand((n, d), 90 + i) for i in range(4))
+    o, lse = orc.dense_attention_forward(q, k, v)
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    ref = _sdpa(qt[None], kt[None], vt[None])[0]
+    assert np.allclose(o, ref.detach().numpy(), rtol=0, atol=1e-12)
+    s = (q @ k.T) / math.sqrt(d)
+    assert np.allclose(lse, np.log(np.exp(s).sum(axis=1)), rtol=0, atol=1e-10)
+    ref.backward(torch.tensor(do))
+    for a, b in zip(orc.dense_attention_backward(q, k, v, do), (qt, kt, vt)):
+        assert np.allclose(a, b.grad.numpy(), rtol=0, atol=1e-10)
+
+
+def test_dense_baseline_is_the_full_k_sparse_case():
+    """With K covering every candidate and no enrichment the sparse oracle is the dense one."""
+    n, d, B = 256, 8, 16
+    q, k, v, do = (_rand((n, d), 95 + i) for i in range(4))
+    ql, kl, vl = (orc.pool_levels(x, B, 1) for x in (q, k, v))
+    sel = orc.select(ql, kl, B, [16])
+    o, lse = orc.attention_forward(q, k, v, kl, vl, sel, B, False)
+    od, lsed = orc.dense_attention_forward(q, k, v)
+    assert np.allclose(o, od, rtol=0, atol=1e-12) and np.allclose(lse, lsed, rtol=0, atol=1e-12)
+    for a, b in zip(orc.attention_backward(q, k, v, kl, vl, sel, do, B, False),
+                    orc.dense_attention_backward(q, k, v, do)):
+        assert np.allclose(a, b, rtol=0, atol=1e-10)
+
+
 # ----------------------------------------------------------------------------- CSC
 
 
