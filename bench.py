@@ -8,7 +8,15 @@ into a HIP graph and replayed; `value` is batch*N tokens per second of graph rep
 second, eager pass with per-kernel HIP events gives each kernel's launch duration; the
 roofline object is for the kernel with the largest total time.  Prints one JSON line.
 
+Beside the headline, `extra` carries:
+  * configs: every workload (forward only for the three forward configs, forward + backward
+    for the two training ones), each timed the same way, with the HBM and MFMA fractions of
+    its attention kernels;
+  * dense_baseline: the library's own dense flash attention at the same shapes (forward at
+    256x256 batch 1, forward + backward at the headline shape) and the speed-up ratios.
+
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config px256_train] [--no-cpu]
+                  [--no-configs] [--no-dense]
 """
 from __future__ import annotations
 
@@ -25,6 +33,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
+FP32_MFMA_PEAK_TFLOPS = 157.3    # fp32 (the fp32 workload runs on the fp32 MFMA)
 KERNEL_SOURCES = {               # kernel -> source file (the traffic record is tied to it)
     "attn_fwd_kernel": "attn_fwd.hip",
     "bwd_query_kernel": "attn_bwd.hip",
@@ -44,6 +53,8 @@ def parse():
                     help="token order of the resident tensors: raster (the reorder is folded into "
                          "every kernel's addressing) or morton (inputs reordered once before "
                          "timing, as when the reorder is hoisted to the network entry)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
     ap.add_argument("--with-copy", action="store_true",
                     help="also launch one Morton reorder (a plain copy of one token tensor) per "
                          "step, outside the timed region: the calibration kernel for HBM "
@@ -51,13 +62,15 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_model(p, elem_bytes=2):
+def kernel_model(p, elem_bytes=None):
     """Algorithmic (compulsory) HBM bytes and FLOPs per launch of the attention kernels.
 
     T = one [b, H, N, 64] token tensor.  Gathers of selected key blocks count once (the
     compulsory traffic); index arrays and pooled levels are counted in full.
     """
     bh, n, d, K, L = p.batch * p.heads, p.n, p.head_dim, p.topk, p.levels
+    if elem_bytes is None:
+        elem_bytes = 2 if p.torch_dtype == torch_bf16() else 4
     T = bh * n * d * elem_bytes
     kq_fine = K * 16
     n_coarse = (L - 1) * K if p.enrich else 0
@@ -76,6 +89,11 @@ def kernel_model(p, elem_bytes=2):
         "bwd_key_kernel": dict(bytes=6 * T + 2 * tok4 + csc1,
                                flops=8 * bh * n * kq_fine * d),
     }
+
+
+def torch_bf16():
+    import torch
+    return torch.bfloat16
 
 
 def traffic_record(kernel, config):
@@ -122,42 +140,35 @@ def cpu_baseline(cfg, x, seconds_budget=12.0):
                        f"in {spent:.1f} s on one thread; tokens counted pro rata")
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
-                                   "part of it (the op shards over (batch, head) with no "
-                                   "exchange, see the design notes)", "n_gpus": args.gpus}))
-        sys.exit(2)
+def _event_ms(fn, reps):
+    import torch
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(reps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / reps
+
+
+def measure(step, steps, warmup, graph=True, with_copy=None):
+    """Eager pass with per-kernel events, then the timed region (graph replays or eager
+    steps).  Returns (ms_step, eager_ms, per_call, per_kernel_ms, per_step_kernel_ms)."""
     import torch
 
-    from hierarchical_top_sparse_amd import _abi, gen, ops
-    from hierarchical_top_sparse_amd.runtime import Step
-
-    cfg = gen.CONFIGS[args.config]
-    h, w, L = cfg["height"], cfg["width"], cfg["levels"]
-    x = gen.make_inputs(cfg["batch"], cfg["heads"], h, w, 64, cfg["dtype"], cfg["seed_base"],
-                        with_grad=True)
-    dev = torch.device("cuda:0")
-    q, k, v, do = (x[t].to(dev) for t in ("q", "k", "v", "do"))
-    p = ops.make_problem(q, h, w, L)
-    if args.layout == "morton":
-        q, k, v, do = (ops.reorder(p, t) for t in (q, k, v, do))
-        p = ops.make_problem(q, h, w, L, layout=ops.LLSA_LAYOUT_MORTON)
-    step = Step(p, q, k, v, do)
+    from hierarchical_top_sparse_amd import _abi
     calls = step.calls()
     stream = torch.cuda.current_stream()
-
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
-    if args.with_copy:
-        copy_dst = torch.empty_like(q)
-        for _ in range(max(1, args.steps)):
-            _abi.llsa_reorder(p, q, copy_dst, False)
+    if with_copy is not None:
+        for _ in range(max(1, steps)):
+            with_copy()
         torch.cuda.synchronize()
-
-    # ---- eager pass with per-kernel events (launch durations for the roofline)
     _abi.llsa_profile_read()
     _abi.llsa_profile_enable(True)
     ev = {name: [] for name, _ in calls}
@@ -165,7 +176,7 @@ def main():
     e_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e_start.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         for name, fn in calls:
             a0 = torch.cuda.Event(enable_timing=True)
             a1 = torch.cuda.Event(enable_timing=True)
@@ -177,36 +188,130 @@ def main():
     torch.cuda.synchronize()
     _abi.llsa_profile_enable(False)
     kprof = _abi.llsa_profile_read()
-    eager_ms = e_start.elapsed_time(e_end) / args.steps
+    eager_ms = e_start.elapsed_time(e_end) / steps
     per_call = {name: sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
                 for name, pairs in ev.items()}
     per_kernel_ms = {name: tot / cnt for name, (cnt, tot) in kprof.items()}
-    per_step_kernel_ms = {name: tot / args.steps for name, (cnt, tot) in kprof.items()}
-
-    # ---- timed region: graph replays of the whole step
-    if args.no_graph:
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0.record(stream)
-        for _ in range(args.steps):
-            step.run()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        ms_step = t0.elapsed_time(t1) / args.steps
-    else:
+    per_step_kernel_ms = {name: tot / steps for name, (cnt, tot) in kprof.items()}
+    if graph:
         step.capture()
-        for _ in range(args.warmup):
+        for _ in range(warmup):
             step.replay()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for _ in range(args.steps):
-            step.replay()
-        t1.record(stream)
-        torch.cuda.synchronize()
-        ms_step = t0.elapsed_time(t1) / args.steps
+        ms_step = _event_ms(step.replay, steps)
+    else:
+        ms_step = _event_ms(step.run, steps)
+    return ms_step, eager_ms, per_call, per_kernel_ms, per_step_kernel_ms
+
+
+def kernel_fractions(p, per_kernel_ms):
+    model = kernel_model(p)
+    bf16 = p.torch_dtype == torch_bf16()
+    peak_tf = BF16_MFMA_PEAK_TFLOPS if bf16 else FP32_MFMA_PEAK_TFLOPS
+    out = {}
+    for kname in model:
+        if kname in per_kernel_ms:
+            t = per_kernel_ms[kname] / 1e3
+            out[kname] = {"ms": round(per_kernel_ms[kname], 4),
+                          "hbm_frac": round(model[kname]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
+                          "mfma_frac": round(model[kname]["flops"] / t / 1e12 / peak_tf, 4)}
+    return out
+
+
+def make_step(cfg_name, layout="raster", backward=None):
+    import torch
+
+    from hierarchical_top_sparse_amd import gen, ops
+    from hierarchical_top_sparse_amd.runtime import Step
+    cfg = gen.CONFIGS[cfg_name]
+    h, w, L = cfg["height"], cfg["width"], cfg["levels"]
+    bwd = cfg["backward"] if backward is None else backward
+    x = gen.make_inputs(cfg["batch"], cfg["heads"], h, w, 64, cfg["dtype"], cfg["seed_base"],
+                        with_grad=bwd)
+    dev = torch.device("cuda:0")
+    q, k, v = (x[t].to(dev) for t in ("q", "k", "v"))
+    do = x["do"].to(dev) if bwd else None
+    p = ops.make_problem(q, h, w, L)
+    if layout == "morton":
+        q, k, v = (ops.reorder(p, t) for t in (q, k, v))
+        do = ops.reorder(p, do) if do is not None else None
+        p = ops.make_problem(q, h, w, L, layout=ops.LLSA_LAYOUT_MORTON)
+    return Step(p, q, k, v, do), x, cfg
+
+
+def config_table(steps, warmup):
+    """tokens/s and attention-kernel roofline fractions of every workload."""
+    from hierarchical_top_sparse_amd import gen
+    rows = {}
+    for name, cfg in gen.CONFIGS.items():
+        step, _, _ = make_step(name)
+        ms, _, _, per_kernel_ms, _ = measure(step, steps, warmup)
+        tokens = cfg["batch"] * cfg["height"] * cfg["width"]
+        rows[name] = {"pass": "fwd+bwd" if cfg["backward"] else "fwd",
+                      "dtype": "bf16" if cfg["dtype"] == torch_bf16() else "f32",
+                      "tokens": tokens, "ms": round(ms, 4),
+                      "tokens_per_s": round(tokens / (ms / 1e3), 1),
+                      "kernels": kernel_fractions(step.p, per_kernel_ms)}
+        del step
+    return rows
+
+
+def dense_baseline(llsa_fwd_ms_256, llsa_train_ms_256):
+    """The library's dense flash attention at 256x256: forward at batch 1 x 6 heads, forward +
+    backward at batch 2 x 6 heads; ratios against the sparse path at the same shapes."""
+    import torch
+
+    from hierarchical_top_sparse_amd import _abi
+    out = {}
+    n = 256 * 256
+    for name, bh, bwd in (("px256_fwd", 6, False), ("px256_train", 12, True)):
+        g = torch.Generator(device="cuda").manual_seed(5)
+        q, k, v, do = (torch.randn(bh, n, 64, device="cuda", generator=g).to(torch.bfloat16)
+                       for _ in range(4))
+        o = torch.empty_like(q)
+        lse = torch.empty(bh, n, device="cuda")
+        dd = torch.empty_like(lse)
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+        def fwd():
+            _abi.llsa_dense_attn_fwd(q, k, v, o, lse)
+
+        def step():
+            fwd()
+            _abi.llsa_dense_attn_bwd(q, k, v, do, lse, dq, dk, dv, dd)
+        fn = step if bwd else fwd
+        fn()
+        ms = _event_ms(fn, 2)
+        flops = 4 * bh * n * n * 64 * (3.5 if bwd else 1.0)
+        sparse_ms = llsa_train_ms_256 if bwd else llsa_fwd_ms_256
+        out[name] = {"pass": "fwd+bwd" if bwd else "fwd", "batch_heads": bh, "ms": round(ms, 3),
+                     "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+                     "mfma_frac": round(flops / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "llsa_ms": round(sparse_ms, 4),
+                     "speedup_llsa_vs_dense": round(ms / sparse_ms, 2)}
+        del q, k, v, do, o, lse, dd, dq, dk, dv
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+                                   "part of it (the op shards over (batch, head) with no "
+                                   "exchange, see the design notes)", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    from hierarchical_top_sparse_amd import _abi
+
+    step, x, cfg = make_step(args.config, args.layout)
+    p = step.p
+    h, w, L = cfg["height"], cfg["width"], cfg["levels"]
+    copy = None
+    if args.with_copy:
+        copy_dst = torch.empty_like(step.q)
+        copy = lambda: _abi.llsa_reorder(p, step.q, copy_dst, False)   # noqa: E731
+    ms_step, eager_ms, per_call, per_kernel_ms, per_step_kernel_ms = measure(
+        step, args.steps, args.warmup, graph=not args.no_graph, with_copy=copy)
     tokens = cfg["batch"] * h * w
     value = tokens / (ms_step / 1e3)
 
@@ -224,20 +329,23 @@ def main():
                 "launch_ms": round(launch_ms, 4),
                 "mfma_frac": round(model[dominant]["flops"] / (launch_ms / 1e3) / 1e12 /
                                    BF16_MFMA_PEAK_TFLOPS, 4)}
-    kernels = {}
-    for kname in model:
-        if kname in per_kernel_ms:
-            t = per_kernel_ms[kname] / 1e3
-            kernels[kname] = {"ms": round(per_kernel_ms[kname], 4),
-                              "hbm_frac": round(model[kname]["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4),
-                              "mfma_frac": round(model[kname]["flops"] / t / 1e12 /
-                                                 BF16_MFMA_PEAK_TFLOPS, 4)}
     extra = {"graph": not args.no_graph, "eager_ms_per_step": round(eager_ms, 4),
              "per_call_ms": {k2: round(v2, 4) for k2, v2 in per_call.items()},
              "per_kernel_ms_per_step": {k2: round(v2, 4) for k2, v2 in
                                         sorted(per_step_kernel_ms.items(),
                                                key=lambda kv: -kv[1])},
-             "attention_kernels": kernels}
+             "attention_kernels": kernel_fractions(p, per_kernel_ms)}
+    del step
+    if not args.no_configs:
+        extra["configs"] = config_table(max(5, args.steps // 2), 2)
+    if not args.no_dense:
+        if "configs" in extra:
+            fwd256 = extra["configs"]["px256"]["ms"]
+        else:
+            s256, _, _ = make_step("px256")
+            fwd256 = measure(s256, 10, 2)[0]
+            del s256
+        extra["dense_baseline"] = dense_baseline(fwd256, ms_step)
     cpu = None if args.no_cpu else cpu_baseline(cfg, x)
     line = {
         "metric": "LLSA fwd+bwd tokens/s at 256x256 pixels (65,536 tok); % MFMA/HBM peak",

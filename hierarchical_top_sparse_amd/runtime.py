@@ -20,9 +20,12 @@ from . import _abi
 
 
 class Step:
-    def __init__(self, p: _abi.Problem, q, k, v, dout):
+    """dout=None makes a forward-only step (pooling, selection, sparse attention)."""
+
+    def __init__(self, p: _abi.Problem, q, k, v, dout=None):
         self.p = p
         self.q, self.k, self.v, self.dout = q, k, v, dout
+        self.backward = dout is not None
         dev, f32 = q.device, torch.float32
         L = p.levels
         lv = lambda l: torch.empty((p.batch, p.heads, p.n_level(l), p.head_dim), device=dev,
@@ -35,19 +38,20 @@ class Step:
                                 dtype=torch.int32) for l in range(1, L + 1)]
         self.o = torch.empty_like(q)
         self.lse = torch.empty((p.batch, p.heads, p.n), device=dev, dtype=f32)
-        self.csc_levels = L if p.enrich else 1
+        self.csc_levels = (L if p.enrich else 1) if self.backward else 0
         self.off = [torch.empty((p.batch, p.heads, p.n_level(l) + 1), device=dev,
                                 dtype=torch.int32) for l in range(1, self.csc_levels + 1)]
         self.rows = [torch.empty((p.batch, p.heads, p.n_level(l) * p.topk), device=dev,
                                  dtype=torch.int32) for l in range(1, self.csc_levels + 1)]
         self.nmat = p.batch * p.heads
-        tws = max(_abi.llsa_index_transpose_workspace(self.nmat, p.n_level(l), p.n_level(l),
-                                                      p.topk)
-                  for l in range(1, self.csc_levels + 1))
+        tws = max([_abi.llsa_index_transpose_workspace(self.nmat, p.n_level(l), p.n_level(l),
+                                                       p.topk)
+                   for l in range(1, self.csc_levels + 1)] + [16])
         self.tws = torch.empty(tws, device=dev, dtype=torch.uint8)
-        _, bws = _abi.llsa_workspace_bytes(p)
+        _, bws = _abi.llsa_workspace_bytes(p) if self.backward else (0, 0)
         self.bws = torch.empty(max(bws, 16), device=dev, dtype=torch.uint8)
-        self.dq, self.dk, self.dv = (torch.empty_like(q) for _ in range(3))
+        self.dq, self.dk, self.dv = ((torch.empty_like(q) for _ in range(3)) if self.backward
+                                     else (None, None, None))
         self.graph = None
         self.side = torch.cuda.Stream(device=dev)
 
@@ -71,7 +75,7 @@ class Step:
                                                      self.v_lv, self.sel, self.o, self.lse))]
         bwd = [("attn_bwd", lambda: a.llsa_attn_bwd(
             p, self.q, self.k, self.v, self.dout, self.lse, self.k_lv, self.v_lv, self.sel,
-            self.off, self.rows, self.dq, self.dk, self.dv, self.bws))]
+            self.off, self.rows, self.dq, self.dk, self.dv, self.bws))] if self.backward else []
         self._parts = (head, fwd, self._transpose_calls(), bwd)
         return head + fwd + self._parts[2] + bwd
 
@@ -82,7 +86,7 @@ class Step:
         head, fwd, tr, bwd = self._parts
         for _, fn in head:
             fn()
-        if not overlap:
+        if not overlap or not tr:
             for _, fn in fwd + tr + bwd:
                 fn()
             return
