@@ -272,8 +272,16 @@ void bwd_query_kernel(BwdArgs a) {
   const int n_u = uniform(__builtin_popcountll(fm));
   {
     const int u = __builtin_popcountll(fm & (~0ull >> (63 - lane))) - 1;
-    if (first) uoff[u] = block_corner(sk >> 8, a.grid) * kDim * 2;
-    if (valid) atomicOr(&umask[u], 1 << ((sk & 63) >> 4));
+    if (first) {   // the run of this key block: one entry per block that picked it
+      int m = 0;
+      for (int r = lane; r < min(lane + kQBlocks, kQPickList); ++r) {
+        const int o = sorted[r];
+        if ((o >> 8) != (sk >> 8)) break;
+        m |= 1 << ((o & 63) >> 4);
+      }
+      uoff[u] = block_corner(sk >> 8, a.grid) * kDim * 2;
+      umask[u] = m;
+    }
   }
   wave_lds_sync();
 
