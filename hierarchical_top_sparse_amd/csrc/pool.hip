@@ -1,11 +1,13 @@
 // Hierarchical compression: recursive mean pooling of Q, K and V (paper summary sec. 三:
 // level l has N / B^l tokens, each the mean of B level-(l-1) tokens).
 //
-// pool12_kernel: one workgroup per (tensor, head, group of B level-1 blocks = B^2 tokens).
-//   Reads the B^2 token rows once (coalesced 128/256-byte rows; raster layout reads 4x4 tiles
-//   as 4 row segments), writes level 1 and reduces level 2 through LDS.  HBM-bound.
+// pool12_{bf16,f32}_kernel: one workgroup per (tensor, head, group of B level-1 blocks = B^2
+//   tokens).  Reads the B^2 token rows once, every thread's loads in flight together
+//   (coalesced 128/256-byte rows; raster layout reads 4x4 tiles as 4 row segments), writes
+//   level 1 and reduces level 2 through LDS.  HBM-bound.
 // pool_next_kernel: level l >= 3 from level l-1 (fp32, tiny).
-// All sums are fp32 in a fixed order; the 1/B factor is exact.
+// All sums are fp32 in a fixed order; the 1/B factor is exact.  pool12_kernel is the profiling
+// name of both level-1/2 kernels.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -17,9 +19,63 @@ struct PoolArgs {
   float* lv2[3];
 };
 
-template <bool BF16>
-__global__ __launch_bounds__(256) void pool12_kernel(PoolArgs args, int n, Grid grid,
-                                                      int groups_per_head) {
+// bf16 tokens: thread t owns level-1 block t / 16 of the group, half (t / 8) % 2 of its 16
+// tokens and the 16-byte channel piece t % 8; its 8 row loads are issued at once (each wave
+// instruction reads 8 whole 128-byte rows), the two halves meet by a cross-lane add.
+__global__ __launch_bounds__(256) void pool12_bf16_kernel(PoolArgs args, int n, Grid grid,
+                                                          int groups_per_head) {
+  __shared__ __attribute__((aligned(16))) float sh[kBlock][kDim];
+  const int tensor = blockIdx.y;
+  const int head = blockIdx.x / groups_per_head;
+  const int group = blockIdx.x - head * groups_per_head;
+  const int t = threadIdx.x;
+  const int blk = t >> 4;          // level-1 block within the group
+  const int half = (t >> 3) & 1;   // tokens 8 half .. 8 half + 7 of the block
+  const int cp = t & 7;            // channels 8 cp .. 8 cp + 7
+  const int first_tok = (group * kBlock + blk) * kBlock + 8 * half;
+  const bf16* x = (const bf16*)args.x[tensor] + (long)head * n * kDim + 8 * cp;
+  bf16x8 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = *(const bf16x8*)(x + (long)token_row(first_tok + i, grid) * kDim);
+  float acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += (float)v[i][c];
+    acc[c] = s + __shfl_xor(s, 8, 64);   // + the other half of the block
+  }
+  f32x4 l1a, l1b;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    l1a[c] = acc[c] * (1.0f / kBlock);
+    l1b[c] = acc[4 + c] * (1.0f / kBlock);
+  }
+  const int n1 = n >> kBlockShift;
+  if (half == 0) {
+    if (args.lv1[tensor]) {
+      float* out = args.lv1[tensor] + ((long)head * n1 + group * kBlock + blk) * kDim + 8 * cp;
+      *(f32x4*)out = l1a;
+      *(f32x4*)(out + 4) = l1b;
+    }
+    *(f32x4*)&sh[blk][8 * cp] = l1a;
+    *(f32x4*)&sh[blk][8 * cp + 4] = l1b;
+  }
+  if (args.lv2[tensor]) {
+    __syncthreads();
+    if (t < kDim) {
+      float s = 0.f;
+#pragma unroll
+      for (int b = 0; b < kBlock; ++b) s += sh[b][t];
+      const int n2 = n1 >> kBlockShift;
+      args.lv2[tensor][((long)head * n2 + group) * kDim + t] = s * (1.0f / kBlock);
+    }
+  }
+}
+
+// fp32 tokens: thread t owns block t / 16 and channels 4 (t % 16) .. +3.
+__global__ __launch_bounds__(256) void pool12_f32_kernel(PoolArgs args, int n, Grid grid,
+                                                         int groups_per_head) {
   __shared__ float sh[kBlock][kDim];
   const int tensor = blockIdx.y;
   const int head = blockIdx.x / groups_per_head;
@@ -29,25 +85,14 @@ __global__ __launch_bounds__(256) void pool12_kernel(PoolArgs args, int n, Grid 
   const int dq = (t & 15) * 4;   // first of 4 channels
   const int first_tok = (group * kBlock + blk) * kBlock;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  if (BF16) {
-    const bf16* x = (const bf16*)args.x[tensor] + (long)head * n * kDim;
-#pragma unroll 4
-    for (int i = 0; i < kBlock; ++i) {
-      const int row = token_row(first_tok + i, grid);
-      const bf16x4 v = *(const bf16x4*)(x + (long)row * kDim + dq);
+  const float* x = (const float*)args.x[tensor] + (long)head * n * kDim;
+  f32x4 v[kBlock];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] += (float)v[c];
-    }
-  } else {
-    const float* x = (const float*)args.x[tensor] + (long)head * n * kDim;
-#pragma unroll 4
-    for (int i = 0; i < kBlock; ++i) {
-      const int row = token_row(first_tok + i, grid);
-      const f32x4 v = *(const f32x4*)(x + (long)row * kDim + dq);
+  for (int i = 0; i < kBlock; ++i) v[i] = *(const f32x4*)(x + (long)token_row(first_tok + i, grid) * kDim + dq);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] += v[c];
-    }
-  }
+  for (int i = 0; i < kBlock; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] += v[i][c];
   f32x4 l1;
 #pragma unroll
   for (int c = 0; c < 4; ++c) l1[c] = acc[c] * (1.0f / kBlock);
@@ -105,11 +150,11 @@ hipError_t launch_pool(const Shape& s, const void* const x[3], float* const* lv[
   const Grid grid{s.hbits, s.wbits, s.raster};
   const dim3 blocks((unsigned)(s.bh * groups_per_head), (unsigned)nt);
   if (s.bf16)
-    LLSA_LAUNCH("pool12_kernel", pool12_kernel<true>, blocks, dim3(256), 0, stream, a, s.n, grid,
-                       groups_per_head);
+    LLSA_LAUNCH("pool12_kernel", pool12_bf16_kernel, blocks, dim3(256), 0, stream, a, s.n, grid,
+                groups_per_head);
   else
-    LLSA_LAUNCH("pool12_kernel", pool12_kernel<false>, blocks, dim3(256), 0, stream, a, s.n, grid,
-                       groups_per_head);
+    LLSA_LAUNCH("pool12_kernel", pool12_f32_kernel, blocks, dim3(256), 0, stream, a, s.n, grid,
+                groups_per_head);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   for (int l = 3; l <= s.levels; ++l) {
