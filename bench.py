@@ -55,6 +55,9 @@ def parse():
                          "timing, as when the reorder is hoisted to the network entry)")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense baseline")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: LLSA vs the dense baseline across "
+                         "resolutions 64^2 .. 512^2 (batch 1, 6 heads), one JSON line each")
     ap.add_argument("--with-copy", action="store_true",
                     help="also launch one Morton reorder (a plain copy of one token tensor) per "
                          "step, outside the timed region: the calibration kernel for HBM "
@@ -292,8 +295,56 @@ def dense_baseline(llsa_fwd_ms_256, llsa_train_ms_256):
     return out
 
 
+def sweep(steps):
+    """Resolution sweep (the shape of the pages' Figure 3 / Figure 4): per side length, LLSA
+    forward and forward + backward against the dense baseline, and the key-major backward
+    kernel's throughput (query-key block pairs per second) as N grows."""
+    import torch
+
+    from hierarchical_top_sparse_amd import _abi, gen, ops
+    from hierarchical_top_sparse_amd.runtime import Step
+    for side, levels in ((64, 2), (128, 2), (256, 3), (512, 3)):
+        n = side * side
+        x = gen.make_inputs(1, 6, side, side, 64, torch.bfloat16, 7000 + side, with_grad=True)
+        q, k, v, do = (x[t].cuda() for t in ("q", "k", "v", "do"))
+        p = ops.make_problem(q, side, side, levels)
+        fwd_ms = measure(Step(p, q, k, v), steps, 2)[0]
+        st = Step(p, q, k, v, do)
+        train_ms, _, _, per_kernel_ms, _ = measure(st, steps, 2)
+        pairs = int(st.sel[0].numel())   # (query block, picked key block) pairs
+        qd, kd, vd, dod = (t.reshape(6, n, 64) for t in (q, k, v, do))
+        o = torch.empty_like(qd)
+        lse = torch.empty(6, n, device="cuda")
+        dd = torch.empty_like(lse)
+        dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+        dfwd = lambda: _abi.llsa_dense_attn_fwd(qd, kd, vd, o, lse)   # noqa: E731
+
+        def dstep():
+            dfwd()
+            _abi.llsa_dense_attn_bwd(qd, kd, vd, dod, lse, dq, dk, dv, dd)
+        dfwd()
+        dense_fwd_ms = _event_ms(dfwd, 2)
+        dstep()
+        dense_train_ms = _event_ms(dstep, 2)
+        key_ms = per_kernel_ms.get("bwd_key_kernel")
+        print(json.dumps({
+            "side": side, "tokens": n, "batch": 1, "heads": 6, "levels": levels,
+            "llsa_fwd_ms": round(fwd_ms, 4), "llsa_train_ms": round(train_ms, 4),
+            "dense_fwd_ms": round(dense_fwd_ms, 3), "dense_train_ms": round(dense_train_ms, 3),
+            "speedup_fwd": round(dense_fwd_ms / fwd_ms, 2),
+            "speedup_train": round(dense_train_ms / train_ms, 2),
+            "llsa_train_tokens_per_s": round(6 * n / (train_ms / 1e3), 1),
+            "key_pass_ms": round(key_ms, 4) if key_ms else None,
+            "key_pass_block_pairs_per_s": round(pairs / (key_ms / 1e3), 1) if key_ms else None,
+        }), flush=True)
+        del st, q, k, v, do, qd, kd, vd, dod, o, lse, dd, dq, dk, dv
+
+
 def main():
     args = parse()
+    if args.sweep:
+        sweep(max(3, args.steps // 2))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
                                    "part of it (the op shards over (batch, head) with no "
