@@ -620,6 +620,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 stQ[32 * kStride];
   __shared__ __attribute__((aligned(16))) bf16 stO[32 * kStride];   // dO rows
+  __shared__ __attribute__((aligned(16))) float pdown[2 * kDim];    // pushed-down dK, dV
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int g = lane >> 4;
@@ -628,6 +629,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
   const int head = uniform(kb / n1);
   const int j = uniform(kb - head * n1);
   const long tok_base = (long)head * a.n;
+
+  // pooled-key gradients pushed down to this block (lane = channel), loaded first so that
+  // they arrive during the CSC lookups instead of after the pair loop
+  float pk_sum = 0.f, pv_sum = 0.f;
+  if (a.enrich) {
+    for (int l = 2; l <= a.levels; ++l) {
+      const int nl = a.n >> (kBlockShift * l);
+      const int anc = j >> (kBlockShift * (l - 1));
+      const float f = 1.0f / (float)(1 << (kBlockShift * l));
+      pk_sum += a.dk_lv[l - 1][((long)head * nl + anc) * kDim + lane] * f;
+      pv_sum += a.dv_lv[l - 1][((long)head * nl + anc) * kDim + lane] * f;
+    }
+  }
 
   const uint32_t head_bytes = (uint32_t)a.n * kDim * 2;
   const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
@@ -769,39 +783,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
   }
 
   // ---- push-down of pooled-key gradients and store (lane holds key n, channels 16t4+4g+i)
-  float pdk[4][4], pdv[4][4];
-#pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pdk[t4][i] = pdv[t4][i] = 0.f;
-  if (a.enrich) {
-    for (int l = 2; l <= a.levels; ++l) {
-      const int nl = a.n >> (kBlockShift * l);
-      const int anc = j >> (kBlockShift * (l - 1));
-      const float f = 1.0f / (float)(1 << (kBlockShift * l));
-      const float* gk = a.dk_lv[l - 1] + ((long)head * nl + anc) * kDim;
-      const float* gv = a.dv_lv[l - 1] + ((long)head * nl + anc) * kDim;
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const f32x4 k4 = *(const f32x4*)(gk + 16 * t4 + 4 * g);
-        const f32x4 v4 = *(const f32x4*)(gv + 16 * t4 + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pdk[t4][i] += k4[i] * f;
-          pdv[t4][i] += v4[i] * f;
-        }
-      }
-    }
-  }
+  pdown[lane] = pk_sum;
+  pdown[kDim + lane] = pv_sum;
+  wave_lds_sync();
   bf16* dkp = a.dk + (tok_base + krow) * kDim;
   bf16* dvp = a.dv + (tok_base + krow) * kDim;
 #pragma unroll
   for (int t4 = 0; t4 < 4; ++t4) {
+    const f32x4 pk = *(const f32x4*)(pdown + 16 * t4 + 4 * g);
+    const f32x4 pv = *(const f32x4*)(pdown + kDim + 16 * t4 + 4 * g);
     bf16x4 rk4, rv4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      rk4[i] = (bf16)(dka[t4][i] * a.scale + pdk[t4][i]);
-      rv4[i] = (bf16)(dva[t4][i] + pdv[t4][i]);
+      rk4[i] = (bf16)(dka[t4][i] * a.scale + pk[i]);
+      rv4[i] = (bf16)(dva[t4][i] + pv[i]);
     }
     *(bf16x4*)(dkp + 16 * t4 + 4 * g) = rk4;
     *(bf16x4*)(dvp + 16 * t4 + 4 * g) = rv4;
