@@ -621,6 +621,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
   __shared__ __attribute__((aligned(16))) bf16 stQ[32 * kStride];
   __shared__ __attribute__((aligned(16))) bf16 stO[32 * kStride];   // dO rows
   __shared__ __attribute__((aligned(16))) float pdown[2 * kDim];    // pushed-down dK, dV
+  __shared__ __attribute__((aligned(16))) float stL[64];            // lse (0..31), D (32..63)
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int g = lane >> 4;
@@ -677,7 +678,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 
   struct PairLd {
     i32x4 q[4], d[4];   // staged Q and dO rows
-    f32x4 l4[2], d4[2];  // lse and D of this lane's queries (tile t: tokens 8g+4t .. +3)
+    float ld;           // lane < 32: lse of pair query lane; else D of pair query lane - 32
     int okA, okB;
   };
   // The query blocks of CSC_1[j] in batches of 64: lane i holds entry base + i as the byte
@@ -705,13 +706,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
       f.q[ins] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
       f.d[ins] = __builtin_amdgcn_raw_buffer_load_b128(rdo, o, 0, 0);
     }
-    const uint32_t tl = lane_second ? tB : tA;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint32_t o = tl + (uint32_t)(((8 * g + 4 * t) & 15) * 4);
-      f.l4[t] = buf_load4f(rl, o);
-      f.d4[t] = buf_load4f(rd, o);
-    }
+    const uint32_t tl = ((lane >> 4) & 1) ? tB : tA;
+    f.ld = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         lane < 32 ? rl : rd, tl + (uint32_t)(n * 4), 0, 0));
     return f;
   };
 
@@ -725,6 +722,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
       *(i32x4*)(stQ + (ins * 8 + srow0) * kStride + 8 * piece) = f.q[ins];
       *(i32x4*)(stO + (ins * 8 + srow0) * kStride + 8 * piece) = f.d[ins];
     }
+    stL[lane] = f.ld;
     wave_lds_sync();
     // S and dP tiles (queries x keys): lane (n, g) holds queries 8g + i + 4t, key n
     const float madd = (lane_second ? f.okB : f.okA) ? 0.f : -INFINITY;
@@ -732,6 +730,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int arow = chunk_key(n, t);
+      const f32x4 l4 = *(const f32x4*)(stL + 8 * g + 4 * t);
+      const f32x4 d4 = *(const f32x4*)(stL + 32 + 8 * g + 4 * t);
       f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
       st = mfma_bf16_k32(lds_row8(stQ, arow, 0, g), kh[0], st);
       st = mfma_bf16_k32(lds_row8(stQ, arow, 1, g), kh[1], st);
@@ -739,9 +739,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
       dp = mfma_bf16_k32(lds_row8(stO, arow, 1, g), vh[1], dp);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pv = fast_exp2(fmaf(st[i], a.c2, madd - f.l4[t][i] * kLog2e));
+        const float pv = fast_exp2(fmaf(st[i], a.c2, madd - l4[i] * kLog2e));
         p[t][i] = pv;
-        dsv[t][i] = pv * (dp[i] - f.d4[t][i]);
+        dsv[t][i] = pv * (dp[i] - d4[i]);
       }
     }
     bf16x8 p_hi, p_lo, ds_hi, ds_lo;
