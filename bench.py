@@ -220,24 +220,26 @@ def kernel_fractions(p, per_kernel_ms):
     return out
 
 
-def make_step(cfg_name, layout="raster", backward=None):
+def make_step(cfg_name, layout="raster", backward=None, levels=None, topk=8):
+    """A runtime Step over the workload's inputs; levels/topk override its L and K."""
     import torch
 
     from hierarchical_top_sparse_amd import gen, ops
     from hierarchical_top_sparse_amd.runtime import Step
     cfg = gen.CONFIGS[cfg_name]
-    h, w, L = cfg["height"], cfg["width"], cfg["levels"]
+    h, w = cfg["height"], cfg["width"]
+    L = levels or cfg["levels"]
     bwd = cfg["backward"] if backward is None else backward
     x = gen.make_inputs(cfg["batch"], cfg["heads"], h, w, 64, cfg["dtype"], cfg["seed_base"],
                         with_grad=bwd)
     dev = torch.device("cuda:0")
     q, k, v = (x[t].to(dev) for t in ("q", "k", "v"))
     do = x["do"].to(dev) if bwd else None
-    p = ops.make_problem(q, h, w, L)
+    p = ops.make_problem(q, h, w, L, topk)
     if layout == "morton":
         q, k, v = (ops.reorder(p, t) for t in (q, k, v))
         do = ops.reorder(p, do) if do is not None else None
-        p = ops.make_problem(q, h, w, L, layout=ops.LLSA_LAYOUT_MORTON)
+        p = ops.make_problem(q, h, w, L, topk, layout=ops.LLSA_LAYOUT_MORTON)
     return Step(p, q, k, v, do), x, cfg
 
 
@@ -295,6 +297,22 @@ def dense_baseline(llsa_fwd_ms_256, llsa_train_ms_256):
     return out
 
 
+def single_level(cfg_name, llsa_ms, steps):
+    """The single-level comparator on the same inputs: one level, top-32 key blocks per query
+    block chosen over all N/16 blocks (the quadratic selection of single-level block-sparse
+    attention), then the same sparse forward and backward."""
+    step, _, cfg = make_step(cfg_name, levels=1, topk=32)
+    ms, _, _, per_kernel_ms, per_step_kernel_ms = measure(step, steps, 2)
+    tokens = cfg["batch"] * cfg["height"] * cfg["width"]
+    out = {"levels": 1, "topk": 32, "ms": round(ms, 4),
+           "tokens_per_s": round(tokens / (ms / 1e3), 1),
+           "per_kernel_ms_per_step": {k2: round(v2, 4) for k2, v2 in
+                                      sorted(per_step_kernel_ms.items(), key=lambda kv: -kv[1])},
+           "llsa_ms": round(llsa_ms, 4), "speedup_llsa_vs_single_level": round(ms / llsa_ms, 2)}
+    del step
+    return out
+
+
 def sweep(steps):
     """Resolution sweep (the shape of the pages' Figure 3 / Figure 4): per side length, LLSA
     forward and forward + backward against the dense baseline, and the key-major backward
@@ -327,12 +345,20 @@ def sweep(steps):
         dstep()
         dense_train_ms = _event_ms(dstep, 2)
         key_ms = per_kernel_ms.get("bwd_key_kernel")
+        p1 = ops.make_problem(q, side, side, 1, 32)
+        s1 = Step(p1, q, k, v, do)
+        single_ms, _, _, single_kernel_ms, _ = measure(s1, steps, 2)
+        del s1
         print(json.dumps({
             "side": side, "tokens": n, "batch": 1, "heads": 6, "levels": levels,
             "llsa_fwd_ms": round(fwd_ms, 4), "llsa_train_ms": round(train_ms, 4),
             "dense_fwd_ms": round(dense_fwd_ms, 3), "dense_train_ms": round(dense_train_ms, 3),
             "speedup_fwd": round(dense_fwd_ms / fwd_ms, 2),
             "speedup_train": round(dense_train_ms / train_ms, 2),
+            "single_level_top32_train_ms": round(single_ms, 4),
+            "single_level_select_ms": round(single_kernel_ms.get("select_kernel", 0.0), 4),
+            "llsa_select_ms": round(per_kernel_ms.get("select_kernel", 0.0), 4),
+            "speedup_vs_single_level": round(single_ms / train_ms, 2),
             "llsa_train_tokens_per_s": round(6 * n / (train_ms / 1e3), 1),
             "key_pass_ms": round(key_ms, 4) if key_ms else None,
             "key_pass_block_pairs_per_s": round(pairs / (key_ms / 1e3), 1) if key_ms else None,
@@ -397,6 +423,7 @@ def main():
             fwd256 = measure(s256, 10, 2)[0]
             del s256
         extra["dense_baseline"] = dense_baseline(fwd256, ms_step)
+        extra["single_level_top32"] = single_level(args.config, ms_step, max(5, args.steps // 2))
     cpu = None if args.no_cpu else cpu_baseline(cfg, x)
     line = {
         "metric": "LLSA fwd+bwd tokens/s at 256x256 pixels (65,536 tok); % MFMA/HBM peak",

@@ -128,7 +128,8 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* st, int t4, int lane) {
 constexpr int kQWaves = 4;
 constexpr int kQBlocks = 2;     // query blocks per wave
 constexpr int kUnits = 2;       // partial units (workgroups) per level-2 group
-constexpr int kQPickList = 64;  // pick-list capacity per wave (2 K <= 32)
+constexpr int kQPickList = 64;  // pick-list capacity per wave
+constexpr int kQPickSlots = kQPickList / kQBlocks;   // pick slots per query block (K <= 32)
 constexpr int kPickSentinel = 0x7f000000;
 
 __host__ __device__ constexpr int bwdq_wave_lds_bytes() {
@@ -190,10 +191,11 @@ void bwd_query_kernel(BwdArgs a) {
       make_rsrc_uniform((const char*)a.dout + (size_t)head * head_bytes, head_bytes);
   const rsrc_t rl = make_rsrc_uniform(a.lse + tok_base, (uint32_t)a.n * 4);
 
-  // ---- the wave's picks (lane 16b + i: pick i of block b) and its query-side operands
+  // ---- the wave's picks (lane 32b + i: pick i of block b) and its query-side operands
   int key = kPickSentinel | lane;
-  if (lane < 16 * kQBlocks && (lane & 15) < K) {
-    const int j = a.sel[0][((long)head * n1 + pb_first + (lane >> 4)) * K + (lane & 15)];
+  if ((lane % kQPickSlots) < K) {
+    const int j =
+        a.sel[0][((long)head * n1 + pb_first + lane / kQPickSlots) * K + lane % kQPickSlots];
     if (j >= 0 && j < n1) key = (j << 8) | lane;
   }
   bf16x8 qh[kQBlocks][2], dh[kQBlocks][2];   // B operands: lane (n, g) row n, ch 32s + 8g..
@@ -277,7 +279,7 @@ void bwd_query_kernel(BwdArgs a) {
       for (int r = lane; r < min(lane + kQBlocks, kQPickList); ++r) {
         const int o = sorted[r];
         if ((o >> 8) != (sk >> 8)) break;
-        m |= 1 << ((o & 63) >> 4);
+        m |= 1 << ((o & 63) / kQPickSlots);
       }
       uoff[u] = block_corner(sk >> 8, a.grid) * kDim * 2;
       umask[u] = m;

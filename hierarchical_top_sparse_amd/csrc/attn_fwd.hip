@@ -2,11 +2,12 @@
 // sec. 三/四: the forward gathers the selected key blocks directly, no dense mask).
 //
 // One workgroup owns one level-2 group (the 16 level-1 query blocks of a 16x16-pixel tile,
-// which share their ancestors and so their coarse keys); each of its 4 waves owns 4
-// consecutive query blocks and works on its own, without workgroup barriers:
-//  1. its 4 K picks are ranked in LDS (keys (id, owner)) into the ascending list U of distinct
-//     key blocks, with a 4-bit mask per entry of the blocks that picked it.  Neighbouring query
-//     blocks choose among the same candidates, so U is much shorter than 4 K;
+// which share their ancestors and so their coarse keys), or half of one when K > 16; each of
+// its 4 waves owns QB consecutive query blocks (QB = 4, or 2 when K > 16, so that the wave's
+// QB K picks fit its 64 lanes) and works on its own, without workgroup barriers:
+//  1. its QB K picks are ranked in LDS (keys (id, owner)) into the ascending list U of distinct
+//     key blocks, with a QB-bit mask per entry of the blocks that picked it.  Neighbouring
+//     query blocks choose among the same candidates, so U is much shorter than QB K;
 //  2. the wave streams U: each key block's 16 K rows and 16 V rows are loaded row-major (each
 //     4-lane quad reads 64 contiguous bytes: the vector memory pipeline charges a quad per
 //     distinct cache line, so MFMA-operand-shaped loads cost 4x as much), two blocks ahead of
@@ -59,7 +60,7 @@ __device__ __forceinline__ void split_bf16(f32x4 a, f32x4 b, bf16x8& hi, bf16x8&
   }
 }
 
-constexpr int kWavePicks = 64;     // 4 query blocks x K (K <= 16)
+constexpr int kWavePicks = 64;     // QB query blocks x K (QB K <= 64)
 constexpr int kSentinel = 0x7f000000;
 
 template <bool BF16>
@@ -88,9 +89,11 @@ static size_t fwd_lds_bytes(bool bf16, int n_coarse) {
          sizeof(float) * 16 * ctiles;
 }
 
-template <bool BF16>
+template <bool BF16, int QB>   // QB: query blocks per wave (4, or 2 for K > 16)
 __global__ __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 2)))
 void attn_fwd_kernel(FwdArgs a) {
+  constexpr int PS = kWavePicks / QB;                     // pick slots per query block
+  constexpr int kUnitsPerGroup = kBlock / (kFwdWaves * QB);   // workgroups per level-2 group
   using C = FwdCfg<BF16>;
   typedef typename std::conditional<BF16, bf16, float>::type T;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -102,8 +105,9 @@ void attn_fwd_kernel(FwdArgs a) {
   const int n1 = a.n >> kBlockShift;
   const int n2 = n1 >> kBlockShift;
   const int wg = uniform(xcd_block(blockIdx.x, gridDim.x));
-  const int head = uniform(wg / n2);   // scalar: buffer descriptors must be wave-uniform
-  const int a2 = uniform(wg - head * n2);
+  const int head = uniform(wg / (kUnitsPerGroup * n2));   // scalar: buffer descriptors must
+  const int rem = uniform(wg - head * kUnitsPerGroup * n2);   // be wave-uniform
+  const int a2 = rem / kUnitsPerGroup;
   const int K = a.topk;
   const long tok_base = (long)head * a.n;
   const int n_coarse = a.enrich ? (a.levels - 1) * K : 0;
@@ -123,20 +127,21 @@ void attn_fwd_kernel(FwdArgs a) {
   const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
   const rsrc_t rk = make_rsrc_uniform((const char*)a.k + (size_t)head * head_bytes, head_bytes);
   const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
-  const int pb_first = a2 * kBlock + 4 * w;   // the wave's first query block
+  // the wave's first query block
+  const int pb_first = a2 * kBlock + (rem % kUnitsPerGroup) * (kFwdWaves * QB) + QB * w;
 
-  // ---- the wave's picks (lane 16b + i: pick i of block b) and its query operands
+  // ---- the wave's picks (lane PS b + i: pick i of block b) and its query operands
   int key = kSentinel | lane;   // sentinels sort after every pick and stay distinct
-  if ((lane & 15) < K) {
-    const int j = a.sel[0][((long)head * n1 + pb_first + (lane >> 4)) * K + (lane & 15)];
+  if ((lane % PS) < K) {
+    const int j = a.sel[0][((long)head * n1 + pb_first + lane / PS) * K + (lane % PS)];
     if (j >= 0 && j < n1) key = (j << 8) | lane;
   }
   // B operand of S^T for block bb: lane (n, g) holds query row n, channels 32s + 8g .. +7
   // (bf16) or 16g + 4c .. +3 (fp32)
-  bf16x8 qh[4][2];
-  f32x4 qf[4][4];
+  bf16x8 qh[QB][2];
+  f32x4 qf[QB][4];
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) {
+  for (int bb = 0; bb < QB; ++bb) {
     const uint32_t qrow =
         (uint32_t)(block_corner(pb_first + bb, a.grid) + tile_offset(n, a.grid)) * C::kRowBytes;
     if constexpr (BF16) {
@@ -213,10 +218,10 @@ void attn_fwd_kernel(FwdArgs a) {
     const int u = __builtin_popcountll(fm & (~0ull >> (63 - lane))) - 1;
     if (first) {   // the run of this key block: one entry per block that picked it
       int m = 0;
-      for (int r = lane; r < min(lane + 4, kWavePicks); ++r) {
+      for (int r = lane; r < min(lane + QB, kWavePicks); ++r) {
         const int o = sorted[r];
         if ((o >> 8) != (sk >> 8)) break;
-        m |= 1 << ((o & 63) >> 4);
+        m |= 1 << ((o & 63) / PS);
       }
       uoff[u] = block_corner(sk >> 8, a.grid) * C::kRowBytes;
       umask[u] = m;
@@ -248,10 +253,10 @@ void attn_fwd_kernel(FwdArgs a) {
   BlockLd fa = load_u(0), fb = load_u(1);
   __syncthreads();   // coarse tiles staged (the only workgroup barrier)
 
-  float m_run[4], l_run[4];   // running max (log2 domain) and this lane's partial sums
-  f32x4 acc[4][4];            // O^T of each block: lane (n, g) holds d = 16 t4 + 4g + i
+  float m_run[QB], l_run[QB];   // running max (log2 domain) and this lane's partial sums
+  f32x4 acc[QB][4];             // O^T of each block: lane (n, g) holds d = 16 t4 + 4g + i
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) {
+  for (int bb = 0; bb < QB; ++bb) {
     m_run[bb] = kMinusBig;
     l_run[bb] = 0.f;
 #pragma unroll
@@ -339,8 +344,10 @@ void attn_fwd_kernel(FwdArgs a) {
   auto for_blocks = [&](auto&& fn) {
     fn(I0{});
     fn(I1{});
-    fn(I2{});
-    fn(I3{});
+    if constexpr (QB > 2) {
+      fn(I2{});
+      fn(I3{});
+    }
   };
 
   // one block of U from its loads: rows to the wave's LDS tile, then the tiles of the blocks
@@ -430,18 +437,27 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const v
   a.c2 = s.scale * kLog2e;
   const int n_coarse = s.enrich ? (s.levels - 1) * s.topk : 0;
   const size_t lds = fwd_lds_bytes(s.bf16, n_coarse);
-  // one workgroup per level-2 group (N is a multiple of 16^2)
-  const unsigned blocks = (unsigned)((long)s.bh * (s.n >> (2 * kBlockShift)));
-  const void* fn = s.bf16 ? (const void*)attn_fwd_kernel<true> : (const void*)attn_fwd_kernel<false>;
+  // one workgroup per level-2 group (N is a multiple of 16^2), two when K > 16
+  const bool wide = s.topk > kWavePicks / 4;
+  const unsigned blocks = (unsigned)((long)s.bh * (s.n >> (2 * kBlockShift)) * (wide ? 2 : 1));
+  const void* fn = s.bf16 ? (wide ? (const void*)attn_fwd_kernel<true, 2>
+                                  : (const void*)attn_fwd_kernel<true, 4>)
+                          : (wide ? (const void*)attn_fwd_kernel<false, 2>
+                                  : (const void*)attn_fwd_kernel<false, 4>);
   if (lds > 65536) {
     const hipError_t e =
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  if (s.bf16)
-    LLSA_LAUNCH("attn_fwd_kernel", attn_fwd_kernel<true>, dim3(blocks), dim3(64 * kFwdWaves), lds, stream, a);
+  const dim3 grid(blocks), block(64 * kFwdWaves);
+  if (s.bf16 && !wide)
+    LLSA_LAUNCH("attn_fwd_kernel", (attn_fwd_kernel<true, 4>), grid, block, lds, stream, a);
+  else if (s.bf16)
+    LLSA_LAUNCH("attn_fwd_kernel", (attn_fwd_kernel<true, 2>), grid, block, lds, stream, a);
+  else if (!wide)
+    LLSA_LAUNCH("attn_fwd_kernel", (attn_fwd_kernel<false, 4>), grid, block, lds, stream, a);
   else
-    LLSA_LAUNCH("attn_fwd_kernel", attn_fwd_kernel<false>, dim3(blocks), dim3(64 * kFwdWaves), lds, stream, a);
+    LLSA_LAUNCH("attn_fwd_kernel", (attn_fwd_kernel<false, 2>), grid, block, lds, stream, a);
   return hipGetLastError();
 }
 

@@ -283,8 +283,11 @@ hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* 
   if (s.topk <= 8)
     LLSA_LAUNCH("select_kernel", select_kernel<8>, dim3(blocks), dim3(64 * kSelWaves), 0, stream,
                 a);
-  else
+  else if (s.topk <= 16)
     LLSA_LAUNCH("select_kernel", select_kernel<16>, dim3(blocks), dim3(64 * kSelWaves), 0,
+                stream, a);
+  else
+    LLSA_LAUNCH("select_kernel", select_kernel<32>, dim3(blocks), dim3(64 * kSelWaves), 0,
                 stream, a);
   return hipGetLastError();
 }

@@ -28,7 +28,7 @@
  *    llsa_last_error() gives a message for the last failure on the calling thread.
  *  - Results are deterministic: no atomics, fixed reduction orders.
  *  - Supported: head_dim 64, block 16 (4x4 pixel tiles), height and width powers of two
- *    >= 4, 256 <= N <= 2^23, N % block^levels == 0, 1 <= topk <= min(16, N / block^levels),
+ *    >= 4, 256 <= N <= 2^23, N % block^levels == 0, 1 <= topk <= min(32, N / block^levels),
  *    1 <= levels <= 6, batch*heads*N < 2^31.  dtype bf16 for every call; f32 for
  *    reorder/pool/select/attn_fwd.
  */
@@ -44,7 +44,7 @@ extern "C" {
 
 #define LLSA_ABI_VERSION 1
 #define LLSA_MAX_LEVELS 6
-#define LLSA_MAX_TOPK 16
+#define LLSA_MAX_TOPK 32
 
 typedef enum {
   LLSA_OK = 0,

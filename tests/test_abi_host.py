@@ -56,7 +56,7 @@ def _p(**kw):
     (dict(height=2, width=256, levels=1), 2),   # a side shorter than a 4x4 tile
     (dict(height=4096, width=4096, levels=1), 2),  # more than 2^23 tokens
     (dict(levels=3), 2),                    # N % B^L != 0
-    (dict(topk=17), 2),                     # above the 16 supported
+    (dict(topk=33), 2),                     # above the 32 supported
     (dict(levels=2, topk=9, height=32, width=64), 2),  # K > N / B^L = 8
     (dict(topk=0), 2),
     (dict(head_dim=128), 4),

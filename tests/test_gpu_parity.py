@@ -74,7 +74,9 @@ def test_pool_matches_oracle(h, w, levels, dtype, layout):
 
 
 @pytest.mark.parametrize("h,w,levels,topk", [(64, 64, 2, 8), (128, 128, 2, 8), (256, 256, 3, 8),
-                                             (128, 256, 3, 5), (64, 64, 1, 16), (64, 64, 2, 3)])
+                                             (128, 256, 3, 5), (64, 64, 1, 16), (64, 64, 2, 3),
+                                             (128, 128, 1, 32), (128, 128, 2, 32),
+                                             (256, 256, 1, 32), (64, 128, 1, 20)])
 def test_select_matches_oracle_within_tie_window(h, w, levels, topk):
     d, ref = _inputs(1, 3, h, w, torch.bfloat16, 21)
     p = _problem(d["q"], h, w, levels, topk)
@@ -190,6 +192,10 @@ def _oracle_sel(ref, h, w, levels, topk, b=0, hh=0):
     (128, 256, 3, 8, True, torch.bfloat16, RASTER),
     (128, 128, 2, 7, False, torch.bfloat16, RASTER),
     (64, 64, 1, 16, False, torch.float32, MORTON),
+    (128, 128, 1, 32, False, torch.bfloat16, RASTER),
+    (128, 128, 2, 32, True, torch.bfloat16, MORTON),
+    (64, 128, 1, 24, False, torch.float32, RASTER),
+    (128, 128, 2, 17, True, torch.float32, RASTER),
 ])
 def test_attn_fwd_on_oracle_indices(h, w, levels, topk, enrich, dtype, layout):
     """Forward attention in isolation: GPU attention on the oracle's own selection."""
@@ -223,6 +229,9 @@ def test_attn_fwd_on_oracle_indices(h, w, levels, topk, enrich, dtype, layout):
     (128, 256, 3, 8, True, RASTER),
     (128, 128, 2, 8, False, RASTER),
     (64, 64, 1, 16, False, RASTER),
+    (128, 128, 1, 32, False, RASTER),
+    (128, 128, 2, 32, True, MORTON),
+    (64, 128, 1, 21, False, RASTER),
 ])
 def test_attn_bwd_on_oracle_indices(h, w, levels, topk, enrich, layout):
     """Backward in isolation: GPU gradients on the oracle's selection (and GPU forward)."""
@@ -253,12 +262,15 @@ def test_attn_bwd_on_oracle_indices(h, w, levels, topk, enrich, layout):
 # ----------------------------------------------------------------------------- whole path
 
 
-def _end_to_end(cfg_name, heads_checked, backward):
+def _end_to_end(cfg_name, heads_checked, backward, levels=None, topk=8):
+    """The whole path on a workload's full shape; levels/topk override the workload's (the
+    single-level comparator: levels 1, topk 32)."""
     cfg = gen.CONFIGS[cfg_name]
-    h, w, L = cfg["height"], cfg["width"], cfg["levels"]
+    h, w = cfg["height"], cfg["width"]
+    L = levels or cfg["levels"]
     d, ref = _inputs(cfg["batch"], cfg["heads"], h, w, cfg["dtype"], cfg["seed_base"],
                      grad=backward)
-    p = _problem(d["q"], h, w, L)
+    p = _problem(d["q"], h, w, L, topk)
     fwd = ops.llsa_forward(p, d["q"], d["k"], d["v"])
     grads = ops.llsa_backward(p, d["q"], d["k"], d["v"], fwd, d["do"]) if backward else None
     torch.cuda.synchronize()
@@ -268,9 +280,9 @@ def _end_to_end(cfg_name, heads_checked, backward):
         q64, k64, v64 = (ref[t][sl] for t in "qkv")
         q_lv = orc.pool_levels(orc.reorder(q64, h, w), 16, L)
         k_lv = orc.pool_levels(orc.reorder(k64, h, w), 16, L)
-        check_selection([s[sl] for s in sel_np], q_lv, k_lv, 8, f"{cfg_name} b{bi} h{hi}")
+        check_selection([s[sl] for s in sel_np], q_lv, k_lv, topk, f"{cfg_name} b{bi} h{hi}")
         sels = [[[s[bi, hi] for s in sel_np]]]
-        res = orc.llsa_forward(q64, k64, v64, h, w, 16, L, 8, True, sel_override=sels)
+        res = orc.llsa_forward(q64, k64, v64, h, w, 16, L, topk, True, sel_override=sels)
         assert_close(to64(fwd["o"][sl]), res["o"], cfg["dtype"], f"{cfg_name} o b{bi} h{hi}")
         assert_close(to64(fwd["lse"][sl]), res["lse"], cfg["dtype"], f"{cfg_name} lse")
         if backward:
@@ -297,6 +309,12 @@ def test_e2e_px256_train():
 
 def test_e2e_px512_train():
     _end_to_end("px512_train", [(0, 3)], backward=True)
+
+
+def test_e2e_px256_train_single_level_top32():
+    """The single-level comparator (one level, K = 32 blocks per query, selection over all
+    4096 blocks) on the 256x256 training shape."""
+    _end_to_end("px256_train", [(0, 2), (1, 5)], backward=True, levels=1, topk=32)
 
 
 def test_deterministic_and_autograd():
