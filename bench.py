@@ -313,6 +313,55 @@ def single_level(cfg_name, llsa_ms, steps):
     return out
 
 
+def mask_comparator(q, k, v, do, height, width, reps):
+    """Single level, K = 32: the CSC backward (index transpose + backward) against the
+    mask-based one (dense block mask + backward whose key-major pass scans it) on the same
+    forward state; per-kernel times from the library's event hook."""
+    import torch
+
+    from hierarchical_top_sparse_amd import _abi, ops
+    p = ops.make_problem(q, height, width, 1, 32)
+    fwd = ops.llsa_forward(p, q, k, v)
+    nmat, n1 = p.batch * p.heads, p.n_level(1)
+    tws = torch.empty(_abi.llsa_index_transpose_workspace(nmat, n1, n1, 32), device=q.device,
+                      dtype=torch.uint8)
+    off = torch.empty((p.batch, p.heads, n1 + 1), device=q.device, dtype=torch.int32)
+    rows = torch.empty((p.batch, p.heads, n1 * 32), device=q.device, dtype=torch.int32)
+    mask = torch.empty((p.batch, p.heads, n1, n1), device=q.device, dtype=torch.uint8)
+    bws = torch.empty(max(16, _abi.llsa_workspace_bytes(p)[1]), device=q.device,
+                      dtype=torch.uint8)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    sel = fwd["sel"]
+
+    def csc():
+        _abi.llsa_index_transpose(nmat, n1, n1, 32, sel[0], off, rows, tws)
+        _abi.llsa_attn_bwd(p, q, k, v, do, fwd["lse"], fwd["k_lv"], fwd["v_lv"], sel, [off],
+                           [rows], dq, dk, dv, bws)
+
+    def masked():
+        _abi.llsa_block_mask(p, sel[0], mask)
+        _abi.llsa_attn_bwd_masked(p, q, k, v, do, fwd["lse"], sel[0], mask, dq, dk, dv, bws)
+    out = {}
+    pairs = int(sel[0].numel())
+    for name, fn in (("csc", csc), ("mask", masked)):
+        fn()
+        ms = _event_ms(fn, reps)
+        _abi.llsa_profile_read()
+        _abi.llsa_profile_enable(True)
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        _abi.llsa_profile_enable(False)
+        kp = {kn: tot / reps for kn, (cnt, tot) in _abi.llsa_profile_read().items()}
+        key_ms = kp.get("bwd_key_mask_kernel" if name == "mask" else "bwd_key_kernel")
+        out[name] = {"bwd_ms": round(ms, 4),
+                     "kernels_ms": {kn: round(t, 4) for kn, t in sorted(kp.items())},
+                     "key_pass_block_pairs_per_s": round(pairs / (key_ms / 1e3), 1)}
+    out["speedup_csc_vs_mask"] = round(out["mask"]["bwd_ms"] / out["csc"]["bwd_ms"], 2)
+    del mask, fwd
+    return out
+
+
 def sweep(steps):
     """Resolution sweep (the shape of the pages' Figure 3 / Figure 4): per side length, LLSA
     forward and forward + backward against the dense baseline, and the key-major backward
@@ -349,6 +398,7 @@ def sweep(steps):
         s1 = Step(p1, q, k, v, do)
         single_ms, _, _, single_kernel_ms, _ = measure(s1, steps, 2)
         del s1
+        mc = mask_comparator(q, k, v, do, side, side, steps)
         print(json.dumps({
             "side": side, "tokens": n, "batch": 1, "heads": 6, "levels": levels,
             "llsa_fwd_ms": round(fwd_ms, 4), "llsa_train_ms": round(train_ms, 4),
@@ -359,6 +409,10 @@ def sweep(steps):
             "single_level_select_ms": round(single_kernel_ms.get("select_kernel", 0.0), 4),
             "llsa_select_ms": round(per_kernel_ms.get("select_kernel", 0.0), 4),
             "speedup_vs_single_level": round(single_ms / train_ms, 2),
+            "single_level_bwd_csc_ms": mc["csc"]["bwd_ms"],
+            "single_level_bwd_mask_ms": mc["mask"]["bwd_ms"],
+            "key_pass_csc_block_pairs_per_s": mc["csc"]["key_pass_block_pairs_per_s"],
+            "key_pass_mask_block_pairs_per_s": mc["mask"]["key_pass_block_pairs_per_s"],
             "llsa_train_tokens_per_s": round(6 * n / (train_ms / 1e3), 1),
             "key_pass_ms": round(key_ms, 4) if key_ms else None,
             "key_pass_block_pairs_per_s": round(pairs / (key_ms / 1e3), 1) if key_ms else None,
@@ -424,6 +478,10 @@ def main():
             del s256
         extra["dense_baseline"] = dense_baseline(fwd256, ms_step)
         extra["single_level_top32"] = single_level(args.config, ms_step, max(5, args.steps // 2))
+        qd, kd, vd, dod = (x[t].to("cuda") for t in ("q", "k", "v", "do"))
+        extra["mask_backward_comparator"] = mask_comparator(qd, kd, vd, dod, h, w,
+                                                            max(5, args.steps // 2))
+        del qd, kd, vd, dod
     cpu = None if args.no_cpu else cpu_baseline(cfg, x)
     line = {
         "metric": "LLSA fwd+bwd tokens/s at 256x256 pixels (65,536 tok); % MFMA/HBM peak",

@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
                                     i32),
             "llsa_dense_attn_bwd": ([i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, vp], i32),
+            "llsa_block_mask": ([P, vp, vp, vp], i32),
+            "llsa_attn_bwd_masked": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+                                     i32),
             "llsa_profile_enable": ([i32], i32),
             "llsa_profile_read": ([ctypes.c_char_p, sz], i32),
         }
@@ -111,8 +114,8 @@ def exported_symbols() -> list:
     return ["llsa_abi_version", "llsa_status_str", "llsa_last_error", "llsa_check",
             "llsa_workspace_bytes", "llsa_reorder", "llsa_pool", "llsa_select", "llsa_attn_fwd",
             "llsa_index_transpose_workspace", "llsa_index_transpose", "llsa_attn_bwd",
-            "llsa_dense_attn_fwd", "llsa_dense_attn_bwd", "llsa_profile_enable",
-            "llsa_profile_read"]
+            "llsa_dense_attn_fwd", "llsa_dense_attn_bwd", "llsa_block_mask",
+            "llsa_attn_bwd_masked", "llsa_profile_enable", "llsa_profile_read"]
 
 
 def _raise(status: int, name: str):
@@ -277,6 +280,34 @@ def llsa_attn_bwd(p: Problem, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_
                                _ptrs(csc_off), _ptrs(csc_rows), _ptr(dq), _ptr(dk), _ptr(dv),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "llsa_attn_bwd")
+
+
+def _mask_shape(p: Problem):
+    return (p.batch, p.heads, p.n_level(1), p.n_level(1))
+
+
+def llsa_block_mask(p: Problem, sel1, mask, stream=None):
+    """Dense level-1 block mask (uint8 [b, H, n_1, n_1]) of Sel_1: the mask-based comparator."""
+    _expect(sel1, _sel_shape(p, 1), torch.int32, "sel1")
+    _expect(mask, _mask_shape(p), torch.uint8, "mask")
+    _raise(lib().llsa_block_mask(ctypes.byref(p.c()), _ptr(sel1), _ptr(mask), _stream(stream)),
+           "llsa_block_mask")
+
+
+def llsa_attn_bwd_masked(p: Problem, q, k, v, dout, lse, sel1, mask, dq, dk, dv, ws,
+                         stream=None):
+    """llsa_attn_bwd without coarse keys, its key-major pass scanning the block mask."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        _expect(t, _tok_shape(p), p.torch_dtype, name)
+    _expect(lse, (p.batch, p.heads, p.n), torch.float32, "lse")
+    _expect(sel1, _sel_shape(p, 1), torch.int32, "sel1")
+    _expect(mask, _mask_shape(p), torch.uint8, "mask")
+    _raise(lib().llsa_attn_bwd_masked(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(dout), _ptr(lse), _ptr(sel1), _ptr(mask), _ptr(dq),
+                                      _ptr(dk), _ptr(dv), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)),
+           "llsa_attn_bwd_masked")
 
 
 def _dense_shapes(q):

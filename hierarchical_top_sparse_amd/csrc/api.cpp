@@ -287,8 +287,71 @@ int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const
     return fail(LLSA_ERR_WORKSPACE, "workspace of %zu bytes needed (%zu given)", need, ws_bytes);
   CHECK_PTR(ws, "ws");
   return hip_status(llsa::launch_attn_bwd(s, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off,
-                                          csc_rows, dq, dk, dv, ws, (hipStream_t)stream),
+                                          csc_rows, nullptr, dq, dk, dv, ws,
+                                          (hipStream_t)stream),
                     "llsa_attn_bwd");
+}
+
+}  // extern "C"
+
+namespace {
+
+// The mask-based comparator: bf16, no coarse keys, and a mask of at most 2^34 bytes.
+int32_t check_masked(const llsa_problem* p) {
+  int32_t st = check_problem(p);
+  if (st != LLSA_OK) return st;
+  if (p->dtype != LLSA_BF16)
+    return fail(LLSA_ERR_UNSUPPORTED, "the mask-based backward is implemented for bf16 only");
+  if (p->levels > 1 && p->enrich)
+    return fail(LLSA_ERR_UNSUPPORTED, "the mask-based backward has no coarse keys: levels must "
+                "be 1 or enrich 0");
+  const long n1 = (long)p->height * p->width / 16;
+  if ((long)p->batch * p->heads * n1 * n1 > (1L << 34))
+    return fail(LLSA_ERR_SHAPE, "block mask of %ld bytes exceeds 2^34",
+                (long)p->batch * p->heads * n1 * n1);
+  return LLSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t llsa_block_mask(const llsa_problem* p, const int32_t* sel1, uint8_t* mask,
+                        void* stream) {
+  int32_t st = check_masked(p);
+  if (st != LLSA_OK) return st;
+  CHECK_PTR(sel1, "sel1");
+  CHECK_PTR(mask, "mask");
+  return hip_status(llsa::launch_block_mask(make_shape(p), sel1, mask, (hipStream_t)stream),
+                    "llsa_block_mask");
+}
+
+int32_t llsa_attn_bwd_masked(const llsa_problem* p, const void* q, const void* k, const void* v,
+                             const void* dout, const float* lse, const int32_t* sel1,
+                             const uint8_t* mask, void* dq, void* dk, void* dv, void* ws,
+                             size_t ws_bytes, void* stream) {
+  int32_t st = check_masked(p);
+  if (st != LLSA_OK) return st;
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  CHECK_PTR(v, "v");
+  CHECK_PTR(dout, "dout");
+  CHECK_PTR(lse, "lse");
+  CHECK_PTR(sel1, "sel1");
+  CHECK_PTR(mask, "mask");
+  CHECK_PTR(dq, "dq");
+  CHECK_PTR(dk, "dk");
+  CHECK_PTR(dv, "dv");
+  const llsa::Shape s = make_shape(p);
+  const size_t need = llsa::bwd_workspace_bytes(s);
+  if (!ws || ws_bytes < need)
+    return fail(LLSA_ERR_WORKSPACE, "workspace of %zu bytes needed (%zu given)", need, ws_bytes);
+  CHECK_PTR(ws, "ws");
+  const int32_t* sel[LLSA_MAX_LEVELS] = {sel1};
+  const int32_t* none[LLSA_MAX_LEVELS] = {};
+  return hip_status(llsa::launch_attn_bwd(s, q, k, v, dout, lse, nullptr, nullptr, sel, none,
+                                          none, mask, dq, dk, dv, ws, (hipStream_t)stream),
+                    "llsa_attn_bwd_masked");
 }
 
 }  // extern "C"

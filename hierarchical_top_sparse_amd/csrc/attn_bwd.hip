@@ -47,6 +47,7 @@ struct BwdArgs {
   float* part_v;
   float* dk_lv[kMaxLv];        // level l >= 2: [bh, n_l, 64]
   float* dv_lv[kMaxLv];
+  const uint8_t* mask;         // block mask [bh, n_1, n_1] (mask-scanning key pass only)
   int bh;
   int n;
   Grid grid;
@@ -618,12 +619,18 @@ __global__ __launch_bounds__(64 * kCgWaves) void coarse_grad_kernel(BwdArgs a,
 // ====================================================================== stage 3: key-major
 // One wave per workgroup: key blocks differ widely in how many query blocks picked them, so a
 // wave that finishes early frees its slot at once.
+// MASK: the comparator of a mask-based backward -- the query blocks of key block j are found
+// by scanning column j of the dense block mask (all n_1 query blocks) instead of reading
+// CSC_1[j].  The scan yields them in ascending order, the order of the CSC rows, and they are
+// processed in the same batches of 64, so both variants give bit-identical dK and dV.
+template <bool MASK>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_kernel(
     BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 stQ[32 * kStride];
   __shared__ __attribute__((aligned(16))) bf16 stO[32 * kStride];   // dO rows
   __shared__ __attribute__((aligned(16))) float pdown[2 * kDim];    // pushed-down dK, dV
   __shared__ __attribute__((aligned(16))) float stL[64];            // lse (0..31), D (32..63)
+  __shared__ int pend[MASK ? 128 : 1];                              // mask hits not yet run
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int g = lane >> 4;
@@ -672,11 +679,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
   for (int ins = 0; ins < 4; ++ins)
     st_off[ins] = (uint32_t)(tile_offset((ins * 8 + srow0) & 15, a.grid) * kDim * 2 + 16 * piece);
   const bool lane_second = g >= 2;   // this lane's queries come from the second block
-
-  const int32_t* off = a.csc_off[0] + (long)head * (n1 + 1);
-  const int32_t* rows = a.csc_rows[0] + (long)head * n1 * a.topk;
-  const int e0 = uniform(off[j]);
-  const int e1 = uniform(off[j + 1]);
 
   struct PairLd {
     i32x4 q[4], d[4];   // staged Q and dO rows
@@ -762,16 +764,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     wave_lds_sync();
   };
 
-  // ---- query-block pairs of CSC_1[j]: two load buffers used in turn
-  for (int base = e0; base < e1; base += 64) {
-    cnt = min(64, e1 - base);
+  // ---- one batch of up to 64 query blocks (lane i: block p_lane of entry i), in pairs with
+  // two load buffers used in turn
+  auto batch = [&](int count, int p_lane) {
+    cnt = count;
     qtab = ttab = kNoRow;
-    if (lane < cnt) {
-      const int p = rows[base + lane];
-      if (p >= 0 && p < n1) {
-        qtab = (uint32_t)block_corner(p, a.grid) * kDim * 2;
-        ttab = (uint32_t)p * kBlock * 4;
-      }
+    if (lane < cnt && p_lane >= 0 && p_lane < n1) {
+      qtab = (uint32_t)block_corner(p_lane, a.grid) * kDim * 2;
+      ttab = (uint32_t)p_lane * kBlock * 4;
     }
     const int npairs = (cnt + 1) >> 1;
     PairLd fa = load_pair(0), fb;
@@ -781,6 +781,41 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
       if (k + 1 >= npairs) break;
       fa = load_pair(k + 2);
       pair(fb);
+    }
+  };
+  if constexpr (!MASK) {
+    const int32_t* off = a.csc_off[0] + (long)head * (n1 + 1);
+    const int32_t* rows = a.csc_rows[0] + (long)head * n1 * a.topk;
+    const int e0 = uniform(off[j]);
+    const int e1 = uniform(off[j + 1]);
+    for (int base = e0; base < e1; base += 64) {
+      const int count = min(64, e1 - base);
+      batch(count, lane < count ? rows[base + lane] : -1);
+    }
+  } else {
+    // column j of the mask, 64 query blocks per step; hits are appended to pend in order and
+    // run 64 at a time
+    const uint8_t* col = a.mask + (long)head * n1 * n1 + j;
+    int npend = 0;
+    for (int scan = 0; scan < n1; scan += 64) {
+      const int p = scan + lane;
+      const bool hit = p < n1 && col[(long)p * n1] != 0;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(hit);
+      if (hit) pend[npend + __builtin_popcountll(bal & ((1ull << lane) - 1))] = p;
+      npend += __builtin_popcountll(bal);
+      if (npend >= 64) {
+        wave_lds_sync();
+        batch(64, pend[lane]);
+        const int rest = npend - 64;
+        const int moved = lane < rest ? pend[64 + lane] : 0;
+        wave_lds_sync();
+        if (lane < rest) pend[lane] = moved;
+        npend = rest;
+      }
+    }
+    if (npend > 0) {
+      wave_lds_sync();
+      batch(npend, lane < npend ? pend[lane] : -1);
     }
   }
 
@@ -840,8 +875,8 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
                            const void* dout, const float* lse,
                            const float* const* k_lv, const float* const* v_lv,
                            const int32_t* const* sel, const int32_t* const* csc_off,
-                           const int32_t* const* csc_rows, void* dq, void* dk, void* dv,
-                           void* ws, hipStream_t stream) {
+                           const int32_t* const* csc_rows, const uint8_t* mask, void* dq,
+                           void* dk, void* dv, void* ws, hipStream_t stream) {
   const BwdLayout L = bwd_layout(s);
   char* base = (char*)ws;
   BwdArgs a{};
@@ -908,7 +943,14 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const long kwaves = (long)s.bh * (s.n >> kBlockShift);
-  LLSA_LAUNCH("bwd_key_kernel", bwd_key_kernel, dim3((unsigned)kwaves), dim3(64), 0, stream, a);
+  if (mask) {
+    a.mask = mask;
+    LLSA_LAUNCH("bwd_key_mask_kernel", bwd_key_kernel<true>, dim3((unsigned)kwaves), dim3(64),
+                0, stream, a);
+  } else {
+    LLSA_LAUNCH("bwd_key_kernel", bwd_key_kernel<false>, dim3((unsigned)kwaves), dim3(64), 0,
+                stream, a);
+  }
   return hipGetLastError();
 }
 

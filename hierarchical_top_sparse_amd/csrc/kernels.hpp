@@ -57,8 +57,13 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
                            const void* dout, const float* lse,
                            const float* const* k_lv, const float* const* v_lv,
                            const int32_t* const* sel, const int32_t* const* csc_off,
-                           const int32_t* const* csc_rows, void* dq, void* dk, void* dv,
-                           void* ws, hipStream_t stream);
+                           const int32_t* const* csc_rows, const uint8_t* mask, void* dq,
+                           void* dk, void* dv, void* ws, hipStream_t stream);
+
+// Dense block mask [bh, n_1, n_1] (1 where key block c is in Sel_1[a]) of the mask-based
+// comparator.
+hipError_t launch_block_mask(const Shape& s, const int32_t* sel1, uint8_t* mask,
+                             hipStream_t stream);
 
 // Dense softmax attention over [bh, n, 64] bf16 sequences (the full-attention baseline).
 hipError_t launch_dense_fwd(int bh, int n, float scale, const void* q, const void* k,

@@ -14,12 +14,13 @@ import torch
 
 from . import _abi
 from ._abi import (LLSA_BF16, LLSA_F32, LLSA_LAYOUT_MORTON, LLSA_LAYOUT_RASTER, Problem,
-                   llsa_attn_bwd, llsa_attn_fwd, llsa_index_transpose,
-                   llsa_index_transpose_workspace, llsa_pool, llsa_reorder, llsa_select,
-                   llsa_workspace_bytes)
+                   llsa_attn_bwd, llsa_attn_bwd_masked, llsa_attn_fwd, llsa_block_mask,
+                   llsa_index_transpose, llsa_index_transpose_workspace, llsa_pool,
+                   llsa_reorder, llsa_select, llsa_workspace_bytes)
 
-__all__ = ["Problem", "make_problem", "llsa_forward", "llsa_backward", "llsa_attention",
-           "reorder", "LLSA_BF16", "LLSA_F32", "LLSA_LAYOUT_MORTON", "LLSA_LAYOUT_RASTER"]
+__all__ = ["Problem", "make_problem", "llsa_forward", "llsa_backward", "llsa_backward_masked",
+           "llsa_attention", "reorder", "LLSA_BF16", "LLSA_F32", "LLSA_LAYOUT_MORTON",
+           "LLSA_LAYOUT_RASTER"]
 
 
 def make_problem(q: torch.Tensor, height: int, width: int, levels: int, topk: int = 8,
@@ -87,6 +88,20 @@ def llsa_backward(p: Problem, q, k, v, fwd: dict, dout):
     llsa_attn_bwd(p, q, k, v, dout, fwd["lse"], fwd["k_lv"], fwd["v_lv"], fwd["sel"], offs,
                   rows, dq, dk, dv, ws)
     return dq, dk, dv
+
+
+def llsa_backward_masked(p: Problem, q, k, v, fwd: dict, dout):
+    """The mask-based comparator of llsa_backward (no coarse keys): builds the dense level-1
+    block mask from Sel_1 and runs the backward whose key-major pass scans it.  Returns
+    (dq, dk, dv, mask)."""
+    mask = torch.empty((p.batch, p.heads, p.n_level(1), p.n_level(1)), device=q.device,
+                       dtype=torch.uint8)
+    llsa_block_mask(p, fwd["sel"][0], mask)
+    _, ws_bytes = llsa_workspace_bytes(p)
+    ws = torch.empty(max(ws_bytes, 16), device=q.device, dtype=torch.uint8)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    llsa_attn_bwd_masked(p, q, k, v, dout, fwd["lse"], fwd["sel"][0], mask, dq, dk, dv, ws)
+    return dq, dk, dv, mask
 
 
 class _LLSAFunction(torch.autograd.Function):

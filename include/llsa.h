@@ -195,6 +195,28 @@ int32_t llsa_dense_attn_bwd(int32_t batch_heads, int32_t n, int32_t head_dim, fl
                             void* stream);
 
 /*
+ * llsa_block_mask / llsa_attn_bwd_masked — the mask-based comparator of the sparse backward
+ * (article sec. 4.1: sparse attention kernels that gather blocks in the forward but build a
+ * T x T binary mask in the backward pay O(T^2) again; its Figure 4 measures such a
+ * dense-mask baseline of the KV backward).  Not part of the sparse path.
+ * llsa_block_mask writes mask: uint8 [batch, heads, n_1, n_1], caller-owned, 16-byte
+ * aligned, mask[b][h][a][c] = 1 iff key block c is in sel1[b][h][a] (sel1 = Sel_1 as from
+ * llsa_select), 0 elsewhere; it clears all batch*heads*n_1^2 bytes.
+ * llsa_attn_bwd_masked computes what llsa_attn_bwd computes for a problem without coarse
+ * keys (levels 1, or enrich 0), with the key-major pass finding the query blocks of each key
+ * block by scanning its column of the mask instead of reading CSC_1; the results are
+ * bit-identical to llsa_attn_bwd's.  Arguments as for llsa_attn_bwd; ws: llsa_workspace_bytes
+ * (bwd) bytes.  Both: bf16 only; LLSA_ERR_UNSUPPORTED if levels > 1 and enrich, LLSA_ERR_SHAPE
+ * if the mask would exceed 2^34 bytes.  Errors otherwise as for the calls above.
+ */
+int32_t llsa_block_mask(const llsa_problem* p, const int32_t* sel1, uint8_t* mask,
+                        void* stream);
+int32_t llsa_attn_bwd_masked(const llsa_problem* p, const void* q, const void* k, const void* v,
+                             const void* dout, const float* lse, const int32_t* sel1,
+                             const uint8_t* mask, void* dq, void* dk, void* dv, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
  * Per-kernel timing (profiling aid, not part of the method).  llsa_profile_enable(1) makes
  * every later kernel launch of the library record a pair of hipEvents on its stream;
  * llsa_profile_read() waits for the recorded events, writes one line per kernel name,

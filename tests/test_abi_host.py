@@ -136,3 +136,25 @@ def test_dense_baseline_validation(L):
                                  None) == 6
     assert L.llsa_dense_attn_bwd(2, 1024, 64, 0.0, *([f] * 8), None, None) == 1
     assert L.llsa_dense_attn_bwd(2, 64, 64, 0.0, *([f] * 9), None) == 2
+
+
+def test_mask_comparator_validation(L):
+    f = ctypes.c_void_p(FAKE)
+    one = _p(height=128, width=128, levels=1, topk=32, dtype=abi.LLSA_BF16)
+    assert abi.llsa_check(one) == 0
+    # coarse keys (levels 2 with enrich) are not supported by the mask-based backward
+    two = _p(height=128, width=128, levels=2, topk=8, dtype=abi.LLSA_BF16)
+    assert L.llsa_block_mask(ctypes.byref(two.c()), f, f, None) == 4
+    assert L.llsa_attn_bwd_masked(ctypes.byref(two.c()), *([f] * 11), 1 << 30, None) == 4
+    # fp32 is not supported; missing / misaligned pointers; workspace too small
+    f32 = _p(height=128, width=128, levels=1, topk=32, dtype=abi.LLSA_F32)
+    assert L.llsa_block_mask(ctypes.byref(f32.c()), f, f, None) == 4
+    assert L.llsa_block_mask(ctypes.byref(one.c()), None, f, None) == 1
+    assert L.llsa_block_mask(ctypes.byref(one.c()), f, ctypes.c_void_p(MISALIGNED), None) == 6
+    assert L.llsa_attn_bwd_masked(ctypes.byref(one.c()), *([f] * 6), None, *([f] * 4), 1 << 30,
+                                  None) == 1
+    assert L.llsa_attn_bwd_masked(ctypes.byref(one.c()), *([f] * 11), 4, None) == 5
+    # a mask over 2^34 bytes: 1024x1024 pixels, n_1 = 65536, 8 heads -> 2^35
+    big = _p(batch=1, heads=8, height=1024, width=1024, levels=1, topk=8, dtype=abi.LLSA_BF16)
+    assert abi.llsa_check(big) == 0
+    assert L.llsa_block_mask(ctypes.byref(big.c()), f, f, None) == 2
