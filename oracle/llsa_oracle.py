@@ -26,6 +26,9 @@ Readings where the pages are silent or garbled (each is listed in the design not
   * ranking scores are plain dot products of pooled Q_l and pooled K_l;
   * enrichment adds, for every level l = 2..L, the K keys selected at level l for the query
     block's level-l ancestor; no de-duplication against the fine keys;
+  * variants (switches, not the method's default): enrich_levels = m keeps only the coarse
+    levels 2..1+m (the finest m; 0 = all), coarse_weight False gives every coarse key weight 1
+    instead of B^l;
   * gradients flow to Q, K, V and through the pooled K/V of the coarse keys (chain rule of
     the mean), not through the top-K selection or the pooled Q.
 
@@ -164,12 +167,13 @@ def select(q_lv: Sequence[np.ndarray], k_lv: Sequence[np.ndarray], block: int,
 
 
 def key_list(p: int, k: np.ndarray, v: np.ndarray, k_lv, v_lv, sel, block: int,
-             enrich: bool):
+             enrich: bool, enrich_levels: int = 0, coarse_weight: bool = True):
     """Keys, values and log-weights attended by level-1 query block p.
 
     Fine: every token of the K blocks in Sel_1[p] (log-weight 0).
     Coarse (enrich): for l = 2..L, the keys Sel_l[a] of block p's level-l ancestor
-    a = p // B^(l-1), each with weight B^l (log-weight l*ln B).
+    a = p // B^(l-1), each with weight B^l (log-weight l*ln B).  Variants: enrich_levels m > 0
+    stops at level min(L, 1 + m); coarse_weight False uses weight 1 (log-weight 0).
     Also returns the identity of every key: (level, index), level 0 = fine token.
     """
     keys, vals, logw, ident = [], [], [], []
@@ -180,18 +184,20 @@ def key_list(p: int, k: np.ndarray, v: np.ndarray, k_lv, v_lv, sel, block: int,
         logw.append(np.zeros(block))
         ident += [(0, int(t)) for t in toks]
     if enrich:
-        for l in range(2, len(sel) + 1):
+        top = len(sel) if not enrich_levels else min(len(sel), 1 + enrich_levels)
+        for l in range(2, top + 1):
             a = p // block ** (l - 1)
             ids = sel[l - 1][a]
             keys.append(k_lv[l - 1][ids])
             vals.append(v_lv[l - 1][ids])
-            logw.append(np.full(len(ids), l * math.log(block)))
+            logw.append(np.full(len(ids), l * math.log(block) if coarse_weight else 0.0))
             ident += [(l, int(j)) for j in ids]
     return np.concatenate(keys), np.concatenate(vals), np.concatenate(logw), ident
 
 
 def attention_forward(q, k, v, k_lv, v_lv, sel, block: int, enrich: bool = True,
-                      scale: float | None = None, blocks=None):
+                      scale: float | None = None, blocks=None, enrich_levels: int = 0,
+                      coarse_weight: bool = True):
     """Per-head forward in Morton order.  Returns (o [N, d], lse [N]) (rows of `blocks` only
     are filled when `blocks` is given; the rest stay NaN).
 
@@ -204,7 +210,8 @@ def attention_forward(q, k, v, k_lv, v_lv, sel, block: int, enrich: bool = True,
     lse = np.full(n, np.nan)
     nblk = n // block
     for p in (range(nblk) if blocks is None else blocks):
-        kk, vv, logw, _ = key_list(p, k, v, k_lv, v_lv, sel, block, enrich)
+        kk, vv, logw, _ = key_list(p, k, v, k_lv, v_lv, sel, block, enrich, enrich_levels,
+                                   coarse_weight)
         rows = slice(p * block, (p + 1) * block)
         s = scale * (q[rows] @ kk.T) + logw[None, :]
         m = s.max(axis=1, keepdims=True)
@@ -216,7 +223,8 @@ def attention_forward(q, k, v, k_lv, v_lv, sel, block: int, enrich: bool = True,
 
 
 def attention_backward(q, k, v, k_lv, v_lv, sel, do, block: int, enrich: bool = True,
-                       scale: float | None = None):
+                       scale: float | None = None, enrich_levels: int = 0,
+                       coarse_weight: bool = True):
     """Per-head gradients (dq, dk, dv) in Morton order, given upstream dO.
 
     Softmax Jacobian per query: P_e = w_e exp(s_e) / Z, dP_e = dO.v_e,
@@ -235,7 +243,8 @@ def attention_backward(q, k, v, k_lv, v_lv, sel, do, block: int, enrich: bool = 
     dk_lv = [np.zeros_like(x) for x in k_lv]
     dv_lv = [np.zeros_like(x) for x in v_lv]
     for p in range(n // block):
-        kk, vv, logw, ident = key_list(p, k, v, k_lv, v_lv, sel, block, enrich)
+        kk, vv, logw, ident = key_list(p, k, v, k_lv, v_lv, sel, block, enrich, enrich_levels,
+                                       coarse_weight)
         rows = slice(p * block, (p + 1) * block)
         s = scale * (q[rows] @ kk.T) + logw[None, :]
         m = s.max(axis=1, keepdims=True)
@@ -327,7 +336,8 @@ def csr_to_csc(sel: np.ndarray, n_cols: int):
 
 
 def llsa_forward(q, k, v, height: int, width: int, block: int, levels: int, topk,
-                 enrich: bool = True, scale: float | None = None, sel_override=None):
+                 enrich: bool = True, scale: float | None = None, sel_override=None,
+                 enrich_levels: int = 0, coarse_weight: bool = True):
     """Full forward: reorder -> pool -> select -> attention -> inverse reorder.
 
     Returns a dict with o (raster), lse (Morton order, [b, H, N]), and the Morton-order
@@ -348,8 +358,9 @@ def llsa_forward(q, k, v, height: int, width: int, block: int, levels: int, topk
             vl = [x[bi, hi] for x in v_lv]
             sel = (select(ql, kl, block, topk) if sel_override is None
                    else sel_override[bi][hi])
-            om[bi, hi], lse[bi, hi] = attention_forward(qm[bi, hi], km[bi, hi], vm[bi, hi],
-                                                        kl, vl, sel, block, enrich, scale)
+            om[bi, hi], lse[bi, hi] = attention_forward(
+                qm[bi, hi], km[bi, hi], vm[bi, hi], kl, vl, sel, block, enrich, scale,
+                enrich_levels=enrich_levels, coarse_weight=coarse_weight)
             row.append(sel)
         sels.append(row)
     return dict(o=reorder(om, height, width, inverse=True), om=om, lse=lse, qm=qm, km=km,
@@ -357,7 +368,8 @@ def llsa_forward(q, k, v, height: int, width: int, block: int, levels: int, topk
 
 
 def llsa_backward(q, k, v, do, height: int, width: int, block: int, levels: int, sels,
-                  enrich: bool = True, scale: float | None = None):
+                  enrich: bool = True, scale: float | None = None, enrich_levels: int = 0,
+                  coarse_weight: bool = True):
     """Full backward on the forward's selection: returns raster-order (dq, dk, dv)."""
     qm, km, vm, dom = (reorder(t, height, width) for t in (q, k, v, do))
     k_lv, v_lv = (pool_levels(t, block, levels) for t in (km, vm))
@@ -368,7 +380,7 @@ def llsa_backward(q, k, v, do, height: int, width: int, block: int, levels: int,
             vl = [x[bi, hi] for x in v_lv]
             dq[bi, hi], dk[bi, hi], dv[bi, hi] = attention_backward(
                 qm[bi, hi], km[bi, hi], vm[bi, hi], kl, vl, sels[bi][hi], dom[bi, hi], block,
-                enrich, scale)
+                enrich, scale, enrich_levels, coarse_weight)
     return tuple(reorder(t, height, width, inverse=True) for t in (dq, dk, dv))
 
 

@@ -195,19 +195,20 @@ def _sdpa(q, k, v, mask=None, scale=None):
                                                             scale=scale)
 
 
-def _dense_mask_formulation(qm, km, vm, sel, B, enrich, scale):
+def _dense_mask_formulation(qm, km, vm, sel, B, enrich, scale, top=None, weighted=True):
     """torch float64: one query row per token against [fine tokens ; pooled keys of levels
-    2..L], with an additive mask holding 0 (selected fine), l*ln B (selected coarse) or
-    -inf.  Token i's level-l ancestor is i // B^l.  Pooling is done with torch so autograd
-    carries gradients through it."""
+    2..top (default L)], with an additive mask holding 0 (selected fine), l*ln B (selected
+    coarse; 0 when not weighted) or -inf.  Token i's level-l ancestor is i // B^l.  Pooling is
+    done with torch so autograd carries gradients through it."""
     n, d = qm.shape
     L = len(sel)
+    top = L if top is None else top
     kl, vl = [km], [vm]
     for _ in range(L):
         kl.append(kl[-1].reshape(-1, B, d).mean(dim=1))
         vl.append(vl[-1].reshape(-1, B, d).mean(dim=1))
-    extra_k = [kl[l] for l in range(2, L + 1)] if enrich else []
-    extra_v = [vl[l] for l in range(2, L + 1)] if enrich else []
+    extra_k = [kl[l] for l in range(2, top + 1)] if enrich else []
+    extra_v = [vl[l] for l in range(2, top + 1)] if enrich else []
     keys = torch.cat([km] + extra_k)
     vals = torch.cat([vm] + extra_v)
     mask = np.full((n, keys.shape[0]), -np.inf)
@@ -218,9 +219,9 @@ def _dense_mask_formulation(qm, km, vm, sel, B, enrich, scale):
             mask[i, blk * B + t] = 0.0
     if enrich:
         base = n
-        for l in range(2, L + 1):
+        for l in range(2, top + 1):
             for slot in range(sel[l - 1].shape[1]):
-                mask[i, base + sel[l - 1][i // B ** l, slot]] = l * math.log(B)
+                mask[i, base + sel[l - 1][i // B ** l, slot]] = l * math.log(B) if weighted else 0
             base += n // B ** l
     return _sdpa(qm[None], keys[None], vals[None], mask[None], scale)[0]
 
@@ -241,6 +242,30 @@ def test_attention_matches_dense_mask_formulation(n, B, L, K, enrich):
     ref = _dense_mask_formulation(torch.tensor(q), torch.tensor(k), torch.tensor(v), sel, B,
                                   enrich, 1 / math.sqrt(q.shape[1]))
     assert np.allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("B,L,levels_kept,weighted", [(4, 3, 1, True), (4, 4, 2, False),
+                                                      (4, 3, 0, False), (16, 2, 1, False)])
+def test_enrichment_variants_match_dense_mask_formulation(B, L, levels_kept, weighted):
+    """The variants: only the finest `levels_kept` coarse levels (0 = all), and weight 1
+    instead of B^l; forward against the masked formulation, backward against its autograd."""
+    n = 4096 if B == 16 else 1024
+    q, k, v, kl, vl, sel = _attn_case(13, n=n, d=8, B=B, L=L, K=2)
+    do = _rand(q.shape, 14)
+    kw = dict(enrich_levels=levels_kept, coarse_weight=weighted)
+    o, _ = orc.attention_forward(q, k, v, kl, vl, sel, B, True, **kw)
+    top = L if levels_kept == 0 else min(L, 1 + levels_kept)
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    ref = _dense_mask_formulation(qt, kt, vt, sel, B, True, 1 / math.sqrt(q.shape[1]), top,
+                                  weighted)
+    assert np.allclose(o, ref.detach().numpy(), rtol=0, atol=1e-12)
+    ref.backward(torch.tensor(do))
+    grads = orc.attention_backward(q, k, v, kl, vl, sel, do, B, True, **kw)
+    for g, t in zip(grads, (qt, kt, vt)):
+        assert np.allclose(g, t.grad.numpy(), rtol=0, atol=1e-10)
+    # the default is the full enrichment with weights B^l: a variant must differ from it
+    o_full, _ = orc.attention_forward(q, k, v, kl, vl, sel, B, True)
+    assert not np.allclose(o, o_full, rtol=0, atol=1e-6) or (levels_kept == 0 and weighted)
 
 
 def test_attention_full_k_no_enrich_is_dense_attention():
