@@ -76,9 +76,9 @@ def kernel_model(p, elem_bytes=None):
         elem_bytes = 2 if p.torch_dtype == torch_bf16() else 4
     T = bh * n * d * elem_bytes
     kq_fine = K * 16
-    n_coarse = (L - 1) * K if p.enrich else 0
+    n_coarse = p.coarse_levels * K
     kq = kq_fine + n_coarse
-    pooled = sum(bh * (n // 16 ** l) * d * 4 * 2 for l in range(2, L + 1)) if p.enrich else 0
+    pooled = sum(bh * (n // 16 ** l) * d * 4 * 2 for l in range(2, 2 + p.coarse_levels))
     sel_bytes = sum(bh * (n // 16 ** l) * K * 4 for l in range(1, L + 1))
     tok4 = bh * n * 4                                     # one fp32 per token (lse or D)
     n2 = n // 256

@@ -20,6 +20,7 @@ _lib = None
 LLSA_F32, LLSA_BF16 = 0, 1
 LLSA_LAYOUT_MORTON, LLSA_LAYOUT_RASTER = 0, 1
 LLSA_MAX_LEVELS = 6
+LLSA_ABI_VERSION = 2   # the llsa_problem layout this binding marshals
 
 
 class LlsaError(RuntimeError):
@@ -32,7 +33,8 @@ class LlsaProblemC(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("batch", "heads", "height", "width", "head_dim", "block", "levels", "topk",
                  "enrich")] + [("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
-                               ("layout", ctypes.c_int32)]
+                               ("layout", ctypes.c_int32), ("enrich_levels", ctypes.c_int32),
+                               ("coarse_unit_weight", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -49,6 +51,16 @@ class Problem:
     scale: float = 0.0
     dtype: int = LLSA_BF16
     layout: int = LLSA_LAYOUT_RASTER
+    enrich_levels: int = 0        # with enrich: only coarse levels 2..1+m (0 = all)
+    coarse_unit_weight: int = 0   # 1: coarse keys weighted 1 instead of B^l
+
+    @property
+    def coarse_levels(self) -> int:
+        """Coarse levels whose keys enrich the attention."""
+        if not self.enrich or self.levels < 2:
+            return 0
+        return self.levels - 1 if not self.enrich_levels else min(self.enrich_levels,
+                                                                   self.levels - 1)
 
     @property
     def n(self) -> int:
@@ -64,7 +76,8 @@ class Problem:
     def c(self) -> LlsaProblemC:
         return LlsaProblemC(self.batch, self.heads, self.height, self.width, self.head_dim,
                             self.block, self.levels, self.topk, int(self.enrich),
-                            float(self.scale), self.dtype, self.layout)
+                            float(self.scale), self.dtype, self.layout, self.enrich_levels,
+                            self.coarse_unit_weight)
 
 
 def lib() -> ctypes.CDLL:
@@ -75,6 +88,10 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
                                "`python -m hierarchical_top_sparse_amd.build`")
         L = ctypes.CDLL(_LIB_PATH)
+        L.llsa_abi_version.restype = ctypes.c_int32
+        if L.llsa_abi_version() != LLSA_ABI_VERSION:
+            raise RuntimeError(f"{_LIB_PATH} has ABI version {L.llsa_abi_version()}, the binding "
+                               f"expects {LLSA_ABI_VERSION}: rebuild it")
         P = ctypes.POINTER(LlsaProblemC)
         vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
         pp = ctypes.POINTER(ctypes.c_void_p)
@@ -230,8 +247,8 @@ def llsa_attn_fwd(p: Problem, q, k, v, k_lv, v_lv, sel, o, lse, stream=None):
         _expect(t, _tok_shape(p), p.torch_dtype, name)
     _expect(lse, (p.batch, p.heads, p.n), torch.float32, "lse")
     _expect(sel[0], _sel_shape(p, 1), torch.int32, "sel[0]")
-    if p.enrich:
-        for l in range(2, p.levels + 1):
+    if p.coarse_levels:
+        for l in range(2, 2 + p.coarse_levels):
             _expect(k_lv[l - 1], _lv_shape(p, l), torch.float32, f"k_lv[{l - 1}]")
             _expect(v_lv[l - 1], _lv_shape(p, l), torch.float32, f"v_lv[{l - 1}]")
             _expect(sel[l - 1], _sel_shape(p, l), torch.int32, f"sel[{l - 1}]")
@@ -265,7 +282,7 @@ def llsa_attn_bwd(p: Problem, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_
                     ("dv", dv)):
         _expect(t, _tok_shape(p), p.torch_dtype, name)
     _expect(lse, (p.batch, p.heads, p.n), torch.float32, "lse")
-    levels = p.levels if p.enrich else 1
+    levels = 1 + p.coarse_levels
     for l in range(1, levels + 1):
         _expect(sel[l - 1], _sel_shape(p, l), torch.int32, f"sel[{l - 1}]")
         _expect(csc_off[l - 1], (p.batch, p.heads, p.n_level(l) + 1), torch.int32,

@@ -72,11 +72,22 @@ int32_t check_problem(const llsa_problem* p) {
                 LLSA_MAX_TOPK, n_top);
   if (p->enrich != 0 && p->enrich != 1)
     return fail(LLSA_ERR_SHAPE, "enrich must be 0 or 1 (got %d)", p->enrich);
+  if (p->enrich_levels < 0)
+    return fail(LLSA_ERR_SHAPE, "enrich_levels must be >= 0 (got %d)", p->enrich_levels);
+  if (p->coarse_unit_weight != 0 && p->coarse_unit_weight != 1)
+    return fail(LLSA_ERR_SHAPE, "coarse_unit_weight must be 0 or 1 (got %d)",
+                p->coarse_unit_weight);
   if (!(p->scale >= 0.f) || std::isinf(p->scale))
     return fail(LLSA_ERR_SHAPE, "scale must be finite and >= 0");
   if ((long)p->batch * p->heads * n >= (1L << 31))
     return fail(LLSA_ERR_SHAPE, "batch*heads*N must be < 2^31");
   return LLSA_OK;
+}
+
+// Coarse levels whose keys enrich the attention: 2 .. 1 + the returned count.
+int coarse_levels(const llsa_problem* p) {
+  if (!p->enrich || p->levels < 2) return 0;
+  return p->enrich_levels == 0 ? p->levels - 1 : std::min(p->enrich_levels, p->levels - 1);
 }
 
 llsa::Shape make_shape(const llsa_problem* p) {
@@ -88,6 +99,8 @@ llsa::Shape make_shape(const llsa_problem* p) {
   s.levels = p->levels;
   s.topk = p->topk;
   s.enrich = p->enrich;
+  s.coarse_levels = coarse_levels(p);
+  s.coarse_lbias = p->coarse_unit_weight ? 0.f : 4.f;   // log2(16): weight 16^l
   s.raster = p->layout == LLSA_LAYOUT_RASTER;
   s.bf16 = p->dtype == LLSA_BF16;
   s.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim);
@@ -204,7 +217,7 @@ int32_t llsa_attn_fwd(const llsa_problem* p, const void* q, const void* k, const
   CHECK_PTR(lse, "lse");
   if (!sel) return fail(LLSA_ERR_NULL, "sel is NULL");
   for (int l = 1; l <= p->levels; ++l) {
-    if (l > 1 && !p->enrich) break;
+    if (l > 1 + coarse_levels(p)) break;
     CHECK_PTR(sel[l - 1], "selection");
     if (l >= 2) {
       if (!k_lv || !v_lv) return fail(LLSA_ERR_NULL, "pooled levels are NULL");
@@ -258,9 +271,9 @@ int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const
   if (st != LLSA_OK) return st;
   if (p->dtype != LLSA_BF16)
     return fail(LLSA_ERR_UNSUPPORTED, "the backward is implemented for bf16 only");
-  if (p->enrich && p->levels >= 2 && (p->levels - 1) * p->topk > 32)
+  if (coarse_levels(p) * p->topk > 32)
     return fail(LLSA_ERR_UNSUPPORTED, "backward supports at most 32 coarse keys per query "
-                "((levels-1)*topk = %d)", (p->levels - 1) * p->topk);
+                "(coarse levels * topk = %d)", coarse_levels(p) * p->topk);
   CHECK_PTR(q, "q");
   CHECK_PTR(k, "k");
   CHECK_PTR(v, "v");
@@ -271,7 +284,7 @@ int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const
   CHECK_PTR(dv, "dv");
   if (!sel || !csc_off || !csc_rows) return fail(LLSA_ERR_NULL, "index arrays are NULL");
   for (int l = 1; l <= p->levels; ++l) {
-    if (l > 1 && !p->enrich) break;
+    if (l > 1 + coarse_levels(p)) break;
     CHECK_PTR(sel[l - 1], "selection");
     CHECK_PTR(csc_off[l - 1], "csc_off");
     CHECK_PTR(csc_rows[l - 1], "csc_rows");
@@ -302,7 +315,7 @@ int32_t check_masked(const llsa_problem* p) {
   if (st != LLSA_OK) return st;
   if (p->dtype != LLSA_BF16)
     return fail(LLSA_ERR_UNSUPPORTED, "the mask-based backward is implemented for bf16 only");
-  if (p->levels > 1 && p->enrich)
+  if (coarse_levels(p) > 0)
     return fail(LLSA_ERR_UNSUPPORTED, "the mask-based backward has no coarse keys: levels must "
                 "be 1 or enrich 0");
   const long n1 = (long)p->height * p->width / 16;

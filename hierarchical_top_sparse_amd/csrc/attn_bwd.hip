@@ -53,7 +53,9 @@ struct BwdArgs {
   Grid grid;
   int levels;
   int topk;
-  int enrich;
+  int enrich;          // 1 if there are coarse keys (coarse_levels > 0)
+  int coarse_levels;   // coarse keys of levels 2 .. 1 + coarse_levels
+  float lbias;         // log2-domain bias per level: 4 (weight 16^l) or 0 (weight 1)
   float scale;
   float c2;   // scale * log2(e)
 };
@@ -170,7 +172,7 @@ void bwd_query_kernel(BwdArgs a) {
   const int pb_first = a2 * kBlock + (rem % kUnits) * (kBlock / kUnits) + kQBlocks * w;
   const int K = a.topk;
   const long tok_base = (long)head * a.n;
-  const int n_coarse = NCT > 0 ? (a.levels - 1) * K : 0;
+  const int n_coarse = NCT > 0 ? a.coarse_levels * K : 0;
 
   char* wb = smem + w * bwdq_wave_lds_bytes();
   bf16* kt = (bf16*)wb;                 // staged K rows (Q rows at a block's end)
@@ -233,7 +235,7 @@ void bwd_query_kernel(BwdArgs a) {
           k1 = *(const f32x4*)(kp + 4);
           v0 = *(const f32x4*)vp;
           v1 = *(const f32x4*)(vp + 4);
-          bias = 4.0f * (float)l;   // log2(16^l)
+          bias = a.lbias * (float)l;   // log2(16^l), or 0 for unit weights
         }
       }
       bf16* base = ct + (cslot >> 4) * 4 * 16 * kStride + (cslot & 15) * kStride + c8;
@@ -514,7 +516,7 @@ __device__ __forceinline__ void coarse_key_sum(const BwdArgs& a, int l, int head
   const int K = a.topk;
   const int nl = a.n >> (kBlockShift * l);
   const int n2 = a.n >> (2 * kBlockShift);
-  const int n_coarse = (a.levels - 1) * K;
+  const int n_coarse = a.coarse_levels * K;
   const int span = kUnits << (kBlockShift * (l - 2));   // partial units under one ancestor
   const uint32_t row_bytes = (uint32_t)n_coarse * kDim * 4;   // one unit's partial rows
   const uint32_t head_bytes = (uint32_t)n2 * kUnits * row_bytes;
@@ -644,7 +646,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
   // they arrive during the CSC lookups instead of after the pair loop
   float pk_sum = 0.f, pv_sum = 0.f;
   if (a.enrich) {
-    for (int l = 2; l <= a.levels; ++l) {
+    for (int l = 2; l <= 1 + a.coarse_levels; ++l) {
       const int nl = a.n >> (kBlockShift * l);
       const int anc = j >> (kBlockShift * (l - 1));
       const float f = 1.0f / (float)(1 << (kBlockShift * l));
@@ -854,12 +856,12 @@ static BwdLayout bwd_layout(const Shape& s) {
     return at;
   };
   L.dd = take(sizeof(float) * (size_t)s.bh * s.n);
-  if (s.enrich && s.levels >= 2) {
+  if (s.coarse_levels > 0) {
     const size_t n2 = (size_t)s.n_level(2);
-    const size_t nc = (size_t)(s.levels - 1) * s.topk;
+    const size_t nc = (size_t)s.coarse_levels * s.topk;
     L.part_k = take(sizeof(float) * s.bh * n2 * kUnits * nc * kDim);
     L.part_v = take(sizeof(float) * s.bh * n2 * kUnits * nc * kDim);
-    for (int l = 2; l <= s.levels; ++l) {
+    for (int l = 2; l <= 1 + s.coarse_levels; ++l) {
       const size_t nl = (size_t)s.n_level(l);
       L.dk_lv[l - 1] = take(sizeof(float) * s.bh * nl * kDim);
       L.dv_lv[l - 1] = take(sizeof(float) * s.bh * nl * kDim);
@@ -896,11 +898,12 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   a.dk = (bf16*)dk;
   a.dv = (bf16*)dv;
   a.dd = (float*)(base + L.dd);
-  const bool coarse = s.enrich && s.levels >= 2;
+  const bool coarse = s.coarse_levels > 0;
+  const int top = 1 + s.coarse_levels;   // the coarsest level with coarse keys
   if (coarse) {
     a.part_k = (float*)(base + L.part_k);
     a.part_v = (float*)(base + L.part_v);
-    for (int l = 2; l <= s.levels; ++l) {
+    for (int l = 2; l <= top; ++l) {
       a.dk_lv[l - 1] = (float*)(base + L.dk_lv[l - 1]);
       a.dv_lv[l - 1] = (float*)(base + L.dv_lv[l - 1]);
     }
@@ -911,12 +914,14 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   a.levels = s.levels;
   a.topk = s.topk;
   a.enrich = coarse ? 1 : 0;
+  a.coarse_levels = s.coarse_levels;
+  a.lbias = s.coarse_lbias;
   a.scale = s.scale;
   a.c2 = s.scale * kLog2e;
 
   const int n2 = s.n >> (2 * kBlockShift);
   const unsigned qblocks = (unsigned)(s.bh * n2 * kUnits);
-  const int n_coarse = coarse ? (s.levels - 1) * s.topk : 0;
+  const int n_coarse = s.coarse_levels * s.topk;
   const size_t qlds = bwd_query_lds_bytes(n_coarse);
   if (n_coarse == 0)
     LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<0>, dim3(qblocks), dim3(64 * kQWaves), qlds,
@@ -932,12 +937,12 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   if (coarse) {
     CoarseGradArgs cg{};
     long blocks = 0;
-    for (int l = 2; l <= s.levels; ++l) {   // level 2: kCgWaves keys per workgroup
+    for (int l = 2; l <= top; ++l) {   // level 2: kCgWaves keys per workgroup
       cg.first_block[l - 1] = (int)blocks;
       const long keys = (long)s.bh * s.n_level(l);
       blocks += l == 2 ? (keys + kCgWaves - 1) / kCgWaves : keys;
     }
-    for (int l = s.levels; l <= kMaxLv; ++l) cg.first_block[l] = (int)blocks;
+    for (int l = top; l <= kMaxLv; ++l) cg.first_block[l] = (int)blocks;
     LLSA_LAUNCH("coarse_grad_kernel", coarse_grad_kernel, dim3((unsigned)blocks),
                 dim3(64 * kCgWaves), 0, stream, a, cg);
     if ((err = hipGetLastError()) != hipSuccess) return err;

@@ -45,8 +45,9 @@ struct FwdArgs {
   Grid grid;
   int levels;
   int topk;
-  int enrich;
-  float c2;   // scale * log2(e)
+  int coarse_levels;   // coarse keys of levels 2 .. 1 + coarse_levels
+  float lbias;         // log2-domain bias per level: 4 (weight 16^l) or 0 (weight 1)
+  float c2;            // scale * log2(e)
 };
 
 __device__ __forceinline__ void split_bf16(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
@@ -110,7 +111,7 @@ void attn_fwd_kernel(FwdArgs a) {
   const int a2 = rem / kUnitsPerGroup;
   const int K = a.topk;
   const long tok_base = (long)head * a.n;
-  const int n_coarse = a.enrich ? (a.levels - 1) * K : 0;
+  const int n_coarse = a.coarse_levels * K;
   const int ctiles = (n_coarse + 15) >> 4;
 
   char* wbase = smem + w * fwd_wave_lds_bytes(BF16);
@@ -172,7 +173,7 @@ void attn_fwd_kernel(FwdArgs a) {
         k1 = *(const f32x4*)(kp + 4);
         v0 = *(const f32x4*)vp;
         v1 = *(const f32x4*)(vp + 4);
-        bias = 4.0f * (float)l;   // log2(16^l)
+        bias = a.lbias * (float)l;   // log2(16^l), or 0 for unit weights
       }
     }
     T* base = ctile + (cslot >> 4) * C::NB * C::kTile + (cslot & 15) * C::kStride + c8;
@@ -433,9 +434,10 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const v
   a.grid = Grid{s.hbits, s.wbits, s.raster};
   a.levels = s.levels;
   a.topk = s.topk;
-  a.enrich = s.enrich;
+  a.coarse_levels = s.coarse_levels;
+  a.lbias = s.coarse_lbias;
   a.c2 = s.scale * kLog2e;
-  const int n_coarse = s.enrich ? (s.levels - 1) * s.topk : 0;
+  const int n_coarse = s.coarse_levels * s.topk;
   const size_t lds = fwd_lds_bytes(s.bf16, n_coarse);
   // one workgroup per level-2 group (N is a multiple of 16^2), two when K > 16
   const bool wide = s.topk > kWavePicks / 4;

@@ -28,6 +28,8 @@ struct Shape {
   int levels;    // L
   int topk;      // K
   int enrich;    // 0/1
+  int coarse_levels;    // enrichment levels 2 .. 1 + coarse_levels (0: none)
+  float coarse_lbias;   // log2 of a level-1 coarse weight ratio: 4 (weight 16^l) or 0 (1)
   int raster;    // token tensors in raster order
   int bf16;      // 1: bf16 token tensors, 0: fp32
   float scale;   // softmax scale

@@ -24,7 +24,8 @@ __all__ = ["Problem", "make_problem", "llsa_forward", "llsa_backward", "llsa_bac
 
 
 def make_problem(q: torch.Tensor, height: int, width: int, levels: int, topk: int = 8,
-                 enrich: bool = True, scale: float = 0.0, layout: int = LLSA_LAYOUT_RASTER):
+                 enrich: bool = True, scale: float = 0.0, layout: int = LLSA_LAYOUT_RASTER,
+                 enrich_levels: int = 0, coarse_unit_weight: bool = False):
     b, h, n, d = q.shape
     if n != height * width:
         raise ValueError(f"token count {n} != height*width {height * width}")
@@ -32,7 +33,8 @@ def make_problem(q: torch.Tensor, height: int, width: int, levels: int, topk: in
     if dtype is None:
         raise ValueError(f"unsupported dtype {q.dtype}")
     return Problem(batch=b, heads=h, height=height, width=width, levels=levels, topk=topk,
-                   enrich=int(enrich), head_dim=d, scale=scale, dtype=dtype, layout=layout)
+                   enrich=int(enrich), head_dim=d, scale=scale, dtype=dtype, layout=layout,
+                   enrich_levels=enrich_levels, coarse_unit_weight=int(coarse_unit_weight))
 
 
 def reorder(p: Problem, x: torch.Tensor, inverse: bool = False) -> torch.Tensor:
@@ -63,7 +65,7 @@ def llsa_forward(p: Problem, q, k, v):
 
 def build_csc(p: Problem, sel):
     """Per level l: CSC of Sel_l (rows = queries, cols = keys, both n_l): (off, rows)."""
-    levels = p.levels if p.enrich else 1
+    levels = 1 + p.coarse_levels
     offs, rows = [], []
     nmat = p.batch * p.heads
     ws_bytes = max(llsa_index_transpose_workspace(nmat, p.n_level(l), p.n_level(l), p.topk)
@@ -122,7 +124,11 @@ class _LLSAFunction(torch.autograd.Function):
 
 
 def llsa_attention(q, k, v, height: int, width: int, levels: int, topk: int = 8,
-                   enrich: bool = True, scale: float = 0.0):
-    """Log-linear sparse attention over raster-ordered pixel tokens [b, H, height*width, 64]."""
-    p = make_problem(q, height, width, levels, topk, enrich, scale, LLSA_LAYOUT_RASTER)
+                   enrich: bool = True, scale: float = 0.0, enrich_levels: int = 0,
+                   coarse_unit_weight: bool = False):
+    """Log-linear sparse attention over raster-ordered pixel tokens [b, H, height*width, 64].
+    enrich_levels / coarse_unit_weight select the enrichment variants (0 / False: the method
+    as described)."""
+    p = make_problem(q, height, width, levels, topk, enrich, scale, LLSA_LAYOUT_RASTER,
+                     enrich_levels, coarse_unit_weight)
     return _LLSAFunction.apply(q, k, v, p)

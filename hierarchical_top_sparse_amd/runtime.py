@@ -38,7 +38,7 @@ class Step:
                                 dtype=torch.int32) for l in range(1, L + 1)]
         self.o = torch.empty_like(q)
         self.lse = torch.empty((p.batch, p.heads, p.n), device=dev, dtype=f32)
-        self.csc_levels = (L if p.enrich else 1) if self.backward else 0
+        self.csc_levels = 1 + p.coarse_levels if self.backward else 0
         self.off = [torch.empty((p.batch, p.heads, p.n_level(l) + 1), device=dev,
                                 dtype=torch.int32) for l in range(1, self.csc_levels + 1)]
         self.rows = [torch.empty((p.batch, p.heads, p.n_level(l) * p.topk), device=dev,

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define LLSA_ABI_VERSION 1
+#define LLSA_ABI_VERSION 2
 #define LLSA_MAX_LEVELS 6
 #define LLSA_MAX_TOPK 32
 
@@ -73,6 +73,11 @@ typedef struct {
   float scale;      /* softmax scale; 0 => 1/sqrt(head_dim) */
   int32_t dtype;    /* llsa_dtype of the token tensors */
   int32_t layout;   /* llsa_layout of the token tensors */
+  /* Enrichment variants (zero = the method as described): */
+  int32_t enrich_levels;      /* with enrich: only the coarse levels 2 .. 1 + enrich_levels
+                                 (the finest ones; clamped to L); 0 = all levels 2..L */
+  int32_t coarse_unit_weight; /* 0: a coarse key of level l has weight B^l (logit bias
+                                 l ln B); 1: weight 1 (no bias) */
 } llsa_problem;
 
 /* ABI version (LLSA_ABI_VERSION of the built library). */

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.llsa_abi_version() == 1
+    assert L.llsa_abi_version() == abi.LLSA_ABI_VERSION == 2
     for code in range(8):
         assert L.llsa_status_str(code)
     assert L.llsa_status_str(99) == b"unknown status"
@@ -59,6 +59,9 @@ def _p(**kw):
     (dict(topk=33), 2),                     # above the 32 supported
     (dict(levels=2, topk=9, height=32, width=64), 2),  # K > N / B^L = 8
     (dict(topk=0), 2),
+    (dict(enrich_levels=-1), 2),
+    (dict(coarse_unit_weight=2), 2),
+    (dict(enrich_levels=5, coarse_unit_weight=1), 0),   # clamped to the L - 1 coarse levels
     (dict(head_dim=128), 4),
     (dict(block=64), 4),                    # a power of 4 but not implemented
     (dict(block=8), 2),                     # not a square tile

@@ -259,6 +259,41 @@ def test_attn_bwd_on_oracle_indices(h, w, levels, topk, enrich, layout):
         assert_close(to64(got), ref_g, torch.bfloat16, name)
 
 
+
+@pytest.mark.parametrize("h,w,levels,topk,enrich_levels,unit_weight", [
+    (128, 256, 3, 8, 1, False),    # only level 2's coarse keys
+    (128, 256, 3, 8, 0, True),     # all coarse levels, weight 1
+    (512, 512, 4, 4, 2, True),     # levels 2..3 of 4, weight 1
+    (128, 128, 2, 8, 3, False),    # enrich_levels beyond L - 1 is clamped
+])
+def test_enrichment_variants_on_oracle_indices(h, w, levels, topk, enrich_levels, unit_weight):
+    """Forward and backward of the enrichment variants against the oracle's variants, on the
+    oracle's selection."""
+    d, ref = _inputs(1, 2, h, w, torch.bfloat16, 43, grad=True)
+    p = ops.make_problem(d["q"], h, w, levels, topk, True, 0.0, RASTER, enrich_levels,
+                         unit_weight)
+    sels = [_oracle_sel(ref, h, w, levels, topk, 0, i) for i in range(2)]
+    sel_t = [torch.from_numpy(np.stack([sels[i][l] for i in range(2)])[None].astype(np.int32))
+             .to(DEV) for l in range(levels)]
+    q, k, v, do = d["q"], d["k"], d["v"], d["do"]
+    kl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    vl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    _abi.llsa_pool(p, None, k, v, None, kl, vl)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, p.n), device=DEV)
+    _abi.llsa_attn_fwd(p, q, k, v, kl, vl, sel_t, o, lse)
+    dq, dk, dv = ops.llsa_backward(p, q, k, v, dict(o=o, lse=lse, k_lv=kl, v_lv=vl, sel=sel_t),
+                                   do)
+    kw = dict(enrich_levels=enrich_levels, coarse_weight=not unit_weight)
+    res = orc.llsa_forward(ref["q"], ref["k"], ref["v"], h, w, 16, levels, topk, True,
+                           sel_override=[sels], **kw)
+    assert_close(to64(o), res["o"], torch.bfloat16, "o")
+    assert_close(to64(lse), res["lse"], torch.bfloat16, "lse")
+    want = orc.llsa_backward(ref["q"], ref["k"], ref["v"], ref["do"], h, w, 16, levels, [sels],
+                             True, **kw)
+    for name, got, ref_g in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        assert_close(to64(got), ref_g, torch.bfloat16, name)
+
 # ----------------------------------------------------------------------------- whole path
 
 
