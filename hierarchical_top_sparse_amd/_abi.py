@@ -55,6 +55,16 @@ class Problem:
     coarse_unit_weight: int = 0   # 1: coarse keys weighted 1 instead of B^l
 
     @property
+    def fine_k(self) -> int:
+        """Picks per 16-token query block as the attention reads them: topk * block / 16."""
+        return self.topk * self.block // 16
+
+    def csc_dims(self, l: int):
+        """(rows = cols, k) of the level-l selection the backward transposes: level 1 in
+        16-token blocks, levels >= 2 as selected."""
+        return (self.n // 16, self.fine_k) if l == 1 else (self.n_level(l), self.topk)
+
+    @property
     def coarse_levels(self) -> int:
         """Coarse levels whose keys enrich the attention."""
         if not self.enrich or self.levels < 2:
@@ -114,6 +124,7 @@ def lib() -> ctypes.CDLL:
             "llsa_dense_attn_bwd": ([i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, vp], i32),
             "llsa_block_mask": ([P, vp, vp, vp], i32),
+            "llsa_expand_blocks": ([P, vp, vp, vp], i32),
             "llsa_attn_bwd_masked": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
                                      i32),
             "llsa_profile_enable": ([i32], i32),
@@ -131,7 +142,7 @@ def exported_symbols() -> list:
     return ["llsa_abi_version", "llsa_status_str", "llsa_last_error", "llsa_check",
             "llsa_workspace_bytes", "llsa_reorder", "llsa_pool", "llsa_select", "llsa_attn_fwd",
             "llsa_index_transpose_workspace", "llsa_index_transpose", "llsa_attn_bwd",
-            "llsa_dense_attn_fwd", "llsa_dense_attn_bwd", "llsa_block_mask",
+            "llsa_dense_attn_fwd", "llsa_dense_attn_bwd", "llsa_block_mask", "llsa_expand_blocks",
             "llsa_attn_bwd_masked", "llsa_profile_enable", "llsa_profile_read"]
 
 
@@ -175,6 +186,10 @@ def _tok_shape(p: Problem):
 
 def _lv_shape(p: Problem, l: int):
     return (p.batch, p.heads, p.n_level(l), p.head_dim)
+
+
+def _fine_sel_shape(p: Problem):
+    return (p.batch, p.heads, p.n // 16, p.fine_k)
 
 
 def _sel_shape(p: Problem, l: int):
@@ -246,7 +261,7 @@ def llsa_attn_fwd(p: Problem, q, k, v, k_lv, v_lv, sel, o, lse, stream=None):
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         _expect(t, _tok_shape(p), p.torch_dtype, name)
     _expect(lse, (p.batch, p.heads, p.n), torch.float32, "lse")
-    _expect(sel[0], _sel_shape(p, 1), torch.int32, "sel[0]")
+    _expect(sel[0], _fine_sel_shape(p), torch.int32, "sel[0]")
     if p.coarse_levels:
         for l in range(2, 2 + p.coarse_levels):
             _expect(k_lv[l - 1], _lv_shape(p, l), torch.float32, f"k_lv[{l - 1}]")
@@ -255,6 +270,14 @@ def llsa_attn_fwd(p: Problem, q, k, v, k_lv, v_lv, sel, o, lse, stream=None):
     _raise(lib().llsa_attn_fwd(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptrs(k_lv),
                                _ptrs(v_lv), _ptrs(sel), _ptr(o), _ptr(lse), _stream(stream)),
            "llsa_attn_fwd")
+
+
+def llsa_expand_blocks(p: Problem, sel1, fine, stream=None):
+    """Level-1 picks of B-token blocks as the 16-token blocks they cover (a copy for B = 16)."""
+    _expect(sel1, _sel_shape(p, 1), torch.int32, "sel1")
+    _expect(fine, _fine_sel_shape(p), torch.int32, "fine")
+    _raise(lib().llsa_expand_blocks(ctypes.byref(p.c()), _ptr(sel1), _ptr(fine), _stream(stream)),
+           "llsa_expand_blocks")
 
 
 def llsa_index_transpose_workspace(nmat: int, rows: int, cols: int, k: int) -> int:
@@ -284,10 +307,11 @@ def llsa_attn_bwd(p: Problem, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_
     _expect(lse, (p.batch, p.heads, p.n), torch.float32, "lse")
     levels = 1 + p.coarse_levels
     for l in range(1, levels + 1):
-        _expect(sel[l - 1], _sel_shape(p, l), torch.int32, f"sel[{l - 1}]")
-        _expect(csc_off[l - 1], (p.batch, p.heads, p.n_level(l) + 1), torch.int32,
-                f"csc_off[{l - 1}]")
-        _expect(csc_rows[l - 1], (p.batch, p.heads, p.n_level(l) * p.topk), torch.int32,
+        rows, kk = p.csc_dims(l)
+        _expect(sel[l - 1], _fine_sel_shape(p) if l == 1 else _sel_shape(p, l), torch.int32,
+                f"sel[{l - 1}]")
+        _expect(csc_off[l - 1], (p.batch, p.heads, rows + 1), torch.int32, f"csc_off[{l - 1}]")
+        _expect(csc_rows[l - 1], (p.batch, p.heads, rows * kk), torch.int32,
                 f"csc_rows[{l - 1}]")
         if l >= 2:
             _expect(k_lv[l - 1], _lv_shape(p, l), torch.float32, f"k_lv[{l - 1}]")

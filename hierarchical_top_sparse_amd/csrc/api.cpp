@@ -53,23 +53,29 @@ int32_t check_problem(const llsa_problem* p) {
                 p->height, p->width);
   if (p->head_dim != 64)
     return fail(LLSA_ERR_UNSUPPORTED, "head_dim %d: only 64 is implemented", p->head_dim);
-  if (p->block != 16)
+  if (p->block != 16 && p->block != 64)
     return fail(p->block > 1 && is_pow2(p->block) && (log2i(p->block) % 2 == 0)
                     ? LLSA_ERR_UNSUPPORTED
                     : LLSA_ERR_SHAPE,
-                "block %d: only 16 (4x4 tiles) is implemented", p->block);
+                "block %d: 16 (4x4 tiles) and 64 (8x8 tiles) are implemented", p->block);
   if (p->levels < 1 || p->levels > LLSA_MAX_LEVELS)
     return fail(LLSA_ERR_SHAPE, "levels %d out of [1, %d]", p->levels, LLSA_MAX_LEVELS);
   const long n = (long)p->height * p->width;
   if (n < 256) return fail(LLSA_ERR_SHAPE, "N = %ld tokens: at least 256 needed", n);
   if (n > (1L << 23)) return fail(LLSA_ERR_SHAPE, "N = %ld tokens: at most 2^23 supported", n);
-  const long span = 1L << (4 * p->levels);
+  const long span = 1L << (log2i(p->block) * p->levels);
+  if (log2i(p->block) * p->levels > 23)
+    return fail(LLSA_ERR_SHAPE, "block^levels exceeds 2^23 tokens");
   if (n % span != 0)
     return fail(LLSA_ERR_SHAPE, "N = %ld is not divisible by block^levels = %ld", n, span);
   const long n_top = n / span;
   if (p->topk < 1 || p->topk > LLSA_MAX_TOPK || p->topk > n_top)
     return fail(LLSA_ERR_SHAPE, "topk %d out of [1, min(%d, N/B^L = %ld)]", p->topk,
                 LLSA_MAX_TOPK, n_top);
+  if (p->topk * (p->block / 16) > LLSA_MAX_TOPK)
+    return fail(LLSA_ERR_UNSUPPORTED, "topk %d with block %d covers %d 16-token blocks per "
+                "query block: at most %d are supported", p->topk, p->block,
+                p->topk * (p->block / 16), LLSA_MAX_TOPK);
   if (p->enrich != 0 && p->enrich != 1)
     return fail(LLSA_ERR_SHAPE, "enrich must be 0 or 1 (got %d)", p->enrich);
   if (p->enrich_levels < 0)
@@ -100,10 +106,12 @@ llsa::Shape make_shape(const llsa_problem* p) {
   s.topk = p->topk;
   s.enrich = p->enrich;
   s.coarse_levels = coarse_levels(p);
-  s.coarse_lbias = p->coarse_unit_weight ? 0.f : 4.f;   // log2(16): weight 16^l
+  s.coarse_lbias = p->coarse_unit_weight ? 0.f : (float)log2i(p->block);   // weight B^l
   s.raster = p->layout == LLSA_LAYOUT_RASTER;
   s.bf16 = p->dtype == LLSA_BF16;
   s.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim);
+  s.bshift = log2i(p->block);
+  s.fine_k = p->topk * (p->block / 16);
   return s;
 }
 
@@ -176,8 +184,9 @@ int32_t llsa_pool(const llsa_problem* p, const void* q, const void* k, const voi
     if (!lv[t]) return fail(LLSA_ERR_NULL, "level array of %s is NULL", names[t]);
     for (int l = 1; l <= p->levels; ++l) {
       float* ptr = lv[t][l - 1];
-      // levels 2..L-1 feed the next level and must be stored when L >= 3
-      if (!ptr && l >= 2 && l < p->levels)
+      // levels below L feed the next level and must be stored: 2..L-1 for block 16 (its
+      // levels 1 and 2 come from the tokens), 1..L-1 for block 64
+      if (!ptr && l < p->levels && (l >= 2 || p->block != 16))
         return fail(LLSA_ERR_NULL, "%s level %d is needed for level %d", names[t], l, l + 1);
       if (ptr && !aligned16(ptr))
         return fail(LLSA_ERR_ALIGN, "%s level %d is not 16-byte aligned", names[t], l);
@@ -203,6 +212,18 @@ int32_t llsa_select(const llsa_problem* p, const float* const* q_lv, const float
   return hip_status(llsa::launch_select(make_shape(p), q_lv, k_lv, sel, level_hi, level_lo,
                                         (hipStream_t)stream),
                     "llsa_select");
+}
+
+int32_t llsa_expand_blocks(const llsa_problem* p, const int32_t* sel1, int32_t* fine,
+                           void* stream) {
+  int32_t st = check_problem(p);
+  if (st != LLSA_OK) return st;
+  CHECK_PTR(sel1, "sel1");
+  CHECK_PTR(fine, "fine");
+  if ((const void*)sel1 == (const void*)fine)
+    return fail(LLSA_ERR_SHAPE, "llsa_expand_blocks cannot run in place");
+  return hip_status(llsa::launch_expand_blocks(make_shape(p), sel1, fine, (hipStream_t)stream),
+                    "llsa_expand_blocks");
 }
 
 int32_t llsa_attn_fwd(const llsa_problem* p, const void* q, const void* k, const void* v,
@@ -318,6 +339,8 @@ int32_t check_masked(const llsa_problem* p) {
   if (coarse_levels(p) > 0)
     return fail(LLSA_ERR_UNSUPPORTED, "the mask-based backward has no coarse keys: levels must "
                 "be 1 or enrich 0");
+  if (p->block != 16)
+    return fail(LLSA_ERR_UNSUPPORTED, "the mask-based backward is implemented for block 16");
   const long n1 = (long)p->height * p->width / 16;
   if ((long)p->batch * p->heads * n1 * n1 > (1L << 34))
     return fail(LLSA_ERR_SHAPE, "block mask of %ld bytes exceeds 2^34",

@@ -52,7 +52,9 @@ struct BwdArgs {
   int n;
   Grid grid;
   int levels;
-  int topk;
+  int topk;            // K: coarse keys per level
+  int fine_k;          // picks per 16-token query block (rows of sel[0], CSC_1): K B / 16
+  int bshift;          // log2(B) of the coarse levels: 4 or 6
   int enrich;          // 1 if there are coarse keys (coarse_levels > 0)
   int coarse_levels;   // coarse keys of levels 2 .. 1 + coarse_levels
   float lbias;         // log2-domain bias per level: 4 (weight 16^l) or 0 (weight 1)
@@ -171,6 +173,7 @@ void bwd_query_kernel(BwdArgs a) {
   const int a2 = rem / kUnits;
   const int pb_first = a2 * kBlock + (rem % kUnits) * (kBlock / kUnits) + kQBlocks * w;
   const int K = a.topk;
+  const int KF = a.fine_k;
   const long tok_base = (long)head * a.n;
   const int n_coarse = NCT > 0 ? a.coarse_levels * K : 0;
 
@@ -196,9 +199,9 @@ void bwd_query_kernel(BwdArgs a) {
 
   // ---- the wave's picks (lane 32b + i: pick i of block b) and its query-side operands
   int key = kPickSentinel | lane;
-  if ((lane % kQPickSlots) < K) {
+  if ((lane % kQPickSlots) < KF) {
     const int j =
-        a.sel[0][((long)head * n1 + pb_first + lane / kQPickSlots) * K + lane % kQPickSlots];
+        a.sel[0][((long)head * n1 + pb_first + lane / kQPickSlots) * KF + lane % kQPickSlots];
     if (j >= 0 && j < n1) key = (j << 8) | lane;
   }
   bf16x8 qh[kQBlocks][2], dh[kQBlocks][2];   // B operands: lane (n, g) row n, ch 32s + 8g..
@@ -225,8 +228,8 @@ void bwd_query_kernel(BwdArgs a) {
       float bias = -INFINITY;
       if (cslot < n_coarse) {
         const int l = 2 + cslot / K;
-        const int nl = a.n >> (kBlockShift * l);
-        const int anc = (a2 * kBlock) >> (kBlockShift * (l - 1));
+        const int nl = a.n >> (a.bshift * l);
+        const int anc = (a2 << (2 * kBlockShift)) >> (a.bshift * l);   // level-l ancestor
         const int id = a.sel[l - 1][((long)head * nl + anc) * K + (cslot - (l - 2) * K)];
         if (id >= 0 && id < nl) {
           const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
@@ -514,10 +517,11 @@ __device__ __forceinline__ void coarse_key_sum(const BwdArgs& a, int l, int head
                                                int part, int nparts, int lane, float& sk,
                                                float& sv) {
   const int K = a.topk;
-  const int nl = a.n >> (kBlockShift * l);
-  const int n2 = a.n >> (2 * kBlockShift);
+  const int nl = a.n >> (a.bshift * l);
+  const int n2 = a.n >> (2 * kBlockShift);   // 256-token groups (the partials' layout)
   const int n_coarse = a.coarse_levels * K;
-  const int span = kUnits << (kBlockShift * (l - 2));   // partial units under one ancestor
+  // partial units (of 256 / kUnits tokens) under one level-l ancestor
+  const int span = 1 << (a.bshift * l - 2 * kBlockShift + 1);
   const uint32_t row_bytes = (uint32_t)n_coarse * kDim * 4;   // one unit's partial rows
   const uint32_t head_bytes = (uint32_t)n2 * kUnits * row_bytes;
   const long head_floats = (long)n2 * kUnits * n_coarse * kDim;
@@ -584,7 +588,7 @@ __global__ __launch_bounds__(64 * kCgWaves) void coarse_grad_kernel(BwdArgs a,
   const int w = uniform(threadIdx.x >> 6);
   const int bid = blockIdx.x;
   if (bid < cg.first_block[2]) {   // level 2: one wave per key
-    const int n2 = a.n >> (2 * kBlockShift);
+    const int n2 = a.n >> (2 * a.bshift);
     const int f = bid * kCgWaves + w;
     if (f >= a.bh * n2) return;
     const int head = uniform(f / n2);
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(64 * kCgWaves) void coarse_grad_kernel(BwdArgs a,
   }
   int l = 3;
   while (l < a.levels && bid >= cg.first_block[l]) ++l;
-  const int nl = a.n >> (kBlockShift * l);
+  const int nl = a.n >> (a.bshift * l);
   const int idx = bid - cg.first_block[l - 1];
   const int head = uniform(idx / nl);
   const int j = uniform(idx - head * nl);
@@ -647,9 +651,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
   float pk_sum = 0.f, pv_sum = 0.f;
   if (a.enrich) {
     for (int l = 2; l <= 1 + a.coarse_levels; ++l) {
-      const int nl = a.n >> (kBlockShift * l);
-      const int anc = j >> (kBlockShift * (l - 1));
-      const float f = 1.0f / (float)(1 << (kBlockShift * l));
+      const int nl = a.n >> (a.bshift * l);
+      const int anc = (j << kBlockShift) >> (a.bshift * l);
+      const float f = 1.0f / (float)(1 << (a.bshift * l));
       pk_sum += a.dk_lv[l - 1][((long)head * nl + anc) * kDim + lane] * f;
       pv_sum += a.dv_lv[l - 1][((long)head * nl + anc) * kDim + lane] * f;
     }
@@ -787,7 +791,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
   };
   if constexpr (!MASK) {
     const int32_t* off = a.csc_off[0] + (long)head * (n1 + 1);
-    const int32_t* rows = a.csc_rows[0] + (long)head * n1 * a.topk;
+    const int32_t* rows = a.csc_rows[0] + (long)head * n1 * a.fine_k;
     const int e0 = uniform(off[j]);
     const int e1 = uniform(off[j + 1]);
     for (int base = e0; base < e1; base += 64) {
@@ -857,7 +861,7 @@ static BwdLayout bwd_layout(const Shape& s) {
   };
   L.dd = take(sizeof(float) * (size_t)s.bh * s.n);
   if (s.coarse_levels > 0) {
-    const size_t n2 = (size_t)s.n_level(2);
+    const size_t n2 = (size_t)s.n >> (2 * kBlockShift);   // 256-token groups
     const size_t nc = (size_t)s.coarse_levels * s.topk;
     L.part_k = take(sizeof(float) * s.bh * n2 * kUnits * nc * kDim);
     L.part_v = take(sizeof(float) * s.bh * n2 * kUnits * nc * kDim);
@@ -913,6 +917,8 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   a.grid = Grid{s.hbits, s.wbits, s.raster};
   a.levels = s.levels;
   a.topk = s.topk;
+  a.fine_k = s.fine_k;
+  a.bshift = s.bshift;
   a.enrich = coarse ? 1 : 0;
   a.coarse_levels = s.coarse_levels;
   a.lbias = s.coarse_lbias;

@@ -44,9 +44,11 @@ struct FwdArgs {
   int n;
   Grid grid;
   int levels;
-  int topk;
+  int topk;            // K: coarse keys per level
+  int fine_k;          // picks per 16-token query block (rows of sel[0]): K B / 16
+  int bshift;          // log2(B) of the coarse levels: 4 or 6
   int coarse_levels;   // coarse keys of levels 2 .. 1 + coarse_levels
-  float lbias;         // log2-domain bias per level: 4 (weight 16^l) or 0 (weight 1)
+  float lbias;         // log2-domain bias per level: log2(B) (weight B^l) or 0 (weight 1)
   float c2;            // scale * log2(e)
 };
 
@@ -110,6 +112,7 @@ void attn_fwd_kernel(FwdArgs a) {
   const int rem = uniform(wg - head * kUnitsPerGroup * n2);   // be wave-uniform
   const int a2 = rem / kUnitsPerGroup;
   const int K = a.topk;
+  const int KF = a.fine_k;
   const long tok_base = (long)head * a.n;
   const int n_coarse = a.coarse_levels * K;
   const int ctiles = (n_coarse + 15) >> 4;
@@ -133,8 +136,8 @@ void attn_fwd_kernel(FwdArgs a) {
 
   // ---- the wave's picks (lane PS b + i: pick i of block b) and its query operands
   int key = kSentinel | lane;   // sentinels sort after every pick and stay distinct
-  if ((lane % PS) < K) {
-    const int j = a.sel[0][((long)head * n1 + pb_first + lane / PS) * K + (lane % PS)];
+  if ((lane % PS) < KF) {
+    const int j = a.sel[0][((long)head * n1 + pb_first + lane / PS) * KF + (lane % PS)];
     if (j >= 0 && j < n1) key = (j << 8) | lane;
   }
   // B operand of S^T for block bb: lane (n, g) holds query row n, channels 32s + 8g .. +7
@@ -163,8 +166,8 @@ void attn_fwd_kernel(FwdArgs a) {
     float bias = -INFINITY;
     if (cslot < n_coarse) {
       const int l = 2 + cslot / K;
-      const int nl = a.n >> (kBlockShift * l);
-      const int anc = pb0 >> (kBlockShift * (l - 1));
+      const int nl = a.n >> (a.bshift * l);
+      const int anc = (pb0 << kBlockShift) >> (a.bshift * l);   // the group's level-l ancestor
       const int id = a.sel[l - 1][((long)head * nl + anc) * K + (cslot - (l - 2) * K)];
       if (id >= 0 && id < nl) {
         const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
@@ -173,7 +176,7 @@ void attn_fwd_kernel(FwdArgs a) {
         k1 = *(const f32x4*)(kp + 4);
         v0 = *(const f32x4*)vp;
         v1 = *(const f32x4*)(vp + 4);
-        bias = a.lbias * (float)l;   // log2(16^l), or 0 for unit weights
+        bias = a.lbias * (float)l;   // log2(B^l), or 0 for unit weights
       }
     }
     T* base = ctile + (cslot >> 4) * C::NB * C::kTile + (cslot & 15) * C::kStride + c8;
@@ -434,13 +437,15 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const v
   a.grid = Grid{s.hbits, s.wbits, s.raster};
   a.levels = s.levels;
   a.topk = s.topk;
+  a.fine_k = s.fine_k;
+  a.bshift = s.bshift;
   a.coarse_levels = s.coarse_levels;
   a.lbias = s.coarse_lbias;
   a.c2 = s.scale * kLog2e;
   const int n_coarse = s.coarse_levels * s.topk;
   const size_t lds = fwd_lds_bytes(s.bf16, n_coarse);
   // one workgroup per level-2 group (N is a multiple of 16^2), two when K > 16
-  const bool wide = s.topk > kWavePicks / 4;
+  const bool wide = s.fine_k > kWavePicks / 4;
   const unsigned blocks = (unsigned)((long)s.bh * (s.n >> (2 * kBlockShift)) * (wide ? 2 : 1));
   const void* fn = s.bf16 ? (wide ? (const void*)attn_fwd_kernel<true, 2>
                                   : (const void*)attn_fwd_kernel<true, 4>)

@@ -33,7 +33,9 @@ struct Shape {
   int raster;    // token tensors in raster order
   int bf16;      // 1: bf16 token tensors, 0: fp32
   float scale;   // softmax scale
-  int n_level(int l) const { return n >> (4 * l); }   // B = 16
+  int bshift;    // log2(B): 4 (B = 16, 4x4 tiles) or 6 (B = 64, 8x8 tiles)
+  int fine_k;    // picks per 16-token query block seen by the attention: K * B / 16
+  int n_level(int l) const { return n >> (bshift * l); }
 };
 
 hipError_t launch_reorder(const Shape& s, const void* x, void* y, int inverse,
@@ -61,6 +63,10 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
                            const int32_t* const* sel, const int32_t* const* csc_off,
                            const int32_t* const* csc_rows, const uint8_t* mask, void* dq,
                            void* dk, void* dv, void* ws, hipStream_t stream);
+
+// Level-1 picks as 16-token blocks: [bh, N/16, K B/16] from [bh, N/B, K].
+hipError_t launch_expand_blocks(const Shape& s, const int32_t* sel1, int32_t* fine,
+                                hipStream_t stream);
 
 // Dense block mask [bh, n_1, n_1] (1 where key block c is in Sel_1[a]) of the mask-based
 // comparator.

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kMaskThreads) void mask_set_kernel(const int32_t* _
 
 hipError_t launch_block_mask(const Shape& s, const int32_t* sel1, uint8_t* mask,
                              hipStream_t stream) {
-  const long n1 = s.n_level(1);
+  const long n1 = s.n >> 4;   // 16-token blocks
   const long chunks = (long)s.bh * n1 * n1 / 16;   // n1 is a multiple of 16
   const long per_block = (long)kMaskThreads * kMaskChunks;
   LLSA_LAUNCH("mask_clear_kernel", mask_clear_kernel,

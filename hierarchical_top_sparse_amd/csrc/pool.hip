@@ -5,7 +5,9 @@
 //   tokens).  Reads the B^2 token rows once, every thread's loads in flight together
 //   (coalesced 128/256-byte rows; raster layout reads 4x4 tiles as 4 row segments), writes
 //   level 1 and reduces level 2 through LDS.  HBM-bound.
-// pool_next_kernel: level l >= 3 from level l-1 (fp32, tiny).
+//   With B = 64 (8x8 tiles) the kernel writes the 64-token means instead, each the mean of four
+//   consecutive 16-token means staged in LDS, and no second level.
+// pool_next_kernel: level l from level l-1 (fp32, tiny): l >= 3 for B = 16, l >= 2 for B = 64.
 // All sums are fp32 in a fixed order; the 1/B factor is exact.  pool12_kernel is the profiling
 // name of both level-1/2 kernels.
 #include "common.hpp"
@@ -15,9 +17,20 @@ namespace llsa {
 
 struct PoolArgs {
   const void* x[3];
-  float* lv1[3];
-  float* lv2[3];
+  float* lv1[3];    // 16-token means (B = 16 level 1)
+  float* lv2[3];    // 256-token means (B = 16 level 2)
+  float* lv64[3];   // 64-token means (B = 64 level 1)
 };
+
+// B = 64 level 1 of one 256-token group from its 16 staged 16-token means: thread t writes
+// channel t % 64 of 64-token block t / 64 (a workgroup barrier first).
+__device__ __forceinline__ void pool64_from_lds(const float (&sh)[kBlock][kDim], float* out,
+                                                int head, int n, int group, int t) {
+  __syncthreads();
+  const int r = t >> 6, c = t & 63;
+  const float s = (sh[4 * r][c] + sh[4 * r + 1][c]) + (sh[4 * r + 2][c] + sh[4 * r + 3][c]);
+  out[((long)head * (n >> 6) + group * 4 + r) * kDim + c] = s * 0.25f;
+}
 
 // bf16 tokens: thread t owns level-1 block t / 16 of the group, half (t / 8) % 2 of its 16
 // tokens and the 16-byte channel piece t % 8; its 8 row loads are issued at once (each wave
@@ -61,6 +74,7 @@ __global__ __launch_bounds__(256) void pool12_bf16_kernel(PoolArgs args, int n, 
     *(f32x4*)&sh[blk][8 * cp] = l1a;
     *(f32x4*)&sh[blk][8 * cp + 4] = l1b;
   }
+  if (args.lv64[tensor]) pool64_from_lds(sh, args.lv64[tensor], head, n, group, t);
   if (args.lv2[tensor]) {
     __syncthreads();
     if (t < kDim) {
@@ -101,6 +115,11 @@ __global__ __launch_bounds__(256) void pool12_f32_kernel(PoolArgs args, int n, G
     float* out = args.lv1[tensor] + ((long)head * n1 + group * kBlock + blk) * kDim + dq;
     *(f32x4*)out = l1;
   }
+  if (args.lv64[tensor]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sh[blk][dq + c] = l1[c];
+    pool64_from_lds(sh, args.lv64[tensor], head, n, group, t);
+  }
   if (args.lv2[tensor]) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) sh[blk][dq + c] = l1[c];
@@ -120,18 +139,19 @@ struct PoolNextArgs {
   float* out[3];
 };
 
-// out[j][d] = mean_t in[j*B + t][d]; one thread per output element.
+// out[j][d] = mean_t in[j*B + t][d] (B = 16 or 64); one thread per output element.
+template <int B>
 __global__ __launch_bounds__(256) void pool_next_kernel(PoolNextArgs args, long total_out) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
   const int tensor = blockIdx.y;
   if (i >= total_out) return;
   const long j = i / kDim;
   const int d = (int)(i - j * kDim);
-  const float* src = args.in[tensor] + (j * kBlock) * kDim + d;
+  const float* src = args.in[tensor] + (j * B) * kDim + d;
   float s = 0.f;
 #pragma unroll
-  for (int t = 0; t < kBlock; ++t) s += src[t * kDim];
-  args.out[tensor][i] = s * (1.0f / kBlock);
+  for (int t = 0; t < B; ++t) s += src[t * kDim];
+  args.out[tensor][i] = s * (1.0f / B);
 }
 
 hipError_t launch_pool(const Shape& s, const void* const x[3], float* const* lv[3],
@@ -141,8 +161,12 @@ hipError_t launch_pool(const Shape& s, const void* const x[3], float* const* lv[
   for (int t = 0; t < 3; ++t) {
     if (!x[t]) continue;
     a.x[nt] = x[t];
-    a.lv1[nt] = lv[t][0];
-    a.lv2[nt] = s.levels >= 2 ? lv[t][1] : nullptr;
+    if (s.bshift == 4) {
+      a.lv1[nt] = lv[t][0];
+      a.lv2[nt] = s.levels >= 2 ? lv[t][1] : nullptr;
+    } else {
+      a.lv64[nt] = lv[t][0];
+    }
     ++nt;
   }
   if (nt == 0) return hipSuccess;
@@ -157,19 +181,23 @@ hipError_t launch_pool(const Shape& s, const void* const x[3], float* const* lv[
                 groups_per_head);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  for (int l = 3; l <= s.levels; ++l) {
+  for (int l = s.bshift == 4 ? 3 : 2; l <= s.levels; ++l) {
     PoolNextArgs b{};
     int m = 0;
     for (int t = 0; t < 3; ++t) {
       if (!x[t] || !lv[t][l - 1]) continue;
+      if (!lv[t][l - 2]) return hipErrorInvalidValue;   // the level below was not stored
       b.in[m] = lv[t][l - 2];
       b.out[m] = lv[t][l - 1];
       ++m;
     }
     if (m == 0) continue;
     const long total = (long)s.bh * s.n_level(l) * kDim;
-    LLSA_LAUNCH("pool_next_kernel", pool_next_kernel, dim3((unsigned)((total + 255) / 256), (unsigned)m),
-                       dim3(256), 0, stream, b, total);
+    const dim3 grid((unsigned)((total + 255) / 256), (unsigned)m);
+    if (s.bshift == 4)
+      LLSA_LAUNCH("pool_next_kernel", pool_next_kernel<16>, grid, dim3(256), 0, stream, b, total);
+    else
+      LLSA_LAUNCH("pool_next_kernel", pool_next_kernel<64>, grid, dim3(256), 0, stream, b, total);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

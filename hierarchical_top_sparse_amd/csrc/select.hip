@@ -43,6 +43,7 @@ struct SelArgs {
   int levels;   // L
   int topk;     // K
   int hi, lo;   // levels computed: hi down to lo
+  int bshift;   // log2(B): 4 or 6; a pick's B children are B / 16 tiles of 16 candidates
 };
 
 __device__ __forceinline__ bool better(float s1, int i1, float s2, int i2) {
@@ -136,12 +137,14 @@ __device__ __forceinline__ void merge_lists(float (&ls)[KMAX], int (&li)[KMAX], 
 // ascending, as pick[0..K) (kNoId beyond K): per query n in the lanes of column n (SINGLE:
 // the one query, in every lane).
 //   all_keys: candidates are all n_rows keys of the level;
-//   else:     candidates are the 16 children of each pick in pickv (lane i holds pick i of
-//             the parent, i < K; ids outside [0, n_rows / 16) are skipped).
+//   else:     candidates are the B = 2^bshift children of each pick in pickv (lane i holds
+//             pick i of the parent, i < K; ids outside [0, n_rows / B) are skipped), B / 16
+//             tiles per pick.
 template <int KMAX, bool SINGLE>
 __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool all_keys,
-                                             int pickv, int K, const f32x4 (&qv)[4], int n,
-                                             int g, int (&pick)[KMAX]) {
+                                             int pickv, int K, int bshift,
+                                             const f32x4 (&qv)[4], int n, int g,
+                                             int (&pick)[KMAX]) {
   float ls[KMAX];
   int li[KMAX];
 #pragma unroll
@@ -149,8 +152,9 @@ __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool a
     ls[j] = -INFINITY;
     li[j] = kNoId;
   }
-  const int n_parent = n_rows >> kBlockShift;
-  const int tiles = all_keys ? (n_rows + 15) >> 4 : K;
+  const int n_parent = n_rows >> bshift;
+  const int sub_shift = bshift - 4;   // log2 of the tiles per pick
+  const int tiles = all_keys ? (n_rows + 15) >> 4 : K << sub_shift;
   for (int t0 = 0; t0 < tiles; t0 += kTilesPerRound) {
     f32x4 kv[kTilesPerRound][4];
     int first[kTilesPerRound];
@@ -162,8 +166,9 @@ __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool a
         if (all_keys) {
           first[i] = 16 * t;
         } else {
-          const int pk = __builtin_amdgcn_readlane(pickv, t);
-          first[i] = (pk >= 0 && pk < n_parent) ? pk * 16 : -1;
+          const int pk = __builtin_amdgcn_readlane(pickv, t >> sub_shift);
+          const int sub = t & ((1 << sub_shift) - 1);
+          first[i] = (pk >= 0 && pk < n_parent) ? (pk << bshift) + 16 * sub : -1;
         }
       }
       load_tile(kh, first[i], n_rows, n, g, kv[i]);
@@ -200,7 +205,8 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelArgs a) {
   const int g = lane >> 4;
   const int K = a.topk;
   const int lo = a.lo;
-  const int n_lo = a.n >> (kBlockShift * lo);
+  const int bs = a.bshift;
+  const int n_lo = a.n >> (bs * lo);
   const int groups = (n_lo + 15) >> 4;
   const int wave =
       uniform(xcd_block((int)blockIdx.x, (int)gridDim.x) * kSelWaves + (int)(threadIdx.x >> 6));
@@ -211,19 +217,21 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelArgs a) {
   // picks of the parent of the level being ranked, one per lane
   int pickv = kNoId;
   if (lo < a.levels) {
-    // the group's parent is query grp at level lo + 1
+    // the group's parent is query (16 grp) >> bs at level lo + 1
     if (a.hi == lo) {   // parent picks given: sel at level lo + 1
-      if (lane < K) pickv = a.sel[lo][((long)head * (n_lo >> 4) + grp) * K + lane];
+      if (lane < K)
+        pickv = a.sel[lo][((long)head * (n_lo >> bs) + ((grp << 4) >> bs)) * K + lane];
     } else {
       // chain: ancestors at levels hi .. lo + 1, each a single query
       for (int lv = a.hi; lv > lo; --lv) {
-        const int shift = kBlockShift * (lv - lo - 1);
-        const int anc = grp >> shift;                 // query id at level lv
-        const int n_lv = a.n >> (kBlockShift * lv);
+        const int shift = bs * (lv - lo);
+        const int anc = (grp << 4) >> shift;          // query id at level lv
+        const int n_lv = a.n >> (bs * lv);
         const bool top = lv == a.levels;
         if (lv == a.hi && !top) {
           // parent picks of the topmost computed ancestor are given at level hi + 1
-          if (lane < K) pickv = a.sel[lv][((long)head * (n_lv >> 4) + (anc >> 4)) * K + lane];
+          if (lane < K)
+            pickv = a.sel[lv][((long)head * (n_lv >> bs) + (anc >> bs)) * K + lane];
         }
         const float* qrow = a.q[lv - 1] + ((long)head * n_lv + anc) * kDim + 16 * g;
         f32x4 qv[4];
@@ -231,13 +239,13 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelArgs a) {
         for (int c = 0; c < 4; ++c) qv[c] = *(const f32x4*)(qrow + 4 * c);
         int pick[KMAX];
         rank_queries<KMAX, true>(a.k[lv - 1] + (long)head * n_lv * kDim, n_lv, top, pickv, K,
-                                 qv, n, g, pick);
+                                 bs, qv, n, g, pick);
         int nv = kNoId;
 #pragma unroll
         for (int r = 0; r < KMAX; ++r)
           if (lane == r) nv = pick[r];
         pickv = nv;
-        if ((grp & ((1 << shift) - 1)) == 0 && lane < K)
+        if (((grp << 4) & ((1 << shift) - 1)) == 0 && lane < K)
           a.sel[lv - 1][((long)head * n_lv + anc) * K + lane] = pickv;
       }
     }
@@ -254,13 +262,36 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelArgs a) {
                    : f32x4{0.f, 0.f, 0.f, 0.f};
   int pick[KMAX];
   rank_queries<KMAX, false>(a.k[lo - 1] + (long)head * n_lo * kDim, n_lo, lo == a.levels, pickv,
-                            K, qv, n, g, pick);
+                            K, bs, qv, n, g, pick);
   if (g == 0 && qvalid) {
     int32_t* dst = a.sel[lo - 1] + ((long)head * n_lo + q_id) * K;
 #pragma unroll
     for (int r = 0; r < KMAX; ++r)
       if (r < K) dst[r] = pick[r];
   }
+}
+
+// Level-1 picks of 64-token blocks as the 16-token blocks they cover: row q of the output (a
+// 16-token query block) lists, for each pick j of its 64-token block q / 4, the blocks
+// 4j .. 4j + 3 (ascending, as the picks are).  With B = 16 a copy.  One thread per output.
+__global__ __launch_bounds__(256) void expand_kernel(const int32_t* __restrict__ sel,
+                                                     int32_t* __restrict__ fine, int sub_shift,
+                                                     int k, long total) {
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int kf = k << sub_shift;
+  const long q16 = t / kf;            // (bh, 16-token query block)
+  const int e = (int)(t - q16 * kf);
+  const int j = sel[(q16 >> sub_shift) * k + (e >> sub_shift)];
+  fine[t] = j < 0 ? -1 : (j << sub_shift) + (e & ((1 << sub_shift) - 1));
+}
+
+hipError_t launch_expand_blocks(const Shape& s, const int32_t* sel1, int32_t* fine,
+                                hipStream_t stream) {
+  const long total = (long)s.bh * (s.n >> kBlockShift) * s.fine_k;
+  LLSA_LAUNCH("expand_kernel", expand_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+              0, stream, sel1, fine, s.bshift - kBlockShift, s.topk, total);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* const* k_lv,
@@ -277,6 +308,7 @@ hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* 
   a.topk = s.topk;
   a.hi = level_hi;
   a.lo = level_lo;
+  a.bshift = s.bshift;
   const int n_lo = s.n_level(level_lo);
   const long waves = (long)s.bh * ((n_lo + 15) >> 4);   // one per group
   const unsigned blocks = (unsigned)((waves + kSelWaves - 1) / kSelWaves);

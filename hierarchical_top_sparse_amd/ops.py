@@ -15,6 +15,7 @@ import torch
 from . import _abi
 from ._abi import (LLSA_BF16, LLSA_F32, LLSA_LAYOUT_MORTON, LLSA_LAYOUT_RASTER, Problem,
                    llsa_attn_bwd, llsa_attn_bwd_masked, llsa_attn_fwd, llsa_block_mask,
+                   llsa_expand_blocks,
                    llsa_index_transpose, llsa_index_transpose_workspace, llsa_pool,
                    llsa_reorder, llsa_select, llsa_workspace_bytes)
 
@@ -25,7 +26,8 @@ __all__ = ["Problem", "make_problem", "llsa_forward", "llsa_backward", "llsa_bac
 
 def make_problem(q: torch.Tensor, height: int, width: int, levels: int, topk: int = 8,
                  enrich: bool = True, scale: float = 0.0, layout: int = LLSA_LAYOUT_RASTER,
-                 enrich_levels: int = 0, coarse_unit_weight: bool = False):
+                 enrich_levels: int = 0, coarse_unit_weight: bool = False,
+                 block: int = 16):
     b, h, n, d = q.shape
     if n != height * width:
         raise ValueError(f"token count {n} != height*width {height * width}")
@@ -34,7 +36,8 @@ def make_problem(q: torch.Tensor, height: int, width: int, levels: int, topk: in
         raise ValueError(f"unsupported dtype {q.dtype}")
     return Problem(batch=b, heads=h, height=height, width=width, levels=levels, topk=topk,
                    enrich=int(enrich), head_dim=d, scale=scale, dtype=dtype, layout=layout,
-                   enrich_levels=enrich_levels, coarse_unit_weight=int(coarse_unit_weight))
+                   enrich_levels=enrich_levels, coarse_unit_weight=int(coarse_unit_weight),
+                   block=block)
 
 
 def reorder(p: Problem, x: torch.Tensor, inverse: bool = False) -> torch.Tensor:
@@ -44,38 +47,47 @@ def reorder(p: Problem, x: torch.Tensor, inverse: bool = False) -> torch.Tensor:
 
 
 def llsa_forward(p: Problem, q, k, v):
-    """Returns a dict: o, lse, q_lv, k_lv, v_lv (levels 1..L, v level 1 is None), sel."""
+    """Returns a dict: o, lse, q_lv, k_lv, v_lv (levels 1..L, v level 1 is None), sel (the
+    selection of every level), fine (level 1 as 16-token blocks: sel[0] itself for B = 16)."""
     dev = q.device
     lv_shape = lambda l: (p.batch, p.heads, p.n_level(l), p.head_dim)
     f32 = dict(device=dev, dtype=torch.float32)
     q_lv = [torch.empty(lv_shape(l), **f32) for l in range(1, p.levels + 1)]
     k_lv = [torch.empty(lv_shape(l), **f32) for l in range(1, p.levels + 1)]
-    # V's level 1 is only an intermediate of the fused pooling (attention reads levels >= 2)
-    v_lv = [None] + [torch.empty(lv_shape(l), **f32) for l in range(2, p.levels + 1)]
+    # attention reads V's levels >= 2 only; level 1 is stored only where the next level is
+    # pooled from it (block 64; with block 16 levels 1 and 2 both come from the tokens)
+    v_lv = [torch.empty(lv_shape(1), **f32) if p.block != 16 and p.levels >= 2 else None] + [
+        torch.empty(lv_shape(l), **f32) for l in range(2, p.levels + 1)]
     need_v = p.enrich and p.levels >= 2
     llsa_pool(p, q, k, v if need_v else None, q_lv, k_lv, v_lv)
     sel = [torch.empty((p.batch, p.heads, p.n_level(l), p.topk), device=dev, dtype=torch.int32)
            for l in range(1, p.levels + 1)]
     llsa_select(p, q_lv, k_lv, sel)
+    fine = sel[0]
+    if p.block != 16:
+        fine = torch.empty((p.batch, p.heads, p.n // 16, p.fine_k), device=dev,
+                           dtype=torch.int32)
+        llsa_expand_blocks(p, sel[0], fine)
     o = torch.empty_like(q)
     lse = torch.empty((p.batch, p.heads, p.n), **f32)
-    llsa_attn_fwd(p, q, k, v, k_lv, v_lv, sel, o, lse)
-    return dict(o=o, lse=lse, q_lv=q_lv, k_lv=k_lv, v_lv=v_lv, sel=sel)
+    llsa_attn_fwd(p, q, k, v, k_lv, v_lv, [fine] + sel[1:], o, lse)
+    return dict(o=o, lse=lse, q_lv=q_lv, k_lv=k_lv, v_lv=v_lv, sel=sel, fine=fine)
 
 
 def build_csc(p: Problem, sel):
-    """Per level l: CSC of Sel_l (rows = queries, cols = keys, both n_l): (off, rows)."""
+    """Per level l: CSC of the attention's selection (level 1 as 16-token blocks, sel[0] =
+    the `fine` array; rows = queries, cols = keys): (off, rows)."""
     levels = 1 + p.coarse_levels
     offs, rows = [], []
     nmat = p.batch * p.heads
-    ws_bytes = max(llsa_index_transpose_workspace(nmat, p.n_level(l), p.n_level(l), p.topk)
-                   for l in range(1, levels + 1))
+    dims = [p.csc_dims(l) for l in range(1, levels + 1)]
+    ws_bytes = max(llsa_index_transpose_workspace(nmat, nl, nl, kk) for nl, kk in dims)
     ws = torch.empty(ws_bytes, device=sel[0].device, dtype=torch.uint8)
     for l in range(1, levels + 1):
-        nl = p.n_level(l)
+        nl, kk = p.csc_dims(l)
         off = torch.empty((p.batch, p.heads, nl + 1), device=ws.device, dtype=torch.int32)
-        r = torch.empty((p.batch, p.heads, nl * p.topk), device=ws.device, dtype=torch.int32)
-        llsa_index_transpose(nmat, nl, nl, p.topk, sel[l - 1], off, r, ws)
+        r = torch.empty((p.batch, p.heads, nl * kk), device=ws.device, dtype=torch.int32)
+        llsa_index_transpose(nmat, nl, nl, kk, sel[l - 1], off, r, ws)
         offs.append(off)
         rows.append(r)
     return offs, rows
@@ -83,12 +95,13 @@ def build_csc(p: Problem, sel):
 
 def llsa_backward(p: Problem, q, k, v, fwd: dict, dout):
     """Returns (dq, dk, dv) for the forward state `fwd`."""
-    offs, rows = build_csc(p, fwd["sel"])
+    sel = [fwd.get("fine", fwd["sel"][0])] + list(fwd["sel"][1:])
+    offs, rows = build_csc(p, sel)
     _, ws_bytes = llsa_workspace_bytes(p)
     ws = torch.empty(max(ws_bytes, 16), device=q.device, dtype=torch.uint8)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    llsa_attn_bwd(p, q, k, v, dout, fwd["lse"], fwd["k_lv"], fwd["v_lv"], fwd["sel"], offs,
-                  rows, dq, dk, dv, ws)
+    llsa_attn_bwd(p, q, k, v, dout, fwd["lse"], fwd["k_lv"], fwd["v_lv"], sel, offs, rows, dq,
+                  dk, dv, ws)
     return dq, dk, dv
 
 

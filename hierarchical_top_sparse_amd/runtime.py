@@ -32,21 +32,27 @@ class Step:
                                    dtype=f32)
         self.q_lv = [lv(l) for l in range(1, L + 1)]
         self.k_lv = [lv(l) for l in range(1, L + 1)]
-        self.v_lv = [None] + [lv(l) for l in range(2, L + 1)]
+        # V level 1 only where level 2 is pooled from it (block 64)
+        self.v_lv = [lv(1) if p.block != 16 and L >= 2 else None] + [lv(l) for l in range(2, L + 1)]
         self.pool_v = bool(p.enrich) and L >= 2
         self.sel = [torch.empty((p.batch, p.heads, p.n_level(l), p.topk), device=dev,
                                 dtype=torch.int32) for l in range(1, L + 1)]
+        # level 1 as the attention reads it (16-token blocks): sel[0] itself for B = 16
+        self.fine = (self.sel[0] if p.block == 16 else
+                     torch.empty((p.batch, p.heads, p.n // 16, p.fine_k), device=dev,
+                                 dtype=torch.int32))
+        self.att_sel = [self.fine] + self.sel[1:]
         self.o = torch.empty_like(q)
         self.lse = torch.empty((p.batch, p.heads, p.n), device=dev, dtype=f32)
         self.csc_levels = 1 + p.coarse_levels if self.backward else 0
-        self.off = [torch.empty((p.batch, p.heads, p.n_level(l) + 1), device=dev,
-                                dtype=torch.int32) for l in range(1, self.csc_levels + 1)]
-        self.rows = [torch.empty((p.batch, p.heads, p.n_level(l) * p.topk), device=dev,
-                                 dtype=torch.int32) for l in range(1, self.csc_levels + 1)]
+        dims = [p.csc_dims(l) for l in range(1, self.csc_levels + 1)]
+        self.off = [torch.empty((p.batch, p.heads, nl + 1), device=dev, dtype=torch.int32)
+                    for nl, _ in dims]
+        self.rows = [torch.empty((p.batch, p.heads, nl * kk), device=dev, dtype=torch.int32)
+                     for nl, kk in dims]
         self.nmat = p.batch * p.heads
-        tws = max([_abi.llsa_index_transpose_workspace(self.nmat, p.n_level(l), p.n_level(l),
-                                                       p.topk)
-                   for l in range(1, self.csc_levels + 1)] + [16])
+        tws = max([_abi.llsa_index_transpose_workspace(self.nmat, nl, nl, kk)
+                   for nl, kk in dims] + [16])
         self.tws = torch.empty(tws, device=dev, dtype=torch.uint8)
         _, bws = _abi.llsa_workspace_bytes(p) if self.backward else (0, 0)
         self.bws = torch.empty(max(bws, 16), device=dev, dtype=torch.uint8)
@@ -59,9 +65,9 @@ class Step:
         a, p = _abi, self.p
         out = []
         for l in range(1, self.csc_levels + 1):
-            nl = p.n_level(l)
-            out.append((f"transpose_l{l}", (lambda l=l, nl=nl: a.llsa_index_transpose(
-                self.nmat, nl, nl, p.topk, self.sel[l - 1], self.off[l - 1], self.rows[l - 1],
+            nl, kk = p.csc_dims(l)
+            out.append((f"transpose_l{l}", (lambda l=l, nl=nl, kk=kk: a.llsa_index_transpose(
+                self.nmat, nl, nl, kk, self.att_sel[l - 1], self.off[l - 1], self.rows[l - 1],
                 self.tws))))
         return out
 
@@ -71,10 +77,12 @@ class Step:
         head = [("pool", lambda: a.llsa_pool(p, self.q, self.k, self.v if self.pool_v else None,
                                              self.q_lv, self.k_lv, self.v_lv)),
                 ("select", lambda: a.llsa_select(p, self.q_lv, self.k_lv, self.sel))]
+        if p.block != 16:
+            head.append(("expand", lambda: a.llsa_expand_blocks(p, self.sel[0], self.fine)))
         fwd = [("attn_fwd", lambda: a.llsa_attn_fwd(p, self.q, self.k, self.v, self.k_lv,
-                                                     self.v_lv, self.sel, self.o, self.lse))]
+                                                     self.v_lv, self.att_sel, self.o, self.lse))]
         bwd = [("attn_bwd", lambda: a.llsa_attn_bwd(
-            p, self.q, self.k, self.v, self.dout, self.lse, self.k_lv, self.v_lv, self.sel,
+            p, self.q, self.k, self.v, self.dout, self.lse, self.k_lv, self.v_lv, self.att_sel,
             self.off, self.rows, self.dq, self.dk, self.dv, self.bws))] if self.backward else []
         self._parts = (head, fwd, self._transpose_calls(), bwd)
         return head + fwd + self._parts[2] + bwd

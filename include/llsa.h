@@ -27,8 +27,9 @@
  *    leave outputs untouched; LLSA_ERR_HIP means a launch failed (outputs undefined).
  *    llsa_last_error() gives a message for the last failure on the calling thread.
  *  - Results are deterministic: no atomics, fixed reduction orders.
- *  - Supported: head_dim 64, block 16 (4x4 pixel tiles), height and width powers of two
- *    >= 4, 256 <= N <= 2^23, N % block^levels == 0, 1 <= topk <= min(32, N / block^levels),
+ *  - Supported: head_dim 64, block 16 (4x4 pixel tiles) or 64 (8x8 pixel tiles), height and
+ *    width powers of two >= 4, 256 <= N <= 2^23, N % block^levels == 0,
+ *    1 <= topk <= min(32, N / block^levels) and topk * block / 16 <= 32,
  *    1 <= levels <= 6, batch*heads*N < 2^31.  dtype bf16 for every call; f32 for
  *    reorder/pool/select/attn_fwd.
  */
@@ -66,7 +67,7 @@ typedef struct {
   int32_t height;   /* pixel rows    (power of two) */
   int32_t width;    /* pixel columns (power of two) */
   int32_t head_dim; /* 64 */
-  int32_t block;    /* B: tokens per pooled token; 16 = a 4x4 tile */
+  int32_t block;    /* B: tokens per pooled token; 16 = a 4x4 tile, 64 = an 8x8 tile */
   int32_t levels;   /* L: pooled levels 1..L; the coarsest has N / B^L tokens */
   int32_t topk;     /* K: keys kept per query at every level */
   int32_t enrich;   /* 0: fine keys only; 1: also the K selected keys of levels 2..L */
@@ -128,6 +129,16 @@ int32_t llsa_select(const llsa_problem* p, const float* const* q_lv, const float
                     int32_t* const* sel, int32_t level_hi, int32_t level_lo, void* stream);
 
 /*
+ * llsa_expand_blocks — level-1 picks as the 16-token blocks they cover, the form the
+ * attention kernels read: fine[b][h][q][i * (B/16) + t] = sel1[b][h][q / (B/16)][i] * (B/16)
+ * + t for t < B/16, i < topk (ascending rows stay ascending; negative ids stay -1).
+ * sel1: [b, H, N/B, topk] (Sel_1 from llsa_select); fine: [b, H, N/16, topk * B / 16],
+ * caller-owned, distinct from sel1.  With block 16 a copy.
+ */
+int32_t llsa_expand_blocks(const llsa_problem* p, const int32_t* sel1, int32_t* fine,
+                           void* stream);
+
+/*
  * llsa_attn_fwd — sparse attention with hierarchical KV enrichment (summary sec. 四;
  * article sec. 三/四: gather of the selected blocks, no dense mask).  Each level-1 query
  * block p (B queries) attends to the B tokens of each block in sel[0][p] and, if enrich,
@@ -136,6 +147,9 @@ int32_t llsa_select(const llsa_problem* p, const float* const* q_lv, const float
  * lse = log sum w e^s.  bf16: MFMA with fp32 accumulation and softmax (pooled keys/values are
  * rounded to bf16 for the MFMA); f32: fp32 MFMA.  k_lv/v_lv: L pointers, levels >= 2 read.
  * Out-of-range indices in sel are skipped.  o: token tensor (layout), lse: [b, H, N] Morton.
+ * sel[0] lists level-1 picks as 16-token blocks: [b, H, N/16, topk * block / 16]; with block
+ * 16 that is Sel_1 itself, with block 64 the output of llsa_expand_blocks.  sel[l-1], l >= 2:
+ * Sel_l as from llsa_select.
  */
 int32_t llsa_attn_fwd(const llsa_problem* p, const void* q, const void* k, const void* v,
                       const float* const* k_lv, const float* const* v_lv,
@@ -168,6 +182,8 @@ int32_t llsa_index_transpose(int32_t nmat, int32_t rows, int32_t cols, int32_t k
  * No gradient through the selection or the pooled Q.  Outputs: complete dq, dk, dv
  * (layout p->layout).  csc_off/csc_rows: L pointers, level l from llsa_index_transpose of
  * sel[l-1] (rows = cols = n_l); levels >= 2 are read only if enrich.  bf16 only.
+ * sel[0], csc_off[0], csc_rows[0]: level 1 as 16-token blocks (sel[0] as for llsa_attn_fwd;
+ * its transpose has rows = cols = N/16 and k = topk * block / 16).
  * ws: llsa_workspace_bytes(bwd) bytes of device memory.
  */
 int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const void* v,

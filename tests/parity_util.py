@@ -77,12 +77,12 @@ def candidate_scores(q_l, k_l, parent, k):
     return cand, scores
 
 
-def check_level(gpu_sel, q_l, k_l, parent, k, where=""):
+def check_level(gpu_sel, q_l, k_l, parent, k, where="", block=B):
     """Teacher-forced check of one level's selection of one head; returns #rows that differ
     from the oracle within the tie window."""
     n = q_l.shape[0]
     want = (orc.select_coarsest(q_l, k_l, k) if parent is None
-            else orc.select_level(q_l, k_l, parent, B, k))
+            else orc.select_level(q_l, k_l, parent, block, k))
     got = np.asarray(gpu_sel, dtype=np.int64)
     assert got.shape == want.shape, where
     diff_rows = np.nonzero((got != want).any(axis=1))[0]
@@ -93,7 +93,7 @@ def check_level(gpu_sel, q_l, k_l, parent, k, where=""):
             c = np.arange(k_l.shape[0])
             s = q_l[a] @ k_l.T
         else:
-            c = (parent[a // B][:, None] * B + np.arange(B)).reshape(-1)
+            c = (parent[a // block][:, None] * block + np.arange(block)).reshape(-1)
             s = k_l[c] @ q_l[a]
         row = got[a]
         assert np.all(np.diff(row) > 0), f"{where} row {a}: not ascending/distinct: {row}"
@@ -110,7 +110,7 @@ def check_level(gpu_sel, q_l, k_l, parent, k, where=""):
     return int(diff_rows.size)
 
 
-def check_selection(gpu_sel, q_lv, k_lv, k, where=""):
+def check_selection(gpu_sel, q_lv, k_lv, k, where="", block=B):
     """gpu_sel: per level [b, H, n_l, K] arrays; q_lv/k_lv: oracle fp64 pooled levels."""
     levels = len(gpu_sel)
     flips = 0
@@ -121,7 +121,7 @@ def check_selection(gpu_sel, q_lv, k_lv, k, where=""):
                 parent = None if l == levels else gpu_sel[l][bi, hi]
                 flips += check_level(gpu_sel[l - 1][bi, hi], q_lv[l - 1][bi, hi],
                                      k_lv[l - 1][bi, hi], parent, k,
-                                     f"{where} b{bi} h{hi} level {l}")
+                                     f"{where} b{bi} h{hi} level {l}", block)
     return flips
 
 

@@ -63,7 +63,10 @@ def _p(**kw):
     (dict(coarse_unit_weight=2), 2),
     (dict(enrich_levels=5, coarse_unit_weight=1), 0),   # clamped to the L - 1 coarse levels
     (dict(head_dim=128), 4),
-    (dict(block=64), 4),                    # a power of 4 but not implemented
+    (dict(block=256), 4),                   # a power of 4 but not implemented
+    (dict(block=64, levels=1), 0),          # 8x8 tiles: 64 blocks of 64 tokens, K = 8
+    (dict(block=64, levels=2), 2),          # N / 64^2 = 1 < K
+    (dict(block=64, levels=1, topk=9), 4),  # 9 picks cover 36 16-token blocks (> 32)
     (dict(block=8), 2),                     # not a square tile
     (dict(levels=0), 2),
     (dict(levels=7), 2),
@@ -161,3 +164,15 @@ def test_mask_comparator_validation(L):
     big = _p(batch=1, heads=8, height=1024, width=1024, levels=1, topk=8, dtype=abi.LLSA_BF16)
     assert abi.llsa_check(big) == 0
     assert L.llsa_block_mask(ctypes.byref(big.c()), f, f, None) == 2
+
+
+def test_block64_pool_needs_level_one(L):
+    """With 8x8 blocks level 2 is pooled from level 1, so a tensor's level 1 must be stored."""
+    f = ctypes.c_void_p(FAKE)
+    p = _p(height=256, width=256, levels=2, dtype=abi.LLSA_BF16, block=64)
+    assert abi.llsa_check(p) == 0
+    lv_missing = (ctypes.c_void_p * 6)(None, FAKE)
+    assert L.llsa_pool(ctypes.byref(p.c()), None, f, None, None, lv_missing, None, None) == 1
+    assert b"level 1" in L.llsa_last_error()
+    lv_bad = (ctypes.c_void_p * 6)(MISALIGNED, FAKE)
+    assert L.llsa_pool(ctypes.byref(p.c()), None, f, None, None, lv_bad, None, None) == 6

@@ -235,7 +235,8 @@ def _attn_case(seed, n=1024, d=16, B=4, L=3, K=3):
 
 @pytest.mark.parametrize("n,B,L,K,enrich", [(4096, 16, 2, 3, True), (1024, 4, 3, 3, True),
                                              (1024, 4, 3, 2, False), (256, 16, 1, 3, False),
-                                             (4096, 4, 4, 2, True)])
+                                             (4096, 4, 4, 2, True), (4096, 64, 1, 3, False),
+                                             (4096, 64, 2, 1, True)])
 def test_attention_matches_dense_mask_formulation(n, B, L, K, enrich):
     q, k, v, kl, vl, sel = _attn_case(11, n=n, B=B, L=L, K=K)
     o, lse = orc.attention_forward(q, k, v, kl, vl, sel, B, enrich)
@@ -321,6 +322,18 @@ def test_backward_matches_autograd_of_dense_mask_formulation(n, B, L, enrich):
     assert np.allclose(dq, qt.grad.numpy(), rtol=0, atol=1e-10)
     assert np.allclose(dk, kt.grad.numpy(), rtol=0, atol=1e-10)
     assert np.allclose(dv, vt.grad.numpy(), rtol=0, atol=1e-10)
+
+
+def test_backward_block64_matches_autograd_of_dense_mask_formulation():
+    """B = 64 (8x8 tiles): two levels, one coarse key per query block."""
+    q, k, v, kl, vl, sel = _attn_case(52, n=4096, d=8, B=64, L=2, K=1)
+    do = _rand(q.shape, 53)
+    dq, dk, dv = orc.attention_backward(q, k, v, kl, vl, sel, do, 64, True)
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    o = _dense_mask_formulation(qt, kt, vt, sel, 64, True, 1 / math.sqrt(q.shape[1]))
+    o.backward(torch.tensor(do))
+    for g, t in zip((dq, dk, dv), (qt, kt, vt)):
+        assert np.allclose(g, t.grad.numpy(), rtol=0, atol=1e-10)
 
 
 def test_backward_finite_differences():
