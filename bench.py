@@ -15,8 +15,13 @@ Beside the headline, `extra` carries:
   * dense_baseline: the library's own dense flash attention at the same shapes (forward at
     256x256 batch 1, forward + backward at the headline shape) and the speed-up ratios.
 
+  * single_level_top32 / mask_backward_comparator: the single-level comparators (one level,
+    K = 32 over all blocks; the dense-mask backward) on the headline inputs.
+--sweep prints one JSON line per side length (64..512) instead: LLSA (B = 16 and B = 64)
+against dense attention and against the single-level comparators.
+
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config px256_train] [--no-cpu]
-                  [--no-configs] [--no-dense]
+                  [--no-configs] [--no-dense] [--sweep]
 """
 from __future__ import annotations
 
@@ -364,8 +369,9 @@ def mask_comparator(q, k, v, do, height, width, reps):
 
 def sweep(steps):
     """Resolution sweep (the shape of the pages' Figure 3 / Figure 4): per side length, LLSA
-    forward and forward + backward against the dense baseline, and the key-major backward
-    kernel's throughput (query-key block pairs per second) as N grows."""
+    forward and forward + backward against the dense baseline with blocks of 16 and of 64
+    tokens, the single-level top-32 comparator, the CSC against the dense-mask key-major pass,
+    and the key-major kernel's throughput (query-key block pairs per second) as N grows."""
     import torch
 
     from hierarchical_top_sparse_amd import _abi, gen, ops
@@ -394,6 +400,11 @@ def sweep(steps):
         dstep()
         dense_train_ms = _event_ms(dstep, 2)
         key_ms = per_kernel_ms.get("bwd_key_kernel")
+        # block 64 (8x8 tiles), K = 8: one level below 256x256 (N / 64^2 < 8), two above
+        l64 = 1 if side < 256 else 2
+        p64 = ops.make_problem(q, side, side, l64, 8, block=64)
+        b64_fwd_ms = measure(Step(p64, q, k, v), steps, 2)[0]
+        b64_train_ms = measure(Step(p64, q, k, v, do), steps, 2)[0]
         p1 = ops.make_problem(q, side, side, 1, 32)
         s1 = Step(p1, q, k, v, do)
         single_ms, _, _, single_kernel_ms, _ = measure(s1, steps, 2)
@@ -405,6 +416,10 @@ def sweep(steps):
             "dense_fwd_ms": round(dense_fwd_ms, 3), "dense_train_ms": round(dense_train_ms, 3),
             "speedup_fwd": round(dense_fwd_ms / fwd_ms, 2),
             "speedup_train": round(dense_train_ms / train_ms, 2),
+            "b64_levels": l64, "b64_fwd_ms": round(b64_fwd_ms, 4),
+            "b64_train_ms": round(b64_train_ms, 4),
+            "b64_speedup_fwd": round(dense_fwd_ms / b64_fwd_ms, 2),
+            "b64_speedup_train": round(dense_train_ms / b64_train_ms, 2),
             "single_level_top32_train_ms": round(single_ms, 4),
             "single_level_select_ms": round(single_kernel_ms.get("select_kernel", 0.0), 4),
             "llsa_select_ms": round(per_kernel_ms.get("select_kernel", 0.0), 4),
