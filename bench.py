@@ -18,10 +18,11 @@ Beside the headline, `extra` carries:
   * single_level_top32 / mask_backward_comparator: the single-level comparators (one level,
     K = 32 over all blocks; the dense-mask backward) on the headline inputs.
 --sweep prints one JSON line per side length (64..512) instead: LLSA (B = 16 and B = 64)
-against dense attention and against the single-level comparators.
+against dense attention and against the single-level comparators.  --dit prints one line for
+the synthetic Pixel-DiT-S training step (LLSA against dense attention inside the network).
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config px256_train] [--no-cpu]
-                  [--no-configs] [--no-dense] [--sweep]
+                  [--no-configs] [--no-dense] [--sweep] [--dit]
 """
 from __future__ import annotations
 
@@ -63,6 +64,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: LLSA vs the dense baseline across "
                          "resolutions 64^2 .. 512^2 (batch 1, 6 heads), one JSON line each")
+    ap.add_argument("--dit", action="store_true",
+                    help="time the synthetic Pixel-DiT-S training step (LLSA vs dense) instead")
     ap.add_argument("--with-copy", action="store_true",
                     help="also launch one Morton reorder (a plain copy of one token tensor) per "
                          "step, outside the timed region: the calibration kernel for HBM "
@@ -367,6 +370,36 @@ def mask_comparator(q, k, v, do, height, width, reps):
     return out
 
 
+def dit_bench(steps, warmup, side=256, batch=2, depth=12):
+    """Synthetic Pixel-DiT-S training step (hidden 384, 6 heads, patch 1x1, depth 12; random
+    weights and data) with LLSA (B = 16, K = 8, L = 3, Morton order hoisted to the network's
+    entry) and with the library's dense attention: images/s and the speed-up (the pages'
+    Table 2 analogue: DiT training throughput with LLSA against full attention)."""
+    import torch
+
+    from hierarchical_top_sparse_amd import dit
+    out = {"model": f"Pixel DiT-S depth {depth}, hidden 384, 6 heads, patch 1x1",
+           "pixels": f"{side}x{side}", "batch": batch, "dtype": "bf16 autocast, fp32 master",
+           "optimizer": "AdamW", "data": "synthetic"}
+    levels = 3 if side >= 256 else 2
+    for mode in ("llsa", "dense"):
+        torch.manual_seed(0)
+        model = dit.PixelDiT(side, side, depth=depth, mode=mode, levels=levels).cuda()
+        opt = torch.optim.AdamW(model.parameters(), lr=1e-4)
+        data = dit.synthetic_batch(batch, side, side, "cuda", seed=1)
+        n = steps if mode == "llsa" else max(2, steps // 4)
+        for _ in range(warmup if mode == "llsa" else 1):
+            dit.train_step(model, opt, data)
+        ms = _event_ms(lambda: dit.train_step(model, opt, data), n)
+        out[mode] = {"ms_per_step": round(ms, 3), "images_per_s": round(batch / (ms / 1e3), 2),
+                     "steps": n}
+        del model, opt, data
+        torch.cuda.empty_cache()
+    out["speedup_llsa_vs_dense"] = round(out["dense"]["ms_per_step"] /
+                                         out["llsa"]["ms_per_step"], 2)
+    return out
+
+
 def sweep(steps):
     """Resolution sweep (the shape of the pages' Figure 3 / Figure 4): per side length, LLSA
     forward and forward + backward against the dense baseline with blocks of 16 and of 64
@@ -439,6 +472,10 @@ def main():
     args = parse()
     if args.sweep:
         sweep(max(3, args.steps // 2))
+        return
+    if args.dit:
+        print(json.dumps({"dit_training_step": dit_bench(max(3, args.steps // 2),
+                                                         min(args.warmup, 3))}))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "

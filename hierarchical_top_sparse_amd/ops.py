@@ -20,7 +20,7 @@ from ._abi import (LLSA_BF16, LLSA_F32, LLSA_LAYOUT_MORTON, LLSA_LAYOUT_RASTER, 
                    llsa_reorder, llsa_select, llsa_workspace_bytes)
 
 __all__ = ["Problem", "make_problem", "llsa_forward", "llsa_backward", "llsa_backward_masked",
-           "llsa_attention", "reorder", "LLSA_BF16", "LLSA_F32", "LLSA_LAYOUT_MORTON",
+           "llsa_attention", "dense_attention", "reorder", "LLSA_BF16", "LLSA_F32", "LLSA_LAYOUT_MORTON",
            "LLSA_LAYOUT_RASTER"]
 
 
@@ -138,10 +138,37 @@ class _LLSAFunction(torch.autograd.Function):
 
 def llsa_attention(q, k, v, height: int, width: int, levels: int, topk: int = 8,
                    enrich: bool = True, scale: float = 0.0, enrich_levels: int = 0,
-                   coarse_unit_weight: bool = False):
-    """Log-linear sparse attention over raster-ordered pixel tokens [b, H, height*width, 64].
-    enrich_levels / coarse_unit_weight select the enrichment variants (0 / False: the method
-    as described)."""
-    p = make_problem(q, height, width, levels, topk, enrich, scale, LLSA_LAYOUT_RASTER,
-                     enrich_levels, coarse_unit_weight)
+                   coarse_unit_weight: bool = False, layout: int = LLSA_LAYOUT_RASTER,
+                   block: int = 16):
+    """Log-linear sparse attention over pixel tokens [b, H, height*width, 64] (raster order,
+    or Morton order with layout LLSA_LAYOUT_MORTON).  enrich_levels / coarse_unit_weight
+    select the enrichment variants (0 / False: the method as described); block 16 or 64."""
+    p = make_problem(q, height, width, levels, topk, enrich, scale, layout, enrich_levels,
+                     coarse_unit_weight, block)
     return _LLSAFunction.apply(q, k, v, p)
+
+
+class _DenseFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, scale):
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:-1], device=q.device, dtype=torch.float32)
+        _abi.llsa_dense_attn_fwd(q, k, v, o, lse, scale)
+        ctx.scale = scale
+        ctx.save_for_backward(q, k, v, lse)
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, lse = ctx.saved_tensors
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        _abi.llsa_dense_attn_bwd(q, k, v, dout.contiguous(), lse, dq, dk, dv,
+                                 torch.empty_like(lse), ctx.scale)
+        return dq, dk, dv, None
+
+
+def dense_attention(q, k, v, scale: float = 0.0):
+    """The library's dense softmax attention over [..., N, 64] bf16 (the full-attention
+    baseline), as an autograd op."""
+    return _DenseFunction.apply(q, k, v, scale)
