@@ -67,25 +67,12 @@ __device__ __forceinline__ int chunk_key(int r, int t) { return 8 * (r >> 2) + (
 // x = hi + lo with both parts in bf16: the pair carries ~16 mantissa bits, so products that
 // sum values of both signs (dS sums to zero per query) keep fp32-level accuracy on the MFMA.
 __device__ __forceinline__ void split8(const float (&x)[2][4], bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bf16 h = (bf16)x[t][i];
-      hi[4 * t + i] = h;
-      lo[4 * t + i] = (bf16)(x[t][i] - (float)h);
-    }
+  split8_bf16(f32x4{x[0][0], x[0][1], x[0][2], x[0][3]}, f32x4{x[1][0], x[1][1], x[1][2], x[1][3]},
+              hi, lo);
 }
 
 __device__ __forceinline__ void split_f32x8(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16 ha = (bf16)a[i], hb = (bf16)b[i];
-    hi[i] = ha;
-    hi[i + 4] = hb;
-    lo[i] = (bf16)(a[i] - (float)ha);
-    lo[i + 4] = (bf16)(b[i] - (float)hb);
-  }
+  split8_bf16(a, b, hi, lo);
 }
 
 __device__ __forceinline__ bf16x8 zero8() {
@@ -147,12 +134,7 @@ static size_t bwd_query_lds_bytes(int n_coarse) {
 }
 
 __device__ __forceinline__ void split4(const float (&x)[4], bf16x4& hi, bf16x4& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16 h = (bf16)x[i];
-    hi[i] = h;
-    lo[i] = (bf16)(x[i] - (float)h);
-  }
+  split4_bf16(x[0], x[1], x[2], x[3], hi, lo);
 }
 
 template <int NCT>   // coarse tiles of 16 slots: 0, 1 or 2
@@ -411,10 +393,10 @@ void bwd_query_kernel(BwdArgs a) {
     bf16* dqp = a.dq + (tok_base + qrow) * kDim;
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
-      bf16x4 r;
+      f32x4 r;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) r[i] = (bf16)((acc_a[bb][t4][i] - Dn * acc_b[bb][t4][i]) * a.scale);
-      *(bf16x4*)(dqp + 16 * t4 + 4 * g) = r;
+      for (int i = 0; i < 4; ++i) r[i] = (acc_a[bb][t4][i] - Dn * acc_b[bb][t4][i]) * a.scale;
+      *(bf16x4*)(dqp + 16 * t4 + 4 * g) = pack4_bf16(r);
     }
     if (NCT > 0) {
       // Q and dO rows of the block (row n = query n) in the wave's tiles, D per query
@@ -716,9 +698,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
       f.q[ins] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
       f.d[ins] = __builtin_amdgcn_raw_buffer_load_b128(rdo, o, 0, 0);
     }
-    const uint32_t tl = ((lane >> 4) & 1) ? tB : tA;
-    f.ld = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                         lane < 32 ? rl : rd, tl + (uint32_t)(n * 4), 0, 0));
+    // lanes 0..31 read the LSE, lanes 32..63 D: one load from each array (the other half of
+    // the wave reads offset kNoRow, i.e. zero), so the buffer descriptor stays wave-uniform
+    const uint32_t tl = (((lane >> 4) & 1) ? tB : tA) + (uint32_t)(n * 4);
+    const float l_part = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rl, lane < 32 ? tl : kNoRow, 0, 0));
+    const float d_part = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rd, lane < 32 ? kNoRow : tl, 0, 0));
+    f.ld = l_part + d_part;
     return f;
   };
 
@@ -835,14 +822,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
   for (int t4 = 0; t4 < 4; ++t4) {
     const f32x4 pk = *(const f32x4*)(pdown + 16 * t4 + 4 * g);
     const f32x4 pv = *(const f32x4*)(pdown + kDim + 16 * t4 + 4 * g);
-    bf16x4 rk4, rv4;
+    f32x4 rk4, rv4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      rk4[i] = (bf16)(dka[t4][i] * a.scale + pk[i]);
-      rv4[i] = (bf16)(dva[t4][i] + pv[i]);
+      rk4[i] = dka[t4][i] * a.scale + pk[i];
+      rv4[i] = dva[t4][i] + pv[i];
     }
-    *(bf16x4*)(dkp + 16 * t4 + 4 * g) = rk4;
-    *(bf16x4*)(dvp + 16 * t4 + 4 * g) = rv4;
+    *(bf16x4*)(dkp + 16 * t4 + 4 * g) = pack4_bf16(rk4);
+    *(bf16x4*)(dvp + 16 * t4 + 4 * g) = pack4_bf16(rv4);
   }
 }
 

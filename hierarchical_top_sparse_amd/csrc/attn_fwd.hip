@@ -53,14 +53,7 @@ struct FwdArgs {
 };
 
 __device__ __forceinline__ void split_bf16(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bf16 ha = (bf16)a[i], hb = (bf16)b[i];
-    hi[i] = ha;
-    hi[i + 4] = hb;
-    lo[i] = (bf16)(a[i] - (float)ha);
-    lo[i + 4] = (bf16)(b[i] - (float)hb);
-  }
+  split8_bf16(a, b, hi, lo);
 }
 
 constexpr int kWavePicks = 64;     // QB query blocks x K (QB K <= 64)
@@ -321,9 +314,7 @@ void attn_fwd_kernel(FwdArgs a) {
       l_run[bb] += p[i];
     }
     if constexpr (BF16) {
-      bf16x4 pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pb[i] = (bf16)p[i];
+      const bf16x4 pb = pack4_bf16(p[0], p[1], p[2], p[3]);
       const int r = (lane & 15) >> 2;
       const int c = lane & 3;
 #pragma unroll
@@ -399,10 +390,10 @@ void attn_fwd_kernel(FwdArgs a) {
       bf16* op = (bf16*)a.o + (tok_base + qrow) * kDim;
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        bf16x4 r;
+        f32x4 r;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r[i] = (bf16)(acc[bb][t4][i] * inv);
-        *(bf16x4*)(op + 16 * t4 + 4 * g) = r;
+        for (int i = 0; i < 4; ++i) r[i] = acc[bb][t4][i] * inv;
+        *(bf16x4*)(op + 16 * t4 + 4 * g) = pack4_bf16(r);
       }
     } else {
       float* op = (float*)a.o + (tok_base + qrow) * kDim;

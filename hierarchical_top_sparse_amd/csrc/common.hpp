@@ -104,20 +104,52 @@ __device__ __forceinline__ rsrc_t make_rsrc_uniform(const void* base, uint32_t b
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ------------------------------------------------------------------ conversions
-__device__ __forceinline__ bf16x8 cvt8_bf16(const float* f) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = (bf16)f[i];
-  return r;
+// Floats go to bf16 (round to nearest even) two at a time: one v_cvt_pk_bf16_f32 per pair,
+// already packed the way the MFMA operands hold them (element 2i in the low half).
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+// a = hi.x + lo.x, b = hi.y + lo.y with hi = bf16(a, b) and lo = bf16 of the remainders: the
+// pair carries ~16 mantissa bits.  The bf16 halves of hi are widened back by a shift / mask.
+__device__ __forceinline__ void split2_bf16(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack2_bf16(a, b);
+  lo = pack2_bf16(a - __builtin_bit_cast(float, hi << 16),
+                  b - __builtin_bit_cast(float, hi & 0xffff0000u));
+}
+__device__ __forceinline__ bf16x4 pack4_bf16(float a, float b, float c, float d) {
+  return __builtin_bit_cast(bf16x4, (u32x2){pack2_bf16(a, b), pack2_bf16(c, d)});
+}
+__device__ __forceinline__ bf16x4 pack4_bf16(f32x4 a) { return pack4_bf16(a[0], a[1], a[2], a[3]); }
+// x[0..3] = hi + lo elementwise
+__device__ __forceinline__ void split4_bf16(float x0, float x1, float x2, float x3, bf16x4& hi,
+                                            bf16x4& lo) {
+  uint32_t h0, l0, h1, l1;
+  split2_bf16(x0, x1, h0, l0);
+  split2_bf16(x2, x3, h1, l1);
+  hi = __builtin_bit_cast(bf16x4, (u32x2){h0, h1});
+  lo = __builtin_bit_cast(bf16x4, (u32x2){l0, l1});
+}
+// (a, b) = hi + lo elementwise, a in elements 0..3, b in 4..7
+__device__ __forceinline__ void split8_bf16(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
+  split2_bf16(a[0], a[1], h[0], l[0]);
+  split2_bf16(a[2], a[3], h[1], l[1]);
+  split2_bf16(b[0], b[1], h[2], l[2]);
+  split2_bf16(b[2], b[3], h[3], l[3]);
+  hi = __builtin_bit_cast(bf16x8, (u32x4){h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, (u32x4){l[0], l[1], l[2], l[3]});
 }
 __device__ __forceinline__ bf16x8 cvt8_bf16(f32x4 a, f32x4 b) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = (bf16)a[i];
-    r[i + 4] = (bf16)b[i];
-  }
-  return r;
+  return __builtin_bit_cast(bf16x8, (u32x4){pack2_bf16(a[0], a[1]), pack2_bf16(a[2], a[3]),
+                                            pack2_bf16(b[0], b[1]), pack2_bf16(b[2], b[3])});
+}
+__device__ __forceinline__ bf16x8 cvt8_bf16(const float* f) {
+  return cvt8_bf16(f32x4{f[0], f[1], f[2], f[3]}, f32x4{f[4], f[5], f[6], f[7]});
 }
 
 // ------------------------------------------------------------------ MFMA
