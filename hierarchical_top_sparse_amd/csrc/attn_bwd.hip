@@ -449,30 +449,33 @@ void bwd_query_kernel(BwdArgs a) {
   finish(I1{});
 
   if (NCT > 0) {
-    // ---- the 4 waves' partials summed in wave order into the unit's rows (the coarse tiles
-    // are no longer read once every wave has passed the first barrier)
-    float* red = (float*)ct;   // [2][16 NCT][64]: dK then dV
-    const int half = NCT * 16 * kDim;
-    for (int turn = 0; turn < kQWaves; ++turn) {
-      __syncthreads();
-      if (w == turn) {
-#pragma unroll
-        for (int c = 0; c < NCT; ++c)
-#pragma unroll
-          for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int e = (16 * c + n) * kDim + 16 * t4 + 4 * g + i;
-              red[e] = (turn ? red[e] : 0.f) + cpk[c][t4][i];
-              red[half + e] = (turn ? red[half + e] : 0.f) + cpv[c][t4][i];
-            }
-      }
-    }
-    __syncthreads();
+    // ---- the 4 waves' partials summed in wave order (0 + 1 + 2 + 3) into the unit's rows,
+    // one chunk (a coarse tile's dK or dV: 16 slots x 64 floats) at a time: every wave stores
+    // its part in its own LDS region, then every thread adds 4 elements of the 4 regions and
+    // stores them, so no wave waits for another's turn.  All earlier LDS use is over after
+    // the first barrier.
+    float* red = (float*)smem;   // [kQWaves][16 * kDim]
+    constexpr int kChunk = 16 * kDim;
     const long out_base = ((long)head * kUnits * n2 + rem) * n_coarse * kDim;
-    for (int e = tid; e < n_coarse * kDim; e += 64 * kQWaves) {
-      a.part_k[out_base + e] = red[e] * a.scale;
-      a.part_v[out_base + e] = red[half + e];
+#pragma unroll
+    for (int chunk = 0; chunk < 2 * NCT; ++chunk) {
+      const int c = chunk >> 1;
+      const bool is_v = chunk & 1;
+      __syncthreads();
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+        *(f32x4*)(red + w * kChunk + n * kDim + 16 * t4 + 4 * g) = is_v ? cpv[c][t4] : cpk[c][t4];
+      __syncthreads();
+      const int e = 4 * tid;   // elements e .. e + 3 of the chunk: slot 16 c + e / 64
+      f32x4 sum = *(const f32x4*)(red + e);
+#pragma unroll
+      for (int r = 1; r < kQWaves; ++r) sum += *(const f32x4*)(red + r * kChunk + e);
+      if (16 * c + e / kDim < n_coarse) {
+        if (is_v)
+          *(f32x4*)(a.part_v + out_base + (long)c * kChunk + e) = sum;
+        else
+          *(f32x4*)(a.part_k + out_base + (long)c * kChunk + e) = sum * a.scale;
+      }
     }
   }
 }
