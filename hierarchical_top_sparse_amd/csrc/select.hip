@@ -1,6 +1,6 @@
 // Coarse-to-fine top-K selection (paper summary sec. 三; article sec. 三).
 //
-// One launch computes every requested level.  Wave w owns a group of 16 sibling queries at
+// One launch computes a range of levels.  Wave w owns a group of 16 sibling queries at
 // the finest requested level lo (the 16 children of query w at level lo + 1, or 16 coarsest
 // queries when lo = L), and first walks the chain of that group's ancestors from level hi
 // down to lo + 1:
@@ -10,6 +10,9 @@
 //     arithmetic, and only the first of them stores its row, so there is no cross-wave
 //     dependency and the whole selection is one kernel.
 // The group itself is then ranked against the children of its parent's picks.
+// A request that spans three or more levels down to level 1 is issued as two launches, levels
+// hi .. 2 and then level 1 from the stored level-2 picks: the level-1 waves, by far the most,
+// then skip the redundant chain (at 512x512 L=3 this is 27% faster; identical picks).
 //
 // Scores are fp32 dot products on the fp32 MFMA (v_mfma_f32_16x16x4f32) in the S^T
 // orientation: lane (n, g) holds the scores of query n against candidates 4g..4g+3 of each
@@ -294,8 +297,9 @@ hipError_t launch_expand_blocks(const Shape& s, const int32_t* sel1, int32_t* fi
   return hipGetLastError();
 }
 
-hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* const* k_lv,
-                         int32_t* const* sel, int level_hi, int level_lo, hipStream_t stream) {
+static hipError_t launch_select_range(const Shape& s, const float* const* q_lv,
+                                      const float* const* k_lv, int32_t* const* sel,
+                                      int level_hi, int level_lo, hipStream_t stream) {
   SelArgs a{};
   for (int l = 0; l < s.levels && l < kSelMaxLv; ++l) {
     a.q[l] = q_lv[l];
@@ -322,6 +326,16 @@ hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* 
     LLSA_LAUNCH("select_kernel", select_kernel<32>, dim3(blocks), dim3(64 * kSelWaves), 0,
                 stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* const* k_lv,
+                         int32_t* const* sel, int level_hi, int level_lo, hipStream_t stream) {
+  if (level_lo == 1 && level_hi >= 3) {
+    const hipError_t e = launch_select_range(s, q_lv, k_lv, sel, level_hi, 2, stream);
+    if (e != hipSuccess) return e;
+    return launch_select_range(s, q_lv, k_lv, sel, 1, 1, stream);
+  }
+  return launch_select_range(s, q_lv, k_lv, sel, level_hi, level_lo, stream);
 }
 
 }  // namespace llsa
