@@ -28,7 +28,9 @@ Readings where the pages are silent or garbled (each is listed in the design not
     block's level-l ancestor; no de-duplication against the fine keys;
   * variants (switches, not the method's default): enrich_levels = m keeps only the coarse
     levels 2..1+m (the finest m; 0 = all), coarse_weight False gives every coarse key weight 1
-    instead of B^l;
+    instead of B^l, exclude_overlap drops a coarse key whose span holds a key the query block
+    already attends one level finer (a fine block for level 2, a level-(l-1) coarse key
+    otherwise), so that no region is covered twice;
   * gradients flow to Q, K, V and through the pooled K/V of the coarse keys (chain rule of
     the mean), not through the top-K selection or the pooled Q.
 
@@ -167,13 +169,16 @@ def select(q_lv: Sequence[np.ndarray], k_lv: Sequence[np.ndarray], block: int,
 
 
 def key_list(p: int, k: np.ndarray, v: np.ndarray, k_lv, v_lv, sel, block: int,
-             enrich: bool, enrich_levels: int = 0, coarse_weight: bool = True):
+             enrich: bool, enrich_levels: int = 0, coarse_weight: bool = True,
+             exclude_overlap: bool = False):
     """Keys, values and log-weights attended by level-1 query block p.
 
     Fine: every token of the K blocks in Sel_1[p] (log-weight 0).
     Coarse (enrich): for l = 2..L, the keys Sel_l[a] of block p's level-l ancestor
     a = p // B^(l-1), each with weight B^l (log-weight l*ln B).  Variants: enrich_levels m > 0
-    stops at level min(L, 1 + m); coarse_weight False uses weight 1 (log-weight 0).
+    stops at level min(L, 1 + m); coarse_weight False uses weight 1 (log-weight 0);
+    exclude_overlap drops a level-l key that is the parent of one of the keys selected one
+    level finer for p (Sel_1[p] for l = 2, Sel_(l-1) of p's level-(l-1) ancestor above).
     Also returns the identity of every key: (level, index), level 0 = fine token.
     """
     keys, vals, logw, ident = [], [], [], []
@@ -188,6 +193,10 @@ def key_list(p: int, k: np.ndarray, v: np.ndarray, k_lv, v_lv, sel, block: int,
         for l in range(2, top + 1):
             a = p // block ** (l - 1)
             ids = sel[l - 1][a]
+            if exclude_overlap:
+                finer = sel[l - 2][p // block ** (l - 2)]
+                covered = {int(x) // block for x in finer}
+                ids = np.array([j for j in ids if int(j) not in covered], dtype=np.int64)
             keys.append(k_lv[l - 1][ids])
             vals.append(v_lv[l - 1][ids])
             logw.append(np.full(len(ids), l * math.log(block) if coarse_weight else 0.0))
@@ -197,7 +206,7 @@ def key_list(p: int, k: np.ndarray, v: np.ndarray, k_lv, v_lv, sel, block: int,
 
 def attention_forward(q, k, v, k_lv, v_lv, sel, block: int, enrich: bool = True,
                       scale: float | None = None, blocks=None, enrich_levels: int = 0,
-                      coarse_weight: bool = True):
+                      coarse_weight: bool = True, exclude_overlap: bool = False):
     """Per-head forward in Morton order.  Returns (o [N, d], lse [N]) (rows of `blocks` only
     are filled when `blocks` is given; the rest stay NaN).
 
@@ -211,7 +220,7 @@ def attention_forward(q, k, v, k_lv, v_lv, sel, block: int, enrich: bool = True,
     nblk = n // block
     for p in (range(nblk) if blocks is None else blocks):
         kk, vv, logw, _ = key_list(p, k, v, k_lv, v_lv, sel, block, enrich, enrich_levels,
-                                   coarse_weight)
+                                   coarse_weight, exclude_overlap)
         rows = slice(p * block, (p + 1) * block)
         s = scale * (q[rows] @ kk.T) + logw[None, :]
         m = s.max(axis=1, keepdims=True)
@@ -224,7 +233,7 @@ def attention_forward(q, k, v, k_lv, v_lv, sel, block: int, enrich: bool = True,
 
 def attention_backward(q, k, v, k_lv, v_lv, sel, do, block: int, enrich: bool = True,
                        scale: float | None = None, enrich_levels: int = 0,
-                       coarse_weight: bool = True):
+                       coarse_weight: bool = True, exclude_overlap: bool = False):
     """Per-head gradients (dq, dk, dv) in Morton order, given upstream dO.
 
     Softmax Jacobian per query: P_e = w_e exp(s_e) / Z, dP_e = dO.v_e,
@@ -244,7 +253,7 @@ def attention_backward(q, k, v, k_lv, v_lv, sel, do, block: int, enrich: bool = 
     dv_lv = [np.zeros_like(x) for x in v_lv]
     for p in range(n // block):
         kk, vv, logw, ident = key_list(p, k, v, k_lv, v_lv, sel, block, enrich, enrich_levels,
-                                       coarse_weight)
+                                       coarse_weight, exclude_overlap)
         rows = slice(p * block, (p + 1) * block)
         s = scale * (q[rows] @ kk.T) + logw[None, :]
         m = s.max(axis=1, keepdims=True)
@@ -337,7 +346,8 @@ def csr_to_csc(sel: np.ndarray, n_cols: int):
 
 def llsa_forward(q, k, v, height: int, width: int, block: int, levels: int, topk,
                  enrich: bool = True, scale: float | None = None, sel_override=None,
-                 enrich_levels: int = 0, coarse_weight: bool = True):
+                 enrich_levels: int = 0, coarse_weight: bool = True,
+                 exclude_overlap: bool = False):
     """Full forward: reorder -> pool -> select -> attention -> inverse reorder.
 
     Returns a dict with o (raster), lse (Morton order, [b, H, N]), and the Morton-order
@@ -360,7 +370,8 @@ def llsa_forward(q, k, v, height: int, width: int, block: int, levels: int, topk
                    else sel_override[bi][hi])
             om[bi, hi], lse[bi, hi] = attention_forward(
                 qm[bi, hi], km[bi, hi], vm[bi, hi], kl, vl, sel, block, enrich, scale,
-                enrich_levels=enrich_levels, coarse_weight=coarse_weight)
+                enrich_levels=enrich_levels, coarse_weight=coarse_weight,
+                exclude_overlap=exclude_overlap)
             row.append(sel)
         sels.append(row)
     return dict(o=reorder(om, height, width, inverse=True), om=om, lse=lse, qm=qm, km=km,
@@ -369,7 +380,7 @@ def llsa_forward(q, k, v, height: int, width: int, block: int, levels: int, topk
 
 def llsa_backward(q, k, v, do, height: int, width: int, block: int, levels: int, sels,
                   enrich: bool = True, scale: float | None = None, enrich_levels: int = 0,
-                  coarse_weight: bool = True):
+                  coarse_weight: bool = True, exclude_overlap: bool = False):
     """Full backward on the forward's selection: returns raster-order (dq, dk, dv)."""
     qm, km, vm, dom = (reorder(t, height, width) for t in (q, k, v, do))
     k_lv, v_lv = (pool_levels(t, block, levels) for t in (km, vm))
@@ -380,7 +391,7 @@ def llsa_backward(q, k, v, do, height: int, width: int, block: int, levels: int,
             vl = [x[bi, hi] for x in v_lv]
             dq[bi, hi], dk[bi, hi], dv[bi, hi] = attention_backward(
                 qm[bi, hi], km[bi, hi], vm[bi, hi], kl, vl, sels[bi][hi], dom[bi, hi], block,
-                enrich, scale, enrich_levels, coarse_weight)
+                enrich, scale, enrich_levels, coarse_weight, exclude_overlap)
     return tuple(reorder(t, height, width, inverse=True) for t in (dq, dk, dv))
 
 

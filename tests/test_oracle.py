@@ -195,7 +195,8 @@ def _sdpa(q, k, v, mask=None, scale=None):
                                                             scale=scale)
 
 
-def _dense_mask_formulation(qm, km, vm, sel, B, enrich, scale, top=None, weighted=True):
+def _dense_mask_formulation(qm, km, vm, sel, B, enrich, scale, top=None, weighted=True,
+                            exclude=False):
     """torch float64: one query row per token against [fine tokens ; pooled keys of levels
     2..top (default L)], with an additive mask holding 0 (selected fine), l*ln B (selected
     coarse; 0 when not weighted) or -inf.  Token i's level-l ancestor is i // B^l.  Pooling is
@@ -220,8 +221,17 @@ def _dense_mask_formulation(qm, km, vm, sel, B, enrich, scale, top=None, weighte
     if enrich:
         base = n
         for l in range(2, top + 1):
+            finer = sel[l - 2][i // B ** (l - 1)]   # [n, K]: keys one level finer, per token
             for slot in range(sel[l - 1].shape[1]):
-                mask[i, base + sel[l - 1][i // B ** l, slot]] = l * math.log(B) if weighted else 0
+                j = sel[l - 1][i // B ** l, slot]
+                value = np.full(n, l * math.log(B) if weighted else 0.0)
+                if exclude:   # the key's token span meets a finer selected key's span
+                    lo, hi = j * B ** l, (j + 1) * B ** l
+                    flo, fhi = finer * B ** (l - 1), (finer + 1) * B ** (l - 1)
+                    meets = ((np.maximum(lo[:, None], flo) < np.minimum(hi[:, None], fhi))
+                             .any(axis=1))
+                    value[meets] = -np.inf
+                mask[i, base + j] = value
             base += n // B ** l
     return _sdpa(qm[None], keys[None], vals[None], mask[None], scale)[0]
 
@@ -267,6 +277,33 @@ def test_enrichment_variants_match_dense_mask_formulation(B, L, levels_kept, wei
     # the default is the full enrichment with weights B^l: a variant must differ from it
     o_full, _ = orc.attention_forward(q, k, v, kl, vl, sel, B, True)
     assert not np.allclose(o, o_full, rtol=0, atol=1e-6) or (levels_kept == 0 and weighted)
+
+
+@pytest.mark.parametrize("B,L,K,levels_kept", [(4, 3, 2, 0), (4, 4, 2, 0), (16, 2, 3, 0),
+                                               (4, 4, 2, 2)])
+def test_overlap_excluded_coarse_keys_match_dense_mask_formulation(B, L, K, levels_kept):
+    """The variant that drops coarse keys whose span meets a finer selected key: forward and
+    backward against the masked formulation built from token spans."""
+    n = 4096 if B == 16 else 1024
+    q, k, v, kl, vl, sel = _attn_case(15, n=n, d=8, B=B, L=L, K=K)
+    do = _rand(q.shape, 16)
+    kw = dict(enrich_levels=levels_kept, exclude_overlap=True)
+    o, _ = orc.attention_forward(q, k, v, kl, vl, sel, B, True, **kw)
+    top = L if levels_kept == 0 else min(L, 1 + levels_kept)
+    qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    ref = _dense_mask_formulation(qt, kt, vt, sel, B, True, 1 / math.sqrt(q.shape[1]), top,
+                                  True, exclude=True)
+    assert np.allclose(o, ref.detach().numpy(), rtol=0, atol=1e-12)
+    ref.backward(torch.tensor(do))
+    for g, t in zip(orc.attention_backward(q, k, v, kl, vl, sel, do, B, True, **kw),
+                    (qt, kt, vt)):
+        assert np.allclose(g, t.grad.numpy(), rtol=0, atol=1e-10)
+    # some coarse keys are dropped and some kept, so the case exercises both branches
+    kept = [len(orc.key_list(p, k, v, kl, vl, sel, B, True, exclude_overlap=True)[3])
+            for p in range(n // B)]
+    full = [len(orc.key_list(p, k, v, kl, vl, sel, B, True)[3]) for p in range(n // B)]
+    assert min(f - c for f, c in zip(full, kept)) >= 0 and sum(full) > sum(kept)
+    assert any(c > K * B for c in kept)
 
 
 def test_attention_full_k_no_enrich_is_dense_attention():
