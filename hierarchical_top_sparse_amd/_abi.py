@@ -20,7 +20,7 @@ _lib = None
 LLSA_F32, LLSA_BF16 = 0, 1
 LLSA_LAYOUT_MORTON, LLSA_LAYOUT_RASTER = 0, 1
 LLSA_MAX_LEVELS = 6
-LLSA_ABI_VERSION = 2   # the llsa_problem layout this binding marshals
+LLSA_ABI_VERSION = 3   # the llsa_problem layout this binding marshals
 
 
 class LlsaError(RuntimeError):
@@ -34,7 +34,8 @@ class LlsaProblemC(ctypes.Structure):
                 ("batch", "heads", "height", "width", "head_dim", "block", "levels", "topk",
                  "enrich")] + [("scale", ctypes.c_float), ("dtype", ctypes.c_int32),
                                ("layout", ctypes.c_int32), ("enrich_levels", ctypes.c_int32),
-                               ("coarse_unit_weight", ctypes.c_int32)]
+                               ("coarse_unit_weight", ctypes.c_int32),
+                               ("coarse_exclude_overlap", ctypes.c_int32)]
 
 
 @dataclass(frozen=True)
@@ -53,6 +54,7 @@ class Problem:
     layout: int = LLSA_LAYOUT_RASTER
     enrich_levels: int = 0        # with enrich: only coarse levels 2..1+m (0 = all)
     coarse_unit_weight: int = 0   # 1: coarse keys weighted 1 instead of B^l
+    coarse_exclude_overlap: int = 0   # 1: drop coarse keys over a finer selected key
 
     @property
     def fine_k(self) -> int:
@@ -87,7 +89,7 @@ class Problem:
         return LlsaProblemC(self.batch, self.heads, self.height, self.width, self.head_dim,
                             self.block, self.levels, self.topk, int(self.enrich),
                             float(self.scale), self.dtype, self.layout, self.enrich_levels,
-                            self.coarse_unit_weight)
+                            self.coarse_unit_weight, self.coarse_exclude_overlap)
 
 
 def lib() -> ctypes.CDLL:

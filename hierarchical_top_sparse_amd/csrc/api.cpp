@@ -83,6 +83,9 @@ int32_t check_problem(const llsa_problem* p) {
   if (p->coarse_unit_weight != 0 && p->coarse_unit_weight != 1)
     return fail(LLSA_ERR_SHAPE, "coarse_unit_weight must be 0 or 1 (got %d)",
                 p->coarse_unit_weight);
+  if (p->coarse_exclude_overlap != 0 && p->coarse_exclude_overlap != 1)
+    return fail(LLSA_ERR_SHAPE, "coarse_exclude_overlap must be 0 or 1 (got %d)",
+                p->coarse_exclude_overlap);
   if (!(p->scale >= 0.f) || std::isinf(p->scale))
     return fail(LLSA_ERR_SHAPE, "scale must be finite and >= 0");
   if ((long)p->batch * p->heads * n >= (1L << 31))
@@ -111,6 +114,7 @@ llsa::Shape make_shape(const llsa_problem* p) {
   s.bf16 = p->dtype == LLSA_BF16;
   s.scale = p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim);
   s.bshift = log2i(p->block);
+  s.exclude_overlap = p->coarse_exclude_overlap;
   s.fine_k = p->topk * (p->block / 16);
   return s;
 }

@@ -57,7 +57,8 @@ struct BwdArgs {
   int bshift;          // log2(B) of the coarse levels: 4 or 6
   int enrich;          // 1 if there are coarse keys (coarse_levels > 0)
   int coarse_levels;   // coarse keys of levels 2 .. 1 + coarse_levels
-  float lbias;         // log2-domain bias per level: 4 (weight 16^l) or 0 (weight 1)
+  float lbias;         // log2-domain bias per level: log2(B) (weight B^l) or 0 (weight 1)
+  int exclude;         // 1: a coarse key over a key selected one level finer is dropped
   float scale;
   float c2;   // scale * log2(e)
 };
@@ -127,10 +128,13 @@ constexpr int kPickSentinel = 0x7f000000;
 __host__ __device__ constexpr int bwdq_wave_lds_bytes() {
   return 2 * 16 * kStride * 2 + 4 * kQPickList * 4 + 48 * 4;
 }
-static size_t bwd_query_lds_bytes(int n_coarse) {
+// ... then the coarse tiles, each slot's bias and key id, and with overlap exclusion per-block
+// biases [waves][2 blocks][ctiles * 16].
+static size_t bwd_query_lds_bytes(int n_coarse, bool exclude) {
   const int ctiles = (n_coarse + 15) / 16;
   return (size_t)kQWaves * bwdq_wave_lds_bytes() + (size_t)ctiles * 4 * 16 * kStride * 2 +
-         sizeof(float) * 16 * ctiles;
+         (sizeof(float) + sizeof(int)) * 16 * ctiles +
+         (exclude ? sizeof(float) * kQWaves * kQBlocks * 16 * ctiles : 0);
 }
 
 __device__ __forceinline__ void split4(const float (&x)[4], bf16x4& hi, bf16x4& lo) {
@@ -170,6 +174,8 @@ void bwd_query_kernel(BwdArgs a) {
   float* dsh = lsh + 32;                       // [16] D of the current block's queries
   bf16* ct = (bf16*)(smem + kQWaves * bwdq_wave_lds_bytes());   // [NCT][K hi, K lo, V hi, V lo]
   float* cbias = (float*)(ct + NCT * 4 * 16 * kStride);
+  int* cid = (int*)(cbias + 16 * NCT);          // key id of each coarse slot (-1: none)
+  float* wxb = (float*)(cid + 16 * NCT) + w * kQBlocks * 16 * NCT;   // exclusion: [bb][slot]
 
   const uint32_t head_bytes = (uint32_t)a.n * kDim * 2;
   const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
@@ -208,19 +214,30 @@ void bwd_query_kernel(BwdArgs a) {
       const int cslot = e >> 3, c8 = (e & 7) * 8;
       f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
       float bias = -INFINITY;
+      int cslot_id = -1;
       if (cslot < n_coarse) {
         const int l = 2 + cslot / K;
         const int nl = a.n >> (a.bshift * l);
         const int anc = (a2 << (2 * kBlockShift)) >> (a.bshift * l);   // level-l ancestor
         const int id = a.sel[l - 1][((long)head * nl + anc) * K + (cslot - (l - 2) * K)];
         if (id >= 0 && id < nl) {
+          cslot_id = id;
           const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
           const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
           k0 = *(const f32x4*)kp;
           k1 = *(const f32x4*)(kp + 4);
           v0 = *(const f32x4*)vp;
           v1 = *(const f32x4*)(vp + 4);
-          bias = a.lbias * (float)l;   // log2(16^l), or 0 for unit weights
+          bias = a.lbias * (float)l;   // log2(B^l), or 0 for unit weights
+          if (a.exclude && l >= 3 && c8 == 0) {
+            // level >= 3: dropped for the whole group if it is the parent of one of the keys
+            // selected at level l - 1 for the group's level-(l-1) ancestor
+            const int nf = a.n >> (a.bshift * (l - 1));
+            const int ancf = (a2 << (2 * kBlockShift)) >> (a.bshift * (l - 1));
+            for (int i = 0; i < K; ++i)
+              if ((a.sel[l - 2][((long)head * nf + ancf) * K + i] >> a.bshift) == id)
+                bias = -INFINITY;
+          }
         }
       }
       bf16* base = ct + (cslot >> 4) * 4 * 16 * kStride + (cslot & 15) * kStride + c8;
@@ -231,7 +248,10 @@ void bwd_query_kernel(BwdArgs a) {
       split_f32x8(v0, v1, hi, lo);
       *(bf16x8*)(base + 32 * kStride) = hi;
       *(bf16x8*)(base + 48 * kStride) = lo;
-      if (c8 == 0) cbias[cslot] = bias;
+      if (c8 == 0) {
+        cbias[cslot] = bias;
+        cid[cslot] = cslot_id;
+      }
     }
   }
 
@@ -296,7 +316,29 @@ void bwd_query_kernel(BwdArgs a) {
     return f;
   };
   BlockLd fa = load_u(0), fb = load_u(1);
-  if (NCT > 0) __syncthreads();   // coarse tiles staged
+  if (NCT > 0) {
+    __syncthreads();   // coarse tiles staged
+    // with overlap exclusion, per-block biases: a level-2 slot is dropped for block bb if one
+    // of bb's fine picks lies in its span (the 16-token block j is in key (16 j) >> 2 log2(B))
+    if (a.exclude) {
+      for (int sl = lane; sl < 16 * NCT; sl += 64) {
+        const int id = cid[sl];
+        const bool lv2 = sl < K && id >= 0;
+#pragma unroll
+        for (int bb = 0; bb < kQBlocks; ++bb) {
+          bool hit = false;
+          if (lv2)
+            for (int i = 0; i < KF; ++i) {
+              const int kk = keys[kQPickSlots * bb + i];
+              hit |= kk < kPickSentinel &&
+                     (((kk >> 8) << kBlockShift) >> (2 * a.bshift)) == id;
+            }
+          wxb[bb * 16 * NCT + sl] = hit ? -INFINITY : cbias[sl];
+        }
+      }
+      wave_lds_sync();
+    }
+  }
 
   f32x4 acc_a[kQBlocks][4], acc_b[kQBlocks][4];
   float dpart[kQBlocks];
@@ -385,7 +427,8 @@ void bwd_query_kernel(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       const bf16* cb0 = ct + c * 4 * 16 * kStride;
-      tile(bbc, cb0, cb0 + 16 * kStride, cb0 + 32 * kStride, cb0 + 48 * kStride, cbias + 16 * c);
+      tile(bbc, cb0, cb0 + 16 * kStride, cb0 + 32 * kStride, cb0 + 48 * kStride,
+           (a.exclude ? wxb + bb * 16 * NCT : cbias) + 16 * c);
     }
     const float Dn = group4_sum(dpart[bb]);
     if (g == 0) a.dd[tok_base + pb * kBlock + n] = Dn;
@@ -421,7 +464,7 @@ void bwd_query_kernel(BwdArgs a) {
           dpq = mfma_bf16_k32(dh[bb][s2], lds_row8(cb0 + 32 * kStride, n, s2, g), dpq);
           dpq = mfma_bf16_k32(dh[bb][s2], lds_row8(cb0 + 48 * kStride, n, s2, g), dpq);
         }
-        const float bias = cbias[16 * c + n];
+        const float bias = (a.exclude ? wxb + bb * 16 * NCT : cbias)[16 * c + n];
         float pq[4], sv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -912,13 +955,14 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   a.enrich = coarse ? 1 : 0;
   a.coarse_levels = s.coarse_levels;
   a.lbias = s.coarse_lbias;
+  a.exclude = s.exclude_overlap && coarse;
   a.scale = s.scale;
   a.c2 = s.scale * kLog2e;
 
   const int n2 = s.n >> (2 * kBlockShift);
   const unsigned qblocks = (unsigned)(s.bh * n2 * kUnits);
   const int n_coarse = s.coarse_levels * s.topk;
-  const size_t qlds = bwd_query_lds_bytes(n_coarse);
+  const size_t qlds = bwd_query_lds_bytes(n_coarse, s.exclude_overlap && coarse);
   if (n_coarse == 0)
     LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<0>, dim3(qblocks), dim3(64 * kQWaves), qlds,
                 stream, a);

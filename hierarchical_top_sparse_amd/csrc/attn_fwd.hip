@@ -49,6 +49,7 @@ struct FwdArgs {
   int bshift;          // log2(B) of the coarse levels: 4 or 6
   int coarse_levels;   // coarse keys of levels 2 .. 1 + coarse_levels
   float lbias;         // log2-domain bias per level: log2(B) (weight B^l) or 0 (weight 1)
+  int exclude;         // 1: a coarse key over a key selected one level finer is dropped
   float c2;            // scale * log2(e)
 };
 
@@ -76,13 +77,16 @@ struct FwdCfg {
 __host__ __device__ constexpr int fwd_wave_lds_bytes(bool bf16) {
   return 2 * 16 * (bf16 ? kStrideBf16 * 2 : kStrideF32 * 4) + (int)sizeof(int) * 4 * kWavePicks;
 }
-static size_t fwd_lds_bytes(bool bf16, int n_coarse) {
+// ... then each slot's bias and key id, and with overlap exclusion per-block biases
+// [waves][4 blocks][ctiles * 16].
+static size_t fwd_lds_bytes(bool bf16, int n_coarse, bool exclude) {
   const int es = bf16 ? 2 : 4;
   const int stride = bf16 ? kStrideBf16 : kStrideF32;
   const int nb = bf16 ? 4 : 2;
   const int ctiles = (n_coarse + 15) / 16;
   return kFwdWaves * fwd_wave_lds_bytes(bf16) + (size_t)ctiles * nb * 16 * stride * es +
-         sizeof(float) * 16 * ctiles;
+         (sizeof(float) + sizeof(int)) * 16 * ctiles +
+         (exclude ? sizeof(float) * kFwdWaves * 4 * 16 * ctiles : 0);
 }
 
 template <bool BF16, int QB>   // QB: query blocks per wave (4, or 2 for K > 16)
@@ -119,6 +123,8 @@ void attn_fwd_kernel(FwdArgs a) {
   int* umask = uoff + kWavePicks;             // [64] blocks of the wave that picked U[u]
   T* ctile = (T*)(smem + kFwdWaves * fwd_wave_lds_bytes(BF16));
   float* cbias = (float*)(ctile + ctiles * C::NB * C::kTile);
+  int* cid = (int*)(cbias + 16 * ctiles);       // key id of each coarse slot (-1: none)
+  float* xbias = (float*)(cid + 16 * ctiles);   // with exclusion: [w][bb][slot] biases
 
   const uint32_t head_bytes = (uint32_t)a.n * C::kRowBytes;
   const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
@@ -157,12 +163,14 @@ void attn_fwd_kernel(FwdArgs a) {
     const int cslot = e >> 3, c8 = (e & 7) * 8;
     f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
     float bias = -INFINITY;
+    int cslot_id = -1;
     if (cslot < n_coarse) {
       const int l = 2 + cslot / K;
       const int nl = a.n >> (a.bshift * l);
       const int anc = (pb0 << kBlockShift) >> (a.bshift * l);   // the group's level-l ancestor
       const int id = a.sel[l - 1][((long)head * nl + anc) * K + (cslot - (l - 2) * K)];
       if (id >= 0 && id < nl) {
+        cslot_id = id;
         const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
         const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
         k0 = *(const f32x4*)kp;
@@ -170,6 +178,15 @@ void attn_fwd_kernel(FwdArgs a) {
         v0 = *(const f32x4*)vp;
         v1 = *(const f32x4*)(vp + 4);
         bias = a.lbias * (float)l;   // log2(B^l), or 0 for unit weights
+        if (a.exclude && l >= 3 && c8 == 0) {
+          // level >= 3: dropped for the whole group if it is the parent of one of the keys
+          // selected at level l - 1 for the group's level-(l-1) ancestor
+          const int nf = a.n >> (a.bshift * (l - 1));
+          const int ancf = (pb0 << kBlockShift) >> (a.bshift * (l - 1));
+          for (int i = 0; i < K; ++i)
+            if ((a.sel[l - 2][((long)head * nf + ancf) * K + i] >> a.bshift) == id)
+              bias = -INFINITY;
+        }
       }
     }
     T* base = ctile + (cslot >> 4) * C::NB * C::kTile + (cslot & 15) * C::kStride + c8;
@@ -187,7 +204,10 @@ void attn_fwd_kernel(FwdArgs a) {
       *(f32x4*)(base + C::kTile) = v0;
       *(f32x4*)(base + C::kTile + 4) = v1;
     }
-    if (c8 == 0) cbias[cslot] = bias;
+    if (c8 == 0) {
+      cbias[cslot] = bias;
+      cid[cslot] = cslot_id;
+    }
   }
 
   // ---- U: rank of each pick key among the wave's 64, distinct ids, owner masks
@@ -249,6 +269,28 @@ void attn_fwd_kernel(FwdArgs a) {
   };
   BlockLd fa = load_u(0), fb = load_u(1);
   __syncthreads();   // coarse tiles staged (the only workgroup barrier)
+
+  // with overlap exclusion, per-block biases: a level-2 slot is dropped for block bb if one of
+  // bb's fine picks lies in its span (the 16-token block j is in key (16 j) >> 2 log2(B))
+  const int cslots = 16 * ctiles;
+  float* wxb = xbias + w * QB * cslots;
+  if (a.exclude) {
+    for (int sl = lane; sl < cslots; sl += 64) {
+      const int id = cid[sl];
+      const bool lv2 = sl < K && id >= 0;
+#pragma unroll
+      for (int bb = 0; bb < QB; ++bb) {
+        bool hit = false;
+        if (lv2)
+          for (int i = 0; i < KF; ++i) {
+            const int kk = keys[PS * bb + i];
+            hit |= kk < kSentinel && (((kk >> 8) << kBlockShift) >> (2 * a.bshift)) == id;
+          }
+        wxb[bb * cslots + sl] = hit ? -INFINITY : cbias[sl];
+      }
+    }
+    wave_lds_sync();
+  }
 
   float m_run[QB], l_run[QB];   // running max (log2 domain) and this lane's partial sums
   f32x4 acc[QB][4];             // O^T of each block: lane (n, g) holds d = 16 t4 + 4g + i
@@ -374,10 +416,12 @@ void attn_fwd_kernel(FwdArgs a) {
   for (int ct = 0; ct < ctiles; ++ct) {
     const T* cb0 = ctile + ct * C::NB * C::kTile;
     for_blocks([&](auto bbc) {
+      constexpr int bb = decltype(bbc)::value;
+      const float* cb = (a.exclude ? wxb + bb * cslots : cbias) + 16 * ct;
       if constexpr (BF16)
-        tile(bbc, cb0, cb0 + C::kTile, cb0 + 2 * C::kTile, cb0 + 3 * C::kTile, cbias + 16 * ct);
+        tile(bbc, cb0, cb0 + C::kTile, cb0 + 2 * C::kTile, cb0 + 3 * C::kTile, cb);
       else
-        tile(bbc, cb0, nullptr, cb0 + C::kTile, nullptr, cbias + 16 * ct);
+        tile(bbc, cb0, nullptr, cb0 + C::kTile, nullptr, cb);
     });
   }
   for_blocks([&](auto bbc) {
@@ -432,9 +476,10 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const v
   a.bshift = s.bshift;
   a.coarse_levels = s.coarse_levels;
   a.lbias = s.coarse_lbias;
+  a.exclude = s.exclude_overlap && s.coarse_levels > 0;
   a.c2 = s.scale * kLog2e;
   const int n_coarse = s.coarse_levels * s.topk;
-  const size_t lds = fwd_lds_bytes(s.bf16, n_coarse);
+  const size_t lds = fwd_lds_bytes(s.bf16, n_coarse, s.exclude_overlap != 0);
   // one workgroup per level-2 group (N is a multiple of 16^2), two when K > 16
   const bool wide = s.fine_k > kWavePicks / 4;
   const unsigned blocks = (unsigned)((long)s.bh * (s.n >> (2 * kBlockShift)) * (wide ? 2 : 1));

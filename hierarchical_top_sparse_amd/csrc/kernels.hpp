@@ -35,6 +35,7 @@ struct Shape {
   float scale;   // softmax scale
   int bshift;    // log2(B): 4 (B = 16, 4x4 tiles) or 6 (B = 64, 8x8 tiles)
   int fine_k;    // picks per 16-token query block seen by the attention: K * B / 16
+  int exclude_overlap;   // 1: coarse keys over a finer selected key are dropped per block
   int n_level(int l) const { return n >> (bshift * l); }
 };
 

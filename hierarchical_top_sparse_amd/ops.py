@@ -27,7 +27,7 @@ __all__ = ["Problem", "make_problem", "llsa_forward", "llsa_backward", "llsa_bac
 def make_problem(q: torch.Tensor, height: int, width: int, levels: int, topk: int = 8,
                  enrich: bool = True, scale: float = 0.0, layout: int = LLSA_LAYOUT_RASTER,
                  enrich_levels: int = 0, coarse_unit_weight: bool = False,
-                 block: int = 16):
+                 block: int = 16, coarse_exclude_overlap: bool = False):
     b, h, n, d = q.shape
     if n != height * width:
         raise ValueError(f"token count {n} != height*width {height * width}")
@@ -37,7 +37,7 @@ def make_problem(q: torch.Tensor, height: int, width: int, levels: int, topk: in
     return Problem(batch=b, heads=h, height=height, width=width, levels=levels, topk=topk,
                    enrich=int(enrich), head_dim=d, scale=scale, dtype=dtype, layout=layout,
                    enrich_levels=enrich_levels, coarse_unit_weight=int(coarse_unit_weight),
-                   block=block)
+                   block=block, coarse_exclude_overlap=int(coarse_exclude_overlap))
 
 
 def reorder(p: Problem, x: torch.Tensor, inverse: bool = False) -> torch.Tensor:

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LLSA_ABI_VERSION 2
+#define LLSA_ABI_VERSION 3
 #define LLSA_MAX_LEVELS 6
 #define LLSA_MAX_TOPK 32
 
@@ -79,6 +79,9 @@ typedef struct {
                                  (the finest ones; clamped to L); 0 = all levels 2..L */
   int32_t coarse_unit_weight; /* 0: a coarse key of level l has weight B^l (logit bias
                                  l ln B); 1: weight 1 (no bias) */
+  int32_t coarse_exclude_overlap; /* 1: drop, per query block, a coarse key of level l that
+                                     is the parent of a key selected for it at level l-1
+                                     (a fine block for l = 2): no region counted twice */
 } llsa_problem;
 
 /* ABI version (LLSA_ABI_VERSION of the built library). */

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.llsa_abi_version() == abi.LLSA_ABI_VERSION == 2
+    assert L.llsa_abi_version() == abi.LLSA_ABI_VERSION == 3
     for code in range(8):
         assert L.llsa_status_str(code)
     assert L.llsa_status_str(99) == b"unknown status"
@@ -62,6 +62,8 @@ def _p(**kw):
     (dict(enrich_levels=-1), 2),
     (dict(coarse_unit_weight=2), 2),
     (dict(enrich_levels=5, coarse_unit_weight=1), 0),   # clamped to the L - 1 coarse levels
+    (dict(coarse_exclude_overlap=2), 2),
+    (dict(coarse_exclude_overlap=1), 0),
     (dict(head_dim=128), 4),
     (dict(block=256), 4),                   # a power of 4 but not implemented
     (dict(block=64, levels=1), 0),          # 8x8 tiles: 64 blocks of 64 tokens, K = 8

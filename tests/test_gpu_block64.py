@@ -130,6 +130,33 @@ def test_attn_bwd_block64_on_oracle_indices(h, w, levels, topk, enrich):
         assert_close(to64(got), ref_g, torch.bfloat16, name)
 
 
+def test_block64_overlap_exclusion_on_oracle_indices():
+    """B = 64 with overlap-excluded coarse keys (256x256, L = 2, K = 8)."""
+    h = w = 256
+    levels, topk = 2, 8
+    d, ref = _inputs(1, 2, h, w, torch.bfloat16, 75, grad=True)
+    p = ops.make_problem(d["q"], h, w, levels, topk, True, 0.0, RASTER, block=B,
+                         coarse_exclude_overlap=True)
+    sels = [_oracle_sel(ref, h, w, levels, topk, i) for i in range(2)]
+    att = _gpu_sel(p, sels, levels)
+    q, k, v, do = d["q"], d["k"], d["v"], d["do"]
+    kl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    vl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    _abi.llsa_pool(p, None, k, v, None, kl, vl)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, p.n), device=DEV)
+    _abi.llsa_attn_fwd(p, q, k, v, kl, vl, att, o, lse)
+    dq, dk, dv = ops.llsa_backward(p, q, k, v, dict(o=o, lse=lse, k_lv=kl, v_lv=vl, sel=att),
+                                   do)
+    res = orc.llsa_forward(ref["q"], ref["k"], ref["v"], h, w, B, levels, topk, True,
+                           sel_override=[sels], exclude_overlap=True)
+    assert_close(to64(o), res["o"], torch.bfloat16, "o")
+    want = orc.llsa_backward(ref["q"], ref["k"], ref["v"], ref["do"], h, w, B, levels, [sels],
+                             True, exclude_overlap=True)
+    for name, got, ref_g in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        assert_close(to64(got), ref_g, torch.bfloat16, name)
+
+
 def test_e2e_block64_px256_train():
     """The whole B = 64 path (L = 2, K = 8) at the 256x256 batch-2 training shape; two heads
     checked against the oracle on the GPU's selection."""

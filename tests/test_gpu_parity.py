@@ -260,18 +260,23 @@ def test_attn_bwd_on_oracle_indices(h, w, levels, topk, enrich, layout):
 
 
 
-@pytest.mark.parametrize("h,w,levels,topk,enrich_levels,unit_weight", [
-    (128, 256, 3, 8, 1, False),    # only level 2's coarse keys
-    (128, 256, 3, 8, 0, True),     # all coarse levels, weight 1
-    (512, 512, 4, 4, 2, True),     # levels 2..3 of 4, weight 1
-    (128, 128, 2, 8, 3, False),    # enrich_levels beyond L - 1 is clamped
+@pytest.mark.parametrize("h,w,levels,topk,enrich_levels,unit_weight,exclude", [
+    (128, 256, 3, 8, 1, False, False),    # only level 2's coarse keys
+    (128, 256, 3, 8, 0, True, False),     # all coarse levels, weight 1
+    (512, 512, 4, 4, 2, True, False),     # levels 2..3 of 4, weight 1
+    (128, 128, 2, 8, 3, False, False),    # enrich_levels beyond L - 1 is clamped
+    (128, 256, 3, 8, 0, False, True),     # overlap-excluded coarse keys
+    (256, 256, 3, 8, 0, False, True),
+    (128, 128, 2, 16, 0, True, True),     # exclusion with 16 picks and unit weights
+    (512, 512, 4, 4, 2, False, True),     # exclusion with levels 2..3 of 4
 ])
-def test_enrichment_variants_on_oracle_indices(h, w, levels, topk, enrich_levels, unit_weight):
+def test_enrichment_variants_on_oracle_indices(h, w, levels, topk, enrich_levels, unit_weight,
+                                               exclude):
     """Forward and backward of the enrichment variants against the oracle's variants, on the
     oracle's selection."""
     d, ref = _inputs(1, 2, h, w, torch.bfloat16, 43, grad=True)
     p = ops.make_problem(d["q"], h, w, levels, topk, True, 0.0, RASTER, enrich_levels,
-                         unit_weight)
+                         unit_weight, coarse_exclude_overlap=exclude)
     sels = [_oracle_sel(ref, h, w, levels, topk, 0, i) for i in range(2)]
     sel_t = [torch.from_numpy(np.stack([sels[i][l] for i in range(2)])[None].astype(np.int32))
              .to(DEV) for l in range(levels)]
@@ -284,7 +289,8 @@ def test_enrichment_variants_on_oracle_indices(h, w, levels, topk, enrich_levels
     _abi.llsa_attn_fwd(p, q, k, v, kl, vl, sel_t, o, lse)
     dq, dk, dv = ops.llsa_backward(p, q, k, v, dict(o=o, lse=lse, k_lv=kl, v_lv=vl, sel=sel_t),
                                    do)
-    kw = dict(enrich_levels=enrich_levels, coarse_weight=not unit_weight)
+    kw = dict(enrich_levels=enrich_levels, coarse_weight=not unit_weight,
+              exclude_overlap=exclude)
     res = orc.llsa_forward(ref["q"], ref["k"], ref["v"], h, w, 16, levels, topk, True,
                            sel_override=[sels], **kw)
     assert_close(to64(o), res["o"], torch.bfloat16, "o")
