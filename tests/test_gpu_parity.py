@@ -358,6 +358,43 @@ def test_e2e_px256_train_single_level_top32():
     _end_to_end("px256_train", [(0, 2), (1, 5)], backward=True, levels=1, topk=32)
 
 
+@pytest.mark.parametrize("h,w,levels,topk", [
+    (16, 16, 1, 1),     # the smallest problem: 256 tokens, one pick
+    (16, 16, 2, 1),     # a coarsest level of a single key
+    (4, 64, 2, 1),      # a side of one 4x4 tile
+    (64, 4, 1, 8),
+    (32, 32, 2, 4),     # K = n_L: every coarsest key is picked
+    (16, 16, 1, 16),    # K = n_1: every block is picked (dense attention, checked below)
+])
+def test_whole_path_small_and_degenerate(h, w, levels, topk):
+    """The whole path (selection, forward, transposes, backward) on the smallest and most
+    degenerate problems the contract allows, against the oracle on the GPU's selection."""
+    d, ref = _inputs(1, 2, h, w, torch.bfloat16, 61, grad=True)
+    p = _problem(d["q"], h, w, levels, topk)
+    fwd = ops.llsa_forward(p, d["q"], d["k"], d["v"])
+    grads = ops.llsa_backward(p, d["q"], d["k"], d["v"], fwd, d["do"])
+    torch.cuda.synchronize()
+    sel_np = [s.cpu().numpy().astype(np.int64) for s in fwd["sel"]]
+    q_lv = orc.pool_levels(orc.reorder(ref["q"], h, w), 16, levels)
+    k_lv = orc.pool_levels(orc.reorder(ref["k"], h, w), 16, levels)
+    check_selection(sel_np, q_lv, k_lv, topk, f"{h}x{w} L{levels} K{topk}")
+    sels = [[[s[0, i] for s in sel_np] for i in range(2)]]
+    res = orc.llsa_forward(ref["q"], ref["k"], ref["v"], h, w, 16, levels, topk, True,
+                           sel_override=sels)
+    assert_close(to64(fwd["o"]), res["o"], torch.bfloat16, "o")
+    assert_close(to64(fwd["lse"]), res["lse"], torch.bfloat16, "lse")
+    want = orc.llsa_backward(ref["q"], ref["k"], ref["v"], ref["do"], h, w, 16, levels, sels,
+                             True)
+    for name, got, ref_g in zip(("dq", "dk", "dv"), grads, want):
+        assert_close(to64(got), ref_g, torch.bfloat16, name)
+    if levels == 1 and topk * 16 == h * w:
+        for i in range(2):   # every key of the head attended: plain softmax attention
+            o_d, _ = orc.dense_attention_forward(*(orc.reorder(ref[t], h, w)[0, i]
+                                                   for t in ("q", "k", "v")))
+            got = orc.reorder(to64(fwd["o"]), h, w)[0, i]
+            assert_close(got, o_d, torch.bfloat16, f"dense-equivalent o head {i}")
+
+
 def test_deterministic_and_autograd():
     h = w = 128
     d, _ = _inputs(1, 2, h, w, torch.bfloat16, 51, grad=True)
