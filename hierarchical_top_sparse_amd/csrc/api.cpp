@@ -299,6 +299,15 @@ int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const
   if (coarse_levels(p) * p->topk > 32)
     return fail(LLSA_ERR_UNSUPPORTED, "backward supports at most 32 coarse keys per query "
                 "(coarse levels * topk = %d)", coarse_levels(p) * p->topk);
+  {
+    // its level-1 index transpose packs (key block, query block) into 32-bit codes
+    const unsigned long n1 = (unsigned long)p->height * p->width / 16;
+    int rb = 0;
+    while ((1UL << rb) < n1) ++rb;
+    if (((n1 + 1) << rb) > (1UL << 32))
+      return fail(LLSA_ERR_UNSUPPORTED, "the backward supports N <= 2^19 tokens per head "
+                  "(N = %lu)", n1 * 16);
+  }
   CHECK_PTR(q, "q");
   CHECK_PTR(k, "k");
   CHECK_PTR(v, "v");

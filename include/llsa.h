@@ -186,7 +186,8 @@ int32_t llsa_index_transpose(int32_t nmat, int32_t rows, int32_t cols, int32_t k
  * (layout p->layout).  csc_off/csc_rows: L pointers, level l from llsa_index_transpose of
  * sel[l-1] (rows = cols = n_l); levels >= 2 are read only if enrich.  bf16 only.
  * sel[0], csc_off[0], csc_rows[0]: level 1 as 16-token blocks (sel[0] as for llsa_attn_fwd;
- * its transpose has rows = cols = N/16 and k = topk * block / 16).
+ * its transpose has rows = cols = N/16 and k = topk * block / 16).  N <= 2^19 per head (the
+ * level-1 transpose's 32-bit codes); LLSA_ERR_UNSUPPORTED above.
  * ws: llsa_workspace_bytes(bwd) bytes of device memory.
  */
 int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const void* v,

@@ -233,8 +233,11 @@ def attention_forward(q, k, v, k_lv, v_lv, sel, block: int, enrich: bool = True,
 
 def attention_backward(q, k, v, k_lv, v_lv, sel, do, block: int, enrich: bool = True,
                        scale: float | None = None, enrich_levels: int = 0,
-                       coarse_weight: bool = True, exclude_overlap: bool = False):
-    """Per-head gradients (dq, dk, dv) in Morton order, given upstream dO.
+                       coarse_weight: bool = True, exclude_overlap: bool = False,
+                       blocks=None):
+    """Per-head gradients (dq, dk, dv) in Morton order, given upstream dO.  With `blocks`,
+    only those level-1 query blocks contribute: their dq rows are exact, and dk/dv hold the
+    sum of their contributions (exact for a key all of whose queries are in `blocks`).
 
     Softmax Jacobian per query: P_e = w_e exp(s_e) / Z, dP_e = dO.v_e,
     dS_e = P_e (dP_e - sum_f P_f dP_f); dq = scale * sum_e dS_e k_e;
@@ -251,7 +254,7 @@ def attention_backward(q, k, v, k_lv, v_lv, sel, do, block: int, enrich: bool = 
     dv = np.zeros_like(v)
     dk_lv = [np.zeros_like(x) for x in k_lv]
     dv_lv = [np.zeros_like(x) for x in v_lv]
-    for p in range(n // block):
+    for p in (range(n // block) if blocks is None else blocks):
         kk, vv, logw, ident = key_list(p, k, v, k_lv, v_lv, sel, block, enrich, enrich_levels,
                                        coarse_weight, exclude_overlap)
         rows = slice(p * block, (p + 1) * block)
@@ -271,7 +274,7 @@ def attention_backward(q, k, v, k_lv, v_lv, sel, do, block: int, enrich: bool = 
             else:
                 dk_lv[lvl - 1][idx] += gk[col]
                 dv_lv[lvl - 1][idx] += gv[col]
-    for l in range(2, levels + 1):
+    for l in range(2, levels + 1 if enrich else 2):   # coarse keys only with enrichment
         span = block ** l
         dk += np.repeat(dk_lv[l - 1], span, axis=0) / span
         dv += np.repeat(dv_lv[l - 1], span, axis=0) / span

@@ -178,3 +178,14 @@ def test_block64_pool_needs_level_one(L):
     assert b"level 1" in L.llsa_last_error()
     lv_bad = (ctypes.c_void_p * 6)(MISALIGNED, FAKE)
     assert L.llsa_pool(ctypes.byref(p.c()), None, f, None, None, lv_bad, None, None) == 6
+
+
+def test_backward_rejects_more_than_2_19_tokens(L):
+    """The level-1 transpose packs (key block, query block) in 32 bits: N <= 2^19 per head."""
+    f = ctypes.c_void_p(FAKE)
+    null6 = (ctypes.c_void_p * 6)()
+    big = _p(height=1024, width=1024, levels=3, dtype=abi.LLSA_BF16, enrich=0)
+    assert abi.llsa_check(big) == 0
+    st = L.llsa_attn_bwd(ctypes.byref(big.c()), *([f] * 5), null6, null6, null6, null6, null6,
+                         *([f] * 4), 1 << 30, None)
+    assert st == 4 and b"2^19" in L.llsa_last_error()

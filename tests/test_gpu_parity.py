@@ -412,3 +412,73 @@ def test_deterministic_and_autograd():
     assert torch.equal(_bits(fwd["o"]), _bits(outs[0][0]))
     for g, g2 in zip(grads, outs[0][1:]):
         assert torch.equal(_bits(g), _bits(g2))
+
+
+def _max_inputs(n, seed):
+    return {t: gen.to_dtype(gen.gaussian(seed + i, 1, 1, n, 64), torch.bfloat16)
+            for i, t in enumerate(("q", "k", "v", "do"))}
+
+
+def test_maximum_size_forward_sampled():
+    """The largest problem the contract allows per head: N = 2^23 tokens (2048 x 4096 pixels,
+    Morton layout, L = 4, K = 8, no enrichment).  Checked where the oracle can be computed
+    piecewise: the selection of sampled sibling groups at every level (teacher-forced, tie
+    window) and O and LSE of sampled query blocks, first and last included."""
+    h, w, L, K = 2048, 4096, 4, 8
+    n = h * w
+    x = _max_inputs(n, 9100)
+    d = {t: v.to(DEV) for t, v in x.items() if t != "do"}
+    p = _problem(d["q"], h, w, L, K, enrich=False, layout=MORTON)
+    fwd = ops.llsa_forward(p, d["q"], d["k"], d["v"])
+    torch.cuda.synchronize()
+    print("maximum size forward: GPU done", flush=True)
+    sel = [s[0, 0].cpu().numpy().astype(np.int64) for s in fwd["sel"]]
+    q, k, v = (x[t][0, 0].double().numpy() for t in ("q", "k", "v"))
+    q_lv, k_lv = orc.pool_levels(q, 16, L), orc.pool_levels(k, 16, L)
+    from tests.parity_util import check_level
+    rng = np.random.default_rng(5)
+    check_level(sel[L - 1], q_lv[L - 1], k_lv[L - 1], None, K, "level 4")
+    for l in range(L - 1, 0, -1):   # a few whole sibling groups per level
+        n_par = q_lv[l].shape[0]
+        for par in sorted({0, n_par - 1, *rng.integers(0, n_par, 3).tolist()}):
+            rows = slice(par * 16, par * 16 + 16)
+            check_level(sel[l - 1][rows], q_lv[l - 1][rows], k_lv[l - 1], sel[l][par:par + 1],
+                        K, f"level {l} parent {par}")
+    n1 = n // 16
+    qb = sorted({0, n1 - 1, *rng.integers(0, n1, 30).tolist()})
+    o_want, lse_want = orc.attention_forward(q, k, v, [], [], sel, 16, False, blocks=qb)
+    rows = np.concatenate([np.arange(b * 16, b * 16 + 16) for b in qb])
+    assert_close(fwd["o"][0, 0].double().cpu().numpy()[rows], o_want[rows], torch.bfloat16,
+                 "o (sampled blocks)")
+    assert_close(fwd["lse"][0, 0].double().cpu().numpy()[rows], lse_want[rows],
+                 torch.bfloat16, "lse (sampled blocks)")
+
+
+def test_maximum_size_backward_sampled():
+    """The largest backward: N = 2^19 tokens (512 x 1024 pixels; the level-1 transpose packs
+    (key block, query block) codes in 32 bits), L = 3, K = 8, no enrichment, Morton layout:
+    dQ of every query block that picked a sampled key block, and dK, dV of those key blocks
+    (exact: without enrichment a key block's gradient comes only from the query blocks that
+    picked it)."""
+    h, w, L, K = 512, 1024, 3, 8
+    n = h * w
+    x = _max_inputs(n, 9200)
+    d = {t: v.to(DEV) for t, v in x.items()}
+    p = _problem(d["q"], h, w, L, K, enrich=False, layout=MORTON)
+    fwd = ops.llsa_forward(p, d["q"], d["k"], d["v"])
+    dq, dk, dv = ops.llsa_backward(p, d["q"], d["k"], d["v"], fwd, d["do"])
+    torch.cuda.synchronize()
+    print("maximum size backward: GPU done", flush=True)
+    sel = [s[0, 0].cpu().numpy().astype(np.int64) for s in fwd["sel"]]
+    q, k, v, do = (x[t][0, 0].double().numpy() for t in ("q", "k", "v", "do"))
+    rng = np.random.default_rng(6)
+    n1 = n // 16
+    kb = sorted({0, n1 - 1, *rng.integers(0, n1, 14).tolist()})
+    users = sorted({int(a) for j in kb for a in np.nonzero((sel[0] == j).any(axis=1))[0]})
+    gq, gk, gv = orc.attention_backward(q, k, v, [], [], sel, do, 16, False, blocks=users)
+    qrows = np.concatenate([np.arange(b * 16, b * 16 + 16) for b in users])
+    krows = np.concatenate([np.arange(j * 16, j * 16 + 16) for j in kb])
+    for name, got, want, r in (("dq", dq, gq, qrows), ("dk", dk, gk, krows),
+                               ("dv", dv, gv, krows)):
+        assert_close(got[0, 0].double().cpu().numpy()[r], want[r], torch.bfloat16,
+                     f"{name} (sampled)")
