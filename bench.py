@@ -6,7 +6,9 @@ transpose of every level -> sparse backward (dQ, dK, dV); the Morton reorder is 
 the kernels' addressing (inputs and outputs stay in raster order).  The step is captured once
 into a HIP graph and replayed; `value` is batch*N tokens per second of graph replays.  A
 second, eager pass with per-kernel HIP events gives each kernel's launch duration; the
-roofline object is for the kernel with the largest total time.  Prints one JSON line.
+roofline object is for the kernel with the largest total time, against the vendor HBM peak
+and against the achievable peak the library's own streaming-copy kernel reaches
+(`extra.calibration`, with the MFMA-only loop's bf16 rate).  Prints one JSON line.
 
 Beside the headline, `extra` carries:
   * configs: every workload (forward only for the three forward configs, forward + backward
@@ -212,6 +214,32 @@ def measure(step, steps, warmup, graph=True, with_copy=None):
     else:
         ms_step = _event_ms(step.run, steps)
     return ms_step, eager_ms, per_call, per_kernel_ms, per_step_kernel_ms
+
+
+def calibration(reps=10):
+    """Achievable peaks from the library's calibration kernels: a plain streaming copy of
+    2 GiB (read + write bytes over time) and an MFMA-only loop of v_mfma_f32_16x16x32_bf16
+    (16 waves per CU, 8 independent chains each)."""
+    import torch
+
+    from hierarchical_top_sparse_amd import _abi
+    nbytes = 2 ** 31
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    copy = lambda: _abi.llsa_calib_copy(src, dst)   # noqa: E731
+    copy()
+    copy_ms = _event_ms(copy, reps)
+    blocks, iters = 4096, 512
+    out = torch.empty(blocks * 256, device="cuda")
+    mfma = lambda: _abi.llsa_calib_mfma(out, blocks, iters)   # noqa: E731
+    mfma()
+    mfma_ms = _event_ms(mfma, reps)
+    flops = blocks * 4 * iters * 8 * 2 * 16 * 16 * 32
+    del src, dst, out
+    return {"copy_bytes": nbytes, "copy_ms": round(copy_ms, 4),
+            "copy_GBps": round(2 * nbytes / (copy_ms / 1e3) / 1e9, 1),
+            "mfma_bf16_TFLOPs": round(flops / (mfma_ms / 1e3) / 1e12, 1)}
 
 
 def kernel_fractions(p, per_kernel_ms):
@@ -512,7 +540,11 @@ def main():
                 "launch_ms": round(launch_ms, 4),
                 "mfma_frac": round(model[dominant]["flops"] / (launch_ms / 1e3) / 1e12 /
                                    BF16_MFMA_PEAK_TFLOPS, 4)}
+    calib = calibration()
+    roofline["achievable_peak"] = calib["copy_GBps"]
+    roofline["frac_of_achievable"] = round(achieved / calib["copy_GBps"], 4)
     extra = {"graph": not args.no_graph, "eager_ms_per_step": round(eager_ms, 4),
+             "calibration": calib,
              "per_call_ms": {k2: round(v2, 4) for k2, v2 in per_call.items()},
              "per_kernel_ms_per_step": {k2: round(v2, 4) for k2, v2 in
                                         sorted(per_step_kernel_ms.items(),

@@ -126,6 +126,8 @@ def lib() -> ctypes.CDLL:
             "llsa_dense_attn_bwd": ([i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, vp], i32),
             "llsa_block_mask": ([P, vp, vp, vp], i32),
+            "llsa_calib_copy": ([vp, vp, sz, vp], i32),
+            "llsa_calib_mfma": ([vp, i32, i32, vp], i32),
             "llsa_expand_blocks": ([P, vp, vp, vp], i32),
             "llsa_attn_bwd_masked": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
                                      i32),
@@ -145,7 +147,8 @@ def exported_symbols() -> list:
             "llsa_workspace_bytes", "llsa_reorder", "llsa_pool", "llsa_select", "llsa_attn_fwd",
             "llsa_index_transpose_workspace", "llsa_index_transpose", "llsa_attn_bwd",
             "llsa_dense_attn_fwd", "llsa_dense_attn_bwd", "llsa_block_mask", "llsa_expand_blocks",
-            "llsa_attn_bwd_masked", "llsa_profile_enable", "llsa_profile_read"]
+            "llsa_attn_bwd_masked", "llsa_calib_copy", "llsa_calib_mfma", "llsa_profile_enable",
+            "llsa_profile_read"]
 
 
 def _raise(status: int, name: str):
@@ -380,6 +383,23 @@ def llsa_dense_attn_bwd(q, k, v, dout, lse, dq, dk, dv, d_rows, scale=0.0, strea
     _raise(lib().llsa_dense_attn_bwd(bh, n, d, float(scale), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                      _ptr(d_rows), _stream(stream)), "llsa_dense_attn_bwd")
+
+
+def llsa_calib_copy(src, dst, stream=None):
+    """Plain streaming copy of a contiguous tensor into another of the same size."""
+    if src.numel() * src.element_size() != dst.numel() * dst.element_size():
+        raise ValueError("src and dst must have the same size in bytes")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    _raise(lib().llsa_calib_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
+                                 _stream(stream)), "llsa_calib_copy")
+
+
+def llsa_calib_mfma(out, blocks: int, iters: int, stream=None):
+    """MFMA-only loop; out: fp32 [blocks * 256]."""
+    _expect(out, (blocks * 256,), torch.float32, "out")
+    _raise(lib().llsa_calib_mfma(_ptr(out), int(blocks), int(iters), _stream(stream)),
+           "llsa_calib_mfma")
 
 
 def llsa_profile_enable(on: bool):

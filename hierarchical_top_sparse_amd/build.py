@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libllsa.so")
 SOURCES = ["api.cpp", "profile.cpp", "reorder.hip", "pool.hip", "select.hip", "attn_fwd.hip",
-           "transpose.hip", "attn_bwd.hip", "mask.hip", "dense_attn.hip"]
+           "transpose.hip", "attn_bwd.hip", "mask.hip", "dense_attn.hip", "calib.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

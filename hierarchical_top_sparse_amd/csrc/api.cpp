@@ -365,6 +365,25 @@ int32_t check_masked(const llsa_problem* p) {
 
 extern "C" {
 
+int32_t llsa_calib_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  CHECK_PTR(src, "src");
+  CHECK_PTR(dst, "dst");
+  if (bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 40))
+    return fail(LLSA_ERR_SHAPE, "bytes = %zu: a nonzero multiple of 16 up to 2^40 is needed",
+                bytes);
+  if (src == dst) return fail(LLSA_ERR_SHAPE, "the copy cannot run in place");
+  return hip_status(llsa::launch_calib_copy(src, dst, bytes, (hipStream_t)stream),
+                    "llsa_calib_copy");
+}
+
+int32_t llsa_calib_mfma(float* out, int32_t blocks, int32_t iters, void* stream) {
+  CHECK_PTR(out, "out");
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 16))
+    return fail(LLSA_ERR_SHAPE, "blocks in [1, 2^20] and iters in [1, 2^16] are needed");
+  return hip_status(llsa::launch_calib_mfma(out, blocks, iters, (hipStream_t)stream),
+                    "llsa_calib_mfma");
+}
+
 int32_t llsa_block_mask(const llsa_problem* p, const int32_t* sel1, uint8_t* mask,
                         void* stream) {
   int32_t st = check_masked(p);

@@ -69,6 +69,11 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
 hipError_t launch_expand_blocks(const Shape& s, const int32_t* sel1, int32_t* fine,
                                 hipStream_t stream);
 
+// Calibration: a plain copy of `bytes` (a multiple of 16) and an MFMA-only loop of `blocks`
+// 4-wave workgroups, `iters` rounds of 8 chains of 16x16x32 bf16 each (out: blocks * 256).
+hipError_t launch_calib_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_calib_mfma(float* out, int blocks, int iters, hipStream_t stream);
+
 // Dense block mask [bh, n_1, n_1] (1 where key block c is in Sel_1[a]) of the mask-based
 // comparator.
 hipError_t launch_block_mask(const Shape& s, const int32_t* sel1, uint8_t* mask,

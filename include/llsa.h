@@ -242,6 +242,19 @@ int32_t llsa_attn_bwd_masked(const llsa_problem* p, const void* q, const void* k
                              size_t ws_bytes, void* stream);
 
 /*
+ * llsa_calib_copy / llsa_calib_mfma — calibration kernels for the achievable peaks (not part
+ * of the method).  llsa_calib_copy copies `bytes` (a nonzero multiple of 16, at most 2^40)
+ * from src to dst (device, 16-byte aligned, not overlapping) with 16-byte vector loads and
+ * stores: (2 * bytes) / time is the reachable HBM bandwidth.  llsa_calib_mfma runs `blocks`
+ * workgroups of 4 waves (1 <= blocks <= 2^20), each wave `iters` rounds (1..2^16) of 8
+ * independent v_mfma_f32_16x16x32_bf16 on constant all-ones operands, and writes
+ * out[blocks * 256] = 8 * 32 * iters per thread (a check that the work was done): the
+ * dense bf16 MFMA rate is blocks * 4 * iters * 8 * 16384 flops / time.
+ */
+int32_t llsa_calib_copy(const void* src, void* dst, size_t bytes, void* stream);
+int32_t llsa_calib_mfma(float* out, int32_t blocks, int32_t iters, void* stream);
+
+/*
  * Per-kernel timing (profiling aid, not part of the method).  llsa_profile_enable(1) makes
  * every later kernel launch of the library record a pair of hipEvents on its stream;
  * llsa_profile_read() waits for the recorded events, writes one line per kernel name,

@@ -189,3 +189,14 @@ def test_backward_rejects_more_than_2_19_tokens(L):
     st = L.llsa_attn_bwd(ctypes.byref(big.c()), *([f] * 5), null6, null6, null6, null6, null6,
                          *([f] * 4), 1 << 30, None)
     assert st == 4 and b"2^19" in L.llsa_last_error()
+
+
+def test_calibration_validation(L):
+    f = ctypes.c_void_p(FAKE)
+    assert L.llsa_calib_copy(f, ctypes.c_void_p(FAKE + 4096), 0, None) == 2
+    assert L.llsa_calib_copy(f, ctypes.c_void_p(FAKE + 4096), 24, None) == 2
+    assert L.llsa_calib_copy(None, f, 64, None) == 1
+    assert L.llsa_calib_copy(f, f, 64, None) == 2
+    assert L.llsa_calib_mfma(f, 0, 16, None) == 2
+    assert L.llsa_calib_mfma(f, 4, 0, None) == 2
+    assert L.llsa_calib_mfma(None, 4, 16, None) == 1
