@@ -48,6 +48,14 @@ struct BwdArgs {
   float* dk_lv[kMaxLv];        // level l >= 2: [bh, n_l, 64]
   float* dv_lv[kMaxLv];
   const uint8_t* mask;         // block mask [bh, n_1, n_1] (mask-scanning key pass only)
+  // key blocks with more than kKeyChunk CSC_1 entries: their entries beyond the first chunk go
+  // to overflow chunks, each one wave of its own, whose partial sums the key block adds
+  int32_t* ov_start;           // [bh, n_1] first overflow chunk of key block j
+  int32_t* ov_count;           // [bh, n_1] overflow chunks of key block j
+  int32_t* ov_table;           // [bh, ov_cap] chunk t: (key block << 16) | chunk index m >= 1
+  int32_t* ov_total;           // [bh] overflow chunks of the head
+  float* ov_part;              // [bh, ov_cap, 64 lanes, 32]: raw dK, dV sums of a chunk
+  int ov_cap;                  // overflow chunks per head the buffers hold
   int bh;
   int n;
   Grid grid;
@@ -652,14 +660,59 @@ __global__ __launch_bounds__(64 * kCgWaves) void coarse_grad_kernel(BwdArgs a,
 
 // ====================================================================== stage 3: key-major
 // One wave per workgroup: key blocks differ widely in how many query blocks picked them, so a
-// wave that finishes early frees its slot at once.
-// MASK: the comparator of a mask-based backward -- the query blocks of key block j are found
-// by scanning column j of the dense block mask (all n_1 query blocks) instead of reading
-// CSC_1[j].  The scan yields them in ascending order, the order of the CSC rows, and they are
-// processed in the same batches of 64, so both variants give bit-identical dK and dV.
-template <bool MASK>
+// wave that finishes early frees its slot at once.  A key block takes at most kKeyChunk CSC_1
+// entries itself; the rest of a popular block (a block every query block picks, as a key
+// with a large norm becomes under random weights) is cut into chunks of kKeyChunk that
+// overflow waves run beforehand, each writing raw partial sums that the key block's wave adds
+// in chunk order: the work stays balanced and the result deterministic.
+// Modes:
+//  * kKeyCsc: the key block's first chunk of CSC_1[j], plus its overflow partials, then store;
+//  * kKeyOverflow: one overflow chunk (from the plan), partial sums only;
+//  * kKeyMask: the comparator of a mask-based backward -- the query blocks of key block j are
+//    found by scanning column j of the dense block mask (all n_1 query blocks) instead of
+//    reading CSC_1[j]; the scan yields them in ascending order, the order of the CSC rows, and
+//    they are processed in the same batches of 64 (no chunking), so both variants give
+//    bit-identical dK and dV when no key block has more than kKeyChunk picks.
+constexpr int kKeyChunk = 128;
+constexpr int kKeyCsc = 0, kKeyMask = 1, kKeyOverflow = 2;
+
+// Overflow plan, one 256-thread workgroup per head: a key block with c > kKeyChunk entries has
+// (c - 1) / kKeyChunk overflow chunks; an exclusive scan over the blocks numbers them.
+__global__ __launch_bounds__(256) void key_plan_kernel(BwdArgs a) {
+  __shared__ int part[256];
+  const int head = blockIdx.x;
+  const int t = threadIdx.x;
+  const int n1 = a.n >> kBlockShift;
+  const int32_t* off = a.csc_off[0] + (long)head * (n1 + 1);
+  const int per = (n1 + 255) / 256;
+  const int c0 = min(n1, t * per), c1 = min(n1, c0 + per);
+  int sum = 0;
+  for (int c = c0; c < c1; ++c) {
+    const int cnt = off[c + 1] - off[c];
+    sum += cnt > 0 ? (cnt - 1) / kKeyChunk : 0;
+  }
+  part[t] = sum;
+  __syncthreads();
+  int start = 0;   // exclusive prefix over the threads before t
+  for (int u = 0; u < t; ++u) start += part[u];
+  int32_t* ovs = a.ov_start + (long)head * n1;
+  int32_t* ovc = a.ov_count + (long)head * n1;
+  int32_t* tab = a.ov_table + (long)head * a.ov_cap;
+  for (int c = c0; c < c1; ++c) {
+    const int cnt = off[c + 1] - off[c];
+    const int ov = cnt > 0 ? (cnt - 1) / kKeyChunk : 0;
+    ovs[c] = start;
+    ovc[c] = ov;
+    for (int m = 1; m <= ov; ++m) tab[start + m - 1] = (c << 16) | m;
+    start += ov;
+  }
+  if (t == 255) a.ov_total[head] = start;
+}
+
+template <int MODE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_kernel(
     BwdArgs a) {
+  constexpr bool MASK = MODE == kKeyMask;
   __shared__ __attribute__((aligned(16))) bf16 stQ[32 * kStride];
   __shared__ __attribute__((aligned(16))) bf16 stO[32 * kStride];   // dO rows
   __shared__ __attribute__((aligned(16))) float pdown[2 * kDim];    // pushed-down dK, dV
@@ -670,14 +723,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
   const int g = lane >> 4;
   const int n1 = a.n >> kBlockShift;
   const int kb = uniform(xcd_block(blockIdx.x, gridDim.x));
-  const int head = uniform(kb / n1);
-  const int j = uniform(kb - head * n1);
+  int head, j, chunk = 0, ov_t = 0;
+  if constexpr (MODE == kKeyOverflow) {
+    head = uniform(kb / a.ov_cap);
+    ov_t = uniform(kb - head * a.ov_cap);
+    if (ov_t >= a.ov_total[head]) return;
+    const int packed = uniform(a.ov_table[(long)head * a.ov_cap + ov_t]);
+    j = packed >> 16;
+    chunk = packed & 0xffff;
+  } else {
+    head = uniform(kb / n1);
+    j = uniform(kb - head * n1);
+  }
   const long tok_base = (long)head * a.n;
 
   // pooled-key gradients pushed down to this block (lane = channel), loaded first so that
   // they arrive during the CSC lookups instead of after the pair loop
   float pk_sum = 0.f, pv_sum = 0.f;
-  if (a.enrich) {
+  if (MODE != kKeyOverflow && a.enrich) {
     for (int l = 2; l <= 1 + a.coarse_levels; ++l) {
       const int nl = a.n >> (a.bshift * l);
       const int anc = (j << kBlockShift) >> (a.bshift * l);
@@ -823,10 +886,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     }
   };
   if constexpr (!MASK) {
+    // this wave's chunk of CSC_1[j]: entries [chunk, chunk + 1) * kKeyChunk
     const int32_t* off = a.csc_off[0] + (long)head * (n1 + 1);
     const int32_t* rows = a.csc_rows[0] + (long)head * n1 * a.fine_k;
-    const int e0 = uniform(off[j]);
-    const int e1 = uniform(off[j + 1]);
+    const int e0 = uniform(off[j] + chunk * kKeyChunk);
+    const int e1 = uniform(min(off[j + 1], e0 + kKeyChunk));
     for (int base = e0; base < e1; base += 64) {
       const int count = min(64, e1 - base);
       batch(count, lane < count ? rows[base + lane] : -1);
@@ -858,6 +922,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     }
   }
 
+  if constexpr (MODE == kKeyOverflow) {   // raw partial sums, lane-major
+    float* dst = a.ov_part + (((long)head * a.ov_cap + ov_t) * 64 + lane) * 32;
+#pragma unroll
+    for (int t4 = 0; t4 < 4; ++t4) {
+      *(f32x4*)(dst + 4 * t4) = dka[t4];
+      *(f32x4*)(dst + 16 + 4 * t4) = dva[t4];
+    }
+    return;
+  }
+  if constexpr (MODE == kKeyCsc) {   // the overflow chunks' partial sums, in chunk order
+    const int ovc = uniform(a.ov_count[(long)head * n1 + j]);
+    const int ovs = uniform(a.ov_start[(long)head * n1 + j]);
+    for (int m = 0; m < ovc; ++m) {
+      const float* src = a.ov_part + (((long)head * a.ov_cap + ovs + m) * 64 + lane) * 32;
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        dka[t4] += *(const f32x4*)(src + 4 * t4);
+        dva[t4] += *(const f32x4*)(src + 16 + 4 * t4);
+      }
+    }
+  }
+
   // ---- push-down of pooled-key gradients and store (lane holds key n, channels 16t4+4g+i)
   pdown[lane] = pk_sum;
   pdown[kDim + lane] = pv_sum;
@@ -881,8 +967,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
 
 // ====================================================================== host side
 struct BwdLayout {
-  size_t dd, part_k, part_v, dk_lv[kMaxLv], dv_lv[kMaxLv], total;
+  size_t dd, part_k, part_v, dk_lv[kMaxLv], dv_lv[kMaxLv];
+  size_t ov_start, ov_count, ov_table, ov_total, ov_part;
+  int ov_cap;
+  size_t total;
 };
+
+// Overflow chunks per head never exceed (N/16) * fine_k / kKeyChunk: a block with c entries
+// has floor((c - 1) / kKeyChunk) of them and the entries sum to (N/16) * fine_k.
+static int key_overflow_cap(const Shape& s) {
+  return std::max(1, (int)(((long)(s.n >> kBlockShift) * s.fine_k) / kKeyChunk));
+}
 
 static BwdLayout bwd_layout(const Shape& s) {
   BwdLayout L{};
@@ -904,6 +999,13 @@ static BwdLayout bwd_layout(const Shape& s) {
       L.dv_lv[l - 1] = take(sizeof(float) * s.bh * nl * kDim);
     }
   }
+  const size_t n1 = (size_t)s.n >> kBlockShift;
+  L.ov_cap = key_overflow_cap(s);
+  L.ov_start = take(sizeof(int32_t) * s.bh * n1);
+  L.ov_count = take(sizeof(int32_t) * s.bh * n1);
+  L.ov_table = take(sizeof(int32_t) * s.bh * (size_t)L.ov_cap);
+  L.ov_total = take(sizeof(int32_t) * s.bh);
+  L.ov_part = take(sizeof(float) * s.bh * (size_t)L.ov_cap * 64 * 32);
   L.total = off;
   return L;
 }
@@ -935,6 +1037,12 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   a.dk = (bf16*)dk;
   a.dv = (bf16*)dv;
   a.dd = (float*)(base + L.dd);
+  a.ov_start = (int32_t*)(base + L.ov_start);
+  a.ov_count = (int32_t*)(base + L.ov_count);
+  a.ov_table = (int32_t*)(base + L.ov_table);
+  a.ov_total = (int32_t*)(base + L.ov_total);
+  a.ov_part = (float*)(base + L.ov_part);
+  a.ov_cap = L.ov_cap;
   const bool coarse = s.coarse_levels > 0;
   const int top = 1 + s.coarse_levels;   // the coarsest level with coarse keys
   if (coarse) {
@@ -959,6 +1067,12 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   a.scale = s.scale;
   a.c2 = s.scale * kLog2e;
 
+  if (!mask) {   // overflow plan of the key-major pass (reads CSC_1 offsets only)
+    LLSA_LAUNCH("key_plan_kernel", key_plan_kernel, dim3((unsigned)s.bh), dim3(256), 0, stream,
+                a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const int n2 = s.n >> (2 * kBlockShift);
   const unsigned qblocks = (unsigned)(s.bh * n2 * kUnits);
   const int n_coarse = s.coarse_levels * s.topk;
@@ -990,10 +1104,13 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   const long kwaves = (long)s.bh * (s.n >> kBlockShift);
   if (mask) {
     a.mask = mask;
-    LLSA_LAUNCH("bwd_key_mask_kernel", bwd_key_kernel<true>, dim3((unsigned)kwaves), dim3(64),
-                0, stream, a);
+    LLSA_LAUNCH("bwd_key_mask_kernel", bwd_key_kernel<kKeyMask>, dim3((unsigned)kwaves),
+                dim3(64), 0, stream, a);
   } else {
-    LLSA_LAUNCH("bwd_key_kernel", bwd_key_kernel<false>, dim3((unsigned)kwaves), dim3(64), 0,
+    LLSA_LAUNCH("bwd_key_overflow_kernel", bwd_key_kernel<kKeyOverflow>,
+                dim3((unsigned)((long)s.bh * a.ov_cap)), dim3(64), 0, stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    LLSA_LAUNCH("bwd_key_kernel", bwd_key_kernel<kKeyCsc>, dim3((unsigned)kwaves), dim3(64), 0,
                 stream, a);
   }
   return hipGetLastError();

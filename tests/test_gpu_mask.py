@@ -37,7 +37,7 @@ def _run(batch, heads, h, w, levels, topk, enrich, seed):
     (1, 2, 128, 256, 2, 8, False, 63),     # levels 2 without coarse keys; n_1 not a power of 4
     (2, 6, 256, 256, 1, 32, True, 64),     # the 256x256 training shape, single level
 ])
-def test_masked_backward_bit_identical_to_csc(batch, heads, h, w, levels, topk, enrich, seed):
+def test_masked_backward_matches_csc(batch, heads, h, w, levels, topk, enrich, seed):
     _, p, fwd, (dq, dk, dv), (mq, mk, mv, mask) = _run(batch, heads, h, w, levels, topk, enrich,
                                                        seed)
     sel = fwd["sel"][0].cpu().numpy()
@@ -46,8 +46,17 @@ def test_masked_backward_bit_identical_to_csc(batch, heads, h, w, levels, topk, 
     bi, hi, ai, _ = np.indices(sel.shape)
     want[bi, hi, ai, sel] = 1
     assert np.array_equal(mask.cpu().numpy(), want)
-    for name, a, b in (("dq", dq, mq), ("dk", dk, mk), ("dv", dv, mv)):
-        assert torch.equal(_bits(a), _bits(b)), name
+    assert torch.equal(_bits(dq), _bits(mq)), "dq"
+    # the CSC pass cuts key blocks with more than 128 picks into chunks (partial sums added in
+    # chunk order); the mask scan runs each block in one wave: bit-identical below that count
+    counts = np.bincount(sel.reshape(-1) + n1 * np.repeat(np.arange(batch * heads),
+                                                          sel.shape[2] * topk),
+                         minlength=batch * heads * n1)
+    for name, a, b in (("dk", dk, mk), ("dv", dv, mv)):
+        if counts.max() <= 128:
+            assert torch.equal(_bits(a), _bits(b)), name
+        else:
+            assert_close(to64(a), to64(b), torch.bfloat16, name)
 
 
 def test_masked_backward_matches_oracle():

@@ -260,6 +260,41 @@ def test_attn_bwd_on_oracle_indices(h, w, levels, topk, enrich, layout):
 
 
 
+@pytest.mark.parametrize("h,w,levels,topk,enrich,popular", [
+    (128, 128, 1, 8, False, 1.0),    # every query block picks blocks 0..7: 1024 picks each
+    (128, 128, 2, 8, True, 0.5),     # half the query blocks do, the rest pick their own
+    (64, 128, 1, 16, False, 0.9),
+])
+def test_attn_bwd_popular_key_blocks(h, w, levels, topk, enrich, popular):
+    """Backward on selections where a few key blocks are picked by (nearly) every query block,
+    the skew of attention to a few large-norm keys: the key-major pass cuts those blocks into
+    chunks of 128 picks run by separate waves and adds their partial sums in chunk order."""
+    d, ref = _inputs(1, 2, h, w, torch.bfloat16, 47, grad=True)
+    p = _problem(d["q"], h, w, levels, topk, enrich)
+    sels = [_oracle_sel(ref, h, w, levels, topk, 0, i) for i in range(2)]
+    rng = np.random.default_rng(3)
+    for i in range(2):
+        s1 = sels[i][0].copy()
+        hot = rng.random(s1.shape[0]) < popular
+        s1[hot] = np.arange(topk)          # the same key blocks for the popular rows
+        sels[i][0] = s1
+    sel_t = [torch.from_numpy(np.stack([sels[i][l] for i in range(2)])[None].astype(np.int32))
+             .to(DEV) for l in range(levels)]
+    q, k, v, do = d["q"], d["k"], d["v"], d["do"]
+    kl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    vl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    _abi.llsa_pool(p, None, k, v, None, kl, vl)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, p.n), device=DEV)
+    _abi.llsa_attn_fwd(p, q, k, v, kl, vl, sel_t, o, lse)
+    dq, dk, dv = ops.llsa_backward(p, q, k, v, dict(o=o, lse=lse, k_lv=kl, v_lv=vl, sel=sel_t),
+                                   do)
+    want = orc.llsa_backward(ref["q"], ref["k"], ref["v"], ref["do"], h, w, 16, levels, [sels],
+                             enrich)
+    for name, got, ref_g in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        assert_close(to64(got), ref_g, torch.bfloat16, name)
+
+
 @pytest.mark.parametrize("h,w,levels,topk,enrich_levels,unit_weight,exclude", [
     (128, 256, 3, 8, 1, False, False),    # only level 2's coarse keys
     (128, 256, 3, 8, 0, True, False),     # all coarse levels, weight 1
