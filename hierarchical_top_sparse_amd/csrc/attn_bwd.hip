@@ -56,6 +56,9 @@ struct BwdArgs {
   int32_t* ov_total;           // [bh] overflow chunks of the head
   float* ov_part;              // [bh, ov_cap, 64 lanes, 32]: raw dK, dV sums of a chunk
   int ov_cap;                  // overflow chunks per head the buffers hold
+  int ov_waves;                // overflow waves per head: wave g runs chunks g, g + ov_waves, ..
+  int plan_blocks;             // leading workgroups of the query-major launch that run the
+                               // overflow plan (one per head, padded to a multiple of 8), or 0
   int bh;
   int n;
   Grid grid;
@@ -149,6 +152,8 @@ __device__ __forceinline__ void split4(const float (&x)[4], bf16x4& hi, bf16x4& 
   split4_bf16(x[0], x[1], x[2], x[3], hi, lo);
 }
 
+__device__ void key_plan(const BwdArgs& a, int head, int* wsum);   // stage 3's plan
+
 template <int NCT>   // coarse tiles of 16 slots: 0, 1 or 2
 __global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_query_kernel(BwdArgs a) {
@@ -161,7 +166,12 @@ void bwd_query_kernel(BwdArgs a) {
   const int r4 = (lane & 15) >> 2, c4 = lane & 3;   // transposed-read lane roles
   const int n1 = a.n >> kBlockShift;
   const int n2 = n1 >> kBlockShift;
-  const int unit = uniform(xcd_block(blockIdx.x, gridDim.x));
+  if ((int)blockIdx.x < a.plan_blocks) {   // leading workgroups: the key-major overflow plan
+    if ((int)blockIdx.x < a.bh) key_plan(a, blockIdx.x, (int*)smem);
+    return;
+  }
+  const int unit =
+      uniform(xcd_block(blockIdx.x - a.plan_blocks, gridDim.x - a.plan_blocks));
   const int head = uniform(unit / (kUnits * n2));
   const int rem = uniform(unit - head * kUnits * n2);
   const int a2 = rem / kUnits;
@@ -667,7 +677,8 @@ __global__ __launch_bounds__(64 * kCgWaves) void coarse_grad_kernel(BwdArgs a,
 // in chunk order: the work stays balanced and the result deterministic.
 // Modes:
 //  * kKeyCsc: the key block's first chunk of CSC_1[j], plus its overflow partials, then store;
-//  * kKeyOverflow: one overflow chunk (from the plan), partial sums only;
+//  * kKeyOverflow: overflow chunks (numbered by the plan), partial sums only; a head's
+//    kOvWaves waves take its chunks in turn, so an empty plan costs one short launch;
 //  * kKeyMask: the comparator of a mask-based backward -- the query blocks of key block j are
 //    found by scanning column j of the dense block mask (all n_1 query blocks) instead of
 //    reading CSC_1[j]; the scan yields them in ascending order, the order of the CSC rows, and
@@ -675,66 +686,60 @@ __global__ __launch_bounds__(64 * kCgWaves) void coarse_grad_kernel(BwdArgs a,
 //    bit-identical dK and dV when no key block has more than kKeyChunk picks.
 constexpr int kKeyChunk = 128;
 constexpr int kKeyCsc = 0, kKeyMask = 1, kKeyOverflow = 2;
+constexpr int kOvWaves = 64;   // overflow waves per head (each loops over chunks)
 
-// Overflow plan, one 256-thread workgroup per head: a key block with c > kKeyChunk entries has
-// (c - 1) / kKeyChunk overflow chunks; an exclusive scan over the blocks numbers them.
-__global__ __launch_bounds__(256) void key_plan_kernel(BwdArgs a) {
-  __shared__ int part[256];
-  const int head = blockIdx.x;
-  const int t = threadIdx.x;
+// Overflow plan of one head, run by one 256-thread workgroup: a key block with c > kKeyChunk
+// entries has (c - 1) / kKeyChunk overflow chunks, numbered by an exclusive scan over the key
+// blocks.  Rounds of 256 blocks (thread t takes block 256 r + t, coalesced), each scanned with
+// wave shuffles plus four wave totals in LDS; the next round's offsets load during the scan.
+__device__ void key_plan(const BwdArgs& a, int head, int* wsum) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int n1 = a.n >> kBlockShift;
   const int32_t* off = a.csc_off[0] + (long)head * (n1 + 1);
-  const int per = (n1 + 255) / 256;
-  const int c0 = min(n1, t * per), c1 = min(n1, c0 + per);
-  int sum = 0;
-  for (int c = c0; c < c1; ++c) {
-    const int cnt = off[c + 1] - off[c];
-    sum += cnt > 0 ? (cnt - 1) / kKeyChunk : 0;
-  }
-  part[t] = sum;
-  __syncthreads();
-  int start = 0;   // exclusive prefix over the threads before t
-  for (int u = 0; u < t; ++u) start += part[u];
   int32_t* ovs = a.ov_start + (long)head * n1;
   int32_t* ovc = a.ov_count + (long)head * n1;
   int32_t* tab = a.ov_table + (long)head * a.ov_cap;
-  for (int c = c0; c < c1; ++c) {
-    const int cnt = off[c + 1] - off[c];
+  auto entries = [&](int c) { return c < n1 ? off[c + 1] - off[c] : 0; };
+  int cnt = entries(t);
+  int base = 0;
+  for (int c0 = 0; c0 < n1; c0 += 256) {
+    const int c = c0 + t;
+    const int next = entries(c + 256);
     const int ov = cnt > 0 ? (cnt - 1) / kKeyChunk : 0;
-    ovs[c] = start;
-    ovc[c] = ov;
-    for (int m = 1; m <= ov; ++m) tab[start + m - 1] = (c << 16) | m;
-    start += ov;
+    int x = ov;   // inclusive scan over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int start = base + x - ov;
+    for (int u = 0; u < w; ++u) start += wsum[u];
+    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();   // the totals are rewritten by the next round
+    if (c < n1) {
+      ovs[c] = start;
+      ovc[c] = ov;
+      for (int m = 1; m <= ov; ++m) tab[start + m - 1] = (c << 16) | m;
+    }
+    cnt = next;
   }
-  if (t == 255) a.ov_total[head] = start;
+  if (t == 0) a.ov_total[head] = base;
 }
 
+// One key block's share of the key-major pass: chunk `chunk` of CSC_1[j] (kKeyCsc: chunk 0
+// plus the overflow partials, then the store; kKeyOverflow: partial sums into slot ov_t), or
+// the whole mask column j (kKeyMask).
 template <int MODE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_kernel(
-    BwdArgs a) {
+__device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int chunk, int ov_t,
+                                          bf16* stQ, bf16* stO, float* pdown, float* stL,
+                                          int* pend) {
   constexpr bool MASK = MODE == kKeyMask;
-  __shared__ __attribute__((aligned(16))) bf16 stQ[32 * kStride];
-  __shared__ __attribute__((aligned(16))) bf16 stO[32 * kStride];   // dO rows
-  __shared__ __attribute__((aligned(16))) float pdown[2 * kDim];    // pushed-down dK, dV
-  __shared__ __attribute__((aligned(16))) float stL[64];            // lse (0..31), D (32..63)
-  __shared__ int pend[MASK ? 128 : 1];                              // mask hits not yet run
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int g = lane >> 4;
   const int n1 = a.n >> kBlockShift;
-  const int kb = uniform(xcd_block(blockIdx.x, gridDim.x));
-  int head, j, chunk = 0, ov_t = 0;
-  if constexpr (MODE == kKeyOverflow) {
-    head = uniform(kb / a.ov_cap);
-    ov_t = uniform(kb - head * a.ov_cap);
-    if (ov_t >= a.ov_total[head]) return;
-    const int packed = uniform(a.ov_table[(long)head * a.ov_cap + ov_t]);
-    j = packed >> 16;
-    chunk = packed & 0xffff;
-  } else {
-    head = uniform(kb / n1);
-    j = uniform(kb - head * n1);
-  }
   const long tok_base = (long)head * a.n;
 
   // pooled-key gradients pushed down to this block (lane = channel), loaded first so that
@@ -965,6 +970,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
   }
 }
 
+template <int MODE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_kernel(
+    BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 stQ[32 * kStride];
+  __shared__ __attribute__((aligned(16))) bf16 stO[32 * kStride];   // dO rows
+  __shared__ __attribute__((aligned(16))) float pdown[2 * kDim];    // pushed-down dK, dV
+  __shared__ __attribute__((aligned(16))) float stL[64];            // lse (0..31), D (32..63)
+  __shared__ int pend[MODE == kKeyMask ? 128 : 1];                  // mask hits not yet run
+  const int kb = uniform(xcd_block(blockIdx.x, gridDim.x));
+  if constexpr (MODE == kKeyOverflow) {
+    const int head = uniform(kb / a.ov_waves);
+    const int total = uniform(a.ov_total[head]);
+    for (int t = uniform(kb - head * a.ov_waves); t < total; t += a.ov_waves) {
+      const int packed = uniform(a.ov_table[(long)head * a.ov_cap + t]);
+      key_block<MODE>(a, head, packed >> 16, packed & 0xffff, t, stQ, stO, pdown, stL, pend);
+    }
+  } else {
+    const int n1 = a.n >> kBlockShift;
+    const int head = uniform(kb / n1);
+    key_block<MODE>(a, head, uniform(kb - head * n1), 0, 0, stQ, stO, pdown, stL, pend);
+  }
+}
+
 // ====================================================================== host side
 struct BwdLayout {
   size_t dd, part_k, part_v, dk_lv[kMaxLv], dv_lv[kMaxLv];
@@ -1067,14 +1095,13 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   a.scale = s.scale;
   a.c2 = s.scale * kLog2e;
 
-  if (!mask) {   // overflow plan of the key-major pass (reads CSC_1 offsets only)
-    LLSA_LAUNCH("key_plan_kernel", key_plan_kernel, dim3((unsigned)s.bh), dim3(256), 0, stream,
-                a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  // the overflow plan of the key-major pass reads only the CSC_1 offsets: its workgroups lead
+  // the query-major launch (a multiple of 8, so the XCD of every query unit is unchanged)
+  static_assert(kQWaves == 4, "the plan runs on 256-thread workgroups");
+  a.plan_blocks = mask ? 0 : (s.bh + 7) / 8 * 8;
+  a.ov_waves = std::min(a.ov_cap, kOvWaves);
   const int n2 = s.n >> (2 * kBlockShift);
-  const unsigned qblocks = (unsigned)(s.bh * n2 * kUnits);
+  const unsigned qblocks = (unsigned)(a.plan_blocks + s.bh * n2 * kUnits);
   const int n_coarse = s.coarse_levels * s.topk;
   const size_t qlds = bwd_query_lds_bytes(n_coarse, s.exclude_overlap && coarse);
   if (n_coarse == 0)
@@ -1108,7 +1135,7 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
                 dim3(64), 0, stream, a);
   } else {
     LLSA_LAUNCH("bwd_key_overflow_kernel", bwd_key_kernel<kKeyOverflow>,
-                dim3((unsigned)((long)s.bh * a.ov_cap)), dim3(64), 0, stream, a);
+                dim3((unsigned)((long)s.bh * a.ov_waves)), dim3(64), 0, stream, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     LLSA_LAUNCH("bwd_key_kernel", bwd_key_kernel<kKeyCsc>, dim3((unsigned)kwaves), dim3(64), 0,
                 stream, a);

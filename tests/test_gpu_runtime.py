@@ -61,7 +61,7 @@ def test_profile_hook_reports_every_kernel():
     prof = _abi.llsa_profile_read()
     for name in ("pool12_kernel", "select_kernel", "attn_fwd_kernel", "tile_sort_kernel",
                  "csc_offsets_kernel", "csc_scatter_kernel", "bwd_query_kernel", "coarse_grad_kernel",
-                 "bwd_key_kernel", "key_plan_kernel", "bwd_key_overflow_kernel"):
+                 "bwd_key_kernel", "bwd_key_overflow_kernel"):
         assert name in prof, name
         cnt, ms = prof[name]
         assert cnt >= 2 and ms > 0.0
