@@ -188,7 +188,9 @@ int32_t llsa_index_transpose(int32_t nmat, int32_t rows, int32_t cols, int32_t k
  * sel[0], csc_off[0], csc_rows[0]: level 1 as 16-token blocks (sel[0] as for llsa_attn_fwd;
  * its transpose has rows = cols = N/16 and k = topk * block / 16).  N <= 2^19 per head (the
  * level-1 transpose's 32-bit codes); LLSA_ERR_UNSUPPORTED above.
- * ws: llsa_workspace_bytes(bwd) bytes of device memory.
+ * Deterministic (no atomics): the query blocks of a key block picked by more than 128 of
+ * them are cut into chunks of 128 whose partial dK/dV sums are added in chunk order.
+ * ws: llsa_workspace_bytes(bwd) bytes of device memory (D, coarse partials, chunk partials).
  */
 int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const void* v,
                       const void* dout, const float* lse,
@@ -229,8 +231,9 @@ int32_t llsa_dense_attn_bwd(int32_t batch_heads, int32_t n, int32_t head_dim, fl
  * llsa_select), 0 elsewhere; it clears all batch*heads*n_1^2 bytes.
  * llsa_attn_bwd_masked computes what llsa_attn_bwd computes for a problem without coarse
  * keys (levels 1, or enrich 0), with the key-major pass finding the query blocks of each key
- * block by scanning its column of the mask instead of reading CSC_1; the results are
- * bit-identical to llsa_attn_bwd's.  Arguments as for llsa_attn_bwd; ws: llsa_workspace_bytes
+ * block by scanning its column of the mask instead of reading CSC_1 (no chunking); the
+ * results are bit-identical to llsa_attn_bwd's when no key block is picked by more than 128
+ * query blocks, and otherwise differ only in the fp32 order of dK/dV sums.  Arguments as for llsa_attn_bwd; ws: llsa_workspace_bytes
  * (bwd) bytes.  Both: bf16 only; LLSA_ERR_UNSUPPORTED if levels > 1 and enrich, LLSA_ERR_SHAPE
  * if the mask would exceed 2^34 bytes.  Errors otherwise as for the calls above.
  */
