@@ -157,6 +157,42 @@ def test_block64_overlap_exclusion_on_oracle_indices():
         assert_close(to64(got), ref_g, torch.bfloat16, name)
 
 
+@pytest.mark.parametrize("enrich_levels,unit_weight,exclude", [
+    (1, False, False),    # only level 2's coarse keys (64^2-token blocks)
+    (0, True, False),     # both coarse levels, weight 1
+    (0, True, True),      # weight 1 and overlap exclusion
+    (1, False, True)])
+def test_block64_enrichment_variants_on_oracle_indices(enrich_levels, unit_weight, exclude):
+    """B = 64 at L = 3 (512x512, K = 1: level 3 is one block per head) crossed with the
+    enrichment switches, forward and backward against the oracle on the oracle's selection."""
+    h = w = 512
+    levels, topk = 3, 1
+    d, ref = _inputs(1, 2, h, w, torch.bfloat16, 76, grad=True)
+    p = ops.make_problem(d["q"], h, w, levels, topk, True, 0.0, RASTER, enrich_levels,
+                         unit_weight, block=B, coarse_exclude_overlap=exclude)
+    sels = [_oracle_sel(ref, h, w, levels, topk, i) for i in range(2)]
+    att = _gpu_sel(p, sels, levels)
+    q, k, v, do = d["q"], d["k"], d["v"], d["do"]
+    kl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    vl = [torch.empty((1, 2, p.n_level(l), 64), device=DEV) for l in range(1, levels + 1)]
+    _abi.llsa_pool(p, None, k, v, None, kl, vl)
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 2, p.n), device=DEV)
+    _abi.llsa_attn_fwd(p, q, k, v, kl, vl, att, o, lse)
+    dq, dk, dv = ops.llsa_backward(p, q, k, v, dict(o=o, lse=lse, k_lv=kl, v_lv=vl, sel=att),
+                                   do)
+    kw = dict(enrich_levels=enrich_levels, coarse_weight=not unit_weight,
+              exclude_overlap=exclude)
+    res = orc.llsa_forward(ref["q"], ref["k"], ref["v"], h, w, B, levels, topk, True,
+                           sel_override=[sels], **kw)
+    assert_close(to64(o), res["o"], torch.bfloat16, "o")
+    assert_close(to64(lse), res["lse"], torch.bfloat16, "lse")
+    want = orc.llsa_backward(ref["q"], ref["k"], ref["v"], ref["do"], h, w, B, levels, [sels],
+                             True, **kw)
+    for name, got, ref_g in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+        assert_close(to64(got), ref_g, torch.bfloat16, name)
+
+
 def test_e2e_block64_px256_train():
     """The whole B = 64 path (L = 2, K = 8) at the 256x256 batch-2 training shape; two heads
     checked against the oracle on the GPU's selection."""
