@@ -53,19 +53,22 @@ __device__ __forceinline__ bool better(float s1, int i1, float s2, int i2) {
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
-// Inserts a candidate whose id is larger than every id already in the list.
+// Inserts a candidate whose id is larger than every id already in the list (scores
+// descending).  c_j = s > ls[j] is monotone in j, so slot j keeps its entry (c_j false), takes
+// the candidate (c_j and not c_{j-1}) or its predecessor's entry (c_{j-1}): all compares are
+// independent, a chain of depth 3 instead of one compare-and-swap step per slot.
 template <int KMAX>
 __device__ __forceinline__ void list_insert(float (&ls)[KMAX], int (&li)[KMAX], float s, int id) {
+  bool c[KMAX];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    const bool b = s > ls[j];
-    const float ts = ls[j];
-    const int ti = li[j];
-    ls[j] = b ? s : ts;
-    li[j] = b ? id : ti;
-    s = b ? ts : s;
-    id = b ? ti : id;
+  for (int j = 0; j < KMAX; ++j) c[j] = s > ls[j];
+#pragma unroll
+  for (int j = KMAX - 1; j >= 1; --j) {
+    ls[j] = c[j] ? (c[j - 1] ? ls[j - 1] : s) : ls[j];
+    li[j] = c[j] ? (c[j - 1] ? li[j - 1] : id) : li[j];
   }
+  ls[0] = c[0] ? s : ls[0];
+  li[0] = c[0] ? id : li[0];
 }
 
 // Candidate rows first + n (channels 16g .. 16g + 15) of a 16-row tile; rows outside
