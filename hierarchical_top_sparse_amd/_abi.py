@@ -20,7 +20,7 @@ _lib = None
 LLSA_F32, LLSA_BF16 = 0, 1
 LLSA_LAYOUT_MORTON, LLSA_LAYOUT_RASTER = 0, 1
 LLSA_MAX_LEVELS = 6
-LLSA_ABI_VERSION = 3   # the llsa_problem layout this binding marshals
+LLSA_ABI_VERSION = 4   # the llsa_problem layout and entry points this binding marshals
 
 
 class LlsaError(RuntimeError):
@@ -116,6 +116,7 @@ def lib() -> ctypes.CDLL:
             "llsa_reorder": ([P, vp, vp, i32, vp], i32),
             "llsa_pool": ([P, vp, vp, vp, pp, pp, pp, vp], i32),
             "llsa_select": ([P, pp, pp, pp, i32, i32, vp], i32),
+            "llsa_pool_select": ([P, vp, vp, vp, pp, pp, pp, pp, vp], i32),
             "llsa_attn_fwd": ([P, vp, vp, vp, pp, pp, pp, vp, vp, vp], i32),
             "llsa_index_transpose_workspace": ([i32, i32, i32, i32, ctypes.POINTER(sz)], i32),
             "llsa_index_transpose": ([i32, i32, i32, i32, vp, vp, vp, vp, sz, vp], i32),
@@ -144,7 +145,8 @@ def lib() -> ctypes.CDLL:
 
 def exported_symbols() -> list:
     return ["llsa_abi_version", "llsa_status_str", "llsa_last_error", "llsa_check",
-            "llsa_workspace_bytes", "llsa_reorder", "llsa_pool", "llsa_select", "llsa_attn_fwd",
+            "llsa_workspace_bytes", "llsa_reorder", "llsa_pool", "llsa_select",
+            "llsa_pool_select", "llsa_attn_fwd",
             "llsa_index_transpose_workspace", "llsa_index_transpose", "llsa_attn_bwd",
             "llsa_dense_attn_fwd", "llsa_dense_attn_bwd", "llsa_block_mask", "llsa_expand_blocks",
             "llsa_attn_bwd_masked", "llsa_calib_copy", "llsa_calib_mfma", "llsa_profile_enable",
@@ -260,6 +262,26 @@ def llsa_select(p: Problem, q_lv, k_lv, sel, level_hi=None, level_lo=1, stream=N
         _expect(sel[level_hi], _sel_shape(p, level_hi + 1), torch.int32, "parent sel")
     _raise(lib().llsa_select(ctypes.byref(p.c()), _ptrs(q_lv), _ptrs(k_lv), _ptrs(sel),
                              level_hi, level_lo, _stream(stream)), "llsa_select")
+
+
+def llsa_pool_select(p: Problem, q, k, v, q_lv, k_lv, v_lv, sel, stream=None):
+    """llsa_pool(q, k, v) then llsa_select of levels L..1, as one call (V's pooling rides in
+    the selection launches where the library can)."""
+    _expect(q, _tok_shape(p), p.torch_dtype, "q")
+    _expect(k, _tok_shape(p), p.torch_dtype, "k")
+    _expect(v, _tok_shape(p), p.torch_dtype, "v")
+    for name, x, lv in (("q", q, q_lv), ("k", k, k_lv), ("v", v, v_lv)):
+        if x is None:
+            continue
+        if len(lv) != p.levels:
+            raise ValueError(f"{name}_lv needs {p.levels} entries")
+        for l, t in enumerate(lv, start=1):
+            _expect(t, _lv_shape(p, l), torch.float32, f"{name}_lv[{l - 1}]")
+    for l in range(1, p.levels + 1):
+        _expect(sel[l - 1], _sel_shape(p, l), torch.int32, f"sel[{l - 1}]")
+    _raise(lib().llsa_pool_select(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptrs(q_lv),
+                                  _ptrs(k_lv), _ptrs(v_lv if v is not None else None),
+                                  _ptrs(sel), _stream(stream)), "llsa_pool_select")
 
 
 def llsa_attn_fwd(p: Problem, q, k, v, k_lv, v_lv, sel, o, lse, stream=None):

@@ -200,6 +200,35 @@ int32_t llsa_pool(const llsa_problem* p, const void* q, const void* k, const voi
   return hip_status(llsa::launch_pool(make_shape(p), x, lv, (hipStream_t)stream), "llsa_pool");
 }
 
+int32_t llsa_pool_select(const llsa_problem* p, const void* q, const void* k, const void* v,
+                         float* const* q_lv, float* const* k_lv, float* const* v_lv,
+                         int32_t* const* sel, void* stream) {
+  int32_t st = check_problem(p);
+  if (st != LLSA_OK) return st;
+  CHECK_PTR(q, "q");
+  CHECK_PTR(k, "k");
+  if (!q_lv || !k_lv || !sel) return fail(LLSA_ERR_NULL, "level or selection array is NULL");
+  const void* x[3] = {q, k, v};
+  float* const* lv[3] = {q_lv, k_lv, v_lv};
+  const char* names[3] = {"q", "k", "v"};
+  for (int t = 0; t < 3; ++t) {
+    if (!x[t]) continue;
+    if (!aligned16(x[t])) return fail(LLSA_ERR_ALIGN, "%s is not 16-byte aligned", names[t]);
+    if (!lv[t]) return fail(LLSA_ERR_NULL, "level array of %s is NULL", names[t]);
+    for (int l = 1; l <= p->levels; ++l) {
+      float* ptr = lv[t][l - 1];
+      // the selection reads every level of Q and K; V's levels below L feed the next one
+      if (!ptr && (t < 2 || (l < p->levels && (l >= 2 || p->block != 16))))
+        return fail(LLSA_ERR_NULL, "%s level %d is needed", names[t], l);
+      if (ptr && !aligned16(ptr))
+        return fail(LLSA_ERR_ALIGN, "%s level %d is not 16-byte aligned", names[t], l);
+    }
+  }
+  for (int l = 1; l <= p->levels; ++l) CHECK_PTR(sel[l - 1], "selection");
+  return hip_status(llsa::launch_pool_select(make_shape(p), x, lv, sel, (hipStream_t)stream),
+                    "llsa_pool_select");
+}
+
 int32_t llsa_select(const llsa_problem* p, const float* const* q_lv, const float* const* k_lv,
                     int32_t* const* sel, int32_t level_hi, int32_t level_lo, void* stream) {
   int32_t st = check_problem(p);

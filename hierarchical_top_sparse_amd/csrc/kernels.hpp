@@ -47,6 +47,8 @@ hipError_t launch_pool(const Shape& s, const void* const x[3], float* const* lv[
 
 hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* const* k_lv,
                          int32_t* const* sel, int level_hi, int level_lo, hipStream_t stream);
+hipError_t launch_pool_select(const Shape& s, const void* const x[3], float* const* lv[3],
+                              int32_t* const* sel, hipStream_t stream);
 
 hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const void* v,
                            const float* const* k_lv, const float* const* v_lv,

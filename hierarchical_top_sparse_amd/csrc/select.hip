@@ -29,6 +29,7 @@
 // pick i) and read with v_readlane.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "pool_impl.hpp"
 
 namespace llsa {
 
@@ -204,8 +205,9 @@ __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool a
   else merge_lists<KMAX, 16, 32>(ls, li, K, pick);
 }
 
+// The waves of selection workgroup bid of nblocks (renumbered per XCD).
 template <int KMAX>
-__global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelArgs a) {
+__device__ __forceinline__ void select_group(const SelArgs& a, int bid, int nblocks) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
   const int g = lane >> 4;
@@ -214,8 +216,7 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelArgs a) {
   const int bs = a.bshift;
   const int n_lo = a.n >> (bs * lo);
   const int groups = (n_lo + 15) >> 4;
-  const int wave =
-      uniform(xcd_block((int)blockIdx.x, (int)gridDim.x) * kSelWaves + (int)(threadIdx.x >> 6));
+  const int wave = uniform(xcd_block(bid, nblocks) * kSelWaves + (int)(threadIdx.x >> 6));
   if (wave >= a.bh * groups) return;
   const int head = uniform(wave / groups);
   const int grp = uniform(wave - head * groups);
@@ -277,6 +278,48 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelArgs a) {
   }
 }
 
+template <int KMAX>
+__global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelArgs a) {
+  select_group<KMAX>(a, blockIdx.x, gridDim.x);
+}
+
+// A selection launch that also pools V (its levels 1 and 2 from the tokens, or level 3 from
+// level 2): the selection's workgroups come first (sel_blocks, a multiple of 8, so that their
+// XCDs are those of a plain launch) and raise their waves' issue priority; the pooling
+// workgroups after them fill the chip while the few selection waves run their dependent
+// chains.  V is first read by the attention, so nothing in the launch depends on it.
+template <int KMAX>
+__global__ __launch_bounds__(64 * kSelWaves) void select_pool12_kernel(SelArgs a, int sel_blocks,
+                                                                       PoolArgs pa, int n,
+                                                                       Grid grid, int gph) {
+  __shared__ __attribute__((aligned(16))) float sh[kBlock][kDim];
+  if ((int)blockIdx.x < sel_blocks) {
+    __builtin_amdgcn_s_setprio(2);
+    select_group<KMAX>(a, blockIdx.x, sel_blocks);
+    return;
+  }
+  pool12_bf16_group(pa, n, grid, gph, 0, (int)blockIdx.x - sel_blocks, sh);
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(64 * kSelWaves) void select_pool_next_kernel(SelArgs a,
+                                                                          int sel_blocks,
+                                                                          PoolNextArgs pb,
+                                                                          long total_out) {
+  if ((int)blockIdx.x < sel_blocks) {
+    __builtin_amdgcn_s_setprio(2);
+    select_group<KMAX>(a, blockIdx.x, sel_blocks);
+    return;
+  }
+  const long i = (long)((int)blockIdx.x - sel_blocks) * 256 + threadIdx.x;
+  if (i < total_out) pool_next_elem<16>(pb, 0, i);
+}
+
+__global__ __launch_bounds__(256) void pool_next_v_kernel(PoolNextArgs pb, long total_out) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < total_out) pool_next_elem<16>(pb, 0, i);
+}
+
 // Level-1 picks of 64-token blocks as the 16-token blocks they cover: row q of the output (a
 // 16-token query block) lists, for each pick j of its 64-token block q / 4, the blocks
 // 4j .. 4j + 3 (ascending, as the picks are).  With B = 16 a copy.  One thread per output.
@@ -300,9 +343,19 @@ hipError_t launch_expand_blocks(const Shape& s, const int32_t* sel1, int32_t* fi
   return hipGetLastError();
 }
 
+// V's pooling carried by a selection launch: kind 1 = levels 1 and 2 from the tokens
+// (pool12 of tensor 0 of pa), kind 2 = one level from the level below (B = 16).
+struct PoolInSelect {
+  int kind = 0;
+  PoolArgs pa{};
+  PoolNextArgs pb{};
+  long total = 0;   // kind 2: output elements
+};
+
 static hipError_t launch_select_range(const Shape& s, const float* const* q_lv,
                                       const float* const* k_lv, int32_t* const* sel,
-                                      int level_hi, int level_lo, hipStream_t stream) {
+                                      int level_hi, int level_lo, hipStream_t stream,
+                                      const PoolInSelect& pv = PoolInSelect{}) {
   SelArgs a{};
   for (int l = 0; l < s.levels && l < kSelMaxLv; ++l) {
     a.q[l] = q_lv[l];
@@ -319,6 +372,36 @@ static hipError_t launch_select_range(const Shape& s, const float* const* q_lv,
   const int n_lo = s.n_level(level_lo);
   const long waves = (long)s.bh * ((n_lo + 15) >> 4);   // one per group
   const unsigned blocks = (unsigned)((waves + kSelWaves - 1) / kSelWaves);
+  if (pv.kind != 0) {
+    const unsigned sb = (blocks + 7) / 8 * 8;
+    const dim3 wg(64 * kSelWaves);
+    if (pv.kind == 1) {
+      const int gph = s.n >> (2 * kBlockShift);
+      const dim3 g(sb + (unsigned)(s.bh * gph));
+      const Grid tg{s.hbits, s.wbits, s.raster};
+      if (s.topk <= 8)
+        LLSA_LAUNCH("select_pool_kernel", select_pool12_kernel<8>, g, wg, 0, stream, a, (int)sb,
+                    pv.pa, s.n, tg, gph);
+      else if (s.topk <= 16)
+        LLSA_LAUNCH("select_pool_kernel", select_pool12_kernel<16>, g, wg, 0, stream, a,
+                    (int)sb, pv.pa, s.n, tg, gph);
+      else
+        LLSA_LAUNCH("select_pool_kernel", select_pool12_kernel<32>, g, wg, 0, stream, a,
+                    (int)sb, pv.pa, s.n, tg, gph);
+    } else {
+      const dim3 g(sb + (unsigned)((pv.total + 255) / 256));
+      if (s.topk <= 8)
+        LLSA_LAUNCH("select_pool_kernel", select_pool_next_kernel<8>, g, wg, 0, stream, a,
+                    (int)sb, pv.pb, pv.total);
+      else if (s.topk <= 16)
+        LLSA_LAUNCH("select_pool_kernel", select_pool_next_kernel<16>, g, wg, 0, stream, a,
+                    (int)sb, pv.pb, pv.total);
+      else
+        LLSA_LAUNCH("select_pool_kernel", select_pool_next_kernel<32>, g, wg, 0, stream, a,
+                    (int)sb, pv.pb, pv.total);
+    }
+    return hipGetLastError();
+  }
   if (s.topk <= 8)
     LLSA_LAUNCH("select_kernel", select_kernel<8>, dim3(blocks), dim3(64 * kSelWaves), 0, stream,
                 a);
@@ -339,6 +422,54 @@ hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* 
     return launch_select_range(s, q_lv, k_lv, sel, 1, 1, stream);
   }
   return launch_select_range(s, q_lv, k_lv, sel, level_hi, level_lo, stream);
+}
+
+// Pooling of Q, K and V and the selection of every level, as llsa_pool then llsa_select
+// (levels L..1).  With B = 16, bf16 tokens, V given and L >= 2, V's pooling rides in the
+// selection launches (levels 1-2 in the first, level 3 in the level-1 launch when L >= 3,
+// levels 4.. after it); otherwise the two calls run as they are.  Same results either way:
+// every kernel body and its arithmetic are the ones of the plain launches.
+hipError_t launch_pool_select(const Shape& s, const void* const x[3], float* const* lv[3],
+                              int32_t* const* sel, hipStream_t stream) {
+  const int L = s.levels;
+  const bool fuse = x[2] && s.bf16 && s.bshift == kBlockShift && L >= 2 && lv[2][1];
+  if (!fuse) {
+    const hipError_t e = launch_pool(s, x, lv, stream);
+    if (e != hipSuccess) return e;
+    return launch_select(s, lv[0], lv[1], sel, L, 1, stream);
+  }
+  const void* qk[3] = {x[0], x[1], nullptr};
+  hipError_t e = launch_pool(s, qk, lv, stream);
+  if (e != hipSuccess) return e;
+  PoolInSelect p12;
+  p12.kind = 1;
+  p12.pa.x[0] = x[2];
+  p12.pa.lv1[0] = lv[2][0];
+  p12.pa.lv2[0] = lv[2][1];
+  if (L == 2) return launch_select_range(s, lv[0], lv[1], sel, 2, 1, stream, p12);
+  e = launch_select_range(s, lv[0], lv[1], sel, L, 2, stream, p12);
+  if (e != hipSuccess) return e;
+  PoolInSelect pn;
+  if (lv[2][2]) {
+    pn.kind = 2;
+    pn.pb.in[0] = lv[2][1];
+    pn.pb.out[0] = lv[2][2];
+    pn.total = (long)s.bh * s.n_level(3) * kDim;
+  }
+  e = launch_select_range(s, lv[0], lv[1], sel, 1, 1, stream, pn);
+  if (e != hipSuccess) return e;
+  for (int l = 4; l <= L; ++l) {   // V's levels above 3: the plain kernel, level by level
+    if (!lv[2][l - 1]) continue;
+    if (!lv[2][l - 2]) return hipErrorInvalidValue;
+    PoolNextArgs b{};
+    b.in[0] = lv[2][l - 2];
+    b.out[0] = lv[2][l - 1];
+    const long total = (long)s.bh * s.n_level(l) * kDim;
+    LLSA_LAUNCH("pool_next_kernel", pool_next_v_kernel, dim3((unsigned)((total + 255) / 256)),
+                dim3(256), 0, stream, b, total);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace llsa

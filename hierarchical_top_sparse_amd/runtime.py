@@ -22,8 +22,11 @@ from . import _abi
 class Step:
     """dout=None makes a forward-only step (pooling, selection, sparse attention)."""
 
-    def __init__(self, p: _abi.Problem, q, k, v, dout=None):
+    def __init__(self, p: _abi.Problem, q, k, v, dout=None, fuse_prologue: bool = True):
         self.p = p
+        # one llsa_pool_select call (V pooled inside the selection launches) instead of
+        # llsa_pool + llsa_select; the same pooled levels and picks either way
+        self.fuse_prologue = fuse_prologue
         self.q, self.k, self.v, self.dout = q, k, v, dout
         self.backward = dout is not None
         dev, f32 = q.device, torch.float32
@@ -74,9 +77,14 @@ class Step:
     def calls(self):
         """(name, thunk) for every C-ABI call of one step, in order (one stream)."""
         a, p = _abi, self.p
-        head = [("pool", lambda: a.llsa_pool(p, self.q, self.k, self.v if self.pool_v else None,
-                                             self.q_lv, self.k_lv, self.v_lv)),
-                ("select", lambda: a.llsa_select(p, self.q_lv, self.k_lv, self.sel))]
+        vv = self.v if self.pool_v else None
+        if self.fuse_prologue:
+            head = [("pool_select", lambda: a.llsa_pool_select(p, self.q, self.k, vv, self.q_lv,
+                                                               self.k_lv, self.v_lv, self.sel))]
+        else:
+            head = [("pool", lambda: a.llsa_pool(p, self.q, self.k, vv, self.q_lv, self.k_lv,
+                                                 self.v_lv)),
+                    ("select", lambda: a.llsa_select(p, self.q_lv, self.k_lv, self.sel))]
         if p.block != 16:
             head.append(("expand", lambda: a.llsa_expand_blocks(p, self.sel[0], self.fine)))
         fwd = [("attn_fwd", lambda: a.llsa_attn_fwd(p, self.q, self.k, self.v, self.k_lv,

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LLSA_ABI_VERSION 3
+#define LLSA_ABI_VERSION 4
 #define LLSA_MAX_LEVELS 6
 #define LLSA_MAX_TOPK 32
 
@@ -130,6 +130,20 @@ int32_t llsa_pool(const llsa_problem* p, const void* q, const void* k, const voi
  */
 int32_t llsa_select(const llsa_problem* p, const float* const* q_lv, const float* const* k_lv,
                     int32_t* const* sel, int32_t level_hi, int32_t level_lo, void* stream);
+
+/*
+ * llsa_pool_select — llsa_pool followed by llsa_select of levels L..1 (summary sec. 三: the
+ * hierarchical compression and the coarse-to-fine search), as one call.  Same arguments and
+ * results as the two calls: q, k (required) and v (NULL skips it) are the tokens; q_lv and
+ * k_lv need all L levels (the selection reads them), v_lv the levels llsa_pool needs; sel:
+ * L pointers as for llsa_select.  V's levels are first read by the attention, not by the
+ * selection, so with block 16, bf16 tokens and L >= 2 its pooling runs inside the selection
+ * launches (their workgroups after the selection's), where it fills the chip while the
+ * selection's few waves run their dependent chains.  Errors as for the two calls.
+ */
+int32_t llsa_pool_select(const llsa_problem* p, const void* q, const void* k, const void* v,
+                         float* const* q_lv, float* const* k_lv, float* const* v_lv,
+                         int32_t* const* sel, void* stream);
 
 /*
  * llsa_expand_blocks — level-1 picks as the 16-token blocks they cover, the form the

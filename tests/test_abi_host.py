@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.llsa_abi_version() == abi.LLSA_ABI_VERSION == 3
+    assert L.llsa_abi_version() == abi.LLSA_ABI_VERSION == 4
     for code in range(8):
         assert L.llsa_status_str(code)
     assert L.llsa_status_str(99) == b"unknown status"
@@ -200,3 +200,23 @@ def test_calibration_validation(L):
     assert L.llsa_calib_mfma(f, 0, 16, None) == 2
     assert L.llsa_calib_mfma(f, 4, 0, None) == 2
     assert L.llsa_calib_mfma(None, 4, 16, None) == 1
+
+
+def test_pool_select_validation(L):
+    """Q and K are required with all their levels (the selection reads them); V is optional."""
+    f = ctypes.c_void_p(FAKE)
+    p = ctypes.byref(_p(height=64, width=64, levels=2).c())
+    lv2 = (ctypes.c_void_p * 6)(FAKE, FAKE)
+    lv_missing1 = (ctypes.c_void_p * 6)(None, FAKE)
+    assert L.llsa_pool_select(p, None, f, f, lv2, lv2, lv2, lv2, None) == 1
+    assert L.llsa_pool_select(p, f, None, f, lv2, lv2, lv2, lv2, None) == 1
+    assert L.llsa_pool_select(p, f, f, None, lv2, None, None, lv2, None) == 1
+    assert L.llsa_pool_select(p, f, f, None, lv_missing1, lv2, None, lv2, None) == 1
+    assert b"q level 1" in L.llsa_last_error()
+    assert L.llsa_pool_select(p, f, f, None, lv2, lv2, None, lv_missing1, None) == 1
+    assert L.llsa_pool_select(p, ctypes.c_void_p(MISALIGNED), f, None, lv2, lv2, None, lv2,
+                              None) == 6
+    lv_bad = (ctypes.c_void_p * 6)(FAKE, MISALIGNED)
+    assert L.llsa_pool_select(p, f, f, f, lv2, lv2, lv_bad, lv2, None) == 6
+    bad = ctypes.byref(_p(height=64, width=64, levels=2, topk=0).c())
+    assert L.llsa_pool_select(bad, f, f, f, lv2, lv2, lv2, lv2, None) == 2

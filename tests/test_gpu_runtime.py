@@ -15,20 +15,23 @@ def _bits(t):
     return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32)
 
 
-def _make(h=128, w=128, levels=2, batch=1, heads=2, seed=61):
+def _make(h=128, w=128, levels=2, batch=1, heads=2, seed=61, fuse_prologue=True):
     x = gen.make_inputs(batch, heads, h, w, 64, torch.bfloat16, seed, with_grad=True)
     q, k, v, do = (x[t].cuda() for t in ("q", "k", "v", "do"))
-    return Step(ops.make_problem(q, h, w, levels), q, k, v, do)
+    return Step(ops.make_problem(q, h, w, levels), q, k, v, do, fuse_prologue=fuse_prologue)
 
 
 @pytest.mark.parametrize("h,w,levels", [(128, 128, 2), (128, 256, 3)])
 def test_graph_replays_match_eager(h, w, levels):
-    step = _make(h, w, levels)
+    """The reference is the eager one-stream step with llsa_pool + llsa_select; the graph is
+    the overlapped step with llsa_pool_select."""
+    step = _make(h, w, levels, fuse_prologue=False)
     step.run(overlap=False)    # one stream: the reference for the overlapped graph
     torch.cuda.synchronize()
     want = {k: v.clone() for k, v in step.outputs().items() if k != "sel"}
     want_sel = [s.clone() for s in step.sel]
     want_csc = [t.clone() for t in step.off + step.rows]
+    step.fuse_prologue = True
     step.capture()
     other = _make(64, 64, 2, seed=62)
     for rep in range(3):
@@ -49,8 +52,10 @@ def test_graph_replays_match_eager(h, w, levels):
         torch.cuda.synchronize()
 
 
-def test_profile_hook_reports_every_kernel():
-    step = _make()
+@pytest.mark.parametrize("fuse_prologue,select_name", [(True, "select_pool_kernel"),
+                                                       (False, "select_kernel")])
+def test_profile_hook_reports_every_kernel(fuse_prologue, select_name):
+    step = _make(fuse_prologue=fuse_prologue)
     step.run()
     torch.cuda.synchronize()
     _abi.llsa_profile_read()
@@ -59,7 +64,7 @@ def test_profile_hook_reports_every_kernel():
     step.run()
     _abi.llsa_profile_enable(False)
     prof = _abi.llsa_profile_read()
-    for name in ("pool12_kernel", "select_kernel", "attn_fwd_kernel", "tile_sort_kernel",
+    for name in ("pool12_kernel", select_name, "attn_fwd_kernel", "tile_sort_kernel",
                  "csc_offsets_kernel", "csc_scatter_kernel", "bwd_query_kernel", "coarse_grad_kernel",
                  "bwd_key_kernel", "bwd_key_overflow_kernel"):
         assert name in prof, name
