@@ -446,6 +446,11 @@ def sweep(steps):
         st = Step(p, q, k, v, do)
         train_ms, _, _, per_kernel_ms, _ = measure(st, steps, 2)
         pairs = int(st.sel[0].numel())   # (query block, picked key block) pairs
+        # the selection alone (its launches, on the step's pooled levels): inside the step
+        # the selection launches also carry V's pooling
+        sel_alone = lambda s_=st: _abi.llsa_select(s_.p, s_.q_lv, s_.k_lv, s_.sel)  # noqa: E731
+        sel_alone()
+        llsa_select_ms = _event_ms(sel_alone, max(steps, 5))
         qd, kd, vd, dod = (t.reshape(6, n, 64) for t in (q, k, v, do))
         o = torch.empty_like(qd)
         lse = torch.empty(6, n, device="cuda")
@@ -468,7 +473,10 @@ def sweep(steps):
         b64_train_ms = measure(Step(p64, q, k, v, do), steps, 2)[0]
         p1 = ops.make_problem(q, side, side, 1, 32)
         s1 = Step(p1, q, k, v, do)
-        single_ms, _, _, single_kernel_ms, _ = measure(s1, steps, 2)
+        single_ms = measure(s1, steps, 2)[0]
+        sel1_alone = lambda s_=s1: _abi.llsa_select(s_.p, s_.q_lv, s_.k_lv, s_.sel)  # noqa: E731
+        sel1_alone()
+        single_select_ms = _event_ms(sel1_alone, max(steps, 5))
         del s1
         mc = mask_comparator(q, k, v, do, side, side, steps)
         print(json.dumps({
@@ -482,8 +490,8 @@ def sweep(steps):
             "b64_speedup_fwd": round(dense_fwd_ms / b64_fwd_ms, 2),
             "b64_speedup_train": round(dense_train_ms / b64_train_ms, 2),
             "single_level_top32_train_ms": round(single_ms, 4),
-            "single_level_select_ms": round(single_kernel_ms.get("select_kernel", 0.0), 4),
-            "llsa_select_ms": round(per_kernel_ms.get("select_kernel", 0.0), 4),
+            "single_level_select_ms": round(single_select_ms, 4),
+            "llsa_select_ms": round(llsa_select_ms, 4),
             "speedup_vs_single_level": round(single_ms / train_ms, 2),
             "single_level_bwd_csc_ms": mc["csc"]["bwd_ms"],
             "single_level_bwd_mask_ms": mc["mask"]["bwd_ms"],
