@@ -55,11 +55,25 @@ __device__ __forceinline__ bool better(float s1, int i1, float s2, int i2) {
 }
 
 // Inserts a candidate whose id is larger than every id already in the list (scores
-// descending).  c_j = s > ls[j] is monotone in j, so slot j keeps its entry (c_j false), takes
-// the candidate (c_j and not c_{j-1}) or its predecessor's entry (c_{j-1}): all compares are
-// independent, a chain of depth 3 instead of one compare-and-swap step per slot.
+// descending).  Lists of up to 8: c_j = s > ls[j] is monotone in j, so slot j keeps its entry
+// (c_j false), takes the candidate (c_j and not c_{j-1}) or its predecessor's entry (c_{j-1}):
+// all compares are independent, a chain of depth 3.  Longer lists: one compare-and-swap step
+// per slot (their 16 or 32 compare masks would not stay in scalar registers).
 template <int KMAX>
 __device__ __forceinline__ void list_insert(float (&ls)[KMAX], int (&li)[KMAX], float s, int id) {
+  if constexpr (KMAX > 8) {
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      const bool b = s > ls[j];
+      const float ts = ls[j];
+      const int ti = li[j];
+      ls[j] = b ? s : ts;
+      li[j] = b ? id : ti;
+      s = b ? ts : s;
+      id = b ? ti : id;
+    }
+    return;
+  }
   bool c[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) c[j] = s > ls[j];
