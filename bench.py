@@ -561,6 +561,15 @@ def main():
     del step
     if not args.no_configs:
         extra["configs"] = config_table(max(5, args.steps // 2), 2)
+        # the core figure without the reorder: the same step on tokens already in Morton order
+        # (a network hoists the reorder to its entry); in raster order the reorder is folded
+        # into every kernel's addressing, so there is no separate reorder launch to leave out
+        other = "morton" if args.layout == "raster" else "raster"
+        s_o, _, _ = make_step(args.config, other)
+        ms_o = measure(s_o, max(10, args.steps // 2), 5)[0]
+        del s_o
+        extra[f"{other}_layout"] = {"ms_per_step": round(ms_o, 4),
+                                    "tokens_per_s": round(tokens / (ms_o / 1e3), 1)}
     if not args.no_dense:
         if "configs" in extra:
             fwd256 = extra["configs"]["px256"]["ms"]
