@@ -16,8 +16,8 @@ from . import _abi
 from ._abi import (LLSA_BF16, LLSA_F32, LLSA_LAYOUT_MORTON, LLSA_LAYOUT_RASTER, Problem,
                    llsa_attn_bwd, llsa_attn_bwd_masked, llsa_attn_fwd, llsa_block_mask,
                    llsa_expand_blocks,
-                   llsa_index_transpose, llsa_index_transpose_workspace, llsa_pool,
-                   llsa_reorder, llsa_select, llsa_workspace_bytes)
+                   llsa_index_transpose, llsa_index_transpose_workspace, llsa_pool_select,
+                   llsa_reorder, llsa_workspace_bytes)
 
 __all__ = ["Problem", "make_problem", "llsa_forward", "llsa_backward", "llsa_backward_masked",
            "llsa_attention", "dense_attention", "reorder", "LLSA_BF16", "LLSA_F32", "LLSA_LAYOUT_MORTON",
@@ -59,10 +59,11 @@ def llsa_forward(p: Problem, q, k, v):
     v_lv = [torch.empty(lv_shape(1), **f32) if p.block != 16 and p.levels >= 2 else None] + [
         torch.empty(lv_shape(l), **f32) for l in range(2, p.levels + 1)]
     need_v = p.enrich and p.levels >= 2
-    llsa_pool(p, q, k, v if need_v else None, q_lv, k_lv, v_lv)
     sel = [torch.empty((p.batch, p.heads, p.n_level(l), p.topk), device=dev, dtype=torch.int32)
            for l in range(1, p.levels + 1)]
-    llsa_select(p, q_lv, k_lv, sel)
+    # pooling and selection in one call (V pooled inside the selection launches), as the step
+    # runner issues them
+    llsa_pool_select(p, q, k, v if need_v else None, q_lv, k_lv, v_lv, sel)
     fine = sel[0]
     if p.block != 16:
         fine = torch.empty((p.batch, p.heads, p.n // 16, p.fine_k), device=dev,
