@@ -23,6 +23,8 @@
 //  * A single query is replicated over the 16 columns; each (tile, candidate) is then kept by
 //    exactly one lane (lane (n, g) takes candidate 4g + n % 4 of the tiles t with
 //    t % 4 = n / 4), and the 64 lists are merged across the whole wave.
+// llsa_pool_select issues the same launches with extra workgroups after the selection's that
+// pool V (select_pool12_kernel, select_pool_next_kernel): V is first read by the attention.
 // Lists only take strictly better scores: every lane sees its candidates in ascending id order
 // (picks are stored ascending), so ties keep the lower id; merges compare (score, id).  The K
 // picks are stored ascending.  The picks a ranking starts from are held one per lane (lane i:
