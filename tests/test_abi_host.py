@@ -220,3 +220,69 @@ def test_pool_select_validation(L):
     assert L.llsa_pool_select(p, f, f, f, lv2, lv2, lv_bad, lv2, None) == 6
     bad = ctypes.byref(_p(height=64, width=64, levels=2, topk=0).c())
     assert L.llsa_pool_select(bad, f, f, f, lv2, lv2, lv2, lv2, None) == 2
+
+
+hyp = pytest.importorskip("hypothesis")
+from hypothesis import HealthCheck, given, settings, strategies as st  # noqa: E402
+
+_INT = st.one_of(st.integers(-4, 70), st.integers(-2 ** 31, 2 ** 31 - 1))
+_SIDE = st.one_of(st.sampled_from([0, 1, 2, 4, 8, 16, 24, 64, 128, 256, 1024, 4096, 8192, -16]),
+                  st.integers(-2 ** 31, 2 ** 31 - 1))
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(batch=_INT, heads=_INT, height=_SIDE, width=_SIDE, levels=_INT, topk=_INT, enrich=_INT,
+       head_dim=st.sampled_from([0, 32, 64, 128, -64]),
+       block=st.sampled_from([0, 1, 4, 8, 16, 32, 64, 256, -16]),
+       scale=st.floats(width=32), dtype=_INT, layout=_INT, enrich_levels=_INT,
+       unit_weight=_INT, exclude=_INT)
+def test_check_never_accepts_what_the_kernels_cannot_run(L, batch, heads, height, width, levels,
+                                                         topk, enrich, head_dim, block, scale,
+                                                         dtype, layout, enrich_levels,
+                                                         unit_weight, exclude):
+    """Any problem: llsa_check returns a defined status without faulting, and every problem it
+    accepts satisfies the limits the kernels rely on and has a sane backward workspace."""
+    p = abi.Problem(batch=batch, heads=heads, height=height, width=width, levels=levels,
+                    topk=topk, enrich=enrich, head_dim=head_dim, block=block, scale=scale,
+                    dtype=dtype, layout=layout, enrich_levels=enrich_levels,
+                    coarse_unit_weight=unit_weight, coarse_exclude_overlap=exclude)
+    status = abi.llsa_check(p)
+    assert 0 <= status <= 7
+    if status:
+        assert abi.llsa_last_error()
+        return
+    n = height * width
+    assert batch >= 1 and heads >= 1 and head_dim == 64 and block in (16, 64)
+    assert 256 <= n <= 1 << 23 and batch * heads * n < 1 << 31
+    assert n % block ** levels == 0 and 1 <= topk <= min(32, n // block ** levels)
+    assert topk * block // 16 <= 32
+    assert dtype in (abi.LLSA_F32, abi.LLSA_BF16) and scale >= 0
+    f, b = abi.llsa_workspace_bytes(p)
+    assert f == 0 and 0 < b < 1 << 44
+
+
+@settings(max_examples=300, deadline=None, suppress_health_check=[HealthCheck.too_slow])
+@given(batch=st.integers(1, 8), heads=st.integers(1, 16),
+       height=st.sampled_from([4, 8, 16, 64, 256, 1024, 2048]),
+       width=st.sampled_from([4, 8, 16, 64, 256, 1024, 2048]), levels=st.integers(1, 4),
+       topk=st.integers(1, 33), enrich=st.integers(0, 1), block=st.sampled_from([16, 64]),
+       dtype=st.integers(0, 1), layout=st.integers(0, 1), enrich_levels=st.integers(0, 4),
+       unit_weight=st.integers(0, 1), exclude=st.integers(0, 1))
+def test_check_and_workspace_on_nearly_valid_problems(L, batch, heads, height, width, levels,
+                                                      topk, enrich, block, dtype, layout,
+                                                      enrich_levels, unit_weight, exclude):
+    """Mostly valid problems: accepted exactly when the documented limits hold, and then the
+    backward workspace covers D (4 bytes per token) and grows with the problem."""
+    p = abi.Problem(batch=batch, heads=heads, height=height, width=width, levels=levels,
+                    topk=topk, enrich=enrich, block=block, dtype=dtype, layout=layout,
+                    enrich_levels=enrich_levels, coarse_unit_weight=unit_weight,
+                    coarse_exclude_overlap=exclude)
+    n = height * width
+    ok = (256 <= n <= 1 << 23 and n % block ** levels == 0
+          and topk <= min(32, n // block ** levels) and topk * block // 16 <= 32
+          and batch * heads * n < 1 << 31)
+    status = abi.llsa_check(p)
+    assert (status == 0) == ok, (status, abi.llsa_last_error())
+    if ok:
+        f, b = abi.llsa_workspace_bytes(p)
+        assert f == 0 and b >= 4 * batch * heads * n
