@@ -176,6 +176,44 @@ def test_index_transpose_bit_exact(nmat, rows, cols, k, seed):
         assert np.array_equal(rws[m][:want_off[-1]], want_rows)
 
 
+def _random_transpose_cases(n_cases=10, seed=2024):
+    """Seeded shapes: rows up to 50,000 (beyond 32 sort tiles: the merge path), columns from
+    1, k up to 32; uniform or skewed (a few popular columns take most entries) column draws."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n_cases):
+        cases.append((int(rng.integers(1, 4)), int(rng.integers(1, 50001)),
+                      int(rng.integers(1, 20001)), int(rng.integers(1, 33)), bool(i % 2), i))
+    return cases
+
+
+@pytest.mark.parametrize("nmat,rows,cols,k,skewed,seed", _random_transpose_cases())
+def test_index_transpose_random_shapes(nmat, rows, cols, k, skewed, seed):
+    """Bit-exact against a stable sort by column, rows ascending within a column, on seeded
+    random shapes (duplicate ids within a row allowed: each entry is kept)."""
+    rng = np.random.default_rng(100 + seed)
+    if skewed:   # Zipf-like column popularity
+        w = 1.0 / np.arange(1, cols + 1) ** 1.2
+        csr = rng.choice(cols, size=(nmat, rows, k), p=w / w.sum())
+    else:
+        csr = rng.integers(0, cols, size=(nmat, rows, k))
+    csr = csr.astype(np.int32)
+    t = torch.from_numpy(csr).to(DEV)
+    off = torch.empty((nmat, cols + 1), dtype=torch.int32, device=DEV)
+    rws = torch.empty((nmat, rows * k), dtype=torch.int32, device=DEV)
+    ws = torch.empty(_abi.llsa_index_transpose_workspace(nmat, rows, cols, k), dtype=torch.uint8,
+                     device=DEV)
+    _abi.llsa_index_transpose(nmat, rows, cols, k, t, off, rws, ws)
+    off, rws = off.cpu().numpy(), rws.cpu().numpy()
+    for m in range(nmat):
+        flat_keys = csr[m].reshape(-1)
+        flat_rows = np.repeat(np.arange(rows), k)
+        order = np.argsort(flat_keys, kind="stable")
+        want_off = np.concatenate([[0], np.cumsum(np.bincount(flat_keys, minlength=cols))])
+        assert np.array_equal(off[m], want_off), (m, rows, cols, k)
+        assert np.array_equal(rws[m], flat_rows[order]), (m, rows, cols, k)
+
+
 # ----------------------------------------------------------------------------- attention
 
 
