@@ -71,3 +71,29 @@ def test_profile_hook_reports_every_kernel(fuse_prologue, select_name):
         cnt, ms = prof[name]
         assert cnt >= 2 and ms > 0.0
     assert _abi.llsa_profile_read() == {}
+
+
+@pytest.mark.parametrize("cfg_name", ["px256_train", "px512_train"])
+def test_benchmarked_graph_equals_the_parity_tested_path(cfg_name):
+    """The step the benchmark times (HIP-graph replays of the whole step: llsa_pool_select,
+    attention, transposes on the side stream, backward) at the workload's full size gives the
+    same bits as ops.llsa_forward / ops.llsa_backward, which the end-to-end parity tests check
+    against the oracle at the same sizes."""
+    cfg = gen.CONFIGS[cfg_name]
+    h, w, L = cfg["height"], cfg["width"], cfg["levels"]
+    x = gen.make_inputs(cfg["batch"], cfg["heads"], h, w, 64, cfg["dtype"], cfg["seed_base"],
+                        with_grad=True)
+    q, k, v, do = (x[t].cuda() for t in ("q", "k", "v", "do"))
+    p = ops.make_problem(q, h, w, L)
+    fwd = ops.llsa_forward(p, q, k, v)
+    dq, dk, dv = ops.llsa_backward(p, q, k, v, fwd, do)
+    torch.cuda.synchronize()
+    step = Step(p, q, k, v, do)
+    step.capture()
+    for _ in range(3):
+        step.replay()
+    torch.cuda.synchronize()
+    for name, ref in (("o", fwd["o"]), ("lse", fwd["lse"]), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.equal(_bits(getattr(step, name)), _bits(ref)), name
+    for a, b in zip(step.sel, fwd["sel"]):
+        assert torch.equal(a, b)
