@@ -302,6 +302,9 @@ def test_attn_bwd_on_oracle_indices(h, w, levels, topk, enrich, layout):
     (128, 128, 1, 8, False, 1.0),    # every query block picks blocks 0..7: 1024 picks each
     (128, 128, 2, 8, True, 0.5),     # half the query blocks do, the rest pick their own
     (64, 128, 1, 16, False, 0.9),
+    (256, 256, 3, 8, True, 1.0),     # full size: 8 blocks of 4096 picks, 248 overflow chunks
+    (256, 256, 3, 8, True, 0.3),     # (the most a head's chunk slots can hold is 256)
+    (256, 256, 2, 16, True, 0.7),    # 16 picks: 16 blocks of ~2900 picks
 ])
 def test_attn_bwd_popular_key_blocks(h, w, levels, topk, enrich, popular):
     """Backward on selections where a few key blocks are picked by (nearly) every query block,
