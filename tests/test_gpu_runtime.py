@@ -15,17 +15,20 @@ def _bits(t):
     return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32)
 
 
-def _make(h=128, w=128, levels=2, batch=1, heads=2, seed=61, fuse_prologue=True):
+def _make(h=128, w=128, levels=2, batch=1, heads=2, seed=61, fuse_prologue=True, block=16):
     x = gen.make_inputs(batch, heads, h, w, 64, torch.bfloat16, seed, with_grad=True)
     q, k, v, do = (x[t].cuda() for t in ("q", "k", "v", "do"))
-    return Step(ops.make_problem(q, h, w, levels), q, k, v, do, fuse_prologue=fuse_prologue)
+    return Step(ops.make_problem(q, h, w, levels, block=block), q, k, v, do,
+                fuse_prologue=fuse_prologue)
 
 
-@pytest.mark.parametrize("h,w,levels", [(128, 128, 2), (128, 256, 3)])
-def test_graph_replays_match_eager(h, w, levels):
+@pytest.mark.parametrize("h,w,levels,block", [(128, 128, 2, 16), (128, 256, 3, 16),
+                                              (256, 256, 2, 64)])
+def test_graph_replays_match_eager(h, w, levels, block):
     """The reference is the eager one-stream step with llsa_pool + llsa_select; the graph is
-    the overlapped step with llsa_pool_select."""
-    step = _make(h, w, levels, fuse_prologue=False)
+    the overlapped step with llsa_pool_select (with block 64 it runs the two plain calls, and
+    the step expands the level-1 picks to 16-token blocks)."""
+    step = _make(h, w, levels, fuse_prologue=False, block=block)
     step.run(overlap=False)    # one stream: the reference for the overlapped graph
     torch.cuda.synchronize()
     want = {k: v.clone() for k, v in step.outputs().items() if k != "sel"}
