@@ -766,11 +766,14 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
 
   // keys of this block as B operands: lane (n, g) holds row n, channels 32s + 8g .. +7
   const int krow = block_corner(j, a.grid) + tile_offset(n, a.grid);
+  // (the key-major pass over CSC_1 loads them once it knows the block has picks: below)
   bf16x8 kh[2], vh[2];
+  if constexpr (MODE != kKeyCsc) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    kh[s] = buf_load8(rk, (uint32_t)(krow * kDim + 32 * s + 8 * g) * 2);
-    vh[s] = buf_load8(rv, (uint32_t)(krow * kDim + 32 * s + 8 * g) * 2);
+    for (int s = 0; s < 2; ++s) {
+      kh[s] = buf_load8(rk, (uint32_t)(krow * kDim + 32 * s + 8 * g) * 2);
+      vh[s] = buf_load8(rv, (uint32_t)(krow * kDim + 32 * s + 8 * g) * 2);
+    }
   }
 
   // lane-constant offsets: staged rows (bytes) and this lane's 4 queries per tile (tokens)
@@ -896,9 +899,45 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
     const int32_t* rows = a.csc_rows[0] + (long)head * n1 * a.fine_k;
     const int e0 = uniform(off[j] + chunk * kKeyChunk);
     const int e1 = uniform(min(off[j + 1], e0 + kKeyChunk));
+    int first_rows = -1;
+    if constexpr (MODE == kKeyCsc) {
+      // A third of the key blocks have no picks and need no key rows.  The others load them
+      // as whole 128-byte lines (lane l: row l / 8 + 8 m, piece l % 8; the vector memory path
+      // pays per line, and the B-operand layout would touch 16 half lines per load), request
+      // the first batch's CSC rows before waiting for them, and rearrange them through the
+      // still unused staging tiles into the B-operand layout (row n, channels 32 s + 8 g).
+      if (e1 > e0) {
+        i32x4 kl[2], vl[2];
+        const uint32_t kbase = (uint32_t)block_corner(j, a.grid) * kDim * 2;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int r = (lane >> 3) + 8 * m;
+          const uint32_t o =
+              kbase + (uint32_t)tile_offset(r, a.grid) * kDim * 2 + 16 * (lane & 7);
+          kl[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
+          vl[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0);
+        }
+        first_rows = lane < min(64, e1 - e0) ? rows[e0 + lane] : -1;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int at = ((lane >> 3) + 8 * m) * kStride + 8 * (lane & 7);
+          *(i32x4*)(stQ + at) = kl[m];
+          *(i32x4*)(stO + at) = vl[m];
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          kh[s] = lds_row8(stQ, n, s, g);
+          vh[s] = lds_row8(stO, n, s, g);
+        }
+        wave_lds_sync();
+      }
+    }
     for (int base = e0; base < e1; base += 64) {
       const int count = min(64, e1 - base);
-      batch(count, lane < count ? rows[base + lane] : -1);
+      const int pl = MODE == kKeyCsc && base == e0 ? first_rows
+                                                   : (lane < count ? rows[base + lane] : -1);
+      batch(count, pl);
     }
   } else {
     // column j of the mask, 64 query blocks per step; hits are appended to pend in order and
