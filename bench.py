@@ -514,9 +514,9 @@ def main():
                                                          min(args.warmup, 3))}))
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
-                                   "part of it (the op shards over (batch, head) with no "
-                                   "exchange, see the design notes)", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "llsa runs on one GPU: multi-GPU runs are not implemented "
+                                   "(the op shards over (batch, head) with no exchange)",
+                          "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
 
