@@ -5,10 +5,15 @@ resident in HBM: pooling -> coarse-to-fine selection -> sparse attention forward
 transpose of every level -> sparse backward (dQ, dK, dV); the Morton reorder is folded into
 the kernels' addressing (inputs and outputs stay in raster order).  The step is captured once
 into a HIP graph and replayed; `value` is batch*N tokens per second of graph replays.  A
-second, eager pass with per-kernel HIP events gives each kernel's launch duration; the
-roofline object is for the kernel with the largest total time, against the vendor HBM peak
-and against the achievable peak the library's own streaming-copy kernel reaches
-(`extra.calibration`, with the MFMA-only loop's bf16 rate).  Prints one JSON line.
+second, eager pass with per-kernel HIP events (recorded by the library on each kernel's own
+stream) gives each kernel's launch duration.  Every row of the path is priced as a unit
+(`extra.units`: its algorithmic bytes per step over the summed time of its launches); the
+roofline object is for the unit with the largest time (the backward: its four kernels),
+against the vendor HBM peak and against the achievable peak the library's own streaming-copy
+kernel reaches (`extra.calibration`, with the MFMA-only loop's bf16 rate).  The pooling,
+selection and transpose kernels get their own HBM fractions (`extra.side_kernels`, units).
+The CPU baseline runs the oracle over the whole workload on the host's cores first, before
+the GPU is touched.  Prints one JSON line.
 
 Beside the headline, `extra` carries:
   * configs: every workload (forward only for the three forward configs, forward + backward
@@ -42,11 +47,6 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 FP32_MFMA_PEAK_TFLOPS = 157.3    # fp32 (the fp32 workload runs on the fp32 MFMA)
-KERNEL_SOURCES = {               # kernel -> source file (the traffic record is tied to it)
-    "attn_fwd_kernel": "attn_fwd.hip",
-    "bwd_query_kernel": "attn_bwd.hip",
-    "bwd_key_kernel": "attn_bwd.hip",
-}
 
 
 def parse():
@@ -109,48 +109,118 @@ def torch_bf16():
     return torch.bfloat16
 
 
-def traffic_record(kernel, config):
-    """Measured HBM bytes per launch from the committed counter record, if it was taken on the
-    current source of the kernel; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json")
+def unit_model(p):
+    """Algorithmic HBM bytes (and FLOPs) per step of each row of the hot path, with the kernels
+    that run it inside the benchmarked step.  Returns (units, side): the units of the scope
+    table's measurement section, and the pooling / selection kernels one by one.
+
+    T = one [b, H, N, 64] token tensor, L_l = one fp32 pooled level l of one tensor.
+      * forward (a5): per query token q, o and its share of K and V read once (4 d bytes of
+        the token dtype) plus its fp32 LSE;
+      * backward (a7): per query token Q, K, V, O, dO read and dQ, dK, dV written (8 d bytes)
+        plus LSE and D (this path recomputes D and never reads O, so it moves 7 of the 8
+        token tensors, but the unit is priced as stated);
+      * pooling and selection (a2-a4, one llsa_pool_select call): the three token tensors
+        read once, every stored level written (V's level 1 is not stored), each level >= 3
+        pooled from the one below; every pooled level of Q and K read once by the selection
+        and every selection written.  Its kernels: pool12 (Q and K: 2T read, levels 1-2
+        written), pool_next (Q and K levels >= 3, V's >= 4) and select_pool (the two
+        selection launches, which also pool V: T read, its levels 2-3 written);
+      * index transpose (a6): per level, the selection read and its CSC written (offsets and
+        rows).
+    Attention FLOPs: forward 4 k_q d, backward 10 k_q d per query (k_q keys per query)."""
+    bh, n, d, K, L = p.batch * p.heads, p.n, p.head_dim, p.topk, p.levels
+    es = 2 if p.torch_dtype == torch_bf16() else 4
+    tokens = bh * n
+    T = tokens * d * es
+    kq = 16 * p.fine_k + p.coarse_levels * K
+    lvb = lambda l: bh * p.n_level(l) * d * 4 if l <= L else 0      # noqa: E731
+    selection = 2 * sum(lvb(l) for l in range(1, L + 1)) + sum(
+        bh * p.n_level(l) * K * 4 for l in range(1, L + 1))
+    side = {
+        "pool12_kernel": 2 * T + 2 * (lvb(1) + lvb(2)),
+        "pool_next_kernel": sum(2 * (lvb(l - 1) + lvb(l)) for l in range(3, L + 1)) +
+                            sum(lvb(l - 1) + lvb(l) for l in range(4, L + 1)),
+        "select_pool_kernel": T + lvb(2) + (lvb(2) + lvb(3) if L >= 3 else 0) + selection,
+    }
+    units = {
+        "pool_select": dict(kernels=list(side), bytes=sum(side.values()),
+                            flops=2 * d * bh * (p.n_level(L) ** 2 + sum(
+                                p.n_level(l) * K * p.block for l in range(1, L)))),
+        "attn_fwd": dict(kernels=["attn_fwd_kernel"], bytes=tokens * (4 * d * es + 4),
+                         flops=4 * tokens * kq * d),
+        "index_transpose": dict(
+            kernels=["tile_sort_kernel", "merge_kernel", "csc_bounds_kernel",
+                     "csc_offsets_kernel", "csc_scatter_kernel"],
+            bytes=sum(bh * (2 * nl * kk * 4 + (nl + 1) * 4)
+                      for nl, kk in (p.csc_dims(l) for l in range(1, 2 + p.coarse_levels))),
+            flops=0),
+        "attn_bwd": dict(kernels=["bwd_query_kernel", "coarse_grad_kernel",
+                                  "bwd_key_overflow_kernel", "bwd_key_kernel"],
+                         bytes=tokens * (8 * d * es + 8), flops=10 * tokens * kq * d),
+    }
+    return units, side
+
+
+def traffic_record(config):
+    """Measured HBM bytes per launch of every kernel of the step, from the committed counter
+    record of the workload; a kernel's entry counts only if it was taken on the current source
+    of the kernel's file."""
+    path = os.path.join(ROOT, "profiles", f"{config}_traffic.json")
     if not os.path.exists(path):
-        return None
+        return {}
     rec = json.load(open(path))
-    src = os.path.join(ROOT, "hierarchical_top_sparse_amd", "csrc", KERNEL_SOURCES[kernel])
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
-        return None
-    return rec
+    out = {}
+    for name, k in rec.get("kernels", {}).items():
+        src = os.path.join(ROOT, k["source"])
+        if not os.path.exists(src):
+            continue
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() == k.get("source_sha256"):
+            out[name] = k
+    return out
 
 
-def cpu_baseline(cfg, x, seconds_budget=12.0):
-    """The oracle (as it stands), single-threaded, on whole (batch, head) slices of the same
-    inputs, fwd + bwd, until the time budget is used; scaled to whole-workload tokens/s."""
-    import torch
+_CPU_SLICES = None   # fp32 copies of the workload's tensors, set before the worker pool forks
+
+
+def _cpu_slice(task):
+    """The oracle's forward + backward on one (batch, head) slice (in a worker process, with
+    single-threaded BLAS); returns the seconds it took."""
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import llsa_oracle as orc
-
-    h, w, L = cfg["height"], cfg["width"], cfg["levels"]
-    slices = [(b, hh) for b in range(cfg["batch"]) for hh in range(cfg["heads"])]
-    done, spent = 0, 0.0
+    b, hh, h, w, L = task
     with threadpool_limits(1):
-        nthreads = torch.get_num_threads()
-        torch.set_num_threads(1)
-        for b, hh in slices:
-            r = {t: x[t][b:b + 1, hh:hh + 1].double().numpy() for t in ("q", "k", "v", "do")}
-            t0 = time.perf_counter()
-            res = orc.llsa_forward(r["q"], r["k"], r["v"], h, w, 16, L, 8, True)
-            orc.llsa_backward(r["q"], r["k"], r["v"], r["do"], h, w, 16, L, res["sel"], True)
-            spent += time.perf_counter() - t0
-            done += 1
-            if spent >= seconds_budget:
-                break
-        torch.set_num_threads(nthreads)
-    tokens = cfg["batch"] * h * w * done / len(slices)
-    return dict(value=round(tokens / spent, 1), unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{done} of {len(slices)} (batch, head) slices of the workload, fwd+bwd "
-                       f"in {spent:.1f} s on one thread; tokens counted pro rata")
+        r = {t: _CPU_SLICES[t][b:b + 1, hh:hh + 1].astype(np.float64)
+             for t in ("q", "k", "v", "do")}
+        t0 = time.perf_counter()
+        res = orc.llsa_forward(r["q"], r["k"], r["v"], h, w, 16, L, 8, True)
+        orc.llsa_backward(r["q"], r["k"], r["v"], r["do"], h, w, 16, L, res["sel"], True)
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(cfg, x):
+    """The oracle (as it stands) over the whole workload on the host's cores: its (batch,
+    head) slices are independent, so one worker process per core runs them (single-threaded
+    BLAS each; the oracle is bound by its Python loops, and threads or more BLAS threads do
+    not speed it up).  Must run before anything touches the GPU: the workers are forked."""
+    import multiprocessing as mp
+    global _CPU_SLICES
+    h, w, L = cfg["height"], cfg["width"], cfg["levels"]
+    _CPU_SLICES = {t: x[t].float().numpy() for t in ("q", "k", "v", "do")}
+    slices = [(b, hh, h, w, L) for b in range(cfg["batch"]) for hh in range(cfg["heads"])]
+    workers = max(1, min(len(os.sched_getaffinity(0)), 16, len(slices)))
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        busy = pool.map(_cpu_slice, slices, chunksize=1)
+    wall = time.perf_counter() - t0
+    _CPU_SLICES = None
+    tokens = cfg["batch"] * h * w
+    return dict(value=round(tokens / wall, 1), unit="tokens/s", cores=workers, kind="oracle",
+                sample=f"the whole workload: all {len(slices)} (batch, head) slices, fwd+bwd, "
+                       f"in {wall:.1f} s wall on {workers} worker processes (one per host "
+                       f"core, single-threaded BLAS); {sum(busy):.1f} s of CPU work")
 
 
 def _event_ms(fn, reps):
@@ -256,8 +326,9 @@ def kernel_fractions(p, per_kernel_ms):
     return out
 
 
-def make_step(cfg_name, layout="raster", backward=None, levels=None, topk=8):
-    """A runtime Step over the workload's inputs; levels/topk override its L and K."""
+def make_step(cfg_name, layout="raster", backward=None, levels=None, topk=8, x=None):
+    """A runtime Step over the workload's inputs (x: the generator's CPU tensors, made here if
+    not given); levels/topk override its L and K."""
     import torch
 
     from hierarchical_top_sparse_amd import gen, ops
@@ -266,8 +337,9 @@ def make_step(cfg_name, layout="raster", backward=None, levels=None, topk=8):
     h, w = cfg["height"], cfg["width"]
     L = levels or cfg["levels"]
     bwd = cfg["backward"] if backward is None else backward
-    x = gen.make_inputs(cfg["batch"], cfg["heads"], h, w, 64, cfg["dtype"], cfg["seed_base"],
-                        with_grad=bwd)
+    if x is None:
+        x = gen.make_inputs(cfg["batch"], cfg["heads"], h, w, 64, cfg["dtype"],
+                            cfg["seed_base"], with_grad=bwd)
     dev = torch.device("cuda:0")
     q, k, v = (x[t].to(dev) for t in ("q", "k", "v"))
     do = x["do"].to(dev) if bwd else None
@@ -520,11 +592,18 @@ def main():
         sys.exit(2)
     import torch
 
+    from hierarchical_top_sparse_amd import gen
+    cfg = gen.CONFIGS[args.config]
+    h, w, L = cfg["height"], cfg["width"], cfg["levels"]
+    x = gen.make_inputs(cfg["batch"], cfg["heads"], h, w, 64, cfg["dtype"], cfg["seed_base"],
+                        with_grad=cfg["backward"])
+    # the CPU leg first: its worker processes are forked before anything touches the GPU
+    cpu = None if args.no_cpu else cpu_baseline(cfg, x)
+
     from hierarchical_top_sparse_amd import _abi
 
-    step, x, cfg = make_step(args.config, args.layout)
+    step, x, cfg = make_step(args.config, args.layout, x=x)
     p = step.p
-    h, w, L = cfg["height"], cfg["width"], cfg["levels"]
     copy = None
     if args.with_copy:
         copy_dst = torch.empty_like(step.q)
@@ -534,20 +613,43 @@ def main():
     tokens = cfg["batch"] * h * w
     value = tokens / (ms_step / 1e3)
 
-    # ---- roofline of the dominant kernel
-    model = kernel_model(p)
-    dominant = max((kname for kname in per_step_kernel_ms if kname in model),
-                   key=lambda kname: per_step_kernel_ms[kname])
-    launch_ms = per_kernel_ms[dominant]
-    achieved = model[dominant]["bytes"] / (launch_ms / 1e3) / 1e9
-    rec = traffic_record(dominant, args.config)
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": rec["hbm_bytes_per_launch"] if rec else None,
-                "alg_bytes_per_launch": model[dominant]["bytes"],
-                "launch_ms": round(launch_ms, 4),
-                "mfma_frac": round(model[dominant]["flops"] / (launch_ms / 1e3) / 1e12 /
-                                   BF16_MFMA_PEAK_TFLOPS, 4)}
+    # ---- rows of the hot path as units (algorithmic bytes per step / their kernels' time
+    # per step); the roofline object is for the unit with the largest time
+    units, side = unit_model(p)
+    traffic = traffic_record(args.config)
+    launches = {kn: per_step_kernel_ms[kn] / per_kernel_ms[kn] for kn in per_kernel_ms}
+    unit_rows = {}
+    for uname, u in units.items():
+        ms = sum(per_step_kernel_ms.get(kn, 0.0) for kn in u["kernels"])
+        if ms <= 0:
+            continue
+        ran = [kn for kn in u["kernels"] if kn in per_step_kernel_ms]
+        measured = (sum(traffic[kn]["hbm_bytes_per_launch"] * launches[kn] for kn in ran)
+                    if all(kn in traffic for kn in ran) else None)
+        unit_rows[uname] = {
+            "kernels": ran, "ms_per_step": round(ms, 4), "alg_bytes": u["bytes"],
+            "achieved_GBps": round(u["bytes"] / (ms / 1e3) / 1e9, 1),
+            "hbm_frac": round(u["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(u["flops"] / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": measured}
+    side_rows = {}
+    for kn, nbytes in side.items():
+        if kn in per_step_kernel_ms:
+            ms = per_step_kernel_ms[kn]
+            side_rows[kn] = {"ms_per_step": round(ms, 4), "alg_bytes": nbytes,
+                             "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                             "traffic": (traffic[kn]["hbm_bytes_per_launch"] * launches[kn]
+                                         if kn in traffic else None)}
+    dominant = max(unit_rows, key=lambda u: unit_rows[u]["ms_per_step"])
+    dom = unit_rows[dominant]
+    launch_ms = dom["ms_per_step"]
+    achieved = dom["achieved_GBps"]
+    roofline = {"bound": "hbm",
+                "kernel": f"{dominant} ({' + '.join(dom['kernels'])})",
+                "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": dom["traffic"],
+                "alg_bytes_per_launch": dom["alg_bytes"], "launch_ms": launch_ms,
+                "mfma_frac": dom["mfma_frac"]}
     calib = calibration()
     roofline["achievable_peak"] = calib["copy_GBps"]
     roofline["frac_of_achievable"] = round(achieved / calib["copy_GBps"], 4)
@@ -557,6 +659,7 @@ def main():
              "per_kernel_ms_per_step": {k2: round(v2, 4) for k2, v2 in
                                         sorted(per_step_kernel_ms.items(),
                                                key=lambda kv: -kv[1])},
+             "units": unit_rows, "side_kernels": side_rows,
              "attention_kernels": kernel_fractions(p, per_kernel_ms)}
     del step
     if not args.no_configs:
@@ -583,7 +686,6 @@ def main():
         extra["mask_backward_comparator"] = mask_comparator(qd, kd, vd, dod, h, w,
                                                             max(5, args.steps // 2))
         del qd, kd, vd, dod
-    cpu = None if args.no_cpu else cpu_baseline(cfg, x)
     line = {
         "metric": "LLSA fwd+bwd tokens/s at 256x256 pixels (65,536 tok); % MFMA/HBM peak",
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

@@ -121,19 +121,32 @@ def llsa_backward_masked(p: Problem, q, k, v, fwd: dict, dout):
 
 
 class _LLSAFunction(torch.autograd.Function):
+    """The backward reads q, k, v, the LSE, the pooled K/V levels and the selections of the
+    forward; those go through save_for_backward (freed once the backward has run).  The output
+    o and the pooled Q are not kept: storing the forward's dict on ctx would make a reference
+    cycle (output -> grad_fn -> ctx -> output) that only the cycle collector frees."""
+
     @staticmethod
     def forward(ctx, q, k, v, p):
         q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
         fwd = llsa_forward(p, q, k, v)
         ctx.p = p
-        ctx.fwd = fwd
-        ctx.save_for_backward(q, k, v)
+        L = p.levels
+        ctx.save_for_backward(q, k, v, fwd["lse"], fwd["fine"], *fwd["k_lv"], *fwd["v_lv"],
+                              *fwd["sel"])
+        ctx.levels = L
         return fwd["o"]
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v = ctx.saved_tensors
-        dq, dk, dv = llsa_backward(ctx.p, q, k, v, ctx.fwd, dout.contiguous())
+        saved = ctx.saved_tensors
+        L = ctx.levels
+        q, k, v, lse, fine = saved[:5]
+        k_lv = list(saved[5:5 + L])
+        v_lv = list(saved[5 + L:5 + 2 * L])
+        sel = list(saved[5 + 2 * L:5 + 3 * L])
+        fwd = dict(lse=lse, fine=fine, k_lv=k_lv, v_lv=v_lv, sel=sel)
+        dq, dk, dv = llsa_backward(ctx.p, q, k, v, fwd, dout.contiguous())
         return dq, dk, dv, None
 
 

@@ -1,0 +1,166 @@
+"""Summaries of rocprofv3 output for the library's kernels (a measurement aid, not part of the
+method): the per-kernel time table of a `--kernel-trace --stats` run, and the HBM traffic per
+launch of every kernel from two `--pmc` runs (FETCH_SIZE, then WRITE_SIZE).
+
+Counters are scaled by what they read for a plain copy of known size in the same run: the
+benchmark's `--with-copy` launches one Morton reorder of a token tensor (T bytes read, T bytes
+written) per step, so fetched bytes = FETCH_SIZE * (T / FETCH_SIZE of the copy) and likewise
+for writes.
+
+  python -m hierarchical_top_sparse_amd.profiling stats <run>_kernel_stats.csv --title ...
+         --command ...                                   (markdown table on stdout)
+  python -m hierarchical_top_sparse_amd.profiling traffic --fetch <fetch>_counter_collection.csv
+         --write <write>_counter_collection.csv --copy-bytes T --workload px256_train
+         --command ... --command ... > profiles/<workload>_traffic.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = "hierarchical_top_sparse_amd/csrc"
+
+# device symbol (without namespace and template arguments) -> the name the library's event
+# profiler gives its launches, and the file the kernel is compiled from
+_KERNELS = {
+    "pool12_bf16_kernel": ("pool12_kernel", "pool.hip"),
+    "pool12_f32_kernel": ("pool12_kernel", "pool.hip"),
+    "pool_next_kernel": ("pool_next_kernel", "pool.hip"),
+    "pool_next_v_kernel": ("pool_next_kernel", "select.hip"),
+    "select_kernel": ("select_kernel", "select.hip"),
+    "select_pool12_kernel": ("select_pool_kernel", "select.hip"),
+    "select_pool_next_kernel": ("select_pool_kernel", "select.hip"),
+    "expand_kernel": ("expand_kernel", "select.hip"),
+    "attn_fwd_kernel": ("attn_fwd_kernel", "attn_fwd.hip"),
+    "tile_sort_kernel": ("tile_sort_kernel", "transpose.hip"),
+    "merge_kernel": ("merge_kernel", "transpose.hip"),
+    "csc_bounds_kernel": ("csc_bounds_kernel", "transpose.hip"),
+    "csc_offsets_kernel": ("csc_offsets_kernel", "transpose.hip"),
+    "csc_scatter_kernel": ("csc_scatter_kernel", "transpose.hip"),
+    "bwd_query_kernel": ("bwd_query_kernel", "attn_bwd.hip"),
+    "coarse_grad_kernel": ("coarse_grad_kernel", "attn_bwd.hip"),
+    "reorder_kernel": ("reorder_kernel", "reorder.hip"),
+    "copy_kernel": ("copy_kernel", "calib.hip"),
+    "mfma_kernel": ("mfma_kernel", "calib.hip"),
+}
+# bwd_key_kernel<MODE>: 0 = the CSC pass, 1 = the mask-scanning comparator, 2 = overflow chunks
+_KEY_MODES = {"0": "bwd_key_kernel", "1": "bwd_key_mask_kernel", "2": "bwd_key_overflow_kernel"}
+
+
+def profile_name(symbol: str):
+    """(profiler name, source file) of a demangled kernel symbol, or None if not ours."""
+    m = re.match(r"\s*(?:void\s+)?(?:llsa::)?(\w+)(?:<([^>]*)>)?", symbol)
+    if not m:
+        return None
+    base, targs = m.group(1), m.group(2)
+    if base == "bwd_key_kernel":
+        return _KEY_MODES.get((targs or "").strip(), "bwd_key_kernel"), "attn_bwd.hip"
+    return _KERNELS.get(base)
+
+
+def _col(row: dict, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError(f"none of {names} in {sorted(row)}")
+
+
+def kernel_stats_table(path: str) -> list:
+    """Rows (symbol, calls, avg_us, min_us, max_us, percent) of a rocprofv3 kernel_stats.csv."""
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append((_col(r, "Name", "KERNEL_NAME"), int(_col(r, "Calls")),
+                         float(_col(r, "AverageNs")) / 1e3, float(_col(r, "MinNs")) / 1e3,
+                         float(_col(r, "MaxNs")) / 1e3, float(_col(r, "Percentage"))))
+    rows.sort(key=lambda t: -t[5])
+    return rows
+
+
+def counters_per_kernel(path: str, counter: str) -> dict:
+    """Mean value of `counter` per dispatch of each profiler name (with its dispatch count)."""
+    tot, cnt = defaultdict(float), defaultdict(int)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if _col(r, "Counter_Name") != counter:
+                continue
+            key = profile_name(_col(r, "Kernel_Name"))
+            if key is None:
+                continue
+            tot[key[0]] += float(_col(r, "Counter_Value"))
+            cnt[key[0]] += 1
+    return {k: (tot[k] / cnt[k], cnt[k]) for k in tot}
+
+
+def traffic_record(fetch_csv, write_csv, copy_bytes, workload, commands) -> dict:
+    fetch = counters_per_kernel(fetch_csv, "FETCH_SIZE")
+    write = counters_per_kernel(write_csv, "WRITE_SIZE")
+    if "reorder_kernel" not in fetch or "reorder_kernel" not in write:
+        raise SystemExit("no calibration copy (reorder_kernel) in the counter runs: run the "
+                         "benchmark with --with-copy")
+    kib = copy_bytes / 1024.0
+    fscale = kib / fetch["reorder_kernel"][0]
+    wscale = kib / write["reorder_kernel"][0]
+    sources = {}   # a profiler name's first listed source (pool_next_kernel: pool.hip)
+    for name, src in list(_KERNELS.values()) + [(v, "attn_bwd.hip")
+                                                for v in _KEY_MODES.values()]:
+        sources.setdefault(name, src)
+    kernels = {}
+    for name in sorted(set(fetch) & set(write)):
+        if name == "reorder_kernel":
+            continue
+        src = f"{CSRC}/{sources[name]}"
+        rd = fetch[name][0] * fscale * 1024.0
+        wr = write[name][0] * wscale * 1024.0
+        kernels[name] = {
+            "source": src,
+            "source_sha256": hashlib.sha256(open(os.path.join(ROOT, src), "rb").read())
+            .hexdigest(),
+            "dispatches": fetch[name][1],
+            "fetch_size_kib_per_dispatch": round(fetch[name][0], 1),
+            "write_size_kib_per_dispatch": round(write[name][0], 1),
+            "hbm_read_bytes_per_launch": int(rd), "hbm_write_bytes_per_launch": int(wr),
+            "hbm_bytes_per_launch": int(rd + wr)}
+    return {"workload": workload,
+            "calibration": f"reorder_kernel, a plain copy of {copy_bytes} bytes: FETCH_SIZE "
+                           f"{fetch['reorder_kernel'][0]:.1f} KiB, WRITE_SIZE "
+                           f"{write['reorder_kernel'][0]:.1f} KiB per dispatch",
+            "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4),
+            "commands": commands, "kernels": kernels}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    st = sub.add_parser("stats")
+    st.add_argument("csv")
+    st.add_argument("--title", required=True)
+    st.add_argument("--command", required=True)
+    tr = sub.add_parser("traffic")
+    tr.add_argument("--fetch", required=True)
+    tr.add_argument("--write", required=True)
+    tr.add_argument("--copy-bytes", type=int, required=True)
+    tr.add_argument("--workload", required=True)
+    tr.add_argument("--command", action="append", default=[])
+    a = ap.parse_args(argv)
+    if a.what == "stats":
+        print(f"# {a.title}\n\nCommand (GPU box, repo root; `TMPDIR=/tmp`):\n\n```\n{a.command}\n"
+              f"```\n\n| kernel | calls | avg µs | min µs | max µs | % of GPU time |\n"
+              f"|---|---:|---:|---:|---:|---:|")
+        for sym, calls, avg, mn, mx, pct in kernel_stats_table(a.csv):
+            print(f"| `{sym}` | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.2f} |")
+    else:
+        json.dump(traffic_record(a.fetch, a.write, a.copy_bytes, a.workload, a.command),
+                  sys.stdout, indent=1)
+        print()
+
+
+if __name__ == "__main__":
+    main()

@@ -79,3 +79,74 @@ def test_training_step_runs(mode):
     assert torch.isfinite(loss)
     moved = sum(int(not torch.equal(p0, p.detach())) for p0, p in zip(before, m.parameters()))
     assert moved == len(before)
+
+
+def _capture_attention_io(h, w, depth, levels, block_index, monkeypatch, seed=5):
+    """Runs one Pixel-DiT-S training forward/backward (bf16 autocast, Morton order hoisted to
+    the network's entry) and returns the Q, K, V that block `block_index`'s attention module
+    hands to LLSA and the gradient the network sends back into its output."""
+    from hierarchical_top_sparse_amd import ops
+    seen = {"calls": 0}
+    real = ops.llsa_attention
+
+    def spy(q, k, v, *args, **kw):
+        o = real(q, k, v, *args, **kw)
+        if seen["calls"] == block_index:
+            seen["qkv"] = tuple(t.detach().clone() for t in (q, k, v))
+            seen["kw"] = kw
+            o.register_hook(lambda g: seen.__setitem__("do", g.detach().contiguous()))
+        seen["calls"] += 1
+        return o
+
+    monkeypatch.setattr(ops, "llsa_attention", spy)
+    torch.manual_seed(seed)
+    m = dit.PixelDiT(h, w, depth=depth, levels=levels).cuda()
+    xt, noise, t, y = dit.synthetic_batch(2, h, w, "cuda", seed=seed)
+    with torch.autocast(device_type="cuda", dtype=torch.bfloat16):
+        pred = m(xt, t, y)
+    torch.nn.functional.mse_loss(pred.float(), noise).backward()
+    torch.cuda.synchronize()
+    monkeypatch.setattr(ops, "llsa_attention", real)
+    return seen
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("h,w,levels,block_index,heads_checked", [
+    (64, 64, 2, 1, None),          # every head of the second block
+    (128, 128, 2, 0, [(0, 0), (1, 3), (1, 5)]),   # FFHQ-128 Pixel DiT-S shape, first block
+])
+def test_llsa_on_model_produced_qkv_matches_oracle(h, w, levels, block_index, heads_checked,
+                                                   monkeypatch):
+    """Pixel-DiT-S (hidden 384, 6 heads, 1x1 patches) as trained on the pages' FFHQ setting:
+    the Q, K, V one attention module produces inside the network (Morton layout) and the
+    gradient the network returns into its output go through LLSA via the library's ops; the
+    selection is checked against the oracle's within the tie window, and O, LSE, dQ, dK, dV
+    against the oracle attention on the GPU's selection at the acceptance bounds."""
+    from hierarchical_top_sparse_amd import ops
+    from tests.parity_util import (assert_close, check_level, lse_tolerance, to64)
+    seen = _capture_attention_io(h, w, 2, levels, block_index, monkeypatch)
+    q, k, v = seen["qkv"]
+    do = seen["do"]
+    assert q.dtype == torch.bfloat16 and q.shape == (2, 6, h * w, 64)
+    assert do.dtype == torch.bfloat16 and do.shape == q.shape
+    p = ops.make_problem(q, h, w, levels, 8, layout=ops.LLSA_LAYOUT_MORTON)
+    fwd = ops.llsa_forward(p, q, k, v)
+    dq, dk, dv = ops.llsa_backward(p, q, k, v, fwd, do)
+    torch.cuda.synchronize()
+    sel = [s.cpu().numpy().astype(np.int64) for s in fwd["sel"]]
+    pairs = heads_checked or [(b, hh) for b in range(2) for hh in range(6)]
+    for b, hh in pairs:
+        qm, km, vm, dom = (to64(t[b, hh]) for t in (q, k, v, do))   # Morton order already
+        q_lv, k_lv, v_lv = (orc.pool_levels(x, 16, levels) for x in (qm, km, vm))
+        for l in range(levels, 0, -1):
+            parent = None if l == levels else sel[l][b, hh]
+            check_level(sel[l - 1][b, hh], q_lv[l - 1], k_lv[l - 1], parent, 8,
+                        f"DiT b{b} h{hh} level {l}")
+        s = [x[b, hh] for x in sel]
+        o_want, lse_want = orc.attention_forward(qm, km, vm, k_lv, v_lv, s, 16, True)
+        assert_close(fwd["o"][b, hh], o_want, torch.bfloat16, f"DiT o b{b} h{hh}")
+        assert_close(fwd["lse"][b, hh], lse_want, torch.bfloat16, f"DiT lse b{b} h{hh}",
+                     tol_abs=lse_tolerance(qm, km, torch.bfloat16, levels))
+        want = orc.attention_backward(qm, km, vm, k_lv, v_lv, s, dom, 16, True)
+        for name, got, ref_g in zip(("dq", "dk", "dv"), (dq, dk, dv), want):
+            assert_close(got[b, hh], ref_g, torch.bfloat16, f"DiT {name} b{b} h{hh}")

@@ -344,6 +344,57 @@ def test_constant_values_and_normalisation():
         assert np.allclose(np.exp(s - lse[p * 16:(p + 1) * 16, None]).sum(1), 1.0, atol=1e-12)
 
 
+@pytest.mark.parametrize("enrich", [False, True])
+def test_attention_forward_restricted_blocks(enrich):
+    """attention_forward(blocks=...) fills exactly the rows of the given query blocks, equal to
+    the dense-mask formulation's rows (torch SDPA), and leaves the others NaN; all blocks give
+    the unrestricted result."""
+    B = 4
+    q, k, v, kl, vl, sel = _attn_case(13, n=1024, d=8, B=B, L=3, K=3)
+    blocks = [0, 5, 17, 255]
+    o, lse = orc.attention_forward(q, k, v, kl, vl, sel, B, enrich, blocks=blocks)
+    ref = _dense_mask_formulation(torch.tensor(q), torch.tensor(k), torch.tensor(v), sel, B,
+                                  enrich, 1 / math.sqrt(q.shape[1])).numpy()
+    rows = np.concatenate([np.arange(b * B, b * B + B) for b in blocks])
+    others = np.setdiff1d(np.arange(q.shape[0]), rows)
+    assert np.allclose(o[rows], ref[rows], rtol=0, atol=1e-12)
+    assert np.isnan(o[others]).all() and np.isnan(lse[others]).all()
+    assert np.isfinite(lse[rows]).all()
+    o_all, lse_all = orc.attention_forward(q, k, v, kl, vl, sel, B, enrich,
+                                           blocks=range(q.shape[0] // B))
+    o_ref, lse_ref = orc.attention_forward(q, k, v, kl, vl, sel, B, enrich)
+    assert np.array_equal(o_all, o_ref) and np.array_equal(lse_all, lse_ref)
+
+
+def test_attention_backward_restricted_blocks():
+    """attention_backward(blocks=users of some key blocks), no enrichment: the users' dq rows
+    and the key blocks' dk, dv rows equal torch float64 autograd of the dense-mask
+    formulation (a key block's gradient comes only from the query blocks that picked it);
+    with enrichment the given blocks' dq rows still do; all blocks give the full result."""
+    B = 4
+    for enrich in (False, True):
+        q, k, v, kl, vl, sel = _attn_case(17, n=1024, d=8, B=B, L=3, K=3)
+        do = _rand(q.shape, 18)
+        kb = [0, 7, 63, 255]
+        users = sorted({int(a) for j in kb for a in np.nonzero((sel[0] == j).any(axis=1))[0]})
+        assert 0 < len(users) < q.shape[0] // B
+        gq, gk, gv = orc.attention_backward(q, k, v, kl, vl, sel, do, B, enrich, blocks=users)
+        qt, kt, vt = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        _dense_mask_formulation(qt, kt, vt, sel, B, enrich,
+                                1 / math.sqrt(q.shape[1])).backward(torch.tensor(do))
+        qrows = np.concatenate([np.arange(b * B, b * B + B) for b in users])
+        krows = np.concatenate([np.arange(j * B, j * B + B) for j in kb])
+        assert np.allclose(gq[qrows], qt.grad.numpy()[qrows], rtol=0, atol=1e-10)
+        if not enrich:
+            assert np.allclose(gk[krows], kt.grad.numpy()[krows], rtol=0, atol=1e-10)
+            assert np.allclose(gv[krows], vt.grad.numpy()[krows], rtol=0, atol=1e-10)
+        full = orc.attention_backward(q, k, v, kl, vl, sel, do, B, enrich)
+        every = orc.attention_backward(q, k, v, kl, vl, sel, do, B, enrich,
+                                       blocks=range(q.shape[0] // B))
+        for a, b in zip(full, every):
+            assert np.array_equal(a, b)
+
+
 # ----------------------------------------------------------------------------- backward
 
 

@@ -1,0 +1,42 @@
+"""The rocprofv3 summaries (host only): symbol names map to the library's profiler names, and
+the traffic record scales each kernel's counters by the calibration copy's."""
+import csv
+
+from hierarchical_top_sparse_amd import profiling
+
+
+def _write(path, rows):
+    cols = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(cols, r)))
+
+
+def test_profile_names():
+    assert profiling.profile_name("llsa::bwd_key_kernel<2>(llsa::BwdArgs)")[0] == \
+        "bwd_key_overflow_kernel"
+    assert profiling.profile_name("void llsa::select_pool_next_kernel<8>(a, b)")[0] == \
+        "select_pool_kernel"
+    assert profiling.profile_name("llsa::pool_next_kernel<16>(x)") == ("pool_next_kernel",
+                                                                       "pool.hip")
+    assert profiling.profile_name("at::native::elementwise_kernel<128, 4>(...)") is None
+
+
+def test_traffic_record_scales_by_the_copy(tmp_path):
+    T = 96 * 2 ** 20
+    _write(tmp_path / "f.csv", [(1, "llsa::reorder_kernel(x)", "FETCH_SIZE", T / 2048),
+                                (2, "llsa::attn_fwd_kernel<true, 4>(a)", "FETCH_SIZE", 1000.0),
+                                (3, "llsa::attn_fwd_kernel<true, 4>(a)", "FETCH_SIZE", 3000.0)])
+    _write(tmp_path / "w.csv", [(1, "llsa::reorder_kernel(x)", "WRITE_SIZE", T / 1024),
+                                (2, "llsa::attn_fwd_kernel<true, 4>(a)", "WRITE_SIZE", 500.0),
+                                (3, "llsa::attn_fwd_kernel<true, 4>(a)", "WRITE_SIZE", 500.0)])
+    rec = profiling.traffic_record(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), T,
+                                   "test", ["cmd"])
+    assert rec["fetch_scale"] == 2.0 and rec["write_scale"] == 1.0
+    k = rec["kernels"]["attn_fwd_kernel"]
+    assert k["dispatches"] == 2
+    assert k["hbm_read_bytes_per_launch"] == 2000 * 2 * 1024
+    assert k["hbm_write_bytes_per_launch"] == 500 * 1024
+    assert k["source"].endswith("attn_fwd.hip") and len(k["source_sha256"]) == 64
