@@ -133,6 +133,8 @@ def lib() -> ctypes.CDLL:
             "llsa_attn_bwd_masked": ([P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
                                      i32),
             "llsa_profile_enable": ([i32], i32),
+            "llsa_attn_bwd_noalloc": ([P, vp, vp, vp, vp, vp, pp, pp, pp, pp, pp, vp, vp, vp, vp],
+                                      i32),
             "llsa_profile_read": ([ctypes.c_char_p, sz], i32),
         }
         for name, (args, res) in sigs.items():
@@ -150,7 +152,7 @@ def exported_symbols() -> list:
             "llsa_index_transpose_workspace", "llsa_index_transpose", "llsa_attn_bwd",
             "llsa_dense_attn_fwd", "llsa_dense_attn_bwd", "llsa_block_mask", "llsa_expand_blocks",
             "llsa_attn_bwd_masked", "llsa_calib_copy", "llsa_calib_mfma", "llsa_profile_enable",
-            "llsa_profile_read"]
+            "llsa_profile_read", "llsa_attn_bwd_noalloc"]
 
 
 def _raise(status: int, name: str):
@@ -326,8 +328,8 @@ def llsa_index_transpose(nmat, rows, cols, k, csr, csc_off, csc_rows, ws, stream
                                       _stream(stream)), "llsa_index_transpose")
 
 
-def llsa_attn_bwd(p: Problem, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_rows, dq, dk,
-                  dv, ws, stream=None):
+def _check_bwd_args(p: Problem, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_rows, dq, dk,
+                    dv):
     for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout), ("dq", dq), ("dk", dk),
                     ("dv", dv)):
         _expect(t, _tok_shape(p), p.torch_dtype, name)
@@ -343,11 +345,29 @@ def llsa_attn_bwd(p: Problem, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_
         if l >= 2:
             _expect(k_lv[l - 1], _lv_shape(p, l), torch.float32, f"k_lv[{l - 1}]")
             _expect(v_lv[l - 1], _lv_shape(p, l), torch.float32, f"v_lv[{l - 1}]")
+
+
+def llsa_attn_bwd(p: Problem, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_rows, dq, dk,
+                  dv, ws, stream=None):
+    _check_bwd_args(p, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_rows, dq, dk, dv)
     _raise(lib().llsa_attn_bwd(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(dout),
                                _ptr(lse), _ptrs(k_lv), _ptrs(v_lv), _ptrs(sel),
                                _ptrs(csc_off), _ptrs(csc_rows), _ptr(dq), _ptr(dk), _ptr(dv),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "llsa_attn_bwd")
+
+
+LLSA_NOALLOC_SCRATCH_BYTES = 96 << 20   # the allocation-free backward's workspace limit
+
+
+def llsa_attn_bwd_noalloc(p: Problem, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_rows,
+                          dq, dk, dv, stream=None):
+    _check_bwd_args(p, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_rows, dq, dk, dv)
+    _raise(lib().llsa_attn_bwd_noalloc(ctypes.byref(p.c()), _ptr(q), _ptr(k), _ptr(v),
+                                       _ptr(dout), _ptr(lse), _ptrs(k_lv), _ptrs(v_lv),
+                                       _ptrs(sel), _ptrs(csc_off), _ptrs(csc_rows), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), _stream(stream)),
+           "llsa_attn_bwd_noalloc")
 
 
 def _mask_shape(p: Problem):

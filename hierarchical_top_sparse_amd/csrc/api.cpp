@@ -315,12 +315,16 @@ int32_t llsa_index_transpose(int32_t nmat, int32_t rows, int32_t cols, int32_t k
                     "llsa_index_transpose");
 }
 
-int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const void* v,
-                      const void* dout, const float* lse,
-                      const float* const* k_lv, const float* const* v_lv,
-                      const int32_t* const* sel, const int32_t* const* csc_off,
-                      const int32_t* const* csc_rows, void* dq, void* dk, void* dv, void* ws,
-                      size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by llsa_attn_bwd and llsa_attn_bwd_noalloc (everything but the workspace).
+int32_t check_bwd(const llsa_problem* p, const void* q, const void* k, const void* v,
+                  const void* dout, const float* lse, const float* const* k_lv,
+                  const float* const* v_lv, const int32_t* const* sel,
+                  const int32_t* const* csc_off, const int32_t* const* csc_rows, void* dq,
+                  void* dk, void* dv) {
   int32_t st = check_problem(p);
   if (st != LLSA_OK) return st;
   if (p->dtype != LLSA_BF16)
@@ -357,6 +361,21 @@ int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const
       CHECK_PTR(v_lv[l - 1], "pooled v");
     }
   }
+  return LLSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const void* v,
+                      const void* dout, const float* lse,
+                      const float* const* k_lv, const float* const* v_lv,
+                      const int32_t* const* sel, const int32_t* const* csc_off,
+                      const int32_t* const* csc_rows, void* dq, void* dk, void* dv, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int32_t st = check_bwd(p, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_rows, dq, dk, dv);
+  if (st != LLSA_OK) return st;
   const llsa::Shape s = make_shape(p);
   const size_t need = llsa::bwd_workspace_bytes(s);
   if (!ws || ws_bytes < need)
@@ -366,6 +385,29 @@ int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const
                                           csc_rows, nullptr, dq, dk, dv, ws,
                                           (hipStream_t)stream),
                     "llsa_attn_bwd");
+}
+
+int32_t llsa_attn_bwd_noalloc(const llsa_problem* p, const void* q, const void* k,
+                              const void* v, const void* dout, const float* lse,
+                              const float* const* k_lv, const float* const* v_lv,
+                              const int32_t* const* sel, const int32_t* const* csc_off,
+                              const int32_t* const* csc_rows, void* dq, void* dk, void* dv,
+                              void* stream) {
+  int32_t st = check_bwd(p, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_rows, dq, dk, dv);
+  if (st != LLSA_OK) return st;
+  const llsa::Shape s = make_shape(p);
+  const size_t need = llsa::bwd_workspace_bytes(s);
+  if (need > (size_t)LLSA_NOALLOC_SCRATCH_BYTES)
+    return fail(LLSA_ERR_WORKSPACE, "this problem needs %zu bytes of backward workspace; the "
+                "allocation-free entry holds at most %zu: use llsa_attn_bwd with a workspace",
+                need, (size_t)LLSA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = hip_status(llsa::noalloc_scratch(&ws), "llsa_attn_bwd_noalloc: scratch address");
+  if (st != LLSA_OK) return st;
+  return hip_status(llsa::launch_attn_bwd(s, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off,
+                                          csc_rows, nullptr, dq, dk, dv, ws,
+                                          (hipStream_t)stream),
+                    "llsa_attn_bwd_noalloc");
 }
 
 }  // extern "C"

@@ -19,6 +19,9 @@
 // read row-major operands; products that contract over keys or queries read their row-major
 // operand from LDS with ds_read_b64_tr_b16.  Chunks of 32 keys (or queries) use the same row
 // interleave as the forward, so score tiles come out in the B-operand layout of the next MFMA.
+#include <mutex>
+
+#include "../../include/llsa.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -1180,6 +1183,37 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
                 stream, a);
   }
   return hipGetLastError();
+}
+
+// ====================================================================== allocation-free entry
+// The backward's workspace as a file-scope device array, for callers that cannot allocate.
+// Each device the library runs on holds its own copy (for the life of the process); in host
+// code `scratch` only names the symbol, so its device address is looked up once per device
+// with hipGetSymbolAddress and kept.  Every call on a device uses that device's copy, and
+// nothing in it has to start at zero (each launch writes what a later one reads), so calls
+// that overlap on one device race and must be serialised by the caller.
+static __device__ __align__(256) char scratch[LLSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace llsa

@@ -60,6 +60,9 @@ hipError_t launch_index_transpose(int nmat, int rows, int cols, int k, const int
                                   hipStream_t stream);
 
 size_t bwd_workspace_bytes(const Shape& s);
+// Device address of this device's allocation-free scratch array (LLSA_NOALLOC_SCRATCH_BYTES),
+// looked up on the first call on each device.
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const void* v,
                            const void* dout, const float* lse,
                            const float* const* k_lv, const float* const* v_lv,

@@ -214,6 +214,28 @@ int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const
                       size_t ws_bytes, void* stream);
 
 /*
+ * llsa_attn_bwd_noalloc — llsa_attn_bwd without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments (minus ws, ws_bytes), kernels and results as
+ * llsa_attn_bwd: bit-identical outputs.  The workspace is a file-scope device array of
+ * LLSA_NOALLOC_SCRATCH_BYTES that every device the library runs on holds until the process
+ * ends; its address is looked up on the first call on each device (the current device, which
+ * must be the stream's).  Allocates nothing, ever.  Problems whose llsa_workspace_bytes (bwd)
+ * exceeds LLSA_NOALLOC_SCRATCH_BYTES fail with LLSA_ERR_WORKSPACE before anything is enqueued
+ * (at 256x256 pixels: batch * heads <= 14 with the default L = 3, K = 8).  All calls on one
+ * device share that device's array and nothing in it persists between calls that the next
+ * call reads: calls that overlap on one device (concurrent streams or threads) race, and the
+ * caller must serialise them.  Errors otherwise as for llsa_attn_bwd.
+ */
+#define LLSA_NOALLOC_SCRATCH_BYTES (96u << 20)
+int32_t llsa_attn_bwd_noalloc(const llsa_problem* p, const void* q, const void* k,
+                              const void* v, const void* dout, const float* lse,
+                              const float* const* k_lv, const float* const* v_lv,
+                              const int32_t* const* sel, const int32_t* const* csc_off,
+                              const int32_t* const* csc_rows, void* dq, void* dk, void* dv,
+                              void* stream);
+
+/*
  * llsa_dense_attn_fwd / llsa_dense_attn_bwd — dense softmax attention over all N keys, the
  * full-attention baseline the sparse method is measured against (paper summary sec. 5.4 and
  * Figure 3 compare against dense FlashAttention at the same sequence length).  Not part of
