@@ -326,9 +326,10 @@ def kernel_fractions(p, per_kernel_ms):
     return out
 
 
-def make_step(cfg_name, layout="raster", backward=None, levels=None, topk=8, x=None):
+def make_step(cfg_name, layout="raster", backward=None, levels=None, topk=8, x=None,
+              head_dim=64):
     """A runtime Step over the workload's inputs (x: the generator's CPU tensors, made here if
-    not given); levels/topk override its L and K."""
+    not given); levels/topk override its L and K, head_dim its channels per head."""
     import torch
 
     from hierarchical_top_sparse_amd import gen, ops
@@ -338,7 +339,7 @@ def make_step(cfg_name, layout="raster", backward=None, levels=None, topk=8, x=N
     L = levels or cfg["levels"]
     bwd = cfg["backward"] if backward is None else backward
     if x is None:
-        x = gen.make_inputs(cfg["batch"], cfg["heads"], h, w, 64, cfg["dtype"],
+        x = gen.make_inputs(cfg["batch"], cfg["heads"], h, w, head_dim, cfg["dtype"],
                             cfg["seed_base"], with_grad=bwd)
     dev = torch.device("cuda:0")
     q, k, v = (x[t].to(dev) for t in ("q", "k", "v"))
@@ -673,6 +674,23 @@ def main():
         del s_o
         extra[f"{other}_layout"] = {"ms_per_step": round(ms_o, 4),
                                     "tokens_per_s": round(tokens / (ms_o / 1e3), 1)}
+    if not args.no_configs:
+        # the same training step with 128-channel heads (the enrichment-ablation variants of
+        # the method crossed with the head width): step time and its units' fractions
+        s128, _, _ = make_step(args.config, head_dim=128)
+        ms128, _, _, pk128, pks128 = measure(s128, max(10, args.steps // 2), 5)
+        u128, _ = unit_model(s128.p)
+        rows128 = {}
+        for un, u in u128.items():
+            ms_u = sum(pks128.get(kn, 0.0) for kn in u["kernels"])
+            if ms_u > 0:
+                rows128[un] = {"ms_per_step": round(ms_u, 4), "alg_bytes": u["bytes"],
+                               "hbm_frac": round(u["bytes"] / (ms_u / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                                 4)}
+        extra["head_dim_128"] = {"ms_per_step": round(ms128, 4),
+                                 "tokens_per_s": round(tokens / (ms128 / 1e3), 1),
+                                 "units": rows128}
+        del s128
     if not args.no_dense:
         if "configs" in extra:
             fwd256 = extra["configs"]["px256"]["ms"]

@@ -51,8 +51,8 @@ int32_t check_problem(const llsa_problem* p) {
   if (!is_pow2(p->height) || !is_pow2(p->width) || p->height < 4 || p->width < 4)
     return fail(LLSA_ERR_SHAPE, "height (%d) and width (%d) must be powers of two >= 4",
                 p->height, p->width);
-  if (p->head_dim != 64)
-    return fail(LLSA_ERR_UNSUPPORTED, "head_dim %d: only 64 is implemented", p->head_dim);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(LLSA_ERR_UNSUPPORTED, "head_dim %d: 64 and 128 are implemented", p->head_dim);
   if (p->block != 16 && p->block != 64)
     return fail(p->block > 1 && is_pow2(p->block) && (log2i(p->block) % 2 == 0)
                     ? LLSA_ERR_UNSUPPORTED
@@ -103,6 +103,7 @@ llsa::Shape make_shape(const llsa_problem* p) {
   llsa::Shape s{};
   s.bh = p->batch * p->heads;
   s.n = p->height * p->width;
+  s.d = p->head_dim;
   s.hbits = log2i(p->height);
   s.wbits = log2i(p->width);
   s.levels = p->levels;
@@ -264,6 +265,8 @@ int32_t llsa_attn_fwd(const llsa_problem* p, const void* q, const void* k, const
                       const int32_t* const* sel, void* o, float* lse, void* stream) {
   int32_t st = check_problem(p);
   if (st != LLSA_OK) return st;
+  if (p->head_dim == 128 && p->dtype != LLSA_BF16)
+    return fail(LLSA_ERR_UNSUPPORTED, "the 128-channel attention is implemented for bf16");
   CHECK_PTR(q, "q");
   CHECK_PTR(k, "k");
   CHECK_PTR(v, "v");
@@ -425,6 +428,8 @@ int32_t check_masked(const llsa_problem* p) {
                 "be 1 or enrich 0");
   if (p->block != 16)
     return fail(LLSA_ERR_UNSUPPORTED, "the mask-based backward is implemented for block 16");
+  if (p->head_dim != 64)
+    return fail(LLSA_ERR_UNSUPPORTED, "the mask-based backward is implemented for head_dim 64");
   const long n1 = (long)p->height * p->width / 16;
   if ((long)p->batch * p->heads * n1 * n1 > (1L << 34))
     return fail(LLSA_ERR_SHAPE, "block mask of %ld bytes exceeds 2^34",

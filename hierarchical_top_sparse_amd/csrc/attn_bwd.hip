@@ -19,6 +19,9 @@
 // read row-major operands; products that contract over keys or queries read their row-major
 // operand from LDS with ds_read_b64_tr_b16.  Chunks of 32 keys (or queries) use the same row
 // interleave as the forward, so score tiles come out in the B-operand layout of the next MFMA.
+// D (head_dim) is 64 or 128: rows, contraction chains and accumulators scale with it; with 128
+// channels a query-major wave owns one query block instead of two (its accumulators double),
+// so a level-2 group has 4 partial units instead of 2.
 #include <mutex>
 
 #include "../../include/llsa.h"
@@ -28,7 +31,8 @@
 namespace llsa {
 
 constexpr int kMaxLv = 6;
-constexpr int kStride = kDim + 8;   // LDS row stride in bf16 elements (144 bytes)
+// LDS row stride in bf16 elements: D + 8 (144 bytes for 64 channels)
+__host__ __device__ constexpr int bstride(int D) { return D + 8; }
 constexpr int kMaxCoarse = 32;      // coarse slots handled by the fused partial sums
 
 struct BwdArgs {
@@ -46,9 +50,9 @@ struct BwdArgs {
   bf16* dk;
   bf16* dv;
   float* dd;                   // D, [bh, N]
-  float* part_k;               // [bh, n2, kUnits, n_coarse, 64]
+  float* part_k;               // [bh, n2, units, n_coarse, D]
   float* part_v;
-  float* dk_lv[kMaxLv];        // level l >= 2: [bh, n_l, 64]
+  float* dk_lv[kMaxLv];        // level l >= 2: [bh, n_l, D]
   float* dv_lv[kMaxLv];
   const uint8_t* mask;         // block mask [bh, n_1, n_1] (mask-scanning key pass only)
   // key blocks with more than kKeyChunk CSC_1 entries: their entries beyond the first chunk go
@@ -57,7 +61,7 @@ struct BwdArgs {
   int32_t* ov_count;           // [bh, n_1] overflow chunks of key block j
   int32_t* ov_table;           // [bh, ov_cap] chunk t: (key block << 16) | chunk index m >= 1
   int32_t* ov_total;           // [bh] overflow chunks of the head
-  float* ov_part;              // [bh, ov_cap, 64 lanes, 32]: raw dK, dV sums of a chunk
+  float* ov_part;              // [bh, ov_cap, 64 lanes, D / 2]: raw dK, dV sums of a chunk
   int ov_cap;                  // overflow chunks per head the buffers hold
   int ov_waves;                // overflow waves per head: wave g runs chunks g, g + ov_waves, ..
   int plan_blocks;             // leading workgroups of the query-major launch that run the
@@ -75,6 +79,7 @@ struct BwdArgs {
   int exclude;         // 1: a coarse key over a key selected one level finer is dropped
   float scale;
   float c2;   // scale * log2(e)
+  int units_log2;      // log2 of the partial units (query-major workgroups) per level-2 group
 };
 
 __device__ __forceinline__ int chunk_key(int r, int t) { return 8 * (r >> 2) + (r & 3) + 4 * t; }
@@ -98,17 +103,19 @@ __device__ __forceinline__ bf16x8 zero8() {
 }
 
 // A operand (rows of a row-major LDS matrix): lane (m, g) gets row `row`, cols 32s + 8g..+7
+template <int D>
 __device__ __forceinline__ bf16x8 lds_row8(const bf16* st, int row, int s, int g) {
-  return *(const bf16x8*)(st + row * kStride + 32 * s + 8 * g);
+  return *(const bf16x8*)(st + row * bstride(D) + 32 * s + 8 * g);
 }
 // Transposed operand: rows k0 + 8g .. +7 (k axis) at column block 16*t4 (lane gets its column)
+template <int D>
 __device__ __forceinline__ bf16x8 lds_tr8(const bf16* st, int t4, int lane) {
   const int g = lane >> 4;
   const int r = (lane & 15) >> 2;
   const int c = lane & 3;
-  const bf16* base = st + (8 * g + r) * kStride + 16 * t4 + 4 * c;
+  const bf16* base = st + (8 * g + r) * bstride(D) + 16 * t4 + 4 * c;
   const bf16x4 lo = lds_read_tr16(base);
-  const bf16x4 hi = lds_read_tr16(base + 4 * kStride);
+  const bf16x4 hi = lds_read_tr16(base + 4 * bstride(D));
   bf16x8 out;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -133,22 +140,26 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* st, int t4, int lane) {
 //    block's queries (Q and dO rows staged in the wave's tiles);
 //  * the 4 waves' partials are summed in a fixed order into the half-group's partial rows.
 constexpr int kQWaves = 4;
-constexpr int kQBlocks = 2;     // query blocks per wave
-constexpr int kUnits = 2;       // partial units (workgroups) per level-2 group
-constexpr int kQPickList = 64;  // pick-list capacity per wave
-constexpr int kQPickSlots = kQPickList / kQBlocks;   // pick slots per query block (K <= 32)
+// query blocks per wave: 2, or 1 with 128 channels
+__host__ __device__ constexpr int q_blocks(int D) { return D == 64 ? 2 : 1; }
+// partial units (workgroups) per level-2 group
+__host__ __device__ constexpr int q_units(int D) { return kBlock / (kQWaves * q_blocks(D)); }
+constexpr int kQPickList = 64;  // pick-list capacity per wave (pick slots per block: 64 / QB)
 constexpr int kPickSentinel = 0x7f000000;
 
-__host__ __device__ constexpr int bwdq_wave_lds_bytes() {
-  return 2 * 16 * kStride * 2 + 4 * kQPickList * 4 + 48 * 4;
+__host__ __device__ constexpr int bwdq_wave_lds_bytes(int D) {
+  return 2 * 16 * bstride(D) * 2 + 4 * kQPickList * 4 + 48 * 4;
 }
 // ... then the coarse tiles, each slot's bias and key id, and with overlap exclusion per-block
-// biases [waves][2 blocks][ctiles * 16].
-static size_t bwd_query_lds_bytes(int n_coarse, bool exclude) {
+// biases [waves][blocks][ctiles * 16].  The end-of-kernel reduction reuses the first
+// kQWaves * 16 * D floats.
+static size_t bwd_query_lds_bytes(int D, int n_coarse, bool exclude) {
   const int ctiles = (n_coarse + 15) / 16;
-  return (size_t)kQWaves * bwdq_wave_lds_bytes() + (size_t)ctiles * 4 * 16 * kStride * 2 +
-         (sizeof(float) + sizeof(int)) * 16 * ctiles +
-         (exclude ? sizeof(float) * kQWaves * kQBlocks * 16 * ctiles : 0);
+  const size_t bytes = (size_t)kQWaves * bwdq_wave_lds_bytes(D) +
+                       (size_t)ctiles * 4 * 16 * bstride(D) * 2 +
+                       (sizeof(float) + sizeof(int)) * 16 * ctiles +
+                       (exclude ? sizeof(float) * kQWaves * q_blocks(D) * 16 * ctiles : 0);
+  return std::max(bytes, sizeof(float) * kQWaves * 16 * D);
 }
 
 __device__ __forceinline__ void split4(const float (&x)[4], bf16x4& hi, bf16x4& lo) {
@@ -157,9 +168,14 @@ __device__ __forceinline__ void split4(const float (&x)[4], bf16x4& hi, bf16x4& 
 
 __device__ void key_plan(const BwdArgs& a, int head, int* wsum);   // stage 3's plan
 
-template <int NCT>   // coarse tiles of 16 slots: 0, 1 or 2
-__global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(2)))
+template <int NCT, int D>   // NCT: coarse tiles of 16 slots (0, 1 or 2); D: head_dim
+__global__ __launch_bounds__(64 * kQWaves) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1)))
 void bwd_query_kernel(BwdArgs a) {
+  constexpr int kQBlocks = q_blocks(D);              // query blocks per wave
+  constexpr int kUnits = q_units(D);                 // partial units per level-2 group
+  constexpr int kQPickSlots = kQPickList / kQBlocks;   // pick slots per query block (K <= 32)
+  constexpr int kStride = bstride(D);
+  constexpr int PPR = D / 8;                         // 16-byte pieces per row
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -184,7 +200,7 @@ void bwd_query_kernel(BwdArgs a) {
   const long tok_base = (long)head * a.n;
   const int n_coarse = NCT > 0 ? a.coarse_levels * K : 0;
 
-  char* wb = smem + w * bwdq_wave_lds_bytes();
+  char* wb = smem + w * bwdq_wave_lds_bytes(D);
   bf16* kt = (bf16*)wb;                 // staged K rows (Q rows at a block's end)
   bf16* vt = kt + 16 * kStride;         // staged V rows (dO rows at a block's end)
   int* keys = (int*)(vt + 16 * kStride);
@@ -193,12 +209,12 @@ void bwd_query_kernel(BwdArgs a) {
   int* umask = uoff + kQPickList;
   float* lsh = (float*)(umask + kQPickList);   // [2][16] log2-domain LSE of the blocks' queries
   float* dsh = lsh + 32;                       // [16] D of the current block's queries
-  bf16* ct = (bf16*)(smem + kQWaves * bwdq_wave_lds_bytes());   // [NCT][K hi, K lo, V hi, V lo]
+  bf16* ct = (bf16*)(smem + kQWaves * bwdq_wave_lds_bytes(D));   // [NCT][K hi, K lo, V hi, V lo]
   float* cbias = (float*)(ct + NCT * 4 * 16 * kStride);
   int* cid = (int*)(cbias + 16 * NCT);          // key id of each coarse slot (-1: none)
   float* wxb = (float*)(cid + 16 * NCT) + w * kQBlocks * 16 * NCT;   // exclusion: [bb][slot]
 
-  const uint32_t head_bytes = (uint32_t)a.n * kDim * 2;
+  const uint32_t head_bytes = (uint32_t)a.n * D * 2;
   const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
   const rsrc_t rk = make_rsrc_uniform((const char*)a.k + (size_t)head * head_bytes, head_bytes);
   const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
@@ -213,15 +229,16 @@ void bwd_query_kernel(BwdArgs a) {
         a.sel[0][((long)head * n1 + pb_first + lane / kQPickSlots) * KF + lane % kQPickSlots];
     if (j >= 0 && j < n1) key = (j << 8) | lane;
   }
-  bf16x8 qh[kQBlocks][2], dh[kQBlocks][2];   // B operands: lane (n, g) row n, ch 32s + 8g..
+  bf16x8 qh[kQBlocks][D / 32], dh[kQBlocks][D / 32];   // B operands: lane (n, g) row n,
+                                                       // channels 32s + 8g ..
   float lraw[kQBlocks];
 #pragma unroll
   for (int bb = 0; bb < kQBlocks; ++bb) {
     const int pb = pb_first + bb;
     const uint32_t qrow =
-        (uint32_t)(block_corner(pb, a.grid) + tile_offset(n, a.grid)) * kDim * 2;
+        (uint32_t)(block_corner(pb, a.grid) + tile_offset(n, a.grid)) * D * 2;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    for (int s2 = 0; s2 < D / 32; ++s2) {
       qh[bb][s2] = buf_load8(rq, qrow + (32 * s2 + 8 * g) * 2);
       dh[bb][s2] = buf_load8(rdo, qrow + (32 * s2 + 8 * g) * 2);
     }
@@ -229,10 +246,10 @@ void bwd_query_kernel(BwdArgs a) {
         float, __builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)(pb * kBlock + n) * 4, 0, 0));
   }
 
-  // ---- coarse keys of the group (slot e / 8, channels 8 (e % 8) ..): bf16 hi + lo parts
+  // ---- coarse keys of the group (slot e / PPR, channels 8 (e % PPR) ..): bf16 hi + lo parts
   if (NCT > 0) {
-    for (int e = tid; e < NCT * 16 * 8; e += 64 * kQWaves) {
-      const int cslot = e >> 3, c8 = (e & 7) * 8;
+    for (int e = tid; e < NCT * 16 * PPR; e += 64 * kQWaves) {
+      const int cslot = e / PPR, c8 = (e % PPR) * 8;
       f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
       float bias = -INFINITY;
       int cslot_id = -1;
@@ -243,8 +260,8 @@ void bwd_query_kernel(BwdArgs a) {
         const int id = a.sel[l - 1][((long)head * nl + anc) * K + (cslot - (l - 2) * K)];
         if (id >= 0 && id < nl) {
           cslot_id = id;
-          const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
-          const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
+          const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * D + c8;
+          const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * D + c8;
           k0 = *(const f32x4*)kp;
           k1 = *(const f32x4*)(kp + 4);
           v0 = *(const f32x4*)vp;
@@ -279,7 +296,7 @@ void bwd_query_kernel(BwdArgs a) {
   // ---- U: ranks of the wave's pick keys, distinct ids, owner masks
   keys[lane] = key;
   umask[lane] = 0;
-  if (g < kQBlocks) lsh[16 * g + n] = (g == 0 ? lraw[0] : lraw[1]) * kLog2e;
+  if (g < kQBlocks) lsh[16 * g + n] = (g == 0 ? lraw[0] : lraw[kQBlocks - 1]) * kLog2e;
   wave_lds_sync();
   {
     int r = 0;
@@ -310,27 +327,29 @@ void bwd_query_kernel(BwdArgs a) {
         if ((o >> 8) != (sk >> 8)) break;
         m |= 1 << ((o & 63) / kQPickSlots);
       }
-      uoff[u] = block_corner(sk >> 8, a.grid) * kDim * 2;
+      uoff[u] = block_corner(sk >> 8, a.grid) * D * 2;
       umask[u] = m;
     }
   }
   wave_lds_sync();
 
-  // ---- the stream of U: row-major loads (lane l: pieces l, l + 64 of 16 rows x 8 pieces)
-  uint32_t poff[2];
+  // ---- the stream of U: row-major loads (lane l: pieces l, l + 64, .. of 16 rows x PPR
+  // pieces)
+  constexpr int kLd = 16 * PPR / 64;
+  uint32_t poff[kLd];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
+  for (int m = 0; m < kLd; ++m) {
     const int e = lane + 64 * m;
-    poff[m] = (uint32_t)tile_offset(e >> 3, a.grid) * kDim * 2 + 16 * (e & 7);
+    poff[m] = (uint32_t)tile_offset(e / PPR, a.grid) * D * 2 + 16 * (e % PPR);
   }
   struct BlockLd {
-    i32x4 k[2], v[2];
+    i32x4 k[kLd], v[kLd];
   };
   auto load_u = [&](int u) -> BlockLd {
     BlockLd f;
     const uint32_t b = u < n_u ? (uint32_t)uniform(uoff[min(u, kQPickList - 1)]) : kNoRow;
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < kLd; ++m) {
       f.k[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, b + poff[m], 0, 0);
       f.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, b + poff[m], 0, 0);
     }
@@ -361,13 +380,14 @@ void bwd_query_kernel(BwdArgs a) {
     }
   }
 
-  f32x4 acc_a[kQBlocks][4], acc_b[kQBlocks][4];
+  f32x4 acc_a[kQBlocks][D / 16], acc_b[kQBlocks][D / 16];
   float dpart[kQBlocks];
 #pragma unroll
   for (int bb = 0; bb < kQBlocks; ++bb) {
     dpart[bb] = 0.f;
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) acc_a[bb][t4] = acc_b[bb][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t4 = 0; t4 < D / 16; ++t4)
+      acc_a[bb][t4] = acc_b[bb][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // One 16-key tile of block bb: K rows kr (+ lo parts klo), V rows vr (+ vlo), per-key biases.
@@ -376,12 +396,12 @@ void bwd_query_kernel(BwdArgs a) {
     constexpr int bb = decltype(bbc)::value;
     f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = st;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      st = mfma_bf16_k32(lds_row8(kr, n, s2, g), qh[bb][s2], st);
-      dp = mfma_bf16_k32(lds_row8(vr, n, s2, g), dh[bb][s2], dp);
+    for (int s2 = 0; s2 < D / 32; ++s2) {
+      st = mfma_bf16_k32(lds_row8<D>(kr, n, s2, g), qh[bb][s2], st);
+      dp = mfma_bf16_k32(lds_row8<D>(vr, n, s2, g), dh[bb][s2], dp);
       if (klo) {
-        st = mfma_bf16_k32(lds_row8(klo, n, s2, g), qh[bb][s2], st);
-        dp = mfma_bf16_k32(lds_row8(vlo, n, s2, g), dh[bb][s2], dp);
+        st = mfma_bf16_k32(lds_row8<D>(klo, n, s2, g), qh[bb][s2], st);
+        dp = mfma_bf16_k32(lds_row8<D>(vlo, n, s2, g), dh[bb][s2], dp);
       }
     }
     float p[4], w1[4];
@@ -397,7 +417,7 @@ void bwd_query_kernel(BwdArgs a) {
     split4(w1, a_hi, a_lo);
     split4(p, b_hi, b_lo);
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
+    for (int t4 = 0; t4 < D / 16; ++t4) {
       const int off = (4 * g + r4) * kStride + 16 * t4 + 4 * c4;
       const bf16x4 ktr = lds_read_tr16(kr + off);
       acc_a[bb][t4] = mfma_bf16_k16(ktr, a_hi, acc_a[bb][t4]);
@@ -416,16 +436,17 @@ void bwd_query_kernel(BwdArgs a) {
 
   auto block_u = [&](const BlockLd& f, int u) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < kLd; ++m) {
       const int e = lane + 64 * m;
-      const int at = (e >> 3) * kStride + (e & 7) * 8;
+      const int at = (e / PPR) * kStride + (e % PPR) * 8;
       *(i32x4*)(kt + at) = f.k[m];
       *(i32x4*)(vt + at) = f.v[m];
     }
     wave_lds_sync();
     const int mask = uniform(umask[u]);
     if (mask & 1) tile(I0{}, kt, nullptr, vt, nullptr, nullptr);
-    if (mask & 2) tile(I1{}, kt, nullptr, vt, nullptr, nullptr);
+    if constexpr (kQBlocks > 1)
+      if (mask & 2) tile(I1{}, kt, nullptr, vt, nullptr, nullptr);
     wave_lds_sync();
   };
   for (int u = 0; u < n_u; u += 2) {
@@ -436,11 +457,12 @@ void bwd_query_kernel(BwdArgs a) {
     fb = load_u(u + 3);
   }
 
-  f32x4 cpk[NCT > 0 ? NCT : 1][4], cpv[NCT > 0 ? NCT : 1][4];   // C^T[d][slot]: lane (slot, g)
+  // C^T[d][slot]: lane (slot, g)
+  f32x4 cpk[NCT > 0 ? NCT : 1][D / 16], cpv[NCT > 0 ? NCT : 1][D / 16];
 #pragma unroll
   for (int c = 0; c < (NCT > 0 ? NCT : 1); ++c)
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) cpk[c][t4] = cpv[c][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t4 = 0; t4 < D / 16; ++t4) cpk[c][t4] = cpv[c][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto finish = [&](auto bbc) {
     constexpr int bb = decltype(bbc)::value;
@@ -454,9 +476,9 @@ void bwd_query_kernel(BwdArgs a) {
     const float Dn = group4_sum(dpart[bb]);
     if (g == 0) a.dd[tok_base + pb * kBlock + n] = Dn;
     const int qrow = block_corner(pb, a.grid) + tile_offset(n, a.grid);
-    bf16* dqp = a.dq + (tok_base + qrow) * kDim;
+    bf16* dqp = a.dq + (tok_base + qrow) * D;
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
+    for (int t4 = 0; t4 < D / 16; ++t4) {
       f32x4 r;
 #pragma unroll
       for (int i = 0; i < 4; ++i) r[i] = (acc_a[bb][t4][i] - Dn * acc_b[bb][t4][i]) * a.scale;
@@ -465,7 +487,7 @@ void bwd_query_kernel(BwdArgs a) {
     if (NCT > 0) {
       // Q and dO rows of the block (row n = query n) in the wave's tiles, D per query
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
+      for (int s2 = 0; s2 < D / 32; ++s2) {
         *(bf16x8*)(kt + n * kStride + 32 * s2 + 8 * g) = qh[bb][s2];
         *(bf16x8*)(vt + n * kStride + 32 * s2 + 8 * g) = dh[bb][s2];
       }
@@ -479,11 +501,11 @@ void bwd_query_kernel(BwdArgs a) {
         // S = Q K_c^T, dP = dO V_c^T: lane (n, g) holds queries 4g + i against slot n
         f32x4 sq = {0.f, 0.f, 0.f, 0.f}, dpq = sq;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          sq = mfma_bf16_k32(qh[bb][s2], lds_row8(cb0, n, s2, g), sq);
-          sq = mfma_bf16_k32(qh[bb][s2], lds_row8(cb0 + 16 * kStride, n, s2, g), sq);
-          dpq = mfma_bf16_k32(dh[bb][s2], lds_row8(cb0 + 32 * kStride, n, s2, g), dpq);
-          dpq = mfma_bf16_k32(dh[bb][s2], lds_row8(cb0 + 48 * kStride, n, s2, g), dpq);
+        for (int s2 = 0; s2 < D / 32; ++s2) {
+          sq = mfma_bf16_k32(qh[bb][s2], lds_row8<D>(cb0, n, s2, g), sq);
+          sq = mfma_bf16_k32(qh[bb][s2], lds_row8<D>(cb0 + 16 * kStride, n, s2, g), sq);
+          dpq = mfma_bf16_k32(dh[bb][s2], lds_row8<D>(cb0 + 32 * kStride, n, s2, g), dpq);
+          dpq = mfma_bf16_k32(dh[bb][s2], lds_row8<D>(cb0 + 48 * kStride, n, s2, g), dpq);
         }
         const float bias = (a.exclude ? wxb + bb * 16 * NCT : cbias)[16 * c + n];
         float pq[4], sv[4];
@@ -496,7 +518,7 @@ void bwd_query_kernel(BwdArgs a) {
         split4(pq, p_hi, p_lo);
         split4(sv, s_hi, s_lo);
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4) {
+        for (int t4 = 0; t4 < D / 16; ++t4) {
           const int off = (4 * g + r4) * kStride + 16 * t4 + 4 * c4;
           const bf16x4 dot = lds_read_tr16(vt + off);   // dO^T
           const bf16x4 qtt = lds_read_tr16(kt + off);   // Q^T
@@ -510,7 +532,7 @@ void bwd_query_kernel(BwdArgs a) {
     }
   };
   finish(I0{});
-  finish(I1{});
+  if constexpr (kQBlocks > 1) finish(I1{});
 
   if (NCT > 0) {
     // ---- the 4 waves' partials summed in wave order (0 + 1 + 2 + 3) into the unit's rows,
@@ -518,27 +540,31 @@ void bwd_query_kernel(BwdArgs a) {
     // its part in its own LDS region, then every thread adds 4 elements of the 4 regions and
     // stores them, so no wave waits for another's turn.  All earlier LDS use is over after
     // the first barrier.
-    float* red = (float*)smem;   // [kQWaves][16 * kDim]
-    constexpr int kChunk = 16 * kDim;
-    const long out_base = ((long)head * kUnits * n2 + rem) * n_coarse * kDim;
+    float* red = (float*)smem;   // [kQWaves][16 * D]
+    constexpr int kChunk = 16 * D;
+    const long out_base = ((long)head * kUnits * n2 + rem) * n_coarse * D;
 #pragma unroll
     for (int chunk = 0; chunk < 2 * NCT; ++chunk) {
       const int c = chunk >> 1;
       const bool is_v = chunk & 1;
       __syncthreads();
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
-        *(f32x4*)(red + w * kChunk + n * kDim + 16 * t4 + 4 * g) = is_v ? cpv[c][t4] : cpk[c][t4];
+      for (int t4 = 0; t4 < D / 16; ++t4)
+        *(f32x4*)(red + w * kChunk + n * D + 16 * t4 + 4 * g) = is_v ? cpv[c][t4] : cpk[c][t4];
       __syncthreads();
-      const int e = 4 * tid;   // elements e .. e + 3 of the chunk: slot 16 c + e / 64
-      f32x4 sum = *(const f32x4*)(red + e);
 #pragma unroll
-      for (int r = 1; r < kQWaves; ++r) sum += *(const f32x4*)(red + r * kChunk + e);
-      if (16 * c + e / kDim < n_coarse) {
-        if (is_v)
-          *(f32x4*)(a.part_v + out_base + (long)c * kChunk + e) = sum;
-        else
-          *(f32x4*)(a.part_k + out_base + (long)c * kChunk + e) = sum * a.scale;
+      for (int it = 0; it < kChunk / (4 * 64 * kQWaves); ++it) {
+        // elements e .. e + 3 of the chunk: slot 16 c + e / D
+        const int e = 4 * tid + 4 * 64 * kQWaves * it;
+        f32x4 sum = *(const f32x4*)(red + e);
+#pragma unroll
+        for (int r = 1; r < kQWaves; ++r) sum += *(const f32x4*)(red + r * kChunk + e);
+        if (16 * c + e / D < n_coarse) {
+          if (is_v)
+            *(f32x4*)(a.part_v + out_base + (long)c * kChunk + e) = sum;
+          else
+            *(f32x4*)(a.part_k + out_base + (long)c * kChunk + e) = sum * a.scale;
+        }
       }
     }
   }
@@ -546,14 +572,15 @@ void bwd_query_kernel(BwdArgs a) {
 
 // ====================================================================== stage 2: coarse keys
 // dK_l[j] = sum over the ancestors a in CSC_l[j] of the partial rows of a's slot holding j, over
-// every partial unit under a (kUnits per level-2 group, 16^(l-2) groups per level-l query).
+// every partial unit under a (2^units_log2 per level-2 group, 16^(l-2) groups per level-l query).
 // One launch for all levels l >= 2, 16-wave workgroups:
-//  * level 2: one wave per key (16 keys per workgroup); a key sums about K * kUnits rows;
+//  * level 2: one wave per key (16 keys per workgroup); a key sums about K * units rows;
 //  * level >= 3: one workgroup per key; its rows (entry, unit) are dealt round-robin to the 16
 //    waves and the waves' sums are added in a fixed order.
 // Lanes first resolve up to 64 CSC entries into partial-row offsets (lane = entry); every lane
 // then sums one channel of the rows, kCgBatch rows per round with all their loads in flight
-// (buffer loads: rows of missing entries read offset kNoRow, i.e. zeros).  Deterministic.
+// (buffer loads: rows of missing entries read offset kNoRow, i.e. zeros); with 128 channels
+// a lane sums channels lane and lane + 64.  Deterministic.
 constexpr int kCgWaves = 16;
 constexpr int kCgBatch = 16;
 
@@ -561,19 +588,23 @@ struct CoarseGradArgs {
   int first_block[kMaxLv + 1];   // level l's workgroups start at first_block[l - 1]
 };
 
-// Sums over this wave's share (rows i = part, part + nparts, ...) of key j's partial rows.
+// Sums over this wave's share (rows i = part, part + nparts, ...) of key j's partial rows:
+// sk[h], sv[h] for channel lane + 64 h.
+template <int D>
 __device__ __forceinline__ void coarse_key_sum(const BwdArgs& a, int l, int head, int j,
-                                               int part, int nparts, int lane, float& sk,
-                                               float& sv) {
+                                               int part, int nparts, int lane,
+                                               float (&sk)[D / 64], float (&sv)[D / 64]) {
+  constexpr int H = D / 64;
+  constexpr int kBatch = kCgBatch / H;   // rows in flight per round (registers: 4 H kBatch)
   const int K = a.topk;
   const int nl = a.n >> (a.bshift * l);
   const int n2 = a.n >> (2 * kBlockShift);   // 256-token groups (the partials' layout)
   const int n_coarse = a.coarse_levels * K;
-  // partial units (of 256 / kUnits tokens) under one level-l ancestor
-  const int span = 1 << (a.bshift * l - 2 * kBlockShift + 1);
-  const uint32_t row_bytes = (uint32_t)n_coarse * kDim * 4;   // one unit's partial rows
-  const uint32_t head_bytes = (uint32_t)n2 * kUnits * row_bytes;
-  const long head_floats = (long)n2 * kUnits * n_coarse * kDim;
+  // partial units (of 256 / units tokens) under one level-l ancestor
+  const int span = 1 << (a.bshift * l - 2 * kBlockShift + a.units_log2);
+  const uint32_t row_bytes = (uint32_t)n_coarse * D * 4;   // one unit's partial rows
+  const uint32_t head_bytes = ((uint32_t)n2 << a.units_log2) * row_bytes;
+  const long head_floats = ((long)n2 << a.units_log2) * n_coarse * D;
   const rsrc_t rk = make_rsrc_uniform(a.part_k + head * head_floats, head_bytes);
   const rsrc_t rv = make_rsrc_uniform(a.part_v + head * head_floats, head_bytes);
   const int32_t* off = a.csc_off[l - 1] + (long)head * (nl + 1);
@@ -581,9 +612,11 @@ __device__ __forceinline__ void coarse_key_sum(const BwdArgs& a, int l, int head
   const int32_t* sel = a.sel[l - 1] + (long)head * nl * K;
   const int e0 = uniform(off[j]);
   const int e1 = uniform(off[j + 1]);
-  float ak[kCgBatch], av[kCgBatch];
+  float ak[H][kBatch], av[H][kBatch];
 #pragma unroll
-  for (int u = 0; u < kCgBatch; ++u) ak[u] = av[u] = 0.f;
+  for (int h = 0; h < H; ++h)
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) ak[h][u] = av[h][u] = 0.f;
   for (int base = e0; base < e1; base += 64) {
     const int cnt = min(64, e1 - base);
     // lane e: byte offset of entry e's row in unit 0 under its ancestor (kNoRow if none)
@@ -595,44 +628,57 @@ __device__ __forceinline__ void coarse_key_sum(const BwdArgs& a, int l, int head
         for (int s = 0; s < K; ++s)
           if (sel[(long)anc * K + s] == j) slot = s;
         if (slot >= 0)
-          src = (uint32_t)anc * span * row_bytes + (uint32_t)((l - 2) * K + slot) * kDim * 4;
+          src = (uint32_t)anc * span * row_bytes + (uint32_t)((l - 2) * K + slot) * D * 4;
       }
     }
     const int total = cnt * span;
-    for (int i0 = part; i0 < total; i0 += nparts * kCgBatch) {
-      float xk[kCgBatch], xv[kCgBatch];
+    for (int i0 = part; i0 < total; i0 += nparts * kBatch) {
+      float xk[H][kBatch], xv[H][kBatch];
 #pragma unroll
-      for (int u = 0; u < kCgBatch; ++u) {
+      for (int u = 0; u < kBatch; ++u) {
         const int i = i0 + u * nparts;
         const int e = i < total ? i / span : 0;
         const uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)src, e);
         const uint32_t o = (i < total && r != kNoRow)
                                ? r + (uint32_t)(i - e * span) * row_bytes + 4 * lane
                                : kNoRow;
-        xk[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rk, o, 0, 0));
-        xv[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, o, 0, 0));
+#pragma unroll
+        for (int h = 0; h < H; ++h) {
+          const uint32_t oh = o == kNoRow ? kNoRow : o + 256 * h;
+          xk[h][u] =
+              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rk, oh, 0, 0));
+          xv[h][u] =
+              __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rv, oh, 0, 0));
+        }
       }
 #pragma unroll
-      for (int u = 0; u < kCgBatch; ++u) {
-        ak[u] += xk[u];
-        av[u] += xv[u];
-      }
+      for (int h = 0; h < H; ++h)
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          ak[h][u] += xk[h][u];
+          av[h][u] += xv[h][u];
+        }
     }
   }
 #pragma unroll
-  for (int w = kCgBatch / 2; w >= 1; w >>= 1)
+  for (int h = 0; h < H; ++h) {
 #pragma unroll
-    for (int u = 0; u < w; ++u) {
-      ak[u] += ak[u + w];
-      av[u] += av[u + w];
-    }
-  sk = ak[0];
-  sv = av[0];
+    for (int w = kBatch / 2; w >= 1; w >>= 1)
+#pragma unroll
+      for (int u = 0; u < w; ++u) {
+        ak[h][u] += ak[h][u + w];
+        av[h][u] += av[h][u + w];
+      }
+    sk[h] = ak[h][0];
+    sv[h] = av[h][0];
+  }
 }
 
+template <int D>
 __global__ __launch_bounds__(64 * kCgWaves) void coarse_grad_kernel(BwdArgs a,
                                                                     CoarseGradArgs cg) {
-  __shared__ float red[2][kCgWaves][kDim];
+  constexpr int H = D / 64;
+  __shared__ float red[2][kCgWaves][D];
   const int lane = threadIdx.x & 63;
   const int w = uniform(threadIdx.x >> 6);
   const int bid = blockIdx.x;
@@ -642,10 +688,13 @@ __global__ __launch_bounds__(64 * kCgWaves) void coarse_grad_kernel(BwdArgs a,
     if (f >= a.bh * n2) return;
     const int head = uniform(f / n2);
     const int j = uniform(f - head * n2);
-    float sk, sv;
-    coarse_key_sum(a, 2, head, j, 0, 1, lane, sk, sv);
-    a.dk_lv[1][((long)head * n2 + j) * kDim + lane] = sk;
-    a.dv_lv[1][((long)head * n2 + j) * kDim + lane] = sv;
+    float sk[H], sv[H];
+    coarse_key_sum<D>(a, 2, head, j, 0, 1, lane, sk, sv);
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      a.dk_lv[1][((long)head * n2 + j) * D + lane + 64 * h] = sk[h];
+      a.dv_lv[1][((long)head * n2 + j) * D + lane + 64 * h] = sv[h];
+    }
     return;
   }
   int l = 3;
@@ -654,20 +703,26 @@ __global__ __launch_bounds__(64 * kCgWaves) void coarse_grad_kernel(BwdArgs a,
   const int idx = bid - cg.first_block[l - 1];
   const int head = uniform(idx / nl);
   const int j = uniform(idx - head * nl);
-  float sk, sv;
-  coarse_key_sum(a, l, head, j, w, kCgWaves, lane, sk, sv);
-  red[0][w][lane] = sk;
-  red[1][w][lane] = sv;
+  float sk[H], sv[H];
+  coarse_key_sum<D>(a, l, head, j, w, kCgWaves, lane, sk, sv);
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    red[0][w][lane + 64 * h] = sk[h];
+    red[1][w][lane + 64 * h] = sv[h];
+  }
   __syncthreads();
   if (w == 0) {
-    float tk = 0.f, tv = 0.f;
 #pragma unroll
-    for (int x = 0; x < kCgWaves; ++x) {
-      tk += red[0][x][lane];
-      tv += red[1][x][lane];
+    for (int h = 0; h < H; ++h) {
+      float tk = 0.f, tv = 0.f;
+#pragma unroll
+      for (int x = 0; x < kCgWaves; ++x) {
+        tk += red[0][x][lane + 64 * h];
+        tv += red[1][x][lane + 64 * h];
+      }
+      a.dk_lv[l - 1][((long)head * nl + j) * D + lane + 64 * h] = tk;
+      a.dv_lv[l - 1][((long)head * nl + j) * D + lane + 64 * h] = tv;
     }
-    a.dk_lv[l - 1][((long)head * nl + j) * kDim + lane] = tk;
-    a.dv_lv[l - 1][((long)head * nl + j) * kDim + lane] = tv;
   }
 }
 
@@ -734,31 +789,41 @@ __device__ void key_plan(const BwdArgs& a, int head, int* wsum) {
 // One key block's share of the key-major pass: chunk `chunk` of CSC_1[j] (kKeyCsc: chunk 0
 // plus the overflow partials, then the store; kKeyOverflow: partial sums into slot ov_t), or
 // the whole mask column j (kKeyMask).
-template <int MODE>
+template <int MODE, int D>
 __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int chunk, int ov_t,
                                           bf16* stQ, bf16* stO, float* pdown, float* stL,
                                           int* pend) {
   constexpr bool MASK = MODE == kKeyMask;
+  constexpr int H = D / 64;               // channels per lane in the push-down
+  constexpr int kStride = bstride(D);
+  constexpr int PPR = D / 8;              // 16-byte pieces per row
+  constexpr int RPI = 64 / PPR;           // rows per load instruction
+  constexpr int NINS = 32 / RPI;          // load instructions for a pair's 32 rows
   const int lane = threadIdx.x;
   const int n = lane & 15;
   const int g = lane >> 4;
   const int n1 = a.n >> kBlockShift;
   const long tok_base = (long)head * a.n;
 
-  // pooled-key gradients pushed down to this block (lane = channel), loaded first so that
-  // they arrive during the CSC lookups instead of after the pair loop
-  float pk_sum = 0.f, pv_sum = 0.f;
+  // pooled-key gradients pushed down to this block (lane = channel, + 64 h), loaded first so
+  // that they arrive during the CSC lookups instead of after the pair loop
+  float pk_sum[H], pv_sum[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) pk_sum[h] = pv_sum[h] = 0.f;
   if (MODE != kKeyOverflow && a.enrich) {
     for (int l = 2; l <= 1 + a.coarse_levels; ++l) {
       const int nl = a.n >> (a.bshift * l);
       const int anc = (j << kBlockShift) >> (a.bshift * l);
       const float f = 1.0f / (float)(1 << (a.bshift * l));
-      pk_sum += a.dk_lv[l - 1][((long)head * nl + anc) * kDim + lane] * f;
-      pv_sum += a.dv_lv[l - 1][((long)head * nl + anc) * kDim + lane] * f;
+#pragma unroll
+      for (int h = 0; h < H; ++h) {
+        pk_sum[h] += a.dk_lv[l - 1][((long)head * nl + anc) * D + lane + 64 * h] * f;
+        pv_sum[h] += a.dv_lv[l - 1][((long)head * nl + anc) * D + lane + 64 * h] * f;
+      }
     }
   }
 
-  const uint32_t head_bytes = (uint32_t)a.n * kDim * 2;
+  const uint32_t head_bytes = (uint32_t)a.n * D * 2;
   const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
   const rsrc_t rk = make_rsrc_uniform((const char*)a.k + (size_t)head * head_bytes, head_bytes);
   const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
@@ -770,26 +835,26 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
   // keys of this block as B operands: lane (n, g) holds row n, channels 32s + 8g .. +7
   const int krow = block_corner(j, a.grid) + tile_offset(n, a.grid);
   // (the key-major pass over CSC_1 loads them once it knows the block has picks: below)
-  bf16x8 kh[2], vh[2];
+  bf16x8 kh[D / 32], vh[D / 32];
   if constexpr (MODE != kKeyCsc) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      kh[s] = buf_load8(rk, (uint32_t)(krow * kDim + 32 * s + 8 * g) * 2);
-      vh[s] = buf_load8(rv, (uint32_t)(krow * kDim + 32 * s + 8 * g) * 2);
+    for (int s = 0; s < D / 32; ++s) {
+      kh[s] = buf_load8(rk, (uint32_t)(krow * D + 32 * s + 8 * g) * 2);
+      vh[s] = buf_load8(rv, (uint32_t)(krow * D + 32 * s + 8 * g) * 2);
     }
   }
 
   // lane-constant offsets: staged rows (bytes) and this lane's 4 queries per tile (tokens)
-  const int srow0 = lane >> 3;
-  const int piece = lane & 7;
-  uint32_t st_off[4];
+  const int srow0 = lane / PPR;
+  const int piece = lane % PPR;
+  uint32_t st_off[NINS];
 #pragma unroll
-  for (int ins = 0; ins < 4; ++ins)
-    st_off[ins] = (uint32_t)(tile_offset((ins * 8 + srow0) & 15, a.grid) * kDim * 2 + 16 * piece);
+  for (int ins = 0; ins < NINS; ++ins)
+    st_off[ins] = (uint32_t)(tile_offset((ins * RPI + srow0) & 15, a.grid) * D * 2 + 16 * piece);
   const bool lane_second = g >= 2;   // this lane's queries come from the second block
 
   struct PairLd {
-    i32x4 q[4], d[4];   // staged Q and dO rows
+    i32x4 q[NINS], d[NINS];   // staged Q and dO rows
     float ld;           // lane < 32: lse of pair query lane; else D of pair query lane - 32
     int okA, okB;
   };
@@ -813,8 +878,8 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
     f.okA = bA != kNoRow;
     f.okB = bB != kNoRow;
 #pragma unroll
-    for (int ins = 0; ins < 4; ++ins) {
-      const uint32_t o = (ins >= 2 ? bB : bA) + st_off[ins];
+    for (int ins = 0; ins < NINS; ++ins) {
+      const uint32_t o = (ins >= NINS / 2 ? bB : bA) + st_off[ins];
       f.q[ins] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
       f.d[ins] = __builtin_amdgcn_raw_buffer_load_b128(rdo, o, 0, 0);
     }
@@ -829,15 +894,15 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
     return f;
   };
 
-  f32x4 dka[4], dva[4];
+  f32x4 dka[D / 16], dva[D / 16];
 #pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4) dka[t4] = dva[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t4 = 0; t4 < D / 16; ++t4) dka[t4] = dva[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto pair = [&](const PairLd& f) {
 #pragma unroll
-    for (int ins = 0; ins < 4; ++ins) {
-      *(i32x4*)(stQ + (ins * 8 + srow0) * kStride + 8 * piece) = f.q[ins];
-      *(i32x4*)(stO + (ins * 8 + srow0) * kStride + 8 * piece) = f.d[ins];
+    for (int ins = 0; ins < NINS; ++ins) {
+      *(i32x4*)(stQ + (ins * RPI + srow0) * kStride + 8 * piece) = f.q[ins];
+      *(i32x4*)(stO + (ins * RPI + srow0) * kStride + 8 * piece) = f.d[ins];
     }
     stL[lane] = f.ld;
     wave_lds_sync();
@@ -850,10 +915,10 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
       const f32x4 l4 = *(const f32x4*)(stL + 8 * g + 4 * t);
       const f32x4 d4 = *(const f32x4*)(stL + 32 + 8 * g + 4 * t);
       f32x4 st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-      st = mfma_bf16_k32(lds_row8(stQ, arow, 0, g), kh[0], st);
-      st = mfma_bf16_k32(lds_row8(stQ, arow, 1, g), kh[1], st);
-      dp = mfma_bf16_k32(lds_row8(stO, arow, 0, g), vh[0], dp);
-      dp = mfma_bf16_k32(lds_row8(stO, arow, 1, g), vh[1], dp);
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) st = mfma_bf16_k32(lds_row8<D>(stQ, arow, s, g), kh[s], st);
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) dp = mfma_bf16_k32(lds_row8<D>(stO, arow, s, g), vh[s], dp);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float pv = fast_exp2(fmaf(st[i], a.c2, madd - l4[i] * kLog2e));
@@ -866,9 +931,9 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
     split8(dsv, ds_hi, ds_lo);
     // dV^T += dO^T P, dK^T += Q^T dS  (contract over the pair's 32 queries)
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const bf16x8 ot = lds_tr8(stO, t4, lane);
-      const bf16x8 qt = lds_tr8(stQ, t4, lane);
+    for (int t4 = 0; t4 < D / 16; ++t4) {
+      const bf16x8 ot = lds_tr8<D>(stO, t4, lane);
+      const bf16x8 qt = lds_tr8<D>(stQ, t4, lane);
       dva[t4] = mfma_bf16_k32(ot, p_hi, dva[t4]);
       dva[t4] = mfma_bf16_k32(ot, p_lo, dva[t4]);
       dka[t4] = mfma_bf16_k32(qt, ds_hi, dka[t4]);
@@ -883,7 +948,7 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
     cnt = count;
     qtab = ttab = kNoRow;
     if (lane < cnt && p_lane >= 0 && p_lane < n1) {
-      qtab = (uint32_t)block_corner(p_lane, a.grid) * kDim * 2;
+      qtab = (uint32_t)block_corner(p_lane, a.grid) * D * 2;
       ttab = (uint32_t)p_lane * kBlock * 4;
     }
     const int npairs = (cnt + 1) >> 1;
@@ -910,28 +975,28 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
       // the first batch's CSC rows before waiting for them, and rearrange them through the
       // still unused staging tiles into the B-operand layout (row n, channels 32 s + 8 g).
       if (e1 > e0) {
-        i32x4 kl[2], vl[2];
-        const uint32_t kbase = (uint32_t)block_corner(j, a.grid) * kDim * 2;
+        i32x4 kl[D / 32], vl[D / 32];
+        const uint32_t kbase = (uint32_t)block_corner(j, a.grid) * D * 2;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int r = (lane >> 3) + 8 * m;
+        for (int m = 0; m < D / 32; ++m) {
+          const int r = lane / PPR + RPI * m;
           const uint32_t o =
-              kbase + (uint32_t)tile_offset(r, a.grid) * kDim * 2 + 16 * (lane & 7);
+              kbase + (uint32_t)tile_offset(r, a.grid) * D * 2 + 16 * (lane % PPR);
           kl[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, o, 0, 0);
           vl[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, o, 0, 0);
         }
         first_rows = lane < min(64, e1 - e0) ? rows[e0 + lane] : -1;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int at = ((lane >> 3) + 8 * m) * kStride + 8 * (lane & 7);
+        for (int m = 0; m < D / 32; ++m) {
+          const int at = (lane / PPR + RPI * m) * kStride + 8 * (lane % PPR);
           *(i32x4*)(stQ + at) = kl[m];
           *(i32x4*)(stO + at) = vl[m];
         }
         wave_lds_sync();
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          kh[s] = lds_row8(stQ, n, s, g);
-          vh[s] = lds_row8(stO, n, s, g);
+        for (int s = 0; s < D / 32; ++s) {
+          kh[s] = lds_row8<D>(stQ, n, s, g);
+          vh[s] = lds_row8<D>(stO, n, s, g);
         }
         wave_lds_sync();
       }
@@ -970,11 +1035,11 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
   }
 
   if constexpr (MODE == kKeyOverflow) {   // raw partial sums, lane-major
-    float* dst = a.ov_part + (((long)head * a.ov_cap + ov_t) * 64 + lane) * 32;
+    float* dst = a.ov_part + (((long)head * a.ov_cap + ov_t) * 64 + lane) * (D / 2);
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
+    for (int t4 = 0; t4 < D / 16; ++t4) {
       *(f32x4*)(dst + 4 * t4) = dka[t4];
-      *(f32x4*)(dst + 16 + 4 * t4) = dva[t4];
+      *(f32x4*)(dst + D / 4 + 4 * t4) = dva[t4];
     }
     return;
   }
@@ -982,25 +1047,28 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
     const int ovc = uniform(a.ov_count[(long)head * n1 + j]);
     const int ovs = uniform(a.ov_start[(long)head * n1 + j]);
     for (int m = 0; m < ovc; ++m) {
-      const float* src = a.ov_part + (((long)head * a.ov_cap + ovs + m) * 64 + lane) * 32;
+      const float* src = a.ov_part + (((long)head * a.ov_cap + ovs + m) * 64 + lane) * (D / 2);
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
+      for (int t4 = 0; t4 < D / 16; ++t4) {
         dka[t4] += *(const f32x4*)(src + 4 * t4);
-        dva[t4] += *(const f32x4*)(src + 16 + 4 * t4);
+        dva[t4] += *(const f32x4*)(src + D / 4 + 4 * t4);
       }
     }
   }
 
   // ---- push-down of pooled-key gradients and store (lane holds key n, channels 16t4+4g+i)
-  pdown[lane] = pk_sum;
-  pdown[kDim + lane] = pv_sum;
-  wave_lds_sync();
-  bf16* dkp = a.dk + (tok_base + krow) * kDim;
-  bf16* dvp = a.dv + (tok_base + krow) * kDim;
 #pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4) {
+  for (int h = 0; h < H; ++h) {
+    pdown[lane + 64 * h] = pk_sum[h];
+    pdown[D + lane + 64 * h] = pv_sum[h];
+  }
+  wave_lds_sync();
+  bf16* dkp = a.dk + (tok_base + krow) * D;
+  bf16* dvp = a.dv + (tok_base + krow) * D;
+#pragma unroll
+  for (int t4 = 0; t4 < D / 16; ++t4) {
     const f32x4 pk = *(const f32x4*)(pdown + 16 * t4 + 4 * g);
-    const f32x4 pv = *(const f32x4*)(pdown + kDim + 16 * t4 + 4 * g);
+    const f32x4 pv = *(const f32x4*)(pdown + D + 16 * t4 + 4 * g);
     f32x4 rk4, rv4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1012,12 +1080,12 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bwd_key_kernel(
-    BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16 stQ[32 * kStride];
-  __shared__ __attribute__((aligned(16))) bf16 stO[32 * kStride];   // dO rows
-  __shared__ __attribute__((aligned(16))) float pdown[2 * kDim];    // pushed-down dK, dV
+template <int MODE, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1)))
+void bwd_key_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16 stQ[32 * bstride(D)];
+  __shared__ __attribute__((aligned(16))) bf16 stO[32 * bstride(D)];   // dO rows
+  __shared__ __attribute__((aligned(16))) float pdown[2 * D];          // pushed-down dK, dV
   __shared__ __attribute__((aligned(16))) float stL[64];            // lse (0..31), D (32..63)
   __shared__ int pend[MODE == kKeyMask ? 128 : 1];                  // mask hits not yet run
   const int kb = uniform(xcd_block(blockIdx.x, gridDim.x));
@@ -1026,12 +1094,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void bw
     const int total = uniform(a.ov_total[head]);
     for (int t = uniform(kb - head * a.ov_waves); t < total; t += a.ov_waves) {
       const int packed = uniform(a.ov_table[(long)head * a.ov_cap + t]);
-      key_block<MODE>(a, head, packed >> 16, packed & 0xffff, t, stQ, stO, pdown, stL, pend);
+      key_block<MODE, D>(a, head, packed >> 16, packed & 0xffff, t, stQ, stO, pdown, stL,
+                         pend);
     }
   } else {
     const int n1 = a.n >> kBlockShift;
     const int head = uniform(kb / n1);
-    key_block<MODE>(a, head, uniform(kb - head * n1), 0, 0, stQ, stO, pdown, stL, pend);
+    key_block<MODE, D>(a, head, uniform(kb - head * n1), 0, 0, stQ, stO, pdown, stL, pend);
   }
 }
 
@@ -1061,12 +1130,13 @@ static BwdLayout bwd_layout(const Shape& s) {
   if (s.coarse_levels > 0) {
     const size_t n2 = (size_t)s.n >> (2 * kBlockShift);   // 256-token groups
     const size_t nc = (size_t)s.coarse_levels * s.topk;
-    L.part_k = take(sizeof(float) * s.bh * n2 * kUnits * nc * kDim);
-    L.part_v = take(sizeof(float) * s.bh * n2 * kUnits * nc * kDim);
+    const size_t units = (size_t)q_units(s.d);
+    L.part_k = take(sizeof(float) * s.bh * n2 * units * nc * s.d);
+    L.part_v = take(sizeof(float) * s.bh * n2 * units * nc * s.d);
     for (int l = 2; l <= 1 + s.coarse_levels; ++l) {
       const size_t nl = (size_t)s.n_level(l);
-      L.dk_lv[l - 1] = take(sizeof(float) * s.bh * nl * kDim);
-      L.dv_lv[l - 1] = take(sizeof(float) * s.bh * nl * kDim);
+      L.dk_lv[l - 1] = take(sizeof(float) * s.bh * nl * s.d);
+      L.dv_lv[l - 1] = take(sizeof(float) * s.bh * nl * s.d);
     }
   }
   const size_t n1 = (size_t)s.n >> kBlockShift;
@@ -1075,7 +1145,7 @@ static BwdLayout bwd_layout(const Shape& s) {
   L.ov_count = take(sizeof(int32_t) * s.bh * n1);
   L.ov_table = take(sizeof(int32_t) * s.bh * (size_t)L.ov_cap);
   L.ov_total = take(sizeof(int32_t) * s.bh);
-  L.ov_part = take(sizeof(float) * s.bh * (size_t)L.ov_cap * 64 * 32);
+  L.ov_part = take(sizeof(float) * s.bh * (size_t)L.ov_cap * 64 * (s.d / 2));
   L.total = off;
   return L;
 }
@@ -1127,6 +1197,7 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   a.n = s.n;
   a.grid = Grid{s.hbits, s.wbits, s.raster};
   a.levels = s.levels;
+  a.units_log2 = q_units(s.d) == 2 ? 1 : 2;
   a.topk = s.topk;
   a.fine_k = s.fine_k;
   a.bshift = s.bshift;
@@ -1143,19 +1214,28 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   a.plan_blocks = mask ? 0 : (s.bh + 7) / 8 * 8;
   a.ov_waves = std::min(a.ov_cap, kOvWaves);
   const int n2 = s.n >> (2 * kBlockShift);
-  const unsigned qblocks = (unsigned)(a.plan_blocks + s.bh * n2 * kUnits);
+  const unsigned qblocks = (unsigned)(a.plan_blocks + s.bh * n2 * q_units(s.d));
   const int n_coarse = s.coarse_levels * s.topk;
-  const size_t qlds = bwd_query_lds_bytes(n_coarse, s.exclude_overlap && coarse);
-  if (n_coarse == 0)
-    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<0>, dim3(qblocks), dim3(64 * kQWaves), qlds,
-                stream, a);
-  else if (n_coarse <= 16)
-    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<1>, dim3(qblocks), dim3(64 * kQWaves), qlds,
-                stream, a);
+  const size_t qlds = bwd_query_lds_bytes(s.d, n_coarse, s.exclude_overlap && coarse);
+  const auto launch_query = [&](auto kernel) -> hipError_t {
+    if (qlds > 65536) {
+      const hipError_t e = hipFuncSetAttribute((const void*)kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)qlds);
+      if (e != hipSuccess) return e;
+    }
+    LLSA_LAUNCH("bwd_query_kernel", kernel, dim3(qblocks), dim3(64 * kQWaves), qlds, stream, a);
+    return hipGetLastError();
+  };
+  const int nct = n_coarse == 0 ? 0 : n_coarse <= 16 ? 1 : 2;
+  hipError_t err;
+  if (s.d == 64)
+    err = nct == 0 ? launch_query(bwd_query_kernel<0, 64>)
+        : nct == 1 ? launch_query(bwd_query_kernel<1, 64>) : launch_query(bwd_query_kernel<2, 64>);
   else
-    LLSA_LAUNCH("bwd_query_kernel", bwd_query_kernel<2>, dim3(qblocks), dim3(64 * kQWaves), qlds,
-                stream, a);
-  hipError_t err = hipGetLastError();
+    err = nct == 0 ? launch_query(bwd_query_kernel<0, 128>)
+        : nct == 1 ? launch_query(bwd_query_kernel<1, 128>)
+                   : launch_query(bwd_query_kernel<2, 128>);
   if (err != hipSuccess) return err;
   if (coarse) {
     CoarseGradArgs cg{};
@@ -1166,21 +1246,30 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
       blocks += l == 2 ? (keys + kCgWaves - 1) / kCgWaves : keys;
     }
     for (int l = top; l <= kMaxLv; ++l) cg.first_block[l] = (int)blocks;
-    LLSA_LAUNCH("coarse_grad_kernel", coarse_grad_kernel, dim3((unsigned)blocks),
-                dim3(64 * kCgWaves), 0, stream, a, cg);
+    if (s.d == 64)
+      LLSA_LAUNCH("coarse_grad_kernel", coarse_grad_kernel<64>, dim3((unsigned)blocks),
+                  dim3(64 * kCgWaves), 0, stream, a, cg);
+    else
+      LLSA_LAUNCH("coarse_grad_kernel", coarse_grad_kernel<128>, dim3((unsigned)blocks),
+                  dim3(64 * kCgWaves), 0, stream, a, cg);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const long kwaves = (long)s.bh * (s.n >> kBlockShift);
-  if (mask) {
+  const dim3 ovgrid((unsigned)((long)s.bh * a.ov_waves)), kgrid((unsigned)kwaves);
+  if (mask) {   // the comparator: 64 channels only (checked by the caller)
     a.mask = mask;
-    LLSA_LAUNCH("bwd_key_mask_kernel", bwd_key_kernel<kKeyMask>, dim3((unsigned)kwaves),
-                dim3(64), 0, stream, a);
-  } else {
-    LLSA_LAUNCH("bwd_key_overflow_kernel", bwd_key_kernel<kKeyOverflow>,
-                dim3((unsigned)((long)s.bh * a.ov_waves)), dim3(64), 0, stream, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    LLSA_LAUNCH("bwd_key_kernel", bwd_key_kernel<kKeyCsc>, dim3((unsigned)kwaves), dim3(64), 0,
+    LLSA_LAUNCH("bwd_key_mask_kernel", (bwd_key_kernel<kKeyMask, 64>), kgrid, dim3(64), 0,
                 stream, a);
+  } else if (s.d == 64) {
+    LLSA_LAUNCH("bwd_key_overflow_kernel", (bwd_key_kernel<kKeyOverflow, 64>), ovgrid, dim3(64),
+                0, stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    LLSA_LAUNCH("bwd_key_kernel", (bwd_key_kernel<kKeyCsc, 64>), kgrid, dim3(64), 0, stream, a);
+  } else {
+    LLSA_LAUNCH("bwd_key_overflow_kernel", (bwd_key_kernel<kKeyOverflow, 128>), ovgrid,
+                dim3(64), 0, stream, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    LLSA_LAUNCH("bwd_key_kernel", (bwd_key_kernel<kKeyCsc, 128>), kgrid, dim3(64), 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -20,6 +20,8 @@
 //     values as bf16 hi + lo parts, weight 16^l as the log2-domain bias 4l), then O and LSE.
 // fp32 tensors use v_mfma_f32_16x16x4f32 with the same data flow.  Workgroups are renumbered
 // so that each XCD (and its L2) works on one contiguous spatial range of level-2 groups.
+// D (head_dim) is 64 or 128 (bf16 only): rows, MFMA contraction chains and accumulators scale
+// with it; with 128 channels a wave owns 2 query blocks (its accumulators double).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,8 +29,10 @@ namespace llsa {
 
 constexpr int kMaxLevels = 6;
 constexpr int kFwdWaves = 4;
-constexpr int kStrideBf16 = kDim + 8;   // 144-byte LDS rows: 16-byte aligned, staggered banks
-constexpr int kStrideF32 = kDim + 4;
+// LDS row strides: D + 8 bf16 (144 bytes for 64 channels: 16-byte aligned, staggered banks),
+// D + 4 floats
+__host__ __device__ constexpr int stride_bf16(int D) { return D + 8; }
+__host__ __device__ constexpr int stride_f32(int D) { return D + 4; }
 constexpr float kMinusBig = -1e30f;     // running-max floor: keeps exp2 arguments finite
 
 struct FwdArgs {
@@ -60,11 +64,11 @@ __device__ __forceinline__ void split_bf16(f32x4 a, f32x4 b, bf16x8& hi, bf16x8&
 constexpr int kWavePicks = 64;     // QB query blocks x K (QB K <= 64)
 constexpr int kSentinel = 0x7f000000;
 
-template <bool BF16>
+template <bool BF16, int D>
 struct FwdCfg {
   static constexpr int ES = BF16 ? 2 : 4;               // element bytes
-  static constexpr int kStride = BF16 ? kStrideBf16 : kStrideF32;
-  static constexpr int kRowBytes = kDim * ES;
+  static constexpr int kStride = BF16 ? stride_bf16(D) : stride_f32(D);
+  static constexpr int kRowBytes = D * ES;
   static constexpr int PPR = kRowBytes / 16;            // 16-byte pieces per row
   static constexpr int kTile = 16 * kStride;            // one 16-row tile (elements)
   static constexpr int NB = BF16 ? 4 : 2;               // coarse buffers: K(hi,lo), V(hi,lo)
@@ -74,27 +78,30 @@ struct FwdCfg {
 
 // Dynamic LDS: per wave a K/V tile pair and its pick lists; per workgroup the coarse tiles
 // [ctiles][NB][16][stride] and their biases.
-__host__ __device__ constexpr int fwd_wave_lds_bytes(bool bf16) {
-  return 2 * 16 * (bf16 ? kStrideBf16 * 2 : kStrideF32 * 4) + (int)sizeof(int) * 4 * kWavePicks;
+__host__ __device__ constexpr int fwd_wave_lds_bytes(bool bf16, int D) {
+  return 2 * 16 * (bf16 ? stride_bf16(D) * 2 : stride_f32(D) * 4) +
+         (int)sizeof(int) * 4 * kWavePicks;
 }
 // ... then each slot's bias and key id, and with overlap exclusion per-block biases
 // [waves][4 blocks][ctiles * 16].
-static size_t fwd_lds_bytes(bool bf16, int n_coarse, bool exclude) {
+static size_t fwd_lds_bytes(bool bf16, int D, int n_coarse, bool exclude) {
   const int es = bf16 ? 2 : 4;
-  const int stride = bf16 ? kStrideBf16 : kStrideF32;
+  const int stride = bf16 ? stride_bf16(D) : stride_f32(D);
   const int nb = bf16 ? 4 : 2;
   const int ctiles = (n_coarse + 15) / 16;
-  return kFwdWaves * fwd_wave_lds_bytes(bf16) + (size_t)ctiles * nb * 16 * stride * es +
+  return kFwdWaves * fwd_wave_lds_bytes(bf16, D) + (size_t)ctiles * nb * 16 * stride * es +
          (sizeof(float) + sizeof(int)) * 16 * ctiles +
          (exclude ? sizeof(float) * kFwdWaves * 4 * 16 * ctiles : 0);
 }
 
-template <bool BF16, int QB>   // QB: query blocks per wave (4, or 2 for K > 16)
-__global__ __launch_bounds__(64 * kFwdWaves) __attribute__((amdgpu_waves_per_eu(BF16 ? 3 : 2)))
-void attn_fwd_kernel(FwdArgs a) {
+// QB: query blocks per wave (4, or 2 for K > 16 or 128 channels); D: head_dim
+template <bool BF16, int QB, int D>
+__global__ __launch_bounds__(64 * kFwdWaves)
+__attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kernel(FwdArgs a) {
   constexpr int PS = kWavePicks / QB;                     // pick slots per query block
   constexpr int kUnitsPerGroup = kBlock / (kFwdWaves * QB);   // workgroups per level-2 group
-  using C = FwdCfg<BF16>;
+  static_assert(BF16 || D == 64, "fp32 tokens: 64 channels");
+  using C = FwdCfg<BF16, D>;
   typedef typename std::conditional<BF16, bf16, float>::type T;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
@@ -114,14 +121,14 @@ void attn_fwd_kernel(FwdArgs a) {
   const int n_coarse = a.coarse_levels * K;
   const int ctiles = (n_coarse + 15) >> 4;
 
-  char* wbase = smem + w * fwd_wave_lds_bytes(BF16);
+  char* wbase = smem + w * fwd_wave_lds_bytes(BF16, D);
   T* kt = (T*)wbase;                          // the staged key block: K rows, then V rows
   T* vt = kt + C::kTile;
   int* keys = (int*)(vt + C::kTile);          // [64] pick keys (id << 8 | index)
   int* sorted = keys + kWavePicks;            // [64] ascending
   int* uoff = sorted + kWavePicks;            // [64] first-row byte offset of U[u]
   int* umask = uoff + kWavePicks;             // [64] blocks of the wave that picked U[u]
-  T* ctile = (T*)(smem + kFwdWaves * fwd_wave_lds_bytes(BF16));
+  T* ctile = (T*)(smem + kFwdWaves * fwd_wave_lds_bytes(BF16, D));
   float* cbias = (float*)(ctile + ctiles * C::NB * C::kTile);
   int* cid = (int*)(cbias + 16 * ctiles);       // key id of each coarse slot (-1: none)
   float* xbias = (float*)(cid + 16 * ctiles);   // with exclusion: [w][bb][slot] biases
@@ -141,26 +148,27 @@ void attn_fwd_kernel(FwdArgs a) {
   }
   // B operand of S^T for block bb: lane (n, g) holds query row n, channels 32s + 8g .. +7
   // (bf16) or 16g + 4c .. +3 (fp32)
-  bf16x8 qh[QB][2];
-  f32x4 qf[QB][4];
+  bf16x8 qh[QB][D / 32];
+  f32x4 qf[QB][D / 16];
 #pragma unroll
   for (int bb = 0; bb < QB; ++bb) {
     const uint32_t qrow =
         (uint32_t)(block_corner(pb_first + bb, a.grid) + tile_offset(n, a.grid)) * C::kRowBytes;
     if constexpr (BF16) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) qh[bb][s2] = buf_load8(rq, qrow + (32 * s2 + 8 * g) * 2);
+      for (int s2 = 0; s2 < D / 32; ++s2)
+        qh[bb][s2] = buf_load8(rq, qrow + (32 * s2 + 8 * g) * 2);
     } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qf[bb][c] = buf_load4f(rq, qrow + (16 * g + 4 * c) * 4);
+      for (int c = 0; c < D / 16; ++c) qf[bb][c] = buf_load4f(rq, qrow + (16 * g + 4 * c) * 4);
     }
   }
 
-  // ---- coarse keys of the group (slot e / 8 of 16 ctiles, channels 8 (e % 8) .. +7): fp32
-  // pooled values as bf16 hi + lo parts (fp32 tensors: as they are) and the slot's bias
+  // ---- coarse keys of the group (slot e / (D/8) of 16 ctiles, channels 8 (e % (D/8)) ..
+  // +7): fp32 pooled values as bf16 hi + lo parts (fp32 tensors: as they are) and the bias
   const int pb0 = a2 * kBlock;
-  for (int e = tid; e < ctiles * 16 * 8; e += 64 * kFwdWaves) {
-    const int cslot = e >> 3, c8 = (e & 7) * 8;
+  for (int e = tid; e < ctiles * 16 * (D / 8); e += 64 * kFwdWaves) {
+    const int cslot = e / (D / 8), c8 = (e % (D / 8)) * 8;
     f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
     float bias = -INFINITY;
     int cslot_id = -1;
@@ -171,8 +179,8 @@ void attn_fwd_kernel(FwdArgs a) {
       const int id = a.sel[l - 1][((long)head * nl + anc) * K + (cslot - (l - 2) * K)];
       if (id >= 0 && id < nl) {
         cslot_id = id;
-        const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
-        const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * kDim + c8;
+        const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * D + c8;
+        const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * D + c8;
         k0 = *(const f32x4*)kp;
         k1 = *(const f32x4*)(kp + 4);
         v0 = *(const f32x4*)vp;
@@ -293,13 +301,13 @@ void attn_fwd_kernel(FwdArgs a) {
   }
 
   float m_run[QB], l_run[QB];   // running max (log2 domain) and this lane's partial sums
-  f32x4 acc[QB][4];             // O^T of each block: lane (n, g) holds d = 16 t4 + 4g + i
+  f32x4 acc[QB][D / 16];        // O^T of each block: lane (n, g) holds d = 16 t4 + 4g + i
 #pragma unroll
   for (int bb = 0; bb < QB; ++bb) {
     m_run[bb] = kMinusBig;
     l_run[bb] = 0.f;
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) acc[bb][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t4 = 0; t4 < D / 16; ++t4) acc[bb][t4] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   // One 16-key tile for block bb: scores x = st * c2 + bias (log2 domain), online softmax,
@@ -314,7 +322,7 @@ void attn_fwd_kernel(FwdArgs a) {
     f32x4 st = {0.f, 0.f, 0.f, 0.f};
     if constexpr (BF16) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
+      for (int s2 = 0; s2 < D / 32; ++s2) {
         st = mfma_bf16_k32(*(const bf16x8*)(ktl + n * C::kStride + 32 * s2 + 8 * g), qh[bb][s2],
                            st);
         if (klo)
@@ -323,7 +331,7 @@ void attn_fwd_kernel(FwdArgs a) {
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < D / 16; ++c) {
         const f32x4 kf = *(const f32x4*)(ktl + n * C::kStride + 16 * g + 4 * c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) st = mfma_f32_k4(kf[e], qf[bb][c][e], st);
@@ -344,7 +352,7 @@ void attn_fwd_kernel(FwdArgs a) {
       const float alpha = fast_exp2(m_run[bb] - m_new);
       l_run[bb] *= alpha;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
+      for (int t4 = 0; t4 < D / 16; ++t4)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[bb][t4][i] *= alpha;
       m_run[bb] = m_new;
@@ -360,14 +368,14 @@ void attn_fwd_kernel(FwdArgs a) {
       const int r = (lane & 15) >> 2;
       const int c = lane & 3;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
+      for (int t4 = 0; t4 < D / 16; ++t4) {
         const int off = (4 * g + r) * C::kStride + 16 * t4 + 4 * c;
         acc[bb][t4] = mfma_bf16_k16(lds_read_tr16(vtl + off), pb, acc[bb][t4]);
         if (vlo) acc[bb][t4] = mfma_bf16_k16(lds_read_tr16(vlo + off), pb, acc[bb][t4]);
       }
     } else {
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4)
+      for (int t4 = 0; t4 < D / 16; ++t4)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           acc[bb][t4] =
@@ -431,18 +439,18 @@ void attn_fwd_kernel(FwdArgs a) {
     const float l_tot = group4_sum(l_run[bb]);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;   // 0 only if every key was skipped
     if constexpr (BF16) {
-      bf16* op = (bf16*)a.o + (tok_base + qrow) * kDim;
+      bf16* op = (bf16*)a.o + (tok_base + qrow) * D;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
+      for (int t4 = 0; t4 < D / 16; ++t4) {
         f32x4 r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) r[i] = acc[bb][t4][i] * inv;
         *(bf16x4*)(op + 16 * t4 + 4 * g) = pack4_bf16(r);
       }
     } else {
-      float* op = (float*)a.o + (tok_base + qrow) * kDim;
+      float* op = (float*)a.o + (tok_base + qrow) * D;
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
+      for (int t4 = 0; t4 < D / 16; ++t4) {
         f32x4 r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) r[i] = acc[bb][t4][i] * inv;
@@ -479,29 +487,26 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const v
   a.exclude = s.exclude_overlap && s.coarse_levels > 0;
   a.c2 = s.scale * kLog2e;
   const int n_coarse = s.coarse_levels * s.topk;
-  const size_t lds = fwd_lds_bytes(s.bf16, n_coarse, s.exclude_overlap != 0);
-  // one workgroup per level-2 group (N is a multiple of 16^2), two when K > 16
-  const bool wide = s.fine_k > kWavePicks / 4;
+  const size_t lds = fwd_lds_bytes(s.bf16, s.d, n_coarse, s.exclude_overlap != 0);
+  // one workgroup per level-2 group (N is a multiple of 16^2), two when a wave owns 2 query
+  // blocks (K > 16, so that its 2 K picks fit 64 lanes; or 128 channels)
+  const bool wide = s.fine_k > kWavePicks / 4 || s.d == 128;
   const unsigned blocks = (unsigned)((long)s.bh * (s.n >> (2 * kBlockShift)) * (wide ? 2 : 1));
-  const void* fn = s.bf16 ? (wide ? (const void*)attn_fwd_kernel<true, 2>
-                                  : (const void*)attn_fwd_kernel<true, 4>)
-                          : (wide ? (const void*)attn_fwd_kernel<false, 2>
-                                  : (const void*)attn_fwd_kernel<false, 4>);
-  if (lds > 65536) {
-    const hipError_t e =
-        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
   const dim3 grid(blocks), block(64 * kFwdWaves);
-  if (s.bf16 && !wide)
-    LLSA_LAUNCH("attn_fwd_kernel", (attn_fwd_kernel<true, 4>), grid, block, lds, stream, a);
-  else if (s.bf16)
-    LLSA_LAUNCH("attn_fwd_kernel", (attn_fwd_kernel<true, 2>), grid, block, lds, stream, a);
-  else if (!wide)
-    LLSA_LAUNCH("attn_fwd_kernel", (attn_fwd_kernel<false, 4>), grid, block, lds, stream, a);
-  else
-    LLSA_LAUNCH("attn_fwd_kernel", (attn_fwd_kernel<false, 2>), grid, block, lds, stream, a);
-  return hipGetLastError();
+  const auto launch = [&](auto kernel) -> hipError_t {
+    if (lds > 65536) {
+      const hipError_t e = hipFuncSetAttribute((const void*)kernel,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    LLSA_LAUNCH("attn_fwd_kernel", kernel, grid, block, lds, stream, a);
+    return hipGetLastError();
+  };
+  if (s.d == 128) return launch(attn_fwd_kernel<true, 2, 128>);   // bf16 only (checked)
+  if (s.bf16)
+    return wide ? launch(attn_fwd_kernel<true, 2, 64>) : launch(attn_fwd_kernel<true, 4, 64>);
+  return wide ? launch(attn_fwd_kernel<false, 2, 64>) : launch(attn_fwd_kernel<false, 4, 64>);
 }
 
 }  // namespace llsa

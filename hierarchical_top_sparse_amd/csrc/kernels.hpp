@@ -23,6 +23,7 @@ void prof_end(void* handle, hipStream_t stream);
 struct Shape {
   int bh;        // batch * heads
   int n;         // tokens per head
+  int d;         // head_dim: 64 or 128
   int hbits;     // log2(height)
   int wbits;     // log2(width)
   int levels;    // L

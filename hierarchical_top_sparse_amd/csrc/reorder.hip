@@ -1,7 +1,8 @@
 // 2D index reordering (raster <-> Morton), a bit-exact permutation of token rows.
 // Method: paper summary sec. 4.2 / Figure 2 and the article's sec. 四 (spatially coherent
 // token order before 1D pooling).  HBM-bound copy: every lane moves 16-byte chunks, so each
-// token row (128 B in bf16, 256 B in fp32) is read and written by whole contiguous segments.
+// token row (128 or 256 B in bf16, 256 or 512 B in fp32) is read and written by whole
+// contiguous segments.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -40,8 +41,9 @@ __global__ __launch_bounds__(kReorderThreads) void reorder_kernel(
 
 hipError_t launch_reorder(const Shape& s, const void* x, void* y, int inverse,
                           hipStream_t stream) {
-  const int row_bytes = kDim * (s.bf16 ? 2 : 4);
-  const int cpr_shift = (row_bytes == 128) ? 3 : 4;
+  const int row_bytes = s.d * (s.bf16 ? 2 : 4);   // 128 .. 512: 8 .. 32 chunks per row
+  int cpr_shift = 0;
+  while ((16 << cpr_shift) < row_bytes) ++cpr_shift;
   const long total = (long)s.bh * s.n << cpr_shift;
   const long per_block = (long)kReorderThreads * kChunksPerThread;
   const long blocks = (total + per_block - 1) / per_block;

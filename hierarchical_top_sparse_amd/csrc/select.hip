@@ -16,8 +16,9 @@
 //
 // Scores are fp32 dot products on the fp32 MFMA (v_mfma_f32_16x16x4f32) in the S^T
 // orientation: lane (n, g) holds the scores of query n against candidates 4g..4g+3 of each
-// 16-row candidate tile.  Tiles are loaded kTilesPerRound at a time, so a ranking costs one or
-// two memory round trips rather than one per tile.
+// 16-row candidate tile, and channels g D/4 .. g D/4 + D/4 - 1 of the rows (D = head_dim, 64
+// or 128).  Tiles are loaded tiles_per_round(D) at a time, so a ranking costs one or two
+// memory round trips rather than one per tile.
 //  * A group (16 queries): each lane keeps a register top-KMAX list of its candidates, and the
 //    four lanes of a query merge their lists with cross-lane steps.
 //  * A single query is replicated over the 16 columns; each (tile, candidate) is then kept by
@@ -38,10 +39,11 @@ namespace llsa {
 constexpr int kSelWaves = 4;
 constexpr int kSelMaxLv = 6;
 constexpr int kNoId = 0x7fffffff;
-constexpr int kTilesPerRound = 4;   // candidate tiles loaded at once
+// candidate tiles loaded at once (their rows stay in registers: fewer for wider rows)
+__host__ __device__ constexpr int tiles_per_round(int D) { return D == 64 ? 4 : 2; }
 
 struct SelArgs {
-  const float* q[kSelMaxLv];   // level l at index l - 1: [bh, n_l, 64] fp32
+  const float* q[kSelMaxLv];   // level l at index l - 1: [bh, n_l, head_dim] fp32
   const float* k[kSelMaxLv];
   int32_t* sel[kSelMaxLv];     // [bh, n_l, K]
   int bh;
@@ -88,26 +90,32 @@ __device__ __forceinline__ void list_insert(float (&ls)[KMAX], int (&li)[KMAX], 
   li[0] = c[0] ? id : li[0];
 }
 
-// Candidate rows first + n (channels 16g .. 16g + 15) of a 16-row tile; rows outside
+// Candidate rows first + n (channels g D/4 .. g D/4 + D/4 - 1) of a 16-row tile; rows outside
 // [0, n_rows) and tiles with first < 0 read as zeros (their scores are never inserted).
+template <int D>
 __device__ __forceinline__ void load_tile(const float* kh, int first, int n_rows, int n, int g,
-                                          f32x4 (&kv)[4]) {
+                                          f32x4 (&kv)[D / 16]) {
   const int row = first + n;
   const bool ok = first >= 0 && row < n_rows;
-  const float* p = kh + (long)(ok ? row : 0) * kDim + 16 * g;
+  const float* p = kh + (long)(ok ? row : 0) * D + (D / 4) * g;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) kv[c] = ok ? *(const f32x4*)(p + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < D / 16; ++c)
+    kv[c] = ok ? *(const f32x4*)(p + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// acc[i] = score of query n against candidate 4g + i of the tile: the 64 channels are
-// contracted in four independent MFMA chains (channels 16g + 4c + e, e = 0..3, per chain c).
-__device__ __forceinline__ f32x4 score_tile(const f32x4 (&kv)[4], const f32x4 (&qv)[4]) {
+// acc[i] = score of query n against candidate 4g + i of the tile: the D channels are
+// contracted in four independent MFMA chains (chain c takes the lane's vectors j = c, c + 4,
+// ..., channels g D/4 + 4j + e, e = 0..3).
+template <int D>
+__device__ __forceinline__ f32x4 score_tile(const f32x4 (&kv)[D / 16], const f32x4 (&qv)[D / 16]) {
   f32x4 acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[c] = mfma_f32_k4(kv[c][e], qv[c][e], acc[c]);
+    for (int j = c; j < D / 16; j += 4)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[c] = mfma_f32_k4(kv[j][e], qv[j][e], acc[c]);
   }
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
@@ -163,11 +171,12 @@ __device__ __forceinline__ void merge_lists(float (&ls)[KMAX], int (&li)[KMAX], 
 //   else:     candidates are the B = 2^bshift children of each pick in pickv (lane i holds
 //             pick i of the parent, i < K; ids outside [0, n_rows / B) are skipped), B / 16
 //             tiles per pick.
-template <int KMAX, bool SINGLE>
+template <int KMAX, bool SINGLE, int D>
 __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool all_keys,
                                              int pickv, int K, int bshift,
-                                             const f32x4 (&qv)[4], int n, int g,
+                                             const f32x4 (&qv)[D / 16], int n, int g,
                                              int (&pick)[KMAX]) {
+  constexpr int kTilesPerRound = tiles_per_round(D);
   float ls[KMAX];
   int li[KMAX];
 #pragma unroll
@@ -179,7 +188,7 @@ __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool a
   const int sub_shift = bshift - 4;   // log2 of the tiles per pick
   const int tiles = all_keys ? (n_rows + 15) >> 4 : K << sub_shift;
   for (int t0 = 0; t0 < tiles; t0 += kTilesPerRound) {
-    f32x4 kv[kTilesPerRound][4];
+    f32x4 kv[kTilesPerRound][D / 16];
     int first[kTilesPerRound];
 #pragma unroll
     for (int i = 0; i < kTilesPerRound; ++i) {
@@ -194,15 +203,15 @@ __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool a
           first[i] = (pk >= 0 && pk < n_parent) ? (pk << bshift) + 16 * sub : -1;
         }
       }
-      load_tile(kh, first[i], n_rows, n, g, kv[i]);
+      load_tile<D>(kh, first[i], n_rows, n, g, kv[i]);
     }
 #pragma unroll
     for (int i = 0; i < kTilesPerRound; ++i) {
       if (first[i] < 0) continue;
-      const f32x4 acc = score_tile(kv[i], qv);
+      const f32x4 acc = score_tile<D>(kv[i], qv);
       if constexpr (SINGLE) {
-        // tile t0 + i is kept by the lanes with n / 4 == i (t0 is a multiple of 4)
-        if ((n >> 2) == i) {
+        // tile t = t0 + i is kept by the lanes with n / 4 == t % 4
+        if ((n >> 2) == ((t0 + i) & 3)) {
           const int e = n & 3;
           const float sc = e == 0 ? acc[0] : e == 1 ? acc[1] : e == 2 ? acc[2] : acc[3];
           const int cid = first[i] + 4 * g + e;
@@ -222,7 +231,7 @@ __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool a
 }
 
 // The waves of selection workgroup bid of nblocks (renumbered per XCD).
-template <int KMAX>
+template <int KMAX, int D>
 __device__ __forceinline__ void select_group(const SelArgs& a, int bid, int nblocks) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 15;
@@ -256,13 +265,13 @@ __device__ __forceinline__ void select_group(const SelArgs& a, int bid, int nblo
           if (lane < K)
             pickv = a.sel[lv][((long)head * (n_lv >> bs) + (anc >> bs)) * K + lane];
         }
-        const float* qrow = a.q[lv - 1] + ((long)head * n_lv + anc) * kDim + 16 * g;
-        f32x4 qv[4];
+        const float* qrow = a.q[lv - 1] + ((long)head * n_lv + anc) * D + (D / 4) * g;
+        f32x4 qv[D / 16];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) qv[c] = *(const f32x4*)(qrow + 4 * c);
+        for (int c = 0; c < D / 16; ++c) qv[c] = *(const f32x4*)(qrow + 4 * c);
         int pick[KMAX];
-        rank_queries<KMAX, true>(a.k[lv - 1] + (long)head * n_lv * kDim, n_lv, top, pickv, K,
-                                 bs, qv, n, g, pick);
+        rank_queries<KMAX, true, D>(a.k[lv - 1] + (long)head * n_lv * D, n_lv, top, pickv, K,
+                                    bs, qv, n, g, pick);
         int nv = kNoId;
 #pragma unroll
         for (int r = 0; r < KMAX; ++r)
@@ -275,17 +284,17 @@ __device__ __forceinline__ void select_group(const SelArgs& a, int bid, int nblo
   }
 
   // the group of 16 queries at level lo
-  const float* qh = a.q[lo - 1] + (long)head * n_lo * kDim;
+  const float* qh = a.q[lo - 1] + (long)head * n_lo * D;
   const int q_id = grp * 16 + n;
   const bool qvalid = q_id < n_lo;
-  f32x4 qv[4];
+  f32x4 qv[D / 16];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    qv[c] = qvalid ? *(const f32x4*)(qh + (long)q_id * kDim + 16 * g + 4 * c)
+  for (int c = 0; c < D / 16; ++c)
+    qv[c] = qvalid ? *(const f32x4*)(qh + (long)q_id * D + (D / 4) * g + 4 * c)
                    : f32x4{0.f, 0.f, 0.f, 0.f};
   int pick[KMAX];
-  rank_queries<KMAX, false>(a.k[lo - 1] + (long)head * n_lo * kDim, n_lo, lo == a.levels, pickv,
-                            K, bs, qv, n, g, pick);
+  rank_queries<KMAX, false, D>(a.k[lo - 1] + (long)head * n_lo * D, n_lo, lo == a.levels,
+                               pickv, K, bs, qv, n, g, pick);
   if (g == 0 && qvalid) {
     int32_t* dst = a.sel[lo - 1] + ((long)head * n_lo + q_id) * K;
 #pragma unroll
@@ -294,9 +303,9 @@ __device__ __forceinline__ void select_group(const SelArgs& a, int bid, int nblo
   }
 }
 
-template <int KMAX>
+template <int KMAX, int D>
 __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelArgs a) {
-  select_group<KMAX>(a, blockIdx.x, gridDim.x);
+  select_group<KMAX, D>(a, blockIdx.x, gridDim.x);
 }
 
 // A selection launch that also pools V (its levels 1 and 2 from the tokens, or level 3 from
@@ -304,36 +313,37 @@ __global__ __launch_bounds__(64 * kSelWaves) void select_kernel(SelArgs a) {
 // XCDs are those of a plain launch) and raise their waves' issue priority; the pooling
 // workgroups after them fill the chip while the few selection waves run their dependent
 // chains.  V is first read by the attention, so nothing in the launch depends on it.
-template <int KMAX>
+template <int KMAX, int D>
 __global__ __launch_bounds__(64 * kSelWaves) void select_pool12_kernel(SelArgs a, int sel_blocks,
                                                                        PoolArgs pa, int n,
                                                                        Grid grid, int gph) {
-  __shared__ __attribute__((aligned(16))) float sh[kBlock][kDim];
+  __shared__ __attribute__((aligned(16))) float sh[kBlock][D];
   if ((int)blockIdx.x < sel_blocks) {
     __builtin_amdgcn_s_setprio(2);
-    select_group<KMAX>(a, blockIdx.x, sel_blocks);
+    select_group<KMAX, D>(a, blockIdx.x, sel_blocks);
     return;
   }
-  pool12_bf16_group(pa, n, grid, gph, 0, (int)blockIdx.x - sel_blocks, sh);
+  pool12_bf16_group<D>(pa, n, grid, gph, 0, (int)blockIdx.x - sel_blocks, sh);
 }
 
-template <int KMAX>
+template <int KMAX, int D>
 __global__ __launch_bounds__(64 * kSelWaves) void select_pool_next_kernel(SelArgs a,
                                                                           int sel_blocks,
                                                                           PoolNextArgs pb,
                                                                           long total_out) {
   if ((int)blockIdx.x < sel_blocks) {
     __builtin_amdgcn_s_setprio(2);
-    select_group<KMAX>(a, blockIdx.x, sel_blocks);
+    select_group<KMAX, D>(a, blockIdx.x, sel_blocks);
     return;
   }
   const long i = (long)((int)blockIdx.x - sel_blocks) * 256 + threadIdx.x;
-  if (i < total_out) pool_next_elem<16>(pb, 0, i);
+  if (i < total_out) pool_next_elem<16, D>(pb, 0, i);
 }
 
+template <int D>
 __global__ __launch_bounds__(256) void pool_next_v_kernel(PoolNextArgs pb, long total_out) {
   const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i < total_out) pool_next_elem<16>(pb, 0, i);
+  if (i < total_out) pool_next_elem<16, D>(pb, 0, i);
 }
 
 // Level-1 picks of 64-token blocks as the 16-token blocks they cover: row q of the output (a
@@ -368,6 +378,29 @@ struct PoolInSelect {
   long total = 0;   // kind 2: output elements
 };
 
+template <int KMAX, int D>
+static hipError_t launch_select_kernels(const Shape& s, const SelArgs& a, unsigned blocks,
+                                        const PoolInSelect& pv, hipStream_t stream) {
+  const dim3 wg(64 * kSelWaves);
+  if (pv.kind == 0) {
+    LLSA_LAUNCH("select_kernel", (select_kernel<KMAX, D>), dim3(blocks), wg, 0, stream, a);
+    return hipGetLastError();
+  }
+  const unsigned sb = (blocks + 7) / 8 * 8;
+  if (pv.kind == 1) {
+    const int gph = s.n >> (2 * kBlockShift);
+    const Grid tg{s.hbits, s.wbits, s.raster};
+    LLSA_LAUNCH("select_pool_kernel", (select_pool12_kernel<KMAX, D>),
+                dim3(sb + (unsigned)(s.bh * gph)), wg, 0, stream, a, (int)sb, pv.pa, s.n, tg,
+                gph);
+  } else {
+    LLSA_LAUNCH("select_pool_kernel", (select_pool_next_kernel<KMAX, D>),
+                dim3(sb + (unsigned)((pv.total + 255) / 256)), wg, 0, stream, a, (int)sb,
+                pv.pb, pv.total);
+  }
+  return hipGetLastError();
+}
+
 static hipError_t launch_select_range(const Shape& s, const float* const* q_lv,
                                       const float* const* k_lv, int32_t* const* sel,
                                       int level_hi, int level_lo, hipStream_t stream,
@@ -388,46 +421,14 @@ static hipError_t launch_select_range(const Shape& s, const float* const* q_lv,
   const int n_lo = s.n_level(level_lo);
   const long waves = (long)s.bh * ((n_lo + 15) >> 4);   // one per group
   const unsigned blocks = (unsigned)((waves + kSelWaves - 1) / kSelWaves);
-  if (pv.kind != 0) {
-    const unsigned sb = (blocks + 7) / 8 * 8;
-    const dim3 wg(64 * kSelWaves);
-    if (pv.kind == 1) {
-      const int gph = s.n >> (2 * kBlockShift);
-      const dim3 g(sb + (unsigned)(s.bh * gph));
-      const Grid tg{s.hbits, s.wbits, s.raster};
-      if (s.topk <= 8)
-        LLSA_LAUNCH("select_pool_kernel", select_pool12_kernel<8>, g, wg, 0, stream, a, (int)sb,
-                    pv.pa, s.n, tg, gph);
-      else if (s.topk <= 16)
-        LLSA_LAUNCH("select_pool_kernel", select_pool12_kernel<16>, g, wg, 0, stream, a,
-                    (int)sb, pv.pa, s.n, tg, gph);
-      else
-        LLSA_LAUNCH("select_pool_kernel", select_pool12_kernel<32>, g, wg, 0, stream, a,
-                    (int)sb, pv.pa, s.n, tg, gph);
-    } else {
-      const dim3 g(sb + (unsigned)((pv.total + 255) / 256));
-      if (s.topk <= 8)
-        LLSA_LAUNCH("select_pool_kernel", select_pool_next_kernel<8>, g, wg, 0, stream, a,
-                    (int)sb, pv.pb, pv.total);
-      else if (s.topk <= 16)
-        LLSA_LAUNCH("select_pool_kernel", select_pool_next_kernel<16>, g, wg, 0, stream, a,
-                    (int)sb, pv.pb, pv.total);
-      else
-        LLSA_LAUNCH("select_pool_kernel", select_pool_next_kernel<32>, g, wg, 0, stream, a,
-                    (int)sb, pv.pb, pv.total);
-    }
-    return hipGetLastError();
-  }
-  if (s.topk <= 8)
-    LLSA_LAUNCH("select_kernel", select_kernel<8>, dim3(blocks), dim3(64 * kSelWaves), 0, stream,
-                a);
-  else if (s.topk <= 16)
-    LLSA_LAUNCH("select_kernel", select_kernel<16>, dim3(blocks), dim3(64 * kSelWaves), 0,
-                stream, a);
-  else
-    LLSA_LAUNCH("select_kernel", select_kernel<32>, dim3(blocks), dim3(64 * kSelWaves), 0,
-                stream, a);
-  return hipGetLastError();
+  const auto by_k = [&](auto dc) {
+    constexpr int D = decltype(dc)::value;
+    if (s.topk <= 8) return launch_select_kernels<8, D>(s, a, blocks, pv, stream);
+    if (s.topk <= 16) return launch_select_kernels<16, D>(s, a, blocks, pv, stream);
+    return launch_select_kernels<32, D>(s, a, blocks, pv, stream);
+  };
+  return s.d == 64 ? by_k(std::integral_constant<int, 64>{})
+                   : by_k(std::integral_constant<int, 128>{});
 }
 
 hipError_t launch_select(const Shape& s, const float* const* q_lv, const float* const* k_lv,
@@ -470,7 +471,7 @@ hipError_t launch_pool_select(const Shape& s, const void* const x[3], float* con
     pn.kind = 2;
     pn.pb.in[0] = lv[2][1];
     pn.pb.out[0] = lv[2][2];
-    pn.total = (long)s.bh * s.n_level(3) * kDim;
+    pn.total = (long)s.bh * s.n_level(3) * s.d;
   }
   e = launch_select_range(s, lv[0], lv[1], sel, 1, 1, stream, pn);
   if (e != hipSuccess) return e;
@@ -480,9 +481,12 @@ hipError_t launch_pool_select(const Shape& s, const void* const x[3], float* con
     PoolNextArgs b{};
     b.in[0] = lv[2][l - 2];
     b.out[0] = lv[2][l - 1];
-    const long total = (long)s.bh * s.n_level(l) * kDim;
-    LLSA_LAUNCH("pool_next_kernel", pool_next_v_kernel, dim3((unsigned)((total + 255) / 256)),
-                dim3(256), 0, stream, b, total);
+    const long total = (long)s.bh * s.n_level(l) * s.d;
+    const dim3 g((unsigned)((total + 255) / 256));
+    if (s.d == 64)
+      LLSA_LAUNCH("pool_next_kernel", pool_next_v_kernel<64>, g, dim3(256), 0, stream, b, total);
+    else
+      LLSA_LAUNCH("pool_next_kernel", pool_next_v_kernel<128>, g, dim3(256), 0, stream, b, total);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

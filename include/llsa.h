@@ -27,11 +27,11 @@
  *    leave outputs untouched; LLSA_ERR_HIP means a launch failed (outputs undefined).
  *    llsa_last_error() gives a message for the last failure on the calling thread.
  *  - Results are deterministic: no atomics, fixed reduction orders.
- *  - Supported: head_dim 64, block 16 (4x4 pixel tiles) or 64 (8x8 pixel tiles), height and
- *    width powers of two >= 4, 256 <= N <= 2^23, N % block^levels == 0,
+ *  - Supported: head_dim 64 or 128, block 16 (4x4 pixel tiles) or 64 (8x8 pixel tiles),
+ *    height and width powers of two >= 4, 256 <= N <= 2^23, N % block^levels == 0,
  *    1 <= topk <= min(32, N / block^levels) and topk * block / 16 <= 32,
  *    1 <= levels <= 6, batch*heads*N < 2^31.  dtype bf16 for every call; f32 for
- *    reorder/pool/select/attn_fwd.
+ *    reorder/pool/select, and for attn_fwd with head_dim 64.
  */
 #ifndef LLSA_H
 #define LLSA_H
@@ -52,7 +52,7 @@ typedef enum {
   LLSA_ERR_NULL = 1,        /* a required pointer is NULL */
   LLSA_ERR_SHAPE = 2,       /* sizes violate the constraints above */
   LLSA_ERR_DTYPE = 3,       /* unknown dtype or layout code */
-  LLSA_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. head_dim != 64) */
+  LLSA_ERR_UNSUPPORTED = 4, /* valid but not implemented (e.g. head_dim 96) */
   LLSA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
   LLSA_ERR_ALIGN = 6,       /* a pointer is not 16-byte aligned */
   LLSA_ERR_HIP = 7          /* a HIP launch failed */
@@ -66,7 +66,7 @@ typedef struct {
   int32_t heads;
   int32_t height;   /* pixel rows    (power of two) */
   int32_t width;    /* pixel columns (power of two) */
-  int32_t head_dim; /* 64 */
+  int32_t head_dim; /* 64 or 128 */
   int32_t block;    /* B: tokens per pooled token; 16 = a 4x4 tile, 64 = an 8x8 tile */
   int32_t levels;   /* L: pooled levels 1..L; the coarsest has N / B^L tokens */
   int32_t topk;     /* K: keys kept per query at every level */
@@ -161,8 +161,10 @@ int32_t llsa_expand_blocks(const llsa_problem* p, const int32_t* sel1, int32_t* 
  * block p (B queries) attends to the B tokens of each block in sel[0][p] and, if enrich,
  * for l = 2..L to the pooled keys/values k_lv/v_lv[l-1][sel[l-1][p / B^(l-1)]] with weight
  * B^l (their exp(score) is multiplied by B^l).  s = scale * q.k; o = sum w e^s v / sum w e^s;
- * lse = log sum w e^s.  bf16: MFMA with fp32 accumulation and softmax (pooled keys/values are
- * rounded to bf16 for the MFMA); f32: fp32 MFMA.  k_lv/v_lv: L pointers, levels >= 2 read.
+ * lse = log sum w e^s.  bf16: MFMA with fp32 accumulation and softmax (the fp32 pooled keys and
+ * values enter the MFMA as bf16 hi + lo parts, about 16 mantissa bits; P is rounded once to
+ * bf16 for P V); f32 (head_dim 64 only, else LLSA_ERR_UNSUPPORTED): fp32 MFMA.  k_lv/v_lv: L
+ * pointers, levels >= 2 read.
  * Out-of-range indices in sel are skipped.  o: token tensor (layout), lse: [b, H, N] Morton.
  * sel[0] lists level-1 picks as 16-token blocks: [b, H, N/16, topk * block / 16]; with block
  * 16 that is Sel_1 itself, with block 64 the output of llsa_expand_blocks.  sel[l-1], l >= 2:
@@ -270,8 +272,8 @@ int32_t llsa_dense_attn_bwd(int32_t batch_heads, int32_t n, int32_t head_dim, fl
  * block by scanning its column of the mask instead of reading CSC_1 (no chunking); the
  * results are bit-identical to llsa_attn_bwd's when no key block is picked by more than 128
  * query blocks, and otherwise differ only in the fp32 order of dK/dV sums.  Arguments as for llsa_attn_bwd; ws: llsa_workspace_bytes
- * (bwd) bytes.  Both: bf16 only; LLSA_ERR_UNSUPPORTED if levels > 1 and enrich, LLSA_ERR_SHAPE
- * if the mask would exceed 2^34 bytes.  Errors otherwise as for the calls above.
+ * (bwd) bytes.  Both: bf16 and head_dim 64 only; LLSA_ERR_UNSUPPORTED if levels > 1 and
+ * enrich, LLSA_ERR_SHAPE if the mask would exceed 2^34 bytes.  Errors otherwise as for the calls above.
  */
 int32_t llsa_block_mask(const llsa_problem* p, const int32_t* sel1, uint8_t* mask,
                         void* stream);

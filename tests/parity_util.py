@@ -108,7 +108,7 @@ def assert_close(x, ref: np.ndarray, dtype: torch.dtype, name: str, tol_abs: flo
 
 
 def lse_tolerance(q_ref: np.ndarray, k_ref: np.ndarray, dtype: torch.dtype, levels: int = 0,
-                  head_dim: int = 64) -> float:
+                  head_dim: int = 64, block: int = 16) -> float:
     """Max-abs bound of the fp32 log-sum-exp (levels: the pooled levels whose keys enrich the
     attention come from, 0 without coarse keys).
 
@@ -116,11 +116,11 @@ def lse_tolerance(q_ref: np.ndarray, k_ref: np.ndarray, dtype: torch.dtype, leve
     largest error of one of its scores (it is a smooth maximum of them).  A score
     scale * sum_c q_c k_c is computed from exact bf16 q and k (their products are exact in
     fp32) and accumulated in fp32 over head_dim products (error <= head_dim 2^-24
-    sum_c |q_c k_c|).  A coarse key is an fp32 mean whose sums add at most 15 rounding errors
-    per level (<= 15 L 2^-24 of the largest |k|), entering the MFMA as bf16 hi + lo parts
-    (relative error <= 2^-18 per element, taken as 2^-17).  So |error| <= scale ||q||_1 max|k|
-    (head_dim 2^-24 [+ 2^-17 + 15 L 2^-24]), plus 1e-5 for the fp32 exponentials and
-    logarithm."""
+    sum_c |q_c k_c|).  A coarse key is an fp32 mean whose sums add at most B - 1 rounding
+    errors per level (<= (B - 1) L 2^-24 of the largest |k|), entering the MFMA as bf16 hi + lo
+    parts (relative error <= 2^-18 per element, taken as 2^-17).  So |error| <= scale ||q||_1
+    max|k| (head_dim 2^-24 [+ 2^-17 + (B - 1) L 2^-24]), plus 1e-5 for the fp32 exponentials
+    and logarithm."""
     if dtype != torch.bfloat16:
         return 1e-4
     scale = 1.0 / np.sqrt(head_dim)
@@ -128,7 +128,7 @@ def lse_tolerance(q_ref: np.ndarray, k_ref: np.ndarray, dtype: torch.dtype, leve
     kmax = np.abs(k_ref).max()
     rel = head_dim * 2.0 ** -24
     if levels >= 2:
-        rel += 2.0 ** -17 + 15 * levels * 2.0 ** -24
+        rel += 2.0 ** -17 + (block - 1) * levels * 2.0 ** -24
     return float(1e-5 + scale * q1 * kmax * rel)
 
 

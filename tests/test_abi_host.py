@@ -64,7 +64,10 @@ def _p(**kw):
     (dict(enrich_levels=5, coarse_unit_weight=1), 0),   # clamped to the L - 1 coarse levels
     (dict(coarse_exclude_overlap=2), 2),
     (dict(coarse_exclude_overlap=1), 0),
-    (dict(head_dim=128), 4),
+    (dict(head_dim=128), 0),
+    (dict(head_dim=128, dtype=abi.LLSA_BF16, height=256, width=256, levels=3), 0),
+    (dict(head_dim=96), 4),
+    (dict(head_dim=32), 4),
     (dict(block=256), 4),                   # a power of 4 but not implemented
     (dict(block=64, levels=1), 0),          # 8x8 tiles: 64 blocks of 64 tokens, K = 8
     (dict(block=64, levels=2), 2),          # N / 64^2 = 1 < K
@@ -252,7 +255,7 @@ def test_check_never_accepts_what_the_kernels_cannot_run(L, batch, heads, height
         assert abi.llsa_last_error()
         return
     n = height * width
-    assert batch >= 1 and heads >= 1 and head_dim == 64 and block in (16, 64)
+    assert batch >= 1 and heads >= 1 and head_dim in (64, 128) and block in (16, 64)
     assert 256 <= n <= 1 << 23 and batch * heads * n < 1 << 31
     assert n % block ** levels == 0 and 1 <= topk <= min(32, n // block ** levels)
     assert topk * block // 16 <= 32
@@ -286,3 +289,20 @@ def test_check_and_workspace_on_nearly_valid_problems(L, batch, heads, height, w
     if ok:
         f, b = abi.llsa_workspace_bytes(p)
         assert f == 0 and b >= 4 * batch * heads * n
+
+
+def test_head128_limits(L):
+    """128-channel heads: the attention runs in bf16 only, the mask-based comparator has 64
+    channels only (both refused before anything is enqueued)."""
+    f = ctypes.c_void_p(FAKE)
+    lv = (ctypes.c_void_p * 6)(FAKE, FAKE)
+    f32 = _p(head_dim=128, dtype=abi.LLSA_F32)
+    assert abi.llsa_check(f32) == 0
+    assert L.llsa_attn_fwd(ctypes.byref(f32.c()), f, f, f, lv, lv, lv, f, f, None) == 4
+    assert b"bf16" in L.llsa_last_error()
+    m = _p(head_dim=128, height=128, width=128, levels=1, topk=32, dtype=abi.LLSA_BF16)
+    assert L.llsa_block_mask(ctypes.byref(m.c()), f, f, None) == 4
+    # the backward workspace grows with the head width
+    p64 = _p(height=256, width=256, levels=3, dtype=abi.LLSA_BF16)
+    p128 = _p(height=256, width=256, levels=3, dtype=abi.LLSA_BF16, head_dim=128)
+    assert abi.llsa_workspace_bytes(p128)[1] > abi.llsa_workspace_bytes(p64)[1]
