@@ -20,7 +20,7 @@ _lib = None
 LLSA_F32, LLSA_BF16 = 0, 1
 LLSA_LAYOUT_MORTON, LLSA_LAYOUT_RASTER = 0, 1
 LLSA_MAX_LEVELS = 6
-LLSA_ABI_VERSION = 4   # the llsa_problem layout and entry points this binding marshals
+LLSA_ABI_VERSION = 5   # the llsa_problem layout and entry points this binding marshals
 
 
 class LlsaError(RuntimeError):
@@ -120,6 +120,8 @@ def lib() -> ctypes.CDLL:
             "llsa_attn_fwd": ([P, vp, vp, vp, pp, pp, pp, vp, vp, vp], i32),
             "llsa_index_transpose_workspace": ([i32, i32, i32, i32, ctypes.POINTER(sz)], i32),
             "llsa_index_transpose": ([i32, i32, i32, i32, vp, vp, vp, vp, sz, vp], i32),
+            "llsa_index_transpose_levels_workspace": ([P, ctypes.POINTER(sz)], i32),
+            "llsa_index_transpose_levels": ([P, pp, pp, pp, vp, sz, vp], i32),
             "llsa_attn_bwd": ([P, vp, vp, vp, vp, vp, pp, pp, pp, pp, pp, vp, vp, vp, vp, sz,
                                vp], i32),
             "llsa_dense_attn_fwd": ([i32, i32, i32, ctypes.c_float, vp, vp, vp, vp, vp, vp],
@@ -152,7 +154,8 @@ def exported_symbols() -> list:
             "llsa_index_transpose_workspace", "llsa_index_transpose", "llsa_attn_bwd",
             "llsa_dense_attn_fwd", "llsa_dense_attn_bwd", "llsa_block_mask", "llsa_expand_blocks",
             "llsa_attn_bwd_masked", "llsa_calib_copy", "llsa_calib_mfma", "llsa_profile_enable",
-            "llsa_profile_read", "llsa_attn_bwd_noalloc"]
+            "llsa_profile_read", "llsa_attn_bwd_noalloc", "llsa_index_transpose_levels",
+            "llsa_index_transpose_levels_workspace"]
 
 
 def _raise(status: int, name: str):
@@ -326,6 +329,28 @@ def llsa_index_transpose(nmat, rows, cols, k, csr, csc_off, csc_rows, ws, stream
     _raise(lib().llsa_index_transpose(nmat, rows, cols, k, _ptr(csr), _ptr(csc_off),
                                       _ptr(csc_rows), _ptr(ws), ws.numel() * ws.element_size(),
                                       _stream(stream)), "llsa_index_transpose")
+
+
+def llsa_index_transpose_levels_workspace(p: Problem) -> int:
+    b = ctypes.c_size_t()
+    _raise(lib().llsa_index_transpose_levels_workspace(ctypes.byref(p.c()), ctypes.byref(b)),
+           "llsa_index_transpose_levels_workspace")
+    return b.value
+
+
+def llsa_index_transpose_levels(p: Problem, sel, csc_off, csc_rows, ws, stream=None):
+    """CSR -> CSC of every level the backward reads (sel[0]: level 1 as 16-token blocks)."""
+    for l in range(1, 2 + p.coarse_levels):
+        rows, kk = p.csc_dims(l)
+        _expect(sel[l - 1], _fine_sel_shape(p) if l == 1 else _sel_shape(p, l), torch.int32,
+                f"sel[{l - 1}]")
+        _expect(csc_off[l - 1], (p.batch, p.heads, rows + 1), torch.int32, f"csc_off[{l - 1}]")
+        _expect(csc_rows[l - 1], (p.batch, p.heads, rows * kk), torch.int32,
+                f"csc_rows[{l - 1}]")
+    _raise(lib().llsa_index_transpose_levels(ctypes.byref(p.c()), _ptrs(sel), _ptrs(csc_off),
+                                             _ptrs(csc_rows), _ptr(ws),
+                                             ws.numel() * ws.element_size(), _stream(stream)),
+           "llsa_index_transpose_levels")
 
 
 def _check_bwd_args(p: Problem, q, k, v, dout, lse, k_lv, v_lv, sel, csc_off, csc_rows, dq, dk,

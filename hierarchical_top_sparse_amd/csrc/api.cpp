@@ -295,7 +295,7 @@ int32_t llsa_index_transpose_workspace(int32_t nmat, int32_t rows, int32_t cols,
   if ((long)nmat * rows * k >= (1L << 31))
     return fail(LLSA_ERR_SHAPE, "nmat*rows*k must be < 2^31");
   const int rbits = log2i(rows);
-  if (((unsigned long)cols + 1) << rbits > (1UL << 32))
+  if (!llsa::transpose_uses_radix(rows, k) && (((unsigned long)cols + 1) << rbits > (1UL << 32)))
     return fail(LLSA_ERR_SHAPE, "(cols+1) * 2^ceil(log2 rows) exceeds 2^32");
   *bytes = llsa::transpose_workspace_bytes(nmat, rows, cols, k);
   return LLSA_OK;
@@ -310,12 +310,70 @@ int32_t llsa_index_transpose(int32_t nmat, int32_t rows, int32_t cols, int32_t k
   CHECK_PTR(csr, "csr");
   CHECK_PTR(csc_off, "csc_off");
   CHECK_PTR(csc_rows, "csc_rows");
-  if (!ws || ws_bytes < need)
+  if (need > 0 && (!ws || ws_bytes < need))
     return fail(LLSA_ERR_WORKSPACE, "workspace of %zu bytes needed (%zu given)", need, ws_bytes);
-  CHECK_PTR(ws, "ws");
+  if (ws) CHECK_PTR(ws, "ws");
   return hip_status(llsa::launch_index_transpose(nmat, rows, cols, k, csr, csc_off, csc_rows, ws,
                                                  (hipStream_t)stream),
                     "llsa_index_transpose");
+}
+
+}  // extern "C"
+
+namespace {
+
+// The transposes the backward reads: level 1 as 16-token blocks (rows = cols = N/16, k = K B /
+// 16), levels 2 .. 1 + coarse levels as selected (rows = cols = n_l, k = K).
+int transpose_levels(const llsa_problem* p, int* nmat, int* rows, int* cols, int* k) {
+  const int nlev = 1 + coarse_levels(p);
+  const int n = p->height * p->width;
+  for (int l = 1; l <= nlev; ++l) {
+    nmat[l - 1] = p->batch * p->heads;
+    rows[l - 1] = cols[l - 1] = l == 1 ? n / 16 : n >> (log2i(p->block) * l);
+    k[l - 1] = l == 1 ? p->topk * (p->block / 16) : p->topk;
+  }
+  return nlev;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t llsa_index_transpose_levels_workspace(const llsa_problem* p, size_t* bytes) {
+  int32_t st = check_problem(p);
+  if (st != LLSA_OK) return st;
+  if (!bytes) return fail(LLSA_ERR_NULL, "bytes is NULL");
+  int nmat[LLSA_MAX_LEVELS], rows[LLSA_MAX_LEVELS], cols[LLSA_MAX_LEVELS], k[LLSA_MAX_LEVELS];
+  const int nlev = transpose_levels(p, nmat, rows, cols, k);
+  for (int l = 0; l < nlev; ++l) {
+    size_t b = 0;
+    st = llsa_index_transpose_workspace(nmat[l], rows[l], cols[l], k[l], &b);
+    if (st != LLSA_OK) return st;
+  }
+  *bytes = llsa::transpose_sets_workspace_bytes(nlev, nmat, rows, cols, k);
+  return LLSA_OK;
+}
+
+int32_t llsa_index_transpose_levels(const llsa_problem* p, const int32_t* const* sel,
+                                    int32_t* const* csc_off, int32_t* const* csc_rows, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  int32_t st = llsa_index_transpose_levels_workspace(p, &need);
+  if (st != LLSA_OK) return st;
+  if (!sel || !csc_off || !csc_rows) return fail(LLSA_ERR_NULL, "index arrays are NULL");
+  int nmat[LLSA_MAX_LEVELS], rows[LLSA_MAX_LEVELS], cols[LLSA_MAX_LEVELS], k[LLSA_MAX_LEVELS];
+  const int nlev = transpose_levels(p, nmat, rows, cols, k);
+  for (int l = 0; l < nlev; ++l) {
+    CHECK_PTR(sel[l], "selection");
+    CHECK_PTR(csc_off[l], "csc_off");
+    CHECK_PTR(csc_rows[l], "csc_rows");
+  }
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(LLSA_ERR_WORKSPACE, "workspace of %zu bytes needed (%zu given)", need, ws_bytes);
+  if (ws) CHECK_PTR(ws, "ws");
+  return hip_status(llsa::launch_transpose_sets(nlev, nmat, rows, cols, k, sel, csc_off, csc_rows,
+                                                ws, (hipStream_t)stream),
+                    "llsa_index_transpose_levels");
 }
 
 }  // extern "C"

@@ -56,6 +56,16 @@ hipError_t launch_attn_fwd(const Shape& s, const void* q, const void* k, const v
                            const int32_t* const* sel, void* o, float* lse, hipStream_t stream);
 
 size_t transpose_workspace_bytes(int nmat, int rows, int cols, int k);
+// true if a matrix of rows x k entries takes the radix path (at most 64 tiles of 4096), which
+// has no limit on (cols + 1) * 2^ceil(log2 rows)
+bool transpose_uses_radix(int rows, int k);
+// Up to 8 matrix sets (nmat[i] matrices of rows[i] x k[i] -> cols[i]) in order on one stream,
+// sharing one workspace.
+size_t transpose_sets_workspace_bytes(int nsets, const int* nmat, const int* rows,
+                                      const int* cols, const int* k);
+hipError_t launch_transpose_sets(int nsets, const int* nmat, const int* rows, const int* cols,
+                                 const int* k, const int32_t* const* csr, int32_t* const* off,
+                                 int32_t* const* rows_out, void* ws, hipStream_t stream);
 hipError_t launch_index_transpose(int nmat, int rows, int cols, int k, const int32_t* csr,
                                   int32_t* off, int32_t* rows_out, void* ws,
                                   hipStream_t stream);

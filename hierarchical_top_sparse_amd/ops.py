@@ -1,7 +1,7 @@
 """LLSA as a PyTorch op: the whole hot path through the C ABI.
 
 forward : [reorder] -> pool -> select -> sparse attention (-> inverse reorder)
-backward: CSR->CSC transpose per level -> sparse backward
+backward: CSR->CSC transpose of every level (one call) -> sparse backward
 
 With layout RASTER (the default) the reorder is folded into the kernels' addressing: the
 inputs are raster-ordered pixel tokens and so are the outputs.  With layout MORTON the caller
@@ -16,7 +16,8 @@ from . import _abi
 from ._abi import (LLSA_BF16, LLSA_F32, LLSA_LAYOUT_MORTON, LLSA_LAYOUT_RASTER, Problem,
                    llsa_attn_bwd, llsa_attn_bwd_masked, llsa_attn_fwd, llsa_block_mask,
                    llsa_expand_blocks,
-                   llsa_index_transpose, llsa_index_transpose_workspace, llsa_pool_select,
+                   llsa_index_transpose_levels, llsa_index_transpose_levels_workspace,
+                   llsa_pool_select,
                    llsa_reorder, llsa_workspace_bytes)
 
 __all__ = ["Problem", "make_problem", "llsa_forward", "llsa_backward", "llsa_backward_masked",
@@ -77,20 +78,16 @@ def llsa_forward(p: Problem, q, k, v):
 
 def build_csc(p: Problem, sel):
     """Per level l: CSC of the attention's selection (level 1 as 16-token blocks, sel[0] =
-    the `fine` array; rows = queries, cols = keys): (off, rows)."""
+    the `fine` array; rows = queries, cols = keys): (off, rows), all levels in one call."""
     levels = 1 + p.coarse_levels
+    dev = sel[0].device
     offs, rows = [], []
-    nmat = p.batch * p.heads
-    dims = [p.csc_dims(l) for l in range(1, levels + 1)]
-    ws_bytes = max(llsa_index_transpose_workspace(nmat, nl, nl, kk) for nl, kk in dims)
-    ws = torch.empty(ws_bytes, device=sel[0].device, dtype=torch.uint8)
     for l in range(1, levels + 1):
         nl, kk = p.csc_dims(l)
-        off = torch.empty((p.batch, p.heads, nl + 1), device=ws.device, dtype=torch.int32)
-        r = torch.empty((p.batch, p.heads, nl * kk), device=ws.device, dtype=torch.int32)
-        llsa_index_transpose(nmat, nl, nl, kk, sel[l - 1], off, r, ws)
-        offs.append(off)
-        rows.append(r)
+        offs.append(torch.empty((p.batch, p.heads, nl + 1), device=dev, dtype=torch.int32))
+        rows.append(torch.empty((p.batch, p.heads, nl * kk), device=dev, dtype=torch.int32))
+    ws = torch.empty(llsa_index_transpose_levels_workspace(p), device=dev, dtype=torch.uint8)
+    llsa_index_transpose_levels(p, sel, offs, rows, ws)
     return offs, rows
 
 

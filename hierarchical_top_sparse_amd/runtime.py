@@ -7,10 +7,11 @@ ROCm) so that replays do not wait on the host between calls; the library allocat
 and never synchronises, and none of its calls records a memset, so the whole step can be
 captured.
 
-The CSR->CSC transposes depend only on the selection, and the sparse forward does not read
-them: `run(overlap=True)` (the default) issues them on a second stream, forked after the
-selection and joined before the backward, so that these small, latency-bound kernels run
-beside the HBM-bound forward instead of after it.  All streams have the default priority.
+The CSR->CSC transposes (every level in one call) depend only on the selection, and the sparse
+forward does not read them: `run(overlap=True)` (the default) issues them on a second stream,
+forked after the selection and joined before the backward, so that these small, latency-bound
+kernels run beside the HBM-bound forward instead of after it.  All streams have the default
+priority.
 """
 from __future__ import annotations
 
@@ -54,9 +55,8 @@ class Step:
         self.rows = [torch.empty((p.batch, p.heads, nl * kk), device=dev, dtype=torch.int32)
                      for nl, kk in dims]
         self.nmat = p.batch * p.heads
-        tws = max([_abi.llsa_index_transpose_workspace(self.nmat, nl, nl, kk)
-                   for nl, kk in dims] + [16])
-        self.tws = torch.empty(tws, device=dev, dtype=torch.uint8)
+        tws = _abi.llsa_index_transpose_levels_workspace(p) if self.backward else 0
+        self.tws = torch.empty(max(tws, 16), device=dev, dtype=torch.uint8)
         _, bws = _abi.llsa_workspace_bytes(p) if self.backward else (0, 0)
         self.bws = torch.empty(max(bws, 16), device=dev, dtype=torch.uint8)
         self.dq, self.dk, self.dv = ((torch.empty_like(q) for _ in range(3)) if self.backward
@@ -65,14 +65,10 @@ class Step:
         self.side = torch.cuda.Stream(device=dev)
 
     def _transpose_calls(self):
-        a, p = _abi, self.p
-        out = []
-        for l in range(1, self.csc_levels + 1):
-            nl, kk = p.csc_dims(l)
-            out.append((f"transpose_l{l}", (lambda l=l, nl=nl, kk=kk: a.llsa_index_transpose(
-                self.nmat, nl, nl, kk, self.att_sel[l - 1], self.off[l - 1], self.rows[l - 1],
-                self.tws))))
-        return out
+        if not self.csc_levels:
+            return []
+        return [("transpose", lambda: _abi.llsa_index_transpose_levels(
+            self.p, self.att_sel, self.off, self.rows, self.tws))]
 
     def calls(self):
         """(name, thunk) for every C-ABI call of one step, in order (one stream)."""

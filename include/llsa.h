@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define LLSA_ABI_VERSION 4
+#define LLSA_ABI_VERSION 5
 #define LLSA_MAX_LEVELS 6
 #define LLSA_MAX_TOPK 32
 
@@ -181,15 +181,31 @@ int32_t llsa_attn_fwd(const llsa_problem* p, const void* q, const void* k, const
  * csc_off: [nmat, cols + 1]; csc_rows: [nmat, rows * k]: the rows that selected column c are
  * csc_rows[off[c] .. off[c+1]) in ascending order.  Entries outside [0, cols) are dropped
  * (off[cols] counts the kept ones; later csc_rows entries are unspecified).
- * Atomic-free (sort of (column, row) codes), so the output is deterministic.
- * ws: device workspace of llsa_index_transpose_workspace() bytes.
- * Requires (cols + 1) * 2^ceil(log2 rows) <= 2^32.
+ * Atomic-free (a stable sort by column), so the output is deterministic.
+ * ws: device workspace of llsa_index_transpose_workspace() bytes (may be 0 for a matrix of at
+ * most 4096 entries: ws may then be NULL).  Matrices of more than 64 tiles of 4096 entries
+ * require (cols + 1) * 2^ceil(log2 rows) <= 2^32.
  */
 int32_t llsa_index_transpose_workspace(int32_t nmat, int32_t rows, int32_t cols, int32_t k,
                                        size_t* bytes);
 int32_t llsa_index_transpose(int32_t nmat, int32_t rows, int32_t cols, int32_t k,
                              const int32_t* csr, int32_t* csc_off, int32_t* csc_rows,
                              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * llsa_index_transpose_levels — llsa_index_transpose of every level the backward reads, as one
+ * call (summary sec. 4.1; article sec. 四): level 1 as 16-token blocks (sel[0] as for
+ * llsa_attn_fwd; rows = cols = N/16, k = topk * block / 16) and, with enrichment, levels
+ * 2 .. 1 + coarse levels (rows = cols = n_l, k = topk).  csc_off[l-1]: [batch, heads, rows + 1],
+ * csc_rows[l-1]: [batch, heads, rows * k], exactly as llsa_index_transpose of that level writes
+ * them.  Levels of at most 64 tiles of 4096 entries run together in two launches.  ws: device
+ * workspace of llsa_index_transpose_levels_workspace() bytes (may be 0: ws may then be NULL).
+ * Atomic-free, deterministic.  Errors as for llsa_index_transpose.
+ */
+int32_t llsa_index_transpose_levels_workspace(const llsa_problem* p, size_t* bytes);
+int32_t llsa_index_transpose_levels(const llsa_problem* p, const int32_t* const* sel,
+                                    int32_t* const* csc_off, int32_t* const* csc_rows, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /*
  * llsa_attn_bwd — sparse backward (summary sec. 4.1 and Figure 4: query-major dQ, key-major

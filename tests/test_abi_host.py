@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_version_and_status_strings(L):
-    assert L.llsa_abi_version() == abi.LLSA_ABI_VERSION == 4
+    assert L.llsa_abi_version() == abi.LLSA_ABI_VERSION == 5
     for code in range(8):
         assert L.llsa_status_str(code)
     assert L.llsa_status_str(99) == b"unknown status"
@@ -111,18 +111,37 @@ def test_entry_points_reject_null_and_misaligned(L):
 def test_workspace_queries(L):
     f, b = abi.llsa_workspace_bytes(_p(dtype=abi.LLSA_BF16))
     assert f == 0 and b > 0
-    # two code buffers + per-run column bounds (cols + 1) and run starts (cols): 8 runs of 4096
     a256 = lambda x: (x + 255) // 256 * 256
+    # up to 64 tiles of 4096 entries (the radix path): each tile's sorted rows and its column
+    # bounds (cols + 1); one tile needs none
     assert abi.llsa_index_transpose_workspace(6, 4096, 4096, 8) == (
-        2 * a256(4 * 6 * 4096 * 8) + a256(4 * 6 * 8 * 4097) + a256(4 * 6 * 8 * 4096))
+        a256(4 * 6 * 8 * 4096) + a256(4 * 6 * 8 * 4097))
+    assert abi.llsa_index_transpose_workspace(3, 256, 256, 8) == 0
+    # more tiles (the bitonic path): two code buffers + per-run column bounds (cols + 1) and
+    # run starts (cols): 80 tiles of 4096 merge into 20 runs of 16384 (at most 32 runs)
+    assert abi.llsa_index_transpose_workspace(1, 40960, 500, 8) == (
+        2 * a256(4 * 40960 * 8) + a256(4 * 20 * 501) + a256(4 * 20 * 500))
     out = ctypes.c_size_t()
     assert L.llsa_index_transpose_workspace(1, 0, 4, 8, ctypes.byref(out)) == 2
+    # the bitonic path's 32-bit codes: (cols + 1) * 2^ceil(log2 rows) <= 2^32
     assert L.llsa_index_transpose_workspace(1, 1 << 20, 1 << 13, 8, ctypes.byref(out)) == 2
-    # workspace too small / missing
+    # the radix path has no such limit
+    assert L.llsa_index_transpose_workspace(1, 1 << 15, 1 << 18, 8, ctypes.byref(out)) == 0
+    # workspace too small / missing (two tiles need one), NULL pointers
     fake = ctypes.c_void_p(FAKE)
-    assert L.llsa_index_transpose(1, 16, 16, 8, fake, fake, fake, None, 0, None) == 5
-    assert L.llsa_index_transpose(1, 16, 16, 8, fake, fake, fake, fake, 8, None) == 5
+    assert L.llsa_index_transpose(1, 1024, 16, 8, fake, fake, fake, None, 0, None) == 5
+    assert L.llsa_index_transpose(1, 1024, 16, 8, fake, fake, fake, fake, 8, None) == 5
     assert L.llsa_index_transpose(1, 16, 16, 8, None, fake, fake, fake, 4096, None) == 1
+    # every level at once: the sum of the radix levels' needs, NULL pointers refused
+    p = _p(height=256, width=256, levels=3, dtype=abi.LLSA_BF16)
+    assert abi.llsa_index_transpose_levels_workspace(p) == (
+        a256(4 * 2 * 8 * 4096) + a256(4 * 2 * 8 * 4097))
+    lv = (ctypes.c_void_p * 6)(FAKE, FAKE, None)
+    full = (ctypes.c_void_p * 6)(FAKE, FAKE, FAKE)
+    assert L.llsa_index_transpose_levels(ctypes.byref(p.c()), full, full, lv, fake, 1 << 30,
+                                         None) == 1
+    assert L.llsa_index_transpose_levels(ctypes.byref(p.c()), full, full, full, None, 0,
+                                         None) == 5
 
 
 def test_backward_rejects_too_many_coarse_keys(L):

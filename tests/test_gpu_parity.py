@@ -562,3 +562,35 @@ def test_maximum_size_backward_sampled():
                                ("dv", dv, gv, krows)):
         assert_close(got[0, 0].double().cpu().numpy()[r], want[r], torch.bfloat16,
                      f"{name} (sampled)")
+
+
+@pytest.mark.parametrize("h,w,levels,topk,block,enrich", [
+    (256, 256, 3, 8, 16, True),     # level 1: 8 tiles per head; levels 2, 3: one tile each
+    (512, 512, 3, 8, 16, True),     # level 1: 32 tiles per head; level 2: 2 tiles
+    (256, 256, 2, 8, 64, True),     # 16-token blocks from 64-token picks (32 picks per row)
+    (128, 128, 1, 32, 16, False),   # the single-level comparator's index
+    (1024, 512, 3, 8, 16, False),   # level 1: 256 tiles per head (the bitonic path)
+])
+def test_index_transpose_levels_bit_exact(h, w, levels, topk, block, enrich):
+    """Every level's CSC in one call equals the oracle's CSC of that level's selection
+    (counts, offsets, rows ascending per key), as the per-level call computes it."""
+    d, _ = _inputs(1, 3, h, w, torch.bfloat16, 81)
+    p = ops.make_problem(d["q"], h, w, levels, topk, enrich, 0.0, RASTER, block=block)
+    fwd = ops.llsa_forward(p, d["q"], d["k"], d["v"])
+    sel = [fwd["fine"]] + list(fwd["sel"][1:])
+    offs, rows = ops.build_csc(p, sel)
+    torch.cuda.synchronize()
+    for l in range(1, 2 + p.coarse_levels):
+        nl, kk = p.csc_dims(l)
+        s_np = sel[l - 1].cpu().numpy()
+        o_np, r_np = offs[l - 1].cpu().numpy(), rows[l - 1].cpu().numpy()
+        for hi in range(3):
+            want_off, want_rows = orc.csr_to_csc(s_np[0, hi].astype(np.int64), nl)
+            assert np.array_equal(o_np[0, hi], want_off), (l, hi)
+            assert np.array_equal(r_np[0, hi], want_rows), (l, hi)
+        one_off = torch.empty_like(offs[l - 1])
+        one_rows = torch.empty_like(rows[l - 1])
+        ws = torch.empty(_abi.llsa_index_transpose_workspace(3, nl, nl, kk), device=DEV,
+                         dtype=torch.uint8)
+        _abi.llsa_index_transpose(3, nl, nl, kk, sel[l - 1], one_off, one_rows, ws)
+        assert torch.equal(one_off, offs[l - 1]) and torch.equal(one_rows, rows[l - 1])

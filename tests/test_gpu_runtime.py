@@ -67,8 +67,8 @@ def test_profile_hook_reports_every_kernel(fuse_prologue, select_name):
     step.run()
     _abi.llsa_profile_enable(False)
     prof = _abi.llsa_profile_read()
-    for name in ("pool12_kernel", select_name, "attn_fwd_kernel", "tile_sort_kernel",
-                 "csc_offsets_kernel", "csc_scatter_kernel", "bwd_query_kernel", "coarse_grad_kernel",
+    for name in ("pool12_kernel", select_name, "attn_fwd_kernel", "csc_radix_kernel",
+                 "csc_assemble_kernel", "bwd_query_kernel", "coarse_grad_kernel",
                  "bwd_key_kernel", "bwd_key_overflow_kernel"):
         assert name in prof, name
         cnt, ms = prof[name]
