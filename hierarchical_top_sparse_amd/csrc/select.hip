@@ -19,17 +19,21 @@
 // 16-row candidate tile, and channels g D/4 .. g D/4 + D/4 - 1 of the rows (D = head_dim, 64
 // or 128).  Tiles are loaded tiles_per_round(D) at a time, so a ranking costs one or two
 // memory round trips rather than one per tile.
-//  * A group (16 queries): each lane keeps a register top-KMAX list of its candidates, and the
-//    four lanes of a query merge their lists with cross-lane steps.
+//  * A group (16 queries): each lane keeps a register top-KMAX list of its candidates (a tile's
+//    four are sorted by a 5-comparator network and merged in by a bitonic top-KMAX merge), and
+//    the four lanes of a query exchange and merge their whole lists twice (v_permlane16_swap,
+//    v_permlane32_swap).
 //  * A single query is replicated over the 16 columns; each (tile, candidate) is then kept by
 //    exactly one lane (lane (n, g) takes candidate 4g + n % 4 of the tiles t with
-//    t % 4 = n / 4), and the 64 lists are merged across the whole wave.
+//    t % 4 = n / 4), and the 64 lists are merged across the whole wave (DPP, then the swaps).
 // llsa_pool_select issues the same launches with extra workgroups after the selection's that
 // pool V (select_pool12_kernel, select_pool_next_kernel): V is first read by the attention.
-// Lists only take strictly better scores: every lane sees its candidates in ascending id order
-// (picks are stored ascending), so ties keep the lower id; merges compare (score, id).  The K
-// picks are stored ascending.  The picks a ranking starts from are held one per lane (lane i:
-// pick i) and read with v_readlane.
+// The ranking is a strict total order: a higher score first and, between equal scores, the
+// lower id.  Candidates are held as 64-bit keys in that order (score bits made unsigned-order
+// above the complemented id), so every compare is one unsigned compare and the picks do not
+// depend on how the candidates are split among lanes or merged.  The K picks are stored
+// ascending.  The picks a ranking starts from are held one per lane (lane i: pick i) and read
+// with v_readlane.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "pool_impl.hpp"
@@ -53,42 +57,6 @@ struct SelArgs {
   int hi, lo;   // levels computed: hi down to lo
   int bshift;   // log2(B): 4 or 6; a pick's B children are B / 16 tiles of 16 candidates
 };
-
-__device__ __forceinline__ bool better(float s1, int i1, float s2, int i2) {
-  return s1 > s2 || (s1 == s2 && i1 < i2);
-}
-
-// Inserts a candidate whose id is larger than every id already in the list (scores
-// descending).  Lists of up to 8: c_j = s > ls[j] is monotone in j, so slot j keeps its entry
-// (c_j false), takes the candidate (c_j and not c_{j-1}) or its predecessor's entry (c_{j-1}):
-// all compares are independent, a chain of depth 3.  Longer lists: one compare-and-swap step
-// per slot (their 16 or 32 compare masks would not stay in scalar registers).
-template <int KMAX>
-__device__ __forceinline__ void list_insert(float (&ls)[KMAX], int (&li)[KMAX], float s, int id) {
-  if constexpr (KMAX > 8) {
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-      const bool b = s > ls[j];
-      const float ts = ls[j];
-      const int ti = li[j];
-      ls[j] = b ? s : ts;
-      li[j] = b ? id : ti;
-      s = b ? ts : s;
-      id = b ? ti : id;
-    }
-    return;
-  }
-  bool c[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) c[j] = s > ls[j];
-#pragma unroll
-  for (int j = KMAX - 1; j >= 1; --j) {
-    ls[j] = c[j] ? (c[j - 1] ? ls[j - 1] : s) : ls[j];
-    li[j] = c[j] ? (c[j - 1] ? li[j - 1] : id) : li[j];
-  }
-  ls[0] = c[0] ? s : ls[0];
-  li[0] = c[0] ? id : li[0];
-}
 
 // Candidate rows first + n (channels g D/4 .. g D/4 + D/4 - 1) of a 16-row tile; rows outside
 // [0, n_rows) and tiles with first < 0 read as zeros (their scores are never inserted).
@@ -120,39 +88,146 @@ __device__ __forceinline__ f32x4 score_tile(const f32x4 (&kv)[D / 16], const f32
   return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
-// Extracts the K best (score, id) of the lists of the lanes in one xor-group (the lanes
-// differing only in the bits of lane_bits), best first, into pick[0..K) of all those lanes
-// (kNoId beyond K), then sorts pick ascending.
-template <int KMAX, int LANE_BITS_LO, int LANE_BITS_HI>
-__device__ __forceinline__ void merge_lists(float (&ls)[KMAX], int (&li)[KMAX], int K,
-                                            int (&pick)[KMAX]) {
+// A candidate as one unsigned 64-bit key whose order is the ranking: the score's bits in an
+// order-preserving unsigned form (-0 taken as +0) above the complemented id, so that a larger
+// key is a larger score or, for equal scores, a lower id.  Every ordering below is on keys,
+// which makes the picks independent of how candidates are grouped and merged.
+using key64 = unsigned long long;
+// Empty list slot: upper half 1, below every candidate's key (a candidate's upper half is at
+// least 0x007fffff for any non-NaN score), decodes to kNoId.  A candidate a lane does not
+// take gets upper half 0, below every slot, and is never kept.
+constexpr key64 kPadKey = (1ull << 32) | 0x80000000ull;
+
+// s + 0 turns -0 into +0 (round to nearest), so both zeros map to the same key
+__device__ __forceinline__ unsigned key_hi(float s) {
+  const unsigned u = f_bits(s + 0.f);
+  return u ^ ((unsigned)((int)u >> 31) | 0x80000000u);
+}
+__device__ __forceinline__ key64 make_key(float s, int id, bool take) {
+  return ((key64)(take ? key_hi(s) : 0u) << 32) | (unsigned)~id;
+}
+__device__ __forceinline__ int key_id(key64 k) { return (int)~(unsigned)k; }
+__device__ __forceinline__ key64 key_max(key64 a, key64 b) { return b > a ? b : a; }
+// compare-exchange for a descending order: a takes the larger key, b the other one (x ^ y ^
+// max, so one compare serves both)
+__device__ __forceinline__ void ce_desc(key64& a, key64& b) {
+  const key64 x = a, y = b;
+  const key64 m = y > x ? y : x;
+  a = m;
+  // v_bitop3 with truth table 0x96: the three-input xor
+  const unsigned lo = __builtin_amdgcn_bitop3_b32((unsigned)x, (unsigned)y, (unsigned)m, 0x96);
+  const unsigned hi = __builtin_amdgcn_bitop3_b32((unsigned)(x >> 32), (unsigned)(y >> 32),
+                                                  (unsigned)(m >> 32), 0x96);
+  b = ((key64)hi << 32) | lo;
+}
+
+// Sorts a bitonic sequence of N keys into descending order (half-cleaners of strides N/2..1).
+template <int N>
+__device__ __forceinline__ void bitonic_merge_desc(key64 (&k)[N]) {
 #pragma unroll
-  for (int r = 0; r < KMAX; ++r) {
-    pick[r] = kNoId;
-    if (r < K) {
-      float bs = ls[0];
-      int bi = li[0];
+  for (int st = N / 2; st >= 1; st >>= 1)
 #pragma unroll
-      for (int mask = LANE_BITS_LO; mask <= LANE_BITS_HI; mask <<= 1) {
-        const float os = shfl_xor_f(bs, mask);
-        const int oi = shfl_xor_i(bi, mask);
-        if (better(os, oi, bs, bi)) {
-          bs = os;
-          bi = oi;
-        }
-      }
-      pick[r] = bi;
-      if (li[0] == bi) {   // pop the winner from its owner's list
+    for (int i = 0; i < N; ++i)
+      if ((i & st) == 0) ce_desc(k[i], k[i + st]);
+}
+
+// L (descending) := the N largest keys of L and b (descending, M <= N): with b padded to N
+// by the lowest key, max(L[i], b[N - 1 - i]) holds exactly those N keys as a bitonic
+// sequence, which the half-cleaners sort.
+template <int N, int M>
+__device__ __forceinline__ void merge_into(key64 (&L)[N], const key64 (&b)[M]) {
 #pragma unroll
-        for (int j = 0; j + 1 < KMAX; ++j) {
-          ls[j] = ls[j + 1];
-          li[j] = li[j + 1];
-        }
-        ls[KMAX - 1] = -INFINITY;
-        li[KMAX - 1] = kNoId;
-      }
-    }
+  for (int i = 0; i < M; ++i) L[N - 1 - i] = key_max(L[N - 1 - i], b[i]);
+  bitonic_merge_desc<N>(L);
+}
+
+// Inserts one key into L (descending).  Up to 8 slots: c_j = x > L[j] is monotone in j, so
+// slot j keeps its key, takes x or takes its predecessor's (independent compares, depth 3);
+// longer lists one compare-exchange step per slot (their masks would not stay in scalar
+// registers).
+template <int N>
+__device__ __forceinline__ void key_insert(key64 (&L)[N], key64 x) {
+  if constexpr (N > 8) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) ce_desc(L[j], x);
+    return;
   }
+  bool c[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) c[j] = x > L[j];
+#pragma unroll
+  for (int j = N - 1; j >= 1; --j) L[j] = c[j] ? (c[j - 1] ? L[j - 1] : x) : L[j];
+  L[0] = c[0] ? x : L[0];
+}
+
+// The four keys of a tile sorted descending (optimal 5-comparator network).
+__device__ __forceinline__ void sort4_desc(key64 (&k)[4]) {
+  ce_desc(k[0], k[1]);
+  ce_desc(k[2], k[3]);
+  ce_desc(k[0], k[2]);
+  ce_desc(k[1], k[3]);
+  ce_desc(k[1], k[2]);
+}
+
+// Cross-lane steps of the merges, all on the VALU.  Each replaces a lane's list by the top N
+// of its own and a partner lane's list, which both lanes then hold:
+//   1, 2: partner within the quad (DPP quad_perm swapping lanes 0-1/2-3, then 0-2/1-3);
+//   4: within 8 lanes (DPP row_half_mirror: lane i and 7 - i, one from each quad);
+//   8: within 16 lanes (DPP row_mirror: lane i and 15 - i, one from each half);
+//   16, 32: v_permlane16_swap (rows 0-1, 2-3) / v_permlane32_swap (halves of the wave), which
+//   return both lanes' values in the same order to both, so the two compute the same merge.
+// Keys are pairwise distinct (pads are equal and interchangeable), so the merged, sorted list
+// does not depend on which side a list came from.
+template <int STEP>
+__device__ __forceinline__ void both_sides(key64 x, key64& a, key64& b) {
+  const unsigned lo = (unsigned)x, hi = (unsigned)(x >> 32);
+  if constexpr (STEP <= 8) {
+    constexpr int ctrl = STEP == 1 ? 0xB1 : STEP == 2 ? 0x4E : STEP == 4 ? 0x141 : 0x140;
+    const unsigned plo = (unsigned)__builtin_amdgcn_update_dpp(0, (int)lo, ctrl, 0xF, 0xF, false);
+    const unsigned phi = (unsigned)__builtin_amdgcn_update_dpp(0, (int)hi, ctrl, 0xF, 0xF, false);
+    a = x;
+    b = ((key64)phi << 32) | plo;
+  } else {
+    const auto l2 = STEP == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                               : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+    const auto h2 = STEP == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                               : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+    a = ((key64)h2[0] << 32) | l2[0];
+    b = ((key64)h2[1] << 32) | l2[1];
+  }
+}
+
+template <int STEP, int N>
+__device__ __forceinline__ void merge_with_partner(key64 (&L)[N]) {
+  // max(a[i], b[N - 1 - i]) over the pair (i, N - 1 - i), so each list is read before written
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const int j = N - 1 - i;
+    key64 ai, bi, aj, bj;
+    both_sides<STEP>(L[i], ai, bi);
+    both_sides<STEP>(L[j], aj, bj);
+    L[i] = key_max(ai, bj);
+    L[j] = key_max(aj, bi);
+  }
+  bitonic_merge_desc<N>(L);
+}
+
+// The K best keys of the lists of the lanes in one group (all 64 lanes for LANE_BITS_LO = 1,
+// the 4 lanes n, n + 16, n + 32, n + 48 for LANE_BITS_LO = 16) as pick[0..K) (ids, kNoId
+// beyond K and for empty slots), sorted ascending.
+template <int KMAX, int LANE_BITS_LO, int LANE_BITS_HI>
+__device__ __forceinline__ void merge_lists(key64 (&L)[KMAX], int K, int (&pick)[KMAX]) {
+  static_assert(LANE_BITS_HI == 32 && (LANE_BITS_LO == 1 || LANE_BITS_LO == 16), "groups");
+  if constexpr (LANE_BITS_LO == 1) {
+    merge_with_partner<1>(L);
+    merge_with_partner<2>(L);
+    merge_with_partner<4>(L);
+    merge_with_partner<8>(L);
+  }
+  merge_with_partner<16>(L);
+  merge_with_partner<32>(L);
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) pick[r] = r < K ? key_id(L[r]) : kNoId;
 #pragma unroll
   for (int i = 0; i < KMAX; ++i)
 #pragma unroll
@@ -177,13 +252,9 @@ __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool a
                                              const f32x4 (&qv)[D / 16], int n, int g,
                                              int (&pick)[KMAX]) {
   constexpr int kTilesPerRound = tiles_per_round(D);
-  float ls[KMAX];
-  int li[KMAX];
+  key64 L[KMAX];
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    ls[j] = -INFINITY;
-    li[j] = kNoId;
-  }
+  for (int j = 0; j < KMAX; ++j) L[j] = kPadKey;
   const int n_parent = n_rows >> bshift;
   const int sub_shift = bshift - 4;   // log2 of the tiles per pick
   const int tiles = all_keys ? (n_rows + 15) >> 4 : K << sub_shift;
@@ -209,25 +280,28 @@ __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool a
     for (int i = 0; i < kTilesPerRound; ++i) {
       if (first[i] < 0) continue;
       const f32x4 acc = score_tile<D>(kv[i], qv);
+      // branch-free: a candidate a lane does not take enters below every slot
       if constexpr (SINGLE) {
         // tile t = t0 + i is kept by the lanes with n / 4 == t % 4
-        if ((n >> 2) == ((t0 + i) & 3)) {
-          const int e = n & 3;
-          const float sc = e == 0 ? acc[0] : e == 1 ? acc[1] : e == 2 ? acc[2] : acc[3];
-          const int cid = first[i] + 4 * g + e;
-          if (cid < n_rows) list_insert<KMAX>(ls, li, sc, cid);
-        }
+        const int e = n & 3;
+        const float sc = e == 0 ? acc[0] : e == 1 ? acc[1] : e == 2 ? acc[2] : acc[3];
+        const int cid = first[i] + 4 * g + e;
+        const bool take = (n >> 2) == ((t0 + i) & 3) && cid < n_rows;
+        key_insert<KMAX>(L, make_key(sc, cid, take));
       } else {
+        key64 tk[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int cid = first[i] + 4 * g + e;
-          if (cid < n_rows) list_insert<KMAX>(ls, li, acc[e], cid);
+          tk[e] = make_key(acc[e], cid, cid < n_rows);
         }
+        sort4_desc(tk);
+        merge_into<KMAX, 4>(L, tk);
       }
     }
   }
-  if constexpr (SINGLE) merge_lists<KMAX, 1, 32>(ls, li, K, pick);
-  else merge_lists<KMAX, 16, 32>(ls, li, K, pick);
+  if constexpr (SINGLE) merge_lists<KMAX, 1, 32>(L, K, pick);
+  else merge_lists<KMAX, 16, 32>(L, K, pick);
 }
 
 // The waves of selection workgroup bid of nblocks (renumbered per XCD).

@@ -39,6 +39,8 @@ _KERNELS = {
     "select_pool_next_kernel": ("select_pool_kernel", "select.hip"),
     "expand_kernel": ("expand_kernel", "select.hip"),
     "attn_fwd_kernel": ("attn_fwd_kernel", "attn_fwd.hip"),
+    "csc_radix_kernel": ("csc_radix_kernel", "transpose.hip"),
+    "csc_assemble_kernel": ("csc_assemble_kernel", "transpose.hip"),
     "tile_sort_kernel": ("tile_sort_kernel", "transpose.hip"),
     "merge_kernel": ("merge_kernel", "transpose.hip"),
     "csc_bounds_kernel": ("csc_bounds_kernel", "transpose.hip"),
@@ -61,7 +63,8 @@ def profile_name(symbol: str):
         return None
     base, targs = m.group(1), m.group(2)
     if base == "bwd_key_kernel":
-        return _KEY_MODES.get((targs or "").strip(), "bwd_key_kernel"), "attn_bwd.hip"
+        mode = (targs or "").split(",")[0].strip()   # <MODE, head_dim>
+        return _KEY_MODES.get(mode, "bwd_key_kernel"), "attn_bwd.hip"
     return _KERNELS.get(base)
 
 

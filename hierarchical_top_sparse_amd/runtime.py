@@ -104,11 +104,13 @@ class Step:
             return
         main = torch.cuda.current_stream()
         self.side.wait_stream(main)
+        # the forward is issued first, so that a captured graph keeps it on the selection's
+        # queue and only the (shorter) transposes cross to another one
+        for _, fn in fwd:
+            fn()
         with torch.cuda.stream(self.side):
             for _, fn in tr:
                 fn()
-        for _, fn in fwd:
-            fn()
         main.wait_stream(self.side)
         for _, fn in bwd:
             fn()

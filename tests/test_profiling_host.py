@@ -21,6 +21,13 @@ def test_profile_names():
         "select_pool_kernel"
     assert profiling.profile_name("llsa::pool_next_kernel<16>(x)") == ("pool_next_kernel",
                                                                        "pool.hip")
+    # kernels templated on the head width as well
+    assert profiling.profile_name("void llsa::bwd_key_kernel<2, 64>(llsa::BwdArgs)")[0] == \
+        "bwd_key_overflow_kernel"
+    assert profiling.profile_name("llsa::bwd_key_kernel<0, 128>(llsa::BwdArgs)")[0] == \
+        "bwd_key_kernel"
+    assert profiling.profile_name("void llsa::csc_radix_kernel(llsa::CscArgs)") == \
+        ("csc_radix_kernel", "transpose.hip")
     assert profiling.profile_name("at::native::elementwise_kernel<128, 4>(...)") is None
 
 
