@@ -12,6 +12,8 @@ for writes.
   python -m hierarchical_top_sparse_amd.profiling traffic --fetch <fetch>_counter_collection.csv
          --write <write>_counter_collection.csv --copy-bytes T --workload px256_train
          --command ... --command ... > profiles/<workload>_traffic.json
+  python -m hierarchical_top_sparse_amd.profiling timeline <run>_kernel_trace.csv --steps 3
+         --title ... --command ...                       (markdown: the last steps' launches)
 """
 from __future__ import annotations
 
@@ -139,6 +141,29 @@ def traffic_record(fetch_csv, write_csv, copy_bytes, workload, commands) -> dict
             "commands": commands, "kernels": kernels}
 
 
+def step_timelines(path: str, first: str = "pool12_kernel", last_steps: int = 3) -> list:
+    """The last `last_steps` complete steps of a rocprofv3 kernel_trace.csv, a step starting at
+    each launch of `first`: per step, rows (name, queue, start_us, end_us) relative to the
+    step's first launch, for the library's own kernels other than the calibration ones."""
+    ev = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = profile_name(_col(r, "Kernel_Name"))
+            if key is None or key[0] in ("copy_kernel", "mfma_kernel", "reorder_kernel"):
+                continue
+            ev.append((int(_col(r, "Start_Timestamp")), int(_col(r, "End_Timestamp")), key[0],
+                       int(_col(r, "Queue_Id"))))
+    ev.sort()
+    starts = [i for i, e in enumerate(ev) if e[2] == first]
+    steps = []
+    for a, b in zip(starts, starts[1:] + [len(ev)]):
+        t0 = ev[a][0]
+        steps.append([(name, q, (s - t0) / 1e3, (e - t0) / 1e3) for s, e, name, q in ev[a:b]])
+    # the last step may be cut short by the end of the run: keep steps as long as the median
+    full = [st for st in steps if len(st) == max(len(x) for x in steps)]
+    return full[-last_steps:]
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -152,6 +177,11 @@ def main(argv=None):
     tr.add_argument("--copy-bytes", type=int, required=True)
     tr.add_argument("--workload", required=True)
     tr.add_argument("--command", action="append", default=[])
+    tl = sub.add_parser("timeline")
+    tl.add_argument("csv")
+    tl.add_argument("--steps", type=int, default=3)
+    tl.add_argument("--title", required=True)
+    tl.add_argument("--command", required=True)
     a = ap.parse_args(argv)
     if a.what == "stats":
         print(f"# {a.title}\n\nCommand (GPU box, repo root; `TMPDIR=/tmp`):\n\n```\n{a.command}\n"
@@ -159,6 +189,21 @@ def main(argv=None):
               f"|---|---:|---:|---:|---:|---:|")
         for sym, calls, avg, mn, mx, pct in kernel_stats_table(a.csv):
             print(f"| `{sym}` | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.2f} |")
+    elif a.what == "timeline":
+        print(f"# {a.title}\n\nCommand (GPU box, repo root; `TMPDIR=/tmp`):\n\n```\n{a.command}\n"
+              f"```\n\nThe last {a.steps} steps of the run (graph replays), each launch's start "
+              f"and end relative to the step's first launch; queues are the hardware queues "
+              f"the runtime put the launches on.")
+        for st in step_timelines(a.csv, last_steps=a.steps):
+            main_q = st[0][1]
+            side = [x for x in st if x[1] != main_q]
+            fwd = [x for x in st if x[0] == "attn_fwd_kernel"]
+            print(f"\nStep of {max(x[3] for x in st):.1f} µs"
+                  + (f": the other queue's launches end at {max(x[3] for x in side):.1f} µs, "
+                     f"the forward at {fwd[0][3]:.1f} µs" if side and fwd else "")
+                  + "\n\n| launch | queue | start µs | end µs | µs |\n|---|---:|---:|---:|---:|")
+            for name, q, t0, t1 in st:
+                print(f"| `{name}` | {q} | {t0:.1f} | {t1:.1f} | {t1 - t0:.1f} |")
     else:
         json.dump(traffic_record(a.fetch, a.write, a.copy_bytes, a.workload, a.command),
                   sys.stdout, indent=1)

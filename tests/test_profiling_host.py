@@ -47,3 +47,24 @@ def test_traffic_record_scales_by_the_copy(tmp_path):
     assert k["hbm_read_bytes_per_launch"] == 2000 * 2 * 1024
     assert k["hbm_write_bytes_per_launch"] == 500 * 1024
     assert k["source"].endswith("attn_fwd.hip") and len(k["source_sha256"]) == 64
+
+
+def test_step_timelines_split_at_the_first_kernel(tmp_path):
+    cols = ["Kernel_Name", "Queue_Id", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    for step, t0 in enumerate((1000, 9000, 20000)):   # ns; the third step is cut short
+        rows.append(("void llsa::pool12_bf16_kernel<64>(a)", 1, t0, t0 + 1000))
+        rows.append(("llsa::copy_kernel(x)", 1, t0 + 1100, t0 + 1200))   # calibration: skipped
+        if step < 2:
+            rows.append(("void llsa::attn_fwd_kernel<true, 4, 64>(a)", 1, t0 + 1500, t0 + 5000))
+            rows.append(("llsa::csc_radix_kernel(a)", 4, t0 + 1600, t0 + 3000))
+    path = tmp_path / "k_kernel_trace.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(cols, r)))
+    steps = profiling.step_timelines(str(path), last_steps=3)
+    assert len(steps) == 2   # the short one is left out
+    assert steps[1] == [("pool12_kernel", 1, 0.0, 1.0), ("attn_fwd_kernel", 1, 1.5, 5.0),
+                        ("csc_radix_kernel", 4, 1.6, 3.0)]
