@@ -573,15 +573,16 @@ void bwd_query_kernel(BwdArgs a) {
 // ====================================================================== stage 2: coarse keys
 // dK_l[j] = sum over the ancestors a in CSC_l[j] of the partial rows of a's slot holding j, over
 // every partial unit under a (2^units_log2 per level-2 group, 16^(l-2) groups per level-l query).
-// One launch for all levels l >= 2, 16-wave workgroups:
-//  * level 2: one wave per key (16 keys per workgroup); a key sums about K * units rows;
-//  * level >= 3: one workgroup per key; its rows (entry, unit) are dealt round-robin to the 16
+// One launch for all levels l >= 2, 8-wave workgroups (measured against 16-wave ones at 256^2
+// b2: 17 us against 21 us per launch):
+//  * level 2: one wave per key (8 keys per workgroup); a key sums about K * units rows;
+//  * level >= 3: one workgroup per key; its rows (entry, unit) are dealt round-robin to the 8
 //    waves and the waves' sums are added in a fixed order.
 // Lanes first resolve up to 64 CSC entries into partial-row offsets (lane = entry); every lane
 // then sums one channel of the rows, kCgBatch rows per round with all their loads in flight
 // (buffer loads: rows of missing entries read offset kNoRow, i.e. zeros); with 128 channels
 // a lane sums channels lane and lane + 64.  Deterministic.
-constexpr int kCgWaves = 16;
+constexpr int kCgWaves = 8;
 constexpr int kCgBatch = 16;
 
 struct CoarseGradArgs {
