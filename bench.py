@@ -150,8 +150,9 @@ def unit_model(p):
         "attn_fwd": dict(kernels=["attn_fwd_kernel"], bytes=tokens * (4 * d * es + 4),
                          flops=4 * tokens * kq * d),
         "index_transpose": dict(
-            kernels=["tile_sort_kernel", "merge_kernel", "csc_bounds_kernel",
-                     "csc_offsets_kernel", "csc_scatter_kernel"],
+            kernels=["csc_radix_kernel", "csc_assemble_kernel", "tile_sort_kernel",
+                     "merge_kernel", "csc_bounds_kernel", "csc_offsets_kernel",
+                     "csc_scatter_kernel"],
             bytes=sum(bh * (2 * nl * kk * 4 + (nl + 1) * 4)
                       for nl, kk in (p.csc_dims(l) for l in range(1, 2 + p.coarse_levels))),
             flops=0),

@@ -14,6 +14,9 @@ for writes.
          --command ... --command ... > profiles/<workload>_traffic.json
   python -m hierarchical_top_sparse_amd.profiling timeline <run>_kernel_trace.csv --steps 3
          --title ... --command ...                       (markdown: the last steps' launches)
+  python -m hierarchical_top_sparse_amd.profiling sq <pass1>_counter_collection.csv
+         <pass2>_counter_collection.csv --kernel ... --title ... --command ... --command ...
+                                                         (markdown: SQ counters per kernel)
 """
 from __future__ import annotations
 
@@ -164,6 +167,39 @@ def step_timelines(path: str, first: str = "pool12_kernel", last_steps: int = 3)
     return full[-last_steps:]
 
 
+# MI355X: GRBM_GUI_ACTIVE is reported summed over the 8 XCDs; 1024 SIMDs in 256 CUs
+_XCDS, _SIMDS, _CUS = 8, 1024, 256
+
+
+def sq_rows(csvs, kernels) -> list:
+    """Per kernel (profiler name): the SQ counters of the given passes averaged over its
+    dispatches, and what they derive to (MFMA busy, bf16 MFMA FLOP, per-wave instruction
+    counts, LDS activity and the share of it spent in bank conflicts)."""
+    vals = defaultdict(lambda: defaultdict(list))
+    for path in csvs:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = profile_name(_col(r, "Kernel_Name"))
+                if key is not None:
+                    vals[key[0]][_col(r, "Counter_Name")].append(float(_col(r, "Counter_Value")))
+    rows = []
+    for kn in kernels:
+        c = {name: sum(v) / len(v) for name, v in vals[kn].items()}
+        gui = c["GRBM_GUI_ACTIVE"] / _XCDS
+        waves = c["SQ_WAVES"]
+        rows.append({
+            "kernel": kn, "gui_cycles": gui,
+            "mfma_busy": c["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * _SIMDS),
+            "mfma_gflop": c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e9,
+            "mfma_per_wave": c["SQ_INSTS_MFMA"] / waves,
+            "valu_per_wave": c["SQ_INSTS_VALU"] / waves,
+            "lds_per_wave": c["SQ_INSTS_LDS"] / waves,
+            "lds_active": c["SQ_LDS_IDX_ACTIVE"] / (gui * _CUS),
+            "bank_conflict_share": (c["SQ_LDS_BANK_CONFLICT"] / c["SQ_LDS_IDX_ACTIVE"]
+                                    if c["SQ_LDS_IDX_ACTIVE"] else 0.0)})
+    return rows
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -182,6 +218,11 @@ def main(argv=None):
     tl.add_argument("--steps", type=int, default=3)
     tl.add_argument("--title", required=True)
     tl.add_argument("--command", required=True)
+    sq = sub.add_parser("sq")
+    sq.add_argument("csv", nargs="+")
+    sq.add_argument("--kernel", action="append", required=True)
+    sq.add_argument("--title", required=True)
+    sq.add_argument("--command", action="append", required=True)
     a = ap.parse_args(argv)
     if a.what == "stats":
         print(f"# {a.title}\n\nCommand (GPU box, repo root; `TMPDIR=/tmp`):\n\n```\n{a.command}\n"
@@ -189,6 +230,23 @@ def main(argv=None):
               f"|---|---:|---:|---:|---:|---:|")
         for sym, calls, avg, mn, mx, pct in kernel_stats_table(a.csv):
             print(f"| `{sym}` | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.2f} |")
+    elif a.what == "sq":
+        cmds = "\n".join(a.command)
+        print(f"# {a.title}\n\nCommands (GPU box, repo root; `TMPDIR=/tmp`), one counter pass "
+              f"each:\n\n```\n{cmds}\n```\n\nPer launch, averaged over the launches of each "
+              f"kernel in the run.  GRBM_GUI_ACTIVE comes summed over the {_XCDS} XCDs, so GUI "
+              f"cycles are that value / {_XCDS}.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GUI "
+              f"cycles x {_SIMDS} SIMDs); MFMA GFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; LDS "
+              f"active = SQ_LDS_IDX_ACTIVE / (GUI cycles x {_CUS} CUs); bank-conflict share = "
+              f"SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.  Per-wave counts divide by SQ_WAVES.\n"
+              f"\n| kernel | GUI cycles | MFMA busy | MFMA GFLOP | MFMA / wave | VALU / wave | "
+              f"LDS / wave | LDS active | LDS cycles in bank conflicts |\n"
+              f"|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+        for r in sq_rows(a.csv, a.kernel):
+            print(f"| `{r['kernel']}` | {r['gui_cycles']:,.0f} | {100 * r['mfma_busy']:.1f} % | "
+                  f"{r['mfma_gflop']:.1f} | {r['mfma_per_wave']:,.0f} | "
+                  f"{r['valu_per_wave']:,.0f} | {r['lds_per_wave']:,.0f} | "
+                  f"{100 * r['lds_active']:.1f} % | {100 * r['bank_conflict_share']:.1f} % |")
     elif a.what == "timeline":
         print(f"# {a.title}\n\nCommand (GPU box, repo root; `TMPDIR=/tmp`):\n\n```\n{a.command}\n"
               f"```\n\nThe last {a.steps} steps of the run (graph replays), each launch's start "

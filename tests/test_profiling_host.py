@@ -68,3 +68,22 @@ def test_step_timelines_split_at_the_first_kernel(tmp_path):
     assert len(steps) == 2   # the short one is left out
     assert steps[1] == [("pool12_kernel", 1, 0.0, 1.0), ("attn_fwd_kernel", 1, 1.5, 5.0),
                         ("csc_radix_kernel", 4, 1.6, 3.0)]
+
+
+def test_sq_rows_derive_busy_flops_and_per_wave_counts(tmp_path):
+    gui = 8 * 1000.0   # summed over the 8 XCDs: 1000 cycles
+    p1 = [(1, "void llsa::attn_fwd_kernel<true, 4, 64>(a)", n, v) for n, v in
+          (("GRBM_GUI_ACTIVE", gui), ("SQ_WAVES", 100.0),
+           ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 250.0), ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 2e6))]
+    p2 = [(1, "void llsa::attn_fwd_kernel<true, 4, 64>(a)", n, v) for n, v in
+          (("GRBM_GUI_ACTIVE", gui), ("SQ_INSTS_VALU", 5000.0), ("SQ_INSTS_MFMA", 300.0),
+           ("SQ_INSTS_LDS", 700.0), ("SQ_LDS_IDX_ACTIVE", 256 * 500.0),
+           ("SQ_LDS_BANK_CONFLICT", 256 * 100.0))]
+    _write(tmp_path / "p1.csv", p1)
+    _write(tmp_path / "p2.csv", p2)
+    (r,) = profiling.sq_rows([str(tmp_path / "p1.csv"), str(tmp_path / "p2.csv")],
+                             ["attn_fwd_kernel"])
+    assert r["gui_cycles"] == 1000.0
+    assert r["mfma_busy"] == 0.25 and r["mfma_gflop"] == 2e6 * 512 / 1e9
+    assert (r["valu_per_wave"], r["mfma_per_wave"], r["lds_per_wave"]) == (50.0, 3.0, 7.0)
+    assert r["lds_active"] == 0.5 and r["bank_conflict_share"] == 0.2
