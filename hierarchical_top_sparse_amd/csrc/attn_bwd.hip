@@ -1081,8 +1081,12 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
   }
 }
 
+// Two waves per SIMD (at most 256 registers): with 128 channels the compiler fits the CSC pass
+// in 254 without spilling (it takes 264 unconstrained, one wave per SIMD; 500 -> 403 us per
+// launch at 256x256 b2), while the overflow pass keeps one wave per SIMD (two would spill 17).
 template <int MODE, int D>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1)))
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(D == 64 || MODE == kKeyCsc ? 2 : 1)))
 void bwd_key_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 stQ[32 * bstride(D)];
   __shared__ __attribute__((aligned(16))) bf16 stO[32 * bstride(D)];   // dO rows
