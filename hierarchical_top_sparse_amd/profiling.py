@@ -14,6 +14,8 @@ for writes.
          --command ... --command ... > profiles/<workload>_traffic.json
   python -m hierarchical_top_sparse_amd.profiling timeline <run>_kernel_trace.csv --steps 3
          --title ... --command ...                       (markdown: the last steps' launches)
+  python -m hierarchical_top_sparse_amd.profiling sweep <bench --sweep output> --command ...
+                                                         (markdown: the resolution sweep tables)
   python -m hierarchical_top_sparse_amd.profiling sq <pass1>_counter_collection.csv
          <pass2>_counter_collection.csv --kernel ... --title ... --command ... --command ...
                                                          (markdown: SQ counters per kernel)
@@ -200,6 +202,50 @@ def sq_rows(csvs, kernels) -> list:
     return rows
 
 
+def sweep_tables(path: str) -> str:
+    """The three tables of the resolution sweep (`bench.py --sweep`, one JSON line per side):
+    LLSA (B = 16 and 64) against dense attention, LLSA against the single-level top-32
+    comparator, and the CSC against the dense-mask key-major pass."""
+    rows = []
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{") and '"side"' in line:
+                rows.append(json.loads(line))
+    g = lambda x: f"{x / 1e9:.2f} G"   # noqa: E731
+    out = ["## LLSA against dense attention (the pages' Figure 3: B = 16 and 64)", "",
+           "| side | tokens | dense fwd ms | B=16 fwd ms | B=16 fwd speed-up | B=64 fwd ms | "
+           "B=64 fwd speed-up | dense fwd+bwd ms | B=16 fwd+bwd ms | B=16 speed-up | "
+           "B=64 fwd+bwd ms | B=64 speed-up |",
+           "|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append(f"| {r['side']} | {r['tokens']} | {r['dense_fwd_ms']:.3f} | "
+                   f"{r['llsa_fwd_ms']:.4f} | {r['speedup_fwd']:.1f}x | {r['b64_fwd_ms']:.4f} | "
+                   f"{r['b64_speedup_fwd']:.1f}x | {r['dense_train_ms']:.3f} | "
+                   f"{r['llsa_train_ms']:.4f} | {r['speedup_train']:.1f}x | "
+                   f"{r['b64_train_ms']:.4f} | {r['b64_speedup_train']:.1f}x |")
+    out += ["", "## Quadratic selection: LLSA against single-level top-32", "",
+            "| side | LLSA select ms | single-level select ms | LLSA fwd+bwd ms | "
+            "single-level fwd+bwd ms | LLSA speed-up |", "|---:|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        out.append(f"| {r['side']} | {r['llsa_select_ms']:.4f} | "
+                   f"{r['single_level_select_ms']:.4f} | {r['llsa_train_ms']:.4f} | "
+                   f"{r['single_level_top32_train_ms']:.4f} | "
+                   f"{r['speedup_vs_single_level']:.2f}x |")
+    out += ["", "## KV backward: index transpose against a dense block mask (the pages' "
+            "Figure 4)", "", "| side | CSC bwd ms | mask bwd ms | CSC key pass pairs/s | "
+            "mask key pass pairs/s | LLSA (K=8) key pass pairs/s |",
+            "|---:|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        llsa = r.get("key_pass_block_pairs_per_s")
+        out.append(f"| {r['side']} | {r['single_level_bwd_csc_ms']:.4f} | "
+                   f"{r['single_level_bwd_mask_ms']:.4f} | "
+                   f"{g(r['key_pass_csc_block_pairs_per_s'])} | "
+                   f"{g(r['key_pass_mask_block_pairs_per_s'])} | "
+                   f"{g(llsa) if llsa else '-'} |")
+    return "\n".join(out)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -218,6 +264,9 @@ def main(argv=None):
     tl.add_argument("--steps", type=int, default=3)
     tl.add_argument("--title", required=True)
     tl.add_argument("--command", required=True)
+    sw = sub.add_parser("sweep")
+    sw.add_argument("jsonl")
+    sw.add_argument("--command", required=True)
     sq = sub.add_parser("sq")
     sq.add_argument("csv", nargs="+")
     sq.add_argument("--kernel", action="append", required=True)
@@ -230,6 +279,9 @@ def main(argv=None):
               f"|---|---:|---:|---:|---:|---:|")
         for sym, calls, avg, mn, mx, pct in kernel_stats_table(a.csv):
             print(f"| `{sym}` | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.2f} |")
+    elif a.what == "sweep":
+        print(f"Command (GPU box, repo root):\n\n```\n{a.command}\n```\n")
+        print(sweep_tables(a.jsonl))
     elif a.what == "sq":
         cmds = "\n".join(a.command)
         print(f"# {a.title}\n\nCommands (GPU box, repo root; `TMPDIR=/tmp`), one counter pass "

@@ -468,10 +468,14 @@ def test_whole_path_small_and_degenerate(h, w, levels, topk):
         assert_close(to64(got), ref_g, torch.bfloat16, name)
     if levels == 1 and topk * 16 == h * w:
         for i in range(2):   # every key of the head attended: plain softmax attention
-            o_d, _ = orc.dense_attention_forward(*(orc.reorder(ref[t], h, w)[0, i]
-                                                   for t in ("q", "k", "v")))
+            qm, km, vm, dom = (orc.reorder(ref[t], h, w)[0, i] for t in ("q", "k", "v", "do"))
+            o_d, _ = orc.dense_attention_forward(qm, km, vm)
             got = orc.reorder(to64(fwd["o"]), h, w)[0, i]
             assert_close(got, o_d, torch.bfloat16, f"dense-equivalent o head {i}")
+            for name, g, want_d in zip(("dq", "dk", "dv"), grads,
+                                       orc.dense_attention_backward(qm, km, vm, dom)):
+                assert_close(orc.reorder(to64(g), h, w)[0, i], want_d, torch.bfloat16,
+                             f"dense-equivalent {name} head {i}")
 
 
 def test_deterministic_and_autograd():

@@ -87,3 +87,21 @@ def test_sq_rows_derive_busy_flops_and_per_wave_counts(tmp_path):
     assert r["mfma_busy"] == 0.25 and r["mfma_gflop"] == 2e6 * 512 / 1e9
     assert (r["valu_per_wave"], r["mfma_per_wave"], r["lds_per_wave"]) == (50.0, 3.0, 7.0)
     assert r["lds_active"] == 0.5 and r["bank_conflict_share"] == 0.2
+
+
+def test_sweep_tables_read_the_bench_lines(tmp_path):
+    import json
+    r = {"side": 64, "tokens": 4096, "dense_fwd_ms": 0.085, "llsa_fwd_ms": 0.05,
+         "speedup_fwd": 1.7, "b64_fwd_ms": 0.0438, "b64_speedup_fwd": 1.94,
+         "dense_train_ms": 0.306, "llsa_train_ms": 0.1154, "speedup_train": 2.65,
+         "b64_train_ms": 0.1245, "b64_speedup_train": 2.46, "llsa_select_ms": 0.0223,
+         "single_level_select_ms": 0.0528, "single_level_top32_train_ms": 0.176,
+         "speedup_vs_single_level": 1.52, "single_level_bwd_csc_ms": 0.0969,
+         "single_level_bwd_mask_ms": 0.0737, "key_pass_csc_block_pairs_per_s": 1.46e9,
+         "key_pass_mask_block_pairs_per_s": 1.45e9, "key_pass_block_pairs_per_s": None}
+    path = tmp_path / "sweep.jsonl"
+    path.write_text("a progress line\n" + json.dumps(r) + "\n")
+    md = profiling.sweep_tables(str(path))
+    assert "| 64 | 4096 | 0.085 | 0.0500 | 1.7x |" in md
+    assert "| 64 | 0.0223 | 0.0528 | 0.1154 | 0.1760 | 1.52x |" in md
+    assert "| 64 | 0.0969 | 0.0737 | 1.46 G | 1.45 G | - |" in md
