@@ -395,9 +395,10 @@ __attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kern
     }
   };
 
-  // one block of U from its loads: rows to the wave's LDS tile, then the tiles of the blocks
-  // that picked it
-  auto block_u = [&](const BlockLd& f, int u) {
+  // one block of U: its rows from their loads to the wave's LDS tile (after which the load
+  // registers take the block two ahead, so that two blocks stay in flight while this one is
+  // computed), then the tiles of the blocks that picked it
+  auto stage_u = [&](const BlockLd& f) {
 #pragma unroll
     for (int m = 0; m < C::kLoads; ++m) {
       const int e = lane + 64 * m;
@@ -405,6 +406,8 @@ __attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kern
       *(i32x4*)(kt + at) = f.k[m];
       *(i32x4*)(vt + at) = f.v[m];
     }
+  };
+  auto compute_u = [&](int u) {
     wave_lds_sync();
     const int mask = uniform(umask[u]);
     for_blocks([&](auto bbc) {
@@ -413,11 +416,13 @@ __attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kern
     wave_lds_sync();
   };
   for (int u = 0; u < n_u; u += 2) {
-    block_u(fa, u);
+    stage_u(fa);
     fa = load_u(u + 2);
+    compute_u(u);
     if (u + 1 >= n_u) break;
-    block_u(fb, u + 1);
+    stage_u(fb);
     fb = load_u(u + 3);
+    compute_u(u + 1);
   }
 
   // ---- coarse keys, then O and the LSE of each block
