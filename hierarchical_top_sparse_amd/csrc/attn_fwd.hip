@@ -165,27 +165,28 @@ __attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kern
   }
 
   // ---- coarse keys of the group (slot e / (D/8) of 16 ctiles, channels 8 (e % (D/8)) ..
-  // +7): fp32 pooled values as bf16 hi + lo parts (fp32 tensors: as they are) and the bias
+  // +7): fp32 pooled values as bf16 hi + lo parts (fp32 tensors: as they are) and the bias.
+  // First each item's key id and bias (their loads overlap the ranking of the picks below),
+  // then, beside the first key blocks' loads, the rows themselves.
   const int pb0 = a2 * kBlock;
-  for (int e = tid; e < ctiles * 16 * (D / 8); e += 64 * kFwdWaves) {
+  constexpr int kCItems = (2 * 16 * (D / 8) + 64 * kFwdWaves - 1) / (64 * kFwdWaves);
+  const int citems = ctiles * 16 * (D / 8);
+  int cit_id[kCItems];
+  float cit_bias[kCItems];
+#pragma unroll
+  for (int it = 0; it < kCItems; ++it) {
+    const int e = tid + 64 * kFwdWaves * it;
     const int cslot = e / (D / 8), c8 = (e % (D / 8)) * 8;
-    f32x4 k0 = {0.f, 0.f, 0.f, 0.f}, k1 = k0, v0 = k0, v1 = k0;
-    float bias = -INFINITY;
-    int cslot_id = -1;
-    if (cslot < n_coarse) {
+    cit_id[it] = -1;
+    cit_bias[it] = -INFINITY;
+    if (e < citems && cslot < n_coarse) {
       const int l = 2 + cslot / K;
       const int nl = a.n >> (a.bshift * l);
       const int anc = (pb0 << kBlockShift) >> (a.bshift * l);   // the group's level-l ancestor
       const int id = a.sel[l - 1][((long)head * nl + anc) * K + (cslot - (l - 2) * K)];
       if (id >= 0 && id < nl) {
-        cslot_id = id;
-        const float* kp = a.k_lv[l - 1] + ((long)head * nl + id) * D + c8;
-        const float* vp = a.v_lv[l - 1] + ((long)head * nl + id) * D + c8;
-        k0 = *(const f32x4*)kp;
-        k1 = *(const f32x4*)(kp + 4);
-        v0 = *(const f32x4*)vp;
-        v1 = *(const f32x4*)(vp + 4);
-        bias = a.lbias * (float)l;   // log2(B^l), or 0 for unit weights
+        cit_id[it] = id;
+        cit_bias[it] = a.lbias * (float)l;   // log2(B^l), or 0 for unit weights
         if (a.exclude && l >= 3 && c8 == 0) {
           // level >= 3: dropped for the whole group if it is the parent of one of the keys
           // selected at level l - 1 for the group's level-(l-1) ancestor
@@ -193,28 +194,9 @@ __attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kern
           const int ancf = (pb0 << kBlockShift) >> (a.bshift * (l - 1));
           for (int i = 0; i < K; ++i)
             if ((a.sel[l - 2][((long)head * nf + ancf) * K + i] >> a.bshift) == id)
-              bias = -INFINITY;
+              cit_bias[it] = -INFINITY;
         }
       }
-    }
-    T* base = ctile + (cslot >> 4) * C::NB * C::kTile + (cslot & 15) * C::kStride + c8;
-    if constexpr (BF16) {
-      bf16x8 hi, lo;
-      split_bf16(k0, k1, hi, lo);
-      *(bf16x8*)base = hi;
-      *(bf16x8*)(base + C::kTile) = lo;
-      split_bf16(v0, v1, hi, lo);
-      *(bf16x8*)(base + 2 * C::kTile) = hi;
-      *(bf16x8*)(base + 3 * C::kTile) = lo;
-    } else {
-      *(f32x4*)base = k0;
-      *(f32x4*)(base + 4) = k1;
-      *(f32x4*)(base + C::kTile) = v0;
-      *(f32x4*)(base + C::kTile + 4) = v1;
-    }
-    if (c8 == 0) {
-      cbias[cslot] = bias;
-      cid[cslot] = cslot_id;
     }
   }
 
@@ -275,7 +257,50 @@ __attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kern
     }
     return f;
   };
+  // the coarse rows (loaded before the first key blocks, so they are waited for first)
+  f32x4 ck[kCItems][2], cv[kCItems][2];
+#pragma unroll
+  for (int it = 0; it < kCItems; ++it) {
+    const int e = tid + 64 * kFwdWaves * it;
+    const int cslot = e / (D / 8), c8 = (e % (D / 8)) * 8;
+    ck[it][0] = ck[it][1] = cv[it][0] = cv[it][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (e < citems && cit_id[it] >= 0) {
+      const int l = 2 + cslot / K;
+      const int nl = a.n >> (a.bshift * l);
+      const float* kp = a.k_lv[l - 1] + ((long)head * nl + cit_id[it]) * D + c8;
+      const float* vp = a.v_lv[l - 1] + ((long)head * nl + cit_id[it]) * D + c8;
+      ck[it][0] = *(const f32x4*)kp;
+      ck[it][1] = *(const f32x4*)(kp + 4);
+      cv[it][0] = *(const f32x4*)vp;
+      cv[it][1] = *(const f32x4*)(vp + 4);
+    }
+  }
   BlockLd fa = load_u(0), fb = load_u(1);
+#pragma unroll
+  for (int it = 0; it < kCItems; ++it) {
+    const int e = tid + 64 * kFwdWaves * it;
+    if (e >= citems) continue;
+    const int cslot = e / (D / 8), c8 = (e % (D / 8)) * 8;
+    T* base = ctile + (cslot >> 4) * C::NB * C::kTile + (cslot & 15) * C::kStride + c8;
+    if constexpr (BF16) {
+      bf16x8 hi, lo;
+      split_bf16(ck[it][0], ck[it][1], hi, lo);
+      *(bf16x8*)base = hi;
+      *(bf16x8*)(base + C::kTile) = lo;
+      split_bf16(cv[it][0], cv[it][1], hi, lo);
+      *(bf16x8*)(base + 2 * C::kTile) = hi;
+      *(bf16x8*)(base + 3 * C::kTile) = lo;
+    } else {
+      *(f32x4*)base = ck[it][0];
+      *(f32x4*)(base + 4) = ck[it][1];
+      *(f32x4*)(base + C::kTile) = cv[it][0];
+      *(f32x4*)(base + C::kTile + 4) = cv[it][1];
+    }
+    if (c8 == 0) {
+      cbias[cslot] = cit_bias[it];
+      cid[cslot] = cit_id[it];
+    }
+  }
   __syncthreads();   // coarse tiles staged (the only workgroup barrier)
 
   // with overlap exclusion, per-block biases: a level-2 slot is dropped for block bb if one of
