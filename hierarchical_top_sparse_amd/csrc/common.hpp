@@ -200,9 +200,6 @@ __device__ __forceinline__ int xcd_block(int bid, int nblocks) {
 }
 
 // ------------------------------------------------------------------ cross-lane
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
-__device__ __forceinline__ int shfl_xor_i(int v, int mask) { return __shfl_xor(v, mask, 64); }
-
 // Reduce over the four 16-lane rows of the wave (lanes n, n+16, n+32, n+48) on the VALU:
 // v_permlane16_swap exchanges rows 0<->1 and 2<->3 between its two operands, and
 // v_permlane32_swap the two 32-lane halves, so with both operands holding v the two results
