@@ -238,6 +238,48 @@ def _event_ms(fn, reps):
     return t0.elapsed_time(t1) / reps
 
 
+def _graph_ms(fn, reps=20, replays=5):
+    """Average duration of fn() from a HIP graph of `reps` back-to-back calls."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (reps * replays)
+
+
+def prologue_parts(step):
+    """What the pooling-and-selection launches hold (graph-timed, each part alone on the step's
+    buffers): Q and K's pooling, V's pooling, the selection of every level, and the fused
+    llsa_pool_select the step issues (V's pooling riding in the selection launches)."""
+    from hierarchical_top_sparse_amd import _abi
+    s, p = step, step.p
+    parts = {
+        "pool_select": lambda: _abi.llsa_pool_select(p, s.q, s.k, s.v, s.q_lv, s.k_lv,
+                                                     s.v_lv, s.sel),
+        "pool_qk": lambda: _abi.llsa_pool(p, s.q, s.k, None, s.q_lv, s.k_lv, s.v_lv),
+        "pool_v": lambda: _abi.llsa_pool(p, None, None, s.v, s.q_lv, s.k_lv, s.v_lv),
+        "select": lambda: _abi.llsa_select(p, s.q_lv, s.k_lv, s.sel),
+    }
+    return {f"{k}_ms": round(_graph_ms(f), 4) for k, f in parts.items()}
+
+
 def measure(step, steps, warmup, graph=True, with_copy=None):
     """Eager pass with per-kernel events, then the timed region (graph replays or eager
     steps).  Returns (ms_step, eager_ms, per_call, per_kernel_ms, per_step_kernel_ms)."""
@@ -662,7 +704,8 @@ def main():
                                         sorted(per_step_kernel_ms.items(),
                                                key=lambda kv: -kv[1])},
              "units": unit_rows, "side_kernels": side_rows,
-             "attention_kernels": kernel_fractions(p, per_kernel_ms)}
+             "attention_kernels": kernel_fractions(p, per_kernel_ms),
+             "prologue": prologue_parts(step)}
     del step
     if not args.no_configs:
         extra["configs"] = config_table(max(5, args.steps // 2), 2)
