@@ -56,6 +56,7 @@ struct SelArgs {
   int topk;     // K
   int hi, lo;   // levels computed: hi down to lo
   int bshift;   // log2(B): 4 or 6; a pick's B children are B / 16 tiles of 16 candidates
+  int parts;    // waves per group at level lo (1 or 2): part p ranks rounds p, p + parts, ..
 };
 
 // Candidate rows first + n (channels g D/4 .. g D/4 + D/4 - 1) of a 16-row tile; rows outside
@@ -212,11 +213,11 @@ __device__ __forceinline__ void merge_with_partner(key64 (&L)[N]) {
   bitonic_merge_desc<N>(L);
 }
 
-// The K best keys of the lists of the lanes in one group (all 64 lanes for LANE_BITS_LO = 1,
-// the 4 lanes n, n + 16, n + 32, n + 48 for LANE_BITS_LO = 16) as pick[0..K) (ids, kNoId
-// beyond K and for empty slots), sorted ascending.
+// Merges the lists of the lanes in one group (all 64 lanes for LANE_BITS_LO = 1, the 4 lanes
+// n, n + 16, n + 32, n + 48 for LANE_BITS_LO = 16): afterwards every lane of it holds the
+// group's best KMAX keys, descending.
 template <int KMAX, int LANE_BITS_LO, int LANE_BITS_HI>
-__device__ __forceinline__ void merge_lists(key64 (&L)[KMAX], int K, int (&pick)[KMAX]) {
+__device__ __forceinline__ void merge_lanes(key64 (&L)[KMAX]) {
   static_assert(LANE_BITS_HI == 32 && (LANE_BITS_LO == 1 || LANE_BITS_LO == 16), "groups");
   if constexpr (LANE_BITS_LO == 1) {
     merge_with_partner<1>(L);
@@ -226,6 +227,11 @@ __device__ __forceinline__ void merge_lists(key64 (&L)[KMAX], int K, int (&pick)
   }
   merge_with_partner<16>(L);
   merge_with_partner<32>(L);
+}
+
+// The ids of the first K keys of L (kNoId beyond K and for empty slots), sorted ascending.
+template <int KMAX>
+__device__ __forceinline__ void picks_of(const key64 (&L)[KMAX], int K, int (&pick)[KMAX]) {
 #pragma unroll
   for (int r = 0; r < KMAX; ++r) pick[r] = r < K ? key_id(L[r]) : kNoId;
 #pragma unroll
@@ -239,9 +245,9 @@ __device__ __forceinline__ void merge_lists(key64 (&L)[KMAX], int K, int (&pick)
     }
 }
 
-// Ranks the queries held in qv (columns n) against one candidate set and returns the K picks,
-// ascending, as pick[0..K) (kNoId beyond K): per query n in the lanes of column n (SINGLE:
-// the one query, in every lane).
+// Ranks the queries held in qv (columns n) against one candidate set (this wave's share of it:
+// rounds of tiles part, part + parts, ..) and returns each query's best KMAX keys, descending,
+// in L of every lane of column n (SINGLE: the one query, in every lane).
 //   all_keys: candidates are all n_rows keys of the level;
 //   else:     candidates are the B = 2^bshift children of each pick in pickv (lane i holds
 //             pick i of the parent, i < K; ids outside [0, n_rows / B) are skipped), B / 16
@@ -250,15 +256,14 @@ template <int KMAX, bool SINGLE, int D>
 __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool all_keys,
                                              int pickv, int K, int bshift,
                                              const f32x4 (&qv)[D / 16], int n, int g,
-                                             int (&pick)[KMAX]) {
+                                             int part, int parts, key64 (&L)[KMAX]) {
   constexpr int kTilesPerRound = tiles_per_round(D);
-  key64 L[KMAX];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) L[j] = kPadKey;
   const int n_parent = n_rows >> bshift;
   const int sub_shift = bshift - 4;   // log2 of the tiles per pick
   const int tiles = all_keys ? (n_rows + 15) >> 4 : K << sub_shift;
-  for (int t0 = 0; t0 < tiles; t0 += kTilesPerRound) {
+  for (int t0 = part * kTilesPerRound; t0 < tiles; t0 += parts * kTilesPerRound) {
     f32x4 kv[kTilesPerRound][D / 16];
     int first[kTilesPerRound];
 #pragma unroll
@@ -300,11 +305,14 @@ __device__ __forceinline__ void rank_queries(const float* kh, int n_rows, bool a
       }
     }
   }
-  if constexpr (SINGLE) merge_lists<KMAX, 1, 32>(L, K, pick);
-  else merge_lists<KMAX, 16, 32>(L, K, pick);
+  if constexpr (SINGLE) merge_lanes<KMAX, 1, 32>(L);
+  else merge_lanes<KMAX, 16, 32>(L);
 }
 
-// The waves of selection workgroup bid of nblocks (renumbered per XCD).
+// The waves of selection workgroup bid of nblocks (renumbered per XCD).  With parts = 2 the
+// two waves of a group each rank half of its candidate tiles, the second hands its lists to
+// the first through LDS, and the first merges and stores (the keys' total order makes the
+// picks independent of the split).
 template <int KMAX, int D>
 __device__ __forceinline__ void select_group(const SelArgs& a, int bid, int nblocks) {
   const int lane = threadIdx.x & 63;
@@ -313,63 +321,86 @@ __device__ __forceinline__ void select_group(const SelArgs& a, int bid, int nblo
   const int K = a.topk;
   const int lo = a.lo;
   const int bs = a.bshift;
+  const int parts = a.parts;
   const int n_lo = a.n >> (bs * lo);
   const int groups = (n_lo + 15) >> 4;
-  const int wave = uniform(xcd_block(bid, nblocks) * kSelWaves + (int)(threadIdx.x >> 6));
-  if (wave >= a.bh * groups) return;
-  const int head = uniform(wave / groups);
-  const int grp = uniform(wave - head * groups);
-
-  // picks of the parent of the level being ranked, one per lane
-  int pickv = kNoId;
-  if (lo < a.levels) {
-    // the group's parent is query (16 grp) >> bs at level lo + 1
-    if (a.hi == lo) {   // parent picks given: sel at level lo + 1
-      if (lane < K)
-        pickv = a.sel[lo][((long)head * (n_lo >> bs) + ((grp << 4) >> bs)) * K + lane];
-    } else {
-      // chain: ancestors at levels hi .. lo + 1, each a single query
-      for (int lv = a.hi; lv > lo; --lv) {
-        const int shift = bs * (lv - lo);
-        const int anc = (grp << 4) >> shift;          // query id at level lv
-        const int n_lv = a.n >> (bs * lv);
-        const bool top = lv == a.levels;
-        if (lv == a.hi && !top) {
-          // parent picks of the topmost computed ancestor are given at level hi + 1
-          if (lane < K)
-            pickv = a.sel[lv][((long)head * (n_lv >> bs) + (anc >> bs)) * K + lane];
-        }
-        const float* qrow = a.q[lv - 1] + ((long)head * n_lv + anc) * D + (D / 4) * g;
-        f32x4 qv[D / 16];
-#pragma unroll
-        for (int c = 0; c < D / 16; ++c) qv[c] = *(const f32x4*)(qrow + 4 * c);
-        int pick[KMAX];
-        rank_queries<KMAX, true, D>(a.k[lv - 1] + (long)head * n_lv * D, n_lv, top, pickv, K,
-                                    bs, qv, n, g, pick);
-        int nv = kNoId;
-#pragma unroll
-        for (int r = 0; r < KMAX; ++r)
-          if (lane == r) nv = pick[r];
-        pickv = nv;
-        if (((grp << 4) & ((1 << shift) - 1)) == 0 && lane < K)
-          a.sel[lv - 1][((long)head * n_lv + anc) * K + lane] = pickv;
-      }
-    }
-  }
-
-  // the group of 16 queries at level lo
-  const float* qh = a.q[lo - 1] + (long)head * n_lo * D;
+  const int slot = uniform(xcd_block(bid, nblocks) * kSelWaves + (int)(threadIdx.x >> 6));
+  const int wave = uniform(slot / parts);          // the group
+  const int part = uniform(slot - wave * parts);
+  const bool active = wave < a.bh * groups;
+  if (parts == 1 && !active) return;
+  const int head = uniform(active ? wave / groups : 0);
+  const int grp = uniform(active ? wave - head * groups : 0);
   const int q_id = grp * 16 + n;
   const bool qvalid = q_id < n_lo;
-  f32x4 qv[D / 16];
+  key64 L[KMAX];
+
+  if (active) {
+    // picks of the parent of the level being ranked, one per lane
+    int pickv = kNoId;
+    if (lo < a.levels) {
+      // the group's parent is query (16 grp) >> bs at level lo + 1
+      if (a.hi == lo) {   // parent picks given: sel at level lo + 1
+        if (lane < K)
+          pickv = a.sel[lo][((long)head * (n_lo >> bs) + ((grp << 4) >> bs)) * K + lane];
+      } else {
+        // chain: ancestors at levels hi .. lo + 1, each a single query
+        for (int lv = a.hi; lv > lo; --lv) {
+          const int shift = bs * (lv - lo);
+          const int anc = (grp << 4) >> shift;          // query id at level lv
+          const int n_lv = a.n >> (bs * lv);
+          const bool top = lv == a.levels;
+          if (lv == a.hi && !top) {
+            // parent picks of the topmost computed ancestor are given at level hi + 1
+            if (lane < K)
+              pickv = a.sel[lv][((long)head * (n_lv >> bs) + (anc >> bs)) * K + lane];
+          }
+          const float* qrow = a.q[lv - 1] + ((long)head * n_lv + anc) * D + (D / 4) * g;
+          f32x4 qv[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c)
-    qv[c] = qvalid ? *(const f32x4*)(qh + (long)q_id * D + (D / 4) * g + 4 * c)
-                   : f32x4{0.f, 0.f, 0.f, 0.f};
-  int pick[KMAX];
-  rank_queries<KMAX, false, D>(a.k[lo - 1] + (long)head * n_lo * D, n_lo, lo == a.levels,
-                               pickv, K, bs, qv, n, g, pick);
+          for (int c = 0; c < D / 16; ++c) qv[c] = *(const f32x4*)(qrow + 4 * c);
+          key64 La[KMAX];
+          rank_queries<KMAX, true, D>(a.k[lv - 1] + (long)head * n_lv * D, n_lv, top, pickv, K,
+                                      bs, qv, n, g, 0, 1, La);
+          int pick[KMAX];
+          picks_of<KMAX>(La, K, pick);
+          int nv = kNoId;
+#pragma unroll
+          for (int r = 0; r < KMAX; ++r)
+            if (lane == r) nv = pick[r];
+          pickv = nv;
+          if (part == 0 && ((grp << 4) & ((1 << shift) - 1)) == 0 && lane < K)
+            a.sel[lv - 1][((long)head * n_lv + anc) * K + lane] = pickv;
+        }
+      }
+    }
+
+    // the group of 16 queries at level lo
+    const float* qh = a.q[lo - 1] + (long)head * n_lo * D;
+    f32x4 qv[D / 16];
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c)
+      qv[c] = qvalid ? *(const f32x4*)(qh + (long)q_id * D + (D / 4) * g + 4 * c)
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+    rank_queries<KMAX, false, D>(a.k[lo - 1] + (long)head * n_lo * D, n_lo, lo == a.levels,
+                                 pickv, K, bs, qv, n, g, part, parts, L);
+  }
+  if (parts > 1) {   // every wave of the workgroup takes the barrier
+    __shared__ key64 xl[kSelWaves / 2][16][KMAX];
+    const int pair = (int)(threadIdx.x >> 7);
+    if (active && part == 1 && g == 0) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) xl[pair][n][j] = L[j];
+    }
+    __syncthreads();
+    if (!active || part != 0) return;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) L[i] = key_max(L[i], xl[pair][n][KMAX - 1 - i]);
+    bitonic_merge_desc<KMAX>(L);
+  }
   if (g == 0 && qvalid) {
+    int pick[KMAX];
+    picks_of<KMAX>(L, K, pick);
     int32_t* dst = a.sel[lo - 1] + ((long)head * n_lo + q_id) * K;
 #pragma unroll
     for (int r = 0; r < KMAX; ++r)
@@ -493,7 +524,11 @@ static hipError_t launch_select_range(const Shape& s, const float* const* q_lv,
   a.lo = level_lo;
   a.bshift = s.bshift;
   const int n_lo = s.n_level(level_lo);
-  const long waves = (long)s.bh * ((n_lo + 15) >> 4);   // one per group
+  // a group's candidate tiles at level lo: two waves share them where the groups are few
+  // (levels >= 2) and there is more than one round of tiles
+  const int tiles_lo = level_lo == s.levels ? (n_lo + 15) / 16 : s.topk << (s.bshift - 4);
+  a.parts = level_lo >= 2 && tiles_lo > tiles_per_round(s.d) ? 2 : 1;
+  const long waves = (long)s.bh * ((n_lo + 15) >> 4) * a.parts;   // parts per group
   const unsigned blocks = (unsigned)((waves + kSelWaves - 1) / kSelWaves);
   const auto by_k = [&](auto dc) {
     constexpr int D = decltype(dc)::value;
