@@ -704,8 +704,9 @@ def main():
                                         sorted(per_step_kernel_ms.items(),
                                                key=lambda kv: -kv[1])},
              "units": unit_rows, "side_kernels": side_rows,
-             "attention_kernels": kernel_fractions(p, per_kernel_ms),
-             "prologue": prologue_parts(step)}
+             "attention_kernels": kernel_fractions(p, per_kernel_ms)}
+    if not args.no_configs:   # (kept out of the headline-only runs the profiles are taken on)
+        extra["prologue"] = prologue_parts(step)
     del step
     if not args.no_configs:
         extra["configs"] = config_table(max(5, args.steps // 2), 2)
