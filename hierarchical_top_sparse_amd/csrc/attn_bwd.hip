@@ -132,8 +132,8 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* st, int t4, int lane) {
 //    2-bit mask of the blocks that picked each; U is streamed with row-major loads (16 K rows
 //    and 16 V rows per block, two blocks ahead in registers) through the wave's LDS tiles;
 //  * for each pick, one 16 x 16 tile: S^T = K Q^T and dP^T = V dO^T (16x16x32), P, P dP, and
-//    A += K^T (P dP), Bv += K^T P (16x16x16, hi + lo parts), so D = sum P dP is exact and
-//    dQ = scale (A - D Bv) needs one pass (the bf16 O is never read);
+//    A += K^T (P dP), Bv += K^T P (hi + lo parts, one 16x16x32 each), so D = sum P dP is
+//    exact and dQ = scale (A - D Bv) needs one pass (the bf16 O is never read);
 //  * the coarse keys (staged once per workgroup as bf16 hi + lo) add their tiles; at the end of
 //    a block its coarse scores are recomputed in the Q K^T orientation, which puts P and dS in
 //    the B-operand layout of the partial sums dV_c += P^T dO and dK_c += dS^T Q over the
@@ -420,10 +420,8 @@ void bwd_query_kernel(BwdArgs a) {
     for (int t4 = 0; t4 < D / 16; ++t4) {
       const int off = (4 * g + r4) * kStride + 16 * t4 + 4 * c4;
       const bf16x4 ktr = lds_read_tr16(kr + off);
-      acc_a[bb][t4] = mfma_bf16_k16(ktr, a_hi, acc_a[bb][t4]);
-      acc_a[bb][t4] = mfma_bf16_k16(ktr, a_lo, acc_a[bb][t4]);
-      acc_b[bb][t4] = mfma_bf16_k16(ktr, b_hi, acc_b[bb][t4]);
-      acc_b[bb][t4] = mfma_bf16_k16(ktr, b_lo, acc_b[bb][t4]);
+      acc_a[bb][t4] = mfma_bf16_k16x2(ktr, a_hi, ktr, a_lo, acc_a[bb][t4]);
+      acc_b[bb][t4] = mfma_bf16_k16x2(ktr, b_hi, ktr, b_lo, acc_b[bb][t4]);
       if (klo) {
         const bf16x4 ktl = lds_read_tr16(klo + off);
         acc_a[bb][t4] = mfma_bf16_k16(ktl, a_hi, acc_a[bb][t4]);
@@ -522,10 +520,8 @@ void bwd_query_kernel(BwdArgs a) {
           const int off = (4 * g + r4) * kStride + 16 * t4 + 4 * c4;
           const bf16x4 dot = lds_read_tr16(vt + off);   // dO^T
           const bf16x4 qtt = lds_read_tr16(kt + off);   // Q^T
-          cpv[c][t4] = mfma_bf16_k16(dot, p_hi, cpv[c][t4]);
-          cpv[c][t4] = mfma_bf16_k16(dot, p_lo, cpv[c][t4]);
-          cpk[c][t4] = mfma_bf16_k16(qtt, s_hi, cpk[c][t4]);
-          cpk[c][t4] = mfma_bf16_k16(qtt, s_lo, cpk[c][t4]);
+          cpv[c][t4] = mfma_bf16_k16x2(dot, p_hi, dot, p_lo, cpv[c][t4]);
+          cpk[c][t4] = mfma_bf16_k16x2(qtt, s_hi, qtt, s_lo, cpk[c][t4]);
         }
       }
       wave_lds_sync();

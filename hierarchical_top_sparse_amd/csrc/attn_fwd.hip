@@ -395,8 +395,11 @@ __attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kern
 #pragma unroll
       for (int t4 = 0; t4 < D / 16; ++t4) {
         const int off = (4 * g + r) * C::kStride + 16 * t4 + 4 * c;
-        acc[bb][t4] = mfma_bf16_k16(lds_read_tr16(vtl + off), pb, acc[bb][t4]);
-        if (vlo) acc[bb][t4] = mfma_bf16_k16(lds_read_tr16(vlo + off), pb, acc[bb][t4]);
+        if (vlo)
+          acc[bb][t4] = mfma_bf16_k16x2(lds_read_tr16(vtl + off), pb, lds_read_tr16(vlo + off),
+                                        pb, acc[bb][t4]);
+        else
+          acc[bb][t4] = mfma_bf16_k16(lds_read_tr16(vtl + off), pb, acc[bb][t4]);
       }
     } else {
 #pragma unroll

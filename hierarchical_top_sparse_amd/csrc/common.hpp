@@ -159,8 +159,21 @@ __device__ __forceinline__ f32x4 mfma_bf16_k32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 // v_mfma_f32_16x16x16_bf16: lane l holds A[l%16][4*(l/16) .. +3], B[4*(l/16) .. +3][l%16].
+// On gfx950 it takes as many cycles as the 16x16x32 form (measured: ~18 cycles per SIMD for
+// either), so it runs at half the rate per flop.
 __device__ __forceinline__ f32x4 mfma_bf16_k16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(*(i16x4*)&a, *(i16x4*)&b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 cat8(bf16x4 x, bf16x4 y) {
+  return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+// Two 16x16x16 products in one 16x16x32: a0 b0 + a1 b1, with each operand pair laid out as
+// the 16x16x16 form holds it.  Lane l's k slots 8(l/16) .. +3 take the first pair's k values
+// 4(l/16) .. +3 and slots +4 .. +7 the second's, so the sum over the 32 slots is the sum of
+// both products (hi + lo parts of one operand: a0 = a1 or b0 = b1).
+__device__ __forceinline__ f32x4 mfma_bf16_k16x2(bf16x4 a0, bf16x4 b0, bf16x4 a1, bf16x4 b1,
+                                                 f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(cat8(a0, a1), cat8(b0, b1), c, 0, 0, 0);
 }
 // v_mfma_f32_16x16x4_f32: lane l holds A[l%16][l/16], B[l/16][l%16].
 __device__ __forceinline__ f32x4 mfma_f32_k4(float a, float b, f32x4 c) {
