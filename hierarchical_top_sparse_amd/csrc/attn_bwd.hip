@@ -894,6 +894,7 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
   f32x4 dka[D / 16], dva[D / 16];
 #pragma unroll
   for (int t4 = 0; t4 < D / 16; ++t4) dka[t4] = dva[t4] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int ovc = 0, ovs = 0;   // the key block's overflow chunks (CSC pass)
 
   auto pair = [&](const PairLd& f) {
 #pragma unroll
@@ -964,6 +965,11 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
     const int32_t* rows = a.csc_rows[0] + (long)head * n1 * a.fine_k;
     const int e0 = uniform(off[j] + chunk * kKeyChunk);
     const int e1 = uniform(min(off[j + 1], e0 + kKeyChunk));
+    if constexpr (MODE == kKeyCsc) {
+      // requested with the offsets, so that no wave ends on a round trip for them
+      ovc = uniform(a.ov_count[(long)head * n1 + j]);
+      ovs = uniform(a.ov_start[(long)head * n1 + j]);
+    }
     int first_rows = -1;
     if constexpr (MODE == kKeyCsc) {
       // A third of the key blocks have no picks and need no key rows.  The others load them
@@ -1041,8 +1047,6 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
     return;
   }
   if constexpr (MODE == kKeyCsc) {   // the overflow chunks' partial sums, in chunk order
-    const int ovc = uniform(a.ov_count[(long)head * n1 + j]);
-    const int ovs = uniform(a.ov_start[(long)head * n1 + j]);
     for (int m = 0; m < ovc; ++m) {
       const float* src = a.ov_part + (((long)head * a.ov_cap + ovs + m) * 64 + lane) * (D / 2);
 #pragma unroll
