@@ -134,7 +134,8 @@ __device__ __forceinline__ bf16x8 lds_tr8(const bf16* st, int t4, int lane) {
 //  * for each pick, one 16 x 16 tile: S^T = K Q^T and dP^T = V dO^T (16x16x32), P, P dP, and
 //    A += K^T (P dP), Bv += K^T P (hi + lo parts, one 16x16x32 each), so D = sum P dP is
 //    exact and dQ = scale (A - D Bv) needs one pass (the bf16 O is never read);
-//  * the coarse keys (staged once per workgroup as bf16 hi + lo) add their tiles; at the end of
+//  * the coarse keys (staged once per workgroup as bf16 hi + lo, each wave counting its share in
+//    LDS and waiting for the count only where it reads them) add their tiles; at the end of
 //    a block its coarse scores are recomputed in the Q K^T orientation, which puts P and dS in
 //    the B-operand layout of the partial sums dV_c += P^T dO and dK_c += dS^T Q over the
 //    block's queries (Q and dO rows staged in the wave's tiles);
@@ -150,15 +151,15 @@ constexpr int kPickSentinel = 0x7f000000;
 __host__ __device__ constexpr int bwdq_wave_lds_bytes(int D) {
   return 2 * 16 * bstride(D) * 2 + 4 * kQPickList * 4 + 48 * 4;
 }
-// ... then the coarse tiles, each slot's bias and key id, and with overlap exclusion per-block
-// biases [waves][blocks][ctiles * 16].  The end-of-kernel reduction reuses the first
-// kQWaves * 16 * D floats.
+// ... then the coarse tiles, each slot's bias and key id, with overlap exclusion per-block
+// biases [waves][blocks][ctiles * 16], and the count of waves that have staged their share of
+// the coarse tiles.  The end-of-kernel reduction reuses the first kQWaves * 16 * D floats.
 static size_t bwd_query_lds_bytes(int D, int n_coarse, bool exclude) {
   const int ctiles = (n_coarse + 15) / 16;
   const size_t bytes = (size_t)kQWaves * bwdq_wave_lds_bytes(D) +
                        (size_t)ctiles * 4 * 16 * bstride(D) * 2 +
                        (sizeof(float) + sizeof(int)) * 16 * ctiles +
-                       (exclude ? sizeof(float) * kQWaves * q_blocks(D) * 16 * ctiles : 0);
+                       (exclude ? sizeof(float) * kQWaves * q_blocks(D) * 16 * ctiles : 0) + 16;
   return std::max(bytes, sizeof(float) * kQWaves * 16 * D);
 }
 
@@ -213,6 +214,19 @@ void bwd_query_kernel(BwdArgs a) {
   float* cbias = (float*)(ct + NCT * 4 * 16 * kStride);
   int* cid = (int*)(cbias + 16 * NCT);          // key id of each coarse slot (-1: none)
   float* wxb = (float*)(cid + 16 * NCT) + w * kQBlocks * 16 * NCT;   // exclusion: [bb][slot]
+  int* staged =
+      (int*)((float*)(cid + 16 * NCT) + (a.exclude ? kQWaves * kQBlocks * 16 * NCT : 0));
+  if (NCT > 0) {
+    if (tid == 0) *staged = 0;
+    __syncthreads();   // the count is zero (the waves start together, so this costs little)
+  }
+  // A wave reads the coarse tiles only at the end of its blocks (or for the exclusion biases),
+  // so each wave counts its staged share and goes on; a reader waits for the count.  The waves
+  // of a workgroup are resident together and stage without waiting for anything.
+  auto wait_staged = [&]() {
+    while (__hip_atomic_load(staged, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kQWaves)
+      __builtin_amdgcn_s_sleep(1);
+  };
 
   const uint32_t head_bytes = (uint32_t)a.n * D * 2;
   const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
@@ -357,10 +371,12 @@ void bwd_query_kernel(BwdArgs a) {
   };
   BlockLd fa = load_u(0), fb = load_u(1);
   if (NCT > 0) {
-    __syncthreads();   // coarse tiles staged
+    if (lane == 0)   // this wave's share of the coarse tiles is staged
+      __hip_atomic_fetch_add(staged, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
     // with overlap exclusion, per-block biases: a level-2 slot is dropped for block bb if one
     // of bb's fine picks lies in its span (the 16-token block j is in key (16 j) >> 2 log2(B))
     if (a.exclude) {
+      wait_staged();
       for (int sl = lane; sl < 16 * NCT; sl += 64) {
         const int id = cid[sl];
         const bool lv2 = sl < K && id >= 0;
@@ -527,6 +543,7 @@ void bwd_query_kernel(BwdArgs a) {
       wave_lds_sync();
     }
   };
+  if (NCT > 0) wait_staged();
   finish(I0{});
   if constexpr (kQBlocks > 1) finish(I1{});
 

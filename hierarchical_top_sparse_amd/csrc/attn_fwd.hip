@@ -18,6 +18,8 @@
 //     O^T += V^T P^T on v_mfma_f32_16x16x16_bf16 with V^T read by ds_read_b64_tr_b16;
 //  4. the coarse keys Sel_l[ancestor], l = 2..L, staged once per workgroup in LDS (fp32 pooled
 //     values as bf16 hi + lo parts, weight 16^l as the log2-domain bias 4l), then O and LSE.
+//     Each wave stages a share of them before its stream and counts it in LDS; a wave waits for
+//     the count only when it reads them, so no wave waits for the slowest one's staging.
 // fp32 tensors use v_mfma_f32_16x16x4f32 with the same data flow.  Workgroups are renumbered
 // so that each XCD (and its L2) works on one contiguous spatial range of level-2 groups.
 // D (head_dim) is 64 or 128 (bf16 only): rows, MFMA contraction chains and accumulators scale
@@ -82,8 +84,8 @@ __host__ __device__ constexpr int fwd_wave_lds_bytes(bool bf16, int D) {
   return 2 * 16 * (bf16 ? stride_bf16(D) * 2 : stride_f32(D) * 4) +
          (int)sizeof(int) * 4 * kWavePicks;
 }
-// ... then each slot's bias and key id, and with overlap exclusion per-block biases
-// [waves][4 blocks][ctiles * 16].
+// ... then each slot's bias and key id, with overlap exclusion per-block biases
+// [waves][4 blocks][ctiles * 16], and the count of waves that have staged their share.
 static size_t fwd_lds_bytes(bool bf16, int D, int n_coarse, bool exclude) {
   const int es = bf16 ? 2 : 4;
   const int stride = bf16 ? stride_bf16(D) : stride_f32(D);
@@ -91,7 +93,7 @@ static size_t fwd_lds_bytes(bool bf16, int D, int n_coarse, bool exclude) {
   const int ctiles = (n_coarse + 15) / 16;
   return kFwdWaves * fwd_wave_lds_bytes(bf16, D) + (size_t)ctiles * nb * 16 * stride * es +
          (sizeof(float) + sizeof(int)) * 16 * ctiles +
-         (exclude ? sizeof(float) * kFwdWaves * 4 * 16 * ctiles : 0);
+         (exclude ? sizeof(float) * kFwdWaves * 4 * 16 * ctiles : 0) + 16;
 }
 
 // QB: query blocks per wave (4, or 2 for K > 16 or 128 channels); D: head_dim
@@ -132,6 +134,9 @@ __attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kern
   float* cbias = (float*)(ctile + ctiles * C::NB * C::kTile);
   int* cid = (int*)(cbias + 16 * ctiles);       // key id of each coarse slot (-1: none)
   float* xbias = (float*)(cid + 16 * ctiles);   // with exclusion: [w][bb][slot] biases
+  int* staged = (int*)(xbias + (a.exclude ? kFwdWaves * 4 * 16 * ctiles : 0));
+  if (tid == 0) *staged = 0;
+  __syncthreads();   // the count is zero (the waves start together, so this costs little)
 
   const uint32_t head_bytes = (uint32_t)a.n * C::kRowBytes;
   const rsrc_t rq = make_rsrc_uniform((const char*)a.q + (size_t)head * head_bytes, head_bytes);
@@ -301,13 +306,22 @@ __attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kern
       cid[cslot] = cit_id[it];
     }
   }
-  __syncthreads();   // coarse tiles staged (the only workgroup barrier)
+  // This wave's share of the coarse tiles is staged.  The tiles are read only after the wave's
+  // stream (or by the exclusion biases below), so a wave counts its share and goes on instead
+  // of waiting at a barrier for the slowest one; a reader waits for the count.  The waves of a
+  // workgroup are resident together and stage without waiting for anything, so the wait ends.
+  if (lane == 0) __hip_atomic_fetch_add(staged, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+  auto wait_staged = [&]() {
+    while (__hip_atomic_load(staged, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < kFwdWaves)
+      __builtin_amdgcn_s_sleep(1);
+  };
 
   // with overlap exclusion, per-block biases: a level-2 slot is dropped for block bb if one of
   // bb's fine picks lies in its span (the 16-token block j is in key (16 j) >> 2 log2(B))
   const int cslots = 16 * ctiles;
   float* wxb = xbias + w * QB * cslots;
   if (a.exclude) {
+    wait_staged();
     for (int sl = lane; sl < cslots; sl += 64) {
       const int id = cid[sl];
       const bool lv2 = sl < K && id >= 0;
@@ -454,6 +468,7 @@ __attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kern
   }
 
   // ---- coarse keys, then O and the LSE of each block
+  wait_staged();
   for (int ct = 0; ct < ctiles; ++ct) {
     const T* cb0 = ctile + ct * C::NB * C::kTile;
     for_blocks([&](auto bbc) {
