@@ -61,9 +61,13 @@ struct BwdArgs {
   int32_t* ov_count;           // [bh, n_1] overflow chunks of key block j
   int32_t* ov_table;           // [bh, ov_cap] chunk t: (key block << 16) | chunk index m >= 1
   int32_t* ov_total;           // [bh] overflow chunks of the head
+  int32_t* ov_done;            // [bh, n_1] overflow chunks of key block j written (the plan
+                               // sets them to 0)
   float* ov_part;              // [bh, ov_cap, 64 lanes, D / 2]: raw dK, dV sums of a chunk
   int ov_cap;                  // overflow chunks per head the buffers hold
   int ov_waves;                // overflow waves per head: wave g runs chunks g, g + ov_waves, ..
+  int ov_blocks;               // leading workgroups of the key-major launch that run the
+                               // overflow chunks (64 channels), or 0 (a launch of their own)
   int plan_blocks;             // leading workgroups of the query-major launch that run the
                                // overflow plan (one per head, padded to a multiple of 8), or 0
   int bh;
@@ -745,12 +749,17 @@ __global__ __launch_bounds__(64 * kCgWaves) void coarse_grad_kernel(BwdArgs a,
 // wave that finishes early frees its slot at once.  A key block takes at most kKeyChunk CSC_1
 // entries itself; the rest of a popular block (a block every query block picks, as a key
 // with a large norm becomes under random weights) is cut into chunks of kKeyChunk that
-// overflow waves run beforehand, each writing raw partial sums that the key block's wave adds
-// in chunk order: the work stays balanced and the result deterministic.
+// overflow waves run, each writing raw partial sums that the key block's wave adds in chunk
+// order: the work stays balanced and the result deterministic.  With 64 channels the overflow
+// waves lead the key-major launch and count each written chunk per key block (a device-scope
+// release); a key block with chunks waits for its count (an acquire) before adding them, so an
+// empty plan costs nothing beyond a few idle waves.  With 128 channels they have a launch of
+// their own (one wave per SIMD: two would spill), and the count is complete before the key
+// blocks start.
 // Modes:
 //  * kKeyCsc: the key block's first chunk of CSC_1[j], plus its overflow partials, then store;
 //  * kKeyOverflow: overflow chunks (numbered by the plan), partial sums only; a head's
-//    kOvWaves waves take its chunks in turn, so an empty plan costs one short launch;
+//    kOvWaves waves take its chunks in turn;
 //  * kKeyMask: the comparator of a mask-based backward -- the query blocks of key block j are
 //    found by scanning column j of the dense block mask (all n_1 query blocks) instead of
 //    reading CSC_1[j]; the scan yields them in ascending order, the order of the CSC rows, and
@@ -771,6 +780,7 @@ __device__ void key_plan(const BwdArgs& a, int head, int* wsum) {
   int32_t* ovs = a.ov_start + (long)head * n1;
   int32_t* ovc = a.ov_count + (long)head * n1;
   int32_t* tab = a.ov_table + (long)head * a.ov_cap;
+  int32_t* done = a.ov_done + (long)head * n1;
   auto entries = [&](int c) { return c < n1 ? off[c + 1] - off[c] : 0; };
   int cnt = entries(t);
   int base = 0;
@@ -793,6 +803,7 @@ __device__ void key_plan(const BwdArgs& a, int head, int* wsum) {
     if (c < n1) {
       ovs[c] = start;
       ovc[c] = ov;
+      done[c] = 0;
       for (int m = 1; m <= ov; ++m) tab[start + m - 1] = (c << 16) | m;
     }
     cnt = next;
@@ -1061,9 +1072,25 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
       *(f32x4*)(dst + 4 * t4) = dka[t4];
       *(f32x4*)(dst + D / 4 + 4 * t4) = dva[t4];
     }
+    // the chunk is written: one count for its key block (a release at device scope, after
+    // every store of the wave)
+    if (lane == 0)
+      __hip_atomic_fetch_add(a.ov_done + (long)head * n1 + j, 1, __ATOMIC_RELEASE,
+                             __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   if constexpr (MODE == kKeyCsc) {   // the overflow chunks' partial sums, in chunk order
+    if (ovc > 0) {
+      // With 64 channels the overflow chunks run in this launch, ahead of the key blocks:
+      // wait until all of this block's are written.  Only key blocks with overflow chunks wait,
+      // a few per head, and the chunks' waves wait for nothing, so the wait ends; it is also
+      // bounded (about 0.2 s) so that no fault elsewhere can turn it into a hang.
+      const int32_t* done = a.ov_done + (long)head * n1 + j;
+      for (int spin = 0; spin < (1 << 22); ++spin) {
+        if (__hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= ovc) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
     for (int m = 0; m < ovc; ++m) {
       const float* src = a.ov_part + (((long)head * a.ov_cap + ovs + m) * 64 + lane) * (D / 2);
 #pragma unroll
@@ -1120,16 +1147,34 @@ void bwd_key_kernel(BwdArgs a) {
                          pend);
     }
   } else {
+    int kbi = kb;
+    if constexpr (MODE == kKeyCsc && D == 64) {
+      if ((int)blockIdx.x < a.ov_blocks) {   // leading workgroups: the overflow chunks
+        const int ob = uniform(xcd_block(blockIdx.x, a.ov_blocks));
+        const int head = uniform(ob / a.ov_waves);
+        if (head >= a.bh) return;   // padding to a multiple of 8 workgroups
+        const int total = uniform(a.ov_total[head]);
+        for (int t = uniform(ob - head * a.ov_waves); t < total; t += a.ov_waves) {
+          const int packed = uniform(a.ov_table[(long)head * a.ov_cap + t]);
+          key_block<kKeyOverflow, D>(a, head, packed >> 16, packed & 0xffff, t, stQ, stO,
+                                     pdown, stL, pend);
+        }
+        return;
+      }
+      // key blocks: numbered without the leading workgroups (a multiple of 8, so each XCD
+      // keeps its contiguous range)
+      kbi = uniform(xcd_block(blockIdx.x - a.ov_blocks, gridDim.x - a.ov_blocks));
+    }
     const int n1 = a.n >> kBlockShift;
-    const int head = uniform(kb / n1);
-    key_block<MODE, D>(a, head, uniform(kb - head * n1), 0, 0, stQ, stO, pdown, stL, pend);
+    const int head = uniform(kbi / n1);
+    key_block<MODE, D>(a, head, uniform(kbi - head * n1), 0, 0, stQ, stO, pdown, stL, pend);
   }
 }
 
 // ====================================================================== host side
 struct BwdLayout {
   size_t dd, part_k, part_v, dk_lv[kMaxLv], dv_lv[kMaxLv];
-  size_t ov_start, ov_count, ov_table, ov_total, ov_part;
+  size_t ov_start, ov_count, ov_table, ov_total, ov_done, ov_part;
   int ov_cap;
   size_t total;
 };
@@ -1167,6 +1212,7 @@ static BwdLayout bwd_layout(const Shape& s) {
   L.ov_count = take(sizeof(int32_t) * s.bh * n1);
   L.ov_table = take(sizeof(int32_t) * s.bh * (size_t)L.ov_cap);
   L.ov_total = take(sizeof(int32_t) * s.bh);
+  L.ov_done = take(sizeof(int32_t) * s.bh * n1);
   L.ov_part = take(sizeof(float) * s.bh * (size_t)L.ov_cap * 64 * (s.d / 2));
   L.total = off;
   return L;
@@ -1203,6 +1249,7 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
   a.ov_count = (int32_t*)(base + L.ov_count);
   a.ov_table = (int32_t*)(base + L.ov_table);
   a.ov_total = (int32_t*)(base + L.ov_total);
+  a.ov_done = (int32_t*)(base + L.ov_done);
   a.ov_part = (float*)(base + L.ov_part);
   a.ov_cap = L.ov_cap;
   const bool coarse = s.coarse_levels > 0;
@@ -1283,10 +1330,10 @@ hipError_t launch_attn_bwd(const Shape& s, const void* q, const void* k, const v
     LLSA_LAUNCH("bwd_key_mask_kernel", (bwd_key_kernel<kKeyMask, 64>), kgrid, dim3(64), 0,
                 stream, a);
   } else if (s.d == 64) {
-    LLSA_LAUNCH("bwd_key_overflow_kernel", (bwd_key_kernel<kKeyOverflow, 64>), ovgrid, dim3(64),
-                0, stream, a);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    LLSA_LAUNCH("bwd_key_kernel", (bwd_key_kernel<kKeyCsc, 64>), kgrid, dim3(64), 0, stream, a);
+    // the overflow chunks lead the key-major launch (no launch of their own)
+    a.ov_blocks = (int)(((long)s.bh * a.ov_waves + 7) / 8 * 8);
+    LLSA_LAUNCH("bwd_key_kernel", (bwd_key_kernel<kKeyCsc, 64>),
+                dim3((unsigned)(a.ov_blocks + kwaves)), dim3(64), 0, stream, a);
   } else {
     LLSA_LAUNCH("bwd_key_overflow_kernel", (bwd_key_kernel<kKeyOverflow, 128>), ovgrid,
                 dim3(64), 0, stream, a);
