@@ -1085,11 +1085,14 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
       // wait until all of this block's are written.  Only key blocks with overflow chunks wait,
       // a few per head, and the chunks' waves wait for nothing, so the wait ends; it is also
       // bounded (about 0.2 s) so that no fault elsewhere can turn it into a hang.
+      // Polls are relaxed loads (an acquire at device scope invalidates this XCD's L2, which
+      // the other waves' gathers live in); one acquire fence follows the last poll.
       const int32_t* done = a.ov_done + (long)head * n1 + j;
       for (int spin = 0; spin < (1 << 22); ++spin) {
-        if (__hip_atomic_load(done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) >= ovc) break;
+        if (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= ovc) break;
         __builtin_amdgcn_s_sleep(2);
       }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     for (int m = 0; m < ovc; ++m) {
       const float* src = a.ov_part + (((long)head * a.ov_cap + ovs + m) * 64 + lane) * (D / 2);
