@@ -854,8 +854,8 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
   const rsrc_t rv = make_rsrc_uniform((const char*)a.v + (size_t)head * head_bytes, head_bytes);
   const rsrc_t rdo =
       make_rsrc_uniform((const char*)a.dout + (size_t)head * head_bytes, head_bytes);
-  const rsrc_t rl = make_rsrc_uniform(a.lse + tok_base, (uint32_t)a.n * 4);
-  const rsrc_t rd = make_rsrc_uniform(a.dd + tok_base, (uint32_t)a.n * 4);
+  const float* lse_h = a.lse + tok_base;   // the head's LSE and D
+  const float* dd_h = a.dd + tok_base;
 
   // keys of this block as B operands: lane (n, g) holds row n, channels 32s + 8g .. +7
   const int krow = block_corner(j, a.grid) + tile_offset(n, a.grid);
@@ -902,20 +902,19 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
     if (2 * k + 1 >= cnt) bB = tB = kNoRow;
     f.okA = bA != kNoRow;
     f.okB = bB != kNoRow;
+    // lanes 0..31 read the LSE, lanes 32..63 D, in one load through a per-lane pointer (an
+    // absent block reads its lane's query of block 0: its P is 0), issued before the rows.
+    // One load into one register: two loads whose sum the compiler formed where it liked
+    // made it wait for every load in flight there, the next pair's rows included.
+    const uint32_t tl = (((lane >> 4) & 1) ? tB : tA);
+    f.ld = *(const float*)((const char*)(lane < 32 ? lse_h : dd_h) + (tl == kNoRow ? 0u : tl) +
+                           n * 4);
 #pragma unroll
     for (int ins = 0; ins < NINS; ++ins) {
       const uint32_t o = (ins >= NINS / 2 ? bB : bA) + st_off[ins];
       f.q[ins] = __builtin_amdgcn_raw_buffer_load_b128(rq, o, 0, 0);
       f.d[ins] = __builtin_amdgcn_raw_buffer_load_b128(rdo, o, 0, 0);
     }
-    // lanes 0..31 read the LSE, lanes 32..63 D: one load from each array (the other half of
-    // the wave reads offset kNoRow, i.e. zero), so the buffer descriptor stays wave-uniform
-    const uint32_t tl = (((lane >> 4) & 1) ? tB : tA) + (uint32_t)(n * 4);
-    const float l_part = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rl, lane < 32 ? tl : kNoRow, 0, 0));
-    const float d_part = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rd, lane < 32 ? kNoRow : tl, 0, 0));
-    f.ld = l_part + d_part;
     return f;
   };
 
@@ -979,12 +978,18 @@ __device__ __forceinline__ void key_block(const BwdArgs& a, int head, int j, int
     }
     const int npairs = (cnt + 1) >> 1;
     PairLd fa = load_pair(0), fb;
-    for (int k = 0; k < npairs; k += 2) {
+    // whole pairs of pairs in the loop, an odd last pair after it (a break inside the loop
+    // body gives the loop head a second entry whose wait counts drain every load in flight)
+    int k = 0;
+    for (; k + 1 < npairs; k += 2) {
       fb = load_pair(k + 1);
       pair(fa);
-      if (k + 1 >= npairs) break;
       fa = load_pair(k + 2);
       pair(fb);
+    }
+    if (k < npairs) {
+      fb = load_pair(k + 1);
+      pair(fa);
     }
   };
   if constexpr (!MASK) {

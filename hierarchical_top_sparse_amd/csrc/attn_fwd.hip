@@ -457,14 +457,21 @@ __attribute__((amdgpu_waves_per_eu(BF16 && D == 64 ? 3 : 2))) void attn_fwd_kern
     });
     wave_lds_sync();
   };
-  for (int u = 0; u < n_u; u += 2) {
+  // Whole pairs in the loop and an odd last block after it: with a break inside the loop
+  // body, one path into the loop head has only the first block's loads in flight, and the
+  // head then waits for every load (the next block's too) instead of the first block's.
+  int u = 0;
+  for (; u + 1 < n_u; u += 2) {
     stage_u(fa);
     fa = load_u(u + 2);
     compute_u(u);
-    if (u + 1 >= n_u) break;
     stage_u(fb);
     fb = load_u(u + 3);
     compute_u(u + 1);
+  }
+  if (u < n_u) {
+    stage_u(fa);
+    compute_u(u);
   }
 
   // ---- coarse keys, then O and the LSE of each block
