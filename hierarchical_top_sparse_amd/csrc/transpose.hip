@@ -370,30 +370,39 @@ __global__ __launch_bounds__(kRThreads) void csc_radix_kernel(CscArgs a) {
   int si = 0;
   while (si + 1 < a.nsets && bid >= a.set[si + 1].first_block) ++si;
   const CscSet& S = a.set[si];
+  // the set's sizes in scalar registers once (read through the dynamic set index, the
+  // compiler otherwise reloads them at each use, each reload waiting for all LDS traffic)
+  int cols = S.cols, kk = S.k, nnz = S.nnz, passes = S.passes, tiles = S.tiles;
+  asm volatile("" : "+s"(cols), "+s"(kk), "+s"(nnz), "+s"(passes), "+s"(tiles));
   const int local = bid - S.first_block;
-  const int mat = local / S.tiles;
-  const int tile = local - mat * S.tiles;
+  const int mat = local / tiles;
+  const int tile = local - mat * tiles;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int base = tile * kRTile;
-  const int len = min(kRTile, S.nnz - base);
-  const int32_t* in = S.csr + (long)mat * S.nnz;
+  const int len = min(kRTile, nnz - base);
+  const int32_t* in = S.csr + (long)mat * nnz;
   uint32_t col[kRRounds];
   int32_t row[kRRounds];
+  // every load issued before any is used (a load inside the bounds test made each one a
+  // round trip of its own); past the tile's end a lane reads its last entry and ignores it
+  int raw[kRRounds];
+#pragma unroll
+  for (int e = 0; e < kRRounds; ++e) raw[e] = in[base + min(e * kRThreads + t, len - 1)];
 #pragma unroll
   for (int e = 0; e < kRRounds; ++e) {
     const int i = e * kRThreads + t;
     if (i < len) {
-      int c = in[base + i];
-      if (c < 0 || c >= S.cols) c = S.cols;   // dropped: sorts behind the kept entries
+      int c = raw[e];
+      if (c < 0 || c >= cols) c = cols;   // dropped: sorts behind the kept entries
       col[e] = (uint32_t)c;
-      row[e] = (base + i) / S.k;
+      row[e] = (base + i) / kk;
     } else {
-      col[e] = (uint32_t)S.cols + 1;          // padding: behind everything
+      col[e] = (uint32_t)cols + 1;          // padding: behind everything
       row[e] = -1;
     }
   }
   const uint64_t below = (1ull << lane) - 1;   // lanes before this one
-  for (int p = 0; p < S.passes; ++p) {
+  for (int p = 0; p < passes; ++p) {
     const int shift = p * kDigitBits;
     for (int h = t; h < kHist; h += kRThreads) hist[h] = 0;
     __syncthreads();
@@ -447,18 +456,18 @@ __global__ __launch_bounds__(kRThreads) void csc_radix_kernel(CscArgs a) {
   // the sorted tile: its rows, and lb[c] = first position whose column is >= c, c = 0..cols
   int32_t* lb;
   int32_t* rows_dst;
-  if (S.tiles == 1) {
-    lb = S.off + (long)mat * (S.cols + 1);
-    rows_dst = S.rows_out + (long)mat * S.nnz;
+  if (tiles == 1) {
+    lb = S.off + (long)mat * (cols + 1);
+    rows_dst = S.rows_out + (long)mat * nnz;
   } else {
-    lb = S.bounds + ((long)mat * S.tiles + tile) * (S.cols + 1);
-    rows_dst = S.trows + ((long)mat * S.tiles + tile) * kRTile;
+    lb = S.bounds + ((long)mat * tiles + tile) * (cols + 1);
+    rows_dst = S.trows + ((long)mat * tiles + tile) * kRTile;
   }
 #pragma unroll
   for (int e = 0; e < kRRounds; ++e)
     if (e * kRThreads + t < len) rows_dst[e * kRThreads + t] = row[e];
-  for (int c0 = t; c0 <= S.cols; c0 += 8 * kRThreads)
-    column_bounds8(col_s, len, c0, kRThreads, S.cols, 0, lb);
+  for (int c0 = t; c0 <= cols; c0 += 8 * kRThreads)
+    column_bounds8(col_s, len, c0, kRThreads, cols, 0, lb);
 }
 
 // Per column range: each of the cblocks workgroups of a matrix owns the CR real columns
