@@ -1,7 +1,8 @@
 // Sparse attention backward (paper summary sec. 4.1 and Figure 4: the KV gradient is
 // computed key-major over a CSR->CSC sparse index transpose, so no T x T mask is formed).
 //
-// Three stages, all deterministic (no atomics):
+// Three stages, all deterministic (every sum in a fixed order; the only atomics are integer
+// completion counts that order work, never sums of data):
 //  1. bwd_query_kernel  (query-major, one wave per level-1 query block, one workgroup per
 //     level-2 group of 16 blocks): D = sum_e P_e dP_e (exact, from the recomputed scores, so
 //     the rounded O is never needed), dQ over the block's fine and coarse keys,

@@ -26,7 +26,8 @@
  *  - Return value: llsa_status.  Validation errors return before anything is enqueued and
  *    leave outputs untouched; LLSA_ERR_HIP means a launch failed (outputs undefined).
  *    llsa_last_error() gives a message for the last failure on the calling thread.
- *  - Results are deterministic: no atomics, fixed reduction orders.
+ *  - Results are deterministic: every sum has a fixed order and no data is added atomically
+ *    (the only atomics are integer completion counts that order work).
  *  - Supported: head_dim 64 or 128, block 16 (4x4 pixel tiles) or 64 (8x8 pixel tiles),
  *    height and width powers of two >= 4, 256 <= N <= 2^23, N % block^levels == 0,
  *    1 <= topk <= min(32, N / block^levels) and topk * block / 16 <= 32,
@@ -220,8 +221,11 @@ int32_t llsa_index_transpose_levels(const llsa_problem* p, const int32_t* const*
  * sel[0], csc_off[0], csc_rows[0]: level 1 as 16-token blocks (sel[0] as for llsa_attn_fwd;
  * its transpose has rows = cols = N/16 and k = topk * block / 16).  N <= 2^19 per head (the
  * level-1 transpose's 32-bit codes); LLSA_ERR_UNSUPPORTED above.
- * Deterministic (no atomics): the query blocks of a key block picked by more than 128 of
- * them are cut into chunks of 128 whose partial dK/dV sums are added in chunk order.
+ * Deterministic: the query blocks of a key block picked by more than 128 of them are cut
+ * into chunks of 128 whose partial dK/dV sums are added in chunk order (with head_dim 64 the
+ * chunks run in the key-major launch, and an integer count per key block, one increment per
+ * written chunk, tells the key block when they are all written; no data is summed
+ * atomically).
  * ws: llsa_workspace_bytes(bwd) bytes of device memory (D, coarse partials, chunk partials).
  */
 int32_t llsa_attn_bwd(const llsa_problem* p, const void* q, const void* k, const void* v,
