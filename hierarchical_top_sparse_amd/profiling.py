@@ -274,17 +274,17 @@ def main(argv=None):
     sq.add_argument("--command", action="append", required=True)
     a = ap.parse_args(argv)
     if a.what == "stats":
-        print(f"# {a.title}\n\nCommand (GPU box, repo root; `TMPDIR=/tmp`):\n\n```\n{a.command}\n"
+        print(f"# {a.title}\n\nCommand (MI355X host, repo root; `TMPDIR=/tmp`):\n\n```\n{a.command}\n"
               f"```\n\n| kernel | calls | avg µs | min µs | max µs | % of GPU time |\n"
               f"|---|---:|---:|---:|---:|---:|")
         for sym, calls, avg, mn, mx, pct in kernel_stats_table(a.csv):
             print(f"| `{sym}` | {calls} | {avg:.2f} | {mn:.2f} | {mx:.2f} | {pct:.2f} |")
     elif a.what == "sweep":
-        print(f"Command (GPU box, repo root):\n\n```\n{a.command}\n```\n")
+        print(f"Command (MI355X host, repo root):\n\n```\n{a.command}\n```\n")
         print(sweep_tables(a.jsonl))
     elif a.what == "sq":
         cmds = "\n".join(a.command)
-        print(f"# {a.title}\n\nCommands (GPU box, repo root; `TMPDIR=/tmp`), one counter pass "
+        print(f"# {a.title}\n\nCommands (MI355X host, repo root; `TMPDIR=/tmp`), one counter pass "
               f"each:\n\n```\n{cmds}\n```\n\nPer launch, averaged over the launches of each "
               f"kernel in the run.  GRBM_GUI_ACTIVE comes summed over the {_XCDS} XCDs, so GUI "
               f"cycles are that value / {_XCDS}.  MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GUI "
@@ -300,7 +300,7 @@ def main(argv=None):
                   f"{r['valu_per_wave']:,.0f} | {r['lds_per_wave']:,.0f} | "
                   f"{100 * r['lds_active']:.1f} % | {100 * r['bank_conflict_share']:.1f} % |")
     elif a.what == "timeline":
-        print(f"# {a.title}\n\nCommand (GPU box, repo root; `TMPDIR=/tmp`):\n\n```\n{a.command}\n"
+        print(f"# {a.title}\n\nCommand (MI355X host, repo root; `TMPDIR=/tmp`):\n\n```\n{a.command}\n"
               f"```\n\nThe last {a.steps} steps of the run (graph replays), each launch's start "
               f"and end relative to the step's first launch; queues are the hardware queues "
               f"the runtime put the launches on.")
