@@ -6,7 +6,8 @@ transpose of every level -> sparse backward (dQ, dK, dV); the Morton reorder is 
 the kernels' addressing (inputs and outputs stay in raster order).  The step is captured once
 into a HIP graph and replayed; `value` is batch*N tokens per second of graph replays.  A
 second, eager pass with per-kernel HIP events (recorded by the library on each kernel's own
-stream) gives each kernel's launch duration.  Every row of the path is priced as a unit
+stream; this pass issues every call on one stream, so each kernel is timed alone) gives each
+kernel's launch duration.  Every row of the path is priced as a unit
 (`extra.units`: its algorithmic bytes per step over the summed time of its launches); the
 roofline object is for the unit with the largest time (the backward: its four kernels),
 against the vendor HBM peak and against the achievable peak the library's own streaming-copy
